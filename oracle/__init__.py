@@ -1,0 +1,177 @@
+"""fp64 CPU oracle for Hedgehog-style linear attention (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library and its Python binding
+never touch it.  The arithmetic lives in ``hh_oracle.c`` (plain C, double
+precision); this module builds it with gcc and marshals numpy arrays.
+
+What each function computes, with its source on the pages ("The Hedgehog &
+the Porcupine: Expressive Linear Attentions with Softmax Mimicry"):
+  featuremap  -- Hedgehog map exp(+-(W x + b)) (section 3.4, "The Hedgehog MLP
+                 Feature Map", Choices 1 and 3) or the degree-2 Taylor map
+                 (section 3.4, "The Taylor Exponential as a Bridge Result").
+  causal      -- Eq. 2 by running sums S_i, z_i (section 3.4, "Complexity
+                 Analysis"), with optional initial and final state.
+  bidir       -- the same sums over all keys (bidirectional encoders).
+  decode_step -- one running-sum update followed by the read-out.
+  quadratic   -- Eq. 2 as an explicit sum over key positions (no running sums),
+                 used to pin the running-sum form and for sampled rows.
+Parity status: every function is pinned by the closed forms and invariants in
+tests/test_oracle_pins.py (no function is "parity unpinned").
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "hh_oracle.c")
+LIB = os.path.join(HERE, "libhh_oracle.so")
+
+MAP_HEDGEHOG = 0
+MAP_TAYLOR2 = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile hh_oracle.c into libhh_oracle.so next to it (gcc, -O2, IEEE fp64)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, SRC,
+                               "-lm", "-lpthread"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build(force=True)
+        lib = ctypes.CDLL(LIB)
+        D = ctypes.c_void_p
+        L = ctypes.c_long
+        I = ctypes.c_int
+        lib.hho_feature_dim.argtypes = [I, I]
+        lib.hho_feature_dim.restype = I
+        lib.hho_causal.argtypes = [I, I, L, L, L, D, D, D, D, D, D, D, D, D, D, I]
+        lib.hho_bidir.argtypes = [I, I, L, L, L, D, D, D, D, D, D, I]
+        lib.hho_decode_step.argtypes = [I, I, L, L, D, D, D, D, D, D, D, D, I]
+        lib.hho_quadratic.argtypes = [I, I, L, L, L, I, D, D, D, D, D, L, D, D, I]
+        lib.hho_featuremap.argtypes = [I, I, L, L, L, D, D, D, D, I]
+        for f in (lib.hho_causal, lib.hho_bidir, lib.hho_decode_step, lib.hho_quadratic,
+                  lib.hho_featuremap):
+            f.restype = None
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def feature_dim(map_: int, d: int) -> int:
+    return int(_load().hho_feature_dim(map_, d))
+
+
+def _params(map_, W, b, H, d):
+    if map_ == MAP_HEDGEHOG:
+        W = _f64(W).reshape(H, d, d)
+        b = None if b is None or np.size(b) == 0 else _f64(b).reshape(H, d)
+    else:
+        W, b = None, None
+    return W, b
+
+
+def featuremap(map_: int, x, W=None, b=None, nthreads: Optional[int] = None) -> np.ndarray:
+    """x [B,H,N,d] -> phi [B,H,N,d'] in float64."""
+    x = _f64(x)
+    B, H, N, d = x.shape
+    W, b = _params(map_, W, b, H, d)
+    dp = feature_dim(map_, d)
+    out = np.empty((B, H, N, dp), np.float64)
+    _load().hho_featuremap(map_, d, B, H, N, _ptr(x), _ptr(W), _ptr(b), _ptr(out),
+                           nthreads or default_threads())
+    return out
+
+
+def causal(map_: int, q, k, v, W=None, b=None, S0=None, z0=None, want_state: bool = False,
+           nthreads: Optional[int] = None):
+    """Causal Eq. 2 by running sums.  q,k,v [B,H,N,d] -> y [B,H,N,d] (float64).
+
+    With want_state, also returns the final (S [B,H,d',d], z [B,H,d'])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    W, b = _params(map_, W, b, H, d)
+    dp = feature_dim(map_, d)
+    S0 = None if S0 is None else _f64(S0).reshape(B, H, dp, d)
+    z0 = None if z0 is None else _f64(z0).reshape(B, H, dp)
+    y = np.empty_like(q)
+    S = np.empty((B, H, dp, d), np.float64) if want_state else None
+    z = np.empty((B, H, dp), np.float64) if want_state else None
+    _load().hho_causal(map_, d, B, H, N, _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(b), _ptr(S0),
+                       _ptr(z0), _ptr(y), _ptr(S), _ptr(z), nthreads or default_threads())
+    return (y, S, z) if want_state else y
+
+
+def bidir(map_: int, q, k, v, W=None, b=None, nthreads: Optional[int] = None) -> np.ndarray:
+    """Bidirectional Eq. 2 (all keys).  q,k,v [B,H,N,d] -> y [B,H,N,d] (float64)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    W, b = _params(map_, W, b, H, d)
+    y = np.empty_like(q)
+    _load().hho_bidir(map_, d, B, H, N, _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(b), _ptr(y),
+                      nthreads or default_threads())
+    return y
+
+
+def decode_step(map_: int, q, k, v, W, b, S, z, nthreads: Optional[int] = None):
+    """One step from (S, z).  q,k,v [B,H,1,d] or [B,H,d]; returns (y [B,H,d], S', z') in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H = q.shape[:2]
+    d = q.shape[-1]
+    W, b = _params(map_, W, b, H, d)
+    dp = feature_dim(map_, d)
+    S = _f64(S).reshape(B, H, dp, d).copy()
+    z = _f64(z).reshape(B, H, dp).copy()
+    y = np.empty((B, H, d), np.float64)
+    _load().hho_decode_step(map_, d, B, H, _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(b), _ptr(S),
+                            _ptr(z), _ptr(y), nthreads or default_threads())
+    return y, S, z
+
+
+def quadratic(map_: int, q, k, v, W=None, b=None, causal: bool = True, rows=None,
+              nthreads: Optional[int] = None) -> np.ndarray:
+    """Explicit quadratic form.  Returns y [B,H,N,d], or [B,H,len(rows),d] for selected rows."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    W, b = _params(map_, W, b, H, d)
+    if rows is not None:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        assert rows.ndim == 1 and (rows.size == 0 or (rows.min() >= 0 and rows.max() < N))
+        nr = rows.size
+    else:
+        nr = N
+    y = np.empty((B, H, nr, d), np.float64)
+    _load().hho_quadratic(map_, d, B, H, N, int(bool(causal)), _ptr(q), _ptr(k), _ptr(v), _ptr(W),
+                          _ptr(b), nr if rows is not None else 0,
+                          _ptr(rows) if rows is not None else None, _ptr(y),
+                          nthreads or default_threads())
+    return y
