@@ -1,0 +1,131 @@
+/*
+ * hh.h -- C ABI of libhh: Hedgehog-style linear attention on AMD MI355X (gfx950).
+ *
+ * The method ("The Hedgehog & the Porcupine: Expressive Linear Attentions with
+ * Softmax Mimicry", arXiv 2402.04347) replaces softmax attention by a kernel
+ * phi(q)^T phi(k) with a learned feature map phi and evaluates Eq. 2
+ *     y_i = phi(q_i)^T S_i / phi(q_i)^T z_i,
+ *     S_i = sum_{j<=i} phi(k_j) v_j^T,   z_i = sum_{j<=i} phi(k_j)
+ * with running sums (paper-graph-ui walkthrough, section 2 and section 3.4
+ * "Complexity Analysis").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout   q, k, v, y: [B][H][N][d] row-major.  W: [H][d][d], row l is the
+ *           direction w_l (u = W x + b, "the l-th row of W", section 3.4,
+ *           Choice 1).  b: [H][d].  phi: [B][H][N][d'].  State S: [B][H][d'][d]
+ *           fp32, z: [B][H][d'] fp32.  d' = 2d (Hedgehog) or 1 + d + d*d (Taylor).
+ *  Dtype    `dtype` selects the element type of q, k, v, W, b, y and phi
+ *           (HH_F32 or HH_BF16).  The state S, z is always fp32.  Products are
+ *           accumulated in fp32 on the GPU.
+ *  Memory   Every tensor pointer is a device pointer owned by the caller and
+ *           16-byte aligned.  The library allocates no device memory and keeps
+ *           no state between calls; scratch space comes from the caller's
+ *           `workspace`.
+ *  Streams  `stream` is a hipStream_t passed as void* (NULL = the default
+ *           stream).  Every call is asynchronous on that stream; the library
+ *           never synchronizes.  Faults inside kernels surface at the caller's
+ *           next synchronization.
+ *  Errors   Arguments are checked on the host before anything is enqueued; on a
+ *           failed check the call returns HH_EINVAL / HH_EUNSUPPORTED /
+ *           HH_EWORKSPACE and launches nothing.  A failed launch returns HH_EHIP.
+ *           hh_last_error() gives a thread-local message for the last failure.
+ *  Threads  Calls are thread-safe (no global mutable state).
+ *  Sizes    B, H >= 1; N >= 0 (N == 0 is a no-op apart from the state outputs);
+ *           N * d < 2^31 and B * H < 2^24.
+ *  Supported head dims: Hedgehog d in {16, 32, 64, 128}; Taylor d == 16.
+ */
+#ifndef HH_H
+#define HH_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HH_OK = 0,           /* success, work enqueued                                  */
+    HH_EINVAL = 1,       /* bad argument: null/misaligned pointer, bad size, aliasing */
+    HH_EUNSUPPORTED = 2, /* valid request outside what the library implements       */
+    HH_EWORKSPACE = 3,   /* workspace missing or smaller than the size query says   */
+    HH_EHIP = 4          /* a HIP launch or runtime call failed                     */
+} hh_status_t;
+
+typedef enum { HH_F32 = 0, HH_BF16 = 1 } hh_dtype_t;
+
+typedef enum {
+    /* phi(x) = [exp(W x + b), exp(-(W x + b))], d' = 2d: the Hedgehog map of
+     * section 3.4, "The Hedgehog MLP Feature Map", Choice 1 (element-wise exp
+     * after one linear layer, shared by q and k of a head) with the negation
+     * mapping of Choice 3 (paperlayer.ai summary, A.1). */
+    HH_MAP_HEDGEHOG = 0,
+    /* phi(x) = [1, x_0..x_{d-1}, x_a x_c / sqrt(2) for a, c in [d] (row-major)],
+     * d' = 1 + d + d^2, so phi(q)^T phi(k) = 1 + q.k + (q.k)^2 / 2: the degree-2
+     * Taylor map of section 3.4, "The Taylor Exponential as a Bridge Result". */
+    HH_MAP_TAYLOR2 = 1
+} hh_map_t;
+
+/* ABI revision of this header; bumped on any incompatible change. */
+int hh_abi_version(void);
+
+/* Feature dimension d' for (map, d): 2d or 1 + d + d^2; -1 if (map, d) is invalid. */
+int hh_feature_dim(int map, int d);
+
+/* Feature map alone (section 3.4, "The Hedgehog MLP Feature Map" / "The Taylor
+ * Exponential as a Bridge Result").
+ *   x   [B][H][N][d]  queries or keys (dtype)
+ *   W   [H][d][d], b [H][d]  Hedgehog parameters (dtype); b may be NULL (zero
+ *       bias); both ignored and may be NULL for the Taylor map
+ *   phi [B][H][N][d'] output (dtype), features in the order documented above.
+ * phi must not overlap x. */
+hh_status_t hh_featuremap(int map, int dtype, int B, int H, int N, int d,
+                          const void *x, const void *W, const void *b,
+                          void *phi, void *stream);
+
+/* Bytes of workspace hh_linattn_fwd needs for this problem (0 = none).  Returns
+ * 0 as well for invalid arguments; the forward call reports those. */
+size_t hh_linattn_fwd_workspace(int map, int dtype, int causal, int B, int H, int N, int d);
+
+/* Linear-attention forward, feature map included (Eq. 2).
+ *   causal = 1: y_i uses keys j <= i (inclusive), as in Eq. 2 (section 2).
+ *   causal = 0: y_i uses every key (bidirectional encoders, paperlayer.ai
+ *               summary, section 1).
+ *   q, k, v [B][H][N][d], W [H][d][d], b [H][d] or NULL   (dtype)
+ *   S0 [B][H][d'][d], z0 [B][H][d'] (fp32): optional initial state, both NULL
+ *       or both set; causal only.  The sums start from them, which resumes a
+ *       sequence that an earlier call ended.
+ *   y  [B][H][N][d] output (dtype); must not overlap q, k, v.
+ *   S_out, z_out (fp32): optional final inclusive state (both NULL or both
+ *       set); causal only.  May alias S0, z0.
+ *   workspace: device scratch of at least hh_linattn_fwd_workspace() bytes
+ *       (may be NULL when that is 0). */
+hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, int d,
+                           const void *q, const void *k, const void *v,
+                           const void *W, const void *b,
+                           const float *S0, const float *z0,
+                           void *y, float *S_out, float *z_out,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* One recurrent decode step (running-sum update of section 3.4, "Complexity
+ * Analysis"): for each (b, h), with f = phi(k), g = phi(q):
+ *     S += f v^T;  z += f;  y = g^T S / g^T z     (update, then read: j <= i)
+ *   q, k, v, y [B][H][d] (dtype, one token per sequence)
+ *   S [B][H][d'][d], z [B][H][d'] fp32, read and written in place.
+ *   W, b as in hh_linattn_fwd.  y must not overlap q, k, v, S, z. */
+hh_status_t hh_linattn_decode_step(int map, int dtype, int B, int H, int d,
+                                   const void *q, const void *k, const void *v,
+                                   const void *W, const void *b,
+                                   float *S, float *z, void *y, void *stream);
+
+/* Static description of a status code. */
+const char *hh_status_str(int status);
+
+/* Thread-local message describing the last failure on this thread ("" if none). */
+const char *hh_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HH_H */

@@ -175,3 +175,22 @@ def quadratic(map_: int, q, k, v, W=None, b=None, causal: bool = True, rows=None
                           _ptr(rows) if rows is not None else None, _ptr(y),
                           nthreads or default_threads())
     return y
+
+
+def prefix_state(map_: int, k, v, W=None, b=None, nthreads: Optional[int] = None):
+    """Running sums after a whole prefix: S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j) (float64).
+
+    The definition of S_N, z_N in section 3.4, "Complexity Analysis", evaluated with the
+    oracle's feature map and a library matrix product per (b, h); one batch row at a time
+    to bound memory.  k, v: [B,H,N,d] -> S [B,H,d',d], z [B,H,d']."""
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, H, N, d = k.shape
+    dp = feature_dim(map_, d)
+    S = np.empty((B, H, dp, d), np.float64)
+    z = np.empty((B, H, dp), np.float64)
+    for bi in range(B):
+        phi = featuremap(map_, k[bi:bi + 1], W, b, nthreads=nthreads)[0]     # [H,N,dp]
+        S[bi] = np.matmul(phi.transpose(0, 2, 1), _f64(v[bi]))
+        z[bi] = phi.sum(axis=1)
+    return S, z

@@ -1,0 +1,181 @@
+"""Hedgehog-style linear attention for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of libhh (include/hh.h), with the same
+entry-point names.  It only marshals arguments: torch supplies device memory
+and the current stream, every step of the computation runs in the HIP
+kernels of libhh.  There is no fallback: if libhh.so is missing, every call
+raises.
+
+    y = hh_linattn_fwd(q, k, v, W, b, causal=True)            # [B,H,N,d]
+    y, S, z = hh_linattn_fwd(q, k, v, W, b, want_state=True)   # + final fp32 state
+    y = hh_linattn_decode_step(q1, k1, v1, W, b, S, z)         # S, z updated in place
+    phi = hh_featuremap(x, W, b)                               # [B,H,N,d']
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+from . import _lib
+from ._lib import (HH_BF16, HH_EHIP, HH_EINVAL, HH_EUNSUPPORTED, HH_EWORKSPACE, HH_F32, HH_MAP_HEDGEHOG,
+                   HH_MAP_TAYLOR2, HH_OK, LibraryMissing)
+
+__all__ = ["hh_feature_dim", "hh_featuremap", "hh_linattn_fwd_workspace", "hh_linattn_fwd",
+           "hh_linattn_decode_step", "hh_status_str", "hh_last_error", "hh_abi_version", "HHError",
+           "LibraryMissing", "HH_F32", "HH_BF16", "HH_MAP_HEDGEHOG", "HH_MAP_TAYLOR2", "HH_OK", "HH_EINVAL",
+           "HH_EUNSUPPORTED", "HH_EWORKSPACE", "HH_EHIP"]
+
+
+class HHError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != HH_OK:
+        lib = _lib.load()
+        raise HHError(status, f"{lib.hh_status_str(status).decode()}: {lib.hh_last_error().decode()}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return HH_BF16
+    if t.dtype == torch.float32:
+        return HH_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _dev(t, name: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def hh_abi_version() -> int:
+    return _lib.load().hh_abi_version()
+
+
+def hh_feature_dim(map: int, d: int) -> int:
+    return _lib.load().hh_feature_dim(map, d)
+
+
+def hh_status_str(status: int) -> str:
+    return _lib.load().hh_status_str(status).decode()
+
+
+def hh_last_error() -> str:
+    return _lib.load().hh_last_error().decode()
+
+
+def hh_featuremap(x, W=None, b=None, *, map: int = HH_MAP_HEDGEHOG, out=None, stream=None):
+    """phi(x) for x [B,H,N,d]; returns [B,H,N,d'] in x's dtype."""
+    lib = _lib.load()
+    torch = _torch()
+    _dev(x, "x")
+    B, H, N, d = x.shape
+    dp = lib.hh_feature_dim(map, d)
+    if dp < 0:
+        raise ValueError(f"invalid map/head dim ({map}, {d})")
+    if out is None:
+        out = torch.empty((B, H, N, dp), dtype=x.dtype, device=x.device)
+    _dev(out, "out", x.dtype)
+    if map == HH_MAP_HEDGEHOG:
+        _dev(W, "W", x.dtype)
+        _dev(b, "b", x.dtype)
+    _check(lib.hh_featuremap(map, _dtype_code(x), B, H, N, d, _ptr(x), _ptr(W), _ptr(b), _ptr(out),
+                             _stream(stream)))
+    return out
+
+
+def hh_linattn_fwd_workspace(map: int, dtype: int, causal: bool, B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.load().hh_linattn_fwd_workspace(map, dtype, int(bool(causal)), B, H, N, d))
+
+
+def hh_linattn_fwd(q, k, v, W=None, b=None, *, causal: bool = True, map: int = HH_MAP_HEDGEHOG, S0=None, z0=None,
+                   out=None, want_state: bool = False, S_out=None, z_out=None, workspace=None, stream=None):
+    """Eq. 2 forward with the feature map included.  q, k, v: [B,H,N,d].
+
+    Returns y, or (y, S_out, z_out) when want_state (fp32 final state)."""
+    lib = _lib.load()
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, nm, q.dtype)
+    B, H, N, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape [B,H,N,d]")
+    dt = _dtype_code(q)
+    dp = lib.hh_feature_dim(map, d)
+    if map == HH_MAP_HEDGEHOG:
+        _dev(W, "W", q.dtype)
+        _dev(b, "b", q.dtype)
+    else:
+        W = b = None
+    _dev(S0, "S0", torch.float32)
+    _dev(z0, "z0", torch.float32)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if want_state and S_out is None:
+        S_out = torch.empty((B, H, dp, d), dtype=torch.float32, device=q.device)
+        z_out = torch.empty((B, H, dp), dtype=torch.float32, device=q.device)
+    _dev(S_out, "S_out", torch.float32)
+    _dev(z_out, "z_out", torch.float32)
+    need = lib.hh_linattn_fwd_workspace(map, dt, int(bool(causal)), B, H, N, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.hh_linattn_fwd(map, dt, int(bool(causal)), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(b),
+                              _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_out), _ptr(z_out), _ptr(workspace), ws_bytes,
+                              _stream(stream)))
+    if S_out is not None:
+        return out, S_out, z_out
+    return out
+
+
+def hh_linattn_decode_step(q, k, v, W, b, S, z, *, map: int = HH_MAP_HEDGEHOG, out=None, stream=None):
+    """One recurrent step.  q, k, v: [B,H,d] or [B,H,1,d]; S [B,H,d',d], z [B,H,d'] fp32 updated in place."""
+    lib = _lib.load()
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, nm, q.dtype)
+    B, H = q.shape[:2]
+    d = q.shape[-1]
+    if q.numel() != B * H * d:
+        raise ValueError("decode expects one token per (b, h)")
+    dt = _dtype_code(q)
+    if map == HH_MAP_HEDGEHOG:
+        _dev(W, "W", q.dtype)
+        _dev(b, "b", q.dtype)
+    else:
+        W = b = None
+    _dev(S, "S", torch.float32)
+    _dev(z, "z", torch.float32)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=q.dtype, device=q.device)
+    _dev(out, "out", q.dtype)
+    _check(lib.hh_linattn_decode_step(map, dt, B, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(b), _ptr(S),
+                                      _ptr(z), _ptr(out), _stream(stream)))
+    return out

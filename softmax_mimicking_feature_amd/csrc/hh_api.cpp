@@ -1,0 +1,368 @@
+// hh_api.cpp -- the C ABI of libhh (include/hh.h): argument checks on the host, planning of
+// the segment split and workspace, and kernel dispatch on the caller's stream.
+//
+// Every check runs before the first HIP call, so invalid arguments return an error with
+// nothing enqueued (and without touching the GPU at all).
+#include "hh.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "hh_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hh_status_t fail(hh_status_t st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+hh_status_t fail(hh_status_t st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+hh_status_t ok() {
+    g_last_error.clear();
+    return HH_OK;
+}
+
+// The runtime's last-error slot may still hold a failure from an unrelated earlier call in
+// the process (another library probing devices); drop it so that the check after our own
+// launches reports only our launches.
+void clear_stale_hip_error() { (void)hipGetLastError(); }
+
+hh_status_t hip_fail(hipError_t e, const char *what) {
+    return fail(HH_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int feature_dim(int map, int d) {
+    if (d < 1 || d > 1024) return -1;
+    if (map == HH_MAP_HEDGEHOG) return 2 * d;
+    if (map == HH_MAP_TAYLOR2) return 1 + d + d * d;
+    return -1;
+}
+
+size_t elem_bytes(int dtype) { return dtype == HH_BF16 ? 2 : 4; }
+
+// Checks shared by the forward and the feature map.
+hh_status_t check_common(int map, int dtype, long B, long H, long N, int d) {
+    if (map != HH_MAP_HEDGEHOG && map != HH_MAP_TAYLOR2) return fail(HH_EINVAL, "unknown map %d", map);
+    if (dtype != HH_F32 && dtype != HH_BF16) return fail(HH_EINVAL, "unknown dtype %d", dtype);
+    if (B < 1 || H < 1) return fail(HH_EINVAL, "B and H must be >= 1 (got B=%ld H=%ld)", B, H);
+    if (B * H >= (1L << 24)) return fail(HH_EINVAL, "B*H = %ld exceeds 2^24", B * H);
+    if (N < 0) return fail(HH_EINVAL, "N must be >= 0 (got %ld)", N);
+    if (map == HH_MAP_HEDGEHOG) {
+        if (d != 16 && d != 32 && d != 64 && d != 128)
+            return fail(HH_EUNSUPPORTED, "Hedgehog head dim %d not supported (16, 32, 64, 128)", d);
+    } else if (d != 16) {
+        return fail(HH_EUNSUPPORTED, "Taylor map head dim %d not supported (16)", d);
+    }
+    if (N * (long)d >= (1L << 31)) return fail(HH_EINVAL, "N*d = %ld exceeds 2^31", N * (long)d);
+    return HH_OK;
+}
+
+hh_status_t check_ptr(const void *p, const char *name, bool required) {
+    if (!p) return required ? fail(HH_EINVAL, "%s is NULL", name) : HH_OK;
+    if (!aligned16(p)) return fail(HH_EINVAL, "%s is not 16-byte aligned", name);
+    return HH_OK;
+}
+
+// ---- planning of the chunked bf16 path -------------------------------------------------
+struct Plan {
+    bool chunked = false;  // bf16 chunked kernels (else the fp32 token path)
+    bool narrow = false;   // Taylor kernels
+    int dpi = 0;           // feature rows of the internal state
+    int nseg = 1, seg_len = 0;
+    bool need_ws = false;  // segment slots in the workspace
+    size_t ws_bytes = 0;
+};
+
+Plan make_plan(int map, int dtype, int causal, long BH, long N, int d, bool has_S0) {
+    Plan pl;
+    if (dtype != HH_BF16 || N == 0) return pl;
+    pl.chunked = true;
+    pl.narrow = map == HH_MAP_TAYLOR2;
+    pl.dpi = pl.narrow ? hh::kTaylorRowsInternal : 2 * d;
+    const long C = 64;
+    const long nch = (N + C - 1) / C;
+    const long target = pl.narrow ? 1024 : 256L * hh::wide_wgs_per_cu(d);
+    long nseg = target / BH;
+    if (nseg < 1) nseg = 1;
+    if (nseg > nch) nseg = nch;
+    const long seg_chunks = (nch + nseg - 1) / nseg;
+    nseg = (nch + seg_chunks - 1) / seg_chunks;
+    pl.nseg = (int)nseg;
+    pl.seg_len = (int)(seg_chunks * C);
+    if (!causal) pl.need_ws = true;
+    else if (pl.nseg > 1) pl.need_ws = true;
+    else if (pl.narrow && has_S0) pl.need_ws = true;  // S0 must be reordered into the internal rows
+    if (pl.need_ws) pl.ws_bytes = (size_t)BH * pl.nseg * ((size_t)pl.dpi * d + pl.dpi) * sizeof(float);
+    return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hh_abi_version(void) { return 1; }
+
+int hh_feature_dim(int map, int d) { return feature_dim(map, d); }
+
+const char *hh_status_str(int s) {
+    switch (s) {
+    case HH_OK: return "HH_OK: success";
+    case HH_EINVAL: return "HH_EINVAL: invalid argument";
+    case HH_EUNSUPPORTED: return "HH_EUNSUPPORTED: unsupported configuration";
+    case HH_EWORKSPACE: return "HH_EWORKSPACE: workspace missing or too small";
+    case HH_EHIP: return "HH_EHIP: HIP runtime error";
+    default: return "unknown hh status";
+    }
+}
+
+const char *hh_last_error(void) { return g_last_error.c_str(); }
+
+hh_status_t hh_featuremap(int map, int dtype, int B, int H, int N, int d, const void *x, const void *W,
+                          const void *b, void *phi, void *stream) {
+    hh_status_t st = check_common(map, dtype, B, H, N, d);
+    if (st != HH_OK) return st;
+    const bool hog = map == HH_MAP_HEDGEHOG;
+    const int dp = feature_dim(map, d);
+    const size_t eb = elem_bytes(dtype);
+    if ((st = check_ptr(x, "x", N > 0)) != HH_OK) return st;
+    if ((st = check_ptr(phi, "phi", N > 0)) != HH_OK) return st;
+    if (hog) {
+        if ((st = check_ptr(W, "W", true)) != HH_OK) return st;
+        if ((st = check_ptr(b, "b", false)) != HH_OK) return st;
+    }
+    const size_t nx = (size_t)B * H * N * d * eb, nphi = (size_t)B * H * N * dp * eb;
+    if (overlap(x, nx, phi, nphi)) return fail(HH_EINVAL, "phi overlaps x");
+    if (N == 0) return ok();
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    clear_stale_hip_error();
+    hipError_t e;
+    if (hog && dtype == HH_BF16)
+        e = hh::launch_featuremap_hedgehog_bf16(d, (const hh::bf16_t *)x, (const hh::bf16_t *)W,
+                                                (const hh::bf16_t *)b, (hh::bf16_t *)phi, B * H, H, N, s);
+    else
+        e = hh::launch_featuremap_generic(map, dtype, d, dp, x, hog ? W : nullptr, hog ? b : nullptr, phi,
+                                          (long)B * H, H, N, s);
+    if (e != hipSuccess) return hip_fail(e, "feature map launch");
+    return ok();
+}
+
+size_t hh_linattn_fwd_workspace(int map, int dtype, int causal, int B, int H, int N, int d) {
+    if (check_common(map, dtype, B, H, N, d) != HH_OK || (causal != 0 && causal != 1)) return 0;
+    // the larger of the plans with and without an initial state
+    const Plan a = make_plan(map, dtype, causal, (long)B * H, N, d, false);
+    const Plan b = make_plan(map, dtype, causal, (long)B * H, N, d, true);
+    return a.ws_bytes > b.ws_bytes ? a.ws_bytes : b.ws_bytes;
+}
+
+hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, int d, const void *q,
+                           const void *k, const void *v, const void *W, const void *b, const float *S0,
+                           const float *z0, void *y, float *S_out, float *z_out, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    hh_status_t st = check_common(map, dtype, B, H, N, d);
+    if (st != HH_OK) return st;
+    if (causal != 0 && causal != 1) return fail(HH_EINVAL, "causal must be 0 or 1 (got %d)", causal);
+    const bool hog = map == HH_MAP_HEDGEHOG;
+    const int dp = feature_dim(map, d);
+    const long BH = (long)B * H;
+    const size_t eb = elem_bytes(dtype);
+    const bool need_io = N > 0;
+    if ((st = check_ptr(q, "q", need_io)) != HH_OK) return st;
+    if ((st = check_ptr(k, "k", need_io)) != HH_OK) return st;
+    if ((st = check_ptr(v, "v", need_io)) != HH_OK) return st;
+    if ((st = check_ptr(y, "y", need_io)) != HH_OK) return st;
+    if (hog) {
+        if ((st = check_ptr(W, "W", need_io)) != HH_OK) return st;
+        if ((st = check_ptr(b, "b", false)) != HH_OK) return st;
+    }
+    if ((S0 == nullptr) != (z0 == nullptr)) return fail(HH_EINVAL, "S0 and z0 must be both set or both NULL");
+    if ((S_out == nullptr) != (z_out == nullptr))
+        return fail(HH_EINVAL, "S_out and z_out must be both set or both NULL");
+    if (!causal && (S0 || S_out)) return fail(HH_EINVAL, "initial/final state is only defined for causal attention");
+    if ((st = check_ptr(S0, "S0", false)) != HH_OK) return st;
+    if ((st = check_ptr(z0, "z0", false)) != HH_OK) return st;
+    if ((st = check_ptr(S_out, "S_out", false)) != HH_OK) return st;
+    if ((st = check_ptr(z_out, "z_out", false)) != HH_OK) return st;
+    const size_t nio = (size_t)BH * N * d * eb;
+    if (overlap(y, nio, q, nio) || overlap(y, nio, k, nio) || overlap(y, nio, v, nio))
+        return fail(HH_EINVAL, "y overlaps q, k or v");
+    const size_t nS = (size_t)BH * dp * d * sizeof(float), nz = (size_t)BH * dp * sizeof(float);
+    if (overlap(y, nio, S_out, nS) || overlap(y, nio, z_out, nz)) return fail(HH_EINVAL, "y overlaps S_out or z_out");
+
+    const Plan pl = make_plan(map, dtype, causal, BH, N, d, S0 != nullptr);
+    if (pl.need_ws) {
+        if (!workspace) return fail(HH_EWORKSPACE, "workspace of %zu bytes required, got NULL", pl.ws_bytes);
+        if (workspace_bytes < pl.ws_bytes)
+            return fail(HH_EWORKSPACE, "workspace of %zu bytes required, got %zu", pl.ws_bytes, workspace_bytes);
+        if (!aligned16(workspace)) return fail(HH_EINVAL, "workspace is not 16-byte aligned");
+        if (overlap(workspace, pl.ws_bytes, y, nio) || overlap(workspace, pl.ws_bytes, q, nio) ||
+            overlap(workspace, pl.ws_bytes, k, nio) || overlap(workspace, pl.ws_bytes, v, nio))
+            return fail(HH_EINVAL, "workspace overlaps an input or output");
+    }
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    clear_stale_hip_error();
+    hipError_t e = hipSuccess;
+    if (N == 0) {
+        if (S_out) e = hh::launch_state_copy(S0, z0, S_out, z_out, (long)BH * dp * d, (long)BH * dp, s);
+        if (e != hipSuccess) return hip_fail(e, "state copy launch");
+        return ok();
+    }
+
+    if (!pl.chunked) {  // fp32 token-by-token path
+        hh::SeqParams sp;
+        sp.q = (const float *)q; sp.k = (const float *)k; sp.v = (const float *)v;
+        sp.W = hog ? (const float *)W : nullptr;
+        sp.b = hog ? (const float *)b : nullptr;
+        sp.y = (float *)y;
+        sp.S0 = S0; sp.z0 = z0; sp.S_out = S_out; sp.z_out = z_out;
+        sp.N = N; sp.H = H; sp.d = d; sp.dp = dp; sp.map = map; sp.causal = causal;
+        e = hh::launch_seq_f32(sp, (int)BH, s);
+        if (e != hipSuccess) return hip_fail(e, "fp32 path launch");
+        return ok();
+    }
+
+    float *wsS = nullptr, *wsZ = nullptr;
+    if (pl.need_ws) {
+        wsS = reinterpret_cast<float *>(workspace);
+        wsZ = wsS + (size_t)BH * pl.nseg * pl.dpi * d;
+    }
+    const long slot_stride = pl.nseg;
+
+    // Which state each segment starts from.
+    const float *S_in = nullptr, *z_in = nullptr;
+    long in_bh = 0, in_seg = 0;
+    hh::PrefixParams pp;
+    memset(&pp, 0, sizeof pp);
+    pp.S_ws = wsS; pp.z_ws = wsZ; pp.S0 = S0; pp.z0 = z0;
+    pp.BH = (int)BH; pp.nseg = pl.nseg; pp.dpi = pl.dpi; pp.dpc = dp; pp.d = d; pp.map = map;
+    bool run_state = false, run_prefix = false;
+    int state_segments = 0;
+    if (causal) {
+        if (pl.nseg > 1) {
+            run_state = true;
+            state_segments = pl.nseg - 1;
+            run_prefix = true;
+            pp.mode = 0;
+            S_in = wsS; z_in = wsZ; in_bh = slot_stride; in_seg = 1;
+        } else if (S0) {
+            if (pl.narrow) {
+                run_prefix = true;
+                pp.mode = 0;
+                S_in = wsS; z_in = wsZ; in_bh = 1; in_seg = 0;
+            } else {
+                S_in = S0; z_in = z0; in_bh = 1; in_seg = 0;
+            }
+        }
+    } else {
+        run_state = true;
+        state_segments = pl.nseg;
+        run_prefix = pl.nseg > 1;
+        pp.mode = 1;
+        pp.S0 = nullptr; pp.z0 = nullptr;
+        S_in = wsS; z_in = wsZ; in_bh = slot_stride; in_seg = 0;
+    }
+    const int out_mode = causal ? 1 : 2;
+
+    if (!pl.narrow) {
+        hh::WideParams wp;
+        memset(&wp, 0, sizeof wp);
+        wp.q = (const hh::bf16_t *)q; wp.k = (const hh::bf16_t *)k; wp.v = (const hh::bf16_t *)v;
+        wp.W = (const hh::bf16_t *)W; wp.b = (const hh::bf16_t *)b; wp.y = (hh::bf16_t *)y;
+        wp.S_ws = wsS; wp.z_ws = wsZ; wp.ws_bh_stride = slot_stride;
+        wp.N = N; wp.H = H; wp.seg_len = pl.seg_len;
+        if (run_state) {
+            wp.nseg_grid = state_segments;
+            e = hh::launch_wide(d, 0, wp, (int)(BH * state_segments), s);
+            if (e != hipSuccess) return hip_fail(e, "segment-state launch");
+        }
+        if (run_prefix) {
+            e = hh::launch_prefix(pp, s);
+            if (e != hipSuccess) return hip_fail(e, "prefix launch");
+        }
+        wp.S_in = S_in; wp.z_in = z_in; wp.in_bh_stride = in_bh; wp.in_seg_stride = in_seg;
+        wp.S_out = S_out; wp.z_out = z_out;
+        wp.nseg_grid = pl.nseg;
+        e = hh::launch_wide(d, out_mode, wp, (int)(BH * pl.nseg), s);
+        if (e != hipSuccess) return hip_fail(e, "chunked forward launch");
+    } else {
+        hh::NarrowParams np;
+        memset(&np, 0, sizeof np);
+        np.q = (const hh::bf16_t *)q; np.k = (const hh::bf16_t *)k; np.v = (const hh::bf16_t *)v;
+        np.y = (hh::bf16_t *)y;
+        np.S_ws = wsS; np.z_ws = wsZ; np.ws_bh_stride = slot_stride;
+        np.N = N; np.seg_len = pl.seg_len;
+        if (run_state) {
+            np.nseg_grid = state_segments;
+            e = hh::launch_narrow(0, np, (int)(BH * state_segments), s);
+            if (e != hipSuccess) return hip_fail(e, "segment-state launch");
+        }
+        if (run_prefix) {
+            e = hh::launch_prefix(pp, s);
+            if (e != hipSuccess) return hip_fail(e, "prefix launch");
+        }
+        np.S_in = S_in; np.z_in = z_in; np.in_bh_stride = in_bh; np.in_seg_stride = in_seg;
+        np.S_out = S_out; np.z_out = z_out;
+        np.nseg_grid = pl.nseg;
+        e = hh::launch_narrow(out_mode, np, (int)(BH * pl.nseg), s);
+        if (e != hipSuccess) return hip_fail(e, "chunked forward launch");
+    }
+    return ok();
+}
+
+hh_status_t hh_linattn_decode_step(int map, int dtype, int B, int H, int d, const void *q, const void *k,
+                                   const void *v, const void *W, const void *b, float *S, float *z, void *y,
+                                   void *stream) {
+    hh_status_t st = check_common(map, dtype, B, H, 1, d);
+    if (st != HH_OK) return st;
+    const bool hog = map == HH_MAP_HEDGEHOG;
+    const int dp = feature_dim(map, d);
+    const long BH = (long)B * H;
+    const size_t eb = elem_bytes(dtype);
+    if ((st = check_ptr(q, "q", true)) != HH_OK) return st;
+    if ((st = check_ptr(k, "k", true)) != HH_OK) return st;
+    if ((st = check_ptr(v, "v", true)) != HH_OK) return st;
+    if ((st = check_ptr(y, "y", true)) != HH_OK) return st;
+    if ((st = check_ptr(S, "S", true)) != HH_OK) return st;
+    if ((st = check_ptr(z, "z", true)) != HH_OK) return st;
+    if (hog) {
+        if ((st = check_ptr(W, "W", true)) != HH_OK) return st;
+        if ((st = check_ptr(b, "b", false)) != HH_OK) return st;
+    }
+    const size_t nio = (size_t)BH * d * eb;
+    const size_t nS = (size_t)BH * dp * d * sizeof(float), nz = (size_t)BH * dp * sizeof(float);
+    if (overlap(y, nio, q, nio) || overlap(y, nio, k, nio) || overlap(y, nio, v, nio) || overlap(y, nio, S, nS) ||
+        overlap(y, nio, z, nz))
+        return fail(HH_EINVAL, "y overlaps q, k, v, S or z");
+    if (overlap(S, nS, z, nz)) return fail(HH_EINVAL, "S overlaps z");
+    hh::DecodeParams dpar;
+    dpar.q = q; dpar.k = k; dpar.v = v; dpar.W = hog ? W : nullptr; dpar.b = hog ? b : nullptr;
+    dpar.y = y; dpar.S = S; dpar.z = z;
+    dpar.H = H; dpar.d = d; dpar.dp = dp; dpar.map = map; dpar.dtype = dtype;
+    clear_stale_hip_error();
+    hipError_t e = hh::launch_decode(dpar, (int)BH, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+}
+
+}  // extern "C"

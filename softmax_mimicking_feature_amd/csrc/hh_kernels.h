@@ -1,0 +1,80 @@
+// hh_kernels.h -- host-side launchers of the libhh kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hh {
+
+typedef uint16_t bf16_t;
+
+// Chunked Hedgehog kernels (bf16).  Modes: 0 segment state, 1 causal, 2 read-out.
+struct WideParams {
+    const bf16_t *q, *k, *v, *W, *b;  // b may be null
+    bf16_t *y;
+    const float *S_in, *z_in;   // starting state (internal row order), or null = zero
+    long in_bh_stride;          // slots per (b,h) in S_in
+    long in_seg_stride;         // slots per segment in S_in (0: one slot shared by all segments)
+    float *S_ws, *z_ws;         // segment aggregates (mode 0)
+    long ws_bh_stride;          // slots per (b,h) in S_ws
+    float *S_out, *z_out;       // final state (mode 1, last segment), or null
+    int N, H, nseg_grid, seg_len;
+};
+hipError_t launch_wide(int d, int mode, const WideParams &p, int grid, hipStream_t st);
+int wide_wgs_per_cu(int d);
+
+// Hedgehog feature map on the matrix cores (bf16): x [BH][N][d] -> phi [BH][N][2d].
+hipError_t launch_featuremap_hedgehog_bf16(int d, const bf16_t *x, const bf16_t *W, const bf16_t *b,
+                                           bf16_t *phi, int BH, int H, int N, hipStream_t st);
+
+// Degree-2 Taylor chunked kernels (bf16, d = 16).  Modes as above.
+struct NarrowParams {
+    const bf16_t *q, *k, *v;
+    bf16_t *y;
+    const float *S_in, *z_in;
+    long in_bh_stride, in_seg_stride;
+    float *S_ws, *z_ws;
+    long ws_bh_stride;
+    float *S_out, *z_out;  // canonical feature order
+    int N, nseg_grid, seg_len;
+};
+hipError_t launch_narrow(int mode, const NarrowParams &p, int grid, hipStream_t st);
+constexpr int kTaylorRowsInternal = 288;  // 273 features padded to 18 blocks of 16
+
+// Scan of segment aggregates into exclusive prefixes (mode 0) or one total (mode 1).
+struct PrefixParams {
+    float *S_ws, *z_ws;            // [BH][nseg][dpi][d], [BH][nseg][dpi]
+    const float *S0, *z0;          // canonical [BH][dpc][d], [BH][dpc] or null
+    int BH, nseg, dpi, dpc, d, map, mode;
+};
+hipError_t launch_prefix(const PrefixParams &p, hipStream_t st);
+
+// S_out = S0 (or 0), z_out = z0 (or 0): the state result of an empty sequence.
+hipError_t launch_state_copy(const float *S0, const float *z0, float *S_out, float *z_out, long nS, long nz,
+                             hipStream_t st);
+
+// fp32 path: one workgroup per (b,h) walks the sequence token by token.
+struct SeqParams {
+    const float *q, *k, *v, *W, *b;
+    float *y;
+    const float *S0, *z0;
+    float *S_out, *z_out;
+    int N, H, d, dp, map, causal;
+};
+hipError_t launch_seq_f32(const SeqParams &p, int BH, hipStream_t st);
+
+// Decode step: one workgroup per (b,h) streams the fp32 state.
+struct DecodeParams {
+    const void *q, *k, *v, *W, *b;
+    void *y;
+    float *S, *z;
+    int H, d, dp, map, dtype;
+};
+hipError_t launch_decode(const DecodeParams &p, int BH, hipStream_t st);
+
+// Feature map on the vector units (fp32 Hedgehog, Taylor in either dtype).
+hipError_t launch_featuremap_generic(int map, int dtype, int d, int dp, const void *x, const void *W,
+                                     const void *b, void *phi, long BH, int H, int N, hipStream_t st);
+
+}  // namespace hh

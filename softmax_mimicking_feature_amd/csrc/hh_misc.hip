@@ -1,0 +1,315 @@
+// hh_misc.hip -- the smaller libhh kernels: segment-state scan, empty-sequence state,
+// the fp32 token-by-token path, the decode step and the vector-unit feature map.
+//
+// Feature maps (paper-graph-ui walkthrough of "The Hedgehog & the Porcupine"):
+//   Hedgehog (section 3.4, "The Hedgehog MLP Feature Map", Choices 1 and 3):
+//       u_l = b_l + sum_m W[l][m] x_m,   phi = [exp(u_0..u_{d-1}), exp(-u_0..-u_{d-1})]
+//   Taylor (section 3.4, "The Taylor Exponential as a Bridge Result"):
+//       phi = [1, x_0..x_{d-1}, x_a x_c / sqrt(2) for a, c in [d], row-major]
+// Running sums and read-out: Eq. 2 with S_i, z_i (section 2; section 3.4 "Complexity Analysis").
+#include "hh_common.h"
+#include "hh_kernels.h"
+
+namespace hh {
+
+// ----------------------------------------------------------------------------------------
+// Internal row order of the Taylor state in the chunked kernels: rows 0..271 hold the
+// canonical features 1..272 (linear then quadratic), row 272 the constant feature,
+// rows 273..287 are zero padding.  Hedgehog rows are stored in canonical order.
+__device__ __forceinline__ int internal_to_canonical_row(int map, int r) {
+    if (map == 0) return r;
+    if (r < 272) return r + 1;
+    if (r == 272) return 0;
+    return -1;
+}
+
+__global__ void prefix_kernel(PrefixParams p) {
+    const long per = (long)p.dpi * p.d + p.dpi;
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long)p.BH * per) return;
+    const int bh = (int)(idx / per);
+    const long e = idx % per;
+    const bool isS = e < (long)p.dpi * p.d;
+    const int row = isS ? (int)(e / p.d) : (int)(e - (long)p.dpi * p.d);
+    const int col = isS ? (int)(e % p.d) : 0;
+    float *base;
+    long stride;
+    if (isS) {
+        stride = (long)p.dpi * p.d;
+        base = p.S_ws + (size_t)bh * p.nseg * stride + e;
+    } else {
+        stride = p.dpi;
+        base = p.z_ws + (size_t)bh * p.nseg * stride + row;
+    }
+    float run = 0.0f;
+    if (p.S0) {
+        const int c = internal_to_canonical_row(p.map, row);
+        if (c >= 0) run = isS ? p.S0[((size_t)bh * p.dpc + c) * p.d + col] : p.z0[(size_t)bh * p.dpc + c];
+    }
+    if (p.mode == 0) {  // exclusive prefix; the last segment's own aggregate is never needed
+        for (int s = 0; s < p.nseg; s++) {
+            const float dlt = (s < p.nseg - 1) ? base[s * stride] : 0.0f;
+            base[s * stride] = run;
+            run += dlt;
+        }
+    } else {  // total over all segments into slot 0
+        for (int s = 0; s < p.nseg; s++) run += base[s * stride];
+        base[0] = run;
+    }
+}
+
+hipError_t launch_prefix(const PrefixParams &p, hipStream_t st) {
+    const long per = (long)p.dpi * p.d + p.dpi;
+    const long total = (long)p.BH * per;
+    const int nt = 256;
+    hipLaunchKernelGGL(prefix_kernel, dim3((unsigned)((total + nt - 1) / nt)), dim3(nt), 0, st, p);
+    return hipGetLastError();
+}
+
+__global__ void state_copy_kernel(const float *S0, const float *z0, float *S_out, float *z_out, long nS, long nz) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < nS) S_out[i] = S0 ? S0[i] : 0.0f;
+    else if (i < nS + nz) z_out[i - nS] = z0 ? z0[i - nS] : 0.0f;
+}
+
+hipError_t launch_state_copy(const float *S0, const float *z0, float *S_out, float *z_out, long nS, long nz,
+                             hipStream_t st) {
+    const long total = nS + nz;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, S0, z0, S_out,
+                       z_out, nS, nz);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------
+// Feature value f of token x (fp32), x already in shared memory.
+template <typename LoadW>
+__device__ __forceinline__ float feature_value(int map, int d, int f, const float *x, LoadW wrow, float bias_l) {
+    if (map == 0) {
+        const int l = f < d ? f : f - d;
+        float u = bias_l;
+        for (int m = 0; m < d; m++) u = fmaf(wrow(l, m), x[m], u);
+        return expf(f < d ? u : -u);
+    }
+    if (f == 0) return 1.0f;
+    if (f <= d) return x[f - 1];
+    const int q = f - 1 - d;
+    return x[q / d] * x[q % d] * 0.70710678118654752f;
+}
+
+__device__ __forceinline__ float ld(const void *p, size_t i, int dtype) {
+    return dtype == 1 ? bf16_bits_to_float(reinterpret_cast<const bf16_t *>(p)[i])
+                      : reinterpret_cast<const float *>(p)[i];
+}
+__device__ __forceinline__ void st(void *p, size_t i, float v, int dtype) {
+    if (dtype == 1) reinterpret_cast<bf16_t *>(p)[i] = float_to_bf16_bits(v);
+    else reinterpret_cast<float *>(p)[i] = v;
+}
+
+// fp32 path.  One workgroup per (b,h); thread t owns state elements e = t + 256 m of
+// S [dp][d] (all in column t % d, since 256 is a multiple of d), kept in registers.
+constexpr int kSeqThreads = 256;
+constexpr int kSeqMaxE = 128;     // dp * d <= 256 * 128
+constexpr int kMaxDp = 288;
+
+__global__ __launch_bounds__(kSeqThreads) void seq_f32_kernel(SeqParams p) {
+    __shared__ float sk[128], sq[128], sv[128];
+    __shared__ float sfk[kMaxDp], sfq[kMaxDp], sz[kMaxDp];
+    __shared__ float sred[kSeqThreads];
+    const int bh = blockIdx.x, h = bh % p.H, t = threadIdx.x;
+    const int d = p.d, dp = p.dp, nE = dp * d;
+    const float *Wh = p.W ? p.W + (size_t)h * d * d : nullptr;
+    const float *bhp = p.b ? p.b + (size_t)h * d : nullptr;
+    auto wrow = [&](int l, int m) { return Wh[l * d + m]; };
+    const size_t seq = (size_t)bh * p.N * d;
+
+    float S[kSeqMaxE];
+#pragma unroll
+    for (int m = 0; m < kSeqMaxE; m++) {
+        const int e = t + kSeqThreads * m;
+        S[m] = (e < nE && p.S0) ? p.S0[(size_t)bh * nE + e] : 0.0f;
+    }
+    for (int f = t; f < dp; f += kSeqThreads) sz[f] = p.z0 ? p.z0[(size_t)bh * dp + f] : 0.0f;
+    const int ncol = t % d;
+
+    // pass over keys (causal: interleaved with queries; bidirectional: all keys first)
+    for (int pass = 0; pass < (p.causal ? 1 : 2); pass++) {
+        const bool do_update = p.causal || pass == 0;
+        const bool do_read = p.causal || pass == 1;
+        for (int i = 0; i < p.N; i++) {
+            __syncthreads();
+            if (t < d) {
+                sk[t] = p.k[seq + (size_t)i * d + t];
+                sq[t] = p.q[seq + (size_t)i * d + t];
+                sv[t] = p.v[seq + (size_t)i * d + t];
+            }
+            __syncthreads();
+            for (int f = t; f < dp; f += kSeqThreads) {
+                const int l = f < d ? f : f - d;
+                const float bl = (p.map == 0 && bhp) ? bhp[l] : 0.0f;
+                if (do_update) sfk[f] = feature_value(p.map, d, f, sk, wrow, bl);
+                if (do_read) sfq[f] = feature_value(p.map, d, f, sq, wrow, bl);
+            }
+            __syncthreads();
+            if (do_update) {
+#pragma unroll
+                for (int m = 0; m < kSeqMaxE; m++) {
+                    const int e = t + kSeqThreads * m;
+                    if (e < nE) S[m] = fmaf(sfk[e / d], sv[ncol], S[m]);
+                }
+                for (int f = t; f < dp; f += kSeqThreads) sz[f] += sfk[f];
+            }
+            if (do_read) {
+                float part = 0.0f;
+#pragma unroll
+                for (int m = 0; m < kSeqMaxE; m++) {
+                    const int e = t + kSeqThreads * m;
+                    if (e < nE) part = fmaf(sfq[e / d], S[m], part);
+                }
+                sred[t] = part;
+                __syncthreads();
+                if (t < d) {
+                    float num = 0.0f;
+                    for (int u = t; u < kSeqThreads; u += d) num += sred[u];
+                    float den = 0.0f;
+                    for (int f = 0; f < dp; f++) den = fmaf(sfq[f], sz[f], den);
+                    p.y[seq + (size_t)i * d + t] = num / den;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (p.S_out) {
+#pragma unroll
+        for (int m = 0; m < kSeqMaxE; m++) {
+            const int e = t + kSeqThreads * m;
+            if (e < nE) p.S_out[(size_t)bh * nE + e] = S[m];
+        }
+        for (int f = t; f < dp; f += kSeqThreads) p.z_out[(size_t)bh * dp + f] = sz[f];
+    }
+}
+
+hipError_t launch_seq_f32(const SeqParams &p, int BH, hipStream_t st) {
+    hipLaunchKernelGGL(seq_f32_kernel, dim3(BH), dim3(kSeqThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------
+// Decode step.  One workgroup per (b,h): features of the new q and k, then one streaming
+// pass over S [dp][d] (read, add phi(k) v^T, write back, accumulate phi(q)^T S), float4
+// per thread.  Thread t always touches column quad t % (d/4).
+constexpr int kDecThreads = 256;
+
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
+    __shared__ float sq[128], sk[128], sv[128];
+    __shared__ float sfq[kMaxDp], sfk[kMaxDp];
+    __shared__ f32x4 sred[kDecThreads];
+    __shared__ float sden[kDecThreads / 64];
+    const int bh = blockIdx.x, h = bh % p.H, t = threadIdx.x;
+    const int d = p.d, dp = p.dp, dt = p.dtype;
+    if (t < d) {
+        sq[t] = ld(p.q, (size_t)bh * d + t, dt);
+        sk[t] = ld(p.k, (size_t)bh * d + t, dt);
+        sv[t] = ld(p.v, (size_t)bh * d + t, dt);
+    }
+    __syncthreads();
+    const void *W = p.W;
+    const size_t woff = (size_t)h * d * d;
+    auto wrow = [&](int l, int m) { return ld(W, woff + (size_t)l * d + m, dt); };
+    for (int f = t; f < dp; f += kDecThreads) {
+        const int l = f < d ? f : f - d;
+        const float bl = (p.map == 0 && p.b) ? ld(p.b, (size_t)h * d + l, dt) : 0.0f;
+        sfk[f] = feature_value(p.map, d, f, sk, wrow, bl);
+        sfq[f] = feature_value(p.map, d, f, sq, wrow, bl);
+    }
+    __syncthreads();
+
+    const int q4 = d / 4;
+    const int c4 = t % q4;
+    const f32x4 vq = f32x4{sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]};
+    f32x4 *S4 = reinterpret_cast<f32x4 *>(p.S + (size_t)bh * dp * d);
+    const int n4 = dp * q4;
+    f32x4 acc = zero4();
+#pragma unroll 8
+    for (int e4 = t; e4 < n4; e4 += kDecThreads) {
+        const int f = e4 / q4;
+        f32x4 s = __builtin_nontemporal_load(S4 + e4);
+        const float a = sfk[f];
+        s[0] = fmaf(a, vq[0], s[0]);
+        s[1] = fmaf(a, vq[1], s[1]);
+        s[2] = fmaf(a, vq[2], s[2]);
+        s[3] = fmaf(a, vq[3], s[3]);
+        __builtin_nontemporal_store(s, S4 + e4);
+        const float gq = sfq[f];
+        acc[0] = fmaf(gq, s[0], acc[0]);
+        acc[1] = fmaf(gq, s[1], acc[1]);
+        acc[2] = fmaf(gq, s[2], acc[2]);
+        acc[3] = fmaf(gq, s[3], acc[3]);
+    }
+    float dpart = 0.0f;
+    float *zb = p.z + (size_t)bh * dp;
+    for (int f = t; f < dp; f += kDecThreads) {
+        const float zz = zb[f] + sfk[f];
+        zb[f] = zz;
+        dpart = fmaf(sfq[f], zz, dpart);
+    }
+    sred[t] = acc;
+    for (int o = 32; o > 0; o >>= 1) dpart += __shfl_xor(dpart, o);
+    if ((t & 63) == 0) sden[t >> 6] = dpart;
+    __syncthreads();
+    if (t < q4) {
+        f32x4 num = zero4();
+        for (int u = t; u < kDecThreads; u += q4) num += sred[u];
+        float den = 0.0f;
+        for (int wv = 0; wv < kDecThreads / 64; wv++) den += sden[wv];
+        for (int c = 0; c < 4; c++) st(p.y, (size_t)bh * d + 4 * t + c, num[c] / den, dt);
+    }
+}
+
+hipError_t launch_decode(const DecodeParams &p, int BH, hipStream_t st) {
+    hipLaunchKernelGGL(decode_kernel, dim3(BH), dim3(kDecThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------
+// Feature map on the vector units.  Hedgehog: one thread per (token, direction) writes
+// both halves.  Taylor: one thread per (token, feature).
+__global__ void fm_generic_kernel(int map, int dtype, int d, int dp, const void *x, const void *W, const void *b,
+                                  void *phi, long ntok, int H, int N) {
+    const long per = map == 0 ? d : dp;
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= ntok * per) return;
+    const long tok = idx / per;
+    const int f = (int)(idx % per);
+    const size_t xo = (size_t)tok * d;
+    if (map == 0) {
+        const int h = (int)((tok / N) % H);
+        const size_t wo = ((size_t)h * d + f) * d;
+        float u = b ? ld(b, (size_t)h * d + f, dtype) : 0.0f;
+        for (int m = 0; m < d; m++) u = fmaf(ld(W, wo + m, dtype), ld(x, xo + m, dtype), u);
+        st(phi, (size_t)tok * dp + f, expf(u), dtype);
+        st(phi, (size_t)tok * dp + d + f, expf(-u), dtype);
+    } else {
+        float val;
+        if (f == 0) val = 1.0f;
+        else if (f <= d) val = ld(x, xo + f - 1, dtype);
+        else {
+            const int q = f - 1 - d;
+            val = ld(x, xo + q / d, dtype) * ld(x, xo + q % d, dtype) * 0.70710678118654752f;
+        }
+        st(phi, (size_t)tok * dp + f, val, dtype);
+    }
+}
+
+hipError_t launch_featuremap_generic(int map, int dtype, int d, int dp, const void *x, const void *W, const void *b,
+                                     void *phi, long BH, int H, int N, hipStream_t st) {
+    const long ntok = BH * (long)N;
+    const long per = map == 0 ? d : dp;
+    const long total = ntok * per;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(fm_generic_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, map, dtype, d, dp,
+                       x, W, b, phi, ntok, H, N);
+    return hipGetLastError();
+}
+
+}  // namespace hh

@@ -1,0 +1,282 @@
+// hh_narrow.hip -- chunked causal / bidirectional attention with the degree-2 Taylor map,
+// head dim 16, on the CDNA4 matrix cores (bf16 in, fp32 state).
+//
+// The Taylor map phi(x) = [1, x, x_a x_c / sqrt(2)] makes phi(q)^T phi(k) = 1 + s + s^2/2
+// with s = q.k exactly (paper-graph-ui walkthrough of "The Hedgehog & the Porcupine",
+// section 3.4, "The Taylor Exponential as a Bridge Result").  The chunk recurrence is the
+// same regrouping of Eq. 2 as in the Hedgehog kernels:
+//     y_c = (phiQ_c Sp + A_c V_c) / (phiQ_c zp + A_c 1),  A_c = tril(phiQ_c phiK_c^T)
+//     Sp += phiK_c^T V_c,  zp += phiK_c^T 1
+// Two choices specific to this map:
+//   * The intra-chunk kernel matrix A_c is formed from the closed form 1 + s + s^2/2
+//     with s = Q_c K_c^T (a K = 16 product), the identity above, instead of a K = 273
+//     product of feature vectors.
+//   * Features are never stored: each lane builds the 8 feature values an MFMA operand
+//     slot needs from the raw q or k values, so one wave holds the whole 288 x 16 fp32
+//     state in registers.
+// Internal feature-row order (a permutation of the canonical one): block 0 = x_0..x_15,
+// block 1 + a = x_a x_p / sqrt(2) for p = 0..15, block 17 = [1, 0 ... 0].  Canonical
+// index c maps to internal row c - 1 (c >= 1) and row 272 (c = 0).
+#include "hh_common.h"
+#include "hh_kernels.h"
+
+namespace hh {
+
+namespace {
+constexpr int D = 16;
+constexpr int C = 64;
+constexpr int FB = 18;          // 16-row feature blocks (288 rows)
+constexpr int KSF = FB / 2;     // 32-wide K steps over features
+constexpr int RR = D + 8;       // row stride of [C][D] tiles (bf16)
+constexpr int RT = C + 8;       // row stride of [D][C] tiles (bf16)
+constexpr float kInvSqrt2 = 0.70710678118654752f;
+enum { NM_STATE = 0, NM_CAUSAL = 1, NM_READOUT = 2 };
+}  // namespace
+
+// Feature value of internal block fb at position p, for a token whose values are x[0..15].
+// xp = x[p] (already multiplied by 1/sqrt(2) for the quadratic blocks: xps).
+__device__ __forceinline__ float taylor_feature(int fb, const float (&x)[D], float xp, float xps, bool const_on) {
+    if (fb == 0) return xp;
+    if (fb == 17) return const_on ? 1.0f : 0.0f;
+    return x[fb - 1] * xps;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(64) void narrow_kernel(NarrowParams p) {
+    __shared__ __attribute__((aligned(16))) bf16_t sQ[C * RR];
+    __shared__ __attribute__((aligned(16))) bf16_t sK[C * RR];
+    __shared__ __attribute__((aligned(16))) bf16_t sKT[D * RT];
+    __shared__ __attribute__((aligned(16))) bf16_t sVT[D * RT];
+
+    const int lane = threadIdx.x, g = lane >> 4, r16 = lane & 15;
+    const int bh = blockIdx.x / p.nseg_grid;
+    const int s = blockIdx.x % p.nseg_grid;
+    const int t_begin = s * p.seg_len;
+    const int t_end = min(p.N, t_begin + p.seg_len);
+    const size_t base = (size_t)bh * p.N * D;
+
+    // State S[f][n] (lane: column n = r16, rows f = 16 fb + 4 g + r) and z (same rows, every column).
+    f32x4 sacc[FB], zacc[FB];
+    {
+        const float *Si = nullptr, *zi = nullptr;
+        if (MODE != NM_STATE && p.S_in) {
+            const size_t slot = (size_t)bh * p.in_bh_stride + (size_t)s * p.in_seg_stride;
+            Si = p.S_in + slot * kTaylorRowsInternal * D;
+            zi = p.z_in + slot * kTaylorRowsInternal;
+        }
+#pragma unroll
+        for (int fb = 0; fb < FB; fb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int f = 16 * fb + 4 * g + r;
+                sacc[fb][r] = Si ? Si[(size_t)f * D + r16] : 0.0f;
+                zacc[fb][r] = zi ? zi[f] : 0.0f;
+            }
+    }
+    const bf16x8 ones = ones_bf16x8();
+
+    for (int t0 = t_begin; t0 < t_end; t0 += C) {
+        const int valid = min(C, t_end - t0);
+        // ---- stage the chunk: q, k row-major; k, v transposed (tokens contiguous)
+        {
+            const int j = lane;
+            const bool ok = j < valid;
+            const bf16_t *qr = p.q + base + (size_t)(t0 + j) * D;
+            const bf16_t *kr = p.k + base + (size_t)(t0 + j) * D;
+            const bf16_t *vr = p.v + base + (size_t)(t0 + j) * D;
+            bf16x8 kq[2], kk[2], kv[2];
+#pragma unroll
+            for (int hlf = 0; hlf < 2; hlf++) {
+                kq[hlf] = (ok && MODE != NM_STATE) ? load8(qr + 8 * hlf) : zero_bf16x8();
+                kk[hlf] = (ok && MODE != NM_READOUT) ? load8(kr + 8 * hlf) : zero_bf16x8();
+                kv[hlf] = (ok && MODE != NM_READOUT) ? load8(vr + 8 * hlf) : zero_bf16x8();
+                store8(sQ + j * RR + 8 * hlf, kq[hlf]);
+                store8(sK + j * RR + 8 * hlf, kk[hlf]);
+            }
+#pragma unroll
+            for (int m = 0; m < D; m++) {
+                reinterpret_cast<__bf16 *>(sKT)[m * RT + j] = kk[m / 8][m % 8];
+                reinterpret_cast<__bf16 *>(sVT)[m * RT + j] = kv[m / 8][m % 8];
+            }
+        }
+        __syncthreads();
+
+        // V as a B operand, K = tokens in the order of two stacked accumulator blocks:
+        // slot s < 4 -> j = 32 ks + 4 g + s, slot s >= 4 -> j = 32 ks + 16 + 4 g + s - 4.
+        bf16x8 vop[2];
+        if (MODE != NM_READOUT) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                const bf16_t *vp = sVT + r16 * RT + 32 * ks + 4 * g;
+                vop[ks] = cat(load4(vp), load4(vp + 16));
+            }
+        }
+
+        if (MODE != NM_STATE) {
+            f32x4 num[4], den[4];
+#pragma unroll
+            for (int ib = 0; ib < 4; ib++) {
+                num[ib] = zero4();
+                den[ib] = zero4();
+            }
+            // ---- read-out against the carried state; phi(q) built per operand slot
+#pragma unroll
+            for (int ib = 0; ib < 4; ib++) {
+                const int i = 16 * ib + r16;
+                float x[D];
+                {
+                    const bf16x8 a0 = load8(sQ + i * RR), a1 = load8(sQ + i * RR + 8);
+#pragma unroll
+                    for (int m = 0; m < 8; m++) {
+                        x[m] = (float)a0[m];
+                        x[8 + m] = (float)a1[m];
+                    }
+                }
+                float xp[4], xps[4];
+                {
+                    const bf16x4 q4 = load4(sQ + i * RR + 4 * g);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        xp[r] = (float)q4[r];
+                        xps[r] = xp[r] * kInvSqrt2;
+                    }
+                }
+#pragma unroll
+                for (int ks = 0; ks < KSF; ks++) {
+                    bf16x8 a;
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        a[r] = (__bf16)taylor_feature(2 * ks, x, xp[r], xps[r], g == 0 && r == 0);
+                        a[4 + r] = (__bf16)taylor_feature(2 * ks + 1, x, xp[r], xps[r], g == 0 && r == 0);
+                    }
+                    num[ib] = mfma_bf16(a, acc_pair_to_operand(sacc[2 * ks], sacc[2 * ks + 1]), num[ib]);
+                    den[ib] = mfma_bf16(a, acc_pair_to_operand(zacc[2 * ks], zacc[2 * ks + 1]), den[ib]);
+                }
+            }
+            // ---- intra-chunk part (causal): A = 1 + s + s^2/2 on j <= i, s = k_j . q_i
+            if (MODE == NM_CAUSAL) {
+                bf16x8 kop[4], qop[4];
+#pragma unroll
+                for (int b = 0; b < 4; b++) {
+                    kop[b] = g < 2 ? load8(sK + (16 * b + r16) * RR + 8 * g) : zero_bf16x8();
+                    qop[b] = g < 2 ? load8(sQ + (16 * b + r16) * RR + 8 * g) : zero_bf16x8();
+                }
+#pragma unroll
+                for (int ib = 0; ib < 4; ib++) {
+                    f32x4 at[4];
+#pragma unroll
+                    for (int jb = 0; jb < 4; jb++) {
+                        if (jb <= ib) {
+                            const f32x4 sdot = mfma_bf16(kop[jb], qop[ib], zero4());
+                            // sdot: lane holds i = 16 ib + r16, j = 16 jb + 4 g + r
+#pragma unroll
+                            for (int r = 0; r < 4; r++) {
+                                const int jl = 16 * jb + 4 * g + r, il = 16 * ib + r16;
+                                const float sv = sdot[r];
+                                const float av = fmaf(0.5f * sv, sv, 1.0f + sv);
+                                at[jb][r] = (jl <= il && jl < valid) ? av : 0.0f;
+                            }
+                        } else {
+                            at[jb] = zero4();
+                        }
+                    }
+#pragma unroll
+                    for (int ks = 0; ks <= ib / 2; ks++) {
+                        const bf16x8 a = acc_pair_to_operand(at[2 * ks], at[2 * ks + 1]);
+                        num[ib] = mfma_bf16(a, vop[ks], num[ib]);
+                        den[ib] = mfma_bf16(a, ones, den[ib]);
+                    }
+                }
+            }
+            // ---- output
+            bf16_t *yb = p.y + base + (size_t)t0 * D;
+#pragma unroll
+            for (int ib = 0; ib < 4; ib++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int i = 16 * ib + 4 * g + r;
+                    if (i < valid) yb[(size_t)i * D + r16] = float_to_bf16_bits(num[ib][r] / den[ib][r]);
+                }
+        }
+
+        if (MODE != NM_READOUT) {
+            // ---- state update: phi(k)^T built per operand slot (rows f = 16 fb + r16, K = tokens)
+            float kr[2][8], okc[2][8];
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                const bf16_t *kp = sKT + r16 * RT + 32 * ks + 4 * g;
+                const bf16x4 lo = load4(kp), hi = load4(kp + 16);
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    kr[ks][r] = (float)lo[r];
+                    kr[ks][4 + r] = (float)hi[r];
+                    const int jlo = 32 * ks + 4 * g + r, jhi = jlo + 16;
+                    okc[ks][r] = (r16 == 0 && jlo < valid) ? 1.0f : 0.0f;
+                    okc[ks][4 + r] = (r16 == 0 && jhi < valid) ? 1.0f : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int fb = 0; fb < FB; fb++)
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++) {
+                    bf16x8 a;
+                    if (fb == 0) {
+#pragma unroll
+                        for (int sl = 0; sl < 8; sl++) a[sl] = (__bf16)kr[ks][sl];
+                    } else if (fb == 17) {
+#pragma unroll
+                        for (int sl = 0; sl < 8; sl++) a[sl] = (__bf16)okc[ks][sl];
+                    } else {
+                        const bf16_t *kp = sKT + (fb - 1) * RT + 32 * ks + 4 * g;
+                        const bf16x4 lo = load4(kp), hi = load4(kp + 16);
+#pragma unroll
+                        for (int r = 0; r < 4; r++) {
+                            a[r] = (__bf16)((float)lo[r] * kr[ks][r] * kInvSqrt2);
+                            a[4 + r] = (__bf16)((float)hi[r] * kr[ks][4 + r] * kInvSqrt2);
+                        }
+                    }
+                    sacc[fb] = mfma_bf16(a, vop[ks], sacc[fb]);
+                    zacc[fb] = mfma_bf16(a, ones, zacc[fb]);
+                }
+        }
+        __syncthreads();
+    }
+
+    // ---- segment end
+    float *So = nullptr, *zo = nullptr;
+    bool canonical = false;
+    if (MODE == NM_STATE) {
+        const size_t slot = (size_t)bh * p.ws_bh_stride + s;
+        So = p.S_ws + slot * kTaylorRowsInternal * D;
+        zo = p.z_ws + slot * kTaylorRowsInternal;
+    } else if (MODE == NM_CAUSAL && p.S_out && s == p.nseg_grid - 1) {
+        So = p.S_out + (size_t)bh * 273 * D;
+        zo = p.z_out + (size_t)bh * 273;
+        canonical = true;
+    }
+    if (So) {
+#pragma unroll
+        for (int fb = 0; fb < FB; fb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int f = 16 * fb + 4 * g + r;
+                int row = f;
+                if (canonical) row = f < 272 ? f + 1 : (f == 272 ? 0 : -1);
+                if (row >= 0) {
+                    So[(size_t)row * D + r16] = sacc[fb][r];
+                    if (r16 == 0) zo[row] = zacc[fb][r];
+                }
+            }
+    }
+}
+
+hipError_t launch_narrow(int mode, const NarrowParams &p, int grid, hipStream_t st) {
+    switch (mode) {
+    case NM_STATE: hipLaunchKernelGGL(narrow_kernel<NM_STATE>, dim3(grid), dim3(64), 0, st, p); break;
+    case NM_CAUSAL: hipLaunchKernelGGL(narrow_kernel<NM_CAUSAL>, dim3(grid), dim3(64), 0, st, p); break;
+    default: hipLaunchKernelGGL(narrow_kernel<NM_READOUT>, dim3(grid), dim3(64), 0, st, p); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hh

@@ -1,0 +1,114 @@
+"""The C ABI without a GPU: libhh loads, exports every function include/hh.h
+declares, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from softmax_mimicking_feature_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hh.h")
+
+HOG, TAY = _lib.HH_MAP_HEDGEHOG, _lib.HH_MAP_TAYLOR2
+F32, BF16 = _lib.HH_F32, _lib.HH_BF16
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hh_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_feature_dim_and_strings(lib):
+    assert lib.hh_abi_version() == 1
+    assert lib.hh_feature_dim(HOG, 128) == 256
+    assert lib.hh_feature_dim(TAY, 16) == 273
+    assert lib.hh_feature_dim(TAY, 64) == 4161
+    assert lib.hh_feature_dim(7, 16) == -1
+    for s in range(5):
+        assert lib.hh_status_str(s).decode().startswith("HH_")
+
+
+# Fake but 16-byte-aligned device addresses: validation must reject the call before
+# anything dereferences them or touches the GPU.
+A = 0x10000
+Bp = 0x20000000
+Cp = 0x30000000
+Dp = 0x40000000
+Wp = 0x50000000
+
+
+def fwd(lib, map_=HOG, dt=BF16, causal=1, B=1, H=2, N=64, d=64, q=A, k=Bp, v=Cp, W=Wp, b=None, S0=None, z0=None,
+        y=Dp, S_out=None, z_out=None, ws=None, ws_bytes=0):
+    return lib.hh_linattn_fwd(map_, dt, causal, B, H, N, d, q, k, v, W, b, S0, z0, y, S_out, z_out, ws, ws_bytes,
+                              None)
+
+
+def test_fwd_rejects_bad_arguments(lib):
+    assert fwd(lib, map_=5) == _lib.HH_EINVAL
+    assert fwd(lib, dt=9) == _lib.HH_EINVAL
+    assert fwd(lib, causal=2) == _lib.HH_EINVAL
+    assert fwd(lib, B=0) == _lib.HH_EINVAL
+    assert fwd(lib, N=-1) == _lib.HH_EINVAL
+    assert fwd(lib, d=48) == _lib.HH_EUNSUPPORTED
+    assert fwd(lib, map_=TAY, d=64) == _lib.HH_EUNSUPPORTED
+    assert fwd(lib, q=None) == _lib.HH_EINVAL
+    assert fwd(lib, y=None) == _lib.HH_EINVAL
+    assert fwd(lib, W=None) == _lib.HH_EINVAL
+    assert fwd(lib, q=A + 8) == _lib.HH_EINVAL                       # misaligned
+    assert fwd(lib, y=A) == _lib.HH_EINVAL                           # y aliases q
+    assert fwd(lib, S0=0x60000000) == _lib.HH_EINVAL                 # S0 without z0
+    assert fwd(lib, causal=0, S0=0x60000000, z0=0x61000000) == _lib.HH_EINVAL  # state with bidirectional
+    assert fwd(lib, N=1 << 25, d=128) == _lib.HH_EINVAL              # N*d >= 2^31
+    assert lib.hh_last_error().decode() != ""
+
+
+def test_fwd_workspace_rules(lib):
+    need = lib.hh_linattn_fwd_workspace(HOG, BF16, 1, 1, 32, 4096, 128)
+    assert need > 0                                                  # several segments per head
+    assert fwd(lib, H=32, N=4096, d=128, ws=None) == _lib.HH_EWORKSPACE
+    assert fwd(lib, H=32, N=4096, d=128, ws=0x70000000, ws_bytes=need - 16) == _lib.HH_EWORKSPACE
+    assert "workspace" in lib.hh_last_error().decode()
+    # bidirectional always needs one state slot per head; fp32 and empty inputs need none
+    assert lib.hh_linattn_fwd_workspace(HOG, BF16, 0, 32, 12, 512, 64) >= 32 * 12 * (128 * 64 + 128) * 4
+    assert lib.hh_linattn_fwd_workspace(HOG, F32, 1, 1, 1, 256, 16) == 0
+    assert lib.hh_linattn_fwd_workspace(HOG, BF16, 1, 1, 1, 0, 16) == 0
+    assert lib.hh_linattn_fwd_workspace(HOG, BF16, 1, 1, 1, 64, 48) == 0  # invalid -> 0
+
+
+def test_featuremap_and_decode_reject_bad_arguments(lib):
+    assert lib.hh_featuremap(HOG, BF16, 1, 1, 8, 64, A, None, None, Dp, None) == _lib.HH_EINVAL   # no W
+    assert lib.hh_featuremap(HOG, BF16, 1, 1, 8, 64, A, Wp, None, A, None) == _lib.HH_EINVAL      # phi aliases x
+    assert lib.hh_featuremap(TAY, BF16, 1, 1, 8, 32, A, None, None, Dp, None) == _lib.HH_EUNSUPPORTED
+    # empty input: valid, nothing to do, no GPU touched
+    assert lib.hh_featuremap(HOG, BF16, 1, 1, 0, 64, None, Wp, None, None, None) == _lib.HH_OK
+    dec = lib.hh_linattn_decode_step
+    assert dec(HOG, BF16, 1, 1, 64, A, Bp, Cp, Wp, None, None, 0x60000000, Dp, None) == _lib.HH_EINVAL  # no S
+    assert dec(HOG, BF16, 1, 1, 64, A, Bp, Cp, Wp, None, 0x60000000, 0x60000010, Dp, None) == _lib.HH_EINVAL
+    assert dec(HOG, BF16, 0, 1, 64, A, Bp, Cp, Wp, None, 0x60000000, 0x61000000, Dp, None) == _lib.HH_EINVAL
+    assert dec(HOG, BF16, 1, 1, 64, A, Bp, Cp, Wp, None, 0x60000000, 0x61000000, A, None) == _lib.HH_EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.LibraryMissing):
+        _lib.load()

@@ -266,3 +266,13 @@ def test_threads_do_not_change_results():
     y1 = oracle.causal(HH, q, k, v, W, b, nthreads=1)
     y8 = oracle.causal(HH, q, k, v, W, b, nthreads=8)
     assert np.array_equal(y1, y8)
+
+
+@pytest.mark.parametrize("map_", [HH, TAY])
+def test_prefix_state_equals_running_sums(map_):
+    rng = np.random.default_rng(81 + map_)
+    q, k, v, W, b = _rand_case(rng, map_, 2, 3, 30, 4)
+    _, S, z = oracle.causal(map_, q, k, v, W, b, want_state=True)
+    S2, z2 = oracle.prefix_state(map_, k, v, W, b)
+    np.testing.assert_allclose(S2, S, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z2, z, rtol=1e-12)
