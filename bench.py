@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the Hedgehog causal linear-attention forward (feature map included).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one hh_linattn_fwd call over one batch of synthetic input (all
+kernels of the path: feature maps, intra-chunk products, state carry,
+read-out).  Inputs, outputs and workspace are resident in HBM before the
+timed region; steps rotate over 4 input sets (about 670 MB for the default
+workload, more than twice the 256 MB MALL) so repeated steps do not run out
+of the last-level cache.  Prints one JSON line.
+
+Default workload: Llama-2-7B head shapes, B=1, H=32, N=4096, d=128, bf16
+(the configuration the throughput metric is quoted on).  Other workloads can
+be selected for measurement with --workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from softmax_mimicking_feature_amd import workloads as wl  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+PEAK_MFMA_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+N_SETS = 4
+METRIC = "causal linear-attn fwd tokens/s (\u03c6 incl.) at Llama-2-7B heads; % MFMA peak"
+
+
+def algorithmic_counts(w: wl.Workload):
+    """Algorithmic FLOPs and HBM bytes of one forward (what the method itself must do).
+
+    Per token-head: feature maps of q and k 4d^2 (Hedgehog; Taylor 2(d^2+d)), state update
+    and read-out 4 d' d, normaliser update / dot / divide 3d' + d.  Bytes: read q, k, v and
+    write y once, plus W and b once per head."""
+    d, dp = w.d, wl.feature_dim(w.map, w.d)
+    th = w.B * w.H * w.N
+    fm = 4 * d * d if w.map == wl.MAP_HEDGEHOG else 2 * (d * d + d)
+    flops = th * (fm + 4 * dp * d + 3 * dp + d)
+    eb = wl.bytes_per_elem(w.dtype)
+    byts = eb * 4 * th * d
+    if w.map == wl.MAP_HEDGEHOG:
+        byts += eb * w.H * (d * d + d)
+    return float(flops), float(byts)
+
+
+def decode_counts(w: wl.Workload):
+    d, dp = w.d, wl.feature_dim(w.map, w.d)
+    bh = w.B * w.H
+    eb = wl.bytes_per_elem(w.dtype)
+    byts = 2 * 4 * bh * (dp * d + dp) + eb * 4 * bh * d + eb * w.H * (d * d + d)
+    fm = 4 * d * d if w.map == wl.MAP_HEDGEHOG else 2 * (d * d + d)
+    flops = bh * (fm + 4 * dp * d + 3 * dp + d)
+    return float(flops), float(byts)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3_llama2_causal", choices=sorted(wl.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path shards over "
+              "(batch, head) pairs with no communication, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import softmax_mimicking_feature_amd as hh
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = wl.CONFIGS[args.workload]
+    tdt = torch.bfloat16 if w.dtype == wl.DT_BF16 else torch.float32
+    decode = args.workload.endswith("decode")
+
+    # ---- input sets (set 0 from the seeded host generator, the others drawn on the GPU
+    #      with the same distributions)
+    host0 = wl.make_inputs(w) if not decode else None
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+
+    def draw(shape, scale):
+        return (torch.randn(shape, generator=g, device=dev) * scale).to(tdt)
+
+    sets = []
+    for si in range(N_SETS):
+        if decode:
+            shp = (w.B, w.H, w.d)
+            s = {"q": draw(shp, w.qk_scale), "k": draw(shp, w.qk_scale), "v": draw(shp, w.v_scale)}
+        elif si == 0:
+            s = {k: torch.from_numpy(host0[k]).to(dev).to(tdt) for k in ("q", "k", "v")}
+        else:
+            shp = (w.B, w.H, w.N, w.d)
+            s = {"q": draw(shp, w.qk_scale), "k": draw(shp, w.qk_scale), "v": draw(shp, w.v_scale)}
+        sets.append(s)
+    if w.map == wl.MAP_HEDGEHOG:
+        if host0 is not None:
+            W = torch.from_numpy(host0["W"]).to(dev).to(tdt)
+            b = torch.from_numpy(host0["b"]).to(dev).to(tdt)
+        else:
+            W = draw((w.H, w.d, w.d), w.w_std)
+            b = draw((w.H, w.d), w.b_std)
+    else:
+        W = b = None
+
+    stream = torch.cuda.current_stream()
+    if decode:
+        dp = wl.feature_dim(w.map, w.d)
+        # a 4096-token prefix state built by the forward itself (values only matter for realism)
+        states = []
+        for si in range(N_SETS):
+            kq = draw((w.B, w.H, w.N, w.d), w.qk_scale)
+            vv = draw((w.B, w.H, w.N, w.d), w.v_scale)
+            _, S, z = hh.hh_linattn_fwd(kq, kq, vv, W, b, map=w.map, want_state=True)
+            states.append((S, z))
+            del kq, vv
+        outs = [torch.empty((w.B, w.H, w.d), dtype=tdt, device=dev) for _ in range(N_SETS)]
+
+        def step(i):
+            s = sets[i % N_SETS]
+            S, z = states[i % N_SETS]
+            hh.hh_linattn_decode_step(s["q"], s["k"], s["v"], W, b, S, z, map=w.map, out=outs[i % N_SETS],
+                                      stream=stream)
+        flops, byts = decode_counts(w)
+    else:
+        need = hh.hh_linattn_fwd_workspace(w.map, w.dtype, w.causal, w.B, w.H, w.N, w.d)
+        wss = [torch.empty((max(need, 16),), dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
+        outs = [torch.empty_like(sets[0]["q"]) for _ in range(N_SETS)]
+
+        def step(i):
+            s = sets[i % N_SETS]
+            hh.hh_linattn_fwd(s["q"], s["k"], s["v"], W, b, causal=w.causal, map=w.map, out=outs[i % N_SETS],
+                              workspace=wss[i % N_SETS], stream=stream)
+        flops, byts = algorithmic_counts(w)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, per-launch events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per = np.array([a.elapsed_time(bq) for a, bq in ev])
+    ms_per_step = total_ms / args.steps
+    launch_ms = float(per.mean())
+
+    tokens = w.B * (1 if decode else w.N)
+    value = tokens / (ms_per_step * 1e-3)
+    ach_gbs = byts / (launch_ms * 1e-3) / 1e9
+    ach_tflops = flops / (launch_ms * 1e-3) / 1e12
+    ai = flops / byts
+    ridge = PEAK_MFMA_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    bound = "hbm" if ai < ridge else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach_gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(ach_tflops, 1), "peak": PEAK_MFMA_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach_tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = ("hh_linattn_decode_step (decode_kernel)" if decode else
+                      "hh_linattn_fwd: segment-state + prefix-scan + chunked causal kernels of one call")
+    roof["launch_ms_mean"] = round(launch_ms, 5)
+    roof["launch_ms_p10_p90"] = [round(float(np.percentile(per, 10)), 5), round(float(np.percentile(per, 90)), 5)]
+    roof["alg_flops"] = flops
+    roof["alg_bytes"] = byts
+    roof["mfma_frac_of_bf16_peak"] = round(ach_tflops / PEAK_MFMA_BF16_TFLOPS, 4)
+
+    cpu = None
+    if not args.no_cpu_baseline and not decode:
+        import oracle
+        nthr = oracle.default_threads()
+        xw = host0
+        t0 = time.perf_counter()
+        if w.causal:
+            oracle.causal(w.map, xw["q"], xw["k"], xw["v"], xw["W"], xw["b"], nthreads=nthr)
+        else:
+            oracle.bidir(w.map, xw["q"], xw["k"], xw["v"], xw["W"], xw["b"], nthreads=nthr)
+        tc = time.perf_counter() - t0
+        cpu = {"value": round(tokens / tc, 1), "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+               "sample": f"one full forward of {w.name} (B{w.B} H{w.H} N{w.N} d{w.d}) by the fp64 oracle, "
+                         f"{tc:.2f} s wall on {nthr} threads"}
+
+    out = {
+        "metric": METRIC if not decode else "decode step tokens/s (one token per sequence)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == wl.DT_BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "map": "hedgehog" if w.map == wl.MAP_HEDGEHOG else "taylor2", "causal": w.causal,
+                   "input_sets_rotated": N_SETS},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
