@@ -29,9 +29,16 @@
 
 namespace hh {
 
+// Row stride (elements) of a bf16 tile read with the transposing LDS load: rows start
+// 32 bytes apart modulo 128 bytes, so the four rows one 16-lane group reads fall in
+// disjoint banks.
+constexpr int tr_stride(int n) { return n + ((((32 - 2 * n) % 128) + 128) % 128) / 2; }
+
 template <int D>
 struct WideCfg {
-    static constexpr int C = 64;                      // tokens per chunk
+    static constexpr int C = D == 128 ? 32 : 64;      // tokens per chunk
+    static constexpr int NCB = C / 16;                // 16-token blocks per chunk
+    static constexpr int KSC = C / 32;                // 32-wide K steps over the chunk's tokens
     static constexpr int NW = D == 128 ? 8 : (D == 64 ? 4 : D / 16);  // waves per workgroup
     static constexpr int NT = NW * 64;
     static constexpr int DP = 2 * D;                  // feature dimension
@@ -43,7 +50,7 @@ struct WideCfg {
     static constexpr int NDQ = NW / NTH;
     static constexpr int DPW = D / NDQ;               // directions per wave
     static constexpr int LB = DPW / 16;               // direction blocks per wave
-    static constexpr int IBT = 4 / NTH;               // token blocks per wave in the feature map
+    static constexpr int IBT = NCB / NTH;             // token blocks per wave in the feature map
     // state: NF feature parts x NN value-column parts
     static constexpr int NF = NW == 8 ? 2 : 1;
     static constexpr int NN = NW / NF;
@@ -51,23 +58,39 @@ struct WideCfg {
     static constexpr int FBW = FB / NF;               // feature blocks per wave
     static constexpr int KSW = FBW / 2;               // read-out K steps per wave
     static constexpr int ZB = FB / NW;                // z-row blocks per wave
-    static constexpr int IBF = 4 / NF;                // output row blocks finalised per wave
-    static constexpr int NJ = NW == 8 ? 2 : 1;        // intra-chunk row-sum slots
-    static constexpr int RQ = DP + 8;                 // row stride of [C][DP] tiles (bf16)
-    static constexpr int RC = C + 8;                  // row stride of [*][C] tiles (bf16)
-    static constexpr int XS = D + 4;                  // row stride of the fp32 exchange tile
+    static constexpr int IBF = NCB / NF;              // output row blocks finalised per wave
+    static constexpr int NJ = (NW == 8) ? 2 : 1;      // intra-chunk row-sum slots
+    static constexpr int VPT = C * (D / 8) / NT;      // 16-byte pieces of V per thread and chunk
+    // LDS tiles
+    static constexpr int RQ = DP + 8;                 // phi(q) [C][RQ]: 16-byte row reads
+    static constexpr int RK = tr_stride(DP);          // phi(k) [C][RK]: row reads and transposing reads
+    static constexpr int RV = tr_stride(D);           // V [C][RV]: transposing reads
+    static constexpr int RA = C + 8;                  // intra scores A [C][RA]
+    static constexpr int XS = D + 4;                  // fp32 exchange tile [C][XS] (NF = 2), aliases phi(q)
+    static constexpr int SZ_PQ = (C * RQ * 2 > (NF == 2 ? C * XS * 4 : 0)) ? C * RQ * 2 : C * XS * 4;
+    static constexpr int SZ_PK = C * RK * 2;
+    // raw q / k of the next chunk, loaded straight from global memory into LDS: [C][D]
+    // bf16, 16-byte granules of row r stored at granule index (g ^ (r % NSW))
+    static constexpr int NG = D / 8;                  // 16-byte granules per row
+    static constexpr int NSW = NG < 8 ? NG : 8;
+    static constexpr int SZ_X = C * D * 2;
+    static constexpr int XBLK = SZ_X / 1024;          // 1 KB direct-load blocks per tile
     static constexpr int OFF_PQ = 0;
-    static constexpr int OFF_PK = OFF_PQ + C * RQ * 2;     // also the exchange tile (NF = 2)
-    static constexpr int OFF_PKT = OFF_PK + C * RQ * 2;
-    static constexpr int OFF_VT = OFF_PKT + DP * RC * 2;
-    static constexpr int OFF_A = OFF_VT + D * RC * 2;
-    static constexpr int OFF_DEN = OFF_A + C * RC * 2;
-    static constexpr int LDS_BYTES = OFF_DEN + (NW + NJ) * C * 4;
+    static constexpr int OFF_PK = OFF_PQ + SZ_PQ;
+    static constexpr int OFF_V = OFF_PK + SZ_PK;
+    static constexpr int OFF_A = OFF_V + C * RV * 2;
+    static constexpr int OFF_DEN = OFF_A + C * RA * 2;
+    static constexpr int OFF_XQ = OFF_DEN + (NW + NJ) * C * 4;
+    static constexpr int OFF_XK = OFF_XQ + SZ_X;
+    // per-head W as MFMA A operands, [D rows][D] bf16 with granule swizzle like the x tiles
+    static constexpr int OFF_W = OFF_XK + SZ_X;
+    static constexpr int LDS_BYTES = OFF_W + D * D * 2;
     static constexpr int MIN_WG_PER_CU = NW == 8 ? 1 : 2;
     static_assert(ZB == 2, "each wave owns one K step of z rows");
-    static_assert(VB >= 1 && LB >= 1 && FBW % 2 == 0, "bad wave split");
-    static_assert(NF == 1 || C * XS * 4 <= C * RQ * 2, "exchange tile must fit in the phiK tile");
+    static_assert(VB >= 1 && LB >= 1 && IBT >= 1 && IBF >= 1 && FBW % 2 == 0, "bad wave split");
+    static_assert(VPT >= 1 && C * (D / 8) % NT == 0, "every lane moves whole V pieces");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(SZ_X % 1024 == 0 && XBLK % NW == 0, "direct loads: whole 1 KB blocks, the same count per wave");
 };
 
 enum { WM_STATE = 0, WM_CAUSAL = 1, WM_READOUT = 2 };
@@ -75,84 +98,123 @@ enum { WM_STATE = 0, WM_CAUSAL = 1, WM_READOUT = 2 };
 // Position of feature f in a row-major feature tile.  With PERM, each 32-feature group is
 // stored in the K order of two stacked accumulator blocks (lane group g reads features
 // {4g..4g+3, 16+4g..16+4g+3} as one 16-byte run), so the read-out operand that pairs with
-// the carried state is one 16-byte LDS read.  The scores read both tiles in the same
-// (physical) order, which is a consistent permutation of their contraction index.
+// the carried state is one 16-byte LDS read.  The scores read both feature tiles in the
+// same physical order, a consistent permutation of their contraction index.  Four
+// consecutive features (f0 % 4 == 0) stay contiguous.
 template <bool PERM>
-__device__ __forceinline__ int feat_pos(int fbase4) {  // fbase4: first of 4 consecutive features, fbase4 % 4 == 0
-    if (!PERM) return fbase4;
-    const int fl = fbase4 & 31;
-    return (fbase4 & ~31) + 8 * ((fl & 15) >> 2) + ((fl & 16) ? 4 : 0);
+__device__ __forceinline__ int feat_pos(int f0) {
+    if (!PERM) return f0;
+    const int fl = f0 & 31;
+    return (f0 & ~31) + 8 * ((fl & 15) >> 2) + ((fl & 16) ? 4 : 0);
 }
 
-__device__ __forceinline__ uint32_t pack2(__bf16 lo, __bf16 hi) {
-    bf16x2 v;
-    v[0] = lo;
-    v[1] = hi;
-    return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ __bf16 lo16(uint32_t u) { return __builtin_bit_cast(bf16x2, u)[0]; }
-__device__ __forceinline__ __bf16 hi16(uint32_t u) { return __builtin_bit_cast(bf16x2, u)[1]; }
-// Exchange a 32-bit value with the neighbouring lane (lane ^ 1), a DPP quad permutation.
-__device__ __forceinline__ uint32_t swap_adjacent(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
+// receives, in slot s, element (i % 4) of the 4-element run addressed by lane 4 s + i / 4.
+// Pointing lane i of a group at row (r0 + i / 4), columns (c0 + 4 (i % 4)) .. +3 of a
+// row-major tile therefore hands lane i column c0 + i, rows r0 .. r0+3: one half of an MFMA
+// operand whose K index runs down the tile's rows.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16_t *p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
 }
 
-// Write 4 features (rows f0 .. f0+3) of token i into a transposed tile [f][token] as 32-bit
-// pairs of tokens: even lanes write rows f0, f0+1 for tokens (i, i+1), odd lanes rows f0+2,
-// f0+3 for tokens (i-1, i), after swapping halves with the neighbouring lane.
-template <int RC>
-__device__ __forceinline__ void store_transposed_pairs(bf16_t *sT, int f0, int i, bool odd, const bf16x4 &v) {
-    const uint32_t send = odd ? pack2(v[0], v[1]) : pack2(v[2], v[3]);
-    const uint32_t recv = swap_adjacent(send);
-    const int ie = i & ~1;
+// MFMA operand from a row-major tile by two transposing reads: lane (column c0 + r16,
+// K rows r0 + 8 g .. r0 + 8 g + 7).  `lane_off` = (8 g + r16 / 4) * stride + 4 * (r16 % 4) is
+// the per-lane part of the address; `koff` = r0 * stride + (position of column c0), a
+// compile-time constant in every caller, so the reads use immediate offsets.
+__device__ __forceinline__ bf16x8 operand_down_rows(const bf16_t *tile, int lane_off, int koff, int stride) {
+    const bf16_t *p = tile + lane_off + koff;
+    return cat(lds_read_tr(p), lds_read_tr(p + 4 * stride));
+}
+
+// Physical position of the 16-feature block k's first column in a PERM feature tile
+// (columns of block k are at this position + 8 q + r for q = 0..3, r = 0..3 of each run).
+__device__ __forceinline__ constexpr int perm_block_pos(int k) { return 32 * (k >> 1) + 4 * (k & 1); }
+
+// Loads of the next chunk, issued one chunk ahead: q and k go straight into LDS staging
+// tiles (global_load_lds), V into a few registers.
+template <int D>
+struct Prefetch {
+    bf16x8 vp[WideCfg<D>::VPT];
+};
+
+__device__ __forceinline__ void load_to_lds_16(const void *gsrc, void *lds_dst_uniform) {
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)(reinterpret_cast<uintptr_t>(lds_dst_uniform)),
+                                     16, 0, 0);
+}
+
+// One [C][D] tile of x into its staging area: wave w moves blocks w, w + NW, ...; lane l of
+// block b lands at slot 64 b + l = (row r, stored granule G), which holds granule G ^ (r % NSW).
+// Rows past the end read a valid row (their values are never used).
+template <int D>
+__device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, int t0, int valid, int w, int lane,
+                                        unsigned char *stage) {
+    using K = WideCfg<D>;
 #pragma unroll
-    for (int k = 0; k < 2; k++) {
-        const __bf16 own = odd ? v[2 + k] : v[k];
-        const __bf16 oth = k == 0 ? lo16(recv) : hi16(recv);
-        const uint32_t word = odd ? pack2(oth, own) : pack2(own, oth);
-        const int row = f0 + (odd ? 2 : 0) + k;
-        *reinterpret_cast<uint32_t *>(sT + row * RC + ie) = word;
+    for (int bb = 0; bb < K::XBLK / K::NW; bb++) {
+        const int blk = w + bb * K::NW;
+        const int slot = 64 * blk + lane;
+        const int r = slot / K::NG, G = slot % K::NG;
+        const int kg = G ^ (r % K::NSW);
+        const int rr = r < valid ? r : 0;
+        load_to_lds_16(x + (size_t)(t0 + rr) * D + 8 * kg, stage + 1024 * blk);
     }
 }
 
-// Feature map of one chunk for this wave's directions and token blocks, written to LDS.
-//   ROWMAJOR : phi[i][pos(f)] (features contiguous), for the scores and the read-out
-//   TRANS    : phi^T[f][i] (tokens contiguous), for the state update
-template <int D, bool IS_KEY, bool FULL, bool ROWMAJOR, bool PERM, bool TRANS>
-__device__ __forceinline__ void phi_chunk(const bf16_t *__restrict__ x, int t0, int valid,
+template <int D, int MODE>
+__device__ __forceinline__ void issue_loads(Prefetch<D> &pf, const WideParams &p, size_t base, int t0, int valid,
+                                            int w, int lane, int tid, unsigned char *smem) {
+    using K = WideCfg<D>;
+    if (MODE != WM_STATE) stage_x<D>(p.q + base, t0, valid, w, lane, smem + K::OFF_XQ);
+    if (MODE != WM_READOUT) {
+        stage_x<D>(p.k + base, t0, valid, w, lane, smem + K::OFF_XK);
+        constexpr int NC = D / 8;
+#pragma unroll
+        for (int it = 0; it < K::VPT; it++) {
+            const int t = tid + it * K::NT;
+            const int j = t / NC, nc = t % NC;
+            pf.vp[it] = j < valid ? load8(p.v + base + (size_t)(t0 + j) * D + 8 * nc) : zero_bf16x8();
+        }
+    }
+}
+
+// x operand for the feature map (B operand: lane column = token i, K = input dim) from a
+// staging tile.
+template <int D>
+__device__ __forceinline__ bf16x8 staged_x_operand(const unsigned char *stage, int i, int ks, int g) {
+    using K = WideCfg<D>;
+    const int kg = 4 * ks + g;
+    if (8 * kg >= D) return zero_bf16x8();
+    return *reinterpret_cast<const bf16x8 *>(stage + 16 * (i * K::NG + (kg ^ (i % K::NSW))));
+}
+
+// Feature map of one chunk for this wave's directions and token blocks from prefetched x,
+// written row-major (features contiguous, position feat_pos) into LDS.
+template <int D, bool IS_KEY, bool FULL, bool PERM = true>
+__device__ __forceinline__ void phi_chunk(const unsigned char *stage, int valid,
                                           const bf16x8 (&wA)[WideCfg<D>::LB][WideCfg<D>::KSD],
                                           const float (&bl2)[WideCfg<D>::LB][4], int th, int dq, int g, int r16,
-                                          bf16_t *sRow, bf16_t *sT) {
+                                          bf16_t *sRow, int stride) {
     using K = WideCfg<D>;
-    f32x4 acc[K::LB][K::IBT];
 #pragma unroll
     for (int ibl = 0; ibl < K::IBT; ibl++) {
         const int i = 16 * (th * K::IBT + ibl) + r16;
         bf16x8 xb[K::KSD];
 #pragma unroll
-        for (int ks = 0; ks < K::KSD; ks++) {
-            const int m0 = 32 * ks + 8 * g;
-            xb[ks] = ((FULL || i < valid) && m0 < D) ? load8(x + (size_t)(t0 + i) * D + m0) : zero_bf16x8();
-        }
+        for (int ks = 0; ks < K::KSD; ks++) xb[ks] = staged_x_operand<D>(stage, i, ks, g);
 #pragma unroll
         for (int mb = 0; mb < K::LB; mb++) {
             f32x4 a = zero4();
 #pragma unroll
             for (int ks = 0; ks < K::KSD; ks++) a = mfma_bf16(wA[mb][ks], xb[ks], a);
-            acc[mb][ibl] = a;
-        }
-    }
-    const bool odd = (r16 & 1) != 0;
-#pragma unroll
-    for (int mb = 0; mb < K::LB; mb++) {
-        const int fb4 = dq * K::DPW + 16 * mb + 4 * g;  // this lane's 4 directions
-#pragma unroll
-        for (int ibl = 0; ibl < K::IBT; ibl++) {
-            const int i = 16 * (th * K::IBT + ibl) + r16;
+            // a: lane holds u for token i and directions fb4 .. fb4 + 3
+            const int fb4 = dq * K::DPW + 16 * mb + 4 * g;
             f32x4 ep, en;
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const float u = acc[mb][ibl][r] * kLog2e + bl2[mb][r];
+                const float u = a[r] * kLog2e + bl2[mb][r];
                 ep[r] = exp2_fast(u);
                 en[r] = exp2_fast(-u);
             }
@@ -160,15 +222,8 @@ __device__ __forceinline__ void phi_chunk(const bf16_t *__restrict__ x, int t0, 
                 ep = zero4();
                 en = zero4();
             }
-            const bf16x4 bp = to_bf16x4(ep), bn = to_bf16x4(en);
-            if (ROWMAJOR) {
-                store4(sRow + i * K::RQ + feat_pos<PERM>(fb4), bp);
-                store4(sRow + i * K::RQ + feat_pos<PERM>(D + fb4), bn);
-            }
-            if (TRANS) {
-                store_transposed_pairs<K::RC>(sT, fb4, i, odd, bp);
-                store_transposed_pairs<K::RC>(sT, D + fb4, i, odd, bn);
-            }
+            store4(sRow + i * stride + feat_pos<PERM>(fb4), to_bf16x4(ep));
+            store4(sRow + i * stride + feat_pos<PERM>(D + fb4), to_bf16x4(en));
         }
     }
 }
@@ -198,102 +253,125 @@ __device__ __forceinline__ void load_directions(const bf16_t *__restrict__ W, co
     }
 }
 
-// V chunk [C][D] -> LDS as V^T [D][C] (tokens contiguous); rows past the end are zero.
-// Lanes 2p and 2p+1 load the same 8 columns of tokens j and j+1 (16 bytes each), swap four
-// columns and write 32-bit token pairs.
-template <int D, bool FULL>
-__device__ __forceinline__ void v_chunk_to_lds(const bf16_t *__restrict__ v, int t0, int valid, int tid,
-                                               bf16_t *sVT) {
+// Per-head W into LDS (swizzled like the x tiles), once per workgroup.
+template <int D>
+__device__ __forceinline__ void stage_w(const bf16_t *__restrict__ W, int h, int tid, unsigned char *sW) {
     using K = WideCfg<D>;
-    constexpr int NC = D / 8;
-    constexpr int PIECES = K::C * NC;
-    static_assert(PIECES % K::NT == 0, "every lane takes part in each pass");
+    const bf16_t *Wh = W + (size_t)h * D * D;
+    for (int t = tid; t < D * K::NG; t += K::NT) {
+        const int l = t / K::NG, kg = t % K::NG;
+        *reinterpret_cast<bf16x8 *>(sW + 16 * (l * K::NG + (kg ^ (l % K::NSW)))) = load8(Wh + (size_t)l * D + 8 * kg);
+    }
+}
+
+// This wave's directions as MFMA A operands from the staged W.
+template <int D>
+__device__ __forceinline__ void load_w_operands(const unsigned char *sW, int dq, int g, int r16,
+                                                bf16x8 (&wA)[WideCfg<D>::LB][WideCfg<D>::KSD]) {
+    using K = WideCfg<D>;
 #pragma unroll
-    for (int it = 0; it < PIECES / K::NT; it++) {
-        const int t = tid + it * K::NT;
-        const int pr = t >> 1;
-        const bool odd = (t & 1) != 0;
-        const int nc = pr % NC, j = 2 * (pr / NC) + (odd ? 1 : 0);
-        const bf16x8 val = (FULL || j < valid) ? load8(v + (size_t)(t0 + j) * D + 8 * nc) : zero_bf16x8();
-        // even lanes keep columns 0..3 and send 4..7; odd lanes keep 4..7 and send 0..3
-        const uint32_t s0 = odd ? pack2(val[0], val[1]) : pack2(val[4], val[5]);
-        const uint32_t s1 = odd ? pack2(val[2], val[3]) : pack2(val[6], val[7]);
-        const uint32_t r0 = swap_adjacent(s0), r1 = swap_adjacent(s1);
-        const __bf16 oth[4] = {lo16(r0), hi16(r0), lo16(r1), hi16(r1)};
-        const int je = j & ~1;
+    for (int mb = 0; mb < K::LB; mb++) {
+        const int l = dq * K::DPW + 16 * mb + r16;
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const __bf16 own = odd ? val[4 + c] : val[c];
-            const uint32_t word = odd ? pack2(oth[c], own) : pack2(own, oth[c]);
-            *reinterpret_cast<uint32_t *>(sVT + (8 * nc + (odd ? 4 : 0) + c) * K::RC + je) = word;
+        for (int ks = 0; ks < K::KSD; ks++) {
+            const int kg = 4 * ks + g;
+            wA[mb][ks] = (8 * kg < D) ? *reinterpret_cast<const bf16x8 *>(sW + 16 * (l * K::NG + (kg ^ (l % K::NSW))))
+                                      : zero_bf16x8();
         }
     }
 }
 
-// Query blocks and key-block range of the intra-chunk scores handled by wave w, and the
-// row-sum slot it writes.  Every (query block, key block <= it) pair is covered once.
-template <int NW>
-__device__ __forceinline__ void score_task(int w, int qq, int &ib, int &jlo, int &jhi, int &slot) {
-    if (NW == 8) {
-        ib = w & 3;
-        jlo = w < 4 ? 0 : 2;
-        jhi = w < 4 ? (ib < 1 ? ib : 1) : ib;
-        slot = w >> 2;
-    } else {
-        ib = w * (4 / NW) + qq;
-        jlo = 0;
-        jhi = ib;
-        slot = 0;
+// Bias of this wave's directions, times log2(e), for the accumulator rows dq DPW + 16 mb + 4 g + r.
+template <int D>
+__device__ __forceinline__ void load_bias(const bf16_t *__restrict__ b, int h, int dq, int g,
+                                          float (&bl2)[WideCfg<D>::LB][4]) {
+    using K = WideCfg<D>;
+#pragma unroll
+    for (int mb = 0; mb < K::LB; mb++)
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            bl2[mb][r] = b ? bf16_bits_to_float(b[(size_t)h * D + dq * K::DPW + 16 * mb + 4 * g + r]) * kLog2e : 0.0f;
+}
+
+// Intra-chunk score task of wave w (query block ib, key blocks jlo..jhi, row-sum slot).
+// Every (query block, key block <= it) pair is covered exactly once; tasks with an empty
+// key range still write zero row sums for their slot.
+template <int NW, int NCB>
+__device__ __forceinline__ bool score_task(int w, int qq, int &ib, int &jlo, int &jhi, int &slot) {
+    if (NW == 8) {  // NCB == 2: (0,0) (1,0) (1,1), plus the empty (0, slot 1)
+        static_assert(NW != 8 || NCB == 2, "8-wave split expects 32-token chunks");
+        if (w >= 4 || qq > 0) return false;
+        ib = (w == 1 || w == 2) ? 1 : 0;
+        jlo = (w == 2) ? 1 : 0;
+        jhi = (w == 3) ? -1 : (w == 2 ? 1 : 0);
+        slot = (w >= 2) ? 1 : 0;
+        return true;
     }
+    constexpr int PER = NCB / NW;
+    if (qq >= PER) return false;
+    ib = w * PER + qq;
+    jlo = 0;
+    jhi = ib;
+    slot = 0;
+    return true;
 }
 
 template <int D, int MODE, bool FULL>
-__device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int t0, int valid, unsigned char *smem,
-                                           const bf16x8 (&wA)[WideCfg<D>::LB][WideCfg<D>::KSD],
+__device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int t0, int valid, int t_next,
+                                           int valid_next, unsigned char *smem, Prefetch<D> &pf,
                                            const float (&bl2)[WideCfg<D>::LB][4],
                                            f32x4 (&sacc)[WideCfg<D>::FBW][WideCfg<D>::VB],
                                            f32x4 (&zacc)[WideCfg<D>::ZB], int tid) {
     using K = WideCfg<D>;
     bf16_t *sPQ = reinterpret_cast<bf16_t *>(smem + K::OFF_PQ);
     bf16_t *sPK = reinterpret_cast<bf16_t *>(smem + K::OFF_PK);
-    bf16_t *sPKT = reinterpret_cast<bf16_t *>(smem + K::OFF_PKT);
-    bf16_t *sVT = reinterpret_cast<bf16_t *>(smem + K::OFF_VT);
+    bf16_t *sV = reinterpret_cast<bf16_t *>(smem + K::OFF_V);
     bf16_t *sA = reinterpret_cast<bf16_t *>(smem + K::OFF_A);
     float *sDen = reinterpret_cast<float *>(smem + K::OFF_DEN);
-    float *sX = reinterpret_cast<float *>(smem + K::OFF_PK);
+    float *sX = reinterpret_cast<float *>(smem + K::OFF_PQ);  // phi(q) is dead once the read-out is done
     const int w = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int th = w / K::NDQ, dq = w % K::NDQ;  // feature-map role
     const int fa = w / K::NN, nq = w % K::NN;     // state role: feature part, value part
 
-    // ---- phase 1: feature maps and V^T into LDS
-    if (MODE == WM_CAUSAL)
-        phi_chunk<D, true, FULL, true, true, true>(p.k + base, t0, valid, wA, bl2, th, dq, g, r16, sPK, sPKT);
-    if (MODE == WM_STATE)
-        phi_chunk<D, true, FULL, false, true, true>(p.k + base, t0, valid, wA, bl2, th, dq, g, r16, nullptr, sPKT);
-    if (MODE != WM_STATE)
-        phi_chunk<D, false, FULL, true, true, false>(p.q + base, t0, valid, wA, bl2, th, dq, g, r16, sPQ, nullptr);
-    if (MODE != WM_READOUT) v_chunk_to_lds<D, FULL>(p.v + base, t0, valid, tid, sVT);
+    // ---- phase 1: V and feature maps into LDS, then start loading the next chunk
+    bf16x8 wA[K::LB][K::KSD];
+    load_w_operands<D>(smem + K::OFF_W, dq, g, r16, wA);
+    if (MODE != WM_READOUT) {
+        constexpr int NC = D / 8;
+#pragma unroll
+        for (int it = 0; it < K::VPT; it++) {
+            const int t = tid + it * K::NT;
+            store8(sV + (t / NC) * K::RV + 8 * (t % NC), pf.vp[it]);
+        }
+        phi_chunk<D, true, FULL>(smem + K::OFF_XK, valid, wA, bl2, th, dq, g, r16, sPK, K::RK);
+    }
+    if (MODE != WM_STATE) phi_chunk<D, false, FULL>(smem + K::OFF_XQ, valid, wA, bl2, th, dq, g, r16, sPQ, K::RQ);
     __syncthreads();
+    // the staging tiles are free again: start moving the next chunk in
+    if (valid_next > 0) issue_loads<D, MODE>(pf, p, base, t_next, valid_next, w, lane, tid, smem);
 
-    f32x4 num[4][K::VB];
+    f32x4 num[K::NCB][K::VB];
     if (MODE != WM_STATE) {
         // ---- phase 2: intra-chunk scores, read-out against the carried state, denominators
         if (MODE == WM_CAUSAL) {
 #pragma unroll
-            for (int qq = 0; qq < (K::NW >= 4 ? 1 : 4 / K::NW); qq++) {
-                int ib, jlo, jhi, slot;
-                score_task<K::NW>(w, qq, ib, jlo, jhi, slot);
-                constexpr int MAXJ = K::NW == 8 ? 2 : 4;
+            for (int qq = 0; qq < K::NCB; qq++) {
+                int ib = 0, jlo = 0, jhi = -1, slot = 0;
+                if (!score_task<K::NW, K::NCB>(w, qq, ib, jlo, jhi, slot)) continue;
+                constexpr int MAXJ = K::NW == 8 ? 1 : K::NCB;
                 f32x4 a[MAXJ];
 #pragma unroll
                 for (int jj = 0; jj < MAXJ; jj++) a[jj] = zero4();
+                if (jlo <= jhi) {
 #pragma unroll
-                for (int ks = 0; ks < K::KSF; ks++) {
-                    const bf16x8 qb = load8(sPQ + (16 * ib + r16) * K::RQ + 32 * ks + 8 * g);
+                    for (int ks = 0; ks < K::KSF; ks++) {
+                        const bf16x8 qb = load8(sPQ + (16 * ib + r16) * K::RQ + 32 * ks + 8 * g);
 #pragma unroll
-                    for (int jj = 0; jj < MAXJ; jj++)
-                        if (jlo + jj <= jhi)
-                            a[jj] = mfma_bf16(load8(sPK + (16 * (jlo + jj) + r16) * K::RQ + 32 * ks + 8 * g), qb, a[jj]);
+                        for (int jj = 0; jj < MAXJ; jj++)
+                            if (jlo + jj <= jhi)
+                                a[jj] = mfma_bf16(load8(sPK + (16 * (jlo + jj) + r16) * K::RK + 32 * ks + 8 * g), qb,
+                                                  a[jj]);
+                    }
                 }
                 float rs = 0.0f;
 #pragma unroll
@@ -309,12 +387,12 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
                     }
                     const bf16x4 ab = to_bf16x4(av);
                     rs += ((float)ab[0] + (float)ab[1]) + ((float)ab[2] + (float)ab[3]);
-                    store4(sA + (16 * ib + r16) * K::RC + 16 * jb + 4 * g, ab);
+                    store4(sA + (16 * ib + r16) * K::RA + 16 * jb + 4 * g, ab);
                 }
-                if (jlo == 0 && (ib & 1) == 0) {  // the K step covering block ib also covers block ib + 1
+                if (jlo == 0 && (ib & 1) == 0 && ib + 1 < K::NCB) {  // the K step over block ib also covers ib + 1
                     bf16x4 zz;
                     zz[0] = zz[1] = zz[2] = zz[3] = (__bf16)0.0f;
-                    store4(sA + (16 * ib + r16) * K::RC + 16 * (ib + 1) + 4 * g, zz);
+                    store4(sA + (16 * ib + r16) * K::RA + 16 * (ib + 1) + 4 * g, zz);
                 }
                 rs += __shfl_xor(rs, 16);
                 rs += __shfl_xor(rs, 32);
@@ -322,7 +400,7 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
             }
         }
 #pragma unroll
-        for (int ib = 0; ib < 4; ib++)
+        for (int ib = 0; ib < K::NCB; ib++)
 #pragma unroll
             for (int vb = 0; vb < K::VB; vb++) num[ib][vb] = zero4();
 #pragma unroll
@@ -332,7 +410,7 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
 #pragma unroll
             for (int vb = 0; vb < K::VB; vb++) sb[vb] = acc_pair_to_operand(sacc[2 * kk][vb], sacc[2 * kk + 1][vb]);
 #pragma unroll
-            for (int ib = 0; ib < 4; ib++) {
+            for (int ib = 0; ib < K::NCB; ib++) {
                 const bf16x8 a = load8(sPQ + (16 * ib + r16) * K::RQ + 32 * ks + 8 * g);
 #pragma unroll
                 for (int vb = 0; vb < K::VB; vb++) num[ib][vb] = mfma_bf16(a, sb[vb], num[ib][vb]);
@@ -341,15 +419,15 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
         {  // partial denominators over this wave's z rows (K step w of the features)
             const bf16x8 zb = acc_pair_to_operand(zacc[0], zacc[1]);
 #pragma unroll
-            for (int ib = 0; ib < 4; ib++) {
+            for (int ib = 0; ib < K::NCB; ib++) {
                 const f32x4 dacc = mfma_bf16(load8(sPQ + (16 * ib + r16) * K::RQ + 32 * w + 8 * g), zb, zero4());
                 if (r16 == 0) *reinterpret_cast<f32x4 *>(sDen + w * K::C + 16 * ib + 4 * g) = dacc;
             }
         }
         if (K::NF == 2) {
-            __syncthreads();  // every wave is done with the phiK tile: reuse it for the exchange
+            __syncthreads();  // every wave is done with the phi(q) tile: reuse it for the exchange
 #pragma unroll
-            for (int ib = 0; ib < 4; ib++) {
+            for (int ib = 0; ib < K::NCB; ib++) {
                 if (ib / K::IBF == fa) continue;
 #pragma unroll
                 for (int vb = 0; vb < K::VB; vb++) {
@@ -363,18 +441,18 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
     __syncthreads();
 
     // ---- phase 3: exchange, intra-chunk product, output, state update
-    bf16x8 vop[2][K::VB];
+    bf16x8 vop[K::KSC][K::VB];
     if (MODE != WM_READOUT) {
+        const int lane_v = (8 * g + (r16 >> 2)) * K::RV + 4 * (r16 & 3) + 16 * nq * K::VB;
 #pragma unroll
-        for (int ks = 0; ks < 2; ks++)
+        for (int ks = 0; ks < K::KSC; ks++)
 #pragma unroll
-            for (int vb = 0; vb < K::VB; vb++)
-                vop[ks][vb] = load8(sVT + (16 * (nq * K::VB + vb) + r16) * K::RC + 32 * ks + 8 * g);
+            for (int vb = 0; vb < K::VB; vb++) vop[ks][vb] = operand_down_rows(sV, lane_v, 32 * ks * K::RV + 16 * vb, K::RV);
     }
     if (MODE != WM_STATE) {
         bf16_t *yb = p.y + base + (size_t)t0 * D;
 #pragma unroll
-        for (int ib = 0; ib < 4; ib++) {
+        for (int ib = 0; ib < K::NCB; ib++) {
             if (ib / K::IBF != fa) continue;  // rows finalised by the other feature part
             const int i0 = 16 * ib + 4 * g;
             if (K::NF == 2) {
@@ -388,7 +466,7 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
             if (MODE == WM_CAUSAL) {
 #pragma unroll
                 for (int ks = 0; ks <= ib / 2; ks++) {
-                    const bf16x8 a = load8(sA + (16 * ib + r16) * K::RC + 32 * ks + 8 * g);
+                    const bf16x8 a = load8(sA + (16 * ib + r16) * K::RA + 32 * ks + 8 * g);
 #pragma unroll
                     for (int vb = 0; vb < K::VB; vb++) num[ib][vb] = mfma_bf16(a, vop[ks][vb], num[ib][vb]);
                 }
@@ -411,22 +489,26 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
     }
     if (MODE != WM_READOUT) {
         const bf16x8 ones = ones_bf16x8();
+        // features of block k sit at perm_block_pos(k) + 8 q + r: lane q = r16 % 4 reads run q
+        const int lane_k = (8 * g + (r16 >> 2)) * K::RK + 8 * (r16 & 3);
+        const bf16_t *sPKf = sPK + perm_block_pos(fa * K::FBW);   // fa * FBW is even
+        const bf16_t *sPKz = sPK + perm_block_pos(w * K::ZB);     // w * ZB is even
 #pragma unroll
-        for (int fb = 0; fb < K::FBW; fb++)
+        for (int ks = 0; ks < K::KSC; ks++) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
-                const bf16x8 a = load8(sPKT + (16 * (fa * K::FBW + fb) + r16) * K::RC + 32 * ks + 8 * g);
+            for (int fb = 0; fb < K::FBW; fb++) {
+                const bf16x8 a = operand_down_rows(sPKf, lane_k, 32 * ks * K::RK + perm_block_pos(fb), K::RK);
 #pragma unroll
                 for (int vb = 0; vb < K::VB; vb++) sacc[fb][vb] = mfma_bf16(a, vop[ks][vb], sacc[fb][vb]);
             }
 #pragma unroll
-        for (int zb = 0; zb < K::ZB; zb++)
-#pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
-                const bf16x8 a = load8(sPKT + (16 * (w * K::ZB + zb) + r16) * K::RC + 32 * ks + 8 * g);
+            for (int zb = 0; zb < K::ZB; zb++) {
+                const bf16x8 a = operand_down_rows(sPKz, lane_k, 32 * ks * K::RK + perm_block_pos(zb), K::RK);
                 zacc[zb] = mfma_bf16(a, ones, zacc[zb]);
             }
+        }
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the next chunk's direct loads have landed in LDS
     __syncthreads();
 }
 
@@ -446,9 +528,12 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
     const int t_end = min(p.N, t_begin + p.seg_len);
     const size_t base = (size_t)bh * p.N * D;
 
-    bf16x8 wA[K::LB][K::KSD];
+    Prefetch<D> pf;
+    if (t_begin < t_end) issue_loads<D, MODE>(pf, p, base, t_begin, min(K::C, t_end - t_begin), w, lane, tid, smem);
+
     float bl2[K::LB][4];
-    load_directions<D>(p.W, p.b, h, dq, g, r16, wA, bl2);
+    load_bias<D>(p.b, h, dq, g, bl2);
+    stage_w<D>(p.W, h, tid, smem + K::OFF_W);
 
     // State: S[f][n] for feature blocks fa*FBW .. and this wave's value columns; z rows of
     // feature blocks w*ZB .. (every column of the z accumulator holds the same value).
@@ -464,22 +549,33 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
 #pragma unroll
         for (int fb = 0; fb < K::FBW; fb++)
 #pragma unroll
-            for (int vb = 0; vb < K::VB; vb++) {
-                const int n = 16 * (nq * K::VB + vb) + r16;
+            for (int vb = 0; vb < K::VB; vb++) sacc[fb][vb] = zero4();
 #pragma unroll
-                for (int r = 0; r < 4; r++)
-                    sacc[fb][vb][r] = Si ? Si[(size_t)(16 * (fa * K::FBW + fb) + 4 * g + r) * D + n] : 0.0f;
-            }
+        for (int zb = 0; zb < K::ZB; zb++) zacc[zb] = zero4();
+        if (Si) {
 #pragma unroll
-        for (int zb = 0; zb < K::ZB; zb++)
+            for (int fb = 0; fb < K::FBW; fb++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) zacc[zb][r] = zi ? zi[16 * (w * K::ZB + zb) + 4 * g + r] : 0.0f;
+                for (int vb = 0; vb < K::VB; vb++) {
+                    const int n = 16 * (nq * K::VB + vb) + r16;
+#pragma unroll
+                    for (int r = 0; r < 4; r++) sacc[fb][vb][r] = Si[(size_t)(16 * (fa * K::FBW + fb) + 4 * g + r) * D + n];
+                }
+#pragma unroll
+            for (int zb = 0; zb < K::ZB; zb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) zacc[zb][r] = zi[16 * (w * K::ZB + zb) + 4 * g + r];
+        }
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
     int t0 = t_begin;
-    for (; t0 + K::C <= t_end; t0 += K::C)
-        chunk_step<D, MODE, true>(p, base, t0, K::C, smem, wA, bl2, sacc, zacc, tid);
-    if (t0 < t_end) chunk_step<D, MODE, false>(p, base, t0, t_end - t0, smem, wA, bl2, sacc, zacc, tid);
+    for (; t0 + K::C <= t_end; t0 += K::C) {
+        const int t_next = t0 + K::C;
+        chunk_step<D, MODE, true>(p, base, t0, K::C, t_next, min(K::C, t_end - t_next), smem, pf, bl2, sacc, zacc, tid);
+    }
+    if (t0 < t_end) chunk_step<D, MODE, false>(p, base, t0, t_end - t0, t_end, 0, smem, pf, bl2, sacc, zacc, tid);
 
     // ---- segment end: publish the aggregate (STATE) or the final state (CAUSAL, last segment)
     float *So = nullptr, *zo = nullptr;
@@ -519,6 +615,7 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void fm_
                                                                         int cpw, int wg_per_bh) {
     using K = WideCfg<D>;
     __shared__ __attribute__((aligned(16))) bf16_t sPhi[K::C * K::RQ];
+    __shared__ __attribute__((aligned(16))) unsigned char sStage[K::SZ_X];
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int th = w / K::NDQ, dq = w % K::NDQ;
@@ -533,10 +630,10 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void fm_
         const int t0 = (part * cpw + c) * K::C;
         if (t0 >= N) break;
         const int valid = min(K::C, N - t0);
-        if (valid == K::C)
-            phi_chunk<D, false, true, true, false, false>(xh, t0, valid, wA, bl2, th, dq, g, r16, sPhi, nullptr);
-        else
-            phi_chunk<D, false, false, true, false, false>(xh, t0, valid, wA, bl2, th, dq, g, r16, sPhi, nullptr);
+        stage_x<D>(xh, t0, valid, w, lane, sStage);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        phi_chunk<D, false, true, false>(sStage, valid, wA, bl2, th, dq, g, r16, sPhi, K::RQ);
         __syncthreads();
         constexpr int P8 = K::DP / 8;
         for (int pi = tid; pi < K::C * P8; pi += K::NT) {
