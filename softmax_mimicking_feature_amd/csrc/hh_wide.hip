@@ -63,11 +63,11 @@ struct WideCfg {
     static constexpr int VPT = C * (D / 8) / NT;      // 16-byte pieces of V per thread and chunk
     // LDS tiles
     static constexpr int RQ = DP + 8;                 // phi(q) [C][RQ]: 16-byte row reads
-    static constexpr int RK = tr_stride(DP);          // phi(k) [C][RK]: row reads and transposing reads
+    static constexpr int RK = DP + 8;                 // phi(k) [C][RK]: row reads and transposing reads
     static constexpr int RV = tr_stride(D);           // V [C][RV]: transposing reads
     static constexpr int RA = C + 8;                  // intra scores A [C][RA]
-    static constexpr int XS = D + 4;                  // fp32 exchange tile [C][XS] (NF = 2), aliases phi(q)
-    static constexpr int SZ_PQ = (C * RQ * 2 > (NF == 2 ? C * XS * 4 : 0)) ? C * RQ * 2 : C * XS * 4;
+    static constexpr int XR = C + 4;                  // fp32 exchange tile [D][XR] (column-major, NF = 2), aliases phi(q)
+    static constexpr int SZ_PQ = (C * RQ * 2 > (NF == 2 ? D * XR * 4 : 0)) ? C * RQ * 2 : D * XR * 4;
     static constexpr int SZ_PK = C * RK * 2;
     // raw q / k of the next chunk, loaded straight from global memory into LDS: [C][D]
     // bf16, 16-byte granules of row r stored at granule index (g ^ (r % NSW))
@@ -129,8 +129,9 @@ __device__ __forceinline__ bf16x8 operand_down_rows(const bf16_t *tile, int lane
     return cat(lds_read_tr(p), lds_read_tr(p + 4 * stride));
 }
 
-// Physical position of the 16-feature block k's first column in a PERM feature tile
-// (columns of block k are at this position + 8 q + r for q = 0..3, r = 0..3 of each run).
+
+// Physical position of the 16-feature block k's first column in a permuted feature tile
+// (columns of block k are at this position + 8 q + r for q = 0..3, r = 0..3).
 __device__ __forceinline__ constexpr int perm_block_pos(int k) { return 32 * (k >> 1) + 4 * (k & 1); }
 
 // Loads of the next chunk, issued one chunk ahead: q and k go straight into LDS staging
@@ -432,8 +433,7 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
 #pragma unroll
                 for (int vb = 0; vb < K::VB; vb++) {
                     const int n = 16 * (nq * K::VB + vb) + r16;
-#pragma unroll
-                    for (int r = 0; r < 4; r++) sX[(16 * ib + 4 * g + r) * K::XS + n] = num[ib][vb][r];
+                    *reinterpret_cast<f32x4 *>(sX + n * K::XR + 16 * ib + 4 * g) = num[ib][vb];
                 }
             }
         }
@@ -459,8 +459,7 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
 #pragma unroll
                 for (int vb = 0; vb < K::VB; vb++) {
                     const int n = 16 * (nq * K::VB + vb) + r16;
-#pragma unroll
-                    for (int r = 0; r < 4; r++) num[ib][vb][r] += sX[(i0 + r) * K::XS + n];
+                    num[ib][vb] += *reinterpret_cast<const f32x4 *>(sX + n * K::XR + i0);
                 }
             }
             if (MODE == WM_CAUSAL) {
