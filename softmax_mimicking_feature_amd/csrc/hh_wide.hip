@@ -66,8 +66,8 @@ struct WideCfg {
     static constexpr int RK = DP + 8;                 // phi(k) [C][RK]: row reads and transposing reads
     static constexpr int RV = tr_stride(D);           // V [C][RV]: transposing reads
     static constexpr int RA = C + 8;                  // intra scores A [C][RA]
-    static constexpr int XR = C + 4;                  // fp32 exchange tile [D][XR] (column-major, NF = 2), aliases phi(q)
-    static constexpr int SZ_PQ = (C * RQ * 2 > (NF == 2 ? D * XR * 4 : 0)) ? C * RQ * 2 : D * XR * 4;
+    static constexpr int XS = D + 4;                  // fp32 exchange tile [C][XS] (NF = 2), aliases phi(q)
+    static constexpr int SZ_PQ = (C * RQ * 2 > (NF == 2 ? C * XS * 4 : 0)) ? C * RQ * 2 : C * XS * 4;
     static constexpr int SZ_PK = C * RK * 2;
     // raw q / k of the next chunk, loaded straight from global memory into LDS: [C][D]
     // bf16, 16-byte granules of row r stored at granule index (g ^ (r % NSW))
@@ -133,6 +133,37 @@ __device__ __forceinline__ bf16x8 operand_down_rows(const bf16_t *tile, int lane
 // Physical position of the 16-feature block k's first column in a permuted feature tile
 // (columns of block k are at this position + 8 q + r for q = 0..3, r = 0..3).
 __device__ __forceinline__ constexpr int perm_block_pos(int k) { return 32 * (k >> 1) + 4 * (k & 1); }
+
+// Value column held by MFMA column c (0..15) of value block vb of the wave with value part nq.
+// The VB blocks of a wave interleave in runs of four, so that a lane of a transposed
+// accumulator (rows = value columns 4 g .. 4 g + 3 of each block) holds the 4 VB contiguous
+// columns 16 VB nq + 4 VB g .. +4 VB - 1 of one token.  The V tile in LDS stores value column
+// value_col(nq, vb, c) at position 16 VB nq + 16 vb + c, so each block's operand is read from
+// 16 contiguous positions.
+template <int VB>
+__device__ __forceinline__ constexpr int value_col(int nq, int vb, int c) {
+    return 16 * VB * nq + 4 * VB * (c >> 2) + 4 * vb + (c & 3);
+}
+
+// Eight consecutive value columns n0 .. n0 + 7 (n0 % 8 == 0) of one token into row `row` of
+// the V tile, at the positions value_col implies.
+template <int VB>
+__device__ __forceinline__ void store_v8(bf16_t *row, int n0, const bf16x8 &v) {
+    if (VB == 1) {
+        store8(row + n0, v);
+    } else {  // VB == 2: columns 8 m .. 8 m + 7 of a 32-column group are runs m of blocks 0 and 1
+        const int grp = n0 & ~31, m = (n0 & 31) >> 3;
+        store4(row + grp + 4 * m, __builtin_shufflevector(v, v, 0, 1, 2, 3));
+        store4(row + grp + 16 + 4 * m, __builtin_shufflevector(v, v, 4, 5, 6, 7));
+    }
+}
+
+// Normalised outputs of one chunk kept in registers until the next chunk is under way, so
+// that the wait for the next chunk's loads does not also wait for these stores to retire.
+template <int D>
+struct PendingY {
+    bf16x4 v[WideCfg<D>::IBF][WideCfg<D>::VB];
+};
 
 // Loads of the next chunk, issued one chunk ahead: q and k go straight into LDS staging
 // tiles (global_load_lds), V into a few registers.
@@ -317,12 +348,31 @@ __device__ __forceinline__ bool score_task(int w, int qq, int &ib, int &jlo, int
     return true;
 }
 
+// Stores the normalised outputs of one chunk: lane (g, r16) holds token 16 ib + r16 of the
+// chunk, value columns value_col(nq, vb, 4 g + r) -- 4 VB contiguous values.
+template <int D, bool FULL>
+__device__ __forceinline__ void store_y(bf16_t *__restrict__ y, size_t base, int t0, int valid, const PendingY<D> &py,
+                                        int fa, int nq, int g, int r16) {
+    using K = WideCfg<D>;
+#pragma unroll
+    for (int ibo = 0; ibo < K::IBF; ibo++) {
+        const int i = 16 * (fa * K::IBF + ibo) + r16;
+        if (!FULL && i >= valid) continue;
+        bf16_t *dst = y + base + (size_t)(t0 + i) * D + value_col<K::VB>(nq, 0, 4 * g);
+        if (K::VB == 2)
+            store8(dst, cat(py.v[ibo][0], py.v[ibo][K::VB - 1]));
+        else
+            store4(dst, py.v[ibo][0]);
+    }
+}
+
 template <int D, int MODE, bool FULL>
 __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int t0, int valid, int t_next,
                                            int valid_next, unsigned char *smem, Prefetch<D> &pf,
                                            const float (&bl2)[WideCfg<D>::LB][4],
                                            f32x4 (&sacc)[WideCfg<D>::FBW][WideCfg<D>::VB],
-                                           f32x4 (&zacc)[WideCfg<D>::ZB], int tid) {
+                                           f32x4 (&zacc)[WideCfg<D>::ZB], PendingY<D> &py, int t_pending,
+                                           const bf16x8 (&wA)[WideCfg<D>::LB][WideCfg<D>::KSD], int tid) {
     using K = WideCfg<D>;
     bf16_t *sPQ = reinterpret_cast<bf16_t *>(smem + K::OFF_PQ);
     bf16_t *sPK = reinterpret_cast<bf16_t *>(smem + K::OFF_PK);
@@ -334,15 +384,16 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
     const int th = w / K::NDQ, dq = w % K::NDQ;  // feature-map role
     const int fa = w / K::NN, nq = w % K::NN;     // state role: feature part, value part
 
+    // outputs of the previous chunk
+    if (MODE != WM_STATE && t_pending >= 0) store_y<D, true>(p.y, base, t_pending, K::C, py, fa, nq, g, r16);
+
     // ---- phase 1: V and feature maps into LDS, then start loading the next chunk
-    bf16x8 wA[K::LB][K::KSD];
-    load_w_operands<D>(smem + K::OFF_W, dq, g, r16, wA);
     if (MODE != WM_READOUT) {
         constexpr int NC = D / 8;
 #pragma unroll
         for (int it = 0; it < K::VPT; it++) {
             const int t = tid + it * K::NT;
-            store8(sV + (t / NC) * K::RV + 8 * (t % NC), pf.vp[it]);
+            store_v8<K::VB>(sV + (t / NC) * K::RV, 8 * (t % NC), pf.vp[it]);
         }
         phi_chunk<D, true, FULL>(smem + K::OFF_XK, valid, wA, bl2, th, dq, g, r16, sPK, K::RK);
     }
@@ -351,7 +402,9 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
     // the staging tiles are free again: start moving the next chunk in
     if (valid_next > 0) issue_loads<D, MODE>(pf, p, base, t_next, valid_next, w, lane, tid, smem);
 
-    f32x4 num[K::NCB][K::VB];
+    // Read-out accumulators are transposed: numT[ib][vb] holds, in lane (g, r16), token
+    // 16 ib + r16 and value columns value_col(nq, vb, 4 g + r).
+    f32x4 numT[K::NCB][K::VB];
     if (MODE != WM_STATE) {
         // ---- phase 2: intra-chunk scores, read-out against the carried state, denominators
         if (MODE == WM_CAUSAL) {
@@ -403,7 +456,7 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
 #pragma unroll
         for (int ib = 0; ib < K::NCB; ib++)
 #pragma unroll
-            for (int vb = 0; vb < K::VB; vb++) num[ib][vb] = zero4();
+            for (int vb = 0; vb < K::VB; vb++) numT[ib][vb] = zero4();
 #pragma unroll
         for (int kk = 0; kk < K::KSW; kk++) {
             const int ks = fa * K::KSW + kk;
@@ -412,17 +465,17 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
             for (int vb = 0; vb < K::VB; vb++) sb[vb] = acc_pair_to_operand(sacc[2 * kk][vb], sacc[2 * kk + 1][vb]);
 #pragma unroll
             for (int ib = 0; ib < K::NCB; ib++) {
-                const bf16x8 a = load8(sPQ + (16 * ib + r16) * K::RQ + 32 * ks + 8 * g);
+                const bf16x8 qop = load8(sPQ + (16 * ib + r16) * K::RQ + 32 * ks + 8 * g);
 #pragma unroll
-                for (int vb = 0; vb < K::VB; vb++) num[ib][vb] = mfma_bf16(a, sb[vb], num[ib][vb]);
+                for (int vb = 0; vb < K::VB; vb++) numT[ib][vb] = mfma_bf16(sb[vb], qop, numT[ib][vb]);
             }
         }
         {  // partial denominators over this wave's z rows (K step w of the features)
             const bf16x8 zb = acc_pair_to_operand(zacc[0], zacc[1]);
 #pragma unroll
             for (int ib = 0; ib < K::NCB; ib++) {
-                const f32x4 dacc = mfma_bf16(load8(sPQ + (16 * ib + r16) * K::RQ + 32 * w + 8 * g), zb, zero4());
-                if (r16 == 0) *reinterpret_cast<f32x4 *>(sDen + w * K::C + 16 * ib + 4 * g) = dacc;
+                const f32x4 dacc = mfma_bf16(zb, load8(sPQ + (16 * ib + r16) * K::RQ + 32 * w + 8 * g), zero4());
+                if (g == 0) sDen[w * K::C + 16 * ib + r16] = dacc[0];
             }
         }
         if (K::NF == 2) {
@@ -431,16 +484,16 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
             for (int ib = 0; ib < K::NCB; ib++) {
                 if (ib / K::IBF == fa) continue;
 #pragma unroll
-                for (int vb = 0; vb < K::VB; vb++) {
-                    const int n = 16 * (nq * K::VB + vb) + r16;
-                    *reinterpret_cast<f32x4 *>(sX + n * K::XR + 16 * ib + 4 * g) = num[ib][vb];
-                }
+                for (int vb = 0; vb < K::VB; vb++)
+                    *reinterpret_cast<f32x4 *>(sX + (16 * ib + r16) * K::XS + value_col<K::VB>(nq, vb, 4 * g)) =
+                        numT[ib][vb];
             }
         }
     }
     __syncthreads();
 
     // ---- phase 3: exchange, intra-chunk product, output, state update
+    // V operands: lane column c <-> value column value_col(nq, vb, c), K = tokens
     bf16x8 vop[K::KSC][K::VB];
     if (MODE != WM_READOUT) {
         const int lane_v = (8 * g + (r16 >> 2)) * K::RV + 4 * (r16 & 3) + 16 * nq * K::VB;
@@ -450,41 +503,37 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
             for (int vb = 0; vb < K::VB; vb++) vop[ks][vb] = operand_down_rows(sV, lane_v, 32 * ks * K::RV + 16 * vb, K::RV);
     }
     if (MODE != WM_STATE) {
-        bf16_t *yb = p.y + base + (size_t)t0 * D;
 #pragma unroll
         for (int ib = 0; ib < K::NCB; ib++) {
             if (ib / K::IBF != fa) continue;  // rows finalised by the other feature part
-            const int i0 = 16 * ib + 4 * g;
+            const int i = 16 * ib + r16;
             if (K::NF == 2) {
 #pragma unroll
-                for (int vb = 0; vb < K::VB; vb++) {
-                    const int n = 16 * (nq * K::VB + vb) + r16;
-                    num[ib][vb] += *reinterpret_cast<const f32x4 *>(sX + n * K::XR + i0);
-                }
+                for (int vb = 0; vb < K::VB; vb++)
+                    numT[ib][vb] += *reinterpret_cast<const f32x4 *>(sX + i * K::XS + value_col<K::VB>(nq, vb, 4 * g));
             }
             if (MODE == WM_CAUSAL) {
 #pragma unroll
                 for (int ks = 0; ks <= ib / 2; ks++) {
-                    const bf16x8 a = load8(sA + (16 * ib + r16) * K::RA + 32 * ks + 8 * g);
+                    const bf16x8 a = load8(sA + i * K::RA + 32 * ks + 8 * g);
 #pragma unroll
-                    for (int vb = 0; vb < K::VB; vb++) num[ib][vb] = mfma_bf16(a, vop[ks][vb], num[ib][vb]);
+                    for (int vb = 0; vb < K::VB; vb++) numT[ib][vb] = mfma_bf16(vop[ks][vb], a, numT[ib][vb]);
                 }
             }
-            f32x4 den = zero4();
+            float den = 0.0f;
 #pragma unroll
-            for (int pw = 0; pw < K::NW + (MODE == WM_CAUSAL ? K::NJ : 0); pw++)
-                den += *reinterpret_cast<const f32x4 *>(sDen + pw * K::C + i0);
-            f32x4 rden;
-#pragma unroll
-            for (int r = 0; r < 4; r++) rden[r] = __builtin_amdgcn_rcpf(den[r]);
+            for (int pw = 0; pw < K::NW + (MODE == WM_CAUSAL ? K::NJ : 0); pw++) den += sDen[pw * K::C + i];
+            const float rden = __builtin_amdgcn_rcpf(den);
 #pragma unroll
             for (int vb = 0; vb < K::VB; vb++) {
-                const int n = 16 * (nq * K::VB + vb) + r16;
+                f32x4 o;
 #pragma unroll
-                for (int r = 0; r < 4; r++)
-                    if (FULL || i0 + r < valid) yb[(size_t)(i0 + r) * D + n] = float_to_bf16_bits(num[ib][vb][r] * rden[r]);
+                for (int r = 0; r < 4; r++) o[r] = numT[ib][vb][r] * rden;
+                py.v[ib % K::IBF][vb] = to_bf16x4(o);
             }
         }
+        // full chunks: stored during the next chunk; the last, partial chunk: now
+        if (!FULL) store_y<D, false>(p.y, base, t0, valid, py, fa, nq, g, r16);
     }
     if (MODE != WM_READOUT) {
         const bf16x8 ones = ones_bf16x8();
@@ -556,7 +605,7 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
             for (int fb = 0; fb < K::FBW; fb++)
 #pragma unroll
                 for (int vb = 0; vb < K::VB; vb++) {
-                    const int n = 16 * (nq * K::VB + vb) + r16;
+                    const int n = value_col<K::VB>(nq, vb, r16);
 #pragma unroll
                     for (int r = 0; r < 4; r++) sacc[fb][vb][r] = Si[(size_t)(16 * (fa * K::FBW + fb) + 4 * g + r) * D + n];
                 }
@@ -568,13 +617,23 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // this wave's directions stay in registers for the whole segment
+    bf16x8 wA[K::LB][K::KSD];
+    load_w_operands<D>(smem + K::OFF_W, dq, g, r16, wA);
 
+    PendingY<D> py;
     int t0 = t_begin;
     for (; t0 + K::C <= t_end; t0 += K::C) {
         const int t_next = t0 + K::C;
-        chunk_step<D, MODE, true>(p, base, t0, K::C, t_next, min(K::C, t_end - t_next), smem, pf, bl2, sacc, zacc, tid);
+        chunk_step<D, MODE, true>(p, base, t0, K::C, t_next, min(K::C, t_end - t_next), smem, pf, bl2, sacc, zacc, py,
+                                  t0 > t_begin ? t0 - K::C : -1, wA, tid);
     }
-    if (t0 < t_end) chunk_step<D, MODE, false>(p, base, t0, t_end - t0, t_end, 0, smem, pf, bl2, sacc, zacc, tid);
+    if (t0 < t_end) {
+        chunk_step<D, MODE, false>(p, base, t0, t_end - t0, t_end, 0, smem, pf, bl2, sacc, zacc, py,
+                                   t0 > t_begin ? t0 - K::C : -1, wA, tid);
+    } else if (MODE != WM_STATE && t0 > t_begin) {
+        store_y<D, true>(p.y, base, t0 - K::C, K::C, py, fa, nq, g, r16);
+    }
 
     // ---- segment end: publish the aggregate (STATE) or the final state (CAUSAL, last segment)
     float *So = nullptr, *zo = nullptr;
@@ -591,7 +650,7 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
         for (int fb = 0; fb < K::FBW; fb++)
 #pragma unroll
             for (int vb = 0; vb < K::VB; vb++) {
-                const int n = 16 * (nq * K::VB + vb) + r16;
+                const int n = value_col<K::VB>(nq, vb, r16);
 #pragma unroll
                 for (int r = 0; r < 4; r++) So[(size_t)(16 * (fa * K::FBW + fb) + 4 * g + r) * D + n] = sacc[fb][vb][r];
             }
