@@ -94,6 +94,9 @@ struct Plan {
     size_t ws_bytes = 0;
 };
 
+// Bytes of the bf16 S part of the wide kernels' segment slots (a multiple of 16).
+size_t wide_slot_S_bytes(long BH, long nseg, int d) { return (size_t)BH * nseg * 2 * d * d * sizeof(uint16_t); }
+
 Plan make_plan(int map, int dtype, int causal, long BH, long N, int d, bool has_S0) {
     Plan pl;
     if (dtype != HH_BF16 || N == 0) return pl;
@@ -113,7 +116,9 @@ Plan make_plan(int map, int dtype, int causal, long BH, long N, int d, bool has_
     if (!causal) pl.need_ws = true;
     else if (pl.nseg > 1) pl.need_ws = true;
     else if (pl.narrow && has_S0) pl.need_ws = true;  // S0 must be reordered into the internal rows
-    if (pl.need_ws) pl.ws_bytes = (size_t)BH * pl.nseg * ((size_t)pl.dpi * d + pl.dpi) * sizeof(float);
+    if (pl.need_ws)
+        pl.ws_bytes = pl.narrow ? (size_t)BH * pl.nseg * ((size_t)pl.dpi * d + pl.dpi) * sizeof(float)
+                                : wide_slot_S_bytes(BH, pl.nseg, d) + (size_t)BH * pl.nseg * pl.dpi * sizeof(float);
     return pl;
 }
 
@@ -285,22 +290,35 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
     const int out_mode = causal ? 1 : 2;
 
     if (!pl.narrow) {
+        // Segment slots: bf16 S in the kernels' register-image layout, fp32 z.  The scan between
+        // the passes never sees S0; a caller's S0 is read directly by every segment.
         hh::WideParams wp;
         memset(&wp, 0, sizeof wp);
         wp.q = (const hh::bf16_t *)q; wp.k = (const hh::bf16_t *)k; wp.v = (const hh::bf16_t *)v;
         wp.W = (const hh::bf16_t *)W; wp.b = (const hh::bf16_t *)b; wp.y = (hh::bf16_t *)y;
-        wp.S_ws = wsS; wp.z_ws = wsZ; wp.ws_bh_stride = slot_stride;
+        hh::bf16_t *slS = nullptr;
+        float *slZ = nullptr;
+        if (pl.need_ws) {
+            slS = reinterpret_cast<hh::bf16_t *>(workspace);
+            slZ = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + wide_slot_S_bytes(BH, pl.nseg, d));
+        }
+        wp.S_slots = slS; wp.z_slots = slZ; wp.slot_bh_stride = pl.nseg;
         wp.N = N; wp.H = H; wp.seg_len = pl.seg_len;
         if (run_state) {
             wp.nseg_grid = state_segments;
             e = hh::launch_wide(d, 0, wp, (int)(BH * state_segments), s);
             if (e != hipSuccess) return hip_fail(e, "segment-state launch");
+            if (pl.nseg > 1) {
+                e = hh::launch_slot_scan(d, slS, slZ, (int)BH, pl.nseg, causal ? 0 : 1, s);
+                if (e != hipSuccess) return hip_fail(e, "segment scan launch");
+            }
         }
-        if (run_prefix) {
-            e = hh::launch_prefix(pp, s);
-            if (e != hipSuccess) return hip_fail(e, "prefix launch");
+        if (causal) {
+            wp.slot_mode = pl.nseg > 1 ? 1 : 0;
+            wp.S_in = S0; wp.z_in = z0; wp.in_bh_stride = 1; wp.in_seg_stride = 0;
+        } else {
+            wp.slot_mode = 2;
         }
-        wp.S_in = S_in; wp.z_in = z_in; wp.in_bh_stride = in_bh; wp.in_seg_stride = in_seg;
         wp.S_out = S_out; wp.z_out = z_out;
         wp.nseg_grid = pl.nseg;
         e = hh::launch_wide(d, out_mode, wp, (int)(BH * pl.nseg), s);

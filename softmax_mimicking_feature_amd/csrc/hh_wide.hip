@@ -59,6 +59,7 @@ struct WideCfg {
     static constexpr int KSW = FBW / 2;               // read-out K steps per wave
     static constexpr int ZB = FB / NW;                // z-row blocks per wave
     static constexpr int IBF = NCB / NF;              // output row blocks finalised per wave
+    static constexpr int IMG8 = FBW * VB / 2;         // bf16x8 pieces of a segment slot per lane
     static constexpr int NJ = (NW == 8) ? 2 : 1;      // intra-chunk row-sum slots
     static constexpr int VPT = C * (D / 8) / NT;      // 16-byte pieces of V per thread and chunk
     // LDS tiles
@@ -585,6 +586,10 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
 
     // State: S[f][n] for feature blocks fa*FBW .. and this wave's value columns; z rows of
     // feature blocks w*ZB .. (every column of the z accumulator holds the same value).
+    // Segment slots in the workspace hold S in bf16 in the register image of this layout:
+    // accumulators k = fb VB + vb of lane `lane` in wave w are paired, the pair j = k / 2 being the
+    // bf16x8 at index (w IMG8 + j) 64 + lane, so that reading and writing a slot are whole 1 KB
+    // rows per instruction.
     f32x4 sacc[K::FBW][K::VB];
     f32x4 zacc[K::ZB];
     {
@@ -614,6 +619,30 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
 #pragma unroll
                 for (int r = 0; r < 4; r++) zacc[zb][r] = zi[16 * (w * K::ZB + zb) + 4 * g + r];
         }
+        int slot = -1;
+        if (MODE != WM_STATE && p.slot_mode == 1 && s > 0) slot = s;
+        if (MODE != WM_STATE && p.slot_mode == 2) slot = 0;
+        if (slot >= 0) {
+            const size_t sl = (size_t)bh * p.slot_bh_stride + slot;
+            const bf16x8 *img = reinterpret_cast<const bf16x8 *>(p.S_slots + sl * K::DP * D) + w * K::IMG8 * 64 + lane;
+            bf16x8 t[K::IMG8];
+#pragma unroll
+            for (int j = 0; j < K::IMG8; j++) t[j] = img[j * 64];
+            const float *zs = p.z_slots + sl * K::DP;
+#pragma unroll
+            for (int zb = 0; zb < K::ZB; zb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) zacc[zb][r] += zs[16 * (w * K::ZB + zb) + 4 * g + r];
+#pragma unroll
+            for (int j = 0; j < K::IMG8; j++) {
+                const int k0 = 2 * j, k1 = 2 * j + 1;
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    sacc[k0 / K::VB][k0 % K::VB][r] += (float)t[j][r];
+                    sacc[k1 / K::VB][k1 % K::VB][r] += (float)t[j][4 + r];
+                }
+            }
+        }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -635,13 +664,27 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
         store_y<D, true>(p.y, base, t0 - K::C, K::C, py, fa, nq, g, r16);
     }
 
-    // ---- segment end: publish the aggregate (STATE) or the final state (CAUSAL, last segment)
-    float *So = nullptr, *zo = nullptr;
+    // ---- segment end: publish the aggregate (STATE, register image) or the final state
+    //      (CAUSAL, last segment, feature-major)
     if (MODE == WM_STATE) {
-        const size_t slot = (size_t)bh * p.ws_bh_stride + s;
-        So = p.S_ws + slot * K::DP * D;
-        zo = p.z_ws + slot * K::DP;
-    } else if (MODE == WM_CAUSAL && p.S_out && s == p.nseg_grid - 1) {
+        const size_t slot = (size_t)bh * p.slot_bh_stride + s;
+        bf16x8 *img = reinterpret_cast<bf16x8 *>(p.S_slots + slot * K::DP * D) + w * K::IMG8 * 64 + lane;
+#pragma unroll
+        for (int j = 0; j < K::IMG8; j++) {
+            const int k0 = 2 * j, k1 = 2 * j + 1;
+            img[j * 64] = cat(to_bf16x4(sacc[k0 / K::VB][k0 % K::VB]), to_bf16x4(sacc[k1 / K::VB][k1 % K::VB]));
+        }
+        float *zs = p.z_slots + slot * K::DP;
+        if (r16 == 0) {
+#pragma unroll
+            for (int zb = 0; zb < K::ZB; zb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) zs[16 * (w * K::ZB + zb) + 4 * g + r] = zacc[zb][r];
+        }
+        return;
+    }
+    float *So = nullptr, *zo = nullptr;
+    if (MODE == WM_CAUSAL && p.S_out && s == p.nseg_grid - 1) {
         So = p.S_out + (size_t)bh * K::DP * D;
         zo = p.z_out + (size_t)bh * K::DP;
     }
@@ -726,6 +769,59 @@ hipError_t launch_featuremap_hedgehog_bf16(int d, const bf16_t *x, const bf16_t 
     case 128: return launch_fm_d<128>(x, W, b, phi, BH, H, N, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+// Segment-slot scan (see launch_slot_scan): one thread per 8 bf16 of S or per z entry.
+template <int D>
+__global__ void slot_scan_kernel(bf16_t *__restrict__ S, float *__restrict__ z, int BH, int nseg, int mode) {
+    constexpr long PS = 2L * D * D / 8, PZ = 2L * D;
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long)BH * (PS + PZ)) return;
+    const long bh = idx / (PS + PZ), e = idx % (PS + PZ);
+    if (e < PS) {
+        constexpr long stride = 2L * D * D;
+        bf16_t *base = S + bh * nseg * stride + 8 * e;
+        float run[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        const int nin = mode == 0 ? nseg - 1 : nseg;
+        for (int s = 0; s < nin; s++) {
+            const bf16x8 a = load8(base + s * stride);
+            if (mode == 0 && s > 0) {
+                bf16x8 o;
+#pragma unroll
+                for (int i = 0; i < 8; i++) o[i] = (__bf16)run[i];
+                store8(base + s * stride, o);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) run[i] += (float)a[i];
+        }
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 8; i++) o[i] = (__bf16)run[i];
+        store8(base + (mode == 0 ? (long)(nseg - 1) * stride : 0), o);
+    } else {
+        float *base = z + bh * nseg * PZ + (e - PS);
+        float run = 0.0f;
+        const int nin = mode == 0 ? nseg - 1 : nseg;
+        for (int s = 0; s < nin; s++) {
+            const float a = base[s * PZ];
+            if (mode == 0 && s > 0) base[s * PZ] = run;
+            run += a;
+        }
+        base[mode == 0 ? (long)(nseg - 1) * PZ : 0] = run;
+    }
+}
+
+hipError_t launch_slot_scan(int d, bf16_t *S_slots, float *z_slots, int BH, int nseg, int mode, hipStream_t st) {
+    const long total = (long)BH * (2L * d * d / 8 + 2L * d);
+    const unsigned grid = (unsigned)((total + 255) / 256);
+    switch (d) {
+    case 16: hipLaunchKernelGGL(slot_scan_kernel<16>, dim3(grid), dim3(256), 0, st, S_slots, z_slots, BH, nseg, mode); break;
+    case 32: hipLaunchKernelGGL(slot_scan_kernel<32>, dim3(grid), dim3(256), 0, st, S_slots, z_slots, BH, nseg, mode); break;
+    case 64: hipLaunchKernelGGL(slot_scan_kernel<64>, dim3(grid), dim3(256), 0, st, S_slots, z_slots, BH, nseg, mode); break;
+    case 128: hipLaunchKernelGGL(slot_scan_kernel<128>, dim3(grid), dim3(256), 0, st, S_slots, z_slots, BH, nseg, mode); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <int D>

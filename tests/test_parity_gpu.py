@@ -243,6 +243,27 @@ def test_many_segments_and_resume(name):
     assert_close(host(y), yo, rtol, atol, "whole y")
 
 
+@pytest.mark.parametrize("d,B,H", [(128, 2, 16), (64, 4, 16)])
+def test_resume_few_segments(d, B, H):
+    # enough heads that each sequence is cut into only a few segments, each of which sums its
+    # predecessors' aggregates on top of the caller's initial state
+    w = small("c3_llama2_causal", B=B, H=H, N=2048, d=d, w_std=d ** -0.5, seed=9200 + d)
+    say(f"resume, few segments d={d} B={B} H={H}")
+    x = wl.make_inputs(w)
+    n1 = 700
+    x1 = {k_: (a[:, :, :n1] if k_ in "qkv" else a) for k_, a in x.items()}
+    x2 = {k_: (a[:, :, n1:] if k_ in "qkv" else a) for k_, a in x.items()}
+    yo, So, zo = oracle_fwd(w, x, want_state=True)
+    _, S1, z1 = oracle_fwd(w.replace(N=n1), x1, want_state=True)
+    y2, S2, z2 = run_fwd(w.replace(N=w.N - n1), x2, S0=S1, z0=z1, want_state=True)
+    rtol, atol = wl.tolerance(w.dtype)
+    assert_close(host(y2), yo[:, :, n1:], rtol, atol, "resumed y")
+    sr, sa = state_tol(w, So)
+    assert_close(host(S2), So, sr, sa, "resumed S_out")
+    zr, za = state_tol(w, zo)
+    assert_close(host(z2), zo, zr, za, "resumed z_out")
+
+
 def test_empty_sequence_returns_initial_state():
     m = hh()
     w = small("c3_llama2_causal", B=1, H=2, N=0, d=64)
