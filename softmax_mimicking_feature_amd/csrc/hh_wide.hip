@@ -63,8 +63,12 @@ struct WideCfg {
     static constexpr int NJ = (NW == 8) ? 2 : 1;      // intra-chunk row-sum slots
     static constexpr int VPT = C * (D / 8) / NT;      // 16-byte pieces of V per thread and chunk
     // LDS tiles
-    static constexpr int RQ = DP + 8;                 // phi(q) [C][RQ]: 16-byte row reads
-    static constexpr int RK = DP + 8;                 // phi(k) [C][RK]: row reads and transposing reads
+    // Row strides of the feature tiles, chosen for the LDS bank mapping of gfx950 (measured):
+    // 16-byte reads of 16 rows x 4 column blocks are conflict-free when the row pitch is 32
+    // (mod 256) bytes; 8-byte writes of that shape and transposing reads with 16-byte-spaced
+    // runs are conflict-free when it is an odd multiple of 8 bytes (mod 256).
+    static constexpr int RQ = DP + 16;                // phi(q) [C][RQ]: 16-byte row reads and writes
+    static constexpr int RK = DP + 12;                // phi(k) [C][RK]: 8-byte row reads, transposing reads
     static constexpr int RV = tr_stride(D);           // V [C][RV]: transposing reads
     static constexpr int RA = C + 8;                  // intra scores A [C][RA]
     static constexpr int XS = D + 4;                  // fp32 exchange tile [C][XS] (NF = 2), aliases phi(q)
@@ -73,7 +77,7 @@ struct WideCfg {
     // raw q / k of the next chunk, loaded straight from global memory into LDS: [C][D]
     // bf16, 16-byte granules of row r stored at granule index (g ^ (r % NSW))
     static constexpr int NG = D / 8;                  // 16-byte granules per row
-    static constexpr int NSW = NG < 8 ? NG : 8;
+    static constexpr int NSW = NG < 8 ? NG : 8;       // XOR swizzle period (rows of fewer than 16 granules)
     static constexpr int SZ_X = C * D * 2;
     static constexpr int XBLK = SZ_X / 1024;          // 1 KB direct-load blocks per tile
     static constexpr int OFF_PQ = 0;
@@ -111,6 +115,9 @@ __device__ __forceinline__ int feat_pos(int f0) {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
+// 16 bytes from an 8-byte-aligned LDS address, as two 8-byte reads.
+__device__ __forceinline__ bf16x8 load8_as_halves(const bf16_t *p) { return cat(load4(p), load4(p + 4)); }
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
 // receives, in slot s, element (i % 4) of the 4-element run addressed by lane 4 s + i / 4.
 // Pointing lane i of a group at row (r0 + i / 4), columns (c0 + 4 (i % 4)) .. +3 of a
@@ -134,6 +141,23 @@ __device__ __forceinline__ bf16x8 operand_down_rows(const bf16_t *tile, int lane
 // Physical position of the 16-feature block k's first column in a permuted feature tile
 // (columns of block k are at this position + 8 q + r for q = 0..3, r = 0..3).
 __device__ __forceinline__ constexpr int perm_block_pos(int k) { return 32 * (k >> 1) + 4 * (k & 1); }
+
+// Stored position of 16-byte granule G of row r in a [rows][D] bf16 staging tile, and its
+// inverse.  256-byte rows are rotated by 2 r granules, so that 16 rows x 4 consecutive
+// granules read together fall on the bank pattern of a 32-byte row pitch; shorter rows are
+// XOR-swizzled.
+template <int D>
+__device__ __forceinline__ int stage_pos(int r, int G) {
+    constexpr int NG = D / 8, NSW = NG < 8 ? NG : 8;
+    if (NG == 16) return (G + 2 * r) & 15;
+    return G ^ (r % NSW);
+}
+template <int D>
+__device__ __forceinline__ int stage_granule(int r, int P) {
+    constexpr int NG = D / 8, NSW = NG < 8 ? NG : 8;
+    if (NG == 16) return (P - 2 * r) & 15;
+    return P ^ (r % NSW);
+}
 
 // Value column held by MFMA column c (0..15) of value block vb of the wave with value part nq.
 // The VB blocks of a wave interleave in runs of four, so that a lane of a transposed
@@ -179,8 +203,8 @@ __device__ __forceinline__ void load_to_lds_16(const void *gsrc, void *lds_dst_u
 }
 
 // One [C][D] tile of x into its staging area: wave w moves blocks w, w + NW, ...; lane l of
-// block b lands at slot 64 b + l = (row r, stored granule G), which holds granule G ^ (r % NSW).
-// Rows past the end read a valid row (their values are never used).
+// block b lands at slot 64 b + l = (row r, stored position P), which holds granule
+// stage_granule(r, P).  Rows past the end read a valid row (their values are never used).
 template <int D>
 __device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, int t0, int valid, int w, int lane,
                                         unsigned char *stage) {
@@ -189,8 +213,8 @@ __device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, int t0, in
     for (int bb = 0; bb < K::XBLK / K::NW; bb++) {
         const int blk = w + bb * K::NW;
         const int slot = 64 * blk + lane;
-        const int r = slot / K::NG, G = slot % K::NG;
-        const int kg = G ^ (r % K::NSW);
+        const int r = slot / K::NG, P = slot % K::NG;
+        const int kg = stage_granule<D>(r, P);
         const int rr = r < valid ? r : 0;
         load_to_lds_16(x + (size_t)(t0 + rr) * D + 8 * kg, stage + 1024 * blk);
     }
@@ -220,7 +244,7 @@ __device__ __forceinline__ bf16x8 staged_x_operand(const unsigned char *stage, i
     using K = WideCfg<D>;
     const int kg = 4 * ks + g;
     if (8 * kg >= D) return zero_bf16x8();
-    return *reinterpret_cast<const bf16x8 *>(stage + 16 * (i * K::NG + (kg ^ (i % K::NSW))));
+    return *reinterpret_cast<const bf16x8 *>(stage + 16 * (i * K::NG + stage_pos<D>(i, kg)));
 }
 
 // Feature map of one chunk for this wave's directions and token blocks from prefetched x,
@@ -237,13 +261,17 @@ __device__ __forceinline__ void phi_chunk(const unsigned char *stage, int valid,
         bf16x8 xb[K::KSD];
 #pragma unroll
         for (int ks = 0; ks < K::KSD; ks++) xb[ks] = staged_x_operand<D>(stage, i, ks, g);
+        // With PERM, direction blocks 2 j and 2 j + 1 of a lane land in one 16-byte run
+        // (positions 8 g .. 8 g + 7 of their 32-feature group): write them together where the
+        // tile pitch allows 16-byte stores.
+        constexpr bool PAIR = PERM && !IS_KEY && K::LB % 2 == 0;
+        bf16x4 pe[K::LB], ne[K::LB];
 #pragma unroll
         for (int mb = 0; mb < K::LB; mb++) {
             f32x4 a = zero4();
 #pragma unroll
             for (int ks = 0; ks < K::KSD; ks++) a = mfma_bf16(wA[mb][ks], xb[ks], a);
             // a: lane holds u for token i and directions fb4 .. fb4 + 3
-            const int fb4 = dq * K::DPW + 16 * mb + 4 * g;
             f32x4 ep, en;
 #pragma unroll
             for (int r = 0; r < 4; r++) {
@@ -255,8 +283,21 @@ __device__ __forceinline__ void phi_chunk(const unsigned char *stage, int valid,
                 ep = zero4();
                 en = zero4();
             }
-            store4(sRow + i * stride + feat_pos<PERM>(fb4), to_bf16x4(ep));
-            store4(sRow + i * stride + feat_pos<PERM>(D + fb4), to_bf16x4(en));
+            pe[mb] = to_bf16x4(ep);
+            ne[mb] = to_bf16x4(en);
+        }
+#pragma unroll
+        for (int mb = 0; mb < K::LB; mb++) {
+            const int fb4 = dq * K::DPW + 16 * mb + 4 * g;
+            if (PAIR) {
+                if (mb % 2 == 0) {
+                    store8(sRow + i * stride + feat_pos<PERM>(fb4), cat(pe[mb], pe[mb + 1]));
+                    store8(sRow + i * stride + feat_pos<PERM>(D + fb4), cat(ne[mb], ne[mb + 1]));
+                }
+            } else {
+                store4(sRow + i * stride + feat_pos<PERM>(fb4), pe[mb]);
+                store4(sRow + i * stride + feat_pos<PERM>(D + fb4), ne[mb]);
+            }
         }
     }
 }
@@ -293,7 +334,7 @@ __device__ __forceinline__ void stage_w(const bf16_t *__restrict__ W, int h, int
     const bf16_t *Wh = W + (size_t)h * D * D;
     for (int t = tid; t < D * K::NG; t += K::NT) {
         const int l = t / K::NG, kg = t % K::NG;
-        *reinterpret_cast<bf16x8 *>(sW + 16 * (l * K::NG + (kg ^ (l % K::NSW)))) = load8(Wh + (size_t)l * D + 8 * kg);
+        *reinterpret_cast<bf16x8 *>(sW + 16 * (l * K::NG + stage_pos<D>(l, kg))) = load8(Wh + (size_t)l * D + 8 * kg);
     }
 }
 
@@ -308,7 +349,7 @@ __device__ __forceinline__ void load_w_operands(const unsigned char *sW, int dq,
 #pragma unroll
         for (int ks = 0; ks < K::KSD; ks++) {
             const int kg = 4 * ks + g;
-            wA[mb][ks] = (8 * kg < D) ? *reinterpret_cast<const bf16x8 *>(sW + 16 * (l * K::NG + (kg ^ (l % K::NSW))))
+            wA[mb][ks] = (8 * kg < D) ? *reinterpret_cast<const bf16x8 *>(sW + 16 * (l * K::NG + stage_pos<D>(l, kg)))
                                       : zero_bf16x8();
         }
     }
@@ -424,8 +465,8 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
 #pragma unroll
                         for (int jj = 0; jj < MAXJ; jj++)
                             if (jlo + jj <= jhi)
-                                a[jj] = mfma_bf16(load8(sPK + (16 * (jlo + jj) + r16) * K::RK + 32 * ks + 8 * g), qb,
-                                                  a[jj]);
+                                a[jj] = mfma_bf16(load8_as_halves(sPK + (16 * (jlo + jj) + r16) * K::RK + 32 * ks + 8 * g),
+                                                  qb, a[jj]);
                     }
                 }
                 float rs = 0.0f;
