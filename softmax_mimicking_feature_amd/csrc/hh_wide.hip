@@ -34,9 +34,9 @@ namespace hh {
 // disjoint banks.
 constexpr int tr_stride(int n) { return n + ((((32 - 2 * n) % 128) + 128) % 128) / 2; }
 
-template <int D>
+template <int D, int C_ = 64>
 struct WideCfg {
-    static constexpr int C = D == 128 ? 32 : 64;      // tokens per chunk
+    static constexpr int C = C_;                      // tokens per chunk
     static constexpr int NCB = C / 16;                // 16-token blocks per chunk
     static constexpr int KSC = C / 32;                // 32-wide K steps over the chunk's tokens
     static constexpr int NW = D == 128 ? 8 : (D == 64 ? 4 : D / 16);  // waves per workgroup
@@ -87,14 +87,16 @@ struct WideCfg {
     static constexpr int OFF_DEN = OFF_A + C * RA * 2;
     static constexpr int OFF_XQ = OFF_DEN + (NW + NJ) * C * 4;
     static constexpr int OFF_XK = OFF_XQ + SZ_X;
-    // per-head W as MFMA A operands, [D rows][D] bf16 with granule swizzle like the x tiles
-    static constexpr int OFF_W = OFF_XK + SZ_X;
-    static constexpr int LDS_BYTES = OFF_W + D * D * 2;
+    // per-head W, [D rows][D] bf16 with granule swizzle like the x tiles: only read once into
+    // registers before the first chunk, so it shares the feature tiles' space
+    static constexpr int OFF_W = OFF_PQ;
+    static constexpr int LDS_BYTES = OFF_XK + SZ_X;
     static constexpr int MIN_WG_PER_CU = NW == 8 ? 1 : 2;
     static_assert(ZB == 2, "each wave owns one K step of z rows");
     static_assert(VB >= 1 && LB >= 1 && IBT >= 1 && IBF >= 1 && FBW % 2 == 0, "bad wave split");
     static_assert(VPT >= 1 && C * (D / 8) % NT == 0, "every lane moves whole V pieces");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(D * D * 2 <= SZ_PQ + SZ_PK, "W fits in the feature tiles");
     static_assert(SZ_X % 1024 == 0 && XBLK % NW == 0, "direct loads: whole 1 KB blocks, the same count per wave");
 };
 
@@ -185,16 +187,16 @@ __device__ __forceinline__ void store_v8(bf16_t *row, int n0, const bf16x8 &v) {
 
 // Normalised outputs of one chunk kept in registers until the next chunk is under way, so
 // that the wait for the next chunk's loads does not also wait for these stores to retire.
-template <int D>
+template <int D, int C>
 struct PendingY {
-    bf16x4 v[WideCfg<D>::IBF][WideCfg<D>::VB];
+    bf16x4 v[WideCfg<D, C>::IBF][WideCfg<D, C>::VB];
 };
 
 // Loads of the next chunk, issued one chunk ahead: q and k go straight into LDS staging
 // tiles (global_load_lds), V into a few registers.
-template <int D>
+template <int D, int C>
 struct Prefetch {
-    bf16x8 vp[WideCfg<D>::VPT];
+    bf16x8 vp[WideCfg<D, C>::VPT];
 };
 
 __device__ __forceinline__ void load_to_lds_16(const void *gsrc, void *lds_dst_uniform) {
@@ -205,10 +207,10 @@ __device__ __forceinline__ void load_to_lds_16(const void *gsrc, void *lds_dst_u
 // One [C][D] tile of x into its staging area: wave w moves blocks w, w + NW, ...; lane l of
 // block b lands at slot 64 b + l = (row r, stored position P), which holds granule
 // stage_granule(r, P).  Rows past the end read a valid row (their values are never used).
-template <int D>
+template <int D, int C>
 __device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, int t0, int valid, int w, int lane,
                                         unsigned char *stage) {
-    using K = WideCfg<D>;
+    using K = WideCfg<D, C>;
 #pragma unroll
     for (int bb = 0; bb < K::XBLK / K::NW; bb++) {
         const int blk = w + bb * K::NW;
@@ -220,13 +222,13 @@ __device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, int t0, in
     }
 }
 
-template <int D, int MODE>
-__device__ __forceinline__ void issue_loads(Prefetch<D> &pf, const WideParams &p, size_t base, int t0, int valid,
+template <int D, int C, int MODE>
+__device__ __forceinline__ void issue_loads(Prefetch<D, C> &pf, const WideParams &p, size_t base, int t0, int valid,
                                             int w, int lane, int tid, unsigned char *smem) {
-    using K = WideCfg<D>;
-    if (MODE != WM_STATE) stage_x<D>(p.q + base, t0, valid, w, lane, smem + K::OFF_XQ);
+    using K = WideCfg<D, C>;
+    if (MODE != WM_STATE) stage_x<D, C>(p.q + base, t0, valid, w, lane, smem + K::OFF_XQ);
     if (MODE != WM_READOUT) {
-        stage_x<D>(p.k + base, t0, valid, w, lane, smem + K::OFF_XK);
+        stage_x<D, C>(p.k + base, t0, valid, w, lane, smem + K::OFF_XK);
         constexpr int NC = D / 8;
 #pragma unroll
         for (int it = 0; it < K::VPT; it++) {
@@ -249,12 +251,12 @@ __device__ __forceinline__ bf16x8 staged_x_operand(const unsigned char *stage, i
 
 // Feature map of one chunk for this wave's directions and token blocks from prefetched x,
 // written row-major (features contiguous, position feat_pos) into LDS.
-template <int D, bool IS_KEY, bool FULL, bool PERM = true>
+template <int D, int C, bool IS_KEY, bool FULL, bool PERM = true>
 __device__ __forceinline__ void phi_chunk(const unsigned char *stage, int valid,
                                           const bf16x8 (&wA)[WideCfg<D>::LB][WideCfg<D>::KSD],
                                           const float (&bl2)[WideCfg<D>::LB][4], int th, int dq, int g, int r16,
                                           bf16_t *sRow, int stride) {
-    using K = WideCfg<D>;
+    using K = WideCfg<D, C>;
 #pragma unroll
     for (int ibl = 0; ibl < K::IBT; ibl++) {
         const int i = 16 * (th * K::IBT + ibl) + r16;
@@ -372,13 +374,27 @@ __device__ __forceinline__ void load_bias(const bf16_t *__restrict__ b, int h, i
 // key range still write zero row sums for their slot.
 template <int NW, int NCB>
 __device__ __forceinline__ bool score_task(int w, int qq, int &ib, int &jlo, int &jhi, int &slot) {
-    if (NW == 8) {  // NCB == 2: (0,0) (1,0) (1,1), plus the empty (0, slot 1)
-        static_assert(NW != 8 || NCB == 2, "8-wave split expects 32-token chunks");
+    if (NW == 8 && NCB == 2) {  // (0,0) (1,0) (1,1), plus the empty (0, slot 1)
         if (w >= 4 || qq > 0) return false;
         ib = (w == 1 || w == 2) ? 1 : 0;
         jlo = (w == 2) ? 1 : 0;
         jhi = (w == 3) ? -1 : (w == 2 ? 1 : 0);
         slot = (w >= 2) ? 1 : 0;
+        return true;
+    }
+    if (NW == 8) {
+        // NCB == 4: the 10 (query, key) block pairs in tasks of one or two pairs, balanced over
+        // the SIMDs (waves w and w + 4 share one); waves 6 and 7 only clear row-sum slots.
+        static_assert(NW != 8 || NCB == 4 || NCB == 2, "8-wave split expects 32- or 64-token chunks");
+        constexpr int T_IB[8] = {0, 1, 2, 3, 3, 2, 0, 1};
+        constexpr int T_LO[8] = {0, 0, 0, 2, 0, 2, 0, 0};
+        constexpr int T_HI[8] = {0, 1, 1, 3, 1, 2, -1, -1};
+        constexpr int T_SL[8] = {0, 0, 0, 1, 0, 1, 1, 1};
+        if (qq > 0) return false;
+        ib = T_IB[w];
+        jlo = T_LO[w];
+        jhi = T_HI[w];
+        slot = T_SL[w];
         return true;
     }
     constexpr int PER = NCB / NW;
@@ -392,10 +408,10 @@ __device__ __forceinline__ bool score_task(int w, int qq, int &ib, int &jlo, int
 
 // Stores the normalised outputs of one chunk: lane (g, r16) holds token 16 ib + r16 of the
 // chunk, value columns value_col(nq, vb, 4 g + r) -- 4 VB contiguous values.
-template <int D, bool FULL>
-__device__ __forceinline__ void store_y(bf16_t *__restrict__ y, size_t base, int t0, int valid, const PendingY<D> &py,
+template <int D, int C, bool FULL>
+__device__ __forceinline__ void store_y(bf16_t *__restrict__ y, size_t base, int t0, int valid, const PendingY<D, C> &py,
                                         int fa, int nq, int g, int r16) {
-    using K = WideCfg<D>;
+    using K = WideCfg<D, C>;
 #pragma unroll
     for (int ibo = 0; ibo < K::IBF; ibo++) {
         const int i = 16 * (fa * K::IBF + ibo) + r16;
@@ -408,14 +424,14 @@ __device__ __forceinline__ void store_y(bf16_t *__restrict__ y, size_t base, int
     }
 }
 
-template <int D, int MODE, bool FULL>
+template <int D, int C, int MODE, bool FULL>
 __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int t0, int valid, int t_next,
-                                           int valid_next, unsigned char *smem, Prefetch<D> &pf,
+                                           int valid_next, unsigned char *smem, Prefetch<D, C> &pf,
                                            const float (&bl2)[WideCfg<D>::LB][4],
                                            f32x4 (&sacc)[WideCfg<D>::FBW][WideCfg<D>::VB],
-                                           f32x4 (&zacc)[WideCfg<D>::ZB], PendingY<D> &py, int t_pending,
+                                           f32x4 (&zacc)[WideCfg<D>::ZB], PendingY<D, C> &py, int t_pending,
                                            const bf16x8 (&wA)[WideCfg<D>::LB][WideCfg<D>::KSD], int tid) {
-    using K = WideCfg<D>;
+    using K = WideCfg<D, C>;
     bf16_t *sPQ = reinterpret_cast<bf16_t *>(smem + K::OFF_PQ);
     bf16_t *sPK = reinterpret_cast<bf16_t *>(smem + K::OFF_PK);
     bf16_t *sV = reinterpret_cast<bf16_t *>(smem + K::OFF_V);
@@ -427,7 +443,7 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
     const int fa = w / K::NN, nq = w % K::NN;     // state role: feature part, value part
 
     // outputs of the previous chunk
-    if (MODE != WM_STATE && t_pending >= 0) store_y<D, true>(p.y, base, t_pending, K::C, py, fa, nq, g, r16);
+    if (MODE != WM_STATE && t_pending >= 0) store_y<D, C, true>(p.y, base, t_pending, K::C, py, fa, nq, g, r16);
 
     // ---- phase 1: V and feature maps into LDS, then start loading the next chunk
     if (MODE != WM_READOUT) {
@@ -437,12 +453,12 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
             const int t = tid + it * K::NT;
             store_v8<K::VB>(sV + (t / NC) * K::RV, 8 * (t % NC), pf.vp[it]);
         }
-        phi_chunk<D, true, FULL>(smem + K::OFF_XK, valid, wA, bl2, th, dq, g, r16, sPK, K::RK);
+        phi_chunk<D, C, true, FULL>(smem + K::OFF_XK, valid, wA, bl2, th, dq, g, r16, sPK, K::RK);
     }
-    if (MODE != WM_STATE) phi_chunk<D, false, FULL>(smem + K::OFF_XQ, valid, wA, bl2, th, dq, g, r16, sPQ, K::RQ);
+    if (MODE != WM_STATE) phi_chunk<D, C, false, FULL>(smem + K::OFF_XQ, valid, wA, bl2, th, dq, g, r16, sPQ, K::RQ);
     __syncthreads();
     // the staging tiles are free again: start moving the next chunk in
-    if (valid_next > 0) issue_loads<D, MODE>(pf, p, base, t_next, valid_next, w, lane, tid, smem);
+    if (valid_next > 0) issue_loads<D, C, MODE>(pf, p, base, t_next, valid_next, w, lane, tid, smem);
 
     // Read-out accumulators are transposed: numT[ib][vb] holds, in lane (g, r16), token
     // 16 ib + r16 and value columns value_col(nq, vb, 4 g + r).
@@ -454,7 +470,7 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
             for (int qq = 0; qq < K::NCB; qq++) {
                 int ib = 0, jlo = 0, jhi = -1, slot = 0;
                 if (!score_task<K::NW, K::NCB>(w, qq, ib, jlo, jhi, slot)) continue;
-                constexpr int MAXJ = K::NW == 8 ? 1 : K::NCB;
+                constexpr int MAXJ = K::NW == 8 ? (K::NCB == 2 ? 1 : 2) : K::NCB;
                 f32x4 a[MAXJ];
 #pragma unroll
                 for (int jj = 0; jj < MAXJ; jj++) a[jj] = zero4();
@@ -575,7 +591,7 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
             }
         }
         // full chunks: stored during the next chunk; the last, partial chunk: now
-        if (!FULL) store_y<D, false>(p.y, base, t0, valid, py, fa, nq, g, r16);
+        if (!FULL) store_y<D, C, false>(p.y, base, t0, valid, py, fa, nq, g, r16);
     }
     if (MODE != WM_READOUT) {
         const bf16x8 ones = ones_bf16x8();
@@ -602,9 +618,14 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
     __syncthreads();
 }
 
+// Tokens per chunk: for d = 128 the causal pass takes 32-token chunks (its registers and
+// scores balance better), the other passes 64.
+constexpr int wide_chunk(int D, int MODE) { return (D == 128 && MODE == WM_CAUSAL) ? 32 : 64; }
+
 template <int D, int MODE>
 __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wide_kernel(WideParams p) {
-    using K = WideCfg<D>;
+    constexpr int C = wide_chunk(D, MODE);
+    using K = WideCfg<D, C>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[K::LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -618,8 +639,8 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
     const int t_end = min(p.N, t_begin + p.seg_len);
     const size_t base = (size_t)bh * p.N * D;
 
-    Prefetch<D> pf;
-    if (t_begin < t_end) issue_loads<D, MODE>(pf, p, base, t_begin, min(K::C, t_end - t_begin), w, lane, tid, smem);
+    Prefetch<D, C> pf;
+    if (t_begin < t_end) issue_loads<D, C, MODE>(pf, p, base, t_begin, min(K::C, t_end - t_begin), w, lane, tid, smem);
 
     float bl2[K::LB][4];
     load_bias<D>(p.b, h, dq, g, bl2);
@@ -690,19 +711,20 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
     // this wave's directions stay in registers for the whole segment
     bf16x8 wA[K::LB][K::KSD];
     load_w_operands<D>(smem + K::OFF_W, dq, g, r16, wA);
+    __syncthreads();  // the W tile is overwritten by the first chunk's features
 
-    PendingY<D> py;
+    PendingY<D, C> py;
     int t0 = t_begin;
     for (; t0 + K::C <= t_end; t0 += K::C) {
         const int t_next = t0 + K::C;
-        chunk_step<D, MODE, true>(p, base, t0, K::C, t_next, min(K::C, t_end - t_next), smem, pf, bl2, sacc, zacc, py,
+        chunk_step<D, C, MODE, true>(p, base, t0, K::C, t_next, min(K::C, t_end - t_next), smem, pf, bl2, sacc, zacc, py,
                                   t0 > t_begin ? t0 - K::C : -1, wA, tid);
     }
     if (t0 < t_end) {
-        chunk_step<D, MODE, false>(p, base, t0, t_end - t0, t_end, 0, smem, pf, bl2, sacc, zacc, py,
+        chunk_step<D, C, MODE, false>(p, base, t0, t_end - t0, t_end, 0, smem, pf, bl2, sacc, zacc, py,
                                    t0 > t_begin ? t0 - K::C : -1, wA, tid);
     } else if (MODE != WM_STATE && t0 > t_begin) {
-        store_y<D, true>(p.y, base, t0 - K::C, K::C, py, fa, nq, g, r16);
+        store_y<D, C, true>(p.y, base, t0 - K::C, K::C, py, fa, nq, g, r16);
     }
 
     // ---- segment end: publish the aggregate (STATE, register image) or the final state
@@ -772,10 +794,10 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void fm_
         const int t0 = (part * cpw + c) * K::C;
         if (t0 >= N) break;
         const int valid = min(K::C, N - t0);
-        stage_x<D>(xh, t0, valid, w, lane, sStage);
+        stage_x<D, K::C>(xh, t0, valid, w, lane, sStage);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        phi_chunk<D, false, true, false>(sStage, valid, wA, bl2, th, dq, g, r16, sPhi, K::RQ);
+        phi_chunk<D, K::C, false, true, false>(sStage, valid, wA, bl2, th, dq, g, r16, sPhi, K::RQ);
         __syncthreads();
         constexpr int P8 = K::DP / 8;
         for (int pi = tid; pi < K::C * P8; pi += K::NT) {
