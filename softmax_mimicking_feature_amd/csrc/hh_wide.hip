@@ -34,9 +34,12 @@ namespace hh {
 // disjoint banks.
 constexpr int tr_stride(int n) { return n + ((((32 - 2 * n) % 128) + 128) % 128) / 2; }
 
-template <int D, int C_ = 64>
+enum { WM_STATE = 0, WM_CAUSAL = 1, WM_READOUT = 2 };
+
+template <int D, int C_ = 64, int MODE_ = WM_CAUSAL>
 struct WideCfg {
     static constexpr int C = C_;                      // tokens per chunk
+    static constexpr int MODE = MODE_;
     static constexpr int NCB = C / 16;                // 16-token blocks per chunk
     static constexpr int KSC = C / 32;                // 32-wide K steps over the chunk's tokens
     static constexpr int NW = D == 128 ? 8 : (D == 64 ? 4 : D / 16);  // waves per workgroup
@@ -61,7 +64,14 @@ struct WideCfg {
     static constexpr int IBF = NCB / NF;              // output row blocks finalised per wave
     static constexpr int IMG8 = FBW * VB / 2;         // bf16x8 pieces of a segment slot per lane
     static constexpr int NJ = (NW == 8) ? 2 : 1;      // intra-chunk row-sum slots
-    static constexpr int VPT = C * (D / 8) / NT;      // 16-byte pieces of V per thread and chunk
+    // Staging buffers for the raw inputs.  With two (one workgroup per CU), q, k and V of the
+    // next chunk are fetched straight into LDS a whole chunk ahead; with one (two workgroups
+    // per CU), q and k are fetched after the feature maps have consumed the buffer and V goes
+    // through registers.
+    static constexpr int NBUF = D == 128 ? 2 : 1;
+    static constexpr bool USE_Q = MODE != WM_STATE;
+    static constexpr bool USE_K = MODE != WM_READOUT;
+    static constexpr int VPT = NBUF == 1 ? C * (D / 8) / NT : 1;  // 16-byte pieces of V per thread and chunk
     // LDS tiles
     // Row strides of the feature tiles, chosen for the LDS bank mapping of gfx950 (measured):
     // 16-byte reads of 16 rows x 4 column blocks are conflict-free when the row pitch is 32
@@ -69,38 +79,39 @@ struct WideCfg {
     // runs are conflict-free when it is an odd multiple of 8 bytes (mod 256).
     static constexpr int RQ = DP + 16;                // phi(q) [C][RQ]: 16-byte row reads and writes
     static constexpr int RK = DP + 12;                // phi(k) [C][RK]: 8-byte row reads, transposing reads
-    static constexpr int RV = tr_stride(D);           // V [C][RV]: transposing reads
+    // V [C][RV]: transposing reads.  Two buffers: unpadded 256-byte rows filled by direct loads,
+    // 16-byte granules rotated by 4 per row (v_pos); one buffer: padded rows.
+    static constexpr int RV = NBUF == 2 ? D : tr_stride(D);
     static constexpr int RA = C + 8;                  // intra scores A [C][RA]
     static constexpr int XS = D + 4;                  // fp32 exchange tile [C][XS] (NF = 2), aliases phi(q)
-    static constexpr int SZ_PQ = (C * RQ * 2 > (NF == 2 ? C * XS * 4 : 0)) ? C * RQ * 2 : C * XS * 4;
-    static constexpr int SZ_PK = C * RK * 2;
-    // raw q / k of the next chunk, loaded straight from global memory into LDS: [C][D]
-    // bf16, 16-byte granules of row r stored at granule index (g ^ (r % NSW))
+    // raw q / k of a chunk, loaded straight from global memory into LDS: [C][D] bf16, 16-byte
+    // granules placed by stage_pos
     static constexpr int NG = D / 8;                  // 16-byte granules per row
     static constexpr int NSW = NG < 8 ? NG : 8;       // XOR swizzle period (rows of fewer than 16 granules)
     static constexpr int SZ_X = C * D * 2;
     static constexpr int XBLK = SZ_X / 1024;          // 1 KB direct-load blocks per tile
+    static constexpr int SZ_PQ = !USE_Q ? 0 : ((C * RQ * 2 > (NF == 2 ? C * XS * 4 : 0)) ? C * RQ * 2 : C * XS * 4);
+    static constexpr int SZ_PK = USE_K ? C * RK * 2 : 0;
+    static constexpr int SZ_V1 = C * RV * 2;
     static constexpr int OFF_PQ = 0;
     static constexpr int OFF_PK = OFF_PQ + SZ_PQ;
     static constexpr int OFF_V = OFF_PK + SZ_PK;
-    static constexpr int OFF_A = OFF_V + C * RV * 2;
-    static constexpr int OFF_DEN = OFF_A + C * RA * 2;
-    static constexpr int OFF_XQ = OFF_DEN + (NW + NJ) * C * 4;
-    static constexpr int OFF_XK = OFF_XQ + SZ_X;
+    static constexpr int OFF_A = OFF_V + (USE_K ? NBUF * SZ_V1 : 0);
+    static constexpr int OFF_DEN = OFF_A + (MODE == WM_CAUSAL ? C * RA * 2 : 0);
+    static constexpr int OFF_XQ = OFF_DEN + (USE_Q ? (NW + NJ) * C * 4 : 0);
+    static constexpr int OFF_XK = OFF_XQ + (USE_Q ? NBUF * SZ_X : 0);
     // per-head W, [D rows][D] bf16 with granule swizzle like the x tiles: only read once into
     // registers before the first chunk, so it shares the feature tiles' space
     static constexpr int OFF_W = OFF_PQ;
-    static constexpr int LDS_BYTES = OFF_XK + SZ_X;
+    static constexpr int LDS_BYTES = OFF_XK + (USE_K ? NBUF * SZ_X : 0);
     static constexpr int MIN_WG_PER_CU = NW == 8 ? 1 : 2;
     static_assert(ZB == 2, "each wave owns one K step of z rows");
     static_assert(VB >= 1 && LB >= 1 && IBT >= 1 && IBF >= 1 && FBW % 2 == 0, "bad wave split");
-    static_assert(VPT >= 1 && C * (D / 8) % NT == 0, "every lane moves whole V pieces");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(NBUF == 2 || (VPT >= 1 && C * (D / 8) % NT == 0), "every lane moves whole V pieces");
     static_assert(D * D * 2 <= SZ_PQ + SZ_PK, "W fits in the feature tiles");
     static_assert(SZ_X % 1024 == 0 && XBLK % NW == 0, "direct loads: whole 1 KB blocks, the same count per wave");
+    static_assert(NBUF == 1 || (D == 128 && VB == 2), "rotated V tile assumes 16 granules per row");
 };
-
-enum { WM_STATE = 0, WM_CAUSAL = 1, WM_READOUT = 2 };
 
 // Position of feature f in a row-major feature tile.  With PERM, each 32-feature group is
 // stored in the K order of two stacked accumulator blocks (lane group g reads features
@@ -194,6 +205,11 @@ struct PendingY {
 
 // Loads of the next chunk, issued one chunk ahead: q and k go straight into LDS staging
 // tiles (global_load_lds), V into a few registers.
+// Stored position of granule G of row r in a two-buffer V tile (256-byte rows): rotated by 4
+// per row, so that the transposing reads of four rows x four 16-byte-spaced runs hit 16
+// distinct granules.
+__device__ __forceinline__ int v_pos(int r, int G) { return (G + 4 * r) & 15; }
+
 template <int D, int C>
 struct Prefetch {
     bf16x8 vp[WideCfg<D, C>::VPT];
@@ -222,13 +238,36 @@ __device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, int t0, in
     }
 }
 
-template <int D, int C, int MODE>
+// One [C][D] tile of V into a two-buffer V tile (positions v_pos); rows past the end read a
+// valid row: their keys' features are exactly zero, so they contribute nothing.
+template <int D, int C>
+__device__ __forceinline__ void stage_v(const bf16_t *__restrict__ v, int t0, int valid, int w, int lane,
+                                        unsigned char *tile) {
+    using K = WideCfg<D, C>;
+#pragma unroll
+    for (int bb = 0; bb < K::XBLK / K::NW; bb++) {
+        const int blk = w + bb * K::NW;
+        const int slot = 64 * blk + lane;
+        const int r = slot / K::NG, P = slot % K::NG;
+        const int G = (P - 4 * r) & 15;
+        const int rr = r < valid ? r : 0;
+        load_to_lds_16(v + (size_t)(t0 + rr) * D + 8 * G, tile + 1024 * blk);
+    }
+}
+
+// Loads of one chunk into staging buffer BUF: q and k (and, with two buffers, V) straight into
+// LDS, otherwise V into registers.
+template <int D, int C, int MODE, int BUF>
 __device__ __forceinline__ void issue_loads(Prefetch<D, C> &pf, const WideParams &p, size_t base, int t0, int valid,
                                             int w, int lane, int tid, unsigned char *smem) {
-    using K = WideCfg<D, C>;
-    if (MODE != WM_STATE) stage_x<D, C>(p.q + base, t0, valid, w, lane, smem + K::OFF_XQ);
+    using K = WideCfg<D, C, MODE>;
+    if (MODE != WM_STATE) stage_x<D, C>(p.q + base, t0, valid, w, lane, smem + K::OFF_XQ + BUF * K::SZ_X);
     if (MODE != WM_READOUT) {
-        stage_x<D, C>(p.k + base, t0, valid, w, lane, smem + K::OFF_XK);
+        stage_x<D, C>(p.k + base, t0, valid, w, lane, smem + K::OFF_XK + BUF * K::SZ_X);
+        if (K::NBUF == 2) {
+            stage_v<D, C>(p.v + base, t0, valid, w, lane, smem + K::OFF_V + BUF * K::SZ_V1);
+            return;
+        }
         constexpr int NC = D / 8;
 #pragma unroll
         for (int it = 0; it < K::VPT; it++) {
@@ -424,17 +463,17 @@ __device__ __forceinline__ void store_y(bf16_t *__restrict__ y, size_t base, int
     }
 }
 
-template <int D, int C, int MODE, bool FULL>
+template <int D, int C, int MODE, bool FULL, int BUF>
 __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int t0, int valid, int t_next,
                                            int valid_next, unsigned char *smem, Prefetch<D, C> &pf,
                                            const float (&bl2)[WideCfg<D>::LB][4],
                                            f32x4 (&sacc)[WideCfg<D>::FBW][WideCfg<D>::VB],
                                            f32x4 (&zacc)[WideCfg<D>::ZB], PendingY<D, C> &py, int t_pending,
                                            const bf16x8 (&wA)[WideCfg<D>::LB][WideCfg<D>::KSD], int tid) {
-    using K = WideCfg<D, C>;
+    using K = WideCfg<D, C, MODE>;
     bf16_t *sPQ = reinterpret_cast<bf16_t *>(smem + K::OFF_PQ);
     bf16_t *sPK = reinterpret_cast<bf16_t *>(smem + K::OFF_PK);
-    bf16_t *sV = reinterpret_cast<bf16_t *>(smem + K::OFF_V);
+    bf16_t *sV = reinterpret_cast<bf16_t *>(smem + K::OFF_V + BUF * K::SZ_V1);
     bf16_t *sA = reinterpret_cast<bf16_t *>(smem + K::OFF_A);
     float *sDen = reinterpret_cast<float *>(smem + K::OFF_DEN);
     float *sX = reinterpret_cast<float *>(smem + K::OFF_PQ);  // phi(q) is dead once the read-out is done
@@ -442,23 +481,30 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
     const int th = w / K::NDQ, dq = w % K::NDQ;  // feature-map role
     const int fa = w / K::NN, nq = w % K::NN;     // state role: feature part, value part
 
+    // two buffers: the next chunk's inputs go into the other one right away
+    if (K::NBUF == 2 && valid_next > 0)
+        issue_loads<D, C, MODE, BUF ^ 1>(pf, p, base, t_next, valid_next, w, lane, tid, smem);
     // outputs of the previous chunk
     if (MODE != WM_STATE && t_pending >= 0) store_y<D, C, true>(p.y, base, t_pending, K::C, py, fa, nq, g, r16);
 
-    // ---- phase 1: V and feature maps into LDS, then start loading the next chunk
+    // ---- phase 1: (V and) feature maps into LDS
     if (MODE != WM_READOUT) {
-        constexpr int NC = D / 8;
+        if (K::NBUF == 1) {
+            constexpr int NC = D / 8;
 #pragma unroll
-        for (int it = 0; it < K::VPT; it++) {
-            const int t = tid + it * K::NT;
-            store_v8<K::VB>(sV + (t / NC) * K::RV, 8 * (t % NC), pf.vp[it]);
+            for (int it = 0; it < K::VPT; it++) {
+                const int t = tid + it * K::NT;
+                store_v8<K::VB>(sV + (t / NC) * K::RV, 8 * (t % NC), pf.vp[it]);
+            }
         }
-        phi_chunk<D, C, true, FULL>(smem + K::OFF_XK, valid, wA, bl2, th, dq, g, r16, sPK, K::RK);
+        phi_chunk<D, C, true, FULL>(smem + K::OFF_XK + BUF * K::SZ_X, valid, wA, bl2, th, dq, g, r16, sPK, K::RK);
     }
-    if (MODE != WM_STATE) phi_chunk<D, C, false, FULL>(smem + K::OFF_XQ, valid, wA, bl2, th, dq, g, r16, sPQ, K::RQ);
+    if (MODE != WM_STATE)
+        phi_chunk<D, C, false, FULL>(smem + K::OFF_XQ + BUF * K::SZ_X, valid, wA, bl2, th, dq, g, r16, sPQ, K::RQ);
     __syncthreads();
-    // the staging tiles are free again: start moving the next chunk in
-    if (valid_next > 0) issue_loads<D, C, MODE>(pf, p, base, t_next, valid_next, w, lane, tid, smem);
+    // one buffer: it is free again, start moving the next chunk in
+    if (K::NBUF == 1 && valid_next > 0)
+        issue_loads<D, C, MODE, 0>(pf, p, base, t_next, valid_next, w, lane, tid, smem);
 
     // Read-out accumulators are transposed: numT[ib][vb] holds, in lane (g, r16), token
     // 16 ib + r16 and value columns value_col(nq, vb, 4 g + r).
@@ -554,11 +600,24 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
     // V operands: lane column c <-> value column value_col(nq, vb, c), K = tokens
     bf16x8 vop[K::KSC][K::VB];
     if (MODE != WM_READOUT) {
-        const int lane_v = (8 * g + (r16 >> 2)) * K::RV + 4 * (r16 & 3) + 16 * nq * K::VB;
+        if (K::NBUF == 2) {
+            // rows 8 g + r16 / 4 (+4, +32 ks keep the rotation), runs of 4 columns 16 bytes apart:
+            // granule 4 nq + r16 % 4, byte 8 vb of it
+            const int r0 = 8 * g + (r16 >> 2);
+            const int lane_v = r0 * K::RV + 8 * v_pos(r0, 4 * nq + (r16 & 3));
 #pragma unroll
-        for (int ks = 0; ks < K::KSC; ks++)
+            for (int ks = 0; ks < K::KSC; ks++)
 #pragma unroll
-            for (int vb = 0; vb < K::VB; vb++) vop[ks][vb] = operand_down_rows(sV, lane_v, 32 * ks * K::RV + 16 * vb, K::RV);
+                for (int vb = 0; vb < K::VB; vb++)
+                    vop[ks][vb] = operand_down_rows(sV, lane_v, 32 * ks * K::RV + 4 * vb, K::RV);
+        } else {
+            const int lane_v = (8 * g + (r16 >> 2)) * K::RV + 4 * (r16 & 3) + 16 * nq * K::VB;
+#pragma unroll
+            for (int ks = 0; ks < K::KSC; ks++)
+#pragma unroll
+                for (int vb = 0; vb < K::VB; vb++)
+                    vop[ks][vb] = operand_down_rows(sV, lane_v, 32 * ks * K::RV + 16 * vb, K::RV);
+        }
     }
     if (MODE != WM_STATE) {
 #pragma unroll
@@ -625,7 +684,8 @@ constexpr int wide_chunk(int D, int MODE) { return (D == 128 && MODE == WM_CAUSA
 template <int D, int MODE>
 __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wide_kernel(WideParams p) {
     constexpr int C = wide_chunk(D, MODE);
-    using K = WideCfg<D, C>;
+    using K = WideCfg<D, C, MODE>;
+    static_assert(K::LDS_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) unsigned char smem[K::LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -640,7 +700,7 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
     const size_t base = (size_t)bh * p.N * D;
 
     Prefetch<D, C> pf;
-    if (t_begin < t_end) issue_loads<D, C, MODE>(pf, p, base, t_begin, min(K::C, t_end - t_begin), w, lane, tid, smem);
+    if (t_begin < t_end) issue_loads<D, C, MODE, 0>(pf, p, base, t_begin, min(K::C, t_end - t_begin), w, lane, tid, smem);
 
     float bl2[K::LB][4];
     load_bias<D>(p.b, h, dq, g, bl2);
@@ -715,17 +775,40 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
 
     PendingY<D, C> py;
     int t0 = t_begin;
-    for (; t0 + K::C <= t_end; t0 += K::C) {
-        const int t_next = t0 + K::C;
-        chunk_step<D, C, MODE, true>(p, base, t0, K::C, t_next, min(K::C, t_end - t_next), smem, pf, bl2, sacc, zacc, py,
-                                  t0 > t_begin ? t0 - K::C : -1, wA, tid);
+    auto prev = [&](int t) { return t > t_begin ? t - K::C : -1; };
+    if (K::NBUF == 2) {
+        // buffers alternate: chunk pairs, then at most one more full chunk and a partial one
+        for (; t0 + 2 * K::C <= t_end; t0 += 2 * K::C) {
+            chunk_step<D, C, MODE, true, 0>(p, base, t0, K::C, t0 + K::C, K::C, smem, pf, bl2, sacc, zacc, py,
+                                            prev(t0), wA, tid);
+            const int t1 = t0 + K::C;
+            chunk_step<D, C, MODE, true, 1>(p, base, t1, K::C, t1 + K::C, min(K::C, t_end - t1 - K::C), smem, pf, bl2,
+                                            sacc, zacc, py, prev(t1), wA, tid);
+        }
+        if (t0 + K::C <= t_end) {
+            chunk_step<D, C, MODE, true, 0>(p, base, t0, K::C, t0 + K::C, min(K::C, t_end - t0 - K::C), smem, pf, bl2,
+                                            sacc, zacc, py, prev(t0), wA, tid);
+            t0 += K::C;
+            if (t0 < t_end)
+                chunk_step<D, C, MODE, false, 1>(p, base, t0, t_end - t0, t_end, 0, smem, pf, bl2, sacc, zacc, py,
+                                                 prev(t0), wA, tid);
+        } else if (t0 < t_end) {
+            chunk_step<D, C, MODE, false, 0>(p, base, t0, t_end - t0, t_end, 0, smem, pf, bl2, sacc, zacc, py,
+                                             prev(t0), wA, tid);
+        }
+    } else {
+        for (; t0 + K::C <= t_end; t0 += K::C) {
+            const int t_next = t0 + K::C;
+            chunk_step<D, C, MODE, true, 0>(p, base, t0, K::C, t_next, min(K::C, t_end - t_next), smem, pf, bl2, sacc,
+                                            zacc, py, prev(t0), wA, tid);
+        }
+        if (t0 < t_end)
+            chunk_step<D, C, MODE, false, 0>(p, base, t0, t_end - t0, t_end, 0, smem, pf, bl2, sacc, zacc, py, prev(t0),
+                                             wA, tid);
     }
-    if (t0 < t_end) {
-        chunk_step<D, C, MODE, false>(p, base, t0, t_end - t0, t_end, 0, smem, pf, bl2, sacc, zacc, py,
-                                   t0 > t_begin ? t0 - K::C : -1, wA, tid);
-    } else if (MODE != WM_STATE && t0 > t_begin) {
-        store_y<D, C, true>(p.y, base, t0 - K::C, K::C, py, fa, nq, g, r16);
-    }
+    // the last chunk's outputs, unless it was partial (stored at once)
+    if (MODE != WM_STATE && t_end > t_begin && (t_end - t_begin) % K::C == 0)
+        store_y<D, C, true>(p.y, base, t_end - K::C, K::C, py, fa, nq, g, r16);
 
     // ---- segment end: publish the aggregate (STATE, register image) or the final state
     //      (CAUSAL, last segment, feature-major)
@@ -914,13 +997,21 @@ hipError_t launch_wide(int d, int mode, const WideParams &p, int grid, hipStream
     }
 }
 
+template <int D>
+constexpr int wide_lds_max() {
+    constexpr int a = WideCfg<D, wide_chunk(D, WM_STATE), WM_STATE>::LDS_BYTES;
+    constexpr int c = WideCfg<D, wide_chunk(D, WM_CAUSAL), WM_CAUSAL>::LDS_BYTES;
+    constexpr int r = WideCfg<D, wide_chunk(D, WM_READOUT), WM_READOUT>::LDS_BYTES;
+    return a > c ? (a > r ? a : r) : (c > r ? c : r);
+}
+
 int wide_wgs_per_cu(int d) {
     int lds = 0;
     switch (d) {
-    case 16: lds = WideCfg<16>::LDS_BYTES; break;
-    case 32: lds = WideCfg<32>::LDS_BYTES; break;
-    case 64: lds = WideCfg<64>::LDS_BYTES; break;
-    case 128: lds = WideCfg<128>::LDS_BYTES; break;
+    case 16: lds = wide_lds_max<16>(); break;
+    case 32: lds = wide_lds_max<32>(); break;
+    case 64: lds = wide_lds_max<64>(); break;
+    case 128: lds = wide_lds_max<128>(); break;
     default: return 1;
     }
     int n = (160 * 1024) / lds;
