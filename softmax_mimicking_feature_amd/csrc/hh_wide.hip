@@ -477,7 +477,8 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
     bf16_t *sA = reinterpret_cast<bf16_t *>(smem + K::OFF_A);
     float *sDen = reinterpret_cast<float *>(smem + K::OFF_DEN);
     float *sX = reinterpret_cast<float *>(smem + K::OFF_PQ);  // phi(q) is dead once the read-out is done
-    const int w = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+    // wave index as a scalar: role branches on it stay scalar (never exec-masked around MFMAs)
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int th = w / K::NDQ, dq = w % K::NDQ;  // feature-map role
     const int fa = w / K::NN, nq = w % K::NN;     // state role: feature part, value part
 
@@ -689,7 +690,8 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
     __shared__ __attribute__((aligned(16))) unsigned char smem[K::LDS_BYTES];
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+    // wave index as a scalar: role branches on it stay scalar (never exec-masked around MFMAs)
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int dq = w % K::NDQ;
     const int fa = w / K::NN, nq = w % K::NN;
     const int bh = blockIdx.x / p.nseg_grid;
@@ -852,6 +854,540 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Segment aggregates for d = 128 with specialised waves.  Waves 0-3 (producers) compute the
+// key feature map of the next chunk while waves 4-7 (consumers) fold the current chunk into
+// the state; each SIMD runs one of each, so the exponentials of one overlap the matrix
+// products of the other.  One workgroup barrier per chunk hands the double-buffered feature
+// tile over.  The aggregate is written in the slot image of wide_kernel<128, *> (consumer
+// (fa, nq) holds the accumulators of that kernel's waves 4 fa + 2 nq and 4 fa + 2 nq + 1).
+struct StateWsCfg {
+    static constexpr int D = 128, C = 64, DP = 256, NT = 512;
+    static constexpr int RK = DP + 12;                    // phi(k) pitch as in wide_kernel
+    static constexpr int SZ_PK = C * RK * 2;
+    static constexpr int SZ_X = C * D * 2;                // k staging and V tile alike
+    static constexpr int OFF_PK = 0;                      // two feature tiles
+    static constexpr int OFF_V = OFF_PK + 2 * SZ_PK;      // two V tiles (granules at v_pos)
+    static constexpr int OFF_XK = OFF_V + 2 * SZ_X;       // two k staging tiles
+    static constexpr int OFF_W = 0;                       // W, before the first feature tile
+    static constexpr int LDS_BYTES = OFF_XK + 2 * SZ_X;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(D * D * 2 <= 2 * SZ_PK, "W fits in the feature tiles");
+};
+
+// Producer wave p: features of directions 32 p .. 32 p + 31 for the 64 tokens of one chunk.
+__device__ __forceinline__ void ws_produce(const unsigned char *stage, int valid, const bf16x8 (&wA)[2][4],
+                                           const float (&bl2)[2][4], int p, int g, int r16, bf16_t *sPK) {
+    using S = StateWsCfg;
+#pragma unroll
+    for (int ib = 0; ib < 4; ib++) {
+        const int i = 16 * ib + r16;
+        bf16x8 xb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) xb[ks] = staged_x_operand<128>(stage, i, ks, g);
+#pragma unroll
+        for (int mb = 0; mb < 2; mb++) {
+            f32x4 a = zero4();
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) a = mfma_bf16(wA[mb][ks], xb[ks], a);
+            f32x4 ep, en;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float u = a[r] * kLog2e + bl2[mb][r];
+                ep[r] = exp2_fast(u);
+                en[r] = exp2_fast(-u);
+            }
+            if (i >= valid) {  // keys past the end contribute nothing
+                ep = zero4();
+                en = zero4();
+            }
+            const int f = 32 * p + 16 * mb + 4 * g;
+            store4(sPK + i * S::RK + feat_pos<true>(f), to_bf16x4(ep));
+            store4(sPK + i * S::RK + feat_pos<true>(128 + f), to_bf16x4(en));
+        }
+    }
+}
+
+// Inputs of a chunk two ahead (k) and one ahead (V) into the buffers freed by the last chunk;
+// issued by every wave (each moves its own 1 KB blocks).
+__device__ __forceinline__ void ws_issue(const WideParams &p, size_t base, int t_begin, int t_end, int c, int n, int w,
+                                         int lane, unsigned char *smem) {
+    using S = StateWsCfg;
+    const int b = c & 1;
+    if (c + 1 < n) {
+        const int t = t_begin + S::C * (c + 1);
+        stage_v<128, 64>(p.v + base, t, min(S::C, t_end - t), w, lane, smem + S::OFF_V + (b ^ 1) * S::SZ_X);
+    }
+    if (c + 2 < n) {
+        const int t = t_begin + S::C * (c + 2);
+        stage_x<128, 64>(p.k + base, t, min(S::C, t_end - t), w, lane, smem + S::OFF_XK + b * S::SZ_X);
+    }
+}
+
+__global__ __launch_bounds__(512, 1) void state_ws_kernel_128(WideParams p) {
+    using S = StateWsCfg;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
+    const int tid = threadIdx.x;
+    // wave index as a scalar: role branches on it stay scalar (never exec-masked around MFMAs)
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+    const int c4 = w & 3;
+    const int bh = blockIdx.x / p.nseg_grid;
+    const int s = blockIdx.x % p.nseg_grid;
+    const int h = bh % p.H;
+    const int t_begin = s * p.seg_len;
+    const int t_end = min(p.N, t_begin + p.seg_len);
+    const size_t base = (size_t)bh * p.N * S::D;
+    const int n = t_end > t_begin ? (t_end - t_begin + S::C - 1) / S::C : 0;
+    auto valid_of = [&](int c) { return min(S::C, t_end - (t_begin + S::C * c)); };
+
+    if (n > 0) {
+        stage_x<128, 64>(p.k + base, t_begin, valid_of(0), w, lane, smem + S::OFF_XK);
+        stage_v<128, 64>(p.v + base, t_begin, valid_of(0), w, lane, smem + S::OFF_V);
+    }
+    if (n > 1) stage_x<128, 64>(p.k + base, t_begin + S::C, valid_of(1), w, lane, smem + S::OFF_XK + S::SZ_X);
+    stage_w<128>(p.W, h, tid, smem + S::OFF_W);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // The two roles run separate loops with the same barriers, one per chunk.
+    if (w < 4) {
+        bf16x8 wA[2][4];
+        float bl2[2][4];
+        load_w_operands<128>(smem + S::OFF_W, c4, g, r16, wA);
+        load_bias<128>(p.b, h, c4, g, bl2);
+        __syncthreads();  // W shares space with the feature tiles
+        if (n > 0) ws_produce(smem + S::OFF_XK, valid_of(0), wA, bl2, c4, g, r16, reinterpret_cast<bf16_t *>(smem + S::OFF_PK));
+        __syncthreads();
+        for (int c = 0; c < n; c++) {
+            ws_issue(p, base, t_begin, t_end, c, n, w, lane, smem);
+            const int b = c & 1;
+            if (c + 1 < n)
+                ws_produce(smem + S::OFF_XK + (b ^ 1) * S::SZ_X, valid_of(c + 1), wA, bl2, c4, g, r16,
+                           reinterpret_cast<bf16_t *>(smem + S::OFF_PK + (b ^ 1) * S::SZ_PK));
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        return;
+    }
+
+    const int fa = c4 >> 1, nq = c4 & 1;
+    f32x4 sacc[8][4];
+    f32x4 zacc[4];
+#pragma unroll
+    for (int fb = 0; fb < 8; fb++)
+#pragma unroll
+        for (int vb = 0; vb < 4; vb++) sacc[fb][vb] = zero4();
+#pragma unroll
+    for (int zb = 0; zb < 4; zb++) zacc[zb] = zero4();
+    const int lane_k = (8 * g + (r16 >> 2)) * S::RK + 8 * (r16 & 3);
+    const int r0 = 8 * g + (r16 >> 2);
+    const int lane_v0 = r0 * S::D + 8 * v_pos(r0, 4 * (2 * nq) + (r16 & 3));
+    const int lane_v1 = r0 * S::D + 8 * v_pos(r0, 4 * (2 * nq + 1) + (r16 & 3));
+    const bf16x8 ones = ones_bf16x8();
+    __syncthreads();  // (producers: W read)
+    __syncthreads();  // (producers: first chunk's features)
+    for (int c = 0; c < n; c++) {
+        ws_issue(p, base, t_begin, t_end, c, n, w, lane, smem);
+        const int b = c & 1;
+        const bf16_t *sPK = reinterpret_cast<const bf16_t *>(smem + S::OFF_PK + b * S::SZ_PK);
+        const bf16_t *sV = reinterpret_cast<const bf16_t *>(smem + S::OFF_V + b * S::SZ_X);
+        const bf16_t *sPKf = sPK + perm_block_pos(8 * fa);
+        const bf16_t *sPKz = sPK + perm_block_pos(4 * c4);
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+            bf16x8 vop[4];
+#pragma unroll
+            for (int vb = 0; vb < 4; vb++)
+                vop[vb] = operand_down_rows(sV, (vb >> 1) ? lane_v1 : lane_v0, 32 * ks * S::D + 4 * (vb & 1), S::D);
+#pragma unroll
+            for (int fb = 0; fb < 8; fb++) {
+                const bf16x8 a = operand_down_rows(sPKf, lane_k, 32 * ks * S::RK + perm_block_pos(fb), S::RK);
+#pragma unroll
+                for (int vb = 0; vb < 4; vb++) sacc[fb][vb] = mfma_bf16(a, vop[vb], sacc[fb][vb]);
+            }
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++) {
+                const bf16x8 a = operand_down_rows(sPKz, lane_k, 32 * ks * S::RK + perm_block_pos(zb), S::RK);
+                zacc[zb] = mfma_bf16(a, ones, zacc[zb]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    const size_t slot = (size_t)bh * p.slot_bh_stride + s;
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++) {
+        const int wq = 4 * fa + 2 * nq + hh;  // the chunked kernel's wave holding these accumulators
+        bf16x8 *img = reinterpret_cast<bf16x8 *>(p.S_slots + slot * S::DP * S::D) + wq * 8 * 64 + lane;
+#pragma unroll
+        for (int fb = 0; fb < 8; fb++) img[fb * 64] = cat(to_bf16x4(sacc[fb][2 * hh]), to_bf16x4(sacc[fb][2 * hh + 1]));
+    }
+    float *zs = p.z_slots + slot * S::DP;
+    if (r16 == 0) {
+#pragma unroll
+        for (int zb = 0; zb < 4; zb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) zs[16 * (4 * c4 + zb) + 4 * g + r] = zacc[zb][r];
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Chunked causal pass for d = 128 with specialised waves (32-token chunks).
+//   producers (waves 0-3, wave p): the scores of chunk c (query block x key block tasks),
+//     then the feature maps of q and k of chunk c + 1, directions 32 p .. 32 p + 31;
+//   consumers (waves 4-7, wave 4 + v): value columns 32 v .. 32 v + 31 of the state for all 256
+//     features (no exchange between waves): read-out of chunk c and its normaliser partial
+//     over features 64 v .. 64 v + 63, the state update with chunk c, and the finished output
+//     of chunk c - 1 (intra-chunk product with the scores computed meanwhile).
+// Each SIMD runs one producer and one consumer, one barrier per chunk.  Feature tiles,
+// scores and normaliser slots are double-buffered, V triple-buffered (used by the update of
+// chunk c and the intra product one chunk later), the raw q / k double-buffered and fetched
+// two chunks ahead.
+struct CausalWsCfg {
+    static constexpr int D = 128, C = 32, DP = 256, NT = 512;
+    static constexpr int RQ = DP + 16, RK = DP + 12, RA = C + 8;
+    static constexpr int SZ_PQ = C * RQ * 2, SZ_PK = C * RK * 2, SZ_X = C * D * 2, SZ_A = C * RA * 2;
+    static constexpr int NDEN = 6;                        // 4 consumer normaliser partials + 2 row sums
+    static constexpr int SZ_DEN = NDEN * C * 4;
+    static constexpr int OFF_PQ = 0;
+    static constexpr int OFF_PK = OFF_PQ + 2 * SZ_PQ;
+    static constexpr int OFF_V = OFF_PK + 2 * SZ_PK;
+    static constexpr int OFF_A = OFF_V + 3 * SZ_X;
+    static constexpr int OFF_DEN = OFF_A + 2 * SZ_A;
+    static constexpr int OFF_XQ = OFF_DEN + 2 * SZ_DEN;
+    static constexpr int OFF_XK = OFF_XQ + 2 * SZ_X;
+    static constexpr int OFF_W = 0;
+    static constexpr int LDS_BYTES = OFF_XK + 2 * SZ_X;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(D * D * 2 <= 2 * SZ_PQ + 2 * SZ_PK, "W fits in the feature tiles");
+};
+
+// Producer: q and k features of one 32-token chunk for directions 32 p .. 32 p + 31.
+__device__ __forceinline__ void cws_features(const unsigned char *xq, const unsigned char *xk, int valid,
+                                             const bf16x8 (&wA)[2][4], const float (&bl2)[2][4], int p, int g,
+                                             int r16, bf16_t *sPQ, bf16_t *sPK) {
+    using S = CausalWsCfg;
+#pragma unroll
+    for (int t = 0; t < 2; t++) {  // 0: keys, 1: queries
+        const unsigned char *stage = t == 0 ? xk : xq;
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++) {
+            const int i = 16 * ib + r16;
+            bf16x8 xb[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) xb[ks] = staged_x_operand<128>(stage, i, ks, g);
+            bf16x4 pe[2], ne[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; mb++) {
+                f32x4 a = zero4();
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) a = mfma_bf16(wA[mb][ks], xb[ks], a);
+                f32x4 ep, en;
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float u = a[r] * kLog2e + bl2[mb][r];
+                    ep[r] = exp2_fast(u);
+                    en[r] = exp2_fast(-u);
+                }
+                if (t == 0 && i >= valid) {  // keys past the end contribute nothing
+                    ep = zero4();
+                    en = zero4();
+                }
+                pe[mb] = to_bf16x4(ep);
+                ne[mb] = to_bf16x4(en);
+            }
+            const int f = 32 * p + 4 * g;  // both direction blocks: positions 8 g .. 8 g + 7 of the group
+            if (t == 0) {
+#pragma unroll
+                for (int mb = 0; mb < 2; mb++) {
+                    store4(sPK + i * S::RK + feat_pos<true>(f + 16 * mb), pe[mb]);
+                    store4(sPK + i * S::RK + feat_pos<true>(128 + f + 16 * mb), ne[mb]);
+                }
+            } else {
+                store8(sPQ + i * S::RQ + feat_pos<true>(f), cat(pe[0], pe[1]));
+                store8(sPQ + i * S::RQ + feat_pos<true>(128 + f), cat(ne[0], ne[1]));
+            }
+        }
+    }
+}
+
+// Producer: scores of one chunk.  Tasks: p0 (0,0), p1 (1,0), p2 (1,1); p3 clears the masked
+// block (0,1) and the second row-sum slot of query block 0.
+__device__ __forceinline__ void cws_scores(const bf16_t *sPQ, const bf16_t *sPK, bf16_t *sA, float *sDen, int p,
+                                           int g, int r16) {
+    using S = CausalWsCfg;
+    if (p == 3) {
+        bf16x4 zz;
+        zz[0] = zz[1] = zz[2] = zz[3] = (__bf16)0.0f;
+        store4(sA + r16 * S::RA + 16 + 4 * g, zz);
+        if (g == 0) sDen[5 * S::C + r16] = 0.0f;
+        return;
+    }
+    const int ib = p == 0 ? 0 : 1, jb = p == 2 ? 1 : 0, slot = p == 2 ? 5 : 4;
+    f32x4 a = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 8; ks++)
+        a = mfma_bf16(load8_as_halves(sPK + (16 * jb + r16) * S::RK + 32 * ks + 8 * g),
+                      load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g), a);
+    // a = A^T[j][i]: lane holds i = 16 ib + r16, j = 16 jb + 4 g + r; keep j <= i
+    if (jb == ib) {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            if (4 * g + r > r16) a[r] = 0.0f;
+    }
+    const bf16x4 ab = to_bf16x4(a);
+    float rs = ((float)ab[0] + (float)ab[1]) + ((float)ab[2] + (float)ab[3]);
+    store4(sA + (16 * ib + r16) * S::RA + 16 * jb + 4 * g, ab);
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    if (g == 0) sDen[slot * S::C + 16 * ib + r16] = rs;
+}
+
+// Consumer: finish the outputs of one chunk (held read-out + intra-chunk product, normalise,
+// store).  Lane (g, r16) owns token 16 ib + r16, value columns value_col<2>(v, vb, 4 g + r).
+__device__ __forceinline__ void cws_output(f32x4 (&numT)[2][2], const bf16_t *sA, const bf16_t *sV, const float *sDen,
+                                           int lane_v, bf16_t *__restrict__ yrow0, int valid, int v, int g, int r16) {
+    using S = CausalWsCfg;
+    bf16x8 vop[2];
+#pragma unroll
+    for (int vb = 0; vb < 2; vb++) vop[vb] = operand_down_rows(sV, lane_v, 4 * vb, S::D);
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++) {
+        const int i = 16 * ib + r16;
+        const bf16x8 a = load8(sA + i * S::RA + 8 * g);
+#pragma unroll
+        for (int vb = 0; vb < 2; vb++) numT[ib][vb] = mfma_bf16(vop[vb], a, numT[ib][vb]);
+        float den = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < S::NDEN; sl++) den += sDen[sl * S::C + i];
+        const float rden = __builtin_amdgcn_rcpf(den);
+        f32x4 o0, o1;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            o0[r] = numT[ib][0][r] * rden;
+            o1[r] = numT[ib][1][r] * rden;
+        }
+        if (i < valid) store8(yrow0 + (size_t)i * S::D + value_col<2>(v, 0, 4 * g), cat(to_bf16x4(o0), to_bf16x4(o1)));
+    }
+}
+
+// Inputs of chunk c + 1 (V) and c + 2 (q, k) into the buffers freed by the last chunk; issued by
+// every wave (each moves its own 1 KB blocks).
+__device__ __forceinline__ void cws_issue(const WideParams &p, size_t base, int t_begin, int t_end, int c, int n,
+                                          int w, int lane, unsigned char *smem) {
+    using S = CausalWsCfg;
+    if (c + 1 < n) {
+        const int t = t_begin + S::C * (c + 1);
+        stage_v<128, 32>(p.v + base, t, min(S::C, t_end - t), w, lane, smem + S::OFF_V + ((c + 1) % 3) * S::SZ_X);
+    }
+    if (c + 2 < n) {
+        const int t = t_begin + S::C * (c + 2), b = c & 1;
+        stage_x<128, 32>(p.q + base, t, min(S::C, t_end - t), w, lane, smem + S::OFF_XQ + b * S::SZ_X);
+        stage_x<128, 32>(p.k + base, t, min(S::C, t_end - t), w, lane, smem + S::OFF_XK + b * S::SZ_X);
+    }
+}
+
+__global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
+    using S = CausalWsCfg;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
+    const int tid = threadIdx.x;
+    // wave index as a scalar: role branches on it stay scalar (never exec-masked around MFMAs)
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+    const int pv = w & 3;  // producer index / consumer value part
+    const int bh = blockIdx.x / p.nseg_grid;
+    const int s = blockIdx.x % p.nseg_grid;
+    const int h = bh % p.H;
+    const int t_begin = s * p.seg_len;
+    const int t_end = min(p.N, t_begin + p.seg_len);
+    const size_t base = (size_t)bh * p.N * S::D;
+    const int n = t_end > t_begin ? (t_end - t_begin + S::C - 1) / S::C : 0;
+    auto valid_of = [&](int c) { return min(S::C, t_end - (t_begin + S::C * c)); };
+    auto pq_buf = [&](int b) { return reinterpret_cast<bf16_t *>(smem + S::OFF_PQ + b * S::SZ_PQ); };
+    auto pk_buf = [&](int b) { return reinterpret_cast<bf16_t *>(smem + S::OFF_PK + b * S::SZ_PK); };
+    auto v_buf = [&](int b) { return reinterpret_cast<const bf16_t *>(smem + S::OFF_V + b * S::SZ_X); };
+    auto a_buf = [&](int b) { return reinterpret_cast<bf16_t *>(smem + S::OFF_A + b * S::SZ_A); };
+    auto den_buf = [&](int b) { return reinterpret_cast<float *>(smem + S::OFF_DEN + b * S::SZ_DEN); };
+
+    if (n > 0) {
+        stage_x<128, 32>(p.q + base, t_begin, valid_of(0), w, lane, smem + S::OFF_XQ);
+        stage_x<128, 32>(p.k + base, t_begin, valid_of(0), w, lane, smem + S::OFF_XK);
+        stage_v<128, 32>(p.v + base, t_begin, valid_of(0), w, lane, smem + S::OFF_V);
+    }
+    if (n > 1) {
+        stage_x<128, 32>(p.q + base, t_begin + S::C, valid_of(1), w, lane, smem + S::OFF_XQ + S::SZ_X);
+        stage_x<128, 32>(p.k + base, t_begin + S::C, valid_of(1), w, lane, smem + S::OFF_XK + S::SZ_X);
+    }
+    stage_w<128>(p.W, h, tid, smem + S::OFF_W);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // The two roles run separate loops with the same barriers, one per chunk.
+    if (w < 4) {
+        bf16x8 wA[2][4];
+        float bl2[2][4];
+        load_w_operands<128>(smem + S::OFF_W, pv, g, r16, wA);
+        load_bias<128>(p.b, h, pv, g, bl2);
+        __syncthreads();  // W shares space with the feature tiles
+        if (n > 0)
+            cws_features(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, pv, g, r16, pq_buf(0), pk_buf(0));
+        __syncthreads();
+        for (int c = 0; c < n; c++) {
+            cws_issue(p, base, t_begin, t_end, c, n, w, lane, smem);
+            const int b2 = c & 1;
+            cws_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), pv, g, r16);
+            if (c + 1 < n)
+                cws_features(smem + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, smem + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
+                             valid_of(c + 1), wA, bl2, pv, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1));
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        return;
+    }
+
+    // consumer: value columns value_col<2>(pv, vb, c) of the state for all 256 features
+    f32x4 sacc[16][2];
+    f32x4 zacc[4];  // z rows of feature blocks 4 pv .. 4 pv + 3
+    f32x4 numT[2][2];
+#pragma unroll
+    for (int fb = 0; fb < 16; fb++) sacc[fb][0] = sacc[fb][1] = zero4();
+#pragma unroll
+    for (int zb = 0; zb < 4; zb++) zacc[zb] = zero4();
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++) numT[ib][0] = numT[ib][1] = zero4();
+    // starting state: the caller's S0 and the exclusive prefix of the earlier segments
+    if (p.S_in) {
+        const float *Si = p.S_in + (size_t)bh * p.in_bh_stride * S::DP * S::D;
+        const float *zi = p.z_in + (size_t)bh * p.in_bh_stride * S::DP;
+#pragma unroll
+        for (int fb = 0; fb < 16; fb++)
+#pragma unroll
+            for (int vb = 0; vb < 2; vb++) {
+                const int nn = value_col<2>(pv, vb, r16);
+#pragma unroll
+                for (int r = 0; r < 4; r++) sacc[fb][vb][r] = Si[(size_t)(16 * fb + 4 * g + r) * S::D + nn];
+            }
+#pragma unroll
+        for (int zb = 0; zb < 4; zb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) zacc[zb][r] = zi[16 * (4 * pv + zb) + 4 * g + r];
+    }
+    if (p.slot_mode == 1 && s > 0) {
+        const size_t sl = (size_t)bh * p.slot_bh_stride + s;
+        const float *zs = p.z_slots + sl * S::DP;
+#pragma unroll
+        for (int fa = 0; fa < 2; fa++) {
+            const bf16x8 *img = reinterpret_cast<const bf16x8 *>(p.S_slots + sl * S::DP * S::D) + (4 * fa + pv) * 8 * 64 + lane;
+            bf16x8 t[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) t[j] = img[j * 64];
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    sacc[8 * fa + j][0][r] += (float)t[j][r];
+                    sacc[8 * fa + j][1][r] += (float)t[j][4 + r];
+                }
+        }
+#pragma unroll
+        for (int zb = 0; zb < 4; zb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) zacc[zb][r] += zs[16 * (4 * pv + zb) + 4 * g + r];
+    }
+    const int lane_k = (8 * g + (r16 >> 2)) * S::RK + 8 * (r16 & 3);
+    const int r0 = 8 * g + (r16 >> 2);
+    const int lane_v = r0 * S::D + 8 * v_pos(r0, 4 * pv + (r16 & 3));
+    const bf16x8 ones = ones_bf16x8();
+    bf16_t *ybase = p.y + base;
+    __syncthreads();  // (producers: W read)
+    __syncthreads();  // (producers: first chunk's features)
+
+    for (int c = 0; c < n; c++) {
+        cws_issue(p, base, t_begin, t_end, c, n, w, lane, smem);
+        const int b2 = c & 1;
+        // outputs of the previous chunk
+        if (c > 0)
+            cws_output(numT, a_buf(b2 ^ 1), v_buf((c + 2) % 3), den_buf(b2 ^ 1), lane_v,
+                       ybase + (size_t)(t_begin + S::C * (c - 1)) * S::D, S::C, pv, g, r16);
+        const bf16_t *sPQ = pq_buf(b2);
+        const bf16_t *sPK = pk_buf(b2);
+        // read-out of this chunk (transposed) and the normaliser partial over features
+        // 64 pv .. 64 pv + 63 (K steps 2 pv and 2 pv + 1)
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++) numT[ib][0] = numT[ib][1] = zero4();
+        // (no branches inside the unrolled loops: each branch would end a scheduling region)
+#pragma unroll
+        for (int ks = 0; ks < 8; ks++) {
+            bf16x8 sb[2];
+#pragma unroll
+            for (int vb = 0; vb < 2; vb++) sb[vb] = acc_pair_to_operand(sacc[2 * ks][vb], sacc[2 * ks + 1][vb]);
+#pragma unroll
+            for (int ib = 0; ib < 2; ib++) {
+                const bf16x8 qop = load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g);
+#pragma unroll
+                for (int vb = 0; vb < 2; vb++) numT[ib][vb] = mfma_bf16(sb[vb], qop, numT[ib][vb]);
+            }
+        }
+        f32x4 dacc[2] = {zero4(), zero4()};
+        {
+            const bf16_t *sPQz = sPQ + 64 * pv;  // K steps 2 pv, 2 pv + 1
+#pragma unroll
+            for (int kz = 0; kz < 2; kz++) {
+                const bf16x8 zop = acc_pair_to_operand(zacc[2 * kz], zacc[2 * kz + 1]);
+#pragma unroll
+                for (int ib = 0; ib < 2; ib++)
+                    dacc[ib] = mfma_bf16(zop, load8(sPQz + (16 * ib + r16) * S::RQ + 32 * kz + 8 * g), dacc[ib]);
+            }
+        }
+        float *sDen = den_buf(b2);
+        if (g == 0) {
+            sDen[pv * S::C + r16] = dacc[0][0];
+            sDen[pv * S::C + 16 + r16] = dacc[1][0];
+        }
+        // state update with this chunk
+        const bf16_t *sV = v_buf(c % 3);
+        bf16x8 vop[2];
+#pragma unroll
+        for (int vb = 0; vb < 2; vb++) vop[vb] = operand_down_rows(sV, lane_v, 4 * vb, S::D);
+#pragma unroll
+        for (int fb = 0; fb < 16; fb++) {
+            const bf16x8 a = operand_down_rows(sPK, lane_k, perm_block_pos(fb), S::RK);
+#pragma unroll
+            for (int vb = 0; vb < 2; vb++) sacc[fb][vb] = mfma_bf16(a, vop[vb], sacc[fb][vb]);
+        }
+        {
+            const bf16_t *sPKz = sPK + perm_block_pos(4 * pv);
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++)
+                zacc[zb] = mfma_bf16(operand_down_rows(sPKz, lane_k, perm_block_pos(zb), S::RK), ones, zacc[zb]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    if (n > 0) {
+        cws_output(numT, a_buf((n - 1) & 1), v_buf((n - 1) % 3), den_buf((n - 1) & 1), lane_v,
+                   ybase + (size_t)(t_begin + S::C * (n - 1)) * S::D, valid_of(n - 1), pv, g, r16);
+    }
+    if (p.S_out && s == p.nseg_grid - 1) {
+        float *So = p.S_out + (size_t)bh * S::DP * S::D;
+        float *zo = p.z_out + (size_t)bh * S::DP;
+#pragma unroll
+        for (int fb = 0; fb < 16; fb++)
+#pragma unroll
+            for (int vb = 0; vb < 2; vb++) {
+                const int nn = value_col<2>(pv, vb, r16);
+#pragma unroll
+                for (int r = 0; r < 4; r++) So[(size_t)(16 * fb + 4 * g + r) * S::D + nn] = sacc[fb][vb][r];
+            }
+        if (r16 == 0) {
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) zo[16 * (4 * pv + zb) + 4 * g + r] = zacc[zb][r];
+        }
+    }
+}
+
 // Stand-alone feature map: each workgroup maps `cpw` chunks of 64 tokens of one head and
 // writes phi [token][2d] through an LDS tile so that global stores are full 16-byte rows.
 template <int D>
@@ -864,7 +1400,8 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void fm_
     __shared__ __attribute__((aligned(16))) bf16_t sPhi[K::C * K::RQ];
     __shared__ __attribute__((aligned(16))) unsigned char sStage[K::SZ_X];
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+    // wave index as a scalar: role branches on it stay scalar (never exec-masked around MFMAs)
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int th = w / K::NDQ, dq = w % K::NDQ;
     const int bh = blockIdx.x / wg_per_bh, part = blockIdx.x % wg_per_bh;
     const int h = bh % H;
@@ -975,10 +1512,16 @@ static hipError_t launch_wide_d(int mode, const WideParams &p, int grid, hipStre
     using K = WideCfg<D>;
     switch (mode) {
     case WM_STATE:
-        hipLaunchKernelGGL((wide_kernel<D, WM_STATE>), dim3(grid), dim3(K::NT), 0, st, p);
+        if (D == 128)
+            hipLaunchKernelGGL(state_ws_kernel_128, dim3(grid), dim3(StateWsCfg::NT), 0, st, p);
+        else
+            hipLaunchKernelGGL((wide_kernel<D, WM_STATE>), dim3(grid), dim3(K::NT), 0, st, p);
         break;
     case WM_CAUSAL:
-        hipLaunchKernelGGL((wide_kernel<D, WM_CAUSAL>), dim3(grid), dim3(K::NT), 0, st, p);
+        if (D == 128)
+            hipLaunchKernelGGL(causal_ws_kernel_128, dim3(grid), dim3(CausalWsCfg::NT), 0, st, p);
+        else
+            hipLaunchKernelGGL((wide_kernel<D, WM_CAUSAL>), dim3(grid), dim3(K::NT), 0, st, p);
         break;
     default:
         hipLaunchKernelGGL((wide_kernel<D, WM_READOUT>), dim3(grid), dim3(K::NT), 0, st, p);
