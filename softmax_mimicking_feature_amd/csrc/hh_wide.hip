@@ -215,9 +215,15 @@ struct Prefetch {
     bf16x8 vp[WideCfg<D, C>::VPT];
 };
 
+// 16 bytes per lane from global memory straight into LDS (lane l -> lds_dst + 16 l), through
+// M0.  Written as inline assembly on purpose: the compiler then does not track these LDS writes
+// and does not stall every later LDS read until they land (it cannot tell the target buffers
+// apart).  Callers make the data visible themselves: s_waitcnt vmcnt(0), then a barrier.  The
+// hidden loads only make the compiler's own vmcnt waits more conservative (loads retire in
+// order), never less.
 __device__ __forceinline__ void load_to_lds_16(const void *gsrc, void *lds_dst_uniform) {
-    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)(reinterpret_cast<uintptr_t>(lds_dst_uniform)),
-                                     16, 0, 0);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_dst_uniform));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gsrc), "s"(lds) : "m0");
 }
 
 // One [C][D] tile of x into its staging area: wave w moves blocks w, w + NW, ...; lane l of
@@ -1063,30 +1069,48 @@ struct CausalWsCfg {
     static_assert(D * D * 2 <= 2 * SZ_PQ + 2 * SZ_PK, "W fits in the feature tiles");
 };
 
-// Producer: q and k features of one 32-token chunk for directions 32 p .. 32 p + 31.
+// Producer: q and k features of one 32-token chunk for directions 32 p .. 32 p + 31.  All
+// operand reads first, then the eight independent product chains, then the exponentials, so
+// that one wave keeps the LDS, matrix and vector pipes busy at once.
 __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsigned char *xk, int valid,
                                              const bf16x8 (&wA)[2][4], const float (&bl2)[2][4], int p, int g,
                                              int r16, bf16_t *sPQ, bf16_t *sPK) {
     using S = CausalWsCfg;
+    bf16x8 xb[2][2][4];  // [keys, queries][token block][K step]
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) xb[t][ib][ks] = staged_x_operand<128>(t == 0 ? xk : xq, 16 * ib + r16, ks, g);
+    f32x4 acc[2][2][2];
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+            for (int mb = 0; mb < 2; mb++) acc[t][ib][mb] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+                for (int mb = 0; mb < 2; mb++) acc[t][ib][mb] = mfma_bf16(wA[mb][ks], xb[t][ib][ks], acc[t][ib][mb]);
+    const int f = 32 * p + 4 * g;  // both direction blocks: positions 8 g .. 8 g + 7 of the group
 #pragma unroll
     for (int t = 0; t < 2; t++) {  // 0: keys, 1: queries
-        const unsigned char *stage = t == 0 ? xk : xq;
 #pragma unroll
         for (int ib = 0; ib < 2; ib++) {
             const int i = 16 * ib + r16;
-            bf16x8 xb[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) xb[ks] = staged_x_operand<128>(stage, i, ks, g);
             bf16x4 pe[2], ne[2];
 #pragma unroll
             for (int mb = 0; mb < 2; mb++) {
-                f32x4 a = zero4();
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) a = mfma_bf16(wA[mb][ks], xb[ks], a);
                 f32x4 ep, en;
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const float u = a[r] * kLog2e + bl2[mb][r];
+                    const float u = acc[t][ib][mb][r] * kLog2e + bl2[mb][r];
                     ep[r] = exp2_fast(u);
                     en[r] = exp2_fast(-u);
                 }
@@ -1097,7 +1121,6 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
                 pe[mb] = to_bf16x4(ep);
                 ne[mb] = to_bf16x4(en);
             }
-            const int f = 32 * p + 4 * g;  // both direction blocks: positions 8 g .. 8 g + 7 of the group
             if (t == 0) {
 #pragma unroll
                 for (int mb = 0; mb < 2; mb++) {
@@ -1121,15 +1144,16 @@ __device__ __forceinline__ void cws_scores(const bf16_t *sPQ, const bf16_t *sPK,
         bf16x4 zz;
         zz[0] = zz[1] = zz[2] = zz[3] = (__bf16)0.0f;
         store4(sA + r16 * S::RA + 16 + 4 * g, zz);
-        if (g == 0) sDen[5 * S::C + r16] = 0.0f;
+        sDen[5 * S::C + r16] = 0.0f;
         return;
     }
     const int ib = p == 0 ? 0 : 1, jb = p == 2 ? 1 : 0, slot = p == 2 ? 5 : 4;
-    f32x4 a = zero4();
+    f32x4 a2[2] = {zero4(), zero4()};  // two chains over alternate K steps
 #pragma unroll
     for (int ks = 0; ks < 8; ks++)
-        a = mfma_bf16(load8_as_halves(sPK + (16 * jb + r16) * S::RK + 32 * ks + 8 * g),
-                      load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g), a);
+        a2[ks & 1] = mfma_bf16(load8_as_halves(sPK + (16 * jb + r16) * S::RK + 32 * ks + 8 * g),
+                               load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g), a2[ks & 1]);
+    f32x4 a = a2[0] + a2[1];
     // a = A^T[j][i]: lane holds i = 16 ib + r16, j = 16 jb + 4 g + r; keep j <= i
     if (jb == ib) {
 #pragma unroll
@@ -1141,7 +1165,7 @@ __device__ __forceinline__ void cws_scores(const bf16_t *sPQ, const bf16_t *sPK,
     store4(sA + (16 * ib + r16) * S::RA + 16 * jb + 4 * g, ab);
     rs += __shfl_xor(rs, 16);
     rs += __shfl_xor(rs, 32);
-    if (g == 0) sDen[slot * S::C + 16 * ib + r16] = rs;
+    sDen[slot * S::C + 16 * ib + r16] = rs;  // the same value in all four lane groups
 }
 
 // Consumer: finish the outputs of one chunk (held read-out + intra-chunk product, normalise,
@@ -1315,7 +1339,13 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
         // 64 pv .. 64 pv + 63 (K steps 2 pv and 2 pv + 1)
 #pragma unroll
         for (int ib = 0; ib < 2; ib++) numT[ib][0] = numT[ib][1] = zero4();
-        // (no branches inside the unrolled loops: each branch would end a scheduling region)
+        // The state update of K step ks (feature blocks 2 ks, 2 ks + 1) follows that step's read-out,
+        // which has already taken the state's bf16 operand: one branch-free region with
+        // independent LDS reads and products to overlap.
+        const bf16_t *sV = v_buf(c % 3);
+        bf16x8 vop[2];
+#pragma unroll
+        for (int vb = 0; vb < 2; vb++) vop[vb] = operand_down_rows(sV, lane_v, 4 * vb, S::D);
 #pragma unroll
         for (int ks = 0; ks < 8; ks++) {
             bf16x8 sb[2];
@@ -1326,6 +1356,12 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
                 const bf16x8 qop = load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g);
 #pragma unroll
                 for (int vb = 0; vb < 2; vb++) numT[ib][vb] = mfma_bf16(sb[vb], qop, numT[ib][vb]);
+            }
+#pragma unroll
+            for (int fb = 2 * ks; fb < 2 * ks + 2; fb++) {
+                const bf16x8 a = operand_down_rows(sPK, lane_k, perm_block_pos(fb), S::RK);
+#pragma unroll
+                for (int vb = 0; vb < 2; vb++) sacc[fb][vb] = mfma_bf16(a, vop[vb], sacc[fb][vb]);
             }
         }
         f32x4 dacc[2] = {zero4(), zero4()};
@@ -1339,23 +1375,11 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
                     dacc[ib] = mfma_bf16(zop, load8(sPQz + (16 * ib + r16) * S::RQ + 32 * kz + 8 * g), dacc[ib]);
             }
         }
+        // every row of dacc holds the token's partial: all four lane groups write the same value
         float *sDen = den_buf(b2);
-        if (g == 0) {
-            sDen[pv * S::C + r16] = dacc[0][0];
-            sDen[pv * S::C + 16 + r16] = dacc[1][0];
-        }
-        // state update with this chunk
-        const bf16_t *sV = v_buf(c % 3);
-        bf16x8 vop[2];
-#pragma unroll
-        for (int vb = 0; vb < 2; vb++) vop[vb] = operand_down_rows(sV, lane_v, 4 * vb, S::D);
-#pragma unroll
-        for (int fb = 0; fb < 16; fb++) {
-            const bf16x8 a = operand_down_rows(sPK, lane_k, perm_block_pos(fb), S::RK);
-#pragma unroll
-            for (int vb = 0; vb < 2; vb++) sacc[fb][vb] = mfma_bf16(a, vop[vb], sacc[fb][vb]);
-        }
-        {
+        sDen[pv * S::C + r16] = dacc[0][0];
+        sDen[pv * S::C + 16 + r16] = dacc[1][0];
+        {  // normaliser rows of this consumer
             const bf16_t *sPKz = sPK + perm_block_pos(4 * pv);
 #pragma unroll
             for (int zb = 0; zb < 4; zb++)
