@@ -1069,67 +1069,62 @@ struct CausalWsCfg {
     static_assert(D * D * 2 <= 2 * SZ_PQ + 2 * SZ_PK, "W fits in the feature tiles");
 };
 
-// Producer: q and k features of one 32-token chunk for directions 32 p .. 32 p + 31.  All
+// Producer p: q and k features of token block p & 1 of a 32-token chunk, for directions
+// 64 (p >> 1) .. 64 (p >> 1) + 63 (so each producer reads only its 16 tokens of q and k).  All
 // operand reads first, then the eight independent product chains, then the exponentials, so
 // that one wave keeps the LDS, matrix and vector pipes busy at once.
 __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsigned char *xk, int valid,
-                                             const bf16x8 (&wA)[2][4], const float (&bl2)[2][4], int p, int g,
+                                             const bf16x8 (&wA)[4][4], const float (&bl2)[4][4], int p, int g,
                                              int r16, bf16_t *sPQ, bf16_t *sPK) {
     using S = CausalWsCfg;
-    bf16x8 xb[2][2][4];  // [keys, queries][token block][K step]
+    const int i = 16 * (p & 1) + r16;
+    bf16x8 xb[2][4];  // [keys, queries][K step]
 #pragma unroll
     for (int t = 0; t < 2; t++)
 #pragma unroll
-        for (int ib = 0; ib < 2; ib++)
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) xb[t][ib][ks] = staged_x_operand<128>(t == 0 ? xk : xq, 16 * ib + r16, ks, g);
-    f32x4 acc[2][2][2];
+        for (int ks = 0; ks < 4; ks++) xb[t][ks] = staged_x_operand<128>(t == 0 ? xk : xq, i, ks, g);
+    f32x4 acc[2][4];
 #pragma unroll
     for (int t = 0; t < 2; t++)
 #pragma unroll
-        for (int ib = 0; ib < 2; ib++)
-#pragma unroll
-            for (int mb = 0; mb < 2; mb++) acc[t][ib][mb] = zero4();
+        for (int mb = 0; mb < 4; mb++) acc[t][mb] = zero4();
 #pragma unroll
     for (int ks = 0; ks < 4; ks++)
 #pragma unroll
         for (int t = 0; t < 2; t++)
 #pragma unroll
-            for (int ib = 0; ib < 2; ib++)
-#pragma unroll
-                for (int mb = 0; mb < 2; mb++) acc[t][ib][mb] = mfma_bf16(wA[mb][ks], xb[t][ib][ks], acc[t][ib][mb]);
-    const int f = 32 * p + 4 * g;  // both direction blocks: positions 8 g .. 8 g + 7 of the group
+            for (int mb = 0; mb < 4; mb++) acc[t][mb] = mfma_bf16(wA[mb][ks], xb[t][ks], acc[t][mb]);
+    const int f0 = 64 * (p >> 1) + 4 * g;
 #pragma unroll
     for (int t = 0; t < 2; t++) {  // 0: keys, 1: queries
+        bf16x4 pe[4], ne[4];
 #pragma unroll
-        for (int ib = 0; ib < 2; ib++) {
-            const int i = 16 * ib + r16;
-            bf16x4 pe[2], ne[2];
+        for (int mb = 0; mb < 4; mb++) {
+            f32x4 ep, en;
 #pragma unroll
-            for (int mb = 0; mb < 2; mb++) {
-                f32x4 ep, en;
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const float u = acc[t][ib][mb][r] * kLog2e + bl2[mb][r];
-                    ep[r] = exp2_fast(u);
-                    en[r] = exp2_fast(-u);
-                }
-                if (t == 0 && i >= valid) {  // keys past the end contribute nothing
-                    ep = zero4();
-                    en = zero4();
-                }
-                pe[mb] = to_bf16x4(ep);
-                ne[mb] = to_bf16x4(en);
+            for (int r = 0; r < 4; r++) {
+                const float u = acc[t][mb][r] * kLog2e + bl2[mb][r];
+                ep[r] = exp2_fast(u);
+                en[r] = exp2_fast(-u);
             }
-            if (t == 0) {
+            if (t == 0 && i >= valid) {  // keys past the end contribute nothing
+                ep = zero4();
+                en = zero4();
+            }
+            pe[mb] = to_bf16x4(ep);
+            ne[mb] = to_bf16x4(en);
+        }
+        if (t == 0) {
 #pragma unroll
-                for (int mb = 0; mb < 2; mb++) {
-                    store4(sPK + i * S::RK + feat_pos<true>(f + 16 * mb), pe[mb]);
-                    store4(sPK + i * S::RK + feat_pos<true>(128 + f + 16 * mb), ne[mb]);
-                }
-            } else {
-                store8(sPQ + i * S::RQ + feat_pos<true>(f), cat(pe[0], pe[1]));
-                store8(sPQ + i * S::RQ + feat_pos<true>(128 + f), cat(ne[0], ne[1]));
+            for (int mb = 0; mb < 4; mb++) {
+                store4(sPK + i * S::RK + feat_pos<true>(f0 + 16 * mb), pe[mb]);
+                store4(sPK + i * S::RK + feat_pos<true>(128 + f0 + 16 * mb), ne[mb]);
+            }
+        } else {  // direction blocks 2 h, 2 h + 1 share one 16-byte run of their 32-feature group
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++) {
+                store8(sPQ + i * S::RQ + feat_pos<true>(f0 + 32 * hh), cat(pe[2 * hh], pe[2 * hh + 1]));
+                store8(sPQ + i * S::RQ + feat_pos<true>(128 + f0 + 32 * hh), cat(ne[2 * hh], ne[2 * hh + 1]));
             }
         }
     }
@@ -1248,10 +1243,23 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
 
     // The two roles run separate loops with the same barriers, one per chunk.
     if (w < 4) {
-        bf16x8 wA[2][4];
-        float bl2[2][4];
-        load_w_operands<128>(smem + S::OFF_W, pv, g, r16, wA);
-        load_bias<128>(p.b, h, pv, g, bl2);
+        // directions 64 (pv >> 1) .. + 63: the two 32-direction groups 2 (pv >> 1), 2 (pv >> 1) + 1
+        bf16x8 wA[4][4];
+        float bl2[4][4];
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+            bf16x8 w2[2][4];
+            float b2[2][4];
+            load_w_operands<128>(smem + S::OFF_W, 2 * (pv >> 1) + hh, g, r16, w2);
+            load_bias<128>(p.b, h, 2 * (pv >> 1) + hh, g, b2);
+#pragma unroll
+            for (int mb = 0; mb < 2; mb++) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) wA[2 * hh + mb][ks] = w2[mb][ks];
+#pragma unroll
+                for (int r = 0; r < 4; r++) bl2[2 * hh + mb][r] = b2[mb][r];
+            }
+        }
         __syncthreads();  // W shares space with the feature tiles
         if (n > 0)
             cws_features(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, pv, g, r16, pq_buf(0), pk_buf(0));
