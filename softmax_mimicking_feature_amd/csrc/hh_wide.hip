@@ -881,25 +881,31 @@ struct StateWsCfg {
     static_assert(D * D * 2 <= 2 * SZ_PK, "W fits in the feature tiles");
 };
 
-// Producer wave p: features of directions 32 p .. 32 p + 31 for the 64 tokens of one chunk.
-__device__ __forceinline__ void ws_produce(const unsigned char *stage, int valid, const bf16x8 (&wA)[2][4],
-                                           const float (&bl2)[2][4], int p, int g, int r16, bf16_t *sPK) {
+// Producer wave p: key features of token blocks 2 (p & 1), 2 (p & 1) + 1 of a 64-token chunk for
+// directions 64 (p >> 1) .. + 63 (each producer reads only its 32 tokens of k).
+__device__ __forceinline__ void ws_produce(const unsigned char *stage, int valid, const bf16x8 (&wA)[4][4],
+                                           const float (&bl2)[4][4], int p, int g, int r16, bf16_t *sPK) {
     using S = StateWsCfg;
+    const int f0 = 64 * (p >> 1) + 4 * g;
 #pragma unroll
-    for (int ib = 0; ib < 4; ib++) {
-        const int i = 16 * ib + r16;
+    for (int ibl = 0; ibl < 2; ibl++) {
+        const int i = 16 * (2 * (p & 1) + ibl) + r16;
         bf16x8 xb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ks++) xb[ks] = staged_x_operand<128>(stage, i, ks, g);
+        f32x4 acc[4];
 #pragma unroll
-        for (int mb = 0; mb < 2; mb++) {
-            f32x4 a = zero4();
+        for (int mb = 0; mb < 4; mb++) acc[mb] = zero4();
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) a = mfma_bf16(wA[mb][ks], xb[ks], a);
+        for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++) acc[mb] = mfma_bf16(wA[mb][ks], xb[ks], acc[mb]);
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) {
             f32x4 ep, en;
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const float u = a[r] * kLog2e + bl2[mb][r];
+                const float u = acc[mb][r] * kLog2e + bl2[mb][r];
                 ep[r] = exp2_fast(u);
                 en[r] = exp2_fast(-u);
             }
@@ -907,9 +913,8 @@ __device__ __forceinline__ void ws_produce(const unsigned char *stage, int valid
                 ep = zero4();
                 en = zero4();
             }
-            const int f = 32 * p + 16 * mb + 4 * g;
-            store4(sPK + i * S::RK + feat_pos<true>(f), to_bf16x4(ep));
-            store4(sPK + i * S::RK + feat_pos<true>(128 + f), to_bf16x4(en));
+            store4(sPK + i * S::RK + feat_pos<true>(f0 + 16 * mb), to_bf16x4(ep));
+            store4(sPK + i * S::RK + feat_pos<true>(128 + f0 + 16 * mb), to_bf16x4(en));
         }
     }
 }
@@ -957,10 +962,23 @@ __global__ __launch_bounds__(512, 1) void state_ws_kernel_128(WideParams p) {
 
     // The two roles run separate loops with the same barriers, one per chunk.
     if (w < 4) {
-        bf16x8 wA[2][4];
-        float bl2[2][4];
-        load_w_operands<128>(smem + S::OFF_W, c4, g, r16, wA);
-        load_bias<128>(p.b, h, c4, g, bl2);
+        // directions 64 (c4 >> 1) .. + 63: the two 32-direction groups 2 (c4 >> 1), 2 (c4 >> 1) + 1
+        bf16x8 wA[4][4];
+        float bl2[4][4];
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+            bf16x8 w2[2][4];
+            float b2[2][4];
+            load_w_operands<128>(smem + S::OFF_W, 2 * (c4 >> 1) + hh, g, r16, w2);
+            load_bias<128>(p.b, h, 2 * (c4 >> 1) + hh, g, b2);
+#pragma unroll
+            for (int mb = 0; mb < 2; mb++) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) wA[2 * hh + mb][ks] = w2[mb][ks];
+#pragma unroll
+                for (int r = 0; r < 4; r++) bl2[2 * hh + mb][r] = b2[mb][r];
+            }
+        }
         __syncthreads();  // W shares space with the feature tiles
         if (n > 0) ws_produce(smem + S::OFF_XK, valid_of(0), wA, bl2, c4, g, r16, reinterpret_cast<bf16_t *>(smem + S::OFF_PK));
         __syncthreads();
