@@ -198,7 +198,10 @@ hipError_t launch_seq_f32(const SeqParams &p, int BH, hipStream_t st) {
 // Decode step.  One workgroup per (b,h): features of the new q and k, then one streaming
 // pass over S [dp][d] (read, add phi(k) v^T, write back, accumulate phi(q)^T S), float4
 // per thread.  Thread t always touches column quad t % (d/4).
-constexpr int kDecThreads = 256;
+#ifndef HH_DEC_THREADS
+#define HH_DEC_THREADS 256
+#endif
+constexpr int kDecThreads = HH_DEC_THREADS;
 
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     __shared__ float sq[128], sk[128], sv[128];
@@ -215,12 +218,50 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     __syncthreads();
     const void *W = p.W;
     const size_t woff = (size_t)h * d * d;
-    auto wrow = [&](int l, int m) { return ld(W, woff + (size_t)l * d + m, dt); };
-    for (int f = t; f < dp; f += kDecThreads) {
-        const int l = f < d ? f : f - d;
-        const float bl = (p.map == 0 && p.b) ? ld(p.b, (size_t)h * d + l, dt) : 0.0f;
-        sfk[f] = feature_value(p.map, d, f, sk, wrow, bl);
-        sfq[f] = feature_value(p.map, d, f, sq, wrow, bl);
+    if (p.map == 0) {
+        // u = W x for q and k together: kDecThreads / d consecutive threads share a row of W and
+        // read contiguous pieces of it, then combine their partial dot products
+        const int tpr = kDecThreads / d < d ? kDecThreads / d : d;
+        const int l = t / tpr, part = t % tpr, ept = d / tpr;
+        float uq = 0.0f, uk = 0.0f;
+        const size_t ro = woff + (size_t)(l < d ? l : 0) * d + (size_t)part * ept;
+        if (l >= d) {
+            // spare threads (more threads than d rows x d elements): nothing to add
+        } else if (dt == 1 && ept % 8 == 0) {
+            const bf16x8 *wr = reinterpret_cast<const bf16x8 *>(reinterpret_cast<const bf16_t *>(W) + ro);
+            for (int j = 0; j < ept / 8; j++) {
+                const bf16x8 wv = wr[j];
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const float wf = (float)wv[e];
+                    uq = fmaf(wf, sq[part * ept + 8 * j + e], uq);
+                    uk = fmaf(wf, sk[part * ept + 8 * j + e], uk);
+                }
+            }
+        } else {
+            for (int m = 0; m < ept; m++) {
+                const float wf = ld(W, ro + m, dt);
+                uq = fmaf(wf, sq[part * ept + m], uq);
+                uk = fmaf(wf, sk[part * ept + m], uk);
+            }
+        }
+        for (int o = tpr / 2; o > 0; o >>= 1) {
+            uq += __shfl_xor(uq, o);
+            uk += __shfl_xor(uk, o);
+        }
+        if (part == 0 && l < d) {
+            const float bl = p.b ? ld(p.b, (size_t)h * d + l, dt) : 0.0f;
+            sfq[l] = expf(uq + bl);
+            sfq[d + l] = expf(-(uq + bl));
+            sfk[l] = expf(uk + bl);
+            sfk[d + l] = expf(-(uk + bl));
+        }
+    } else {
+        auto wrow = [&](int l, int m) { return ld(W, woff + (size_t)l * d + m, dt); };
+        for (int f = t; f < dp; f += kDecThreads) {
+            sfk[f] = feature_value(p.map, d, f, sk, wrow, 0.0f);
+            sfq[f] = feature_value(p.map, d, f, sq, wrow, 0.0f);
+        }
     }
     __syncthreads();
 
@@ -230,7 +271,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     f32x4 *S4 = reinterpret_cast<f32x4 *>(p.S + (size_t)bh * dp * d);
     const int n4 = dp * q4;
     f32x4 acc = zero4();
-#pragma unroll 8
+#pragma unroll 16
     for (int e4 = t; e4 < n4; e4 += kDecThreads) {
         const int f = e4 / q4;
         f32x4 s = __builtin_nontemporal_load(S4 + e4);
