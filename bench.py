@@ -36,6 +36,7 @@ from softmax_mimicking_feature_amd import workloads as wl  # noqa: E402
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 PEAK_MFMA_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 N_SETS = 4
+GRAPH_STEPS = 20                 # calls per captured graph (a multiple of N_SETS)
 METRIC = "causal linear-attn fwd tokens/s (\u03c6 incl.) at Llama-2-7B heads; % MFMA peak"
 
 
@@ -111,6 +112,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c3_llama2_causal", choices=sorted(wl.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from Python instead of replaying captured HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -174,43 +177,66 @@ def main():
             del kq, vv
         outs = [torch.empty((w.B, w.H, w.d), dtype=tdt, device=dev) for _ in range(N_SETS)]
 
-        def step(i):
+        def step(i, st):
             s = sets[i % N_SETS]
             S, z = states[i % N_SETS]
             hh.hh_linattn_decode_step(s["q"], s["k"], s["v"], W, b, S, z, map=w.map, out=outs[i % N_SETS],
-                                      stream=stream)
+                                      stream=st)
         flops, byts = decode_counts(w)
     else:
         need = hh.hh_linattn_fwd_workspace(w.map, w.dtype, w.causal, w.B, w.H, w.N, w.d)
         wss = [torch.empty((max(need, 16),), dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
         outs = [torch.empty_like(sets[0]["q"]) for _ in range(N_SETS)]
 
-        def step(i):
+        def step(i, st):
             s = sets[i % N_SETS]
             hh.hh_linattn_fwd(s["q"], s["k"], s["v"], W, b, causal=w.causal, map=w.map, out=outs[i % N_SETS],
-                              workspace=wss[i % N_SETS], stream=stream)
+                              workspace=wss[i % N_SETS], stream=st)
         flops, byts = algorithmic_counts(w)
 
-    for i in range(args.warmup):
-        step(i)
+    # GRAPH_STEPS consecutive calls (cycling over the input sets) captured as one HIP graph, so
+    # that host launch cost stays out of the timed region (a decode step is shorter than a
+    # Python call); a "launch" below is then one replay of GRAPH_STEPS calls.  --eager launches
+    # every call from Python.
+    gsteps = 1 if args.eager else GRAPH_STEPS
+    if args.steps % gsteps:
+        args.steps += gsteps - args.steps % gsteps
+    if args.eager:
+        def run(i):
+            step(i, stream)
+    else:
+        for j in range(N_SETS):
+            step(j, stream)  # each input set once before capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for j in range(gsteps):
+                step(j, torch.cuda.current_stream())
+
+        def run(i):
+            graph.replay()
+
+    for i in range(max(1, args.warmup // gsteps)):
+        run(i)
     torch.cuda.synchronize()
 
     # ---- timed region: K steps, per-launch events on the launch stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    nlaunch = args.steps // gsteps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nlaunch)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for i in range(args.steps):
+    for i in range(nlaunch):
         ev[i][0].record(stream)
-        step(i)
+        run(i)
         ev[i][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    per = np.array([a.elapsed_time(bq) for a, bq in ev])
+    per = np.array([a.elapsed_time(bq) for a, bq in ev]) / gsteps  # per call
     ms_per_step = total_ms / args.steps
     launch_ms = float(per.mean())
 
@@ -232,6 +258,7 @@ def main():
     roof["kernel"] = ("hh_linattn_decode_step (decode_kernel)" if decode else
                       "hh_linattn_fwd: the segment-state, segment-scan and chunked kernels of one call")
     roof["launch_ms_mean"] = round(launch_ms, 5)
+    roof["calls_per_timed_launch"] = gsteps  # a timed launch: one graph replay of this many calls
     roof["launch_ms_p10_p90"] = [round(float(np.percentile(per, 10)), 5), round(float(np.percentile(per, 90)), 5)]
     roof["alg_flops"] = flops
     roof["alg_bytes"] = byts
@@ -271,7 +298,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "map": "hedgehog" if w.map == wl.MAP_HEDGEHOG else "taylor2", "causal": w.causal,
-                   "input_sets_rotated": N_SETS},
+                   "input_sets_rotated": N_SETS, "launch": "eager" if args.eager else "hip_graph_replay"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),

@@ -356,3 +356,64 @@ def test_decode_taylor_small():
     rtol, atol = wl.tolerance(w.dtype)
     assert_close(host(y), yo, rtol, atol, "taylor decode y")
     assert_close(S.cpu().numpy(), So, 1e-5, 1e-4, "taylor decode S")
+
+
+# ------------------------------------------------------------------ graph capture ----
+
+@pytest.mark.parametrize("d,causal", [(128, True), (64, True), (64, False)])
+def test_graph_replay_matches_eager(d, causal):
+    # The library's calls can be captured into a HIP graph (no allocation, no memset inside):
+    # every replay, with other eager work in between, reproduces the eager result bit for bit.
+    m = hh()
+    w = small("c3_llama2_causal", B=1, H=8, N=2048, d=d, w_std=d ** -0.5, seed=9300 + d, causal=causal)
+    say(f"graph replay d={d} causal={causal}")
+    x = wl.make_inputs(w)
+    x2 = wl.make_inputs(w.replace(seed=w.seed + 1))
+    dt = TORCH_DT[w.dtype]
+    q, k, v, W, b = (dev(x[n], dt) for n in ("q", "k", "v", "W", "b"))
+    q2, k2, v2 = (dev(x2[n], dt) for n in ("q", "k", "v"))
+    need = m.hh_linattn_fwd_workspace(w.map, w.dtype, int(causal), w.B, w.H, w.N, w.d)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty_like(ws)
+    y_eager = m.hh_linattn_fwd(q, k, v, W, b, causal=causal, map=w.map, workspace=ws)
+    torch.cuda.synchronize()
+    y_g = torch.empty_like(q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.hh_linattn_fwd(q, k, v, W, b, causal=causal, map=w.map, out=y_g, workspace=ws,
+                         stream=torch.cuda.current_stream())
+    for rep in range(3):
+        y_g.zero_()
+        g.replay()
+        other = m.hh_linattn_fwd(q2, k2, v2, W, b, causal=causal, map=w.map, workspace=ws2)  # eager in between
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_eager), f"replay {rep} differs from the eager call"
+        del other
+
+
+def test_graph_replay_decode_matches_eager():
+    m = hh()
+    w = wl.CONFIGS["c3_llama2_decode"].replace(B=2, H=4)
+    say("graph replay decode")
+    g_ = torch.Generator(device="cuda")
+    g_.manual_seed(77)
+    dp = 2 * w.d
+    shp = (w.B, w.H, w.d)
+    q, k, v = ((torch.randn(shp, generator=g_, device="cuda") * 0.3).bfloat16() for _ in range(3))
+    W = (torch.randn((w.H, w.d, w.d), generator=g_, device="cuda") * w.d ** -0.5).bfloat16()
+    S0 = torch.rand((w.B, w.H, dp, w.d), generator=g_, device="cuda")
+    z0 = torch.rand((w.B, w.H, dp), generator=g_, device="cuda") + 1.0
+    S_e, z_e = S0.clone(), z0.clone()
+    y_e = m.hh_linattn_decode_step(q, k, v, W, None, S_e, z_e)
+    torch.cuda.synchronize()
+    S_g, z_g = S0.clone(), z0.clone()
+    y_g = torch.empty_like(q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.hh_linattn_decode_step(q, k, v, W, None, S_g, z_g, out=y_g, stream=torch.cuda.current_stream())
+    for rep in range(3):
+        S_g.copy_(S0)
+        z_g.copy_(z0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e) and torch.equal(S_g, S_e) and torch.equal(z_g, z_e), f"replay {rep}"
