@@ -1372,23 +1372,32 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
         bf16x8 vop[2];
 #pragma unroll
         for (int vb = 0; vb < 2; vb++) vop[vb] = operand_down_rows(sV, lane_v, 4 * vb, S::D);
+        // Operands of K step ks + 1 are read while the products of step ks run (one step of
+        // software pipelining; the scheduling fences keep the reads ahead of the products).
+        bf16x8 qn[2], an[2];
+        auto load_step = [&](int ks, bf16x8(&qo)[2], bf16x8(&ao)[2]) {
+#pragma unroll
+            for (int ib = 0; ib < 2; ib++) qo[ib] = load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g);
+#pragma unroll
+            for (int j = 0; j < 2; j++) ao[j] = operand_down_rows(sPK, lane_k, perm_block_pos(2 * ks + j), S::RK);
+        };
+        load_step(0, qn, an);
 #pragma unroll
         for (int ks = 0; ks < 8; ks++) {
+            bf16x8 qc[2] = {qn[0], qn[1]}, ac[2] = {an[0], an[1]};
+            if (ks < 7) load_step(ks + 1, qn, an);
             bf16x8 sb[2];
 #pragma unroll
             for (int vb = 0; vb < 2; vb++) sb[vb] = acc_pair_to_operand(sacc[2 * ks][vb], sacc[2 * ks + 1][vb]);
 #pragma unroll
-            for (int ib = 0; ib < 2; ib++) {
-                const bf16x8 qop = load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g);
+            for (int ib = 0; ib < 2; ib++)
 #pragma unroll
-                for (int vb = 0; vb < 2; vb++) numT[ib][vb] = mfma_bf16(sb[vb], qop, numT[ib][vb]);
-            }
+                for (int vb = 0; vb < 2; vb++) numT[ib][vb] = mfma_bf16(sb[vb], qc[ib], numT[ib][vb]);
 #pragma unroll
-            for (int fb = 2 * ks; fb < 2 * ks + 2; fb++) {
-                const bf16x8 a = operand_down_rows(sPK, lane_k, perm_block_pos(fb), S::RK);
+            for (int j = 0; j < 2; j++)
 #pragma unroll
-                for (int vb = 0; vb < 2; vb++) sacc[fb][vb] = mfma_bf16(a, vop[vb], sacc[fb][vb]);
-            }
+                for (int vb = 0; vb < 2; vb++) sacc[2 * ks + j][vb] = mfma_bf16(ac[j], vop[vb], sacc[2 * ks + j][vb]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         f32x4 dacc[2] = {zero4(), zero4()};
         {
