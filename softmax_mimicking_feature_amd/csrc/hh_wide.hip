@@ -1161,11 +1161,17 @@ __device__ __forceinline__ void cws_scores(const bf16_t *sPQ, const bf16_t *sPK,
         return;
     }
     const int ib = p == 0 ? 0 : 1, jb = p == 2 ? 1 : 0, slot = p == 2 ? 5 : 4;
-    f32x4 a2[2] = {zero4(), zero4()};  // two chains over alternate K steps
+    // all operand reads first, then two product chains over alternate K steps
+    bf16x8 ka[8], qb[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ks++)
-        a2[ks & 1] = mfma_bf16(load8_as_halves(sPK + (16 * jb + r16) * S::RK + 32 * ks + 8 * g),
-                               load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g), a2[ks & 1]);
+    for (int ks = 0; ks < 8; ks++) {
+        ka[ks] = load8_as_halves(sPK + (16 * jb + r16) * S::RK + 32 * ks + 8 * g);
+        qb[ks] = load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 a2[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int ks = 0; ks < 8; ks++) a2[ks & 1] = mfma_bf16(ka[ks], qb[ks], a2[ks & 1]);
     f32x4 a = a2[0] + a2[1];
     // a = A^T[j][i]: lane holds i = 16 ib + r16, j = 16 jb + 4 g + r; keep j <= i
     if (jb == ib) {
@@ -1278,6 +1284,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
                 for (int r = 0; r < 4; r++) bl2[2 * hh + mb][r] = b2[mb][r];
             }
         }
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // W shares space with the feature tiles
         if (n > 0)
             cws_features(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, pv, g, r16, pq_buf(0), pk_buf(0));
@@ -1355,49 +1362,90 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     for (int c = 0; c < n; c++) {
         cws_issue(p, base, t_begin, t_end, c, n, w, lane, smem);
         const int b2 = c & 1;
-        // outputs of the previous chunk
-        if (c > 0)
-            cws_output(numT, a_buf(b2 ^ 1), v_buf((c + 2) % 3), den_buf(b2 ^ 1), lane_v,
-                       ybase + (size_t)(t_begin + S::C * (c - 1)) * S::D, S::C, pv, g, r16);
         const bf16_t *sPQ = pq_buf(b2);
         const bf16_t *sPK = pk_buf(b2);
-        // read-out of this chunk (transposed) and the normaliser partial over features
-        // 64 pv .. 64 pv + 63 (K steps 2 pv and 2 pv + 1)
+        // One branch-free stream per chunk: the outputs of chunk c - 1 (intra-chunk product with
+        // its scores, normalisation, store) ride along the first K steps of the read-out of chunk
+        // c (transposed, into nt) and the state update with chunk c.  The state update of K step
+        // ks (feature blocks 2 ks, 2 ks + 1) follows that step's read-out, which has already taken
+        // the state's bf16 operand.  Operands of K step ks + 1 are read while the products of
+        // step ks run; the scheduling fences keep the reads ahead of the products.
+        const bf16_t *sVp = v_buf((c + 2) % 3);
+        const bf16_t *sAp = a_buf(b2 ^ 1);
+        const float *sDp = den_buf(b2 ^ 1);
+        bf16x8 vp[2], ao[2];
 #pragma unroll
-        for (int ib = 0; ib < 2; ib++) numT[ib][0] = numT[ib][1] = zero4();
-        // The state update of K step ks (feature blocks 2 ks, 2 ks + 1) follows that step's read-out,
-        // which has already taken the state's bf16 operand: one branch-free region with
-        // independent LDS reads and products to overlap.
+        for (int vb = 0; vb < 2; vb++) vp[vb] = operand_down_rows(sVp, lane_v, 4 * vb, S::D);
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++) ao[ib] = load8(sAp + (16 * ib + r16) * S::RA + 8 * g);
         const bf16_t *sV = v_buf(c % 3);
         bf16x8 vop[2];
 #pragma unroll
         for (int vb = 0; vb < 2; vb++) vop[vb] = operand_down_rows(sV, lane_v, 4 * vb, S::D);
-        // Operands of K step ks + 1 are read while the products of step ks run (one step of
-        // software pipelining; the scheduling fences keep the reads ahead of the products).
         bf16x8 qn[2], an[2];
-        auto load_step = [&](int ks, bf16x8(&qo)[2], bf16x8(&ao)[2]) {
+        auto load_step = [&](int ks, bf16x8(&qo)[2], bf16x8(&ao2)[2]) {
 #pragma unroll
             for (int ib = 0; ib < 2; ib++) qo[ib] = load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g);
 #pragma unroll
-            for (int j = 0; j < 2; j++) ao[j] = operand_down_rows(sPK, lane_k, perm_block_pos(2 * ks + j), S::RK);
+            for (int j = 0; j < 2; j++) ao2[j] = operand_down_rows(sPK, lane_k, perm_block_pos(2 * ks + j), S::RK);
         };
         load_step(0, qn, an);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 nt[2][2];
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++) nt[ib][0] = nt[ib][1] = zero4();
+        float dsum[2];
 #pragma unroll
         for (int ks = 0; ks < 8; ks++) {
             bf16x8 qc[2] = {qn[0], qn[1]}, ac[2] = {an[0], an[1]};
             if (ks < 7) load_step(ks + 1, qn, an);
+            if (ks == 0) {  // intra-chunk product of chunk c - 1
+#pragma unroll
+                for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+                    for (int vb = 0; vb < 2; vb++) numT[ib][vb] = mfma_bf16(vp[vb], ao[ib], numT[ib][vb]);
+            }
+            if (ks == 1) {  // its normaliser: the partial slots of every wave
+#pragma unroll
+                for (int ib = 0; ib < 2; ib++) {
+                    float d = 0.0f;
+#pragma unroll
+                    for (int sl = 0; sl < S::NDEN; sl++) d += sDp[sl * S::C + 16 * ib + r16];
+                    dsum[ib] = d;
+                }
+            }
             bf16x8 sb[2];
 #pragma unroll
             for (int vb = 0; vb < 2; vb++) sb[vb] = acc_pair_to_operand(sacc[2 * ks][vb], sacc[2 * ks + 1][vb]);
 #pragma unroll
             for (int ib = 0; ib < 2; ib++)
 #pragma unroll
-                for (int vb = 0; vb < 2; vb++) numT[ib][vb] = mfma_bf16(sb[vb], qc[ib], numT[ib][vb]);
+                for (int vb = 0; vb < 2; vb++) nt[ib][vb] = mfma_bf16(sb[vb], qc[ib], nt[ib][vb]);
 #pragma unroll
             for (int j = 0; j < 2; j++)
 #pragma unroll
                 for (int vb = 0; vb < 2; vb++) sacc[2 * ks + j][vb] = mfma_bf16(ac[j], vop[vb], sacc[2 * ks + j][vb]);
+            if (ks == 2 && c > 0) {  // outputs of chunk c - 1 (every token of it is valid)
+                bf16_t *yrow0 = ybase + (size_t)(t_begin + S::C * (c - 1)) * S::D;
+#pragma unroll
+                for (int ib = 0; ib < 2; ib++) {
+                    const float rden = __builtin_amdgcn_rcpf(dsum[ib]);
+                    f32x4 o0, o1;
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        o0[r] = numT[ib][0][r] * rden;
+                        o1[r] = numT[ib][1][r] * rden;
+                    }
+                    store8(yrow0 + (size_t)(16 * ib + r16) * S::D + value_col<2>(pv, 0, 4 * g),
+                           cat(to_bf16x4(o0), to_bf16x4(o1)));
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++) {
+            numT[ib][0] = nt[ib][0];
+            numT[ib][1] = nt[ib][1];
         }
         f32x4 dacc[2] = {zero4(), zero4()};
         {
