@@ -226,6 +226,44 @@ __device__ __forceinline__ void load_to_lds_16(const void *gsrc, void *lds_dst_u
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gsrc), "s"(lds) : "m0");
 }
 
+// The same from a uniform base address (SGPRs) plus a 32-bit per-lane byte offset, so that the
+// per-chunk address is one scalar add instead of per-lane 64-bit arithmetic.
+__device__ __forceinline__ void load_to_lds_16s(const void *sbase, uint32_t voff, void *lds_dst_uniform) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_dst_uniform));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
+                 : "m0");
+}
+
+// Per-lane source offsets of the direct loads of [C][128] bf16 tiles by 8 waves (wave w moves
+// 1 KB blocks w, w + 8, ...): byte offsets within the tile's rows for the q / k staging layout
+// (stage_pos) and the V layout (v_pos), the offset used when the lane's row lies past the end
+// (it then reads row 0, whose granule P is stored at position P in both layouts), and the row.
+template <int C>
+struct DmaLanes128 {
+    static constexpr int NB = C / 32;
+    uint32_t ox[NB], ov[NB], o0[NB];
+    int row[NB];
+    __device__ __forceinline__ DmaLanes128(int w, int lane) {
+#pragma unroll
+        for (int bb = 0; bb < NB; bb++) {
+            const int slot = 64 * (w + 8 * bb) + lane;
+            const int r = slot / 16, P = slot % 16;
+            row[bb] = r;
+            ox[bb] = 2 * (r * 128 + 8 * stage_granule<128>(r, P));
+            ov[bb] = 2 * (r * 128 + 8 * ((P - 4 * r) & 15));
+            o0[bb] = 16 * P;
+        }
+    }
+    // tile rows t0 .. t0 + C - 1 of x (valid of them) into `stage`, q / k layout or V layout
+    template <bool V>
+    __device__ __forceinline__ void issue(const bf16_t *x, int t0, int valid, int w, unsigned char *stage) const {
+        const bf16_t *src = x + (size_t)t0 * 128;
+#pragma unroll
+        for (int bb = 0; bb < NB; bb++)
+            load_to_lds_16s(src, row[bb] < valid ? (V ? ov[bb] : ox[bb]) : o0[bb], stage + 1024 * (w + 8 * bb));
+    }
+};
+
 // One [C][D] tile of x into its staging area: wave w moves blocks w, w + NW, ...; lane l of
 // block b lands at slot 64 b + l = (row r, stored position P), which holds granule
 // stage_granule(r, P).  Rows past the end read a valid row (their values are never used).
@@ -921,17 +959,17 @@ __device__ __forceinline__ void ws_produce(const unsigned char *stage, int valid
 
 // Inputs of a chunk two ahead (k) and one ahead (V) into the buffers freed by the last chunk;
 // issued by every wave (each moves its own 1 KB blocks).
-__device__ __forceinline__ void ws_issue(const WideParams &p, size_t base, int t_begin, int t_end, int c, int n, int w,
-                                         int lane, unsigned char *smem) {
+__device__ __forceinline__ void ws_issue(const WideParams &p, const DmaLanes128<64> &dl, size_t base, int t_begin,
+                                         int t_end, int c, int n, int w, unsigned char *smem) {
     using S = StateWsCfg;
     const int b = c & 1;
     if (c + 1 < n) {
         const int t = t_begin + S::C * (c + 1);
-        stage_v<128, 64>(p.v + base, t, min(S::C, t_end - t), w, lane, smem + S::OFF_V + (b ^ 1) * S::SZ_X);
+        dl.issue<true>(p.v + base, t, min(S::C, t_end - t), w, smem + S::OFF_V + (b ^ 1) * S::SZ_X);
     }
     if (c + 2 < n) {
         const int t = t_begin + S::C * (c + 2);
-        stage_x<128, 64>(p.k + base, t, min(S::C, t_end - t), w, lane, smem + S::OFF_XK + b * S::SZ_X);
+        dl.issue<false>(p.k + base, t, min(S::C, t_end - t), w, smem + S::OFF_XK + b * S::SZ_X);
     }
 }
 
@@ -949,6 +987,7 @@ __global__ __launch_bounds__(512, 1) void state_ws_kernel_128(WideParams p) {
     const int t_end = min(p.N, t_begin + p.seg_len);
     const size_t base = (size_t)bh * p.N * S::D;
     const int n = t_end > t_begin ? (t_end - t_begin + S::C - 1) / S::C : 0;
+    const DmaLanes128<64> dl(w, lane);
     auto valid_of = [&](int c) { return min(S::C, t_end - (t_begin + S::C * c)); };
 
     if (n > 0) {
@@ -983,7 +1022,7 @@ __global__ __launch_bounds__(512, 1) void state_ws_kernel_128(WideParams p) {
         if (n > 0) ws_produce(smem + S::OFF_XK, valid_of(0), wA, bl2, c4, g, r16, reinterpret_cast<bf16_t *>(smem + S::OFF_PK));
         __syncthreads();
         for (int c = 0; c < n; c++) {
-            ws_issue(p, base, t_begin, t_end, c, n, w, lane, smem);
+            ws_issue(p, dl, base, t_begin, t_end, c, n, w, smem);
             const int b = c & 1;
             if (c + 1 < n)
                 ws_produce(smem + S::OFF_XK + (b ^ 1) * S::SZ_X, valid_of(c + 1), wA, bl2, c4, g, r16,
@@ -1011,7 +1050,7 @@ __global__ __launch_bounds__(512, 1) void state_ws_kernel_128(WideParams p) {
     __syncthreads();  // (producers: W read)
     __syncthreads();  // (producers: first chunk's features)
     for (int c = 0; c < n; c++) {
-        ws_issue(p, base, t_begin, t_end, c, n, w, lane, smem);
+        ws_issue(p, dl, base, t_begin, t_end, c, n, w, smem);
         const int b = c & 1;
         const bf16_t *sPK = reinterpret_cast<const bf16_t *>(smem + S::OFF_PK + b * S::SZ_PK);
         const bf16_t *sV = reinterpret_cast<const bf16_t *>(smem + S::OFF_V + b * S::SZ_X);
@@ -1217,17 +1256,17 @@ __device__ __forceinline__ void cws_output(f32x4 (&numT)[2][2], const bf16_t *sA
 
 // Inputs of chunk c + 1 (V) and c + 2 (q, k) into the buffers freed by the last chunk; issued by
 // every wave (each moves its own 1 KB blocks).
-__device__ __forceinline__ void cws_issue(const WideParams &p, size_t base, int t_begin, int t_end, int c, int n,
-                                          int w, int lane, unsigned char *smem) {
+__device__ __forceinline__ void cws_issue(const WideParams &p, const DmaLanes128<32> &dl, size_t base, int t_begin,
+                                          int t_end, int c, int n, int w, unsigned char *smem) {
     using S = CausalWsCfg;
     if (c + 1 < n) {
         const int t = t_begin + S::C * (c + 1);
-        stage_v<128, 32>(p.v + base, t, min(S::C, t_end - t), w, lane, smem + S::OFF_V + ((c + 1) % 3) * S::SZ_X);
+        dl.issue<true>(p.v + base, t, min(S::C, t_end - t), w, smem + S::OFF_V + ((c + 1) % 3) * S::SZ_X);
     }
     if (c + 2 < n) {
         const int t = t_begin + S::C * (c + 2), b = c & 1;
-        stage_x<128, 32>(p.q + base, t, min(S::C, t_end - t), w, lane, smem + S::OFF_XQ + b * S::SZ_X);
-        stage_x<128, 32>(p.k + base, t, min(S::C, t_end - t), w, lane, smem + S::OFF_XK + b * S::SZ_X);
+        dl.issue<false>(p.q + base, t, min(S::C, t_end - t), w, smem + S::OFF_XQ + b * S::SZ_X);
+        dl.issue<false>(p.k + base, t, min(S::C, t_end - t), w, smem + S::OFF_XK + b * S::SZ_X);
     }
 }
 
@@ -1245,6 +1284,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     const int t_end = min(p.N, t_begin + p.seg_len);
     const size_t base = (size_t)bh * p.N * S::D;
     const int n = t_end > t_begin ? (t_end - t_begin + S::C - 1) / S::C : 0;
+    const DmaLanes128<32> dl(w, lane);
     auto valid_of = [&](int c) { return min(S::C, t_end - (t_begin + S::C * c)); };
     auto pq_buf = [&](int b) { return reinterpret_cast<bf16_t *>(smem + S::OFF_PQ + b * S::SZ_PQ); };
     auto pk_buf = [&](int b) { return reinterpret_cast<bf16_t *>(smem + S::OFF_PK + b * S::SZ_PK); };
@@ -1290,7 +1330,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
             cws_features(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, pv, g, r16, pq_buf(0), pk_buf(0));
         __syncthreads();
         for (int c = 0; c < n; c++) {
-            cws_issue(p, base, t_begin, t_end, c, n, w, lane, smem);
+            cws_issue(p, dl, base, t_begin, t_end, c, n, w, smem);
             const int b2 = c & 1;
             cws_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), pv, g, r16);
             if (c + 1 < n)
@@ -1360,7 +1400,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     __syncthreads();  // (producers: first chunk's features)
 
     for (int c = 0; c < n; c++) {
-        cws_issue(p, base, t_begin, t_end, c, n, w, lane, smem);
+        cws_issue(p, dl, base, t_begin, t_end, c, n, w, smem);
         const int b2 = c & 1;
         const bf16_t *sPQ = pq_buf(b2);
         const bf16_t *sPK = pk_buf(b2);
