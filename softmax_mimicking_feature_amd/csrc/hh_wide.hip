@@ -921,6 +921,7 @@ struct StateWsCfg {
 
 // Producer wave p: key features of token blocks 2 (p & 1), 2 (p & 1) + 1 of a 64-token chunk for
 // directions 64 (p >> 1) .. + 63 (each producer reads only its 32 tokens of k).
+template <bool FULL>
 __device__ __forceinline__ void ws_produce(const unsigned char *stage, int valid, const bf16x8 (&wA)[4][4],
                                            const float (&bl2)[4][4], int p, int g, int r16, bf16_t *sPK) {
     using S = StateWsCfg;
@@ -947,7 +948,7 @@ __device__ __forceinline__ void ws_produce(const unsigned char *stage, int valid
                 ep[r] = exp2_fast(u);
                 en[r] = exp2_fast(-u);
             }
-            if (i >= valid) {  // keys past the end contribute nothing
+            if (!FULL && i >= valid) {  // keys past the end contribute nothing
                 ep = zero4();
                 en = zero4();
             }
@@ -955,6 +956,15 @@ __device__ __forceinline__ void ws_produce(const unsigned char *stage, int valid
             store4(sPK + i * S::RK + feat_pos<true>(128 + f0 + 16 * mb), to_bf16x4(en));
         }
     }
+}
+
+// Full chunks skip the per-lane masking of keys past the end.
+__device__ __forceinline__ void ws_produce_any(const unsigned char *stage, int valid, const bf16x8 (&wA)[4][4],
+                                               const float (&bl2)[4][4], int p, int g, int r16, bf16_t *sPK) {
+    if (valid >= StateWsCfg::C)
+        ws_produce<true>(stage, valid, wA, bl2, p, g, r16, sPK);
+    else
+        ws_produce<false>(stage, valid, wA, bl2, p, g, r16, sPK);
 }
 
 // Inputs of a chunk two ahead (k) and one ahead (V) into the buffers freed by the last chunk;
@@ -1019,13 +1029,13 @@ __global__ __launch_bounds__(512, 1) void state_ws_kernel_128(WideParams p) {
             }
         }
         __syncthreads();  // W shares space with the feature tiles
-        if (n > 0) ws_produce(smem + S::OFF_XK, valid_of(0), wA, bl2, c4, g, r16, reinterpret_cast<bf16_t *>(smem + S::OFF_PK));
+        if (n > 0) ws_produce_any(smem + S::OFF_XK, valid_of(0), wA, bl2, c4, g, r16, reinterpret_cast<bf16_t *>(smem + S::OFF_PK));
         __syncthreads();
         for (int c = 0; c < n; c++) {
             ws_issue(p, dl, base, t_begin, t_end, c, n, w, smem);
             const int b = c & 1;
             if (c + 1 < n)
-                ws_produce(smem + S::OFF_XK + (b ^ 1) * S::SZ_X, valid_of(c + 1), wA, bl2, c4, g, r16,
+                ws_produce_any(smem + S::OFF_XK + (b ^ 1) * S::SZ_X, valid_of(c + 1), wA, bl2, c4, g, r16,
                            reinterpret_cast<bf16_t *>(smem + S::OFF_PK + (b ^ 1) * S::SZ_PK));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -1130,6 +1140,7 @@ struct CausalWsCfg {
 // 64 (p >> 1) .. 64 (p >> 1) + 63 (so each producer reads only its 16 tokens of q and k).  All
 // operand reads first, then the eight independent product chains, then the exponentials, so
 // that one wave keeps the LDS, matrix and vector pipes busy at once.
+template <bool FULL>
 __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsigned char *xk, int valid,
                                              const bf16x8 (&wA)[4][4], const float (&bl2)[4][4], int p, int g,
                                              int r16, bf16_t *sPQ, bf16_t *sPK) {
@@ -1164,7 +1175,7 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
                 ep[r] = exp2_fast(u);
                 en[r] = exp2_fast(-u);
             }
-            if (t == 0 && i >= valid) {  // keys past the end contribute nothing
+            if (!FULL && t == 0 && i >= valid) {  // keys past the end contribute nothing
                 ep = zero4();
                 en = zero4();
             }
@@ -1185,6 +1196,16 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
             }
         }
     }
+}
+
+// Full chunks skip the per-lane masking of keys past the end.
+__device__ __forceinline__ void cws_features_any(const unsigned char *xq, const unsigned char *xk, int valid,
+                                                 const bf16x8 (&wA)[4][4], const float (&bl2)[4][4], int p, int g,
+                                                 int r16, bf16_t *sPQ, bf16_t *sPK) {
+    if (valid >= CausalWsCfg::C)
+        cws_features<true>(xq, xk, valid, wA, bl2, p, g, r16, sPQ, sPK);
+    else
+        cws_features<false>(xq, xk, valid, wA, bl2, p, g, r16, sPQ, sPK);
 }
 
 // Producer: scores of one chunk.  Tasks: p0 (0,0), p1 (1,0), p2 (1,1); p3 clears the masked
@@ -1327,14 +1348,14 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // W shares space with the feature tiles
         if (n > 0)
-            cws_features(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, pv, g, r16, pq_buf(0), pk_buf(0));
+            cws_features_any(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, pv, g, r16, pq_buf(0), pk_buf(0));
         __syncthreads();
         for (int c = 0; c < n; c++) {
             cws_issue(p, dl, base, t_begin, t_end, c, n, w, smem);
             const int b2 = c & 1;
             cws_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), pv, g, r16);
             if (c + 1 < n)
-                cws_features(smem + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, smem + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
+                cws_features_any(smem + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, smem + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
                              valid_of(c + 1), wA, bl2, pv, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
