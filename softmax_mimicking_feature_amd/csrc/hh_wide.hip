@@ -113,6 +113,21 @@ struct WideCfg {
     static_assert(NBUF == 1 || (D == 128 && VB == 2), "rotated V tile assumes 16 granules per row");
 };
 
+// Workgroup -> (head bh, segment s) for grids of BH x nseg workgroups.  Workgroups are dealt to
+// the eight XCDs round-robin (blockIdx mod 8); when BH is a multiple of 8, all segments of a head
+// go to one XCD, so that the head's W (and its state slot) is fetched into that XCD's L2 once.
+__device__ __forceinline__ void wg_head_segment(int nseg, int &bh, int &s) {
+    const int b = blockIdx.x, BH = gridDim.x / nseg;
+    if (BH % 8 == 0) {
+        const int j = b >> 3;
+        bh = (b & 7) + 8 * (j / nseg);
+        s = j % nseg;
+    } else {
+        bh = b / nseg;
+        s = b % nseg;
+    }
+}
+
 // Position of feature f in a row-major feature tile.  With PERM, each 32-feature group is
 // stored in the K order of two stacked accumulator blocks (lane group g reads features
 // {4g..4g+3, 16+4g..16+4g+3} as one 16-byte run), so the read-out operand that pairs with
@@ -410,6 +425,13 @@ __device__ __forceinline__ void load_directions(const bf16_t *__restrict__ W, co
             bl2[mb][r] = b ? bf16_bits_to_float(b[(size_t)h * D + lb]) * kLog2e : 0.0f;
         }
     }
+}
+
+// Per-head W (d = 128) into LDS by direct loads, in the layout of stage_w: a [128][128] tile
+// staged like the x tiles (8 waves, four 1 KB blocks each).
+__device__ __forceinline__ void stage_w_dma128(const bf16_t *__restrict__ W, int h, int w, int lane, unsigned char *sW) {
+    const DmaLanes128<128> wl(w, lane);
+    wl.issue<false>(W + (size_t)h * 128 * 128, 0, 128, w, sW);
 }
 
 // Per-head W into LDS (swizzled like the x tiles), once per workgroup.
@@ -738,8 +760,8 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int dq = w % K::NDQ;
     const int fa = w / K::NN, nq = w % K::NN;
-    const int bh = blockIdx.x / p.nseg_grid;
-    const int s = blockIdx.x % p.nseg_grid;
+    int bh, s;
+    wg_head_segment(p.nseg_grid, bh, s);
     const int h = bh % p.H;
     const int t_begin = s * p.seg_len;
     const int t_end = min(p.N, t_begin + p.seg_len);
@@ -990,8 +1012,8 @@ __global__ __launch_bounds__(512, 1) void state_ws_kernel_128(WideParams p) {
     // wave index as a scalar: role branches on it stay scalar (never exec-masked around MFMAs)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int c4 = w & 3;
-    const int bh = blockIdx.x / p.nseg_grid;
-    const int s = blockIdx.x % p.nseg_grid;
+    int bh, s;
+    wg_head_segment(p.nseg_grid, bh, s);
     const int h = bh % p.H;
     const int t_begin = s * p.seg_len;
     const int t_end = min(p.N, t_begin + p.seg_len);
@@ -1005,7 +1027,20 @@ __global__ __launch_bounds__(512, 1) void state_ws_kernel_128(WideParams p) {
         stage_v<128, 64>(p.v + base, t_begin, valid_of(0), w, lane, smem + S::OFF_V);
     }
     if (n > 1) stage_x<128, 64>(p.k + base, t_begin + S::C, valid_of(1), w, lane, smem + S::OFF_XK + S::SZ_X);
-    stage_w<128>(p.W, h, tid, smem + S::OFF_W);
+    stage_w_dma128(p.W, h, w, lane, smem + S::OFF_W);
+    // the producers' bias (directions 64 (c4 >> 1) .. + 63), its latency overlapping the staging
+    float bl2[4][4];
+    if (w < 4) {
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+            float b2[2][4];
+            load_bias<128>(p.b, h, 2 * (c4 >> 1) + hh, g, b2);
+#pragma unroll
+            for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) bl2[2 * hh + mb][r] = b2[mb][r];
+        }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -1013,20 +1048,14 @@ __global__ __launch_bounds__(512, 1) void state_ws_kernel_128(WideParams p) {
     if (w < 4) {
         // directions 64 (c4 >> 1) .. + 63: the two 32-direction groups 2 (c4 >> 1), 2 (c4 >> 1) + 1
         bf16x8 wA[4][4];
-        float bl2[4][4];
 #pragma unroll
         for (int hh = 0; hh < 2; hh++) {
             bf16x8 w2[2][4];
-            float b2[2][4];
             load_w_operands<128>(smem + S::OFF_W, 2 * (c4 >> 1) + hh, g, r16, w2);
-            load_bias<128>(p.b, h, 2 * (c4 >> 1) + hh, g, b2);
 #pragma unroll
-            for (int mb = 0; mb < 2; mb++) {
+            for (int mb = 0; mb < 2; mb++)
 #pragma unroll
                 for (int ks = 0; ks < 4; ks++) wA[2 * hh + mb][ks] = w2[mb][ks];
-#pragma unroll
-                for (int r = 0; r < 4; r++) bl2[2 * hh + mb][r] = b2[mb][r];
-            }
         }
         __syncthreads();  // W shares space with the feature tiles
         if (n > 0) ws_produce_any(smem + S::OFF_XK, valid_of(0), wA, bl2, c4, g, r16, reinterpret_cast<bf16_t *>(smem + S::OFF_PK));
@@ -1298,8 +1327,8 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     // wave index as a scalar: role branches on it stay scalar (never exec-masked around MFMAs)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int pv = w & 3;  // producer index / consumer value part
-    const int bh = blockIdx.x / p.nseg_grid;
-    const int s = blockIdx.x % p.nseg_grid;
+    int bh, s;
+    wg_head_segment(p.nseg_grid, bh, s);
     const int h = bh % p.H;
     const int t_begin = s * p.seg_len;
     const int t_end = min(p.N, t_begin + p.seg_len);
@@ -1322,7 +1351,26 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
         stage_x<128, 32>(p.q + base, t_begin + S::C, valid_of(1), w, lane, smem + S::OFF_XQ + S::SZ_X);
         stage_x<128, 32>(p.k + base, t_begin + S::C, valid_of(1), w, lane, smem + S::OFF_XK + S::SZ_X);
     }
-    stage_w<128>(p.W, h, tid, smem + S::OFF_W);
+    // The consumers' share of the prefix slot is fetched now, so that its latency overlaps the
+    // staging loads (it is added to the state after the barrier).
+    const bool use_slot = w >= 4 && p.slot_mode == 1 && s > 0;
+    bf16x8 slot_raw[2][8];
+    float zslot[4][4];
+    if (use_slot) {
+        const size_t sl = (size_t)bh * p.slot_bh_stride + s;
+        const float *zs = p.z_slots + sl * S::DP;
+#pragma unroll
+        for (int fa = 0; fa < 2; fa++) {
+            const bf16x8 *img = reinterpret_cast<const bf16x8 *>(p.S_slots + sl * S::DP * S::D) + (4 * fa + pv) * 8 * 64 + lane;
+#pragma unroll
+            for (int j = 0; j < 8; j++) slot_raw[fa][j] = img[j * 64];
+        }
+#pragma unroll
+        for (int zb = 0; zb < 4; zb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) zslot[zb][r] = zs[16 * (4 * pv + zb) + 4 * g + r];
+    }
+    stage_w_dma128(p.W, h, w, lane, smem + S::OFF_W);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -1390,27 +1438,20 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
 #pragma unroll
             for (int r = 0; r < 4; r++) zacc[zb][r] = zi[16 * (4 * pv + zb) + 4 * g + r];
     }
-    if (p.slot_mode == 1 && s > 0) {
-        const size_t sl = (size_t)bh * p.slot_bh_stride + s;
-        const float *zs = p.z_slots + sl * S::DP;
+    if (use_slot) {
 #pragma unroll
-        for (int fa = 0; fa < 2; fa++) {
-            const bf16x8 *img = reinterpret_cast<const bf16x8 *>(p.S_slots + sl * S::DP * S::D) + (4 * fa + pv) * 8 * 64 + lane;
-            bf16x8 t[8];
-#pragma unroll
-            for (int j = 0; j < 8; j++) t[j] = img[j * 64];
+        for (int fa = 0; fa < 2; fa++)
 #pragma unroll
             for (int j = 0; j < 8; j++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    sacc[8 * fa + j][0][r] += (float)t[j][r];
-                    sacc[8 * fa + j][1][r] += (float)t[j][4 + r];
+                    sacc[8 * fa + j][0][r] += (float)slot_raw[fa][j][r];
+                    sacc[8 * fa + j][1][r] += (float)slot_raw[fa][j][4 + r];
                 }
-        }
 #pragma unroll
         for (int zb = 0; zb < 4; zb++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) zacc[zb][r] += zs[16 * (4 * pv + zb) + 4 * g + r];
+            for (int r = 0; r < 4; r++) zacc[zb][r] += zslot[zb][r];
     }
     const int lane_k = (8 * g + (r16 >> 2)) * S::RK + 8 * (r16 & 3);
     const int r0 = 8 * g + (r16 >> 2);
