@@ -249,6 +249,10 @@ __device__ __forceinline__ void load_to_lds_16s(const void *sbase, uint32_t voff
                  : "m0");
 }
 
+// s_waitcnt immediates (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
+// LDS operations finished and at most `vm` vector memory operations outstanding.
+constexpr int waitcnt_lds_vm(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | (((vm >> 4) & 3) << 14); }
+
 // Per-lane source offsets of the direct loads of [C][128] bf16 tiles by 8 waves (wave w moves
 // 1 KB blocks w, w + 8, ...): byte offsets within the tile's rows for the q / k staging layout
 // (stage_pos) and the V layout (v_pos), the offset used when the lane's row lies past the end
@@ -921,97 +925,93 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
 }
 
 // ---------------------------------------------------------------------------------------
-// Segment aggregates for d = 128 with specialised waves.  Waves 0-3 (producers) compute the
-// key feature map of the next chunk while waves 4-7 (consumers) fold the current chunk into
-// the state; each SIMD runs one of each, so the exponentials of one overlap the matrix
-// products of the other.  One workgroup barrier per chunk hands the double-buffered feature
-// tile over.  The aggregate is written in the slot image of wide_kernel<128, *> (consumer
-// (fa, nq) holds the accumulators of that kernel's waves 4 fa + 2 nq and 4 fa + 2 nq + 1).
-struct StateWsCfg {
+// Segment aggregate for d = 128 with symmetric waves (64-token chunks).  Wave w owns feature
+// blocks w (exp(+u) of directions 16 w .. 16 w + 15) and 8 + w (their exp(-u)): it computes those
+// features for all tokens of the chunk with the tokens as the MFMA rows (x from LDS, W^T in
+// registers), turns them into the A operands of its own state update straight from the
+// accumulators, and adds phi(k)^T V and phi(k)^T 1 into its rows of S and z.  The key features
+// never pass through LDS, and every wave has exponentials to issue.  The contraction over the
+// chunk's tokens runs in the order the accumulators hold them: K index 8 g + s of K step kt is
+// token 32 kt + 4 g + s (s < 4) or 32 kt + 16 + 4 g + s - 4; V is read in the same order.
+struct StateSymCfg {
     static constexpr int D = 128, C = 64, DP = 256, NT = 512;
-    static constexpr int RK = DP + 12;                    // phi(k) pitch as in wide_kernel
-    static constexpr int SZ_PK = C * RK * 2;
     static constexpr int SZ_X = C * D * 2;                // k staging and V tile alike
-    static constexpr int OFF_PK = 0;                      // two feature tiles
-    static constexpr int OFF_V = OFF_PK + 2 * SZ_PK;      // two V tiles (granules at v_pos)
-    static constexpr int OFF_XK = OFF_V + 2 * SZ_X;       // two k staging tiles
-    static constexpr int OFF_W = 0;                       // W, before the first feature tile
-    static constexpr int LDS_BYTES = OFF_XK + 2 * SZ_X;
+    static constexpr int NB = 3;                          // staging buffers: chunk c + 2 loads during chunk c
+    static constexpr int OFF_W = 0;                       // W [128][128], x-tile layout
+    static constexpr int OFF_V = OFF_W + D * D * 2;       // V tiles (granules at v_pos)
+    static constexpr int OFF_XK = OFF_V + NB * SZ_X;      // k staging tiles
+    static constexpr int LDS_BYTES = OFF_XK + NB * SZ_X;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static_assert(D * D * 2 <= 2 * SZ_PK, "W fits in the feature tiles");
 };
 
-// Producer wave p: key features of token blocks 2 (p & 1), 2 (p & 1) + 1 of a 64-token chunk for
-// directions 64 (p >> 1) .. + 63 (each producer reads only its 32 tokens of k).
-template <bool FULL>
-__device__ __forceinline__ void ws_produce(const unsigned char *stage, int valid, const bf16x8 (&wA)[4][4],
-                                           const float (&bl2)[4][4], int p, int g, int r16, bf16_t *sPK) {
-    using S = StateWsCfg;
-    const int f0 = 64 * (p >> 1) + 4 * g;
+// V operand of value block vb and token K step kt in the token order above: two transposing
+// reads, rows 32 kt + 4 g .. + 3 and 32 kt + 16 + 4 g .. + 3.  lane_v[vb] addresses row
+// 4 g + r16 / 4 of value columns 16 vb + 4 (r16 % 4) .. + 3 in the rotated V tile; the row
+// rotation repeats every 4 rows, so rows 16 and 32 further use the same granule positions.
+__device__ __forceinline__ bf16x8 ssy_v_operand(const bf16_t *sV, int lane_v, int kt) {
+    using S = StateSymCfg;
+    return cat(lds_read_tr(sV + lane_v + 32 * kt * S::D), lds_read_tr(sV + lane_v + (32 * kt + 16) * S::D));
+}
+
+__device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t *sV, int valid, const bf16x8 (&wB)[4],
+                                          float bias2, const int (&lane_v)[8], const bf16x8 &ones, f32x4 (&sacc)[2][8],
+                                          f32x4 (&zacc)[2], int g, int r16) {
+    // u^T for the four token blocks: rows tokens 16 tb + 4 g + r, column direction 16 w + r16
+    // (x operands of K step ks + 1 read during the products of step ks)
+    bf16x8 xn[4], xc[4];
 #pragma unroll
-    for (int ibl = 0; ibl < 2; ibl++) {
-        const int i = 16 * (2 * (p & 1) + ibl) + r16;
-        bf16x8 xb[4];
+    for (int tb = 0; tb < 4; tb++) xn[tb] = staged_x_operand<128>(xk, 16 * tb + r16, 0, g);
+    f32x4 u[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) xb[ks] = staged_x_operand<128>(stage, i, ks, g);
-        f32x4 acc[4];
+    for (int tb = 0; tb < 4; tb++) u[tb] = zero4();
 #pragma unroll
-        for (int mb = 0; mb < 4; mb++) acc[mb] = zero4();
+    for (int ks = 0; ks < 4; ks++) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++)
+        for (int tb = 0; tb < 4; tb++) xc[tb] = xn[tb];
+        if (ks < 3) {
 #pragma unroll
-            for (int mb = 0; mb < 4; mb++) acc[mb] = mfma_bf16(wA[mb][ks], xb[ks], acc[mb]);
-#pragma unroll
-        for (int mb = 0; mb < 4; mb++) {
-            f32x4 ep, en;
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float u = acc[mb][r] * kLog2e + bl2[mb][r];
-                ep[r] = exp2_fast(u);
-                en[r] = exp2_fast(-u);
-            }
-            if (!FULL && i >= valid) {  // keys past the end contribute nothing
-                ep = zero4();
-                en = zero4();
-            }
-            store4(sPK + i * S::RK + feat_pos<true>(f0 + 16 * mb), to_bf16x4(ep));
-            store4(sPK + i * S::RK + feat_pos<true>(128 + f0 + 16 * mb), to_bf16x4(en));
+            for (int tb = 0; tb < 4; tb++) xn[tb] = staged_x_operand<128>(xk, 16 * tb + r16, ks + 1, g);
         }
+#pragma unroll
+        for (int tb = 0; tb < 4; tb++) u[tb] = mfma_bf16(xc[tb], wB[ks], u[tb]);
+    }
+    // V operands of the first K step while the exponentials run
+    bf16x8 vo[8];
+#pragma unroll
+    for (int vb = 0; vb < 8; vb++) vo[vb] = ssy_v_operand(sV, lane_v[vb], 0);
+    bf16x4 ep[4], en[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; tb++) {
+        f32x4 a, b;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const float x = u[tb][r] * kLog2e + bias2;
+            a[r] = exp2_fast(x);
+            b[r] = exp2_fast(-x);
+            if (16 * tb + 4 * g + r >= valid) a[r] = b[r] = 0.0f;  // keys past the end add nothing
+        }
+        ep[tb] = to_bf16x4(a);
+        en[tb] = to_bf16x4(b);
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+        const bf16x8 ap = cat(ep[2 * kt], ep[2 * kt + 1]), an = cat(en[2 * kt], en[2 * kt + 1]);
+#pragma unroll
+        for (int vb = 0; vb < 8; vb++) {
+            sacc[0][vb] = mfma_bf16(ap, vo[vb], sacc[0][vb]);
+            sacc[1][vb] = mfma_bf16(an, vo[vb], sacc[1][vb]);
+            if (kt == 0) vo[vb] = ssy_v_operand(sV, lane_v[vb], 1);  // the second K step's, in place
+        }
+        zacc[0] = mfma_bf16(ap, ones, zacc[0]);
+        zacc[1] = mfma_bf16(an, ones, zacc[1]);
     }
 }
 
-// Full chunks skip the per-lane masking of keys past the end.
-__device__ __forceinline__ void ws_produce_any(const unsigned char *stage, int valid, const bf16x8 (&wA)[4][4],
-                                               const float (&bl2)[4][4], int p, int g, int r16, bf16_t *sPK) {
-    if (valid >= StateWsCfg::C)
-        ws_produce<true>(stage, valid, wA, bl2, p, g, r16, sPK);
-    else
-        ws_produce<false>(stage, valid, wA, bl2, p, g, r16, sPK);
-}
-
-// Inputs of a chunk two ahead (k) and one ahead (V) into the buffers freed by the last chunk;
-// issued by every wave (each moves its own 1 KB blocks).
-__device__ __forceinline__ void ws_issue(const WideParams &p, const DmaLanes128<64> &dl, size_t base, int t_begin,
-                                         int t_end, int c, int n, int w, unsigned char *smem) {
-    using S = StateWsCfg;
-    const int b = c & 1;
-    if (c + 1 < n) {
-        const int t = t_begin + S::C * (c + 1);
-        dl.issue<true>(p.v + base, t, min(S::C, t_end - t), w, smem + S::OFF_V + (b ^ 1) * S::SZ_X);
-    }
-    if (c + 2 < n) {
-        const int t = t_begin + S::C * (c + 2);
-        dl.issue<false>(p.k + base, t, min(S::C, t_end - t), w, smem + S::OFF_XK + b * S::SZ_X);
-    }
-}
-
-__global__ __launch_bounds__(512, 1) void state_ws_kernel_128(WideParams p) {
-    using S = StateWsCfg;
+__global__ __launch_bounds__(512, 1) void state_sym_kernel_128(WideParams p) {
+    using S = StateSymCfg;
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
     const int tid = threadIdx.x;
-    // wave index as a scalar: role branches on it stay scalar (never exec-masked around MFMAs)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
-    const int c4 = w & 3;
     int bh, s;
     wg_head_segment(p.nseg_grid, bh, s);
     const int h = bh % p.H;
@@ -1021,116 +1021,78 @@ __global__ __launch_bounds__(512, 1) void state_ws_kernel_128(WideParams p) {
     const int n = t_end > t_begin ? (t_end - t_begin + S::C - 1) / S::C : 0;
     const DmaLanes128<64> dl(w, lane);
     auto valid_of = [&](int c) { return min(S::C, t_end - (t_begin + S::C * c)); };
+    auto v_buf = [&](int b) { return reinterpret_cast<const bf16_t *>(smem + S::OFF_V + b * S::SZ_X); };
+    auto x_buf = [&](int b) { return smem + S::OFF_XK + b * S::SZ_X; };
 
-    if (n > 0) {
-        stage_x<128, 64>(p.k + base, t_begin, valid_of(0), w, lane, smem + S::OFF_XK);
-        stage_v<128, 64>(p.v + base, t_begin, valid_of(0), w, lane, smem + S::OFF_V);
-    }
-    if (n > 1) stage_x<128, 64>(p.k + base, t_begin + S::C, valid_of(1), w, lane, smem + S::OFF_XK + S::SZ_X);
     stage_w_dma128(p.W, h, w, lane, smem + S::OFF_W);
-    // the producers' bias (directions 64 (c4 >> 1) .. + 63), its latency overlapping the staging
-    float bl2[4][4];
-    if (w < 4) {
-#pragma unroll
-        for (int hh = 0; hh < 2; hh++) {
-            float b2[2][4];
-            load_bias<128>(p.b, h, 2 * (c4 >> 1) + hh, g, b2);
-#pragma unroll
-            for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) bl2[2 * hh + mb][r] = b2[mb][r];
-        }
+    for (int c = 0; c < 2 && c < n; c++) {  // chunks 0 and 1; the loop fetches two chunks ahead
+        dl.issue<false>(p.k + base, t_begin + S::C * c, valid_of(c), w, x_buf(c));
+        dl.issue<true>(p.v + base, t_begin + S::C * c, valid_of(c), w, smem + S::OFF_V + c * S::SZ_X);
     }
+    // bias of this lane's direction 16 w + r16, times log2(e)
+    const float bias2 = p.b ? bf16_bits_to_float(p.b[(size_t)h * S::D + 16 * w + r16]) * kLog2e : 0.0f;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    // The two roles run separate loops with the same barriers, one per chunk.
-    if (w < 4) {
-        // directions 64 (c4 >> 1) .. + 63: the two 32-direction groups 2 (c4 >> 1), 2 (c4 >> 1) + 1
-        bf16x8 wA[4][4];
+    // W^T as the B operand: lane column = direction 16 w + r16, K = input dims 32 ks + 8 g .. + 7
+    bf16x8 wB[4];
+    {
+        const int l = 16 * w + r16;
 #pragma unroll
-        for (int hh = 0; hh < 2; hh++) {
-            bf16x8 w2[2][4];
-            load_w_operands<128>(smem + S::OFF_W, 2 * (c4 >> 1) + hh, g, r16, w2);
-#pragma unroll
-            for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) wA[2 * hh + mb][ks] = w2[mb][ks];
-        }
-        __syncthreads();  // W shares space with the feature tiles
-        if (n > 0) ws_produce_any(smem + S::OFF_XK, valid_of(0), wA, bl2, c4, g, r16, reinterpret_cast<bf16_t *>(smem + S::OFF_PK));
-        __syncthreads();
-        for (int c = 0; c < n; c++) {
-            ws_issue(p, dl, base, t_begin, t_end, c, n, w, smem);
-            const int b = c & 1;
-            if (c + 1 < n)
-                ws_produce_any(smem + S::OFF_XK + (b ^ 1) * S::SZ_X, valid_of(c + 1), wA, bl2, c4, g, r16,
-                           reinterpret_cast<bf16_t *>(smem + S::OFF_PK + (b ^ 1) * S::SZ_PK));
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        }
-        return;
+        for (int ks = 0; ks < 4; ks++)
+            wB[ks] = *reinterpret_cast<const bf16x8 *>(smem + S::OFF_W + 16 * (l * 16 + stage_pos<128>(l, 4 * ks + g)));
     }
-
-    const int fa = c4 >> 1, nq = c4 & 1;
-    f32x4 sacc[8][4];
-    f32x4 zacc[4];
+    int lane_v[8];
+    {
+        const int row = 4 * g + (r16 >> 2);
 #pragma unroll
-    for (int fb = 0; fb < 8; fb++)
-#pragma unroll
-        for (int vb = 0; vb < 4; vb++) sacc[fb][vb] = zero4();
-#pragma unroll
-    for (int zb = 0; zb < 4; zb++) zacc[zb] = zero4();
-    const int lane_k = (8 * g + (r16 >> 2)) * S::RK + 8 * (r16 & 3);
-    const int r0 = 8 * g + (r16 >> 2);
-    const int lane_v0 = r0 * S::D + 8 * v_pos(r0, 4 * (2 * nq) + (r16 & 3));
-    const int lane_v1 = r0 * S::D + 8 * v_pos(r0, 4 * (2 * nq + 1) + (r16 & 3));
+        for (int vb = 0; vb < 8; vb++) lane_v[vb] = row * S::D + 8 * v_pos(row, 2 * vb + ((r16 & 3) >> 1)) + 4 * (r16 & 1);
+    }
     const bf16x8 ones = ones_bf16x8();
-    __syncthreads();  // (producers: W read)
-    __syncthreads();  // (producers: first chunk's features)
+    f32x4 sacc[2][8];  // [exp(+u), exp(-u)][value block]: rows 16 fb + 4 g + r, columns 16 vb + r16
+    f32x4 zacc[2];
+#pragma unroll
+    for (int f = 0; f < 2; f++) {
+#pragma unroll
+        for (int vb = 0; vb < 8; vb++) sacc[f][vb] = zero4();
+        zacc[f] = zero4();
+    }
     for (int c = 0; c < n; c++) {
-        ws_issue(p, dl, base, t_begin, t_end, c, n, w, smem);
-        const int b = c & 1;
-        const bf16_t *sPK = reinterpret_cast<const bf16_t *>(smem + S::OFF_PK + b * S::SZ_PK);
-        const bf16_t *sV = reinterpret_cast<const bf16_t *>(smem + S::OFF_V + b * S::SZ_X);
-        const bf16_t *sPKf = sPK + perm_block_pos(8 * fa);
-        const bf16_t *sPKz = sPK + perm_block_pos(4 * c4);
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-            bf16x8 vop[4];
-#pragma unroll
-            for (int vb = 0; vb < 4; vb++)
-                vop[vb] = operand_down_rows(sV, (vb >> 1) ? lane_v1 : lane_v0, 32 * ks * S::D + 4 * (vb & 1), S::D);
-#pragma unroll
-            for (int fb = 0; fb < 8; fb++) {
-                const bf16x8 a = operand_down_rows(sPKf, lane_k, 32 * ks * S::RK + perm_block_pos(fb), S::RK);
-#pragma unroll
-                for (int vb = 0; vb < 4; vb++) sacc[fb][vb] = mfma_bf16(a, vop[vb], sacc[fb][vb]);
-            }
-#pragma unroll
-            for (int zb = 0; zb < 4; zb++) {
-                const bf16x8 a = operand_down_rows(sPKz, lane_k, 32 * ks * S::RK + perm_block_pos(zb), S::RK);
-                zacc[zb] = mfma_bf16(a, ones, zacc[zb]);
-            }
+        const int b = c % S::NB;
+        const bool ahead = c + 2 < n;
+        if (ahead) {  // k and V of chunk c + 2 into the buffers chunk c - 1 used
+            const int t = t_begin + S::C * (c + 2), b2 = (c + 2) % S::NB;
+            dl.issue<false>(p.k + base, t, min(S::C, t_end - t), w, x_buf(b2));
+            dl.issue<true>(p.v + base, t, min(S::C, t_end - t), w, smem + S::OFF_V + b2 * S::SZ_X);
         }
-        __builtin_amdgcn_s_waitcnt(0);
+        ssy_chunk(x_buf(b), v_buf(b), valid_of(c), wB, bias2, lane_v, ones, sacc, zacc, g, r16);
+        // chunk c + 1's loads (issued a chunk ago) have landed; chunk c + 2's stay in flight
+        if (ahead)
+            __builtin_amdgcn_s_waitcnt(waitcnt_lds_vm(2 * DmaLanes128<64>::NB));
+        else
+            __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
+    // Slot s in the register image the causal pass reads: entry ((4 fa + pv) 8 + j) 64 + lane of
+    // bf16x8, lane (g, c) holding rows 16 (8 fa + j) + 4 g + r, value columns value_col<2>(pv, h, c)
+    // in halves h.  Value column 16 vb + r16 of this lane is in entry pv = vb / 2 at
+    // c = 4 (m / 8) + m % 4, half (m / 4) % 2, with m = 16 (vb % 2) + r16.
     const size_t slot = (size_t)bh * p.slot_bh_stride + s;
+    bf16x4 *img = reinterpret_cast<bf16x4 *>(p.S_slots + slot * S::DP * S::D);
 #pragma unroll
-    for (int hh = 0; hh < 2; hh++) {
-        const int wq = 4 * fa + 2 * nq + hh;  // the chunked kernel's wave holding these accumulators
-        bf16x8 *img = reinterpret_cast<bf16x8 *>(p.S_slots + slot * S::DP * S::D) + wq * 8 * 64 + lane;
+    for (int f = 0; f < 2; f++)
 #pragma unroll
-        for (int fb = 0; fb < 8; fb++) img[fb * 64] = cat(to_bf16x4(sacc[fb][2 * hh]), to_bf16x4(sacc[fb][2 * hh + 1]));
-    }
+        for (int vb = 0; vb < 8; vb++) {
+            const int m = 16 * (vb & 1) + r16;
+            const int entry = ((4 * f + (vb >> 1)) * 8 + w) * 64 + 16 * g + 4 * (m >> 3) + (m & 3);
+            img[2 * entry + ((m >> 2) & 1)] = to_bf16x4(sacc[f][vb]);
+        }
     float *zs = p.z_slots + slot * S::DP;
     if (r16 == 0) {
 #pragma unroll
-        for (int zb = 0; zb < 4; zb++)
+        for (int f = 0; f < 2; f++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) zs[16 * (4 * c4 + zb) + 4 * g + r] = zacc[zb][r];
+            for (int r = 0; r < 4; r++) zs[16 * (8 * f + w) + 4 * g + r] = zacc[f][r];
     }
 }
 
@@ -1722,7 +1684,7 @@ static hipError_t launch_wide_d(int mode, const WideParams &p, int grid, hipStre
     switch (mode) {
     case WM_STATE:
         if (D == 128)
-            hipLaunchKernelGGL(state_ws_kernel_128, dim3(grid), dim3(StateWsCfg::NT), 0, st, p);
+            hipLaunchKernelGGL(state_sym_kernel_128, dim3(grid), dim3(StateSymCfg::NT), 0, st, p);
         else
             hipLaunchKernelGGL((wide_kernel<D, WM_STATE>), dim3(grid), dim3(K::NT), 0, st, p);
         break;
