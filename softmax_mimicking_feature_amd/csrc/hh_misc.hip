@@ -46,14 +46,29 @@ __global__ void prefix_kernel(PrefixParams p) {
         const int c = internal_to_canonical_row(p.map, row);
         if (c >= 0) run = isS ? p.S0[((size_t)bh * p.dpc + c) * p.d + col] : p.z0[(size_t)bh * p.dpc + c];
     }
+    // Segments go in groups of G: all loads of a group are issued before its stores, so that a
+    // thread waits for memory once per group rather than once per segment.
+    constexpr int G = 16;
     if (p.mode == 0) {  // exclusive prefix; the last segment's own aggregate is never needed
-        for (int s = 0; s < p.nseg; s++) {
-            const float dlt = (s < p.nseg - 1) ? base[s * stride] : 0.0f;
-            base[s * stride] = run;
-            run += dlt;
+        for (int s0 = 0; s0 < p.nseg; s0 += G) {
+            float a[G];
+#pragma unroll
+            for (int j = 0; j < G; j++) a[j] = (s0 + j < p.nseg - 1) ? base[(s0 + j) * stride] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < G; j++)
+                if (s0 + j < p.nseg) {
+                    base[(s0 + j) * stride] = run;
+                    run += a[j];
+                }
         }
     } else {  // total over all segments into slot 0
-        for (int s = 0; s < p.nseg; s++) run += base[s * stride];
+        for (int s0 = 0; s0 < p.nseg; s0 += G) {
+            float a[G];
+#pragma unroll
+            for (int j = 0; j < G; j++) a[j] = (s0 + j < p.nseg) ? base[(s0 + j) * stride] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < G; j++) run += a[j];
+        }
         base[0] = run;
     }
 }
