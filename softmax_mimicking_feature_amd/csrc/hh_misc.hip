@@ -217,6 +217,7 @@ hipError_t launch_seq_f32(const SeqParams &p, int BH, hipStream_t st) {
 #define HH_DEC_THREADS 256
 #endif
 constexpr int kDecThreads = HH_DEC_THREADS;
+constexpr int kDecHeld = 32;  // state pieces per thread fetched up front (all of them for d = 128)
 
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     __shared__ float sq[128], sk[128], sv[128];
@@ -225,6 +226,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     __shared__ float sden[kDecThreads / 64];
     const int bh = blockIdx.x, h = bh % p.H, t = threadIdx.x;
     const int d = p.d, dp = p.dp, dt = p.dtype;
+    // This thread's part of S (16-byte pieces e4 = t + kDecThreads i) is requested before the
+    // feature maps are computed, so that the state read overlaps them; states with more pieces
+    // than kDecHeld per thread take the streaming loop below for the rest.
+    const int q4 = d / 4;
+    const int n4 = dp * q4;
+    f32x4 *S4 = reinterpret_cast<f32x4 *>(p.S + (size_t)bh * dp * d);
+    f32x4 held[kDecHeld];
+#pragma unroll
+    for (int i = 0; i < kDecHeld; i++) {
+        const int e4 = t + kDecThreads * i;
+        if (e4 < n4) held[i] = __builtin_nontemporal_load(S4 + e4);
+    }
     if (t < d) {
         sq[t] = ld(p.q, (size_t)bh * d + t, dt);
         sk[t] = ld(p.k, (size_t)bh * d + t, dt);
@@ -280,14 +293,30 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     }
     __syncthreads();
 
-    const int q4 = d / 4;
     const int c4 = t % q4;
     const f32x4 vq = f32x4{sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]};
-    f32x4 *S4 = reinterpret_cast<f32x4 *>(p.S + (size_t)bh * dp * d);
-    const int n4 = dp * q4;
     f32x4 acc = zero4();
+#pragma unroll
+    for (int i = 0; i < kDecHeld; i++) {
+        const int e4 = t + kDecThreads * i;
+        if (e4 < n4) {
+            const int f = e4 / q4;
+            f32x4 s = held[i];
+            const float a = sfk[f];
+            s[0] = fmaf(a, vq[0], s[0]);
+            s[1] = fmaf(a, vq[1], s[1]);
+            s[2] = fmaf(a, vq[2], s[2]);
+            s[3] = fmaf(a, vq[3], s[3]);
+            __builtin_nontemporal_store(s, S4 + e4);
+            const float gq = sfq[f];
+            acc[0] = fmaf(gq, s[0], acc[0]);
+            acc[1] = fmaf(gq, s[1], acc[1]);
+            acc[2] = fmaf(gq, s[2], acc[2]);
+            acc[3] = fmaf(gq, s[3], acc[3]);
+        }
+    }
 #pragma unroll 16
-    for (int e4 = t; e4 < n4; e4 += kDecThreads) {
+    for (int e4 = t + kDecThreads * kDecHeld; e4 < n4; e4 += kDecThreads) {
         const int f = e4 / q4;
         f32x4 s = __builtin_nontemporal_load(S4 + e4);
         const float a = sfk[f];
