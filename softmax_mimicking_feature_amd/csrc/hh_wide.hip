@@ -925,60 +925,108 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
 }
 
 // ---------------------------------------------------------------------------------------
-// Segment aggregate for d = 128 with symmetric waves (64-token chunks).  Wave w owns feature
-// blocks w (exp(+u) of directions 16 w .. 16 w + 15) and 8 + w (their exp(-u)): it computes those
-// features for all tokens of the chunk with the tokens as the MFMA rows (x from LDS, W^T in
-// registers), turns them into the A operands of its own state update straight from the
-// accumulators, and adds phi(k)^T V and phi(k)^T 1 into its rows of S and z.  The key features
-// never pass through LDS, and every wave has exponentials to issue.  The contraction over the
-// chunk's tokens runs in the order the accumulators hold them: K index 8 g + s of K step kt is
-// token 32 kt + 4 g + s (s < 4) or 32 kt + 16 + 4 g + s - 4; V is read in the same order.
+// Segment aggregates with symmetric waves (d = 64 and 128, 64-token chunks).  Wave w of the
+// d / 16 waves owns feature blocks w (exp(+u) of directions 16 w .. 16 w + 15) and d / 16 + w
+// (their exp(-u)): it computes those features for all tokens of the chunk with the tokens as
+// the MFMA rows (x from LDS, W^T in registers), turns them into the A operands of its own
+// state update straight from the accumulators, and adds phi(k)^T V and phi(k)^T 1 into its rows
+// of S and z.  The key features never pass through LDS, and every wave has exponentials to
+// issue.  The contraction over the chunk's tokens runs in the order the accumulators hold
+// them: K index 8 g + s of K step kt is token 32 kt + 4 g + s (s < 4) or 32 kt + 16 + 4 g + s - 4;
+// V is read in the same order.
+template <int D>
 struct StateSymCfg {
-    static constexpr int D = 128, C = 64, DP = 256, NT = 512;
+    static constexpr int C = 64, DP = 2 * D, NW = D / 16, NT = 64 * NW;
+    static constexpr int NG = D / 8;                      // 16-byte granules per row
+    static constexpr int KSD = D / 32;                    // K steps over the head dim
+    static constexpr int VB = D / 16;                     // value blocks
     static constexpr int SZ_X = C * D * 2;                // k staging and V tile alike
     static constexpr int NB = 3;                          // staging buffers: chunk c + 2 loads during chunk c
-    static constexpr int OFF_W = 0;                       // W [128][128], x-tile layout
-    static constexpr int OFF_V = OFF_W + D * D * 2;       // V tiles (granules at v_pos)
+    static constexpr int OFF_W = 0;                       // W [D][D], x-tile layout
+    static constexpr int OFF_V = OFF_W + D * D * 2;       // V tiles (granules at ssy_vpos)
     static constexpr int OFF_XK = OFF_V + NB * SZ_X;      // k staging tiles
     static constexpr int LDS_BYTES = OFF_XK + NB * SZ_X;
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static constexpr int WG_PER_CU = D == 128 ? 1 : 2;
+    static_assert(LDS_BYTES * WG_PER_CU <= 160 * 1024, "LDS budget");
+};
+
+// Stored position of granule G of row r in this kernel's V tiles: rotated by 64 bytes per row
+// (d = 128) or 32 bytes per row (d = 64), so that the transposing reads of four rows fall in
+// distinct banks; the rotation repeats every 4 rows.
+template <int D>
+__device__ __forceinline__ int ssy_vpos(int r, int G) {
+    return D == 128 ? (G + 4 * r) & 15 : (G + 2 * r) & 7;
+}
+
+// Direct loads of [C][D] bf16 tiles by NWV waves (wave w moves 1 KB blocks w, w + NWV, ...):
+// per-lane byte offsets within the tile for the q / k staging layout (stage_pos) and this
+// kernel's V layout, the offset for a lane whose row lies past the end (row 0, whose granule P
+// sits at position P in both layouts), and the row.
+template <int D, int C, int NWV>
+struct DmaLanesT {
+    static constexpr int NG = D / 8;
+    static constexpr int NB = C * D * 2 / 1024 / NWV;
+    uint32_t ox[NB], ov[NB], o0[NB];
+    int row[NB];
+    __device__ __forceinline__ DmaLanesT(int w, int lane) {
+#pragma unroll
+        for (int bb = 0; bb < NB; bb++) {
+            const int slot = 64 * (w + NWV * bb) + lane;
+            const int r = slot / NG, P = slot % NG;
+            row[bb] = r;
+            ox[bb] = 2 * (r * D + 8 * stage_granule<D>(r, P));
+            // granule G is stored at ssy_vpos(r, G): position P holds G = P - rotation
+            ov[bb] = 2 * (r * D + 8 * (D == 128 ? ((P - 4 * r) & 15) : ((P - 2 * r) & 7)));
+            o0[bb] = 16 * P;
+        }
+    }
+    template <bool V>
+    __device__ __forceinline__ void issue(const bf16_t *x, int t0, int valid, int w, unsigned char *stage) const {
+        const bf16_t *src = x + (size_t)t0 * D;
+#pragma unroll
+        for (int bb = 0; bb < NB; bb++)
+            load_to_lds_16s(src, row[bb] < valid ? (V ? ov[bb] : ox[bb]) : o0[bb], stage + 1024 * (w + NWV * bb));
+    }
 };
 
 // V operand of value block vb and token K step kt in the token order above: two transposing
 // reads, rows 32 kt + 4 g .. + 3 and 32 kt + 16 + 4 g .. + 3.  lane_v[vb] addresses row
-// 4 g + r16 / 4 of value columns 16 vb + 4 (r16 % 4) .. + 3 in the rotated V tile; the row
-// rotation repeats every 4 rows, so rows 16 and 32 further use the same granule positions.
+// 4 g + r16 / 4 of value columns 16 vb + 4 (r16 % 4) .. + 3; rows 16 and 32 further use the same
+// granule positions.
+template <int D>
 __device__ __forceinline__ bf16x8 ssy_v_operand(const bf16_t *sV, int lane_v, int kt) {
-    using S = StateSymCfg;
-    return cat(lds_read_tr(sV + lane_v + 32 * kt * S::D), lds_read_tr(sV + lane_v + (32 * kt + 16) * S::D));
+    return cat(lds_read_tr(sV + lane_v + 32 * kt * D), lds_read_tr(sV + lane_v + (32 * kt + 16) * D));
 }
 
-__device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t *sV, int valid, const bf16x8 (&wB)[4],
-                                          float bias2, const int (&lane_v)[8], const bf16x8 &ones, f32x4 (&sacc)[2][8],
-                                          f32x4 (&zacc)[2], int g, int r16) {
+template <int D>
+__device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t *sV, int valid,
+                                          const bf16x8 (&wB)[StateSymCfg<D>::KSD], float bias2,
+                                          const int (&lane_v)[StateSymCfg<D>::VB], const bf16x8 &ones,
+                                          f32x4 (&sacc)[2][StateSymCfg<D>::VB], f32x4 (&zacc)[2], int g, int r16) {
+    using S = StateSymCfg<D>;
     // u^T for the four token blocks: rows tokens 16 tb + 4 g + r, column direction 16 w + r16
     // (x operands of K step ks + 1 read during the products of step ks)
     bf16x8 xn[4], xc[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; tb++) xn[tb] = staged_x_operand<128>(xk, 16 * tb + r16, 0, g);
+    for (int tb = 0; tb < 4; tb++) xn[tb] = staged_x_operand<D>(xk, 16 * tb + r16, 0, g);
     f32x4 u[4];
 #pragma unroll
     for (int tb = 0; tb < 4; tb++) u[tb] = zero4();
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
+    for (int ks = 0; ks < S::KSD; ks++) {
 #pragma unroll
         for (int tb = 0; tb < 4; tb++) xc[tb] = xn[tb];
-        if (ks < 3) {
+        if (ks + 1 < S::KSD) {
 #pragma unroll
-            for (int tb = 0; tb < 4; tb++) xn[tb] = staged_x_operand<128>(xk, 16 * tb + r16, ks + 1, g);
+            for (int tb = 0; tb < 4; tb++) xn[tb] = staged_x_operand<D>(xk, 16 * tb + r16, ks + 1, g);
         }
 #pragma unroll
         for (int tb = 0; tb < 4; tb++) u[tb] = mfma_bf16(xc[tb], wB[ks], u[tb]);
     }
     // V operands of the first K step while the exponentials run
-    bf16x8 vo[8];
+    bf16x8 vo[S::VB];
 #pragma unroll
-    for (int vb = 0; vb < 8; vb++) vo[vb] = ssy_v_operand(sV, lane_v[vb], 0);
+    for (int vb = 0; vb < S::VB; vb++) vo[vb] = ssy_v_operand<D>(sV, lane_v[vb], 0);
     bf16x4 ep[4], en[4];
 #pragma unroll
     for (int tb = 0; tb < 4; tb++) {
@@ -997,18 +1045,19 @@ __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t 
     for (int kt = 0; kt < 2; kt++) {
         const bf16x8 ap = cat(ep[2 * kt], ep[2 * kt + 1]), an = cat(en[2 * kt], en[2 * kt + 1]);
 #pragma unroll
-        for (int vb = 0; vb < 8; vb++) {
+        for (int vb = 0; vb < S::VB; vb++) {
             sacc[0][vb] = mfma_bf16(ap, vo[vb], sacc[0][vb]);
             sacc[1][vb] = mfma_bf16(an, vo[vb], sacc[1][vb]);
-            if (kt == 0) vo[vb] = ssy_v_operand(sV, lane_v[vb], 1);  // the second K step's, in place
+            if (kt == 0) vo[vb] = ssy_v_operand<D>(sV, lane_v[vb], 1);  // the second K step's, in place
         }
         zacc[0] = mfma_bf16(ap, ones, zacc[0]);
         zacc[1] = mfma_bf16(an, ones, zacc[1]);
     }
 }
 
-__global__ __launch_bounds__(512, 1) void state_sym_kernel_128(WideParams p) {
-    using S = StateSymCfg;
+template <int D>
+__global__ __launch_bounds__(StateSymCfg<D>::NT, StateSymCfg<D>::WG_PER_CU) void state_sym_kernel(WideParams p) {
+    using S = StateSymCfg<D>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
@@ -1017,43 +1066,47 @@ __global__ __launch_bounds__(512, 1) void state_sym_kernel_128(WideParams p) {
     const int h = bh % p.H;
     const int t_begin = s * p.seg_len;
     const int t_end = min(p.N, t_begin + p.seg_len);
-    const size_t base = (size_t)bh * p.N * S::D;
+    const size_t base = (size_t)bh * p.N * D;
     const int n = t_end > t_begin ? (t_end - t_begin + S::C - 1) / S::C : 0;
-    const DmaLanes128<64> dl(w, lane);
+    const DmaLanesT<D, S::C, S::NW> dl(w, lane);
     auto valid_of = [&](int c) { return min(S::C, t_end - (t_begin + S::C * c)); };
     auto v_buf = [&](int b) { return reinterpret_cast<const bf16_t *>(smem + S::OFF_V + b * S::SZ_X); };
     auto x_buf = [&](int b) { return smem + S::OFF_XK + b * S::SZ_X; };
 
-    stage_w_dma128(p.W, h, w, lane, smem + S::OFF_W);
+    {  // W into LDS by direct loads, x-tile layout
+        const DmaLanesT<D, D, S::NW> wl(w, lane);
+        wl.template issue<false>(p.W + (size_t)h * D * D, 0, D, w, smem + S::OFF_W);
+    }
     for (int c = 0; c < 2 && c < n; c++) {  // chunks 0 and 1; the loop fetches two chunks ahead
-        dl.issue<false>(p.k + base, t_begin + S::C * c, valid_of(c), w, x_buf(c));
-        dl.issue<true>(p.v + base, t_begin + S::C * c, valid_of(c), w, smem + S::OFF_V + c * S::SZ_X);
+        dl.template issue<false>(p.k + base, t_begin + S::C * c, valid_of(c), w, x_buf(c));
+        dl.template issue<true>(p.v + base, t_begin + S::C * c, valid_of(c), w, smem + S::OFF_V + c * S::SZ_X);
     }
     // bias of this lane's direction 16 w + r16, times log2(e)
-    const float bias2 = p.b ? bf16_bits_to_float(p.b[(size_t)h * S::D + 16 * w + r16]) * kLog2e : 0.0f;
+    const float bias2 = p.b ? bf16_bits_to_float(p.b[(size_t)h * D + 16 * w + r16]) * kLog2e : 0.0f;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // W^T as the B operand: lane column = direction 16 w + r16, K = input dims 32 ks + 8 g .. + 7
-    bf16x8 wB[4];
+    bf16x8 wB[S::KSD];
     {
         const int l = 16 * w + r16;
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++)
-            wB[ks] = *reinterpret_cast<const bf16x8 *>(smem + S::OFF_W + 16 * (l * 16 + stage_pos<128>(l, 4 * ks + g)));
+        for (int ks = 0; ks < S::KSD; ks++)
+            wB[ks] = *reinterpret_cast<const bf16x8 *>(smem + S::OFF_W + 16 * (l * S::NG + stage_pos<D>(l, 4 * ks + g)));
     }
-    int lane_v[8];
+    int lane_v[S::VB];
     {
         const int row = 4 * g + (r16 >> 2);
 #pragma unroll
-        for (int vb = 0; vb < 8; vb++) lane_v[vb] = row * S::D + 8 * v_pos(row, 2 * vb + ((r16 & 3) >> 1)) + 4 * (r16 & 1);
+        for (int vb = 0; vb < S::VB; vb++)
+            lane_v[vb] = row * D + 8 * ssy_vpos<D>(row, 2 * vb + ((r16 & 3) >> 1)) + 4 * (r16 & 1);
     }
     const bf16x8 ones = ones_bf16x8();
-    f32x4 sacc[2][8];  // [exp(+u), exp(-u)][value block]: rows 16 fb + 4 g + r, columns 16 vb + r16
+    f32x4 sacc[2][S::VB];  // [exp(+u), exp(-u)][value block]: rows 16 fb + 4 g + r, columns 16 vb + r16
     f32x4 zacc[2];
 #pragma unroll
     for (int f = 0; f < 2; f++) {
 #pragma unroll
-        for (int vb = 0; vb < 8; vb++) sacc[f][vb] = zero4();
+        for (int vb = 0; vb < S::VB; vb++) sacc[f][vb] = zero4();
         zacc[f] = zero4();
     }
     for (int c = 0; c < n; c++) {
@@ -1061,38 +1114,48 @@ __global__ __launch_bounds__(512, 1) void state_sym_kernel_128(WideParams p) {
         const bool ahead = c + 2 < n;
         if (ahead) {  // k and V of chunk c + 2 into the buffers chunk c - 1 used
             const int t = t_begin + S::C * (c + 2), b2 = (c + 2) % S::NB;
-            dl.issue<false>(p.k + base, t, min(S::C, t_end - t), w, x_buf(b2));
-            dl.issue<true>(p.v + base, t, min(S::C, t_end - t), w, smem + S::OFF_V + b2 * S::SZ_X);
+            dl.template issue<false>(p.k + base, t, min(S::C, t_end - t), w, x_buf(b2));
+            dl.template issue<true>(p.v + base, t, min(S::C, t_end - t), w, smem + S::OFF_V + b2 * S::SZ_X);
         }
-        ssy_chunk(x_buf(b), v_buf(b), valid_of(c), wB, bias2, lane_v, ones, sacc, zacc, g, r16);
+        ssy_chunk<D>(x_buf(b), v_buf(b), valid_of(c), wB, bias2, lane_v, ones, sacc, zacc, g, r16);
         // chunk c + 1's loads (issued a chunk ago) have landed; chunk c + 2's stay in flight
         if (ahead)
-            __builtin_amdgcn_s_waitcnt(waitcnt_lds_vm(2 * DmaLanes128<64>::NB));
+            __builtin_amdgcn_s_waitcnt(waitcnt_lds_vm(2 * DmaLanesT<D, S::C, S::NW>::NB));
         else
             __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
-    // Slot s in the register image the causal pass reads: entry ((4 fa + pv) 8 + j) 64 + lane of
-    // bf16x8, lane (g, c) holding rows 16 (8 fa + j) + 4 g + r, value columns value_col<2>(pv, h, c)
-    // in halves h.  Value column 16 vb + r16 of this lane is in entry pv = vb / 2 at
-    // c = 4 (m / 8) + m % 4, half (m / 4) % 2, with m = 16 (vb % 2) + r16.
+    // Slot s in the register image the chunked pass of the same d reads back.
     const size_t slot = (size_t)bh * p.slot_bh_stride + s;
-    bf16x4 *img = reinterpret_cast<bf16x4 *>(p.S_slots + slot * S::DP * S::D);
+    bf16x4 *img = reinterpret_cast<bf16x4 *>(p.S_slots + slot * S::DP * D);
 #pragma unroll
     for (int f = 0; f < 2; f++)
 #pragma unroll
-        for (int vb = 0; vb < 8; vb++) {
-            const int m = 16 * (vb & 1) + r16;
-            const int entry = ((4 * f + (vb >> 1)) * 8 + w) * 64 + 16 * g + 4 * (m >> 3) + (m & 3);
-            img[2 * entry + ((m >> 2) & 1)] = to_bf16x4(sacc[f][vb]);
+        for (int vb = 0; vb < S::VB; vb++) {
+            int e2;  // index of the 8-byte half that holds these four values
+            if (D == 128) {
+                // causal_ws_kernel_128: entry ((4 fa + pv) 8 + j) 64 + lane of bf16x8, lane (g, c)
+                // holding rows 16 (8 fa + j) + 4 g + r, value columns value_col<2>(pv, h, c) in halves
+                // h.  Value column 16 vb + r16 is in entry pv = vb / 2 at c = 4 (m / 8) + m % 4,
+                // half (m / 4) % 2, with m = 16 (vb % 2) + r16; here fa = f, j = w.
+                const int m = 16 * (vb & 1) + r16;
+                e2 = 2 * (((4 * f + (vb >> 1)) * 8 + w) * 64 + 16 * g + 4 * (m >> 3) + (m & 3)) + ((m >> 2) & 1);
+            } else {
+                // wide_kernel<64>: entry (wv 4 + j) 64 + lane of bf16x8, wave wv owning value block
+                // wv, lane (g, r16) holding rows 16 (2 j) + 4 g + r and 16 (2 j + 1) + 4 g + r of
+                // value column 16 wv + r16 in its halves; here the feature block is 4 f + w.
+                const int fb = 4 * f + w;
+                e2 = 2 * ((vb * 4 + (fb >> 1)) * 64 + 16 * g + r16) + (fb & 1);
+            }
+            img[e2] = to_bf16x4(sacc[f][vb]);
         }
     float *zs = p.z_slots + slot * S::DP;
     if (r16 == 0) {
 #pragma unroll
         for (int f = 0; f < 2; f++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) zs[16 * (8 * f + w) + 4 * g + r] = zacc[f][r];
+            for (int r = 0; r < 4; r++) zs[16 * (S::NW * f + w) + 4 * g + r] = zacc[f][r];
     }
 }
 
@@ -1683,8 +1746,9 @@ static hipError_t launch_wide_d(int mode, const WideParams &p, int grid, hipStre
     using K = WideCfg<D>;
     switch (mode) {
     case WM_STATE:
-        if (D == 128)
-            hipLaunchKernelGGL(state_sym_kernel_128, dim3(grid), dim3(StateSymCfg::NT), 0, st, p);
+        if (D == 128 || D == 64)
+            hipLaunchKernelGGL((state_sym_kernel<D == 128 ? 128 : 64>), dim3(grid),
+                               dim3(StateSymCfg<D == 128 ? 128 : 64>::NT), 0, st, p);
         else
             hipLaunchKernelGGL((wide_kernel<D, WM_STATE>), dim3(grid), dim3(K::NT), 0, st, p);
         break;
