@@ -303,18 +303,21 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
             slZ = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + wide_slot_S_bytes(BH, pl.nseg, d));
         }
         wp.S_slots = slS; wp.z_slots = slZ; wp.slot_bh_stride = pl.nseg;
+        // d = 128 causal with few segments per sequence: the chunked pass sums the aggregates of
+        // the earlier segments itself (at most 7 slots, still in L2) instead of a separate scan
+        const bool direct_prefix = causal && d == 128 && pl.nseg <= 8;
         wp.N = N; wp.H = H; wp.seg_len = pl.seg_len;
         if (run_state) {
             wp.nseg_grid = state_segments;
             e = hh::launch_wide(d, 0, wp, (int)(BH * state_segments), s);
             if (e != hipSuccess) return hip_fail(e, "segment-state launch");
-            if (pl.nseg > 1) {
+            if (pl.nseg > 1 && !direct_prefix) {
                 e = hh::launch_slot_scan(d, slS, slZ, (int)BH, pl.nseg, causal ? 0 : 1, s);
                 if (e != hipSuccess) return hip_fail(e, "segment scan launch");
             }
         }
         if (causal) {
-            wp.slot_mode = pl.nseg > 1 ? 1 : 0;
+            wp.slot_mode = pl.nseg > 1 ? (direct_prefix ? 3 : 1) : 0;
             wp.S_in = S0; wp.z_in = z0; wp.in_bh_stride = 1; wp.in_seg_stride = 0;
         } else {
             wp.slot_mode = 2;

@@ -1367,35 +1367,88 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     auto a_buf = [&](int b) { return reinterpret_cast<bf16_t *>(smem + S::OFF_A + b * S::SZ_A); };
     auto den_buf = [&](int b) { return reinterpret_cast<float *>(smem + S::OFF_DEN + b * S::SZ_DEN); };
 
-    if (n > 0) {
-        stage_x<128, 32>(p.q + base, t_begin, valid_of(0), w, lane, smem + S::OFF_XQ);
-        stage_x<128, 32>(p.k + base, t_begin, valid_of(0), w, lane, smem + S::OFF_XK);
-        stage_v<128, 32>(p.v + base, t_begin, valid_of(0), w, lane, smem + S::OFF_V);
-    }
-    if (n > 1) {
-        stage_x<128, 32>(p.q + base, t_begin + S::C, valid_of(1), w, lane, smem + S::OFF_XQ + S::SZ_X);
-        stage_x<128, 32>(p.k + base, t_begin + S::C, valid_of(1), w, lane, smem + S::OFF_XK + S::SZ_X);
-    }
-    // The consumers' share of the prefix slot is fetched now, so that its latency overlaps the
-    // staging loads (it is added to the state after the barrier).
-    const bool use_slot = w >= 4 && p.slot_mode == 1 && s > 0;
-    bf16x8 slot_raw[2][8];
-    float zslot[4][4];
-    if (use_slot) {
-        const size_t sl = (size_t)bh * p.slot_bh_stride + s;
-        const float *zs = p.z_slots + sl * S::DP;
+    // Consumer state: value columns value_col<2>(pv, vb, c) of S for all 256 features, z rows of
+    // feature blocks 4 pv .. 4 pv + 3 (declared here, used by the consumer waves only).
+    f32x4 sacc[16][2];
+    f32x4 zacc[4];
+    if (w < 4) {
+        // Producers issue every staging load of the prologue (each moves the 1 KB blocks of waves w
+        // and w + 4 of the eight-wave layout), so that the consumers' load queues hold only their
+        // own prefix loads below: loads retire in order per wave, and a consumer waiting for a prefix
+        // slot then never waits for staging traffic as well.
 #pragma unroll
-        for (int fa = 0; fa < 2; fa++) {
-            const bf16x8 *img = reinterpret_cast<const bf16x8 *>(p.S_slots + sl * S::DP * S::D) + (4 * fa + pv) * 8 * 64 + lane;
-#pragma unroll
-            for (int j = 0; j < 8; j++) slot_raw[fa][j] = img[j * 64];
+        for (int hw = 0; hw < 2; hw++) {
+            const int vw = w + 4 * hw;
+            if (n > 0) {
+                stage_x<128, 32>(p.q + base, t_begin, valid_of(0), vw, lane, smem + S::OFF_XQ);
+                stage_x<128, 32>(p.k + base, t_begin, valid_of(0), vw, lane, smem + S::OFF_XK);
+                stage_v<128, 32>(p.v + base, t_begin, valid_of(0), vw, lane, smem + S::OFF_V);
+            }
+            if (n > 1) {
+                stage_x<128, 32>(p.q + base, t_begin + S::C, valid_of(1), vw, lane, smem + S::OFF_XQ + S::SZ_X);
+                stage_x<128, 32>(p.k + base, t_begin + S::C, valid_of(1), vw, lane, smem + S::OFF_XK + S::SZ_X);
+            }
+            stage_w_dma128(p.W, h, vw, lane, smem + S::OFF_W);
         }
+    } else {
+        // Starting state: the caller's S0, plus the earlier segments' contribution.  slot_mode 1:
+        // slot s holds their exclusive prefix; slot_mode 3: slots 0 .. s - 1 hold their aggregates
+        // (written by the segment-state pass just before, by workgroups of the same XCD), summed
+        // here in fp32 while the producers' staging loads are in flight.
 #pragma unroll
-        for (int zb = 0; zb < 4; zb++)
+        for (int fb = 0; fb < 16; fb++) sacc[fb][0] = sacc[fb][1] = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; r++) zslot[zb][r] = zs[16 * (4 * pv + zb) + 4 * g + r];
+        for (int zb = 0; zb < 4; zb++) zacc[zb] = zero4();
+        if (p.S_in) {
+            const float *Si = p.S_in + (size_t)bh * p.in_bh_stride * S::DP * S::D;
+            const float *zi = p.z_in + (size_t)bh * p.in_bh_stride * S::DP;
+#pragma unroll
+            for (int fb = 0; fb < 16; fb++)
+#pragma unroll
+                for (int vb = 0; vb < 2; vb++) {
+                    const int nn = value_col<2>(pv, vb, r16);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) sacc[fb][vb][r] = Si[(size_t)(16 * fb + 4 * g + r) * S::D + nn];
+                }
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) zacc[zb][r] = zi[16 * (4 * pv + zb) + 4 * g + r];
+        }
+        int t0 = 0, t1 = 0;  // slots to add
+        if (s > 0 && p.slot_mode == 1) t0 = s, t1 = s + 1;
+        if (s > 0 && p.slot_mode == 3) t0 = 0, t1 = s;
+        for (int t = t0; t < t1; t++) {
+            const size_t sl = (size_t)bh * p.slot_bh_stride + t;
+            const float *zs = p.z_slots + sl * S::DP;
+            bf16x8 slot_raw[2][8];
+            float zslot[4][4];
+#pragma unroll
+            for (int fa = 0; fa < 2; fa++) {
+                const bf16x8 *img =
+                    reinterpret_cast<const bf16x8 *>(p.S_slots + sl * S::DP * S::D) + (4 * fa + pv) * 8 * 64 + lane;
+#pragma unroll
+                for (int j = 0; j < 8; j++) slot_raw[fa][j] = img[j * 64];
+            }
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) zslot[zb][r] = zs[16 * (4 * pv + zb) + 4 * g + r];
+#pragma unroll
+            for (int fa = 0; fa < 2; fa++)
+#pragma unroll
+                for (int j = 0; j < 8; j++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        sacc[8 * fa + j][0][r] += (float)slot_raw[fa][j][r];
+                        sacc[8 * fa + j][1][r] += (float)slot_raw[fa][j][4 + r];
+                    }
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) zacc[zb][r] += zslot[zb][r];
+        }
     }
-    stage_w_dma128(p.W, h, w, lane, smem + S::OFF_W);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -1436,48 +1489,10 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
         return;
     }
 
-    // consumer: value columns value_col<2>(pv, vb, c) of the state for all 256 features
-    f32x4 sacc[16][2];
-    f32x4 zacc[4];  // z rows of feature blocks 4 pv .. 4 pv + 3
+    // consumer
     f32x4 numT[2][2];
 #pragma unroll
-    for (int fb = 0; fb < 16; fb++) sacc[fb][0] = sacc[fb][1] = zero4();
-#pragma unroll
-    for (int zb = 0; zb < 4; zb++) zacc[zb] = zero4();
-#pragma unroll
     for (int ib = 0; ib < 2; ib++) numT[ib][0] = numT[ib][1] = zero4();
-    // starting state: the caller's S0 and the exclusive prefix of the earlier segments
-    if (p.S_in) {
-        const float *Si = p.S_in + (size_t)bh * p.in_bh_stride * S::DP * S::D;
-        const float *zi = p.z_in + (size_t)bh * p.in_bh_stride * S::DP;
-#pragma unroll
-        for (int fb = 0; fb < 16; fb++)
-#pragma unroll
-            for (int vb = 0; vb < 2; vb++) {
-                const int nn = value_col<2>(pv, vb, r16);
-#pragma unroll
-                for (int r = 0; r < 4; r++) sacc[fb][vb][r] = Si[(size_t)(16 * fb + 4 * g + r) * S::D + nn];
-            }
-#pragma unroll
-        for (int zb = 0; zb < 4; zb++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) zacc[zb][r] = zi[16 * (4 * pv + zb) + 4 * g + r];
-    }
-    if (use_slot) {
-#pragma unroll
-        for (int fa = 0; fa < 2; fa++)
-#pragma unroll
-            for (int j = 0; j < 8; j++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    sacc[8 * fa + j][0][r] += (float)slot_raw[fa][j][r];
-                    sacc[8 * fa + j][1][r] += (float)slot_raw[fa][j][4 + r];
-                }
-#pragma unroll
-        for (int zb = 0; zb < 4; zb++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) zacc[zb][r] += zslot[zb][r];
-    }
     const int lane_k = (8 * g + (r16 >> 2)) * S::RK + 8 * (r16 & 3);
     const int r0 = 8 * g + (r16 >> 2);
     const int lane_v = r0 * S::D + 8 * v_pos(r0, 4 * pv + (r16 & 3));
