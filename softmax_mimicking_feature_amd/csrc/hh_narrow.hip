@@ -41,22 +41,23 @@ __device__ __forceinline__ float taylor_feature(int fb, const float (&x)[D], flo
     return x[fb - 1] * xps;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(64) void narrow_kernel(NarrowParams p) {
-    __shared__ __attribute__((aligned(16))) bf16_t sQ[C * RR];
-    __shared__ __attribute__((aligned(16))) bf16_t sK[C * RR];
-    __shared__ __attribute__((aligned(16))) bf16_t sKT[D * RT];
-    __shared__ __attribute__((aligned(16))) bf16_t sVT[D * RT];
-
-    const int lane = threadIdx.x, g = lane >> 4, r16 = lane & 15;
-    const int bh = blockIdx.x / p.nseg_grid;
-    const int s = blockIdx.x % p.nseg_grid;
+// Work of wave H of the two waves of a workgroup.  Wave H holds the state rows of the K steps
+// [KS0, KS1) (feature blocks 2 KS0 .. 2 KS1 - 1): wave 0 steps 0-4, wave 1 steps 5-8 plus the
+// intra-chunk part, so each wave builds only its own feature operands.  The read-out partials
+// over the two halves meet in LDS: each wave finishes two of the four 16-token blocks.
+template <int MODE, int H>
+__device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s, int lane, bf16_t *sQ, bf16_t *sK,
+                                            bf16_t *sKT, bf16_t *sVT, f32x4 *sX) {
+    constexpr int KS0 = H == 0 ? 0 : 5, KS1 = H == 0 ? 5 : KSF;
+    constexpr int NB = 2 * (KS1 - KS0);  // feature blocks held by this wave
+    constexpr int FB0 = 2 * KS0;
+    const int g = lane >> 4, r16 = lane & 15;
     const int t_begin = s * p.seg_len;
     const int t_end = min(p.N, t_begin + p.seg_len);
     const size_t base = (size_t)bh * p.N * D;
 
     // State S[f][n] (lane: column n = r16, rows f = 16 fb + 4 g + r) and z (same rows, every column).
-    f32x4 sacc[FB], zacc[FB];
+    f32x4 sacc[NB], zacc[NB];
     {
         const float *Si = nullptr, *zi = nullptr;
         if (MODE != NM_STATE && p.S_in) {
@@ -65,38 +66,44 @@ __global__ __launch_bounds__(64) void narrow_kernel(NarrowParams p) {
             zi = p.z_in + slot * kTaylorRowsInternal;
         }
 #pragma unroll
-        for (int fb = 0; fb < FB; fb++)
+        for (int lb = 0; lb < NB; lb++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int f = 16 * fb + 4 * g + r;
-                sacc[fb][r] = Si ? Si[(size_t)f * D + r16] : 0.0f;
-                zacc[fb][r] = zi ? zi[f] : 0.0f;
+                const int f = 16 * (FB0 + lb) + 4 * g + r;
+                sacc[lb][r] = Si ? Si[(size_t)f * D + r16] : 0.0f;
+                zacc[lb][r] = zi ? zi[f] : 0.0f;
             }
     }
     const bf16x8 ones = ones_bf16x8();
 
     for (int t0 = t_begin; t0 < t_end; t0 += C) {
         const int valid = min(C, t_end - t0);
-        // ---- stage the chunk: q, k row-major; k, v transposed (tokens contiguous)
+        // ---- stage the chunk (lane = token): wave 0 q and k row-major and v transposed, wave 1 k
+        // transposed (tokens contiguous)
         {
             const int j = lane;
             const bool ok = j < valid;
             const bf16_t *qr = p.q + base + (size_t)(t0 + j) * D;
             const bf16_t *kr = p.k + base + (size_t)(t0 + j) * D;
             const bf16_t *vr = p.v + base + (size_t)(t0 + j) * D;
-            bf16x8 kq[2], kk[2], kv[2];
+            if (H == 0) {
+                bf16x8 kq[2], kk[2], kv[2];
 #pragma unroll
-            for (int hlf = 0; hlf < 2; hlf++) {
-                kq[hlf] = (ok && MODE != NM_STATE) ? load8(qr + 8 * hlf) : zero_bf16x8();
-                kk[hlf] = (ok && MODE != NM_READOUT) ? load8(kr + 8 * hlf) : zero_bf16x8();
-                kv[hlf] = (ok && MODE != NM_READOUT) ? load8(vr + 8 * hlf) : zero_bf16x8();
-                store8(sQ + j * RR + 8 * hlf, kq[hlf]);
-                store8(sK + j * RR + 8 * hlf, kk[hlf]);
-            }
+                for (int hlf = 0; hlf < 2; hlf++) {
+                    kq[hlf] = (ok && MODE != NM_STATE) ? load8(qr + 8 * hlf) : zero_bf16x8();
+                    kk[hlf] = (ok && MODE == NM_CAUSAL) ? load8(kr + 8 * hlf) : zero_bf16x8();
+                    kv[hlf] = (ok && MODE != NM_READOUT) ? load8(vr + 8 * hlf) : zero_bf16x8();
+                    store8(sQ + j * RR + 8 * hlf, kq[hlf]);
+                    store8(sK + j * RR + 8 * hlf, kk[hlf]);
+                }
 #pragma unroll
-            for (int m = 0; m < D; m++) {
-                reinterpret_cast<__bf16 *>(sKT)[m * RT + j] = kk[m / 8][m % 8];
-                reinterpret_cast<__bf16 *>(sVT)[m * RT + j] = kv[m / 8][m % 8];
+                for (int m = 0; m < D; m++) reinterpret_cast<__bf16 *>(sVT)[m * RT + j] = kv[m / 8][m % 8];
+            } else {
+                bf16x8 kk[2];
+#pragma unroll
+                for (int hlf = 0; hlf < 2; hlf++) kk[hlf] = (ok && MODE != NM_READOUT) ? load8(kr + 8 * hlf) : zero_bf16x8();
+#pragma unroll
+                for (int m = 0; m < D; m++) reinterpret_cast<__bf16 *>(sKT)[m * RT + j] = kk[m / 8][m % 8];
             }
         }
         __syncthreads();
@@ -119,7 +126,8 @@ __global__ __launch_bounds__(64) void narrow_kernel(NarrowParams p) {
                 num[ib] = zero4();
                 den[ib] = zero4();
             }
-            // ---- read-out against the carried state; phi(q) built per operand slot
+            // ---- read-out against the carried state over this wave's K steps; phi(q) built per
+            // operand slot
 #pragma unroll
             for (int ib = 0; ib < 4; ib++) {
                 const int i = 16 * ib + r16;
@@ -142,19 +150,20 @@ __global__ __launch_bounds__(64) void narrow_kernel(NarrowParams p) {
                     }
                 }
 #pragma unroll
-                for (int ks = 0; ks < KSF; ks++) {
+                for (int ks = KS0; ks < KS1; ks++) {
                     bf16x8 a;
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
                         a[r] = (__bf16)taylor_feature(2 * ks, x, xp[r], xps[r], g == 0 && r == 0);
                         a[4 + r] = (__bf16)taylor_feature(2 * ks + 1, x, xp[r], xps[r], g == 0 && r == 0);
                     }
-                    num[ib] = mfma_bf16(a, acc_pair_to_operand(sacc[2 * ks], sacc[2 * ks + 1]), num[ib]);
-                    den[ib] = mfma_bf16(a, acc_pair_to_operand(zacc[2 * ks], zacc[2 * ks + 1]), den[ib]);
+                    const int lb = 2 * (ks - KS0);
+                    num[ib] = mfma_bf16(a, acc_pair_to_operand(sacc[lb], sacc[lb + 1]), num[ib]);
+                    den[ib] = mfma_bf16(a, acc_pair_to_operand(zacc[lb], zacc[lb + 1]), den[ib]);
                 }
             }
-            // ---- intra-chunk part (causal): A = 1 + s + s^2/2 on j <= i, s = k_j . q_i
-            if (MODE == NM_CAUSAL) {
+            // ---- intra-chunk part (causal, wave 1): A = 1 + s + s^2/2 on j <= i, s = k_j . q_i
+            if (MODE == NM_CAUSAL && H == 1) {
                 bf16x8 kop[4], qop[4];
 #pragma unroll
                 for (int b = 0; b < 4; b++) {
@@ -188,15 +197,27 @@ __global__ __launch_bounds__(64) void narrow_kernel(NarrowParams p) {
                     }
                 }
             }
-            // ---- output
+            // ---- partials for the other wave's token blocks go through LDS; this wave finishes
+            // token blocks 2 H, 2 H + 1
+#pragma unroll
+            for (int ibl = 0; ibl < 2; ibl++) {
+                const int ib = 2 * (1 - H) + ibl;
+                sX[((H * 2 + ibl) * 2 + 0) * 64 + lane] = num[ib];
+                sX[((H * 2 + ibl) * 2 + 1) * 64 + lane] = den[ib];
+            }
+            __syncthreads();
             bf16_t *yb = p.y + base + (size_t)t0 * D;
 #pragma unroll
-            for (int ib = 0; ib < 4; ib++)
+            for (int ibl = 0; ibl < 2; ibl++) {
+                const int ib = 2 * H + ibl;
+                const f32x4 on = sX[(((1 - H) * 2 + ibl) * 2 + 0) * 64 + lane];
+                const f32x4 od = sX[(((1 - H) * 2 + ibl) * 2 + 1) * 64 + lane];
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     const int i = 16 * ib + 4 * g + r;
-                    if (i < valid) yb[(size_t)i * D + r16] = float_to_bf16_bits(num[ib][r] / den[ib][r]);
+                    if (i < valid) yb[(size_t)i * D + r16] = float_to_bf16_bits((num[ib][r] + on[r]) / (den[ib][r] + od[r]));
                 }
+            }
         }
 
         if (MODE != NM_READOUT) {
@@ -216,9 +237,10 @@ __global__ __launch_bounds__(64) void narrow_kernel(NarrowParams p) {
                 }
             }
 #pragma unroll
-            for (int fb = 0; fb < FB; fb++)
+            for (int lb = 0; lb < NB; lb++)
 #pragma unroll
                 for (int ks = 0; ks < 2; ks++) {
+                    const int fb = FB0 + lb;
                     bf16x8 a;
                     if (fb == 0) {
 #pragma unroll
@@ -235,14 +257,14 @@ __global__ __launch_bounds__(64) void narrow_kernel(NarrowParams p) {
                             a[4 + r] = (__bf16)((float)hi[r] * kr[ks][4 + r] * kInvSqrt2);
                         }
                     }
-                    sacc[fb] = mfma_bf16(a, vop[ks], sacc[fb]);
-                    zacc[fb] = mfma_bf16(a, ones, zacc[fb]);
+                    sacc[lb] = mfma_bf16(a, vop[ks], sacc[lb]);
+                    zacc[lb] = mfma_bf16(a, ones, zacc[lb]);
                 }
         }
         __syncthreads();
     }
 
-    // ---- segment end
+    // ---- segment end: this wave's rows
     float *So = nullptr, *zo = nullptr;
     bool canonical = false;
     if (MODE == NM_STATE) {
@@ -256,25 +278,41 @@ __global__ __launch_bounds__(64) void narrow_kernel(NarrowParams p) {
     }
     if (So) {
 #pragma unroll
-        for (int fb = 0; fb < FB; fb++)
+        for (int lb = 0; lb < NB; lb++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int f = 16 * fb + 4 * g + r;
+                const int f = 16 * (FB0 + lb) + 4 * g + r;
                 int row = f;
                 if (canonical) row = f < 272 ? f + 1 : (f == 272 ? 0 : -1);
                 if (row >= 0) {
-                    So[(size_t)row * D + r16] = sacc[fb][r];
-                    if (r16 == 0) zo[row] = zacc[fb][r];
+                    So[(size_t)row * D + r16] = sacc[lb][r];
+                    if (r16 == 0) zo[row] = zacc[lb][r];
                 }
             }
     }
 }
 
+template <int MODE>
+__global__ __launch_bounds__(128, 2) void narrow_kernel(NarrowParams p) {
+    __shared__ __attribute__((aligned(16))) bf16_t sQ[C * RR];
+    __shared__ __attribute__((aligned(16))) bf16_t sK[C * RR];
+    __shared__ __attribute__((aligned(16))) bf16_t sKT[D * RT];
+    __shared__ __attribute__((aligned(16))) bf16_t sVT[D * RT];
+    __shared__ __attribute__((aligned(16))) f32x4 sX[2 * 2 * 2 * 64];  // read-out partials [wave][block][num, den][lane]
+    const int bh = blockIdx.x / p.nseg_grid;
+    const int s = blockIdx.x % p.nseg_grid;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (w == 0)
+        narrow_wave<MODE, 0>(p, bh, s, lane, sQ, sK, sKT, sVT, sX);
+    else
+        narrow_wave<MODE, 1>(p, bh, s, lane, sQ, sK, sKT, sVT, sX);
+}
+
 hipError_t launch_narrow(int mode, const NarrowParams &p, int grid, hipStream_t st) {
     switch (mode) {
-    case NM_STATE: hipLaunchKernelGGL(narrow_kernel<NM_STATE>, dim3(grid), dim3(64), 0, st, p); break;
-    case NM_CAUSAL: hipLaunchKernelGGL(narrow_kernel<NM_CAUSAL>, dim3(grid), dim3(64), 0, st, p); break;
-    default: hipLaunchKernelGGL(narrow_kernel<NM_READOUT>, dim3(grid), dim3(64), 0, st, p); break;
+    case NM_STATE: hipLaunchKernelGGL(narrow_kernel<NM_STATE>, dim3(grid), dim3(128), 0, st, p); break;
+    case NM_CAUSAL: hipLaunchKernelGGL(narrow_kernel<NM_CAUSAL>, dim3(grid), dim3(128), 0, st, p); break;
+    default: hipLaunchKernelGGL(narrow_kernel<NM_READOUT>, dim3(grid), dim3(128), 0, st, p); break;
     }
     return hipGetLastError();
 }
