@@ -307,12 +307,12 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
             slZ = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + wide_slot_S_bytes(BH, pl.nseg, d));
         }
         wp.S_slots = slS; wp.z_slots = slZ; wp.slot_bh_stride = pl.nseg;
-        // d = 128 causal with few segments per sequence: the chunked pass sums the aggregates of
-        // the earlier segments itself (at most 7 slots, still in L2) instead of a separate scan
-        const bool direct_prefix = causal && d == 128 && pl.nseg <= 8;
+        // causal with few segments per sequence: the chunked pass sums the aggregates of the
+        // earlier segments itself (at most 7 slots, still in L2) instead of a separate scan
+        const bool direct_prefix = causal && pl.nseg <= 8;
         wp.seg_count = pl.nseg;
-        // those segments taper (see seg_range) when they are long enough for it to matter
-        wp.seg_skew16 = direct_prefix && ((N + 31) / 32) / pl.nseg >= 8 ? HH_SEG_SKEW16 : 0;
+        // for d = 128 those segments taper (see seg_range) when they are long enough to matter
+        wp.seg_skew16 = direct_prefix && d == 128 && ((N + 31) / 32) / pl.nseg >= 8 ? HH_SEG_SKEW16 : 0;
         wp.N = N; wp.H = H; wp.seg_len = pl.seg_len;
         if (run_state) {
             wp.nseg_grid = state_segments;

@@ -26,7 +26,7 @@ struct WideParams {
     int slot_mode;              // slot added to the starting state of segment s (modes 1, 2):
                                 //   0 none, 1 slot s if s > 0 (exclusive prefixes), 2 slot 0 (total),
                                 //   3 the sum of slots 0 .. s - 1 (segment aggregates, summed by the
-                                //   d = 128 causal pass itself; no scan)
+                                //   causal pass itself; no scan)
 };
 // Segment slots of the wide kernels: per (b,h), nseg slots of S (2 d * d bf16) and z
 // (2 d floats).  Mode 0: aggregates of slots 0 .. nseg-2 become exclusive prefixes in slots

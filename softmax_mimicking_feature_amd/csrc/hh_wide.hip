@@ -835,10 +835,13 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
 #pragma unroll
                 for (int r = 0; r < 4; r++) zacc[zb][r] = zi[16 * (w * K::ZB + zb) + 4 * g + r];
         }
-        int slot = -1;
-        if (MODE != WM_STATE && p.slot_mode == 1 && s > 0) slot = s;
-        if (MODE != WM_STATE && p.slot_mode == 2) slot = 0;
-        if (slot >= 0) {
+        // slots added to the starting state: the exclusive prefix (slot_mode 1), the total
+        // (slot_mode 2) or the earlier segments' aggregates, summed here (slot_mode 3)
+        int t0 = 0, t1 = 0;
+        if (MODE != WM_STATE && p.slot_mode == 1 && s > 0) t0 = s, t1 = s + 1;
+        if (MODE != WM_STATE && p.slot_mode == 2) t0 = 0, t1 = 1;
+        if (MODE != WM_STATE && p.slot_mode == 3) t0 = 0, t1 = s;
+        for (int slot = t0; slot < t1; slot++) {
             const size_t sl = (size_t)bh * p.slot_bh_stride + slot;
             const bf16x8 *img = reinterpret_cast<const bf16x8 *>(p.S_slots + sl * K::DP * D) + w * K::IMG8 * 64 + lane;
             bf16x8 t[K::IMG8];
