@@ -314,6 +314,13 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
         // for d = 128 those segments taper (see seg_range) when they are long enough to matter
         wp.seg_skew16 = direct_prefix && d == 128 && ((N + 31) / 32) / pl.nseg >= 8 ? HH_SEG_SKEW16 : 0;
         wp.N = N; wp.H = H; wp.seg_len = pl.seg_len;
+        if (!causal && pl.nseg == 1 && d == 64) {
+            // one segment per sequence: state and read-out in one workgroup, the total in LDS
+            wp.nseg_grid = 1;
+            e = hh::launch_bidir_fused(d, wp, (int)BH, s);
+            if (e != hipSuccess) return hip_fail(e, "bidirectional forward launch");
+            return ok();
+        }
         if (run_state) {
             wp.nseg_grid = state_segments;
             e = hh::launch_wide(d, 0, wp, (int)(BH * state_segments), s);

@@ -33,6 +33,9 @@ struct WideParams {
 // 1 .. nseg-1; mode 1: the total of all nseg slots goes to slot 0.  Sums run in fp32.
 hipError_t launch_slot_scan(int d, bf16_t *S_slots, float *z_slots, int BH, int nseg, int mode, hipStream_t st);
 hipError_t launch_wide(int d, int mode, const WideParams &p, int grid, hipStream_t st);
+// Bidirectional forward with one segment per sequence (d = 64): state and read-out in one
+// workgroup per sequence, the total state handed over in LDS (no workspace).
+hipError_t launch_bidir_fused(int d, const WideParams &p, int BH, hipStream_t st);
 int wide_wgs_per_cu(int d);
 
 // Hedgehog feature map on the matrix cores (bf16): x [BH][N][d] -> phi [BH][N][2d].

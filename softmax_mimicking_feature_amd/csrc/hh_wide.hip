@@ -774,20 +774,18 @@ __device__ __forceinline__ void chunk_step(const WideParams &p, size_t base, int
 // scores balance better), the other passes 64.
 constexpr int wide_chunk(int D, int MODE) { return (D == 128 && MODE == WM_CAUSAL) ? 32 : 64; }
 
+// One workgroup's work: segment s of sequence bh, with `smem` the K::LDS_BYTES of its tiles.
 template <int D, int MODE>
-__global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wide_kernel(WideParams p) {
+__device__ __forceinline__ void wide_body(const WideParams &p, unsigned char *smem, int bh, int s) {
     constexpr int C = wide_chunk(D, MODE);
     using K = WideCfg<D, C, MODE>;
     static_assert(K::LDS_BYTES <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[K::LDS_BYTES];
 
     const int tid = threadIdx.x;
     // wave index as a scalar: role branches on it stay scalar (never exec-masked around MFMAs)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int dq = w % K::NDQ;
     const int fa = w / K::NN, nq = w % K::NN;
-    int bh, s;
-    wg_head_segment(p.nseg_grid, bh, s);
     const int h = bh % p.H;
     const int t_begin = s * p.seg_len;
     const int t_end = min(p.N, t_begin + p.seg_len);
@@ -949,6 +947,14 @@ __global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wid
     }
 }
 
+template <int D, int MODE>
+__global__ __launch_bounds__(WideCfg<D>::NT, WideCfg<D>::MIN_WG_PER_CU) void wide_kernel(WideParams p) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[WideCfg<D, wide_chunk(D, MODE), MODE>::LDS_BYTES];
+    int bh, s;
+    wg_head_segment(p.nseg_grid, bh, s);
+    wide_body<D, MODE>(p, smem, bh, s);
+}
+
 // ---------------------------------------------------------------------------------------
 // Segment aggregates with symmetric waves (d = 64 and 128, 64-token chunks).  Wave w of the
 // d / 16 waves owns feature blocks w (exp(+u) of directions 16 w .. 16 w + 15) and d / 16 + w
@@ -1080,14 +1086,13 @@ __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t 
     }
 }
 
+// One workgroup's work: the aggregate of segment s of sequence bh into slot bh slot_bh_stride + s,
+// with `smem` the S::LDS_BYTES of its tiles.
 template <int D>
-__global__ __launch_bounds__(StateSymCfg<D>::NT, StateSymCfg<D>::WG_PER_CU) void state_sym_kernel(WideParams p) {
+__device__ __forceinline__ void state_sym_body(const WideParams &p, unsigned char *smem, int bh, int s) {
     using S = StateSymCfg<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
-    int bh, s;
-    wg_head_segment(p.nseg_grid, bh, s);
     const int h = bh % p.H;
     int t_begin, t_end;
     seg_range(p, s, t_begin, t_end);
@@ -1182,6 +1187,52 @@ __global__ __launch_bounds__(StateSymCfg<D>::NT, StateSymCfg<D>::WG_PER_CU) void
 #pragma unroll
             for (int r = 0; r < 4; r++) zs[16 * (S::NW * f + w) + 4 * g + r] = zacc[f][r];
     }
+}
+
+template <int D>
+__global__ __launch_bounds__(StateSymCfg<D>::NT, StateSymCfg<D>::WG_PER_CU) void state_sym_kernel(WideParams p) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[StateSymCfg<D>::LDS_BYTES];
+    int bh, s;
+    wg_head_segment(p.nseg_grid, bh, s);
+    state_sym_body<D>(p, smem, bh, s);
+}
+
+// Bidirectional mode with one segment per sequence (d = 64): the total state S = phiK^T V,
+// z = phiK^T 1 of the whole sequence and the read-out against it in one workgroup.  The state
+// pass leaves the total in LDS, in the register image the read-out loads its slot from, instead
+// of a workspace slot in memory that a second kernel reads back.
+template <int D>
+struct BidirFusedCfg {
+    static constexpr int TILES = StateSymCfg<D>::LDS_BYTES > WideCfg<D, 64, WM_READOUT>::LDS_BYTES
+                                     ? StateSymCfg<D>::LDS_BYTES
+                                     : WideCfg<D, 64, WM_READOUT>::LDS_BYTES;
+    static constexpr int SLOT_S = 2 * D * D * 2;  // bf16 S image
+    static constexpr int SLOT_Z = 2 * D * 4;      // fp32 z
+    static_assert(StateSymCfg<D>::NT == WideCfg<D>::NT, "both passes use the same workgroup");
+    static_assert((TILES + SLOT_S + SLOT_Z) * 2 <= 160 * 1024, "two workgroups per CU");
+};
+
+template <int D>
+__global__ __launch_bounds__(WideCfg<D>::NT, 2) void bidir_fused_kernel(WideParams p) {
+    using F = BidirFusedCfg<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[F::TILES];
+    __shared__ __attribute__((aligned(16))) bf16_t slotS[F::SLOT_S / 2];
+    __shared__ __attribute__((aligned(16))) float slotZ[F::SLOT_Z / 4];
+    const int bh = blockIdx.x;
+    WideParams q = p;
+    q.S_slots = slotS;  // generic pointers to LDS: slot 0 of every sequence
+    q.z_slots = slotZ;
+    q.slot_bh_stride = 0;
+    q.slot_mode = 2;
+    state_sym_body<D>(q, smem, bh, 0);
+    __syncthreads();  // the total is complete, the state pass's tiles are free
+    wide_body<D, WM_READOUT>(q, smem, bh, 0);
+}
+
+hipError_t launch_bidir_fused(int d, const WideParams &p, int BH, hipStream_t st) {
+    if (d != 64) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bidir_fused_kernel<64>, dim3(BH), dim3(WideCfg<64>::NT), 0, st, p);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------
