@@ -15,10 +15,6 @@
 
 #include "hh_kernels.h"
 
-#ifndef HH_SEG_SKEW16
-#define HH_SEG_SKEW16 8  // taper of the chunked pass's segments, in 1/16 chunk per predecessor
-#endif
-
 namespace {
 
 thread_local std::string g_last_error;
@@ -310,9 +306,6 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
         // causal with few segments per sequence: the chunked pass sums the aggregates of the
         // earlier segments itself (at most 7 slots, still in L2) instead of a separate scan
         const bool direct_prefix = causal && pl.nseg <= 8;
-        wp.seg_count = pl.nseg;
-        // for d = 128 those segments taper (see seg_range) when they are long enough to matter
-        wp.seg_skew16 = direct_prefix && d == 128 && ((N + 31) / 32) / pl.nseg >= 8 ? HH_SEG_SKEW16 : 0;
         wp.N = N; wp.H = H; wp.seg_len = pl.seg_len;
         if (!causal && pl.nseg == 1 && d == 64) {
             // one segment per sequence: state and read-out in one workgroup, the total in LDS

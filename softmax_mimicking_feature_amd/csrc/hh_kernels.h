@@ -21,8 +21,6 @@ struct WideParams {
     long slot_bh_stride;        // slots per (b,h)
     float *S_out, *z_out;       // final state (mode 1, last segment), or null
     int N, H, nseg_grid, seg_len;
-    int seg_count;              // segments per sequence (the chunked pass's grid; the state pass may run fewer)
-    int seg_skew16;             // 0: uniform segments of seg_len tokens; else the tapered cut of seg_range
     int slot_mode;              // slot added to the starting state of segment s (modes 1, 2):
                                 //   0 none, 1 slot s if s > 0 (exclusive prefixes), 2 slot 0 (total),
                                 //   3 the sum of slots 0 .. s - 1 (segment aggregates, summed by the

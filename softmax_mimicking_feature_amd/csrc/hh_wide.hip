@@ -128,28 +128,6 @@ __device__ __forceinline__ void wg_head_segment(int nseg, int &bh, int &s) {
     }
 }
 
-// Token range [tb, te) of segment s.  seg_skew16 == 0: uniform segments of seg_len tokens.
-// Otherwise the sequence is cut at 32-token units and segment k starts at unit
-// round(k u / n + r k (n - k) / 2), r = seg_skew16 / 16 (u units, n segments): earlier segments are
-// a little longer, so that the later ones, which first sum more of their predecessors'
-// aggregates, finish at the same time.  The segment-state and chunked passes share it.
-__device__ __forceinline__ void seg_range(const WideParams &p, int s, int &tb, int &te) {
-    if (p.seg_skew16 == 0) {
-        tb = s * p.seg_len;
-        te = min(p.N, tb + p.seg_len);
-        return;
-    }
-    const int n = p.seg_count;
-    const long u = (p.N + 31) >> 5;
-    auto start = [&](int k) {
-        if (k >= n) return p.N;
-        const long num = 32L * k * u + (long)p.seg_skew16 * k * (n - k) * n + 16L * n;
-        return (int)min((long)p.N, (num / (32L * n)) * 32);
-    };
-    tb = start(s);
-    te = start(s + 1);
-}
-
 // Position of feature f in a row-major feature tile.  With PERM, each 32-feature group is
 // stored in the K order of two stacked accumulator blocks (lane group g reads features
 // {4g..4g+3, 16+4g..16+4g+3} as one 16-byte run), so the read-out operand that pairs with
@@ -1094,8 +1072,8 @@ __device__ __forceinline__ void state_sym_body(const WideParams &p, unsigned cha
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int h = bh % p.H;
-    int t_begin, t_end;
-    seg_range(p, s, t_begin, t_end);
+    const int t_begin = s * p.seg_len;
+    const int t_end = min(p.N, t_begin + p.seg_len);
     const size_t base = (size_t)bh * p.N * D;
     const int n = t_end > t_begin ? (t_end - t_begin + S::C - 1) / S::C : 0;
     const DmaLanesT<D, S::C, S::NW> dl(w, lane);
@@ -1431,8 +1409,8 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     int bh, s;
     wg_head_segment(p.nseg_grid, bh, s);
     const int h = bh % p.H;
-    int t_begin, t_end;
-    seg_range(p, s, t_begin, t_end);
+    const int t_begin = s * p.seg_len;
+    const int t_end = min(p.N, t_begin + p.seg_len);
     const size_t base = (size_t)bh * p.N * S::D;
     const int n = t_end > t_begin ? (t_end - t_begin + S::C - 1) / S::C : 0;
     const DmaLanes128<32> dl(w, lane);
