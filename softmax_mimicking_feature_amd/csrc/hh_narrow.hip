@@ -222,7 +222,7 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
 
         if (MODE != NM_READOUT) {
             // ---- state update: phi(k)^T built per operand slot (rows f = 16 fb + r16, K = tokens)
-            float kr[2][8], okc[2][8];
+            float kr[2][8], krs[2][8], okc[2][8];
 #pragma unroll
             for (int ks = 0; ks < 2; ks++) {
                 const bf16_t *kp = sKT + r16 * RT + 32 * ks + 4 * g;
@@ -231,6 +231,8 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                 for (int r = 0; r < 4; r++) {
                     kr[ks][r] = (float)lo[r];
                     kr[ks][4 + r] = (float)hi[r];
+                    krs[ks][r] = kr[ks][r] * kInvSqrt2;
+                    krs[ks][4 + r] = kr[ks][4 + r] * kInvSqrt2;
                     const int jlo = 32 * ks + 4 * g + r, jhi = jlo + 16;
                     okc[ks][r] = (r16 == 0 && jlo < valid) ? 1.0f : 0.0f;
                     okc[ks][4 + r] = (r16 == 0 && jhi < valid) ? 1.0f : 0.0f;
@@ -253,8 +255,8 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                         const bf16x4 lo = load4(kp), hi = load4(kp + 16);
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
-                            a[r] = (__bf16)((float)lo[r] * kr[ks][r] * kInvSqrt2);
-                            a[4 + r] = (__bf16)((float)hi[r] * kr[ks][4 + r] * kInvSqrt2);
+                            a[r] = (__bf16)((float)lo[r] * krs[ks][r]);
+                            a[4 + r] = (__bf16)((float)hi[r] * krs[ks][4 + r]);
                         }
                     }
                     sacc[lb] = mfma_bf16(a, vop[ks], sacc[lb]);
