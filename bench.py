@@ -84,10 +84,11 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, decode: bool = False):
     """HBM bytes per call from the committed FETCH_SIZE / WRITE_SIZE summary of this workload,
     or None when there is none or the kernels changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"hh_linattn_fwd_{workload}_traffic.md")
+    entry = "hh_linattn_decode_step" if decode else "hh_linattn_fwd"
+    path = os.path.join(ROOT, "profiles", f"{entry}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -264,15 +265,24 @@ def main():
     ridge = PEAK_MFMA_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     bound = "hbm" if ai < ridge else "mfma"
     if bound == "hbm":
-        traffic = recorded_traffic(args.workload)
+        traffic = recorded_traffic(args.workload, decode)
         roof = {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach_gbs / PEAK_HBM_GBS, 4),
                 "traffic": None if traffic is None else round(traffic / (launch_ms * 1e-3) / 1e9, 1)}
     else:
         roof = {"bound": "mfma", "achieved": round(ach_tflops, 1), "peak": PEAK_MFMA_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach_tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = ("hh_linattn_decode_step (decode_kernel)" if decode else
-                      "hh_linattn_fwd: the segment-state, segment-scan and chunked kernels of one call")
+    if decode:
+        roof["kernel"] = "hh_linattn_decode_step (decode_kernel)"
+    elif w.map == wl.MAP_TAYLOR2:
+        roof["kernel"] = ("hh_linattn_fwd: every kernel of one call (segment aggregates, exclusive prefix "
+                          "over segments, chunked causal pass)")
+    elif not w.causal:
+        roof["kernel"] = ("hh_linattn_fwd: every kernel of one call (total state and read-out; one fused "
+                          "kernel when a sequence is one segment)")
+    else:
+        roof["kernel"] = ("hh_linattn_fwd: every kernel of one call (segment-state pass, then the chunked pass, "
+                          "which adds the earlier segments' aggregates itself)")
     roof["launch_ms_mean"] = round(launch_ms, 5)
     roof["calls_per_timed_launch"] = gsteps  # a timed launch: one graph replay of this many calls
     roof["launch_ms_p10_p90"] = [round(float(np.percentile(per, 10)), 5), round(float(np.percentile(per, 90)), 5)]
@@ -300,7 +310,9 @@ def main():
                          f"{tc:.2f} s wall on {nthr} threads"}
 
     out = {
-        "metric": METRIC if not decode else "decode step tokens/s (one token per sequence)",
+        "metric": (METRIC if w.name == "c3_llama2_causal" else
+                   "decode step tokens/s (one token per sequence)" if decode else
+                   f"{'causal' if w.causal else 'bidirectional'} linear-attn fwd tokens/s (\u03c6 incl.), {w.name}"),
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
