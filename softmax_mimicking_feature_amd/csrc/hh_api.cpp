@@ -351,6 +351,7 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
         }
         np.S_in = S_in; np.z_in = z_in; np.in_bh_stride = in_bh; np.in_seg_stride = in_seg;
         np.S_out = S_out; np.z_out = z_out;
+        np.S0c = S0; np.z0c = z0;
         np.nseg_grid = pl.nseg;
         e = hh::launch_narrow(out_mode, np, (int)(BH * pl.nseg), s);
         if (e != hipSuccess) return hip_fail(e, "chunked forward launch");

@@ -49,10 +49,12 @@ struct NarrowParams {
     float *S_ws, *z_ws;
     long ws_bh_stride;
     float *S_out, *z_out;  // canonical feature order
+    const float *S0c, *z0c;  // the caller's initial state, canonical order (or null), read only for
+                             // the part of S_out the packed basis does not hold
     int N, nseg_grid, seg_len;
 };
 hipError_t launch_narrow(int mode, const NarrowParams &p, int grid, hipStream_t st);
-constexpr int kTaylorRowsInternal = 288;  // 273 features padded to 18 blocks of 16
+constexpr int kTaylorRowsInternal = 160;  // 153 packed symmetric features padded to 10 blocks of 16
 
 // Scan of segment aggregates into exclusive prefixes (mode 0) or one total (mode 1).
 struct PrefixParams {

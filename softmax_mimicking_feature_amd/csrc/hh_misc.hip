@@ -1,4 +1,4 @@
-// hh_misc.hip -- the smaller libhh kernels: segment-state scan, empty-sequence state,
+// hh_misc.hip -- the smaller libhh kernels: Taylor segment prefix, empty-sequence state,
 // the fp32 token-by-token path, the decode step and the vector-unit feature map.
 //
 // Feature maps (paper-graph-ui walkthrough of "The Hedgehog & the Porcupine"):
@@ -13,14 +13,30 @@
 namespace hh {
 
 // ----------------------------------------------------------------------------------------
-// Internal row order of the Taylor state in the chunked kernels: rows 0..271 hold the
-// canonical features 1..272 (linear then quadratic), row 272 the constant feature,
-// rows 273..287 are zero padding.  Hedgehog rows are stored in canonical order.
-__device__ __forceinline__ int internal_to_canonical_row(int map, int r) {
-    if (map == 0) return r;
-    if (r < 272) return r + 1;
-    if (r == 272) return 0;
-    return -1;
+// Internal rows of the Taylor state in the chunked kernels: a packed symmetric basis of 160
+// rows (1 + 16 + 136 features, padded).  Row p < 16: the linear feature x_p (canonical row
+// 1 + p).  Row 16 (1 + o) + p, o = 0..7: the pair (p, c = p + o mod 16); o = 0 is the
+// diagonal x_p^2 / sqrt(2) (canonical row 17 + 17 p), o > 0 the off-diagonal feature x_p x_c,
+// which carries both canonical rows (p, c) and (c, p), each x_p x_c / sqrt(2).  Rows 144 + p:
+// the pair (p, p + 8) for p < 8, the constant feature at p = 8 (canonical row 0), zero above.
+// Value of internal row r of a canonical state X (element (row, col) at X[row * ld + col]):
+// a pair row is (X_pc + X_cp) / sqrt(2), which keeps every query's read-out of X unchanged.
+__device__ __forceinline__ float taylor_packed_value(const float *X, int r, int col, int ld) {
+    constexpr float kInvSqrt2 = 0.70710678118654752f;
+    if (r < 16) return X[(size_t)(1 + r) * ld + col];
+    int p, c;
+    if (r < 144) {
+        const int o = r / 16 - 1;
+        p = r % 16;
+        if (o == 0) return X[(size_t)(17 + 17 * p) * ld + col];
+        c = (p + o) & 15;
+    } else {
+        p = r - 144;
+        if (p == 8) return X[col];
+        if (p > 8) return 0.0f;
+        c = p + 8;
+    }
+    return (X[(size_t)(17 + 16 * p + c) * ld + col] + X[(size_t)(17 + 16 * c + p) * ld + col]) * kInvSqrt2;
 }
 
 __global__ void prefix_kernel(PrefixParams p) {
@@ -43,8 +59,9 @@ __global__ void prefix_kernel(PrefixParams p) {
     }
     float run = 0.0f;
     if (p.S0) {
-        const int c = internal_to_canonical_row(p.map, row);
-        if (c >= 0) run = isS ? p.S0[((size_t)bh * p.dpc + c) * p.d + col] : p.z0[(size_t)bh * p.dpc + c];
+        if (p.map == 0) run = isS ? p.S0[((size_t)bh * p.dpc + row) * p.d + col] : p.z0[(size_t)bh * p.dpc + row];
+        else run = isS ? taylor_packed_value(p.S0 + (size_t)bh * p.dpc * p.d, row, col, p.d)
+                       : taylor_packed_value(p.z0 + (size_t)bh * p.dpc, row, 0, 1);
     }
     // Segments go in groups of G: all loads of a group are issued before its stores, so that a
     // thread waits for memory once per group rather than once per segment.

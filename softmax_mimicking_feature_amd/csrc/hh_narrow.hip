@@ -12,11 +12,16 @@
 //     with s = Q_c K_c^T (a K = 16 product), the identity above, instead of a K = 273
 //     product of feature vectors.
 //   * Features are never stored: each lane builds the 8 feature values an MFMA operand
-//     slot needs from the raw q or k values, so one wave holds the whole 288 x 16 fp32
-//     state in registers.
-// Internal feature-row order (a permutation of the canonical one): block 0 = x_0..x_15,
-// block 1 + a = x_a x_p / sqrt(2) for p = 0..15, block 17 = [1, 0 ... 0].  Canonical
-// index c maps to internal row c - 1 (c >= 1) and row 272 (c = 0).
+//     slot needs from the raw q or k values, so two waves hold the whole state in registers.
+//   * The state is kept in a packed symmetric basis.  phi(q)^T phi(k) only involves the
+//     quadratic features through sum_{a,c} q_a q_c k_a k_c / 2, in which the pairs (a, c) and
+//     (c, a) contribute equally; so one feature per unordered pair carries both: x_a x_c for
+//     a != c, x_a^2 / sqrt(2) on the diagonal.  1 + 16 + 136 = 153 features (padded to 160)
+//     give the same phi(q)^T phi(k) as the 273 canonical ones, and the canonical state is
+//     recovered exactly: S_ac = S_ca = (packed row {a,c}) / sqrt(2) off the diagonal.
+// Internal feature-row order: block 0 = x_p; block 1 + o (o = 0..7) = the pair (p, p + o mod
+// 16) for p = 0..15 (o = 0: the diagonal); block 9 = the pairs (p, p + 8) for p < 8, the
+// constant 1 at p = 8, zero rows at p > 8.  Every unordered pair appears exactly once.
 #include "hh_common.h"
 #include "hh_kernels.h"
 
@@ -25,7 +30,7 @@ namespace hh {
 namespace {
 constexpr int D = 16;
 constexpr int C = 64;
-constexpr int FB = 18;          // 16-row feature blocks (288 rows)
+constexpr int FB = 10;          // 16-row feature blocks (160 rows)
 constexpr int KSF = FB / 2;     // 32-wide K steps over features
 constexpr int RR = D + 8;       // row stride of [C][D] tiles (bf16)
 constexpr int RT = C + 8;       // row stride of [D][C] tiles (bf16)
@@ -33,22 +38,24 @@ constexpr float kInvSqrt2 = 0.70710678118654752f;
 enum { NM_STATE = 0, NM_CAUSAL = 1, NM_READOUT = 2 };
 }  // namespace
 
-// Feature value of internal block fb at position p, for a token whose values are x[0..15].
-// xp = x[p] (already multiplied by 1/sqrt(2) for the quadratic blocks: xps).
-__device__ __forceinline__ float taylor_feature(int fb, const float (&x)[D], float xp, float xps, bool const_on) {
-    if (fb == 0) return xp;
-    if (fb == 17) return const_on ? 1.0f : 0.0f;
-    return x[fb - 1] * xps;
+// Packed feature of internal block fb at position 4 g + r of a token, from the token's values
+// rotated by the lane group: x[j] = value (4 g + j) mod 16.  m9 = (g < 2), c9 = (g == 2) select
+// block 9's pair rows, its constant and its zero rows.
+__device__ __forceinline__ float packed_feature(int fb, int r, const float (&x)[12], float m9, float c9) {
+    if (fb == 0) return x[r];
+    if (fb == 1) return x[r] * x[r] * kInvSqrt2;
+    if (fb < 9) return x[r] * x[r + fb - 1];
+    return r == 0 ? fmaf(x[0] * x[8], m9, c9) : x[r] * x[r + 8] * m9;
 }
 
 // Work of wave H of the two waves of a workgroup.  Wave H holds the state rows of the K steps
-// [KS0, KS1) (feature blocks 2 KS0 .. 2 KS1 - 1): wave 0 steps 0-4, wave 1 steps 5-8 plus the
+// [KS0, KS1) (feature blocks 2 KS0 .. 2 KS1 - 1): wave 0 steps 0-2, wave 1 steps 3-4 plus the
 // intra-chunk part, so each wave builds only its own feature operands.  The read-out partials
 // over the two halves meet in LDS: each wave finishes two of the four 16-token blocks.
 template <int MODE, int H>
 __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s, int lane, bf16_t *sQ, bf16_t *sK,
                                             bf16_t *sKT, bf16_t *sVT, f32x4 *sX) {
-    constexpr int KS0 = H == 0 ? 0 : 5, KS1 = H == 0 ? 5 : KSF;
+    constexpr int KS0 = H == 0 ? 0 : 3, KS1 = H == 0 ? 3 : KSF;
     constexpr int NB = 2 * (KS1 - KS0);  // feature blocks held by this wave
     constexpr int FB0 = 2 * KS0;
     const int g = lane >> 4, r16 = lane & 15;
@@ -75,6 +82,8 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
             }
     }
     const bf16x8 ones = ones_bf16x8();
+    const float m9 = g < 2 ? 1.0f : 0.0f, c9 = g == 2 ? 1.0f : 0.0f;          // query side, block 9
+    const float m9k = r16 < 8 ? 1.0f : 0.0f;                                    // key side, block 9
 
     for (int t0 = t_begin; t0 < t_end; t0 += C) {
         const int valid = min(C, t_end - t0);
@@ -131,31 +140,24 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
 #pragma unroll
             for (int ib = 0; ib < 4; ib++) {
                 const int i = 16 * ib + r16;
-                float x[D];
-                {
-                    const bf16x8 a0 = load8(sQ + i * RR), a1 = load8(sQ + i * RR + 8);
+                // the token's values rotated by the lane group, as far as this wave's blocks reach
+                constexpr int NRUN = H == 0 ? 2 : 3;
+                float x[12];
 #pragma unroll
-                    for (int m = 0; m < 8; m++) {
-                        x[m] = (float)a0[m];
-                        x[8 + m] = (float)a1[m];
-                    }
-                }
-                float xp[4], xps[4];
-                {
-                    const bf16x4 q4 = load4(sQ + i * RR + 4 * g);
+                for (int m = 0; m < 12; m++) x[m] = 0.0f;
 #pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        xp[r] = (float)q4[r];
-                        xps[r] = xp[r] * kInvSqrt2;
-                    }
+                for (int m = 0; m < NRUN; m++) {
+                    const bf16x4 q4 = load4(sQ + i * RR + 4 * ((g + m) & 3));
+#pragma unroll
+                    for (int r = 0; r < 4; r++) x[4 * m + r] = (float)q4[r];
                 }
 #pragma unroll
                 for (int ks = KS0; ks < KS1; ks++) {
                     bf16x8 a;
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
-                        a[r] = (__bf16)taylor_feature(2 * ks, x, xp[r], xps[r], g == 0 && r == 0);
-                        a[4 + r] = (__bf16)taylor_feature(2 * ks + 1, x, xp[r], xps[r], g == 0 && r == 0);
+                        a[r] = (__bf16)packed_feature(2 * ks, r, x, m9, c9);
+                        a[4 + r] = (__bf16)packed_feature(2 * ks + 1, r, x, m9, c9);
                     }
                     const int lb = 2 * (ks - KS0);
                     num[ib] = mfma_bf16(a, acc_pair_to_operand(sacc[lb], sacc[lb + 1]), num[ib]);
@@ -221,7 +223,9 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
         }
 
         if (MODE != NM_READOUT) {
-            // ---- state update: phi(k)^T built per operand slot (rows f = 16 fb + r16, K = tokens)
+            // ---- state update: phi(k)^T built per operand slot (rows: position p = r16 of each
+            // block, K = tokens); the pair partner of p in block 1 + o is row (p + o) mod 16 of
+            // the transposed key tile
             float kr[2][8], krs[2][8], okc[2][8];
 #pragma unroll
             for (int ks = 0; ks < 2; ks++) {
@@ -234,8 +238,8 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                     krs[ks][r] = kr[ks][r] * kInvSqrt2;
                     krs[ks][4 + r] = kr[ks][4 + r] * kInvSqrt2;
                     const int jlo = 32 * ks + 4 * g + r, jhi = jlo + 16;
-                    okc[ks][r] = (r16 == 0 && jlo < valid) ? 1.0f : 0.0f;
-                    okc[ks][4 + r] = (r16 == 0 && jhi < valid) ? 1.0f : 0.0f;
+                    okc[ks][r] = (r16 == 8 && jlo < valid) ? 1.0f : 0.0f;
+                    okc[ks][4 + r] = (r16 == 8 && jhi < valid) ? 1.0f : 0.0f;
                 }
             }
 #pragma unroll
@@ -247,16 +251,18 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                     if (fb == 0) {
 #pragma unroll
                         for (int sl = 0; sl < 8; sl++) a[sl] = (__bf16)kr[ks][sl];
-                    } else if (fb == 17) {
+                    } else if (fb == 1) {
 #pragma unroll
-                        for (int sl = 0; sl < 8; sl++) a[sl] = (__bf16)okc[ks][sl];
+                        for (int sl = 0; sl < 8; sl++) a[sl] = (__bf16)(kr[ks][sl] * krs[ks][sl]);
                     } else {
-                        const bf16_t *kp = sKT + (fb - 1) * RT + 32 * ks + 4 * g;
+                        const int o = fb < 9 ? fb - 1 : 8;
+                        const bf16_t *kp = sKT + ((r16 + o) & 15) * RT + 32 * ks + 4 * g;
                         const bf16x4 lo = load4(kp), hi = load4(kp + 16);
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
-                            a[r] = (__bf16)((float)lo[r] * krs[ks][r]);
-                            a[4 + r] = (__bf16)((float)hi[r] * krs[ks][4 + r]);
+                            const float plo = (float)lo[r] * kr[ks][r], phi_ = (float)hi[r] * kr[ks][4 + r];
+                            a[r] = (__bf16)(fb < 9 ? plo : fmaf(plo, m9k, okc[ks][r]));
+                            a[4 + r] = (__bf16)(fb < 9 ? phi_ : fmaf(phi_, m9k, okc[ks][4 + r]));
                         }
                     }
                     sacc[lb] = mfma_bf16(a, vop[ks], sacc[lb]);
@@ -278,17 +284,62 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
         zo = p.z_out + (size_t)bh * 273;
         canonical = true;
     }
-    if (So) {
+    if (So && !canonical) {
 #pragma unroll
         for (int lb = 0; lb < NB; lb++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int f = 16 * (FB0 + lb) + 4 * g + r;
-                int row = f;
-                if (canonical) row = f < 272 ? f + 1 : (f == 272 ? 0 : -1);
-                if (row >= 0) {
-                    So[(size_t)row * D + r16] = sacc[lb][r];
-                    if (r16 == 0) zo[row] = zacc[lb][r];
+                So[(size_t)f * D + r16] = sacc[lb][r];
+                if (r16 == 0) zo[f] = zacc[lb][r];
+            }
+    } else if (So) {
+        // canonical rows: 0 constant, 1 + a linear, 17 + 16 a + c the pair (a, c).  A packed pair
+        // row splits into its two canonical rows, each 1/sqrt(2) of it; the antisymmetric part of
+        // the caller's initial state, which the packed basis cannot hold (and which no output
+        // depends on), is added back so that S_out = S0 + the sum over the keys exactly.
+        const float *S0c = p.S0c ? p.S0c + (size_t)bh * 273 * D : nullptr;
+        const float *z0c = p.z0c ? p.z0c + (size_t)bh * 273 : nullptr;
+#pragma unroll
+        for (int lb = 0; lb < NB; lb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int fb = FB0 + lb, pos = 4 * g + r;
+                const float sv = sacc[lb][r], zv = zacc[lb][r];
+                int ca = -1, cb = -1;
+                if (fb == 0) {
+                    ca = 1 + pos;
+                } else if (fb == 1) {
+                    ca = 17 + 17 * pos;
+                } else if (fb < 9 || pos < 8) {
+                    const int c = (pos + (fb < 9 ? fb - 1 : 8)) & 15;
+                    ca = 17 + 16 * pos + c;
+                    cb = 17 + 16 * c + pos;
+                } else if (pos == 8) {
+                    ca = 0;
+                }
+                if (ca < 0) continue;
+                if (cb < 0) {
+                    So[(size_t)ca * D + r16] = sv;
+                    if (r16 == 0) zo[ca] = zv;
+                    continue;
+                }
+                float sa = sv * kInvSqrt2, sb = sa, za = zv * kInvSqrt2, zb = za;
+                if (S0c) {
+                    const float h = 0.5f * (S0c[(size_t)ca * D + r16] - S0c[(size_t)cb * D + r16]);
+                    sa += h;
+                    sb -= h;
+                }
+                if (z0c) {
+                    const float h = 0.5f * (z0c[ca] - z0c[cb]);
+                    za += h;
+                    zb -= h;
+                }
+                So[(size_t)ca * D + r16] = sa;
+                So[(size_t)cb * D + r16] = sb;
+                if (r16 == 0) {
+                    zo[ca] = za;
+                    zo[cb] = zb;
                 }
             }
     }

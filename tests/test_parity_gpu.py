@@ -264,6 +264,48 @@ def test_resume_few_segments(d, B, H):
     assert_close(host(z2), zo, zr, za, "resumed z_out")
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 2, 300), (8, 128, 200)])
+def test_taylor_resume_from_any_state(B, H, N):
+    # The Taylor kernels carry the state in a packed symmetric basis (one row per unordered
+    # pair of quadratic features).  A caller's initial state need not be symmetric in the
+    # quadratic rows: the outputs only see its symmetric part, and S_out must still equal
+    # S0 + the sum over the keys, antisymmetric part included.  The initial state here is the
+    # oracle's state after 100 random keys plus an antisymmetric perturbation of its quadratic
+    # rows (which leaves every denominator as it was).  Many segments per sequence, then one.
+    w = small("c5_taylor_causal", B=B, H=H, N=N, seed=9300 + N)
+    say(f"taylor resume from an arbitrary state B={B} H={H} N={N}")
+    x = wl.make_inputs(w)
+    pre = wl.make_inputs(w.replace(N=100, seed=9301))
+    _, S1, z1 = oracle_fwd(w.replace(N=100), pre, want_state=True)
+    rng = np.random.default_rng(9302)
+    R = rng.standard_normal((B, H, 16, 16, w.d)) * float(np.abs(S1).mean())
+    Rz = rng.standard_normal((B, H, 16, 16)) * float(np.abs(z1).mean())
+    S0 = S1.copy()
+    z0 = z1.copy()
+    S0[:, :, 17:273] += (R - R.transpose(0, 1, 3, 2, 4)).reshape(B, H, 256, w.d)
+    z0[:, :, 17:273] += (Rz - Rz.transpose(0, 1, 3, 2)).reshape(B, H, 256)
+    S0 = S0.astype(np.float32)
+    z0 = z0.astype(np.float32)
+    y, S, z = run_fwd(w, x, S0=S0, z0=z0, want_state=True)
+    yo, So, zo = oracle_fwd(w, x, S0=S0.astype(np.float64), z0=z0.astype(np.float64), want_state=True)
+    rtol, atol = wl.tolerance(w.dtype)
+    assert_close(host(y), yo, rtol, atol, "y from an arbitrary state")
+    sr, sa = state_tol(w, So)
+    assert_close(host(S), So, sr, sa, "S_out")
+    zr, za = state_tol(w, zo)
+    assert_close(host(z), zo, zr, za, "z_out")
+
+    def antisym(X, cols):
+        Q = np.asarray(X, np.float64)[:, :, 17:273].reshape(B, H, 16, 16, cols)
+        return Q - Q.transpose(0, 1, 3, 2, 4)
+
+    # the keys add a symmetric quadratic part: the antisymmetric part is S0's, to fp32 rounding
+    Sg = host(S)
+    assert_close(antisym(Sg, w.d), antisym(S0, w.d), 0.0, 1e-5 * float(np.abs(Sg).max()), "antisym S_out")
+    zg = host(z)[..., None]
+    assert_close(antisym(zg, 1), antisym(z0[..., None], 1), 0.0, 1e-5 * float(np.abs(zg).max()), "antisym z_out")
+
+
 def test_empty_sequence_returns_initial_state():
     m = hh()
     w = small("c3_llama2_causal", B=1, H=2, N=0, d=64)
