@@ -85,37 +85,48 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
     const float m9 = g < 2 ? 1.0f : 0.0f, c9 = g == 2 ? 1.0f : 0.0f;          // query side, block 9
     const float m9k = r16 < 8 ? 1.0f : 0.0f;                                    // key side, block 9
 
+    // Chunk inputs (lane = token) are fetched into registers one chunk ahead, so their memory
+    // latency overlaps the previous chunk's work: wave 0 q, k, v, wave 1 k.
+    bf16x8 pq[2], pk[2], pv[2];
+    auto fetch = [&](int tc) {
+        const bool ok = tc + lane < t_end;
+        const bf16_t *qr = p.q + base + (size_t)(tc + lane) * D;
+        const bf16_t *kr = p.k + base + (size_t)(tc + lane) * D;
+        const bf16_t *vr = p.v + base + (size_t)(tc + lane) * D;
+#pragma unroll
+        for (int hlf = 0; hlf < 2; hlf++) {
+            if (H == 0) {
+                pq[hlf] = (ok && MODE != NM_STATE) ? load8(qr + 8 * hlf) : zero_bf16x8();
+                pk[hlf] = (ok && MODE == NM_CAUSAL) ? load8(kr + 8 * hlf) : zero_bf16x8();
+                pv[hlf] = (ok && MODE != NM_READOUT) ? load8(vr + 8 * hlf) : zero_bf16x8();
+            } else {
+                pk[hlf] = (ok && MODE != NM_READOUT) ? load8(kr + 8 * hlf) : zero_bf16x8();
+            }
+        }
+    };
+    fetch(t_begin);
+
     for (int t0 = t_begin; t0 < t_end; t0 += C) {
         const int valid = min(C, t_end - t0);
-        // ---- stage the chunk (lane = token): wave 0 q and k row-major and v transposed, wave 1 k
-        // transposed (tokens contiguous)
+        // ---- stage the chunk: wave 0 q and k row-major and v transposed, wave 1 k transposed
+        // (tokens contiguous)
         {
             const int j = lane;
-            const bool ok = j < valid;
-            const bf16_t *qr = p.q + base + (size_t)(t0 + j) * D;
-            const bf16_t *kr = p.k + base + (size_t)(t0 + j) * D;
-            const bf16_t *vr = p.v + base + (size_t)(t0 + j) * D;
             if (H == 0) {
-                bf16x8 kq[2], kk[2], kv[2];
 #pragma unroll
                 for (int hlf = 0; hlf < 2; hlf++) {
-                    kq[hlf] = (ok && MODE != NM_STATE) ? load8(qr + 8 * hlf) : zero_bf16x8();
-                    kk[hlf] = (ok && MODE == NM_CAUSAL) ? load8(kr + 8 * hlf) : zero_bf16x8();
-                    kv[hlf] = (ok && MODE != NM_READOUT) ? load8(vr + 8 * hlf) : zero_bf16x8();
-                    store8(sQ + j * RR + 8 * hlf, kq[hlf]);
-                    store8(sK + j * RR + 8 * hlf, kk[hlf]);
+                    store8(sQ + j * RR + 8 * hlf, pq[hlf]);
+                    store8(sK + j * RR + 8 * hlf, pk[hlf]);
                 }
 #pragma unroll
-                for (int m = 0; m < D; m++) reinterpret_cast<__bf16 *>(sVT)[m * RT + j] = kv[m / 8][m % 8];
+                for (int m = 0; m < D; m++) reinterpret_cast<__bf16 *>(sVT)[m * RT + j] = pv[m / 8][m % 8];
             } else {
-                bf16x8 kk[2];
 #pragma unroll
-                for (int hlf = 0; hlf < 2; hlf++) kk[hlf] = (ok && MODE != NM_READOUT) ? load8(kr + 8 * hlf) : zero_bf16x8();
-#pragma unroll
-                for (int m = 0; m < D; m++) reinterpret_cast<__bf16 *>(sKT)[m * RT + j] = kk[m / 8][m % 8];
+                for (int m = 0; m < D; m++) reinterpret_cast<__bf16 *>(sKT)[m * RT + j] = pk[m / 8][m % 8];
             }
         }
         __syncthreads();
+        if (t0 + C < t_end) fetch(t0 + C);
 
         // V as a B operand, K = tokens in the order of two stacked accumulator blocks:
         // slot s < 4 -> j = 32 ks + 4 g + s, slot s >= 4 -> j = 32 ks + 16 + 4 g + s - 4.
