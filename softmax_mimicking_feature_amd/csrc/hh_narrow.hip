@@ -34,6 +34,9 @@ constexpr int FB = 10;          // 16-row feature blocks (160 rows)
 constexpr int KSF = FB / 2;     // 32-wide K steps over features
 constexpr int RR = D + 8;       // row stride of [C][D] tiles (bf16)
 constexpr int RT = C + 8;       // row stride of [D][C] tiles (bf16)
+constexpr int QFP = D + 8;      // row stride of the fp32 [C][D] query tile: 96 bytes, so the 16-byte
+                                // reads of 16 rows x 4 column runs hit distinct banks
+constexpr int KTP = C + 8;      // row stride of the fp32 [D][C] key tile: 288 bytes (32 mod 256)
 constexpr float kInvSqrt2 = 0.70710678118654752f;
 enum { NM_STATE = 0, NM_CAUSAL = 1, NM_READOUT = 2 };
 }  // namespace
@@ -54,7 +57,7 @@ __device__ __forceinline__ float packed_feature(int fb, int r, const float (&x)[
 // over the two halves meet in LDS: each wave finishes two of the four 16-token blocks.
 template <int MODE, int H>
 __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s, int lane, bf16_t *sQ, bf16_t *sK,
-                                            bf16_t *sKT, bf16_t *sVT, f32x4 *sX) {
+                                            float *sQf, float *sKTf, bf16_t *sVT, f32x4 *sX) {
     constexpr int KS0 = H == 0 ? 0 : 3, KS1 = H == 0 ? 3 : KSF;
     constexpr int NB = 2 * (KS1 - KS0);  // feature blocks held by this wave
     constexpr int FB0 = 2 * KS0;
@@ -108,21 +111,35 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
 
     for (int t0 = t_begin; t0 < t_end; t0 += C) {
         const int valid = min(C, t_end - t0);
-        // ---- stage the chunk: wave 0 q and k row-major and v transposed, wave 1 k transposed
-        // (tokens contiguous)
+        // ---- stage the chunk: wave 0 q in fp32 (feature values) and, for the intra-chunk
+        // products, q and k in bf16, and v transposed; wave 1 k transposed in fp32 (tokens
+        // contiguous).  Feature values are formed in fp32, so the tiles they come from hold fp32.
         {
             const int j = lane;
             if (H == 0) {
+                if (MODE == NM_CAUSAL) {
 #pragma unroll
-                for (int hlf = 0; hlf < 2; hlf++) {
-                    store8(sQ + j * RR + 8 * hlf, pq[hlf]);
-                    store8(sK + j * RR + 8 * hlf, pk[hlf]);
+                    for (int hlf = 0; hlf < 2; hlf++) {
+                        store8(sQ + j * RR + 8 * hlf, pq[hlf]);
+                        store8(sK + j * RR + 8 * hlf, pk[hlf]);
+                    }
                 }
+                if (MODE != NM_STATE) {
 #pragma unroll
-                for (int m = 0; m < D; m++) reinterpret_cast<__bf16 *>(sVT)[m * RT + j] = pv[m / 8][m % 8];
-            } else {
+                    for (int m4 = 0; m4 < D / 4; m4++) {
+                        f32x4 f;
 #pragma unroll
-                for (int m = 0; m < D; m++) reinterpret_cast<__bf16 *>(sKT)[m * RT + j] = pk[m / 8][m % 8];
+                        for (int r = 0; r < 4; r++) f[r] = (float)pq[m4 / 2][4 * (m4 % 2) + r];
+                        *reinterpret_cast<f32x4 *>(sQf + j * QFP + 4 * m4) = f;
+                    }
+                }
+                if (MODE != NM_READOUT) {
+#pragma unroll
+                    for (int m = 0; m < D; m++) reinterpret_cast<__bf16 *>(sVT)[m * RT + j] = pv[m / 8][m % 8];
+                }
+            } else if (MODE != NM_READOUT) {
+#pragma unroll
+                for (int m = 0; m < D; m++) sKTf[m * KTP + j] = (float)pk[m / 8][m % 8];
             }
         }
         __syncthreads();
@@ -158,9 +175,9 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                 for (int m = 0; m < 12; m++) x[m] = 0.0f;
 #pragma unroll
                 for (int m = 0; m < NRUN; m++) {
-                    const bf16x4 q4 = load4(sQ + i * RR + 4 * ((g + m) & 3));
+                    const f32x4 q4 = *reinterpret_cast<const f32x4 *>(sQf + i * QFP + 4 * ((g + m) & 3));
 #pragma unroll
-                    for (int r = 0; r < 4; r++) x[4 * m + r] = (float)q4[r];
+                    for (int r = 0; r < 4; r++) x[4 * m + r] = q4[r];
                 }
 #pragma unroll
                 for (int ks = KS0; ks < KS1; ks++) {
@@ -177,6 +194,19 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
             }
             // ---- intra-chunk part (causal, wave 1): A = 1 + s + s^2/2 on j <= i, s = k_j . q_i
             if (MODE == NM_CAUSAL && H == 1) {
+                // keys past the end of the chunk count in no row sum (their v rows are zero)
+                bf16x8 onesv[2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+                    for (int sl = 0; sl < 8; sl++) {
+                        const int j = 32 * ks + (sl < 4 ? 4 * g + sl : 16 + 4 * g + sl - 4);
+                        onesv[ks][sl] = (__bf16)(j < valid ? 1.0f : 0.0f);
+                    }
+                // causal mask of the diagonal blocks: key 4 g + r of the block against query r16
+                float cm[4];
+#pragma unroll
+                for (int r = 0; r < 4; r++) cm[r] = 4 * g + r <= r16 ? 1.0f : 0.0f;
                 bf16x8 kop[4], qop[4];
 #pragma unroll
                 for (int b = 0; b < 4; b++) {
@@ -193,10 +223,9 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                             // sdot: lane holds i = 16 ib + r16, j = 16 jb + 4 g + r
 #pragma unroll
                             for (int r = 0; r < 4; r++) {
-                                const int jl = 16 * jb + 4 * g + r, il = 16 * ib + r16;
                                 const float sv = sdot[r];
-                                const float av = fmaf(0.5f * sv, sv, 1.0f + sv);
-                                at[jb][r] = (jl <= il && jl < valid) ? av : 0.0f;
+                                const float av = fmaf(sv, fmaf(0.5f, sv, 1.0f), 1.0f);
+                                at[jb][r] = jb < ib ? av : av * cm[r];
                             }
                         } else {
                             at[jb] = zero4();
@@ -206,7 +235,7 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                     for (int ks = 0; ks <= ib / 2; ks++) {
                         const bf16x8 a = acc_pair_to_operand(at[2 * ks], at[2 * ks + 1]);
                         num[ib] = mfma_bf16(a, vop[ks], num[ib]);
-                        den[ib] = mfma_bf16(a, ones, den[ib]);
+                        den[ib] = mfma_bf16(a, onesv[ks], den[ib]);
                     }
                 }
             }
@@ -228,7 +257,9 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     const int i = 16 * ib + 4 * g + r;
-                    if (i < valid) yb[(size_t)i * D + r16] = float_to_bf16_bits((num[ib][r] + on[r]) / (den[ib][r] + od[r]));
+                    if (i < valid)
+                        yb[(size_t)i * D + r16] =
+                            float_to_bf16_bits((num[ib][r] + on[r]) * __builtin_amdgcn_rcpf(den[ib][r] + od[r]));
                 }
             }
         }
@@ -240,12 +271,12 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
             float kr[2][8], krs[2][8], okc[2][8];
 #pragma unroll
             for (int ks = 0; ks < 2; ks++) {
-                const bf16_t *kp = sKT + r16 * RT + 32 * ks + 4 * g;
-                const bf16x4 lo = load4(kp), hi = load4(kp + 16);
+                const float *kp = sKTf + r16 * KTP + 32 * ks + 4 * g;
+                const f32x4 lo = *reinterpret_cast<const f32x4 *>(kp), hi = *reinterpret_cast<const f32x4 *>(kp + 16);
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    kr[ks][r] = (float)lo[r];
-                    kr[ks][4 + r] = (float)hi[r];
+                    kr[ks][r] = lo[r];
+                    kr[ks][4 + r] = hi[r];
                     krs[ks][r] = kr[ks][r] * kInvSqrt2;
                     krs[ks][4 + r] = kr[ks][4 + r] * kInvSqrt2;
                     const int jlo = 32 * ks + 4 * g + r, jhi = jlo + 16;
@@ -267,11 +298,12 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                         for (int sl = 0; sl < 8; sl++) a[sl] = (__bf16)(kr[ks][sl] * krs[ks][sl]);
                     } else {
                         const int o = fb < 9 ? fb - 1 : 8;
-                        const bf16_t *kp = sKT + ((r16 + o) & 15) * RT + 32 * ks + 4 * g;
-                        const bf16x4 lo = load4(kp), hi = load4(kp + 16);
+                        const float *kp = sKTf + ((r16 + o) & 15) * KTP + 32 * ks + 4 * g;
+                        const f32x4 lo = *reinterpret_cast<const f32x4 *>(kp);
+                        const f32x4 hi = *reinterpret_cast<const f32x4 *>(kp + 16);
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
-                            const float plo = (float)lo[r] * kr[ks][r], phi_ = (float)hi[r] * kr[ks][4 + r];
+                            const float plo = lo[r] * kr[ks][r], phi_ = hi[r] * kr[ks][4 + r];
                             a[r] = (__bf16)(fb < 9 ? plo : fmaf(plo, m9k, okc[ks][r]));
                             a[4 + r] = (__bf16)(fb < 9 ? phi_ : fmaf(phi_, m9k, okc[ks][4 + r]));
                         }
@@ -360,16 +392,17 @@ template <int MODE>
 __global__ __launch_bounds__(128, 2) void narrow_kernel(NarrowParams p) {
     __shared__ __attribute__((aligned(16))) bf16_t sQ[C * RR];
     __shared__ __attribute__((aligned(16))) bf16_t sK[C * RR];
-    __shared__ __attribute__((aligned(16))) bf16_t sKT[D * RT];
+    __shared__ __attribute__((aligned(16))) float sQf[C * QFP];
+    __shared__ __attribute__((aligned(16))) float sKTf[D * KTP];
     __shared__ __attribute__((aligned(16))) bf16_t sVT[D * RT];
     __shared__ __attribute__((aligned(16))) f32x4 sX[2 * 2 * 2 * 64];  // read-out partials [wave][block][num, den][lane]
     const int bh = blockIdx.x / p.nseg_grid;
     const int s = blockIdx.x % p.nseg_grid;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (w == 0)
-        narrow_wave<MODE, 0>(p, bh, s, lane, sQ, sK, sKT, sVT, sX);
+        narrow_wave<MODE, 0>(p, bh, s, lane, sQ, sK, sQf, sKTf, sVT, sX);
     else
-        narrow_wave<MODE, 1>(p, bh, s, lane, sQ, sK, sKT, sVT, sX);
+        narrow_wave<MODE, 1>(p, bh, s, lane, sQ, sK, sQf, sKTf, sVT, sX);
 }
 
 hipError_t launch_narrow(int mode, const NarrowParams &p, int grid, hipStream_t st) {
