@@ -1239,7 +1239,8 @@ struct CausalWsCfg {
     static constexpr int OFF_XQ = OFF_DEN + 2 * SZ_DEN;
     static constexpr int OFF_XK = OFF_XQ + 2 * SZ_X;
     static constexpr int OFF_W = 0;
-    static constexpr int LDS_BYTES = OFF_XK + 2 * SZ_X;
+    static constexpr int OFF_SYNC = OFF_XK + 2 * SZ_X;   // producers' arrival counter
+    static constexpr int LDS_BYTES = OFF_SYNC + 16;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(D * D * 2 <= 2 * SZ_PQ + 2 * SZ_PK, "W fits in the feature tiles");
 };
@@ -1399,6 +1400,15 @@ __device__ __forceinline__ void cws_issue(const WideParams &p, const DmaLanes128
     }
 }
 
+// Barrier of the four producer waves alone, on a counter in LDS (the consumers take no part: they
+// are summing their starting state meanwhile).  Each producer's LDS writes and landed direct loads
+// are complete before it arrives; `target` counts arrivals since the counter was cleared.
+__device__ __forceinline__ void producer_barrier(unsigned int *cnt, unsigned int target, int lane) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) __builtin_amdgcn_s_sleep(1);
+}
+
 __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     using S = CausalWsCfg;
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
@@ -1421,11 +1431,14 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     auto a_buf = [&](int b) { return reinterpret_cast<bf16_t *>(smem + S::OFF_A + b * S::SZ_A); };
     auto den_buf = [&](int b) { return reinterpret_cast<float *>(smem + S::OFF_DEN + b * S::SZ_DEN); };
 
-    // Consumer state: value columns value_col<2>(pv, vb, c) of S for all 256 features, z rows of
-    // feature blocks 4 pv .. 4 pv + 3 (declared here, used by the consumer waves only).
-    f32x4 sacc[16][2];
-    f32x4 zacc[4];
+    unsigned int *psync = reinterpret_cast<unsigned int *>(smem + S::OFF_SYNC);
+    if (tid == 0) *psync = 0u;
+    __syncthreads();
+    // The two roles run separate streams with the same barriers: one before the first chunk, then
+    // one per chunk.
     if (w < 4) {
+        bf16x8 wA[4][4];  // W operands, directions 64 (pv >> 1) .. + 63
+        float bl2[4][4];
         // Producers issue every staging load of the prologue (each moves the 1 KB blocks of waves w
         // and w + 4 of the eight-wave layout), so that the consumers' load queues hold only their
         // own prefix loads below: loads retire in order per wave, and a consumer waiting for a prefix
@@ -1444,7 +1457,47 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
             }
             stage_w_dma128(p.W, h, vw, lane, smem + S::OFF_W);
         }
-    } else {
+        // Then, while the consumers sum their starting state, the W operands and the feature maps of
+        // the first chunk (W shares space with the feature tiles: every producer has read it before
+        // any feature is written).
+        producer_barrier(psync, 4, lane);
+        // the two 32-direction groups 2 (pv >> 1), 2 (pv >> 1) + 1
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+            bf16x8 w2[2][4];
+            float b2[2][4];
+            load_w_operands<128>(smem + S::OFF_W, 2 * (pv >> 1) + hh, g, r16, w2);
+            load_bias<128>(p.b, h, 2 * (pv >> 1) + hh, g, b2);
+#pragma unroll
+            for (int mb = 0; mb < 2; mb++) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) wA[2 * hh + mb][ks] = w2[mb][ks];
+#pragma unroll
+                for (int r = 0; r < 4; r++) bl2[2 * hh + mb][r] = b2[mb][r];
+            }
+        }
+        producer_barrier(psync, 8, lane);
+        if (n > 0)
+            cws_features_any(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, pv, g, r16, pq_buf(0), pk_buf(0));
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int c = 0; c < n; c++) {
+            cws_issue(p, dl, base, t_begin, t_end, c, n, w, smem);
+            const int b2 = c & 1;
+            cws_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), pv, g, r16);
+            if (c + 1 < n)
+                cws_features_any(smem + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, smem + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
+                             valid_of(c + 1), wA, bl2, pv, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1));
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        return;
+    }
+    // Consumer state: value columns value_col<2>(pv, vb, c) of S for all 256 features, z rows of
+    // feature blocks 4 pv .. 4 pv + 3.
+    f32x4 sacc[16][2];
+    f32x4 zacc[4];
+    {
         // Starting state: the caller's S0, plus the earlier segments' contribution.  slot_mode 1:
         // slot s holds their exclusive prefix; slot_mode 3: slots 0 .. s - 1 hold their aggregates
         // (written by the segment-state pass just before, by workgroups of the same XCD), summed
@@ -1476,7 +1529,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
             const size_t sl = (size_t)bh * p.slot_bh_stride + t;
             const float *zs = p.z_slots + sl * S::DP;
             bf16x8 slot_raw[2][8];
-            float zslot[4][4];
+            f32x4 zslot[4];
 #pragma unroll
             for (int fa = 0; fa < 2; fa++) {
                 const bf16x8 *img =
@@ -1485,9 +1538,8 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
                 for (int j = 0; j < 8; j++) slot_raw[fa][j] = img[j * 64];
             }
 #pragma unroll
-            for (int zb = 0; zb < 4; zb++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) zslot[zb][r] = zs[16 * (4 * pv + zb) + 4 * g + r];
+            for (int zb = 0; zb < 4; zb++) zslot[zb] = *reinterpret_cast<const f32x4 *>(zs + 16 * (4 * pv + zb) + 4 * g);
+            __builtin_amdgcn_sched_barrier(0);  // all of the slot's loads in flight before the first sum
 #pragma unroll
             for (int fa = 0; fa < 2; fa++)
 #pragma unroll
@@ -1506,44 +1558,6 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // The two roles run separate loops with the same barriers, one per chunk.
-    if (w < 4) {
-        // directions 64 (pv >> 1) .. + 63: the two 32-direction groups 2 (pv >> 1), 2 (pv >> 1) + 1
-        bf16x8 wA[4][4];
-        float bl2[4][4];
-#pragma unroll
-        for (int hh = 0; hh < 2; hh++) {
-            bf16x8 w2[2][4];
-            float b2[2][4];
-            load_w_operands<128>(smem + S::OFF_W, 2 * (pv >> 1) + hh, g, r16, w2);
-            load_bias<128>(p.b, h, 2 * (pv >> 1) + hh, g, b2);
-#pragma unroll
-            for (int mb = 0; mb < 2; mb++) {
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) wA[2 * hh + mb][ks] = w2[mb][ks];
-#pragma unroll
-                for (int r = 0; r < 4; r++) bl2[2 * hh + mb][r] = b2[mb][r];
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // W shares space with the feature tiles
-        if (n > 0)
-            cws_features_any(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, pv, g, r16, pq_buf(0), pk_buf(0));
-        __syncthreads();
-        for (int c = 0; c < n; c++) {
-            cws_issue(p, dl, base, t_begin, t_end, c, n, w, smem);
-            const int b2 = c & 1;
-            cws_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), pv, g, r16);
-            if (c + 1 < n)
-                cws_features_any(smem + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, smem + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
-                             valid_of(c + 1), wA, bl2, pv, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1));
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        }
-        return;
-    }
-
-    // consumer
     f32x4 numT[2][2];
 #pragma unroll
     for (int ib = 0; ib < 2; ib++) numT[ib][0] = numT[ib][1] = zero4();
@@ -1552,8 +1566,6 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     const int lane_v = r0 * S::D + 8 * v_pos(r0, 4 * pv + (r16 & 3));
     const bf16x8 ones = ones_bf16x8();
     bf16_t *ybase = p.y + base;
-    __syncthreads();  // (producers: W read)
-    __syncthreads();  // (producers: first chunk's features)
 
     for (int c = 0; c < n; c++) {
         cws_issue(p, dl, base, t_begin, t_end, c, n, w, smem);
