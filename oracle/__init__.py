@@ -65,8 +65,9 @@ def _load():
         lib.hho_decode_step.argtypes = [I, I, L, L, D, D, D, D, D, D, D, D, I]
         lib.hho_quadratic.argtypes = [I, I, L, L, L, I, D, D, D, D, D, L, D, D, I]
         lib.hho_featuremap.argtypes = [I, I, L, L, L, D, D, D, D, I]
+        lib.hho_distill.argtypes = [I, I, L, L, L, D, D, D, D, L, D, D, I]
         for f in (lib.hho_causal, lib.hho_bidir, lib.hho_decode_step, lib.hho_quadratic,
-                  lib.hho_featuremap):
+                  lib.hho_featuremap, lib.hho_distill):
             f.restype = None
         _lib = lib
     return _lib
@@ -194,3 +195,20 @@ def prefix_state(map_: int, k, v, W=None, b=None, nthreads: Optional[int] = None
         S[bi] = np.matmul(phi.transpose(0, 2, 1), _f64(v[bi]))
         z[bi] = phi.sum(axis=1)
     return S, z
+
+
+def distill_loss(map_: int, q, k, W=None, b=None, rows=None, nthreads: Optional[int] = None) -> np.ndarray:
+    """Attention-weight distillation loss (Eq. 4 of the walkthrough's section 3.4) per query:
+    q, k [B,H,N,d] -> L [B,H,N] (float64), or [B,H,len(rows)] for the listed query rows.
+
+    L_i = -sum_{j<=i} p_ij log(a_ij / sum_{m<=i} a_im), with p_ij the causal softmax of
+    q_i.k_j / sqrt(d) and a_ij = phi(q_i).phi(k_j)."""
+    q, k = _f64(q), _f64(k)
+    B, H, N, d = q.shape
+    W, b = _params(map_, W, b, H, d)
+    r = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    nr = N if r is None else len(r)
+    out = np.empty((B, H, nr), np.float64)
+    _load().hho_distill(map_, d, B, H, N, _ptr(q), _ptr(k), _ptr(W), _ptr(b), 0 if r is None else nr,
+                        _ptr(r), _ptr(out), nthreads or default_threads())
+    return out

@@ -20,6 +20,11 @@
  *     (section 3.4, "The Taylor Exponential as a Bridge Result").
  *   - Bidirectional (encoder) attention: the same sums taken over every key
  *     (paperlayer section 1: bidirectional BERT conversions).
+ *   - Attention-weight distillation loss, Eq. 4 (section 3.4, "The Attention
+ *     Weight Distillation Loss"): for query i, the cross-entropy between the
+ *     causal softmax weights of q_i.k_j / sqrt(d) over j <= i (the raw q, k, not
+ *     their features) and the linear weights phi(q_i).phi(k_j) normalised over
+ *     the same keys.
  *
  * Readings taken where the pages are silent or garbled:
  *   - W is stored [d_out][d_in] row-major and u = W x + b (the pages call w_l
@@ -177,6 +182,44 @@ static void quadratic_rows_one(int map, int d, long N, int causal, const double 
     free(g); free(f); free(num);
 }
 
+/* Distillation loss of the listed query rows (all rows when rows == NULL), directly from Eq. 4:
+ * p_ij = exp(q_i.k_j / sqrt(d)) / sum_{m<=i} exp(q_i.k_m / sqrt(d)),
+ * a_ij = phi(q_i).phi(k_j),
+ * L_i = -sum_{j<=i} p_ij log(a_ij / sum_{m<=i} a_im).
+ * The softmax is evaluated with its maximum logit subtracted (the same weights). */
+static void distill_rows_one(int map, int d, long N, const double *q, const double *k, const double *W,
+                             const double *b, long nrows, const long *rows, double *loss) {
+    int dp = hho_feature_dim(map, d);
+    double *g = malloc(sizeof(double) * dp);
+    double *f = malloc(sizeof(double) * dp);
+    double *logit = malloc(sizeof(double) * (N > 0 ? N : 1));
+    double *a = malloc(sizeof(double) * (N > 0 ? N : 1));
+    const double scale = 1.0 / sqrt((double)d);
+    long count = rows ? nrows : N;
+    for (long r = 0; r < count; r++) {
+        long i = rows ? rows[r] : r;
+        phi_one(map, d, q + i * d, W, b, g);
+        double mx = -INFINITY, asum = 0.0;
+        for (long j = 0; j <= i; j++) {
+            double s = 0.0;
+            for (int c = 0; c < d; c++) s += q[i * d + c] * k[j * d + c];
+            logit[j] = s * scale;
+            if (logit[j] > mx) mx = logit[j];
+            phi_one(map, d, k + j * d, W, b, f);
+            double aij = 0.0;
+            for (int t = 0; t < dp; t++) aij += g[t] * f[t];
+            a[j] = aij;
+            asum += aij;
+        }
+        double psum = 0.0;
+        for (long j = 0; j <= i; j++) psum += exp(logit[j] - mx);
+        double L = 0.0;
+        for (long j = 0; j <= i; j++) L -= (exp(logit[j] - mx) / psum) * log(a[j] / asum);
+        loss[r] = L;
+    }
+    free(g); free(f); free(logit); free(a);
+}
+
 /* One decode step from (S, z), in place: S += phi(k) v^T; z += phi(k); y = phi(q)^T S / phi(q)^T z. */
 static void decode_one(int map, int d, const double *q, const double *k, const double *v,
                        const double *W, const double *b, double *S, double *z, double *y) {
@@ -201,7 +244,7 @@ static void decode_one(int map, int d, const double *q, const double *k, const d
 /* ---- batched entry points: B*H independent sequences, threads over them ---- */
 
 typedef struct {
-    int op;        /* 0 causal, 1 bidirectional, 2 decode, 3 quadratic rows, 4 featuremap */
+    int op;        /* 0 causal, 1 bidirectional, 2 decode, 3 quadratic rows, 4 featuremap, 5 distillation loss */
     int map, d, H, causal;
     long BH, N;
     const double *q, *k, *v, *W, *b, *S0, *z0;
@@ -239,6 +282,10 @@ static void run_pair(job_t *j, long p) {
         break;
     case 4:
         hho_featuremap_head(j->map, d, j->N, j->q + p * seq, W, b, j->y + (size_t)p * j->N * dp);
+        break;
+    case 5:
+        distill_rows_one(j->map, d, j->N, j->q + p * seq, j->k + p * seq, W, b, j->nrows, j->rows,
+                         j->y + (size_t)p * (j->rows ? j->nrows : j->N));
         break;
     }
 }
@@ -322,5 +369,16 @@ void hho_featuremap(int map, int d, long B, long H, long N, const double *x, con
     memset(&j, 0, sizeof j);
     j.op = 4; j.map = map; j.d = d; j.H = (int)H; j.BH = B * H; j.N = N;
     j.q = x; j.W = W; j.b = b; j.y = phi;
+    run_job(&j, nthreads);
+}
+
+/* Distillation loss (Eq. 4) of q, k [B*H][N][d] -> loss [B*H][nrows or N] for the listed query rows
+ * (rows == NULL: all rows). */
+void hho_distill(int map, int d, long B, long H, long N, const double *q, const double *k, const double *W,
+                 const double *b, long nrows, const long *rows, double *loss, int nthreads) {
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.op = 5; j.map = map; j.d = d; j.H = (int)H; j.BH = B * H; j.N = N;
+    j.q = q; j.k = k; j.W = W; j.b = b; j.y = loss; j.nrows = nrows; j.rows = rows;
     run_job(&j, nthreads);
 }

@@ -17,7 +17,12 @@ Each pin is chosen so that a plausible slip in the oracle fails at least one:
     Taylor worked examples;
   - S transposed or a wrong index in the read-out: quadratic form vs running
     sums, convex-hull bound;
-  - state not carried or double counted: split-resume, decode chain.
+  - state not carried or double counted: split-resume, decode chain;
+  - distillation loss (Eq. 4, section 3.4 "The Attention Weight Distillation
+    Loss"): a key beyond the causal boundary or a wrong normaliser (first-query
+    loss, uniform cases), a missing 1/sqrt(d) or a misplaced softmax (two-key
+    logistic case), a loss below the target's entropy (Gibbs inequality), and
+    the Taylor kernel's agreement with exp at small scores.
 """
 
 import json
@@ -276,3 +281,96 @@ def test_prefix_state_equals_running_sums(map_):
     S2, z2 = oracle.prefix_state(map_, k, v, W, b)
     np.testing.assert_allclose(S2, S, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(z2, z, rtol=1e-12)
+
+
+# ---- attention-weight distillation loss (Eq. 4 of the walkthrough's section 3.4) ----
+
+def _softmax_rows(logits):
+    from scipy.special import softmax
+    return softmax(logits, axis=-1)
+
+
+@pytest.mark.parametrize("map_,d", [(HH, 8), (TAY, 4)])
+def test_distill_first_query_loss_is_zero(map_, d):
+    # one key: both distributions put all weight on it
+    rng = np.random.default_rng(61)
+    q = rng.standard_normal((2, 3, 20, d))
+    k = rng.standard_normal((2, 3, 20, d))
+    W = rng.standard_normal((3, d, d)) / math.sqrt(d)
+    L = oracle.distill_loss(map_, q, k, W, None)
+    assert np.all(np.abs(L[:, :, 0]) < 1e-12)
+
+
+def test_distill_uniform_cases_give_log_count():
+    # q = 0 makes the softmax uniform; W = b = 0 (Hedgehog) or q = 0 (Taylor: phi(0).phi(k) = 1)
+    # makes the linear weights uniform too: L_i = log(i + 1)
+    rng = np.random.default_rng(62)
+    N, d = 40, 8
+    k = rng.standard_normal((1, 2, N, d))
+    q0 = np.zeros((1, 2, N, d))
+    want = np.log(np.arange(1, N + 1))
+    L = oracle.distill_loss(HH, q0, k, np.zeros((2, d, d)), np.zeros((2, d)))
+    assert np.allclose(L[0, 0], want, rtol=0, atol=1e-12) and np.allclose(L[0, 1], want, rtol=0, atol=1e-12)
+    L = oracle.distill_loss(TAY, q0, k)
+    assert np.allclose(L[0, 0], want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("map_,d", [(HH, 8), (TAY, 4)])
+def test_distill_gibbs_inequality(map_, d):
+    # a cross-entropy is at least the entropy of its target distribution
+    rng = np.random.default_rng(63)
+    N = 30
+    q = rng.standard_normal((1, 1, N, d))
+    k = rng.standard_normal((1, 1, N, d))
+    W = rng.standard_normal((1, d, d)) / math.sqrt(d)
+    L = oracle.distill_loss(map_, q, k, W, None)[0, 0]
+    for i in range(N):
+        p = _softmax_rows(q[0, 0, i] @ k[0, 0, : i + 1].T / math.sqrt(d))
+        H = -np.sum(p * np.log(p))
+        assert L[i] >= H - 1e-12
+
+
+def test_distill_taylor_small_scores_match_softmax():
+    # d = 1: the Taylor kernel 1 + s + s^2/2 equals exp(s) up to s^3/6, and the softmax logits are
+    # s / sqrt(1) = s, so the predicted weights are the softmax weights up to that remainder and the
+    # loss is the softmax entropy up to a few times max|s|^3 / 6
+    rng = np.random.default_rng(64)
+    N = 25
+    q = rng.uniform(-0.3, 0.3, (1, 1, N, 1))
+    k = rng.uniform(-0.3, 0.3, (1, 1, N, 1))
+    L = oracle.distill_loss(TAY, q, k)[0, 0]
+    smax = float(np.max(np.abs(q))) * float(np.max(np.abs(k)))
+    for i in range(N):
+        p = _softmax_rows(q[0, 0, i] @ k[0, 0, : i + 1].T)
+        H = -np.sum(p * np.log(p))
+        assert abs(L[i] - H) <= 4 * smax ** 3 / 6 + 1e-12
+
+
+def test_distill_two_keys_logistic():
+    # with two keys the softmax is the logistic function of the logit difference; the linear
+    # weights come from the (separately pinned) feature map
+    from scipy.special import expit
+    rng = np.random.default_rng(65)
+    d = 8
+    q = rng.standard_normal((1, 1, 2, d))
+    k = rng.standard_normal((1, 1, 2, d))
+    W = rng.standard_normal((1, d, d)) / math.sqrt(d)
+    b = rng.standard_normal((1, d)) * 0.1
+    L = oracle.distill_loss(HH, q, k, W, b)[0, 0, 1]
+    fq = oracle.featuremap(HH, q, W, b)[0, 0, 1]
+    fk = oracle.featuremap(HH, k, W, b)[0, 0]
+    a = fk @ fq
+    p1 = expit((q[0, 0, 1] @ k[0, 0, 1] - q[0, 0, 1] @ k[0, 0, 0]) / math.sqrt(d))
+    want = -((1 - p1) * math.log(a[0] / a.sum()) + p1 * math.log(a[1] / a.sum()))
+    assert abs(L - want) < 1e-12
+
+
+def test_distill_rows_subset_matches_all_rows():
+    rng = np.random.default_rng(66)
+    q = rng.standard_normal((2, 2, 50, 8))
+    k = rng.standard_normal((2, 2, 50, 8))
+    W = rng.standard_normal((2, 8, 8)) / math.sqrt(8)
+    full = oracle.distill_loss(HH, q, k, W, None)
+    rows = [49, 0, 17, 33]
+    part = oracle.distill_loss(HH, q, k, W, None, rows=rows)
+    assert np.array_equal(part, full[:, :, rows])
