@@ -61,6 +61,21 @@ def algorithmic_counts(w: wl.Workload):
     return float(flops), float(byts)
 
 
+def distill_counts(w: wl.Workload):
+    """Algorithmic FLOPs and HBM bytes of one distillation loss (Eq. 4).
+
+    Per (query, key) pair with j <= i: the logit q.k (2d) and the linear weight phi(q).phi(k)
+    (2d'); per token-head the feature maps of q and k (4d^2).  Bytes: read q and k, write one fp32
+    loss per query, plus W and b once per head."""
+    d, dp = w.d, wl.feature_dim(w.map, w.d)
+    th = w.B * w.H * w.N
+    pairs = w.B * w.H * w.N * (w.N + 1) // 2
+    flops = pairs * (2 * d + 2 * dp) + th * 4 * d * d
+    eb = wl.bytes_per_elem(w.dtype)
+    byts = eb * 2 * th * d + 4 * th + eb * w.H * (d * d + d)
+    return float(flops), float(byts)
+
+
 def decode_counts(w: wl.Workload):
     d, dp = w.d, wl.feature_dim(w.map, w.d)
     bh = w.B * w.H
@@ -140,6 +155,7 @@ def main():
     w = wl.CONFIGS[args.workload]
     tdt = torch.bfloat16 if w.dtype == wl.DT_BF16 else torch.float32
     decode = args.workload.endswith("decode")
+    distill = args.workload.endswith("distill")
 
     # ---- input sets (set 0 from the seeded host generator, the others drawn on the GPU
     #      with the same distributions)
@@ -190,6 +206,16 @@ def main():
             hh.hh_linattn_decode_step(s["q"], s["k"], s["v"], W, b, S, z, map=w.map, out=outs[i % N_SETS],
                                       stream=st)
         flops, byts = decode_counts(w)
+    elif distill:
+        need = hh.hh_distill_loss_workspace(w.map, w.dtype, w.B, w.H, w.N, w.d)
+        wss = [torch.empty((max(need, 16),), dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
+        outs = [torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev) for _ in range(N_SETS)]
+
+        def step(i, st):
+            s = sets[i % N_SETS]
+            hh.hh_distill_loss(s["q"], s["k"], W, b, map=w.map, out=outs[i % N_SETS], workspace=wss[i % N_SETS],
+                               stream=st)
+        flops, byts = distill_counts(w)
     else:
         need = hh.hh_linattn_fwd_workspace(w.map, w.dtype, w.causal, w.B, w.H, w.N, w.d)
         wss = [torch.empty((max(need, 16),), dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
@@ -274,6 +300,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(ach_tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None}
     if decode:
         roof["kernel"] = "hh_linattn_decode_step (decode_kernel)"
+    elif distill:
+        roof["kernel"] = "hh_distill_loss: every kernel of one call (feature maps of q and k, then distill_kernel)"
     elif w.map == wl.MAP_TAYLOR2:
         roof["kernel"] = ("hh_linattn_fwd: every kernel of one call (segment aggregates, exclusive prefix "
                           "over segments, chunked causal pass)")
@@ -291,7 +319,25 @@ def main():
     roof["mfma_frac_of_bf16_peak"] = round(ach_tflops / PEAK_MFMA_BF16_TFLOPS, 4)
 
     cpu = None
-    if not args.no_cpu_baseline and not decode:
+    if not args.no_cpu_baseline and distill:
+        import oracle
+        nthr = oracle.default_threads()
+        xw = host0
+        # query rows spread evenly over the sequence (their mean cost is the full loss's), in rounds
+        # of 16 rows per head until about 10 s of wall time
+        rows_done, tc, rnd = 0, 0.0, 0
+        while rnd < 30 and (tc < 10.0 or rnd == 0):
+            rows = [int((w.N - 1) * (j + 0.5 * (rnd % 2)) / 16) for j in range(16)]
+            t0 = time.perf_counter()
+            oracle.distill_loss(w.map, xw["q"], xw["k"], xw["W"], xw["b"], rows=rows, nthreads=nthr)
+            tc += time.perf_counter() - t0
+            rows_done += len(rows) * w.B
+            rnd += 1
+        cpu = {"value": round(rows_done / tc, 1), "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+               "sample": f"{rnd} rounds of 16 query rows per head (all {w.H} heads, rows spread over the sequence) "
+                         f"of {w.name} (B{w.B} H{w.H} N{w.N} d{w.d}) by the fp64 oracle, {tc:.2f} s wall on "
+                         f"{nthr} threads"}
+    elif not args.no_cpu_baseline and not decode:
         import oracle
         nthr = oracle.default_threads()
         xw = host0
@@ -312,6 +358,7 @@ def main():
     out = {
         "metric": (METRIC if w.name == "c3_llama2_causal" else
                    "decode step tokens/s (one token per sequence)" if decode else
+                   "distillation loss (Eq. 4) query tokens/s at Llama-2-7B heads" if distill else
                    f"{'causal' if w.causal else 'bidirectional'} linear-attn fwd tokens/s (\u03c6 incl.), {w.name}"),
         "value": round(value, 1),
         "unit": "tokens/s",

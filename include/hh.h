@@ -118,6 +118,27 @@ hh_status_t hh_linattn_decode_step(int map, int dtype, int B, int H, int d,
                                    const void *W, const void *b,
                                    float *S, float *z, void *y, void *stream);
 
+/* Bytes of workspace hh_distill_loss needs (the features of q and k for the Hedgehog map,
+ * 0 for the Taylor map).  Returns 0 as well for invalid arguments. */
+size_t hh_distill_loss_workspace(int map, int dtype, int B, int H, int N, int d);
+
+/* Attention-weight distillation loss of Eq. 4 (paper-graph-ui walkthrough, section 3.4, "The
+ * Attention Weight Distillation Loss"), per query: for each (b, h) and i,
+ *     p_ij = exp(q_i.k_j / sqrt(d)) / sum_{m<=i} exp(q_i.k_m / sqrt(d))      (j <= i)
+ *     a_ij = phi(q_i).phi(k_j)
+ *     loss_i = -sum_{j<=i} p_ij log(a_ij / sum_{m<=i} a_im)
+ * the cross-entropy between the causal softmax weights of the raw q, k and the linear-attention
+ * weights of their features.  The total loss of the pages is the sum of loss over b, h, i.
+ *   q, k [B][H][N][d] (bf16; fp32 inputs return HH_EUNSUPPORTED), W [H][d][d], b [H][d] or
+ *       NULL as in hh_linattn_fwd (Taylor map: ignored, d = 16).
+ *   loss [B][H][N] fp32 output; must not overlap q or k.
+ *   workspace: device scratch of at least hh_distill_loss_workspace() bytes (may be NULL when
+ *       that is 0); must not overlap the other arguments.
+ * The features enter the weights rounded to bf16, as in the forward pass. */
+hh_status_t hh_distill_loss(int map, int dtype, int B, int H, int N, int d,
+                            const void *q, const void *k, const void *W, const void *b,
+                            float *loss, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *hh_status_str(int status);
 

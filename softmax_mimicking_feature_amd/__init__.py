@@ -10,6 +10,7 @@ raises.
     y, S, z = hh_linattn_fwd(q, k, v, W, b, want_state=True)   # + final fp32 state
     y = hh_linattn_decode_step(q1, k1, v1, W, b, S, z)         # S, z updated in place
     phi = hh_featuremap(x, W, b)                               # [B,H,N,d']
+    loss = hh_distill_loss(q, k, W, b)                         # [B,H,N] per-query Eq. 4 loss
 """
 
 from __future__ import annotations
@@ -21,7 +22,7 @@ from ._lib import (HH_BF16, HH_EHIP, HH_EINVAL, HH_EUNSUPPORTED, HH_EWORKSPACE, 
                    HH_MAP_TAYLOR2, HH_OK, LibraryMissing)
 
 __all__ = ["hh_feature_dim", "hh_featuremap", "hh_linattn_fwd_workspace", "hh_linattn_fwd",
-           "hh_linattn_decode_step", "hh_status_str", "hh_last_error", "hh_abi_version", "HHError",
+           "hh_linattn_decode_step", "hh_distill_loss_workspace", "hh_distill_loss", "hh_status_str", "hh_last_error", "hh_abi_version", "HHError",
            "LibraryMissing", "HH_F32", "HH_BF16", "HH_MAP_HEDGEHOG", "HH_MAP_TAYLOR2", "HH_OK", "HH_EINVAL",
            "HH_EUNSUPPORTED", "HH_EWORKSPACE", "HH_EHIP"]
 
@@ -178,4 +179,35 @@ def hh_linattn_decode_step(q, k, v, W, b, S, z, *, map: int = HH_MAP_HEDGEHOG, o
     _dev(out, "out", q.dtype)
     _check(lib.hh_linattn_decode_step(map, dt, B, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(b), _ptr(S),
                                       _ptr(z), _ptr(out), _stream(stream)))
+    return out
+
+
+def hh_distill_loss_workspace(map: int, dtype: int, B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.load().hh_distill_loss_workspace(map, dtype, B, H, N, d))
+
+
+def hh_distill_loss(q, k, W=None, b=None, *, map: int = HH_MAP_HEDGEHOG, out=None, workspace=None, stream=None):
+    """Attention-weight distillation loss (Eq. 4) per query.  q, k: [B,H,N,d] bf16 -> loss [B,H,N] fp32."""
+    lib = _lib.load()
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k")):
+        _dev(t, nm, q.dtype)
+    B, H, N, d = q.shape
+    if k.shape != q.shape:
+        raise ValueError("q and k must have the same shape [B,H,N,d]")
+    dt = _dtype_code(q)
+    if map == HH_MAP_HEDGEHOG:
+        _dev(W, "W", q.dtype)
+        _dev(b, "b", q.dtype)
+    else:
+        W = b = None
+    if out is None:
+        out = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32)
+    need = lib.hh_distill_loss_workspace(map, dt, B, H, N, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.hh_distill_loss(map, dt, B, H, N, d, _ptr(q), _ptr(k), _ptr(W), _ptr(b), _ptr(out), _ptr(workspace),
+                               ws_bytes, _stream(stream)))
     return out

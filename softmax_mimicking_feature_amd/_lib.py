@@ -14,7 +14,8 @@ HH_MAP_HEDGEHOG, HH_MAP_TAYLOR2 = 0, 1
 
 # Every function declared in include/hh.h.
 EXPORTS = ("hh_abi_version", "hh_feature_dim", "hh_featuremap", "hh_linattn_fwd_workspace",
-           "hh_linattn_fwd", "hh_linattn_decode_step", "hh_status_str", "hh_last_error")
+           "hh_linattn_fwd", "hh_linattn_decode_step", "hh_distill_loss_workspace", "hh_distill_loss",
+           "hh_status_str", "hh_last_error")
 
 
 class LibraryMissing(RuntimeError):
@@ -53,6 +54,10 @@ def load() -> ctypes.CDLL:
     lib.hh_linattn_fwd.restype = I
     lib.hh_linattn_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P]
     lib.hh_linattn_decode_step.restype = I
+    lib.hh_distill_loss_workspace.argtypes = [I, I, I, I, I, I]
+    lib.hh_distill_loss_workspace.restype = Z
+    lib.hh_distill_loss.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, Z, P]
+    lib.hh_distill_loss.restype = I
     lib.hh_status_str.argtypes = [I]
     lib.hh_status_str.restype = ctypes.c_char_p
     lib.hh_last_error.argtypes = []

@@ -359,6 +359,63 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
     return ok();
 }
 
+size_t hh_distill_loss_workspace(int map, int dtype, int B, int H, int N, int d) {
+    if (check_common(map, dtype, B, H, N, d) != HH_OK || dtype != HH_BF16 || map != HH_MAP_HEDGEHOG) return 0;
+    return 2 * (size_t)B * H * N * 2 * d * sizeof(uint16_t);
+}
+
+hh_status_t hh_distill_loss(int map, int dtype, int B, int H, int N, int d, const void *q, const void *k,
+                            const void *W, const void *b, float *loss, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    hh_status_t st = check_common(map, dtype, B, H, N, d);
+    if (st != HH_OK) return st;
+    if (dtype != HH_BF16) return fail(HH_EUNSUPPORTED, "distillation loss: bf16 inputs only");
+    const bool hog = map == HH_MAP_HEDGEHOG;
+    const bool need = N > 0;
+    if ((st = check_ptr(q, "q", need)) != HH_OK) return st;
+    if ((st = check_ptr(k, "k", need)) != HH_OK) return st;
+    if ((st = check_ptr(loss, "loss", need)) != HH_OK) return st;
+    if (hog) {
+        if ((st = check_ptr(W, "W", need)) != HH_OK) return st;
+        if ((st = check_ptr(b, "b", false)) != HH_OK) return st;
+    }
+    const long BH = (long)B * H;
+    const size_t nio = (size_t)BH * N * d * sizeof(uint16_t), nl = (size_t)BH * N * sizeof(float);
+    if (overlap(loss, nl, q, nio) || overlap(loss, nl, k, nio)) return fail(HH_EINVAL, "loss overlaps q or k");
+    const size_t need_ws = hh_distill_loss_workspace(map, dtype, B, H, N, d);
+    if (need_ws > 0) {
+        if (!workspace) return fail(HH_EWORKSPACE, "workspace of %zu bytes required, got NULL", need_ws);
+        if (workspace_bytes < need_ws)
+            return fail(HH_EWORKSPACE, "workspace of %zu bytes required, got %zu", need_ws, workspace_bytes);
+        if (!aligned16(workspace)) return fail(HH_EINVAL, "workspace is not 16-byte aligned");
+        if (overlap(workspace, need_ws, q, nio) || overlap(workspace, need_ws, k, nio) ||
+            overlap(workspace, need_ws, loss, nl))
+            return fail(HH_EINVAL, "workspace overlaps an input or output");
+    }
+    if (N == 0) return ok();
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    clear_stale_hip_error();
+    hipError_t e;
+    hh::DistillParams dp;
+    dp.q = (const hh::bf16_t *)q; dp.k = (const hh::bf16_t *)k;
+    dp.phi_q = dp.phi_k = nullptr;
+    dp.loss = loss; dp.N = N;
+    if (hog) {
+        hh::bf16_t *fq = reinterpret_cast<hh::bf16_t *>(workspace);
+        hh::bf16_t *fk = fq + (size_t)BH * N * 2 * d;
+        e = hh::launch_featuremap_hedgehog_bf16(d, (const hh::bf16_t *)q, (const hh::bf16_t *)W,
+                                                (const hh::bf16_t *)b, fq, (int)BH, H, N, s);
+        if (e != hipSuccess) return hip_fail(e, "feature map launch");
+        e = hh::launch_featuremap_hedgehog_bf16(d, (const hh::bf16_t *)k, (const hh::bf16_t *)W,
+                                                (const hh::bf16_t *)b, fk, (int)BH, H, N, s);
+        if (e != hipSuccess) return hip_fail(e, "feature map launch");
+        dp.phi_q = fq; dp.phi_k = fk;
+    }
+    e = hh::launch_distill(map, d, dp, (int)BH, s);
+    if (e != hipSuccess) return hip_fail(e, "distillation loss launch");
+    return ok();
+}
+
 hh_status_t hh_linattn_decode_step(int map, int dtype, int B, int H, int d, const void *q, const void *k,
                                    const void *v, const void *W, const void *b, float *S, float *z, void *y,
                                    void *stream) {

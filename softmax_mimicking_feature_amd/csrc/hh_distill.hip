@@ -1,0 +1,207 @@
+// hh_distill.hip -- fused attention-weight distillation loss on the CDNA4 matrix cores.
+//
+// The loss of Eq. 4 (paper-graph-ui walkthrough of "The Hedgehog & the Porcupine", section 3.4,
+// "The Attention Weight Distillation Loss"): for query i of one (batch, head),
+//     p_ij = softmax over j <= i of q_i.k_j / sqrt(d)          (the raw q and k)
+//     a_ij = phi(q_i).phi(k_j)                                  (the feature map's kernel)
+//     L_i  = -sum_{j<=i} p_ij log(a_ij / sum_{m<=i} a_im)
+// Since the p_ij sum to 1, L_i = -(sum_j e_ij log a_ij) / (sum_j e_ij) + log(sum_j a_ij) with
+// e_ij = exp(q_i.k_j / sqrt(d) - m_i) for any m_i; the kernel keeps, per query, a running maximum
+// m_i of the logits and the three sums, rescaling two of them when m_i grows (the usual one-pass
+// softmax), so the n^2 weights are never stored.
+//
+// One workgroup owns 64 queries of one (b,h) (16 per wave) and walks the key tiles of 64 up to
+// its diagonal.  Per 16-key block, the scores come from the matrix cores with the keys as rows
+// and the queries as columns, so a lane holds one query and four keys: the per-query reductions
+// run inside the lane and across the four lane groups (two shuffles).
+//   Hedgehog: a = phi(q).phi(k) with the 2d features of q and k precomputed by the feature-map
+//             kernel (bf16, as the forward pass uses them).
+//   Taylor:   a = 1 + s + s^2/2 with s = q.k, the map's closed form (section 3.4, "The Taylor
+//             Exponential as a Bridge Result"), from the same product as the logits.
+// The next key tile is fetched into registers while the current one is in use.
+#include "hh_common.h"
+#include "hh_kernels.h"
+
+namespace hh {
+
+namespace {
+constexpr int QT = 64;  // queries per workgroup
+constexpr int KT = 64;  // keys per tile
+constexpr float kLn2 = 0.69314718055994531f;
+}  // namespace
+
+template <int D, bool TAY>
+struct DistillCfg {
+    static constexpr int DF = TAY ? 0 : 2 * D;         // feature columns staged per key
+    static constexpr int KP = D + 16;                   // row pitch of the key tile (bf16)
+    static constexpr int FP = DF + 16;                  // row pitch of the key-feature tile
+    static constexpr int KSD = (D + 31) / 32;           // K steps over the head dim (d = 16: half)
+    static constexpr int KSF = DF / 32;                 // K steps over the features
+    static constexpr int GK = KT * D / 8;               // 16-byte pieces of a key tile
+    static constexpr int GF = KT * DF / 8;              // 16-byte pieces of a key-feature tile
+    static constexpr int PK = (GK + 255) / 256;         // pieces per thread
+    static constexpr int PF = (GF + 255) / 256;
+};
+
+template <int D, bool TAY>
+__global__ __launch_bounds__(256) void distill_kernel(DistillParams p) {
+    using C = DistillCfg<D, TAY>;
+    __shared__ __attribute__((aligned(16))) bf16_t sK[KT * C::KP];
+    __shared__ __attribute__((aligned(16))) bf16_t sF[TAY ? 8 : KT * C::FP];
+    const int nqt = (p.N + QT - 1) / QT;
+    const int bh = blockIdx.x / nqt;
+    // the longest rows of queries (most key tiles) are dispatched first
+    const int qt = nqt - 1 - blockIdx.x % nqt;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+    const size_t base = (size_t)bh * p.N;
+    const int qi = QT * qt + 16 * w + r16;  // this lane's query
+    const bool qok = qi < p.N;
+
+    // Query operands (B operands: column = query, K = head dims / features), kept in registers.
+    bf16x8 qop[C::KSD], fop[TAY ? 1 : C::KSF];
+#pragma unroll
+    for (int ks = 0; ks < C::KSD; ks++) {
+        const int c0 = 32 * ks + 8 * g;
+        qop[ks] = (qok && c0 < D) ? load8(p.q + (base + qi) * D + c0) : zero_bf16x8();
+    }
+    if (!TAY) {
+#pragma unroll
+        for (int ks = 0; ks < C::KSF; ks++)
+            fop[ks] = qok ? load8(p.phi_q + (base + qi) * C::DF + 32 * ks + 8 * g) : zero_bf16x8();
+    }
+
+    // Key tiles through registers: piece e of a tile is row e / (D / 8), 16-byte column e % (D / 8).
+    bf16x8 rk[C::PK], rf[TAY ? 1 : C::PF];
+    auto fetch = [&](int kt) {
+#pragma unroll
+        for (int u = 0; u < C::PK; u++) {
+            const int e = tid + 256 * u;
+            const int row = e / (D / 8), c8 = e % (D / 8), j = KT * kt + row;
+            rk[u] = (e < C::GK && j < p.N) ? load8(p.k + (base + j) * D + 8 * c8) : zero_bf16x8();
+        }
+        if (!TAY) {
+#pragma unroll
+            for (int u = 0; u < C::PF; u++) {
+                const int e = tid + 256 * u;
+                const int row = e / (C::DF / 8), c8 = e % (C::DF / 8), j = KT * kt + row;
+                rf[u] = (e < C::GF && j < p.N) ? load8(p.phi_k + (base + j) * C::DF + 8 * c8) : zero_bf16x8();
+            }
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int u = 0; u < C::PK; u++) {
+            const int e = tid + 256 * u;
+            if (e < C::GK) store8(sK + (e / (D / 8)) * C::KP + 8 * (e % (D / 8)), rk[u]);
+        }
+        if (!TAY) {
+#pragma unroll
+            for (int u = 0; u < C::PF; u++) {
+                const int e = tid + 256 * u;
+                if (e < C::GF) store8(sF + (e / (C::DF / 8)) * C::FP + 8 * (e % (C::DF / 8)), rf[u]);
+            }
+        }
+    };
+
+    // Per query (this lane's share of the keys): running maximum of the logits in log2 units, and
+    // the sums of e = 2^(logit - m), of e log2(a), and of a.
+    const float lscale = kLog2e * rsqrtf((float)D);
+    float m = -1.0e30f, l = 0.0f, t = 0.0f, r = 0.0f;
+
+    fetch(0);
+    for (int kt = 0; kt <= qt; kt++) {
+        __syncthreads();  // the previous tile is no longer read
+        stage();
+        __syncthreads();
+        if (kt < qt) fetch(kt + 1);
+
+        float x[4][4], av[4][4];
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) {
+            // A operands: key rows 16 nb + r16 of the tile; lane holds query r16, keys 4 g + rr
+            f32x4 s = zero4();
+#pragma unroll
+            for (int ks = 0; ks < C::KSD; ks++) {
+                const int c0 = 32 * ks + 8 * g;
+                const bf16x8 a = c0 < D ? load8(sK + (16 * nb + r16) * C::KP + c0) : zero_bf16x8();
+                s = mfma_bf16(a, qop[ks], s);
+            }
+            if (TAY) {
+#pragma unroll
+                for (int rr = 0; rr < 4; rr++) {
+                    x[nb][rr] = s[rr] * lscale;
+                    av[nb][rr] = fmaf(s[rr], fmaf(0.5f, s[rr], 1.0f), 1.0f);
+                }
+            } else {
+                f32x4 aa = zero4();
+#pragma unroll
+                for (int ks = 0; ks < C::KSF; ks++)
+                    aa = mfma_bf16(load8(sF + (16 * nb + r16) * C::FP + 32 * ks + 8 * g), fop[ks], aa);
+#pragma unroll
+                for (int rr = 0; rr < 4; rr++) {
+                    x[nb][rr] = s[rr] * lscale;
+                    av[nb][rr] = aa[rr];
+                }
+            }
+        }
+        // keys past the query (the causal boundary) or past the end take no part
+        const int kbase = KT * kt + 4 * g;
+        const bool full = KT * kt + KT - 1 <= QT * qt && KT * kt + KT <= p.N;  // no key of the tile masked
+        float mb = -1.0e30f;
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) {
+                const int j = kbase + 16 * nb + rr;
+                const bool ok = full || (j <= qi && j < p.N);
+                if (!ok) x[nb][rr] = -1.0e30f;
+                if (!ok) av[nb][rr] = 0.0f;
+                mb = fmaxf(mb, x[nb][rr]);
+            }
+        mb = fmaxf(mb, __shfl_xor(mb, 16));
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        const float mn = fmaxf(m, mb);
+        const float sc = exp2_fast(m - mn);
+        l *= sc;
+        t *= sc;
+        m = mn;
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) {
+                const float e = exp2_fast(x[nb][rr] - m);  // 0 for the masked keys
+                l += e;
+                r += av[nb][rr];
+                // masked keys: e = 0 and a = 0; the log of the stand-in 1 keeps 0 * log from NaN
+                t = fmaf(e, __builtin_amdgcn_logf(av[nb][rr] > 0.0f ? av[nb][rr] : 1.0f), t);
+            }
+    }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    t += __shfl_xor(t, 16);
+    t += __shfl_xor(t, 32);
+    r += __shfl_xor(r, 16);
+    r += __shfl_xor(r, 32);
+    if (g == 0 && qok) p.loss[base + qi] = (__builtin_amdgcn_logf(r) - t / l) * kLn2;
+}
+
+hipError_t launch_distill(int map, int d, const DistillParams &p, int BH, hipStream_t st) {
+    const int nqt = (p.N + QT - 1) / QT;
+    const dim3 grid((unsigned)((long)BH * nqt)), block(256);
+    if (map == 1) {
+        if (d != 16) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((distill_kernel<16, true>), grid, block, 0, st, p);
+        return hipGetLastError();
+    }
+    switch (d) {
+    case 16: hipLaunchKernelGGL((distill_kernel<16, false>), grid, block, 0, st, p); break;
+    case 32: hipLaunchKernelGGL((distill_kernel<32, false>), grid, block, 0, st, p); break;
+    case 64: hipLaunchKernelGGL((distill_kernel<64, false>), grid, block, 0, st, p); break;
+    case 128: hipLaunchKernelGGL((distill_kernel<128, false>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hh

@@ -73,6 +73,11 @@ def _cfg() -> Dict[str, Workload]:
         "c3_llama2_decode", MAP_HEDGEHOG, DT_BF16, True, B=16, H=32, N=4096, d=128, seed=2003,
         qk_scale=s3, v_scale=s3, w_std=128 ** -0.5, b_std=0.0,
         description="Llama-2-7B-shaped decode step over a 4096-token fp32 state, batch 16")
+    c["c3_llama2_distill"] = Workload(
+        "c3_llama2_distill", MAP_HEDGEHOG, DT_BF16, True, B=1, H=32, N=4096, d=128, seed=1003,
+        qk_scale=s3, v_scale=s3, w_std=128 ** -0.5, b_std=0.0,
+        description="attention-weight distillation loss (Eq. 4) at the Llama-2-7B head shapes, bf16, "
+                    "B1 H32 N4096 d128 (the causal workload's inputs; v unused)")
     c["c4_bert_bidir"] = Workload(
         "c4_bert_bidir", MAP_HEDGEHOG, DT_BF16, False, B=32, H=12, N=512, d=64, seed=1004,
         qk_scale=1.0, v_scale=1.0, w_std=64 ** -0.5, b_std=0.0,

@@ -108,6 +108,26 @@ def test_featuremap_and_decode_reject_bad_arguments(lib):
     assert dec(HOG, BF16, 1, 1, 64, A, Bp, Cp, Wp, None, 0x60000000, 0x61000000, A, None) == _lib.HH_EINVAL
 
 
+def test_distill_loss_rejects_bad_arguments(lib):
+    def call(map_=HOG, dt=BF16, B=1, H=2, N=64, d=64, q=A, k=Bp, W=Wp, b=None, loss=Dp, ws=Cp, ws_bytes=1 << 30):
+        return lib.hh_distill_loss(map_, dt, B, H, N, d, q, k, W, b, loss, ws, ws_bytes, None)
+    need = lib.hh_distill_loss_workspace(HOG, BF16, 1, 2, 64, 64)
+    assert need == 2 * 2 * 64 * 128 * 2                       # bf16 features of q and k
+    assert lib.hh_distill_loss_workspace(TAY, BF16, 1, 2, 64, 16) == 0
+    assert lib.hh_distill_loss_workspace(HOG, F32, 1, 2, 64, 64) == 0
+    assert call(dt=F32) == _lib.HH_EUNSUPPORTED               # bf16 inputs only
+    assert call(d=48) == _lib.HH_EUNSUPPORTED
+    assert call(map_=TAY, d=64) == _lib.HH_EUNSUPPORTED
+    assert call(loss=None) == _lib.HH_EINVAL
+    assert call(q=A + 2) == _lib.HH_EINVAL                     # misaligned
+    assert call(W=None) == _lib.HH_EINVAL
+    assert call(ws=None) == _lib.HH_EWORKSPACE
+    assert call(ws_bytes=need - 1) == _lib.HH_EWORKSPACE
+    assert call(loss=A) == _lib.HH_EINVAL                      # loss overlaps q
+    assert call(ws=A) == _lib.HH_EINVAL                        # workspace overlaps q
+    assert call(N=0, q=None, k=None, loss=None, W=None, ws=None, ws_bytes=0) == _lib.HH_OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(_lib, "_lib", None)
