@@ -399,7 +399,7 @@ hh_status_t hh_distill_loss(int map, int dtype, int B, int H, int N, int d, cons
     hh::DistillParams dp;
     dp.q = (const hh::bf16_t *)q; dp.k = (const hh::bf16_t *)k;
     dp.phi_q = dp.phi_k = nullptr;
-    dp.loss = loss; dp.N = N;
+    dp.loss = loss; dp.N = N; dp.BH = (int)BH;
     if (hog) {
         hh::bf16_t *fq = reinterpret_cast<hh::bf16_t *>(workspace);
         hh::bf16_t *fk = fq + (size_t)BH * N * 2 * d;

@@ -10,8 +10,8 @@
 // m_i of the logits and the three sums, rescaling two of them when m_i grows (the usual one-pass
 // softmax), so the n^2 weights are never stored.
 //
-// One workgroup owns 64 queries of one (b,h) (16 per wave) and walks the key tiles of 64 up to
-// its diagonal.  Per 16-key block, the scores come from the matrix cores with the keys as rows
+// One workgroup of eight waves owns 128 queries of one (b,h) (16 per wave) and walks the key
+// tiles of 64 up to its diagonal; each staged tile serves all eight waves.  Per 16-key block, the scores come from the matrix cores with the keys as rows
 // and the queries as columns, so a lane holds one query and four keys: the per-query reductions
 // run inside the lane and across the four lane groups (two shuffles).
 //   Hedgehog: a = phi(q).phi(k) with the 2d features of q and k precomputed by the feature-map
@@ -25,7 +25,8 @@
 namespace hh {
 
 namespace {
-constexpr int QT = 64;  // queries per workgroup
+constexpr int QT = 128;  // queries per workgroup
+constexpr int NT = 512;  // threads per workgroup (eight waves of 16 queries)
 constexpr int KT = 64;  // keys per tile
 constexpr float kLn2 = 0.69314718055994531f;
 }  // namespace
@@ -39,19 +40,28 @@ struct DistillCfg {
     static constexpr int KSF = DF / 32;                 // K steps over the features
     static constexpr int GK = KT * D / 8;               // 16-byte pieces of a key tile
     static constexpr int GF = KT * DF / 8;              // 16-byte pieces of a key-feature tile
-    static constexpr int PK = (GK + 255) / 256;         // pieces per thread
-    static constexpr int PF = (GF + 255) / 256;
+    static constexpr int PK = (GK + NT - 1) / NT;       // pieces per thread
+    static constexpr int PF = (GF + NT - 1) / NT;
 };
 
 template <int D, bool TAY>
-__global__ __launch_bounds__(256) void distill_kernel(DistillParams p) {
+__global__ __launch_bounds__(NT) void distill_kernel(DistillParams p) {
     using C = DistillCfg<D, TAY>;
     __shared__ __attribute__((aligned(16))) bf16_t sK[KT * C::KP];
     __shared__ __attribute__((aligned(16))) bf16_t sF[TAY ? 8 : KT * C::FP];
     const int nqt = (p.N + QT - 1) / QT;
-    const int bh = blockIdx.x / nqt;
-    // the longest rows of queries (most key tiles) are dispatched first
-    const int qt = nqt - 1 - blockIdx.x % nqt;
+    // The longest rows of queries (most key tiles) are dispatched first.  Workgroups go to the
+    // eight XCDs round-robin (blockIdx mod 8): when the (b,h) count allows, all query tiles of one
+    // (b,h) land on one XCD, so its keys and key features are fetched into that XCD's L2 once.
+    int bh, qt;
+    if (p.BH % 8 == 0) {
+        const int nhx = p.BH / 8, k = blockIdx.x / 8;
+        bh = blockIdx.x % 8 + 8 * (k % nhx);
+        qt = nqt - 1 - k / nhx;
+    } else {
+        bh = blockIdx.x / nqt;
+        qt = nqt - 1 - blockIdx.x % nqt;
+    }
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const size_t base = (size_t)bh * p.N;
@@ -76,14 +86,14 @@ __global__ __launch_bounds__(256) void distill_kernel(DistillParams p) {
     auto fetch = [&](int kt) {
 #pragma unroll
         for (int u = 0; u < C::PK; u++) {
-            const int e = tid + 256 * u;
+            const int e = tid + NT * u;
             const int row = e / (D / 8), c8 = e % (D / 8), j = KT * kt + row;
             rk[u] = (e < C::GK && j < p.N) ? load8(p.k + (base + j) * D + 8 * c8) : zero_bf16x8();
         }
         if (!TAY) {
 #pragma unroll
             for (int u = 0; u < C::PF; u++) {
-                const int e = tid + 256 * u;
+                const int e = tid + NT * u;
                 const int row = e / (C::DF / 8), c8 = e % (C::DF / 8), j = KT * kt + row;
                 rf[u] = (e < C::GF && j < p.N) ? load8(p.phi_k + (base + j) * C::DF + 8 * c8) : zero_bf16x8();
             }
@@ -92,13 +102,13 @@ __global__ __launch_bounds__(256) void distill_kernel(DistillParams p) {
     auto stage = [&]() {
 #pragma unroll
         for (int u = 0; u < C::PK; u++) {
-            const int e = tid + 256 * u;
+            const int e = tid + NT * u;
             if (e < C::GK) store8(sK + (e / (D / 8)) * C::KP + 8 * (e % (D / 8)), rk[u]);
         }
         if (!TAY) {
 #pragma unroll
             for (int u = 0; u < C::PF; u++) {
-                const int e = tid + 256 * u;
+                const int e = tid + NT * u;
                 if (e < C::GF) store8(sF + (e / (C::DF / 8)) * C::FP + 8 * (e % (C::DF / 8)), rf[u]);
             }
         }
@@ -109,39 +119,57 @@ __global__ __launch_bounds__(256) void distill_kernel(DistillParams p) {
     const float lscale = kLog2e * rsqrtf((float)D);
     float m = -1.0e30f, l = 0.0f, t = 0.0f, r = 0.0f;
 
+    // key tiles up to the one holding the workgroup's last query (or the sequence's last key)
+    const int nkt = min(QT * qt + QT - 1, p.N - 1) / KT + 1;
     fetch(0);
-    for (int kt = 0; kt <= qt; kt++) {
+    for (int kt = 0; kt < nkt; kt++) {
         __syncthreads();  // the previous tile is no longer read
         stage();
         __syncthreads();
-        if (kt < qt) fetch(kt + 1);
+        if (kt + 1 < nkt) fetch(kt + 1);
 
+        // A operands: key rows 16 nb + r16 of the tile; lane holds query r16, keys 4 g + rr.  Each
+        // group of operand reads is issued before its products, so the reads overlap one another.
         float x[4][4], av[4][4];
+        {
+            bf16x8 ko[4][C::KSD];
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++) {
-            // A operands: key rows 16 nb + r16 of the tile; lane holds query r16, keys 4 g + rr
-            f32x4 s = zero4();
+            for (int nb = 0; nb < 4; nb++)
 #pragma unroll
-            for (int ks = 0; ks < C::KSD; ks++) {
-                const int c0 = 32 * ks + 8 * g;
-                const bf16x8 a = c0 < D ? load8(sK + (16 * nb + r16) * C::KP + c0) : zero_bf16x8();
-                s = mfma_bf16(a, qop[ks], s);
-            }
-            if (TAY) {
-#pragma unroll
-                for (int rr = 0; rr < 4; rr++) {
-                    x[nb][rr] = s[rr] * lscale;
-                    av[nb][rr] = fmaf(s[rr], fmaf(0.5f, s[rr], 1.0f), 1.0f);
+                for (int ks = 0; ks < C::KSD; ks++) {
+                    const int c0 = 32 * ks + 8 * g;
+                    ko[nb][ks] = c0 < D ? load8(sK + (16 * nb + r16) * C::KP + c0) : zero_bf16x8();
                 }
-            } else {
-                f32x4 aa = zero4();
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int ks = 0; ks < C::KSF; ks++)
-                    aa = mfma_bf16(load8(sF + (16 * nb + r16) * C::FP + 32 * ks + 8 * g), fop[ks], aa);
+            for (int nb = 0; nb < 4; nb++) {
+                f32x4 s = zero4();
+#pragma unroll
+                for (int ks = 0; ks < C::KSD; ks++) s = mfma_bf16(ko[nb][ks], qop[ks], s);
 #pragma unroll
                 for (int rr = 0; rr < 4; rr++) {
                     x[nb][rr] = s[rr] * lscale;
-                    av[nb][rr] = aa[rr];
+                    if (TAY) av[nb][rr] = fmaf(s[rr], fmaf(0.5f, s[rr], 1.0f), 1.0f);
+                }
+            }
+        }
+        if (!TAY) {
+#pragma unroll
+            for (int np = 0; np < 2; np++) {  // two key blocks per group of reads
+                bf16x8 fo[2][TAY ? 1 : C::KSF];
+#pragma unroll
+                for (int h = 0; h < 2; h++)
+#pragma unroll
+                    for (int ks = 0; ks < C::KSF; ks++)
+                        fo[h][ks] = load8(sF + (16 * (2 * np + h) + r16) * C::FP + 32 * ks + 8 * g);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    f32x4 aa = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < C::KSF; ks++) aa = mfma_bf16(fo[h][ks], fop[ks], aa);
+#pragma unroll
+                    for (int rr = 0; rr < 4; rr++) av[2 * np + h][rr] = aa[rr];
                 }
             }
         }
@@ -188,7 +216,7 @@ __global__ __launch_bounds__(256) void distill_kernel(DistillParams p) {
 
 hipError_t launch_distill(int map, int d, const DistillParams &p, int BH, hipStream_t st) {
     const int nqt = (p.N + QT - 1) / QT;
-    const dim3 grid((unsigned)((long)BH * nqt)), block(256);
+    const dim3 grid((unsigned)((long)BH * nqt)), block(NT);
     if (map == 1) {
         if (d != 16) return hipErrorInvalidValue;
         hipLaunchKernelGGL((distill_kernel<16, true>), grid, block, 0, st, p);

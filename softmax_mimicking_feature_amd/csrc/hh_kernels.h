@@ -73,7 +73,7 @@ hipError_t launch_state_copy(const float *S0, const float *z0, float *S_out, flo
 struct DistillParams {
     const bf16_t *q, *k, *phi_q, *phi_k;
     float *loss;
-    int N;
+    int N, BH;
 };
 hipError_t launch_distill(int map, int d, const DistillParams &p, int BH, hipStream_t st);
 
