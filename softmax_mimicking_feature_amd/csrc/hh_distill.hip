@@ -177,16 +177,24 @@ __global__ __launch_bounds__(NT) void distill_kernel(DistillParams p) {
         const int kbase = KT * kt + 4 * g;
         const bool full = KT * kt + KT - 1 <= QT * qt && KT * kt + KT <= p.N;  // no key of the tile masked
         float mb = -1.0e30f;
+        if (full) {
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++)
+            for (int nb = 0; nb < 4; nb++)
 #pragma unroll
-            for (int rr = 0; rr < 4; rr++) {
-                const int j = kbase + 16 * nb + rr;
-                const bool ok = full || (j <= qi && j < p.N);
-                if (!ok) x[nb][rr] = -1.0e30f;
-                if (!ok) av[nb][rr] = 0.0f;
-                mb = fmaxf(mb, x[nb][rr]);
-            }
+                for (int rr = 0; rr < 4; rr++) mb = fmaxf(mb, x[nb][rr]);
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+                for (int rr = 0; rr < 4; rr++) {
+                    const int j = kbase + 16 * nb + rr;
+                    if (!(j <= qi && j < p.N)) {
+                        x[nb][rr] = -1.0e30f;  // e = 0
+                        av[nb][rr] = 0.0f;
+                    }
+                    mb = fmaxf(mb, x[nb][rr]);
+                }
+        }
         mb = fmaxf(mb, __shfl_xor(mb, 16));
         mb = fmaxf(mb, __shfl_xor(mb, 32));
         const float mn = fmaxf(m, mb);
@@ -194,16 +202,28 @@ __global__ __launch_bounds__(NT) void distill_kernel(DistillParams p) {
         l *= sc;
         t *= sc;
         m = mn;
+        if (full) {  // every weight a > 0
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++)
+            for (int nb = 0; nb < 4; nb++)
 #pragma unroll
-            for (int rr = 0; rr < 4; rr++) {
-                const float e = exp2_fast(x[nb][rr] - m);  // 0 for the masked keys
-                l += e;
-                r += av[nb][rr];
-                // masked keys: e = 0 and a = 0; the log of the stand-in 1 keeps 0 * log from NaN
-                t = fmaf(e, __builtin_amdgcn_logf(av[nb][rr] > 0.0f ? av[nb][rr] : 1.0f), t);
-            }
+                for (int rr = 0; rr < 4; rr++) {
+                    const float e = exp2_fast(x[nb][rr] - m);
+                    l += e;
+                    r += av[nb][rr];
+                    t = fmaf(e, __builtin_amdgcn_logf(av[nb][rr]), t);
+                }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+                for (int rr = 0; rr < 4; rr++) {
+                    const float e = exp2_fast(x[nb][rr] - m);  // 0 for the masked keys
+                    l += e;
+                    r += av[nb][rr];
+                    // masked keys: e = 0 and a = 0; the log of the stand-in 1 keeps 0 * log from NaN
+                    t = fmaf(e, __builtin_amdgcn_logf(av[nb][rr] > 0.0f ? av[nb][rr] : 1.0f), t);
+                }
+        }
     }
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
