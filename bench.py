@@ -301,7 +301,7 @@ def main():
     if decode:
         roof["kernel"] = "hh_linattn_decode_step (decode_kernel)"
     elif distill:
-        roof["kernel"] = "hh_distill_loss: every kernel of one call (feature maps of q and k, then distill_kernel)"
+        roof["kernel"] = "hh_distill_loss: every kernel of one call (feature map of k, then distill_kernel, which maps its queries itself)"
     elif w.map == wl.MAP_TAYLOR2:
         roof["kernel"] = ("hh_linattn_fwd: every kernel of one call (segment aggregates, exclusive prefix "
                           "over segments, chunked causal pass)")

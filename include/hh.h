@@ -118,8 +118,8 @@ hh_status_t hh_linattn_decode_step(int map, int dtype, int B, int H, int d,
                                    const void *W, const void *b,
                                    float *S, float *z, void *y, void *stream);
 
-/* Bytes of workspace hh_distill_loss needs (the features of q and k for the Hedgehog map,
- * 0 for the Taylor map).  Returns 0 as well for invalid arguments. */
+/* Bytes of workspace hh_distill_loss needs (the features of k for the Hedgehog map, 0 for the
+ * Taylor map).  Returns 0 as well for invalid arguments. */
 size_t hh_distill_loss_workspace(int map, int dtype, int B, int H, int N, int d);
 
 /* Attention-weight distillation loss of Eq. 4 (paper-graph-ui walkthrough, section 3.4, "The

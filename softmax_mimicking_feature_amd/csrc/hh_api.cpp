@@ -361,7 +361,7 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
 
 size_t hh_distill_loss_workspace(int map, int dtype, int B, int H, int N, int d) {
     if (check_common(map, dtype, B, H, N, d) != HH_OK || dtype != HH_BF16 || map != HH_MAP_HEDGEHOG) return 0;
-    return 2 * (size_t)B * H * N * 2 * d * sizeof(uint16_t);
+    return (size_t)B * H * N * 2 * d * sizeof(uint16_t);  // the features of k
 }
 
 hh_status_t hh_distill_loss(int map, int dtype, int B, int H, int N, int d, const void *q, const void *k,
@@ -398,18 +398,16 @@ hh_status_t hh_distill_loss(int map, int dtype, int B, int H, int N, int d, cons
     hipError_t e;
     hh::DistillParams dp;
     dp.q = (const hh::bf16_t *)q; dp.k = (const hh::bf16_t *)k;
-    dp.phi_q = dp.phi_k = nullptr;
-    dp.loss = loss; dp.N = N; dp.BH = (int)BH;
+    dp.phi_k = nullptr;
+    dp.W = hog ? (const hh::bf16_t *)W : nullptr;
+    dp.b = hog ? (const hh::bf16_t *)b : nullptr;
+    dp.loss = loss; dp.N = N; dp.BH = (int)BH; dp.H = H;
     if (hog) {
-        hh::bf16_t *fq = reinterpret_cast<hh::bf16_t *>(workspace);
-        hh::bf16_t *fk = fq + (size_t)BH * N * 2 * d;
-        e = hh::launch_featuremap_hedgehog_bf16(d, (const hh::bf16_t *)q, (const hh::bf16_t *)W,
-                                                (const hh::bf16_t *)b, fq, (int)BH, H, N, s);
-        if (e != hipSuccess) return hip_fail(e, "feature map launch");
+        hh::bf16_t *fk = reinterpret_cast<hh::bf16_t *>(workspace);
         e = hh::launch_featuremap_hedgehog_bf16(d, (const hh::bf16_t *)k, (const hh::bf16_t *)W,
                                                 (const hh::bf16_t *)b, fk, (int)BH, H, N, s);
         if (e != hipSuccess) return hip_fail(e, "feature map launch");
-        dp.phi_q = fq; dp.phi_k = fk;
+        dp.phi_k = fk;
     }
     e = hh::launch_distill(map, d, dp, (int)BH, s);
     if (e != hipSuccess) return hip_fail(e, "distillation loss launch");

@@ -14,8 +14,13 @@
 // tiles of 64 up to its diagonal; each staged tile serves all eight waves.  Per 16-key block, the scores come from the matrix cores with the keys as rows
 // and the queries as columns, so a lane holds one query and four keys: the per-query reductions
 // run inside the lane and across the four lane groups (two shuffles).
-//   Hedgehog: a = phi(q).phi(k) with the 2d features of q and k precomputed by the feature-map
-//             kernel (bf16, as the forward pass uses them).
+//   Hedgehog: a = phi(q).phi(k).  The key features (2d per key, bf16 as the forward pass uses
+//             them) are precomputed by the feature-map kernel, since every query tile reads them;
+//             each wave maps its own 16 queries in its prologue (u = W q + b on the matrix cores,
+//             W staged once per workgroup in the key-feature tile's space, then the exponentials),
+//             straight into the operand registers of the weight products:
+//             two 16-direction accumulator blocks give lane group g the features 4g..4g+3 and
+//             16+4g..16+4g+3 of a 32-feature step, and the key features are read in that order.
 //   Taylor:   a = 1 + s + s^2/2 with s = q.k, the map's closed form (section 3.4, "The Taylor
 //             Exponential as a Bridge Result"), from the same product as the logits.
 // The next key tile is fetched into registers while the current one is in use.
@@ -76,9 +81,50 @@ __global__ __launch_bounds__(NT) void distill_kernel(DistillParams p) {
         qop[ks] = (qok && c0 < D) ? load8(p.q + (base + qi) * D + c0) : zero_bf16x8();
     }
     if (!TAY) {
+        // u[l][query] for directions l = 16 mb + 4 g + rr (A: W rows, B: the query operands), then
+        // feature step ks (ks < d / 32: exp(u), else exp(-u)) from direction blocks 2 (ks mod d/32)
+        // and 2 (ks mod d/32) + 1
+        const int h = bh % p.H;
+        const bf16_t *Wh = p.W + (size_t)h * D * D;
+        constexpr int WP = D + 8;  // row pitch of W in LDS (the key-feature tile is free until the first tile)
+        static_assert(D * WP <= KT * C::FP, "W fits in the key-feature tile");
+        for (int e = tid; e < D * D / 8; e += NT) store8(sF + (e / (D / 8)) * WP + 8 * (e % (D / 8)), load8(Wh + 8 * e));
+        __syncthreads();
+        constexpr int NMB = D / 16;
+        f32x4 u[NMB];
 #pragma unroll
-        for (int ks = 0; ks < C::KSF; ks++)
-            fop[ks] = qok ? load8(p.phi_q + (base + qi) * C::DF + 32 * ks + 8 * g) : zero_bf16x8();
+        for (int mb = 0; mb < NMB; mb++) {
+            bf16x8 wa[C::KSD];
+#pragma unroll
+            for (int ks = 0; ks < C::KSD; ks++) {
+                const int m0 = 32 * ks + 8 * g;
+                wa[ks] = m0 < D ? load8(sF + (16 * mb + r16) * WP + m0) : zero_bf16x8();
+            }
+            u[mb] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < C::KSD; ks++) u[mb] = mfma_bf16(wa[ks], qop[ks], u[mb]);
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) {
+                const float bb = p.b ? bf16_bits_to_float(p.b[(size_t)h * D + 16 * mb + 4 * g + rr]) : 0.0f;
+                u[mb][rr] = (u[mb][rr] + bb) * kLog2e;
+            }
+        }
+        // (d = 16: one step, exp(u) of the 16 directions then exp(-u) of the same)
+        constexpr int HALF = C::KSF / 2 > 0 ? C::KSF / 2 : 1;
+#pragma unroll
+        for (int ks = 0; ks < C::KSF; ks++) {
+            const int mb0 = D == 16 ? 0 : 2 * (ks % HALF);
+            const int mb1 = D == 16 ? 0 : mb0 + 1;
+            const float sg0 = D == 16 ? 1.0f : (ks < HALF ? 1.0f : -1.0f);
+            const float sg1 = D == 16 ? -1.0f : sg0;
+            f32x4 lo, hi;
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) {
+                lo[rr] = exp2_fast(sg0 * u[mb0][rr]);
+                hi[rr] = exp2_fast(sg1 * u[mb1][rr]);
+            }
+            fop[ks] = qok ? acc_pair_to_operand(lo, hi) : zero_bf16x8();
+        }
     }
 
     // Key tiles through registers: piece e of a tile is row e / (D / 8), 16-byte column e % (D / 8).
@@ -106,10 +152,20 @@ __global__ __launch_bounds__(NT) void distill_kernel(DistillParams p) {
             if (e < C::GK) store8(sK + (e / (D / 8)) * C::KP + 8 * (e % (D / 8)), rk[u]);
         }
         if (!TAY) {
+            // key features stored in the K order of the query operands: within each 32-feature
+            // group, the 4-feature units 0..3 go to slots 0, 2, 4, 6 and units 4..7 to slots 1, 3,
+            // 5, 7, so that the 16-byte read of lane group g holds features 4g.. and 16+4g..
 #pragma unroll
             for (int u = 0; u < C::PF; u++) {
                 const int e = tid + NT * u;
-                if (e < C::GF) store8(sF + (e / (C::DF / 8)) * C::FP + 8 * (e % (C::DF / 8)), rf[u]);
+                if (e < C::GF) {
+                    const int row = e / (C::DF / 8), c8 = e % (C::DF / 8);
+                    const int grp = c8 >> 2, lu = 2 * (c8 & 3);                 // local units lu, lu + 1
+                    const int s0 = lu < 4 ? 2 * lu : 2 * (lu - 4) + 1, s1 = lu + 1 < 4 ? 2 * (lu + 1) : 2 * (lu - 3) + 1;
+                    bf16_t *dst = sF + row * C::FP + 32 * grp;
+                    store4(dst + 4 * s0, __builtin_shufflevector(rf[u], rf[u], 0, 1, 2, 3));
+                    store4(dst + 4 * s1, __builtin_shufflevector(rf[u], rf[u], 4, 5, 6, 7));
+                }
             }
         }
     };

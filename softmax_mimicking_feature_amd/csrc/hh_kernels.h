@@ -68,12 +68,12 @@ hipError_t launch_prefix(const PrefixParams &p, hipStream_t st);
 hipError_t launch_state_copy(const float *S0, const float *z0, float *S_out, float *z_out, long nS, long nz,
                              hipStream_t st);
 
-// Distillation loss (one workgroup per 64 queries of a (b,h)).  phi_q / phi_k: the 2d bf16
-// features of q and k (Hedgehog), unused for the Taylor map.
+// Distillation loss (one workgroup per 128 queries of a (b,h)).  phi_k: the 2d bf16 features of
+// k; W, b: the Hedgehog parameters (the kernel maps the queries itself).  Unused for the Taylor map.
 struct DistillParams {
-    const bf16_t *q, *k, *phi_q, *phi_k;
+    const bf16_t *q, *k, *phi_k, *W, *b;
     float *loss;
-    int N, BH;
+    int N, BH, H;
 };
 hipError_t launch_distill(int map, int d, const DistillParams &p, int BH, hipStream_t st);
 

@@ -112,7 +112,7 @@ def test_distill_loss_rejects_bad_arguments(lib):
     def call(map_=HOG, dt=BF16, B=1, H=2, N=64, d=64, q=A, k=Bp, W=Wp, b=None, loss=Dp, ws=Cp, ws_bytes=1 << 30):
         return lib.hh_distill_loss(map_, dt, B, H, N, d, q, k, W, b, loss, ws, ws_bytes, None)
     need = lib.hh_distill_loss_workspace(HOG, BF16, 1, 2, 64, 64)
-    assert need == 2 * 2 * 64 * 128 * 2                       # bf16 features of q and k
+    assert need == 2 * 64 * 128 * 2                           # bf16 features of k
     assert lib.hh_distill_loss_workspace(TAY, BF16, 1, 2, 64, 16) == 0
     assert lib.hh_distill_loss_workspace(HOG, F32, 1, 2, 64, 64) == 0
     assert call(dt=F32) == _lib.HH_EUNSUPPORTED               # bf16 inputs only
