@@ -34,6 +34,7 @@ constexpr int QT = 128;  // queries per workgroup
 constexpr int NT = 512;  // threads per workgroup (eight waves of 16 queries)
 constexpr int KT = 64;  // keys per tile
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kSchedValu = 0x2, kSchedMfma = 0x8, kSchedDsRead = 0x100;  // scheduling-group masks
 }  // namespace
 
 template <int D, bool TAY>
@@ -175,111 +176,140 @@ __global__ __launch_bounds__(NT) void distill_kernel(DistillParams p) {
     const float lscale = kLog2e * rsqrtf((float)D);
     float m = -1.0e30f, l = 0.0f, t = 0.0f, r = 0.0f;
 
-    // key tiles up to the one holding the workgroup's last query (or the sequence's last key)
-    const int nkt = min(QT * qt + QT - 1, p.N - 1) / KT + 1;
-    fetch(0);
-    for (int kt = 0; kt < nkt; kt++) {
-        __syncthreads();  // the previous tile is no longer read
-        stage();
-        __syncthreads();
-        if (kt + 1 < nkt) fetch(kt + 1);
-
-        // A operands: key rows 16 nb + r16 of the tile; lane holds query r16, keys 4 g + rr.  Each
-        // group of operand reads is issued before its products, so the reads overlap one another.
-        float x[4][4], av[4][4];
-        {
-            bf16x8 ko[4][C::KSD];
+    // The products of the staged tile: raw scores s (A operands: key rows 16 nb + r16 of the tile;
+    // lane holds query r16, keys 4 g + rr of block nb) and the weights a.  Each group of operand
+    // reads is issued before its products, so the reads overlap one another; vector work (the
+    // update of the previous tile) may be scheduled between them.
+    auto products = [&](float (&x)[4][4], float (&av)[4][4], bool fenced) {
 #pragma unroll
-            for (int nb = 0; nb < 4; nb++)
+        for (int n2 = 0; n2 < 2; n2++) {  // two key blocks per group of reads
+            bf16x8 ko[2][C::KSD];
+#pragma unroll
+            for (int h = 0; h < 2; h++)
 #pragma unroll
                 for (int ks = 0; ks < C::KSD; ks++) {
                     const int c0 = 32 * ks + 8 * g;
-                    ko[nb][ks] = c0 < D ? load8(sK + (16 * nb + r16) * C::KP + c0) : zero_bf16x8();
+                    ko[h][ks] = c0 < D ? load8(sK + (16 * (2 * n2 + h) + r16) * C::KP + c0) : zero_bf16x8();
                 }
-            __builtin_amdgcn_sched_barrier(0);
+            if (fenced) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int nb = 0; nb < 4; nb++) {
-                f32x4 s = zero4();
+            for (int h = 0; h < 2; h++) {
+                const int nb = 2 * n2 + h;
+                f32x4 sv = zero4();
 #pragma unroll
-                for (int ks = 0; ks < C::KSD; ks++) s = mfma_bf16(ko[nb][ks], qop[ks], s);
+                for (int ks = 0; ks < C::KSD; ks++) sv = mfma_bf16(ko[h][ks], qop[ks], sv);
 #pragma unroll
                 for (int rr = 0; rr < 4; rr++) {
-                    x[nb][rr] = s[rr] * lscale;
-                    if (TAY) av[nb][rr] = fmaf(s[rr], fmaf(0.5f, s[rr], 1.0f), 1.0f);
+                    x[nb][rr] = sv[rr];
+                    if (TAY) av[nb][rr] = fmaf(sv[rr], fmaf(0.5f, sv[rr], 1.0f), 1.0f);
                 }
             }
         }
         if (!TAY) {
 #pragma unroll
-            for (int np = 0; np < 2; np++) {  // two key blocks per group of reads
-                bf16x8 fo[2][TAY ? 1 : C::KSF];
+            for (int nb = 0; nb < 4; nb++) {  // one key block per group of reads
+                bf16x8 fo[TAY ? 1 : C::KSF];
 #pragma unroll
-                for (int h = 0; h < 2; h++)
+                for (int ks = 0; ks < C::KSF; ks++) fo[ks] = load8(sF + (16 * nb + r16) * C::FP + 32 * ks + 8 * g);
+                if (fenced) __builtin_amdgcn_sched_barrier(0);
+                f32x4 aa = zero4();
 #pragma unroll
-                    for (int ks = 0; ks < C::KSF; ks++)
-                        fo[h][ks] = load8(sF + (16 * (2 * np + h) + r16) * C::FP + 32 * ks + 8 * g);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int ks = 0; ks < C::KSF; ks++) aa = mfma_bf16(fo[ks], fop[ks], aa);
 #pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    f32x4 aa = zero4();
-#pragma unroll
-                    for (int ks = 0; ks < C::KSF; ks++) aa = mfma_bf16(fo[h][ks], fop[ks], aa);
-#pragma unroll
-                    for (int rr = 0; rr < 4; rr++) av[2 * np + h][rr] = aa[rr];
-                }
+                for (int rr = 0; rr < 4; rr++) av[nb][rr] = aa[rr];
             }
         }
-        // keys past the query (the causal boundary) or past the end take no part
-        const int kbase = KT * kt + 4 * g;
-        const bool full = KT * kt + KT - 1 <= QT * qt && KT * kt + KT <= p.N;  // no key of the tile masked
+    };
+    // The one-pass softmax update with one tile's scores: new maximum (across the four lane groups
+    // of a query), rescaled sums, then the tile's terms.  Keys of a masked tile past the query or
+    // past the end get s = -inf (e = 0) and a = 0; the log of the stand-in 1 keeps 0 log 0 from a
+    // NaN.  A tile with no masked key takes the branch-free form.
+    auto update = [&](float (&x)[4][4], float (&av)[4][4], bool masked, int kt) {
         float mb = -1.0e30f;
-        if (full) {
-#pragma unroll
-            for (int nb = 0; nb < 4; nb++)
-#pragma unroll
-                for (int rr = 0; rr < 4; rr++) mb = fmaxf(mb, x[nb][rr]);
-        } else {
+        if (masked) {
+            const int kbase = KT * kt + 4 * g;
 #pragma unroll
             for (int nb = 0; nb < 4; nb++)
 #pragma unroll
                 for (int rr = 0; rr < 4; rr++) {
                     const int j = kbase + 16 * nb + rr;
                     if (!(j <= qi && j < p.N)) {
-                        x[nb][rr] = -1.0e30f;  // e = 0
+                        x[nb][rr] = -1.0e30f;
                         av[nb][rr] = 0.0f;
                     }
-                    mb = fmaxf(mb, x[nb][rr]);
                 }
         }
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) mb = fmaxf(mb, x[nb][rr]);
         mb = fmaxf(mb, __shfl_xor(mb, 16));
         mb = fmaxf(mb, __shfl_xor(mb, 32));
-        const float mn = fmaxf(m, mb);
+        const float mn = fmaxf(m, mb * lscale);  // lscale > 0: the maximum of the scaled logits
         const float sc = exp2_fast(m - mn);
         l *= sc;
         t *= sc;
         m = mn;
-        if (full) {  // every weight a > 0
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++)
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) {
+                const float e = exp2_fast(fmaf(x[nb][rr], lscale, -m));
+                l += e;
+                r += av[nb][rr];
+                t = fmaf(e, __builtin_amdgcn_logf(masked ? (av[nb][rr] > 0.0f ? av[nb][rr] : 1.0f) : av[nb][rr]), t);
+            }
+    };
+    const int nkt = min(QT * qt + QT - 1, p.N - 1) / KT + 1;
+    const int nfull = min(min((QT * qt + 1) / KT, p.N / KT), nkt);
+    auto next_tile = [&](int kt) {
+        __syncthreads();  // the previous tile is no longer read
+        stage();
+        __syncthreads();
+        if (kt + 1 < nkt) fetch(kt + 1);
+    };
+
+    // Key tiles up to the one holding the workgroup's last query (or the sequence's last key).
+    // The leading tiles with no masked key (below the diagonal and inside the sequence) run as a
+    // software pipeline: the products of tile kt are issued alongside the update with tile kt - 1,
+    // so each wave keeps the matrix and vector pipes busy at once; the masked tiles follow.
+    fetch(0);
+    int kt = 0;
+    if (nfull > 0) {
+        float xp[4][4], ap[4][4];
+        next_tile(0);
+        products(xp, ap, true);
+        for (kt = 1; kt < nfull; kt++) {
+            next_tile(kt);
+            float x[4][4], av[4][4];
+            products(x, av, false);
+            update(xp, ap, false, kt - 1);
 #pragma unroll
             for (int nb = 0; nb < 4; nb++)
 #pragma unroll
                 for (int rr = 0; rr < 4; rr++) {
-                    const float e = exp2_fast(x[nb][rr] - m);
-                    l += e;
-                    r += av[nb][rr];
-                    t = fmaf(e, __builtin_amdgcn_logf(av[nb][rr]), t);
+                    xp[nb][rr] = x[nb][rr];
+                    ap[nb][rr] = av[nb][rr];
                 }
-        } else {
+            // Issue order: the first group of operand reads, then each product with three vector
+            // instructions of the update beside it and one read of a later group.
+            if (D == 128) {
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
 #pragma unroll
-            for (int nb = 0; nb < 4; nb++)
-#pragma unroll
-                for (int rr = 0; rr < 4; rr++) {
-                    const float e = exp2_fast(x[nb][rr] - m);  // 0 for the masked keys
-                    l += e;
-                    r += av[nb][rr];
-                    // masked keys: e = 0 and a = 0; the log of the stand-in 1 keeps 0 * log from NaN
-                    t = fmaf(e, __builtin_amdgcn_logf(av[nb][rr] > 0.0f ? av[nb][rr] : 1.0f), t);
+                for (int i = 0; i < 48; i++) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
+                    if (i < 40) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
                 }
+            }
         }
+        update(xp, ap, false, nfull - 1);
+    }
+    for (; kt < nkt; kt++) {
+        next_tile(kt);
+        float x[4][4], av[4][4];
+        products(x, av, true);
+        update(x, av, true, kt);
     }
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
