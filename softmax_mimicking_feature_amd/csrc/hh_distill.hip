@@ -291,15 +291,16 @@ __global__ __launch_bounds__(NT) void distill_kernel(DistillParams p) {
                     xp[nb][rr] = x[nb][rr];
                     ap[nb][rr] = av[nb][rr];
                 }
-            // Issue order: the first group of operand reads, then each product with three vector
-            // instructions of the update beside it and one read of a later group.
+            // Issue order: four operand reads, then each product with two vector instructions of
+            // the update beside it and the next operand read (measured against three and four
+            // vector instructions and two, eight and sixteen reads ahead).
             if (D == 128) {
-                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
                 for (int i = 0; i < 48; i++) {
                     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
-                    if (i < 40) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 2, 0);
+                    if (i < 44) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
                 }
             }
         }
