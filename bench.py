@@ -144,7 +144,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path shards over "
-              "(batch, head) pairs with no communication, see DESIGN.md)", file=sys.stderr)
+              "(batch, head) pairs with no communication)", file=sys.stderr)
         sys.exit(2)
 
     import torch
