@@ -65,6 +65,15 @@ def _dev(t, name: str, dtype=None):
     return t
 
 
+def _shape(t, name: str, shape) -> None:
+    """Host-side size check: the C ABI receives raw pointers and cannot tell an undersized
+    buffer from a valid one, so every tensor's shape is checked before anything is launched."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -95,11 +104,17 @@ def hh_featuremap(x, W=None, b=None, *, map: int = HH_MAP_HEDGEHOG, out=None, st
     """phi(x) for x [B,H,N,d]; returns [B,H,N,d'] in x's dtype."""
     lib = _lib.load()
     torch = _torch()
-    _dev(x, "x")
+    if x.dim() != 4:
+        raise ValueError(f"x must be [B,H,N,d], got {list(x.shape)}")
     B, H, N, d = x.shape
     dp = lib.hh_feature_dim(map, d)
     if dp < 0:
         raise ValueError(f"invalid map/head dim ({map}, {d})")
+    if map == HH_MAP_HEDGEHOG:
+        _shape(W, "W", (H, d, d))
+        _shape(b, "b", (H, d))
+    _shape(out, "out", (B, H, N, dp))
+    _dev(x, "x")
     if out is None:
         out = torch.empty((B, H, N, dp), dtype=x.dtype, device=x.device)
     _dev(out, "out", x.dtype)
@@ -122,18 +137,31 @@ def hh_linattn_fwd(q, k, v, W=None, b=None, *, causal: bool = True, map: int = H
     Returns y, or (y, S_out, z_out) when want_state (fp32 final state)."""
     lib = _lib.load()
     torch = _torch()
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, nm, q.dtype)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B,H,N,d], got {list(q.shape)}")
     B, H, N, d = q.shape
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape [B,H,N,d]")
-    dt = _dtype_code(q)
     dp = lib.hh_feature_dim(map, d)
+    if dp < 0:
+        raise ValueError(f"invalid map/head dim ({map}, {d})")
     if map == HH_MAP_HEDGEHOG:
-        _dev(W, "W", q.dtype)
-        _dev(b, "b", q.dtype)
+        if W is None:
+            raise ValueError("W is required for the Hedgehog map")
+        _shape(W, "W", (H, d, d))
+        _shape(b, "b", (H, d))
     else:
         W = b = None
+    _shape(out, "out", q.shape)
+    for t, nm in ((S0, "S0"), (S_out, "S_out")):
+        _shape(t, nm, (B, H, dp, d))
+    for t, nm in ((z0, "z0"), (z_out, "z_out")):
+        _shape(t, nm, (B, H, dp))
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, nm, q.dtype)
+    dt = _dtype_code(q)
+    _dev(W, "W", q.dtype)
+    _dev(b, "b", q.dtype)
     _dev(S0, "S0", torch.float32)
     _dev(z0, "z0", torch.float32)
     if out is None:
@@ -160,18 +188,31 @@ def hh_linattn_decode_step(q, k, v, W, b, S, z, *, map: int = HH_MAP_HEDGEHOG, o
     """One recurrent step.  q, k, v: [B,H,d] or [B,H,1,d]; S [B,H,d',d], z [B,H,d'] fp32 updated in place."""
     lib = _lib.load()
     torch = _torch()
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, nm, q.dtype)
+    if q.dim() not in (3, 4) or (q.dim() == 4 and q.shape[2] != 1):
+        raise ValueError(f"decode expects q of shape [B,H,d] or [B,H,1,d], got {list(q.shape)}")
     B, H = q.shape[:2]
     d = q.shape[-1]
-    if q.numel() != B * H * d:
-        raise ValueError("decode expects one token per (b, h)")
-    dt = _dtype_code(q)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    dp = lib.hh_feature_dim(map, d)
+    if dp < 0:
+        raise ValueError(f"invalid map/head dim ({map}, {d})")
     if map == HH_MAP_HEDGEHOG:
-        _dev(W, "W", q.dtype)
-        _dev(b, "b", q.dtype)
+        if W is None:
+            raise ValueError("W is required for the Hedgehog map")
+        _shape(W, "W", (H, d, d))
+        _shape(b, "b", (H, d))
     else:
         W = b = None
+    _shape(S, "S", (B, H, dp, d))
+    _shape(z, "z", (B, H, dp))
+    if out is not None and out.numel() != B * H * d:
+        raise ValueError(f"out must hold B*H*d = {B * H * d} elements, got {list(out.shape)}")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, nm, q.dtype)
+    dt = _dtype_code(q)
+    _dev(W, "W", q.dtype)
+    _dev(b, "b", q.dtype)
     _dev(S, "S", torch.float32)
     _dev(z, "z", torch.float32)
     if out is None:
@@ -190,17 +231,24 @@ def hh_distill_loss(q, k, W=None, b=None, *, map: int = HH_MAP_HEDGEHOG, out=Non
     """Attention-weight distillation loss (Eq. 4) per query.  q, k: [B,H,N,d] bf16 -> loss [B,H,N] fp32."""
     lib = _lib.load()
     torch = _torch()
-    for t, nm in ((q, "q"), (k, "k")):
-        _dev(t, nm, q.dtype)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B,H,N,d], got {list(q.shape)}")
     B, H, N, d = q.shape
     if k.shape != q.shape:
         raise ValueError("q and k must have the same shape [B,H,N,d]")
-    dt = _dtype_code(q)
     if map == HH_MAP_HEDGEHOG:
-        _dev(W, "W", q.dtype)
-        _dev(b, "b", q.dtype)
+        if W is None:
+            raise ValueError("W is required for the Hedgehog map")
+        _shape(W, "W", (H, d, d))
+        _shape(b, "b", (H, d))
     else:
         W = b = None
+    _shape(out, "out", (B, H, N))
+    for t, nm in ((q, "q"), (k, "k")):
+        _dev(t, nm, q.dtype)
+    dt = _dtype_code(q)
+    _dev(W, "W", q.dtype)
+    _dev(b, "b", q.dtype)
     if out is None:
         out = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _dev(out, "out", torch.float32)
