@@ -9,13 +9,20 @@ What each function computes, with its source on the pages ("The Hedgehog &
 the Porcupine: Expressive Linear Attentions with Softmax Mimicry"):
   featuremap  -- Hedgehog map exp(+-(W x + b)) (section 3.4, "The Hedgehog MLP
                  Feature Map", Choices 1 and 3) or the degree-2 Taylor map
-                 (section 3.4, "The Taylor Exponential as a Bridge Result").
+                 (section 3.4, "The Taylor Exponential as a Bridge Result");
+                 the single-sided exp(W x + b) with d' = d (Choice 1 and the
+                 default d' = d of the same section); the softmax over the d
+                 feature directions, no bias (Choice 4), single-sided (d' = d)
+                 or with the negation mapping as one softmax per half (d' = 2d).
   causal      -- Eq. 2 by running sums S_i, z_i (section 3.4, "Complexity
                  Analysis"), with optional initial and final state.
   bidir       -- the same sums over all keys (bidirectional encoders).
   decode_step -- one running-sum update followed by the read-out.
   quadratic   -- Eq. 2 as an explicit sum over key positions (no running sums),
                  used to pin the running-sum form and for sampled rows.
+  causal_features -- the running-sum form from given features phi(q_i), phi(k_j).
+  backward    -- gradients of sum(dy * y) with respect to q, k, v, W and b,
+                 from the explicit form by the chain rule.
 Parity status: every function is pinned by the closed forms and invariants in
 tests/test_oracle_pins.py (no function is "parity unpinned").
 """
@@ -35,6 +42,9 @@ LIB = os.path.join(HERE, "libhh_oracle.so")
 
 MAP_HEDGEHOG = 0
 MAP_TAYLOR2 = 1
+MAP_HEDGEHOG_SOFTMAX = 2
+MAP_EXP = 3
+MAP_SOFTMAX = 4
 
 _lib = None
 
@@ -66,8 +76,10 @@ def _load():
         lib.hho_quadratic.argtypes = [I, I, L, L, L, I, D, D, D, D, D, L, D, D, I]
         lib.hho_featuremap.argtypes = [I, I, L, L, L, D, D, D, D, I]
         lib.hho_distill.argtypes = [I, I, L, L, L, D, D, D, D, L, D, D, I]
+        lib.hho_causal_features.argtypes = [I, I, L, L, D, D, D, D, D, D, D, D, I]
+        lib.hho_backward.argtypes = [I, I, L, L, L, I, D, D, D, D, D, D, D, D, D, D, D, I]
         for f in (lib.hho_causal, lib.hho_bidir, lib.hho_decode_step, lib.hho_quadratic,
-                  lib.hho_featuremap, lib.hho_distill):
+                  lib.hho_featuremap, lib.hho_distill, lib.hho_causal_features, lib.hho_backward):
             f.restype = None
         _lib = lib
     return _lib
@@ -93,11 +105,13 @@ def feature_dim(map_: int, d: int) -> int:
 
 
 def _params(map_, W, b, H, d):
-    if map_ == MAP_HEDGEHOG:
-        W = _f64(W).reshape(H, d, d)
+    if map_ == MAP_TAYLOR2:
+        return None, None
+    W = _f64(W).reshape(H, d, d)
+    if map_ in (MAP_HEDGEHOG, MAP_EXP):
         b = None if b is None or np.size(b) == 0 else _f64(b).reshape(H, d)
-    else:
-        W, b = None, None
+    else:  # the softmax maps have no bias
+        b = None
     return W, b
 
 
@@ -129,6 +143,24 @@ def causal(map_: int, q, k, v, W=None, b=None, S0=None, z0=None, want_state: boo
     z = np.empty((B, H, dp), np.float64) if want_state else None
     _load().hho_causal(map_, d, B, H, N, _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(b), _ptr(S0),
                        _ptr(z0), _ptr(y), _ptr(S), _ptr(z), nthreads or default_threads())
+    return (y, S, z) if want_state else y
+
+
+def causal_features(phiq, phik, v, S0=None, z0=None, want_state: bool = False, nthreads: Optional[int] = None):
+    """Causal Eq. 2 by running sums from given features phi(q_i), phi(k_j) [B,H,N,d'] and values
+    v [B,H,N,d] (the recurrence of section 3.4, "Complexity Analysis", with the feature map
+    already applied).  Returns y [B,H,N,d], and the final (S, z) with want_state."""
+    phiq, phik, v = _f64(phiq), _f64(phik), _f64(v)
+    B, H, N, d = v.shape
+    dp = phiq.shape[-1]
+    assert phiq.shape == (B, H, N, dp) and phik.shape == (B, H, N, dp)
+    S0 = None if S0 is None else _f64(S0).reshape(B, H, dp, d)
+    z0 = None if z0 is None else _f64(z0).reshape(B, H, dp)
+    y = np.empty_like(v)
+    S = np.empty((B, H, dp, d), np.float64) if want_state else None
+    z = np.empty((B, H, dp), np.float64) if want_state else None
+    _load().hho_causal_features(d, dp, B * H, N, _ptr(phiq), _ptr(phik), _ptr(v), _ptr(S0), _ptr(z0), _ptr(y),
+                                _ptr(S), _ptr(z), nthreads or default_threads())
     return (y, S, z) if want_state else y
 
 
@@ -195,6 +227,28 @@ def prefix_state(map_: int, k, v, W=None, b=None, nthreads: Optional[int] = None
         S[bi] = np.matmul(phi.transpose(0, 2, 1), _f64(v[bi]))
         z[bi] = phi.sum(axis=1)
     return S, z
+
+
+def backward(map_: int, q, k, v, W=None, b=None, dy=None, causal: bool = True, nthreads: Optional[int] = None):
+    """Gradients of L = sum(dy * y) with y the forward of Eq. 2 (causal or bidirectional).
+
+    Written from the explicit form a_ij = phi(q_i).phi(k_j): dL/da_ij = dy_i.(v_j - y_i) / den_i,
+    then the chain rule through a_ij to the features and through the feature map to q, k and the
+    map's parameters (the gradients that training from scratch needs, section 3.4, "Training
+    Protocols for the Three Regimes").  Returns (dq, dk, dv [B,H,N,d], dW [H,d,d], db [H,d]);
+    dW and db sum over the batch, the tokens and both q and k (None for the Taylor map; db None
+    for the maps without a bias)."""
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    B, H, N, d = q.shape
+    W, b = _params(map_, W, b, H, d)
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    dWp = np.empty((B, H, d, d), np.float64)
+    dbp = np.empty((B, H, d), np.float64)
+    _load().hho_backward(map_, d, B, H, N, int(bool(causal)), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(b),
+                         _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dWp), _ptr(dbp), nthreads or default_threads())
+    dW = None if map_ == MAP_TAYLOR2 else dWp.sum(axis=0)
+    db = dbp.sum(axis=0) if map_ in (MAP_HEDGEHOG, MAP_EXP) else None
+    return dq, dk, dv, dW, db
 
 
 def distill_loss(map_: int, q, k, W=None, b=None, rows=None, nthreads: Optional[int] = None) -> np.ndarray:

@@ -46,10 +46,14 @@
 
 #define HHO_HEDGEHOG 0
 #define HHO_TAYLOR2 1
+#define HHO_HEDGEHOG_SOFTMAX 2
+#define HHO_EXP 3
+#define HHO_SOFTMAX 4
 
 int hho_feature_dim(int map, int d) {
-    if (map == HHO_HEDGEHOG) return 2 * d;
+    if (map == HHO_HEDGEHOG || map == HHO_HEDGEHOG_SOFTMAX) return 2 * d;
     if (map == HHO_TAYLOR2) return 1 + d + d * d;
+    if (map == HHO_EXP || map == HHO_SOFTMAX) return d;
     return -1;
 }
 
@@ -73,9 +77,47 @@ static void phi_taylor(int d, const double *x, double *out) {
         for (int c = 0; c < d; c++) out[1 + d + (size_t)a * d + c] = x[a] * x[c] * r;
 }
 
+/* Single-sided exponential map (Choice 1, the default d' = d): phi_l = exp(w_l.x + b_l). */
+static void phi_exp(int d, const double *x, const double *W, const double *b, double *out) {
+    for (int l = 0; l < d; l++) {
+        double u = b ? b[l] : 0.0;
+        for (int m = 0; m < d; m++) u += W[(size_t)l * d + m] * x[m];
+        out[l] = exp(u);
+    }
+}
+
+/* Softmax over the d feature directions (Choice 4, no bias): out_l = exp(s u_l) / sum_i exp(s u_i)
+ * with u = W x and sign s = +1 or -1.  Evaluated with the largest s u_i subtracted first (the
+ * same value). */
+static void softmax_dirs(int d, const double *x, const double *W, double sgn, double *out) {
+    double mx = -INFINITY;
+    for (int l = 0; l < d; l++) {
+        double u = 0.0;
+        for (int m = 0; m < d; m++) u += W[(size_t)l * d + m] * x[m];
+        out[l] = sgn * u;
+        if (out[l] > mx) mx = out[l];
+    }
+    double sum = 0.0;
+    for (int l = 0; l < d; l++) {
+        out[l] = exp(out[l] - mx);
+        sum += out[l];
+    }
+    for (int l = 0; l < d; l++) out[l] /= sum;
+}
+
 static void phi_one(int map, int d, const double *x, const double *W, const double *b, double *out) {
-    if (map == HHO_HEDGEHOG) phi_hedgehog(d, x, W, b, out);
-    else phi_taylor(d, x, out);
+    switch (map) {
+    case HHO_HEDGEHOG: phi_hedgehog(d, x, W, b, out); break;
+    case HHO_TAYLOR2: phi_taylor(d, x, out); break;
+    case HHO_EXP: phi_exp(d, x, W, b, out); break;
+    case HHO_SOFTMAX: softmax_dirs(d, x, W, 1.0, out); break;
+    case HHO_HEDGEHOG_SOFTMAX:
+        /* Choice 4 with the negation mapping of Choice 3: one softmax over the d projections,
+         * one over their negations (each half sums to 1) */
+        softmax_dirs(d, x, W, 1.0, out);
+        softmax_dirs(d, x, W, -1.0, out + d);
+        break;
+    }
 }
 
 /* Feature map of ntok tokens of one head: x [ntok][d] -> phi [ntok][d']. */
@@ -83,6 +125,61 @@ void hho_featuremap_head(int map, int d, long ntok, const double *x, const doubl
                          double *phi) {
     int dp = hho_feature_dim(map, d);
     for (long t = 0; t < ntok; t++) phi_one(map, d, x + t * d, W, b, phi + t * dp);
+}
+
+/* Chain rule through one feature map: given x, the map's parameters and dL/dphi, add dL/dx to
+ * dx and (maps with parameters) dL/dW, dL/db to dW [d][d], db [d].
+ *   Hedgehog: u = W x + b, phi = [e^u, e^-u]: dL/du_l = dphi_l e^u_l - dphi_{d+l} e^-u_l.
+ *   exp (single-sided): dL/du_l = dphi_l e^u_l.
+ *   softmax over directions p = softmax(s u), u = W x: dL/du = s p (dphi - <dphi, p>); the
+ *   two-sided softmax map adds its s = +1 and s = -1 halves.
+ *   Taylor: phi = [1, x_m, x_a x_c / sqrt 2]: dL/dx_m = dphi_{1+m} + sum_c (dphi_{mc} + dphi_{cm}) x_c / sqrt 2.
+ * Then dx = W^T du, dW += du x^T, db += du. */
+static void phi_backward(int map, int d, const double *x, const double *W, const double *b, const double *dphi,
+                         double *dx, double *dW, double *db) {
+    if (map == HHO_TAYLOR2) {
+        const double r = 1.0 / sqrt(2.0);
+        for (int m = 0; m < d; m++) {
+            double g = dphi[1 + m];
+            for (int c = 0; c < d; c++)
+                g += (dphi[1 + d + (size_t)m * d + c] + dphi[1 + d + (size_t)c * d + m]) * x[c] * r;
+            dx[m] += g;
+        }
+        return;
+    }
+    double *u = malloc(sizeof(double) * d), *du = malloc(sizeof(double) * d), *p = malloc(sizeof(double) * d);
+    const int with_b = map == HHO_HEDGEHOG || map == HHO_EXP;
+    for (int l = 0; l < d; l++) {
+        double a = (with_b && b) ? b[l] : 0.0;
+        for (int m = 0; m < d; m++) a += W[(size_t)l * d + m] * x[m];
+        u[l] = a;
+        du[l] = 0.0;
+    }
+    if (map == HHO_HEDGEHOG) {
+        for (int l = 0; l < d; l++) du[l] = dphi[l] * exp(u[l]) - dphi[d + l] * exp(-u[l]);
+    } else if (map == HHO_EXP) {
+        for (int l = 0; l < d; l++) du[l] = dphi[l] * exp(u[l]);
+    } else {
+        const int halves = map == HHO_HEDGEHOG_SOFTMAX ? 2 : 1;
+        for (int hf = 0; hf < halves; hf++) {
+            const double sgn = hf == 0 ? 1.0 : -1.0;
+            softmax_dirs(d, x, W, sgn, p);
+            const double *dp_ = dphi + (size_t)hf * d;
+            double dot = 0.0;
+            for (int l = 0; l < d; l++) dot += dp_[l] * p[l];
+            for (int l = 0; l < d; l++) du[l] += sgn * p[l] * (dp_[l] - dot);
+        }
+    }
+    for (int m = 0; m < d; m++) {
+        double g = 0.0;
+        for (int l = 0; l < d; l++) g += W[(size_t)l * d + m] * du[l];
+        dx[m] += g;
+    }
+    for (int l = 0; l < d; l++) {
+        for (int m = 0; m < d; m++) dW[(size_t)l * d + m] += du[l] * x[m];
+        if (with_b) db[l] += du[l];
+    }
+    free(u); free(du); free(p);
 }
 
 /* ---- one (batch, head) sequence ------------------------------------------ */
@@ -123,6 +220,36 @@ static void causal_one(int map, int d, long N, const double *q, const double *k,
     if (S_out) memcpy(S_out, S, sizeof(double) * dp * d);
     if (z_out) memcpy(z_out, z, sizeof(double) * dp);
     free(S); free(z); free(f); free(g); free(num);
+}
+
+/* Causal attention by running sums from given features: the same recurrence as causal_one
+ * with f = phik[i] and g = phiq[i] ([N][d'] each) instead of the feature map. */
+static void causal_feat_one(int d, int dp, long N, const double *phiq, const double *phik, const double *v,
+                            const double *S0, const double *z0, double *y, double *S_out, double *z_out) {
+    double *S = calloc((size_t)dp * d, sizeof(double));
+    double *z = calloc((size_t)dp, sizeof(double));
+    double *num = malloc(sizeof(double) * d);
+    if (S0) memcpy(S, S0, sizeof(double) * dp * d);
+    if (z0) memcpy(z, z0, sizeof(double) * dp);
+    for (long i = 0; i < N; i++) {
+        const double *f = phik + (size_t)i * dp, *g = phiq + (size_t)i * dp, *vi = v + i * d;
+        for (int a = 0; a < dp; a++) {
+            double *Sa = S + (size_t)a * d;
+            for (int c = 0; c < d; c++) Sa[c] += f[a] * vi[c];
+            z[a] += f[a];
+        }
+        double den = 0.0;
+        for (int c = 0; c < d; c++) num[c] = 0.0;
+        for (int a = 0; a < dp; a++) {
+            const double *Sa = S + (size_t)a * d;
+            for (int c = 0; c < d; c++) num[c] += g[a] * Sa[c];
+            den += g[a] * z[a];
+        }
+        for (int c = 0; c < d; c++) y[i * d + c] = num[c] / den;
+    }
+    if (S_out) memcpy(S_out, S, sizeof(double) * dp * d);
+    if (z_out) memcpy(z_out, z, sizeof(double) * dp);
+    free(S); free(z); free(num);
 }
 
 /* Bidirectional attention: S and z summed over every key, then each query reads them. */
@@ -180,6 +307,61 @@ static void quadratic_rows_one(int map, int d, long N, int causal, const double 
         for (int c = 0; c < d; c++) y[r * d + c] = num[c] / den;
     }
     free(g); free(f); free(num);
+}
+
+/* Gradients of L = sum_i dy_i . y_i through Eq. 2, from its explicit form: with
+ * a_ij = phi(q_i).phi(k_j) over the keys query i sees (j <= i, or all j), den_i = sum_j a_ij and
+ * y_i = sum_j a_ij v_j / den_i, the chain rule gives
+ *   dL/da_ij = dy_i . (v_j - y_i) / den_i,
+ *   dL/dphi(q_i) = sum_j dL/da_ij phi(k_j),   dL/dphi(k_j) = sum_i dL/da_ij phi(q_i),
+ *   dL/dv_j = sum_i (a_ij / den_i) dy_i,
+ * then phi_backward takes dL/dphi to dL/dq, dL/dk and the parameters.  dq, dk, dv [N][d] are
+ * written; dW [d][d] and db [d] are accumulated (they sum over every token and both q and k). */
+static void backward_one(int map, int d, long N, int causal, const double *q, const double *k, const double *v,
+                         const double *W, const double *b, const double *dy, double *dq, double *dk, double *dv,
+                         double *dW, double *db) {
+    const int dp = hho_feature_dim(map, d);
+    double *fq = malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * dp);
+    double *fk = malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * dp);
+    double *dfq = calloc((size_t)(N > 0 ? N : 1) * dp, sizeof(double));
+    double *dfk = calloc((size_t)(N > 0 ? N : 1) * dp, sizeof(double));
+    double *a = malloc(sizeof(double) * (N > 0 ? N : 1));
+    double *y = malloc(sizeof(double) * d);
+    for (long t = 0; t < N; t++) {
+        phi_one(map, d, q + t * d, W, b, fq + (size_t)t * dp);
+        phi_one(map, d, k + t * d, W, b, fk + (size_t)t * dp);
+    }
+    memset(dv, 0, sizeof(double) * N * d);
+    for (long i = 0; i < N; i++) {
+        const long jend = causal ? i + 1 : N;
+        double den = 0.0;
+        for (int c = 0; c < d; c++) y[c] = 0.0;
+        for (long j = 0; j < jend; j++) {
+            double s = 0.0;
+            for (int t = 0; t < dp; t++) s += fq[(size_t)i * dp + t] * fk[(size_t)j * dp + t];
+            a[j] = s;
+            den += s;
+            for (int c = 0; c < d; c++) y[c] += s * v[j * d + c];
+        }
+        for (int c = 0; c < d; c++) y[c] /= den;
+        for (long j = 0; j < jend; j++) {
+            double tij = 0.0;
+            for (int c = 0; c < d; c++) tij += dy[i * d + c] * (v[j * d + c] - y[c]);
+            tij /= den;
+            for (int t = 0; t < dp; t++) {
+                dfq[(size_t)i * dp + t] += tij * fk[(size_t)j * dp + t];
+                dfk[(size_t)j * dp + t] += tij * fq[(size_t)i * dp + t];
+            }
+            for (int c = 0; c < d; c++) dv[j * d + c] += a[j] / den * dy[i * d + c];
+        }
+    }
+    memset(dq, 0, sizeof(double) * N * d);
+    memset(dk, 0, sizeof(double) * N * d);
+    for (long t = 0; t < N; t++) {
+        phi_backward(map, d, q + t * d, W, b, dfq + (size_t)t * dp, dq + t * d, dW, db);
+        phi_backward(map, d, k + t * d, W, b, dfk + (size_t)t * dp, dk + t * d, dW, db);
+    }
+    free(fq); free(fk); free(dfq); free(dfk); free(a); free(y);
 }
 
 /* Distillation loss of the listed query rows (all rows when rows == NULL), directly from Eq. 4:
@@ -244,11 +426,12 @@ static void decode_one(int map, int d, const double *q, const double *k, const d
 /* ---- batched entry points: B*H independent sequences, threads over them ---- */
 
 typedef struct {
-    int op;        /* 0 causal, 1 bidirectional, 2 decode, 3 quadratic rows, 4 featuremap, 5 distillation loss */
-    int map, d, H, causal;
+    int op;        /* 0 causal, 1 bidirectional, 2 decode, 3 quadratic rows, 4 featuremap, 5 distillation loss,
+                      6 causal from given features, 7 backward */
+    int map, d, dp, H, causal;
     long BH, N;
-    const double *q, *k, *v, *W, *b, *S0, *z0;
-    double *y, *S_out, *z_out;
+    const double *q, *k, *v, *W, *b, *S0, *z0, *dy;
+    double *y, *S_out, *z_out, *dq, *dk, *dv, *dW, *db;
     long nrows;
     const long *rows;
     long next;     /* shared work counter */
@@ -259,8 +442,10 @@ static void run_pair(job_t *j, long p) {
     int d = j->d;
     int dp = hho_feature_dim(j->map, d);
     long h = p % j->H;
-    const double *W = j->map == HHO_HEDGEHOG ? j->W + (size_t)h * d * d : NULL;
-    const double *b = (j->map == HHO_HEDGEHOG && j->b) ? j->b + (size_t)h * d : NULL;
+    const int has_W = j->map != HHO_TAYLOR2;
+    const int has_b = j->map == HHO_HEDGEHOG || j->map == HHO_EXP;
+    const double *W = has_W ? j->W + (size_t)h * d * d : NULL;
+    const double *b = (has_b && j->b) ? j->b + (size_t)h * d : NULL;
     size_t seq = (size_t)j->N * d;
     switch (j->op) {
     case 0:
@@ -282,6 +467,17 @@ static void run_pair(job_t *j, long p) {
         break;
     case 4:
         hho_featuremap_head(j->map, d, j->N, j->q + p * seq, W, b, j->y + (size_t)p * j->N * dp);
+        break;
+    case 6:
+        causal_feat_one(d, j->dp, j->N, j->q + p * j->N * j->dp, j->k + p * j->N * j->dp, j->v + p * seq,
+                        j->S0 ? j->S0 + (size_t)p * j->dp * d : NULL, j->z0 ? j->z0 + (size_t)p * j->dp : NULL,
+                        j->y + p * seq, j->S_out ? j->S_out + (size_t)p * j->dp * d : NULL,
+                        j->z_out ? j->z_out + (size_t)p * j->dp : NULL);
+        break;
+    case 7:  /* per-pair parameter gradients: dW [BH][d][d], db [BH][d] (summed by the caller) */
+        backward_one(j->map, d, j->N, j->causal, j->q + p * seq, j->k + p * seq, j->v + p * seq, W, b,
+                     j->dy + p * seq, j->dq + p * seq, j->dk + p * seq, j->dv + p * seq,
+                     j->dW + (size_t)p * d * d, j->db + (size_t)p * d);
         break;
     case 5:
         distill_rows_one(j->map, d, j->N, j->q + p * seq, j->k + p * seq, W, b, j->nrows, j->rows,
@@ -380,5 +576,33 @@ void hho_distill(int map, int d, long B, long H, long N, const double *q, const 
     memset(&j, 0, sizeof j);
     j.op = 5; j.map = map; j.d = d; j.H = (int)H; j.BH = B * H; j.N = N;
     j.q = q; j.k = k; j.W = W; j.b = b; j.y = loss; j.nrows = nrows; j.rows = rows;
+    run_job(&j, nthreads);
+}
+
+/* Causal Eq. 2 from given features: phiq, phik [B*H][N][dp], v, y [B*H][N][d]; optional
+ * S0/S_out [B*H][dp][d], z0/z_out [B*H][dp]. */
+void hho_causal_features(int d, int dp, long BH, long N, const double *phiq, const double *phik, const double *v,
+                         const double *S0, const double *z0, double *y, double *S_out, double *z_out,
+                         int nthreads) {
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.op = 6; j.d = d; j.dp = dp; j.H = 1; j.BH = BH; j.N = N;
+    j.q = phiq; j.k = phik; j.v = v; j.S0 = S0; j.z0 = z0;
+    j.y = y; j.S_out = S_out; j.z_out = z_out;
+    run_job(&j, nthreads);
+}
+
+/* Backward of the forward (causal or bidirectional): q, k, v, dy, dq, dk, dv [B*H][N][d];
+ * dW [B*H][d][d] and db [B*H][d] receive each sequence's parameter gradient (zeroed here). */
+void hho_backward(int map, int d, long B, long H, long N, int causal, const double *q, const double *k,
+                  const double *v, const double *W, const double *b, const double *dy, double *dq, double *dk,
+                  double *dv, double *dW, double *db, int nthreads) {
+    job_t j;
+    memset(&j, 0, sizeof j);
+    memset(dW, 0, sizeof(double) * B * H * d * d);
+    memset(db, 0, sizeof(double) * B * H * d);
+    j.op = 7; j.map = map; j.d = d; j.H = (int)H; j.BH = B * H; j.N = N; j.causal = causal;
+    j.q = q; j.k = k; j.v = v; j.W = W; j.b = b; j.dy = dy;
+    j.dq = dq; j.dk = dk; j.dv = dv; j.dW = dW; j.db = db;
     run_job(&j, nthreads);
 }
