@@ -113,6 +113,18 @@ def recorded_traffic(workload: str, decode: bool = False):
     return int(m.group(1))
 
 
+def host_cpu_model() -> str:
+    """Model name of the host CPU (from /proc/cpuinfo), for the CPU-baseline record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device-to-device copy of known size, profiled to scale the HBM byte counters."""
     import torch
@@ -285,8 +297,10 @@ def main():
 
     tokens = w.B * (1 if decode else w.N)
     value = tokens / (ms_per_step * 1e-3)
-    ach_gbs = byts / (launch_ms * 1e-3) / 1e9
-    ach_tflops = flops / (launch_ms * 1e-3) / 1e12
+    # achieved rates over the whole timed region (the same clock as `value`); the mean of the
+    # per-launch events is reported beside them
+    ach_gbs = byts / (ms_per_step * 1e-3) / 1e9
+    ach_tflops = flops / (ms_per_step * 1e-3) / 1e12
     ai = flops / byts
     ridge = PEAK_MFMA_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     bound = "hbm" if ai < ridge else "mfma"
@@ -294,7 +308,7 @@ def main():
         traffic = recorded_traffic(args.workload, decode)
         roof = {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach_gbs / PEAK_HBM_GBS, 4),
-                "traffic": None if traffic is None else round(traffic / (launch_ms * 1e-3) / 1e9, 1)}
+                "traffic": None if traffic is None else round(traffic / (ms_per_step * 1e-3) / 1e9, 1)}
     else:
         roof = {"bound": "mfma", "achieved": round(ach_tflops, 1), "peak": PEAK_MFMA_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach_tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None}
@@ -319,6 +333,7 @@ def main():
     roof["mfma_frac_of_bf16_peak"] = round(ach_tflops / PEAK_MFMA_BF16_TFLOPS, 4)
 
     cpu = None
+    cpu_model = host_cpu_model()
     if not args.no_cpu_baseline and distill:
         import oracle
         nthr = oracle.default_threads()
@@ -333,10 +348,18 @@ def main():
             tc += time.perf_counter() - t0
             rows_done += len(rows) * w.B
             rnd += 1
+        # the same rows once more on one thread
+        rows = [int((w.N - 1) * (j + 0.5) / 16) for j in range(16)]
+        t0 = time.perf_counter()
+        oracle.distill_loss(w.map, xw["q"], xw["k"], xw["W"], xw["b"], rows=rows, nthreads=1)
+        t1 = time.perf_counter() - t0
         cpu = {"value": round(rows_done / tc, 1), "unit": "tokens/s", "cores": nthr, "kind": "oracle",
                "sample": f"{rnd} rounds of 16 query rows per head (all {w.H} heads, rows spread over the sequence) "
                          f"of {w.name} (B{w.B} H{w.H} N{w.N} d{w.d}) by the fp64 oracle, {tc:.2f} s wall on "
-                         f"{nthr} threads"}
+                         f"{nthr} threads",
+               "cpu_model": cpu_model,
+               "value_1_thread": round(len(rows) * w.B / t1, 2),
+               "sample_1_thread": f"one round of 16 query rows per head on 1 thread, {t1:.2f} s wall"}
     elif not args.no_cpu_baseline and not decode:
         import oracle
         nthr = oracle.default_threads()
@@ -351,9 +374,19 @@ def main():
                 oracle.bidir(w.map, xw["q"], xw["k"], xw["v"], xw["W"], xw["b"], nthreads=nthr)
             tc += time.perf_counter() - t0
             reps += 1
+        # one whole forward on a single thread
+        t0 = time.perf_counter()
+        if w.causal:
+            oracle.causal(w.map, xw["q"], xw["k"], xw["v"], xw["W"], xw["b"], nthreads=1)
+        else:
+            oracle.bidir(w.map, xw["q"], xw["k"], xw["v"], xw["W"], xw["b"], nthreads=1)
+        t1 = time.perf_counter() - t0
         cpu = {"value": round(reps * tokens / tc, 1), "unit": "tokens/s", "cores": nthr, "kind": "oracle",
                "sample": f"{reps} full forwards of {w.name} (B{w.B} H{w.H} N{w.N} d{w.d}) by the fp64 oracle, "
-                         f"{tc:.2f} s wall on {nthr} threads"}
+                         f"{tc:.2f} s wall on {nthr} threads",
+               "cpu_model": cpu_model,
+               "value_1_thread": round(tokens / t1, 1),
+               "sample_1_thread": f"one full forward on 1 thread, {t1:.2f} s wall"}
 
     out = {
         "metric": (METRIC if w.name == "c3_llama2_causal" else

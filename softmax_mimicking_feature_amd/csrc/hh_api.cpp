@@ -94,8 +94,8 @@ struct Plan {
     size_t ws_bytes = 0;
 };
 
-// Bytes of the bf16 S part of the wide kernels' segment slots (a multiple of 16).
-size_t wide_slot_S_bytes(long BH, long nseg, int d) { return (size_t)BH * nseg * 2 * d * d * sizeof(uint16_t); }
+// Bytes of the fp32 S part of the wide kernels' segment slots (a multiple of 16).
+size_t wide_slot_S_bytes(long BH, long nseg, int d) { return (size_t)BH * nseg * 2 * d * d * sizeof(float); }
 
 Plan make_plan(int map, int dtype, int causal, long BH, long N, int d, bool has_S0) {
     Plan pl;
@@ -290,16 +290,16 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
     const int out_mode = causal ? 1 : 2;
 
     if (!pl.narrow) {
-        // Segment slots: bf16 S in the kernels' register-image layout, fp32 z.  The scan between
+        // Segment slots: fp32 S in the kernels' register-image layout, fp32 z.  The scan between
         // the passes never sees S0; a caller's S0 is read directly by every segment.
         hh::WideParams wp;
         memset(&wp, 0, sizeof wp);
         wp.q = (const hh::bf16_t *)q; wp.k = (const hh::bf16_t *)k; wp.v = (const hh::bf16_t *)v;
         wp.W = (const hh::bf16_t *)W; wp.b = (const hh::bf16_t *)b; wp.y = (hh::bf16_t *)y;
-        hh::bf16_t *slS = nullptr;
+        float *slS = nullptr;
         float *slZ = nullptr;
         if (pl.need_ws) {
-            slS = reinterpret_cast<hh::bf16_t *>(workspace);
+            slS = reinterpret_cast<float *>(workspace);
             slZ = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + wide_slot_S_bytes(BH, pl.nseg, d));
         }
         wp.S_slots = slS; wp.z_slots = slZ; wp.slot_bh_stride = pl.nseg;

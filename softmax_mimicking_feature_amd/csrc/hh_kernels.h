@@ -16,8 +16,8 @@ struct WideParams {
     const float *S_in, *z_in;   // starting state (internal row order), or null = zero
     long in_bh_stride;          // slots per (b,h) in S_in
     long in_seg_stride;         // slots per segment in S_in (0: one slot shared by all segments)
-    bf16_t *S_slots;            // segment slots: S in bf16, in the register-image layout of the
-    float *z_slots;             //   wide kernel; z in fp32, feature order
+    float *S_slots;             // segment slots: S in fp32, in the register-image layout of the
+    float *z_slots;             //   kernel that reads them back; z in fp32, feature order
     long slot_bh_stride;        // slots per (b,h)
     float *S_out, *z_out;       // final state (mode 1, last segment), or null
     int N, H, nseg_grid, seg_len;
@@ -26,10 +26,10 @@ struct WideParams {
                                 //   3 the sum of slots 0 .. s - 1 (segment aggregates, summed by the
                                 //   causal pass itself; no scan)
 };
-// Segment slots of the wide kernels: per (b,h), nseg slots of S (2 d * d bf16) and z
+// Segment slots of the wide kernels: per (b,h), nseg slots of S (2 d * d floats) and z
 // (2 d floats).  Mode 0: aggregates of slots 0 .. nseg-2 become exclusive prefixes in slots
 // 1 .. nseg-1; mode 1: the total of all nseg slots goes to slot 0.  Sums run in fp32.
-hipError_t launch_slot_scan(int d, bf16_t *S_slots, float *z_slots, int BH, int nseg, int mode, hipStream_t st);
+hipError_t launch_slot_scan(int d, float *S_slots, float *z_slots, int BH, int nseg, int mode, hipStream_t st);
 hipError_t launch_wide(int d, int mode, const WideParams &p, int grid, hipStream_t st);
 // Bidirectional forward with one segment per sequence (d = 64): state and read-out in one
 // workgroup per sequence, the total state handed over in LDS (no workspace).

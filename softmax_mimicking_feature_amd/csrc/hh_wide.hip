@@ -62,7 +62,7 @@ struct WideCfg {
     static constexpr int KSW = FBW / 2;               // read-out K steps per wave
     static constexpr int ZB = FB / NW;                // z-row blocks per wave
     static constexpr int IBF = NCB / NF;              // output row blocks finalised per wave
-    static constexpr int IMG8 = FBW * VB / 2;         // bf16x8 pieces of a segment slot per lane
+    static constexpr int IMG8 = FBW * VB / 2;         // accumulator pairs of a segment slot per lane
     static constexpr int NJ = (NW == 8) ? 2 : 1;      // intra-chunk row-sum slots
     // Staging buffers for the raw inputs.  With two (one workgroup per CU), q, k and V of the
     // next chunk are fetched straight into LDS a whole chunk ahead; with one (two workgroups
@@ -126,6 +126,17 @@ __device__ __forceinline__ void wg_head_segment(int nseg, int &bh, int &s) {
         bh = b / nseg;
         s = b % nseg;
     }
+}
+
+// Segment slots keep S in fp32 in the register image of the kernel that reads them back:
+// the two accumulators (halves h = 0, 1) that lane L of a wave holds as piece e are stored as
+// f32x4 at index (2 e + h) 64 + L, so that each wave instruction writes or reads one contiguous
+// kilobyte.  The aggregates are carried between segments without any rounding.
+__device__ __forceinline__ f32x4 *slot_piece(float *S, int e, int h, int L) {
+    return reinterpret_cast<f32x4 *>(S) + (2 * e + h) * 64 + L;
+}
+__device__ __forceinline__ const f32x4 *slot_piece(const float *S, int e, int h, int L) {
+    return reinterpret_cast<const f32x4 *>(S) + (2 * e + h) * 64 + L;
 }
 
 // Position of feature f in a row-major feature tile.  With PERM, each 32-feature group is
@@ -778,9 +789,9 @@ __device__ __forceinline__ void wide_body(const WideParams &p, unsigned char *sm
 
     // State: S[f][n] for feature blocks fa*FBW .. and this wave's value columns; z rows of
     // feature blocks w*ZB .. (every column of the z accumulator holds the same value).
-    // Segment slots in the workspace hold S in bf16 in the register image of this layout:
-    // accumulators k = fb VB + vb of lane `lane` in wave w are paired, the pair j = k / 2 being the
-    // bf16x8 at index (w IMG8 + j) 64 + lane, so that reading and writing a slot are whole 1 KB
+    // Segment slots in the workspace hold S in fp32 in the register image of this layout:
+    // accumulators k = fb VB + vb of lane `lane` in wave w are paired, the pair j = k / 2 being
+    // slot piece w IMG8 + j (halves k0, k1), so that reading and writing a slot are whole 1 KB
     // rows per instruction.
     f32x4 sacc[K::FBW][K::VB];
     f32x4 zacc[K::ZB];
@@ -819,10 +830,12 @@ __device__ __forceinline__ void wide_body(const WideParams &p, unsigned char *sm
         if (MODE != WM_STATE && p.slot_mode == 3) t0 = 0, t1 = s;
         for (int slot = t0; slot < t1; slot++) {
             const size_t sl = (size_t)bh * p.slot_bh_stride + slot;
-            const bf16x8 *img = reinterpret_cast<const bf16x8 *>(p.S_slots + sl * K::DP * D) + w * K::IMG8 * 64 + lane;
-            bf16x8 t[K::IMG8];
+            const float *img = p.S_slots + sl * K::DP * D;
+            f32x4 t[K::IMG8][2];
 #pragma unroll
-            for (int j = 0; j < K::IMG8; j++) t[j] = img[j * 64];
+            for (int j = 0; j < K::IMG8; j++)
+#pragma unroll
+                for (int hf = 0; hf < 2; hf++) t[j][hf] = *slot_piece(img, w * K::IMG8 + j, hf, lane);
             const float *zs = p.z_slots + sl * K::DP;
 #pragma unroll
             for (int zb = 0; zb < K::ZB; zb++)
@@ -831,11 +844,8 @@ __device__ __forceinline__ void wide_body(const WideParams &p, unsigned char *sm
 #pragma unroll
             for (int j = 0; j < K::IMG8; j++) {
                 const int k0 = 2 * j, k1 = 2 * j + 1;
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    sacc[k0 / K::VB][k0 % K::VB][r] += (float)t[j][r];
-                    sacc[k1 / K::VB][k1 % K::VB][r] += (float)t[j][4 + r];
-                }
+                sacc[k0 / K::VB][k0 % K::VB] += t[j][0];
+                sacc[k1 / K::VB][k1 % K::VB] += t[j][1];
             }
         }
     }
@@ -887,11 +897,12 @@ __device__ __forceinline__ void wide_body(const WideParams &p, unsigned char *sm
     //      (CAUSAL, last segment, feature-major)
     if (MODE == WM_STATE) {
         const size_t slot = (size_t)bh * p.slot_bh_stride + s;
-        bf16x8 *img = reinterpret_cast<bf16x8 *>(p.S_slots + slot * K::DP * D) + w * K::IMG8 * 64 + lane;
+        float *img = p.S_slots + slot * K::DP * D;
 #pragma unroll
         for (int j = 0; j < K::IMG8; j++) {
             const int k0 = 2 * j, k1 = 2 * j + 1;
-            img[j * 64] = cat(to_bf16x4(sacc[k0 / K::VB][k0 % K::VB]), to_bf16x4(sacc[k1 / K::VB][k1 % K::VB]));
+            *slot_piece(img, w * K::IMG8 + j, 0, lane) = sacc[k0 / K::VB][k0 % K::VB];
+            *slot_piece(img, w * K::IMG8 + j, 1, lane) = sacc[k1 / K::VB][k1 % K::VB];
         }
         float *zs = p.z_slots + slot * K::DP;
         if (r16 == 0) {
@@ -1136,27 +1147,31 @@ __device__ __forceinline__ void state_sym_body(const WideParams &p, unsigned cha
 
     // Slot s in the register image the chunked pass of the same d reads back.
     const size_t slot = (size_t)bh * p.slot_bh_stride + s;
-    bf16x4 *img = reinterpret_cast<bf16x4 *>(p.S_slots + slot * S::DP * D);
+    float *img = p.S_slots + slot * S::DP * D;
 #pragma unroll
     for (int f = 0; f < 2; f++)
 #pragma unroll
         for (int vb = 0; vb < S::VB; vb++) {
-            int e2;  // index of the 8-byte half that holds these four values
+            int e, hf, L;  // piece, half and lane of the reader that holds these four values
             if (D == 128) {
-                // causal_ws_kernel_128: entry ((4 fa + pv) 8 + j) 64 + lane of bf16x8, lane (g, c)
-                // holding rows 16 (8 fa + j) + 4 g + r, value columns value_col<2>(pv, h, c) in halves
-                // h.  Value column 16 vb + r16 is in entry pv = vb / 2 at c = 4 (m / 8) + m % 4,
-                // half (m / 4) % 2, with m = 16 (vb % 2) + r16; here fa = f, j = w.
+                // causal_ws_kernel_128: piece (4 fa + pv) 8 + j of lane (g, c), holding rows
+                // 16 (8 fa + j) + 4 g + r, value columns value_col<2>(pv, h, c) in halves h.  Value
+                // column 16 vb + r16 is in piece pv = vb / 2 at c = 4 (m / 8) + m % 4, half (m / 4) % 2,
+                // with m = 16 (vb % 2) + r16; here fa = f, j = w.
                 const int m = 16 * (vb & 1) + r16;
-                e2 = 2 * (((4 * f + (vb >> 1)) * 8 + w) * 64 + 16 * g + 4 * (m >> 3) + (m & 3)) + ((m >> 2) & 1);
+                e = (4 * f + (vb >> 1)) * 8 + w;
+                L = 16 * g + 4 * (m >> 3) + (m & 3);
+                hf = (m >> 2) & 1;
             } else {
-                // wide_kernel<64>: entry (wv 4 + j) 64 + lane of bf16x8, wave wv owning value block
-                // wv, lane (g, r16) holding rows 16 (2 j) + 4 g + r and 16 (2 j + 1) + 4 g + r of
-                // value column 16 wv + r16 in its halves; here the feature block is 4 f + w.
+                // wide_kernel<64>: piece wv 4 + j of lane (g, r16), wave wv owning value block wv,
+                // holding rows 16 (2 j) + 4 g + r and 16 (2 j + 1) + 4 g + r of value column
+                // 16 wv + r16 in its halves; here the feature block is 4 f + w.
                 const int fb = 4 * f + w;
-                e2 = 2 * ((vb * 4 + (fb >> 1)) * 64 + 16 * g + r16) + (fb & 1);
+                e = vb * 4 + (fb >> 1);
+                L = 16 * g + r16;
+                hf = fb & 1;
             }
-            img[e2] = to_bf16x4(sacc[f][vb]);
+            *slot_piece(img, e, hf, L) = sacc[f][vb];
         }
     float *zs = p.z_slots + slot * S::DP;
     if (r16 == 0) {
@@ -1181,25 +1196,26 @@ __global__ __launch_bounds__(StateSymCfg<D>::NT, StateSymCfg<D>::WG_PER_CU) void
 // of a workspace slot in memory that a second kernel reads back.
 template <int D>
 struct BidirFusedCfg {
-    static constexpr int TILES = StateSymCfg<D>::LDS_BYTES > WideCfg<D, 64, WM_READOUT>::LDS_BYTES
-                                     ? StateSymCfg<D>::LDS_BYTES
-                                     : WideCfg<D, 64, WM_READOUT>::LDS_BYTES;
-    static constexpr int SLOT_S = 2 * D * D * 2;  // bf16 S image
+    static constexpr int SLOT_S = 2 * D * D * 4;  // fp32 S image
     static constexpr int SLOT_Z = 2 * D * 4;      // fp32 z
+    // The total lives after the read-out pass's tiles: the state pass writes it once its own tiles
+    // are consumed, and the read-out's first loads (q staging, W) do not reach it before the
+    // read-out has taken the total into registers.
+    static constexpr int OFF_SLOT = (WideCfg<D, 64, WM_READOUT>::LDS_BYTES + 15) / 16 * 16;
+    static constexpr int END_SLOT = OFF_SLOT + SLOT_S + SLOT_Z;
+    static constexpr int TILES = StateSymCfg<D>::LDS_BYTES > END_SLOT ? StateSymCfg<D>::LDS_BYTES : END_SLOT;
     static_assert(StateSymCfg<D>::NT == WideCfg<D>::NT, "both passes use the same workgroup");
-    static_assert((TILES + SLOT_S + SLOT_Z) * 2 <= 160 * 1024, "two workgroups per CU");
+    static_assert(TILES * 2 <= 160 * 1024, "two workgroups per CU");
 };
 
 template <int D>
 __global__ __launch_bounds__(WideCfg<D>::NT, 2) void bidir_fused_kernel(WideParams p) {
     using F = BidirFusedCfg<D>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[F::TILES];
-    __shared__ __attribute__((aligned(16))) bf16_t slotS[F::SLOT_S / 2];
-    __shared__ __attribute__((aligned(16))) float slotZ[F::SLOT_Z / 4];
     const int bh = blockIdx.x;
     WideParams q = p;
-    q.S_slots = slotS;  // generic pointers to LDS: slot 0 of every sequence
-    q.z_slots = slotZ;
+    q.S_slots = reinterpret_cast<float *>(smem + F::OFF_SLOT);  // generic pointers to LDS: slot 0 of every sequence
+    q.z_slots = reinterpret_cast<float *>(smem + F::OFF_SLOT + F::SLOT_S);
     q.slot_bh_stride = 0;
     q.slot_mode = 2;
     state_sym_body<D>(q, smem, bh, 0);
@@ -1528,27 +1544,25 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
         for (int t = t0; t < t1; t++) {
             const size_t sl = (size_t)bh * p.slot_bh_stride + t;
             const float *zs = p.z_slots + sl * S::DP;
-            bf16x8 slot_raw[2][8];
+            const float *img = p.S_slots + sl * S::DP * S::D;
             f32x4 zslot[4];
 #pragma unroll
-            for (int fa = 0; fa < 2; fa++) {
-                const bf16x8 *img =
-                    reinterpret_cast<const bf16x8 *>(p.S_slots + sl * S::DP * S::D) + (4 * fa + pv) * 8 * 64 + lane;
-#pragma unroll
-                for (int j = 0; j < 8; j++) slot_raw[fa][j] = img[j * 64];
-            }
-#pragma unroll
             for (int zb = 0; zb < 4; zb++) zslot[zb] = *reinterpret_cast<const f32x4 *>(zs + 16 * (4 * pv + zb) + 4 * g);
-            __builtin_amdgcn_sched_barrier(0);  // all of the slot's loads in flight before the first sum
+            // the slot in two halves of 64 registers (the state itself holds 128)
 #pragma unroll
-            for (int fa = 0; fa < 2; fa++)
+            for (int fa = 0; fa < 2; fa++) {
+                f32x4 slot_raw[8][2];
 #pragma unroll
                 for (int j = 0; j < 8; j++)
 #pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        sacc[8 * fa + j][0][r] += (float)slot_raw[fa][j][r];
-                        sacc[8 * fa + j][1][r] += (float)slot_raw[fa][j][4 + r];
-                    }
+                    for (int hf = 0; hf < 2; hf++) slot_raw[j][hf] = *slot_piece(img, (4 * fa + pv) * 8 + j, hf, lane);
+                __builtin_amdgcn_sched_barrier(0);  // the half's loads in flight before its first sum
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    sacc[8 * fa + j][0] += slot_raw[j][0];
+                    sacc[8 * fa + j][1] += slot_raw[j][1];
+                }
+            }
 #pragma unroll
             for (int zb = 0; zb < 4; zb++)
 #pragma unroll
@@ -1769,37 +1783,29 @@ hipError_t launch_featuremap_hedgehog_bf16(int d, const bf16_t *x, const bf16_t 
     }
 }
 
-// Segment-slot scan (see launch_slot_scan): one thread per 8 bf16 of S or per z entry.
+// Segment-slot scan (see launch_slot_scan), in fp32: one thread per 4 floats of S or per z
+// entry.  The sum runs over the slots of one (b,h) in segment order; the slot layout does not
+// matter (every slot of a head has the same layout).
 template <int D>
-__global__ void slot_scan_kernel(bf16_t *__restrict__ S, float *__restrict__ z, int BH, int nseg, int mode) {
-    constexpr long PS = 2L * D * D / 8, PZ = 2L * D;
+__global__ void slot_scan_kernel(float *__restrict__ S, float *__restrict__ z, int BH, int nseg, int mode) {
+    constexpr long PS = 2L * D * D / 4, PZ = 2L * D;
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (long)BH * (PS + PZ)) return;
     const long bh = idx / (PS + PZ), e = idx % (PS + PZ);
+    const int nin = mode == 0 ? nseg - 1 : nseg;
     if (e < PS) {
-        constexpr long stride = 2L * D * D;
-        bf16_t *base = S + bh * nseg * stride + 8 * e;
-        float run[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        const int nin = mode == 0 ? nseg - 1 : nseg;
+        constexpr long stride = 2L * D * D / 4;
+        f32x4 *base = reinterpret_cast<f32x4 *>(S) + bh * nseg * stride + e;
+        f32x4 run = zero4();
         for (int s = 0; s < nin; s++) {
-            const bf16x8 a = load8(base + s * stride);
-            if (mode == 0 && s > 0) {
-                bf16x8 o;
-#pragma unroll
-                for (int i = 0; i < 8; i++) o[i] = (__bf16)run[i];
-                store8(base + s * stride, o);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; i++) run[i] += (float)a[i];
+            const f32x4 a = base[s * stride];
+            if (mode == 0 && s > 0) base[s * stride] = run;
+            run += a;
         }
-        bf16x8 o;
-#pragma unroll
-        for (int i = 0; i < 8; i++) o[i] = (__bf16)run[i];
-        store8(base + (mode == 0 ? (long)(nseg - 1) * stride : 0), o);
+        base[mode == 0 ? (long)(nseg - 1) * stride : 0] = run;
     } else {
         float *base = z + bh * nseg * PZ + (e - PS);
         float run = 0.0f;
-        const int nin = mode == 0 ? nseg - 1 : nseg;
         for (int s = 0; s < nin; s++) {
             const float a = base[s * PZ];
             if (mode == 0 && s > 0) base[s * PZ] = run;
@@ -1809,8 +1815,8 @@ __global__ void slot_scan_kernel(bf16_t *__restrict__ S, float *__restrict__ z, 
     }
 }
 
-hipError_t launch_slot_scan(int d, bf16_t *S_slots, float *z_slots, int BH, int nseg, int mode, hipStream_t st) {
-    const long total = (long)BH * (2L * d * d / 8 + 2L * d);
+hipError_t launch_slot_scan(int d, float *S_slots, float *z_slots, int BH, int nseg, int mode, hipStream_t st) {
+    const long total = (long)BH * (2L * d * d / 4 + 2L * d);
     const unsigned grid = (unsigned)((total + 255) / 256);
     switch (d) {
     case 16: hipLaunchKernelGGL(slot_scan_kernel<16>, dim3(grid), dim3(256), 0, st, S_slots, z_slots, BH, nseg, mode); break;

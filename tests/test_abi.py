@@ -88,8 +88,8 @@ def test_fwd_workspace_rules(lib):
     assert fwd(lib, H=32, N=4096, d=128, ws=0x70000000, ws_bytes=need - 16) == _lib.HH_EWORKSPACE
     assert "workspace" in lib.hh_last_error().decode()
     # bidirectional always needs one state slot per head; fp32 and empty inputs need none
-    # (a slot holds S in bf16 and z in fp32)
-    assert lib.hh_linattn_fwd_workspace(HOG, BF16, 0, 32, 12, 512, 64) >= 32 * 12 * (128 * 64 * 2 + 128 * 4)
+    # (a slot holds S and z in fp32)
+    assert lib.hh_linattn_fwd_workspace(HOG, BF16, 0, 32, 12, 512, 64) >= 32 * 12 * (128 * 64 * 4 + 128 * 4)
     assert lib.hh_linattn_fwd_workspace(HOG, F32, 1, 1, 1, 256, 16) == 0
     assert lib.hh_linattn_fwd_workspace(HOG, BF16, 1, 1, 1, 0, 16) == 0
     assert lib.hh_linattn_fwd_workspace(HOG, BF16, 1, 1, 1, 64, 48) == 0  # invalid -> 0

@@ -73,14 +73,30 @@ def test_distill_taylor(N):
 
 
 def test_distill_llama2_heads_sampled_rows():
-    # the Llama-2-7B head shapes at full length (B1 H32 N4096 d128); the oracle on sampled rows
+    # the Llama-2-7B head shapes at full length (B1 H32 N4096 d128); the oracle on sampled rows:
+    # both sides of every 64-row tile boundary, rows spread through the middle of the tiles, and
+    # for two heads every row of two 128-query workgroup tiles (all 8 waves x 16 lanes)
     w = wl.CONFIGS["c3_llama2_causal"]
     say("distill B1 H32 N4096 d128, sampled rows")
     x = wl.make_inputs(w)
     L = gpu_loss(w, x)
-    rows = [0, 63, 64, 2047, 4095]
-    check(L[:, :, rows], oracle_loss(w, x, rows=rows), "sampled rows")
+    rows = sorted({0, w.N - 1} | {r for t in range(1, w.N // 64) for r in (64 * t - 1, 64 * t)} |
+                  {64 * t + (17 * t + 5) % 64 for t in range(w.N // 64)})
+    assert len(rows) >= 128
+    check(L[:, :, rows], oracle_loss(w, x, rows=rows), f"{len(rows)} sampled rows per head")
+    full = list(range(1920, 2048)) + list(range(3968, 4096))
+    xs = {k_: (a[:, :2] if k_ in ("q", "k", "v") else a[:2]) for k_, a in x.items()}
+    check(L[:, :2, full], oracle_loss(w.replace(H=2), xs, rows=full), "two whole query tiles, heads 0-1")
     assert np.all(L >= -1e-3)  # a cross-entropy is never negative
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_distill_full_eight_heads(d):
+    # B*H a multiple of 8: the query tiles of each head are grouped on one XCD; every row compared
+    w = wl.CONFIGS["c3_llama2_causal"].replace(B=1, H=8, N=1000, d=d, w_std=d ** -0.5, seed=9650 + d)
+    say(f"distill B1 H8 N1000 d={d}, every row")
+    x = wl.make_inputs(w)
+    check(gpu_loss(w, x), oracle_loss(w, x), "loss")
 
 
 def test_distill_repeatable_bitwise():
