@@ -95,19 +95,23 @@ def bf16_feature_state(w, x):
     phik = round_(oracle.featuremap(w.map, x["k"], x["W"], x["b"]))
     phiq = round_(oracle.featuremap(w.map, x["q"], x["W"], x["b"]))
     _, S, z = oracle.causal_features(phiq, phik, x["v"], want_state=True)
-    return S, z
+    return S, z, float(np.abs(phik).max())
 
 
 def check_carried_state(w, x, S, z):
-    """fp32 carry: elementwise rtol 1e-3 with atol 1e-4 max|S| against the sums of the bf16
-    features, and normwise 1e-4 (a bf16 hand-off between segments is off by ~1e-3 normwise)."""
+    """fp32 carry: normwise 1e-4 against the sums of the bf16 features (a bf16 hand-off between
+    segments is off by ~1e-3 normwise).  Elementwise rtol 1e-3 plus an atol of one term of the
+    sum at two bf16 ulps (2^-7 max|phi(k)| max|v|): the kernels' fp32 features round to bf16 a
+    last bit differently from the oracle's fp64 features for a few keys in a million."""
     if not (w.map == wl.MAP_HEDGEHOG and w.dtype == wl.DT_BF16):
         return
-    Sb, zb = bf16_feature_state(w, x)
-    assert_close(host(S), Sb, 1e-3, 1e-4 * float(np.abs(Sb).max()), "S_out vs sums of bf16 features")
-    assert_close(host(z), zb, 1e-4, 0.0, "z_out vs sums of bf16 features")
-    nrm = np.linalg.norm(host(S) - Sb) / np.linalg.norm(Sb)
-    assert nrm <= 1e-4, nrm
+    Sb, zb, fmax = bf16_feature_state(w, x)
+    assert_close(host(S), Sb, 1e-3, 2.0 ** -7 * fmax * float(np.abs(x["v"]).max()), "S_out vs sums of bf16 features")
+    assert_close(host(z), zb, 1e-4, 2.0 ** -7 * fmax, "z_out vs sums of bf16 features")
+    for got, want, nm in ((host(S), Sb, "S"), (host(z), zb, "z")):
+        nrm = np.linalg.norm(got - want) / np.linalg.norm(want)
+        print(f"  {nm}_out normwise vs sums of bf16 features: {nrm:.3e}", flush=True)
+        assert nrm <= 1e-4, nrm
 
 
 def state_tol(w, S):
