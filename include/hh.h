@@ -107,6 +107,21 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
                            void *y, float *S_out, float *z_out,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* hh_linattn_fwd without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Arguments and results are those of hh_linattn_fwd.  The segment slots live in a scratch
+ * array that the library owns: 64 MiB per device, allocated when the library is loaded and held
+ * until the process ends.  A problem whose hh_linattn_fwd_workspace() exceeds that returns
+ * HH_EWORKSPACE with nothing enqueued.  This call allocates nothing.  Every call on one device
+ * shares that device's array: calls that overlap in time on one device (other streams, other
+ * threads) race on it and must be serialised by the caller; the array needs no clearing (each
+ * call writes every slot it later reads). */
+hh_status_t hh_linattn_fwd_noalloc(int map, int dtype, int causal, int B, int H, int N, int d,
+                                   const void *q, const void *k, const void *v,
+                                   const void *W, const void *b,
+                                   const float *S0, const float *z0,
+                                   void *y, float *S_out, float *z_out, void *stream);
+
 /* One recurrent decode step (running-sum update of section 3.4, "Complexity
  * Analysis"): for each (b, h), with f = phi(k), g = phi(q):
  *     S += f v^T;  z += f;  y = g^T S / g^T z     (update, then read: j <= i)

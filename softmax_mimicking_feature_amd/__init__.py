@@ -21,7 +21,7 @@ from . import _lib
 from ._lib import (HH_BF16, HH_EHIP, HH_EINVAL, HH_EUNSUPPORTED, HH_EWORKSPACE, HH_F32, HH_MAP_HEDGEHOG,
                    HH_MAP_TAYLOR2, HH_OK, LibraryMissing)
 
-__all__ = ["hh_feature_dim", "hh_featuremap", "hh_linattn_fwd_workspace", "hh_linattn_fwd",
+__all__ = ["hh_feature_dim", "hh_featuremap", "hh_linattn_fwd_workspace", "hh_linattn_fwd", "hh_linattn_fwd_noalloc",
            "hh_linattn_decode_step", "hh_distill_loss_workspace", "hh_distill_loss", "hh_status_str", "hh_last_error", "hh_abi_version", "HHError",
            "LibraryMissing", "HH_F32", "HH_BF16", "HH_MAP_HEDGEHOG", "HH_MAP_TAYLOR2", "HH_OK", "HH_EINVAL",
            "HH_EUNSUPPORTED", "HH_EWORKSPACE", "HH_EHIP"]
@@ -179,6 +179,50 @@ def hh_linattn_fwd(q, k, v, W=None, b=None, *, causal: bool = True, map: int = H
     _check(lib.hh_linattn_fwd(map, dt, int(bool(causal)), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(b),
                               _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_out), _ptr(z_out), _ptr(workspace), ws_bytes,
                               _stream(stream)))
+    if S_out is not None:
+        return out, S_out, z_out
+    return out
+
+
+def hh_linattn_fwd_noalloc(q, k, v, W=None, b=None, *, causal: bool = True, map: int = HH_MAP_HEDGEHOG, S0=None,
+                           z0=None, out=None, S_out=None, z_out=None, stream=None):
+    """hh_linattn_fwd with the library's own scratch instead of a workspace: allocates nothing
+    when `out` (and S_out, z_out if wanted) are given.  Returns out, or (out, S_out, z_out)."""
+    lib = _lib.load()
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B,H,N,d], got {list(q.shape)}")
+    B, H, N, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape [B,H,N,d]")
+    dp = lib.hh_feature_dim(map, d)
+    if dp < 0:
+        raise ValueError(f"invalid map/head dim ({map}, {d})")
+    if map == HH_MAP_HEDGEHOG:
+        if W is None:
+            raise ValueError("W is required for the Hedgehog map")
+        _shape(W, "W", (H, d, d))
+        _shape(b, "b", (H, d))
+    else:
+        W = b = None
+    _shape(out, "out", q.shape)
+    for t, nm in ((S0, "S0"), (S_out, "S_out")):
+        _shape(t, nm, (B, H, dp, d))
+    for t, nm in ((z0, "z0"), (z_out, "z_out")):
+        _shape(t, nm, (B, H, dp))
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, nm, q.dtype)
+    dt = _dtype_code(q)
+    _dev(W, "W", q.dtype)
+    _dev(b, "b", q.dtype)
+    for t, nm in ((S0, "S0"), (z0, "z0"), (S_out, "S_out"), (z_out, "z_out")):
+        _dev(t, nm, torch.float32)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    _check(lib.hh_linattn_fwd_noalloc(map, dt, int(bool(causal)), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(W),
+                                      _ptr(b), _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_out), _ptr(z_out),
+                                      _stream(stream)))
     if S_out is not None:
         return out, S_out, z_out
     return out

@@ -359,6 +359,28 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
     return ok();
 }
 
+hh_status_t hh_linattn_fwd_noalloc(int map, int dtype, int causal, int B, int H, int N, int d, const void *q,
+                                   const void *k, const void *v, const void *W, const void *b, const float *S0,
+                                   const float *z0, void *y, float *S_out, float *z_out, void *stream) {
+    hh_status_t st = check_common(map, dtype, B, H, N, d);
+    if (st != HH_OK) return st;
+    if (causal != 0 && causal != 1) return fail(HH_EINVAL, "causal must be 0 or 1 (got %d)", causal);
+    const size_t need = hh_linattn_fwd_workspace(map, dtype, causal, B, H, N, d);
+    if (need > hh::kNoAllocScratchBytes)
+        return fail(HH_EWORKSPACE,
+                    "hh_linattn_fwd_noalloc: this problem needs %zu bytes of scratch, beyond the library's "
+                    "fixed %zu; call hh_linattn_fwd with a workspace instead",
+                    need, (size_t)hh::kNoAllocScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        clear_stale_hip_error();
+        const hipError_t e = hh::noalloc_scratch(&ws);
+        if (e != hipSuccess) return hip_fail(e, "scratch address");
+    }
+    return hh_linattn_fwd(map, dtype, causal, B, H, N, d, q, k, v, W, b, S0, z0, y, S_out, z_out, ws,
+                          need > 0 ? hh::kNoAllocScratchBytes : 0, stream);
+}
+
 size_t hh_distill_loss_workspace(int map, int dtype, int B, int H, int N, int d) {
     if (check_common(map, dtype, B, H, N, d) != HH_OK || dtype != HH_BF16 || map != HH_MAP_HEDGEHOG) return 0;
     return (size_t)B * H * N * 2 * d * sizeof(uint16_t);  // the features of k

@@ -9,6 +9,11 @@ namespace hh {
 
 typedef uint16_t bf16_t;
 
+// Size of the library-owned scratch array behind hh_linattn_fwd_noalloc (one per device).
+constexpr size_t kNoAllocScratchBytes = 64u << 20;
+// Device address of that array on the current device (resolved once per device, then cached).
+hipError_t noalloc_scratch(void **ptr);
+
 // Chunked Hedgehog kernels (bf16).  Modes: 0 segment state, 1 causal, 2 read-out.
 struct WideParams {
     const bf16_t *q, *k, *v, *W, *b;  // b may be null

@@ -95,6 +95,21 @@ def test_fwd_workspace_rules(lib):
     assert lib.hh_linattn_fwd_workspace(HOG, BF16, 1, 1, 1, 64, 48) == 0  # invalid -> 0
 
 
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    # causal B1 H32 N4096 d128 needs 32 MiB of slots, within the fixed 64 MiB; bidirectional
+    # attention over 1024 sequences of d = 128 needs one 129 KiB total per sequence, beyond it
+    call = lib.hh_linattn_fwd_noalloc
+    assert lib.hh_linattn_fwd_workspace(HOG, BF16, 1, 1, 32, 4096, 128) <= 64 << 20
+    assert lib.hh_linattn_fwd_workspace(HOG, BF16, 0, 32, 32, 1024, 128) > 64 << 20
+    assert call(HOG, BF16, 0, 32, 32, 1024, 128, A, Bp, Cp, Wp, None, None, None, Dp, None, None, None) == \
+        _lib.HH_EWORKSPACE
+    assert "scratch" in lib.hh_last_error().decode()
+    assert call(HOG, BF16, 1, 1, 2, 64, 48, A, Bp, Cp, Wp, None, None, None, Dp, None, None, None) == \
+        _lib.HH_EUNSUPPORTED
+    assert call(HOG, BF16, 2, 1, 2, 64, 64, A, Bp, Cp, Wp, None, None, None, Dp, None, None, None) == \
+        _lib.HH_EINVAL
+
+
 def test_featuremap_and_decode_reject_bad_arguments(lib):
     assert lib.hh_featuremap(HOG, BF16, 1, 1, 8, 64, A, None, None, Dp, None) == _lib.HH_EINVAL   # no W
     assert lib.hh_featuremap(HOG, BF16, 1, 1, 8, 64, A, Wp, None, A, None) == _lib.HH_EINVAL      # phi aliases x
