@@ -52,12 +52,12 @@ def algorithmic_counts(w: wl.Workload):
     write y once, plus W and b once per head."""
     d, dp = w.d, wl.feature_dim(w.map, w.d)
     th = w.B * w.H * w.N
-    fm = 4 * d * d if w.map == wl.MAP_HEDGEHOG else 2 * (d * d + d)
+    fm = 2 * (d * d + d) if w.map == wl.MAP_TAYLOR2 else 4 * d * d
     flops = th * (fm + 4 * dp * d + 3 * dp + d)
     eb = wl.bytes_per_elem(w.dtype)
     byts = eb * 4 * th * d
-    if w.map == wl.MAP_HEDGEHOG:
-        byts += eb * w.H * (d * d + d)
+    if w.map != wl.MAP_TAYLOR2:
+        byts += eb * w.H * (d * d + (d if wl.map_has_bias(w.map) else 0))
     return float(flops), float(byts)
 
 
@@ -189,13 +189,15 @@ def main():
             shp = (w.B, w.H, w.N, w.d)
             s = {"q": draw(shp, w.qk_scale), "k": draw(shp, w.qk_scale), "v": draw(shp, w.v_scale)}
         sets.append(s)
-    if w.map == wl.MAP_HEDGEHOG:
+    if w.map != wl.MAP_TAYLOR2:
         if host0 is not None:
             W = torch.from_numpy(host0["W"]).to(dev).to(tdt)
             b = torch.from_numpy(host0["b"]).to(dev).to(tdt)
         else:
             W = draw((w.H, w.d, w.d), w.w_std)
             b = draw((w.H, w.d), w.b_std)
+        if not wl.map_has_bias(w.map):
+            b = None
     else:
         W = b = None
 
@@ -319,6 +321,9 @@ def main():
     elif w.map == wl.MAP_TAYLOR2:
         roof["kernel"] = ("hh_linattn_fwd: every kernel of one call (segment aggregates, exclusive prefix "
                           "over segments, chunked causal pass)")
+    elif w.map != wl.MAP_HEDGEHOG:
+        roof["kernel"] = ("hh_linattn_fwd: every kernel of one call (feature maps of q and k into the workspace, "
+                          "segment aggregates, chunked causal pass over the features)")
     elif not w.causal:
         roof["kernel"] = ("hh_linattn_fwd: every kernel of one call (total state and read-out; one fused "
                           "kernel when a sequence is one segment)")
@@ -406,7 +411,9 @@ def main():
         "dtype": "bf16" if w.dtype == wl.DT_BF16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "map": "hedgehog" if w.map == wl.MAP_HEDGEHOG else "taylor2", "causal": w.causal,
+                   "map": {wl.MAP_HEDGEHOG: "hedgehog", wl.MAP_TAYLOR2: "taylor2",
+                           wl.MAP_HEDGEHOG_SOFTMAX: "hedgehog_softmax", wl.MAP_EXP: "exp",
+                           wl.MAP_SOFTMAX: "softmax"}[w.map], "causal": w.causal,
                    "input_sets_rotated": N_SETS, "launch": "eager" if args.eager else "hip_graph_replay"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -33,7 +33,9 @@
  *  Threads  Calls are thread-safe (no global mutable state).
  *  Sizes    B, H >= 1; N >= 0 (N == 0 is a no-op apart from the state outputs);
  *           N * d < 2^31 and B * H < 2^24.
- *  Supported head dims: Hedgehog d in {16, 32, 64, 128}; Taylor d == 16.
+ *  Supported head dims: d in {16, 32, 64, 128} for the maps with a W; Taylor d == 16.
+ *  Maps 2-4 run the attention over features that a feature-map kernel writes into the
+ *  workspace first (bf16), so their forward needs a workspace even with one segment.
  */
 #ifndef HH_H
 #define HH_H
@@ -63,20 +65,30 @@ typedef enum {
     /* phi(x) = [1, x_0..x_{d-1}, x_a x_c / sqrt(2) for a, c in [d] (row-major)],
      * d' = 1 + d + d^2, so phi(q)^T phi(k) = 1 + q.k + (q.k)^2 / 2: the degree-2
      * Taylor map of section 3.4, "The Taylor Exponential as a Bridge Result". */
-    HH_MAP_TAYLOR2 = 1
+    HH_MAP_TAYLOR2 = 1,
+    /* phi(x) = [softmax(W x), softmax(-W x)], d' = 2d, no bias (b must be NULL): the softmax
+     * over the feature directions of Choice 4 (section 3.4), with the negation mapping of
+     * Choice 3, one softmax per half (each half sums to 1). */
+    HH_MAP_HEDGEHOG_SOFTMAX = 2,
+    /* phi(x) = exp(W x + b), d' = d: the single-sided map of Choice 1 with the default d' = d of
+     * the same section ("The Hedgehog MLP Feature Map"). */
+    HH_MAP_EXP = 3,
+    /* phi(x) = softmax(W x), d' = d, no bias (b must be NULL): Choice 4 as printed. */
+    HH_MAP_SOFTMAX = 4
 } hh_map_t;
 
 /* ABI revision of this header; bumped on any incompatible change. */
 int hh_abi_version(void);
 
-/* Feature dimension d' for (map, d): 2d or 1 + d + d^2; -1 if (map, d) is invalid. */
+/* Feature dimension d' for (map, d): 2d, 1 + d + d^2 or d; -1 if (map, d) is invalid. */
 int hh_feature_dim(int map, int d);
 
 /* Feature map alone (section 3.4, "The Hedgehog MLP Feature Map" / "The Taylor
  * Exponential as a Bridge Result").
  *   x   [B][H][N][d]  queries or keys (dtype)
- *   W   [H][d][d], b [H][d]  Hedgehog parameters (dtype); b may be NULL (zero
- *       bias); both ignored and may be NULL for the Taylor map
+ *   W   [H][d][d], b [H][d]  map parameters (dtype); b may be NULL (zero bias) for the
+ *       maps with a bias and must be NULL for the softmax maps; both ignored and may be NULL
+ *       for the Taylor map
  *   phi [B][H][N][d'] output (dtype), features in the order documented above.
  * phi must not overlap x. */
 hh_status_t hh_featuremap(int map, int dtype, int B, int H, int N, int d,

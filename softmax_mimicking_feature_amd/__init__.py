@@ -18,12 +18,13 @@ from __future__ import annotations
 from typing import Optional
 
 from . import _lib
-from ._lib import (HH_BF16, HH_EHIP, HH_EINVAL, HH_EUNSUPPORTED, HH_EWORKSPACE, HH_F32, HH_MAP_HEDGEHOG,
-                   HH_MAP_TAYLOR2, HH_OK, LibraryMissing)
+from ._lib import (HH_BF16, HH_EHIP, HH_EINVAL, HH_EUNSUPPORTED, HH_EWORKSPACE, HH_F32, HH_MAP_EXP, HH_MAP_HEDGEHOG,
+                   HH_MAP_HEDGEHOG_SOFTMAX, HH_MAP_SOFTMAX, HH_MAP_TAYLOR2, HH_OK, LibraryMissing)
 
 __all__ = ["hh_feature_dim", "hh_featuremap", "hh_linattn_fwd_workspace", "hh_linattn_fwd", "hh_linattn_fwd_noalloc",
            "hh_linattn_decode_step", "hh_distill_loss_workspace", "hh_distill_loss", "hh_status_str", "hh_last_error", "hh_abi_version", "HHError",
-           "LibraryMissing", "HH_F32", "HH_BF16", "HH_MAP_HEDGEHOG", "HH_MAP_TAYLOR2", "HH_OK", "HH_EINVAL",
+           "LibraryMissing", "HH_F32", "HH_BF16", "HH_MAP_HEDGEHOG", "HH_MAP_TAYLOR2", "HH_MAP_HEDGEHOG_SOFTMAX",
+           "HH_MAP_EXP", "HH_MAP_SOFTMAX", "HH_OK", "HH_EINVAL",
            "HH_EUNSUPPORTED", "HH_EWORKSPACE", "HH_EHIP"]
 
 
@@ -63,6 +64,22 @@ def _dev(t, name: str, dtype=None):
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     return t
+
+
+def _map_params(map: int, W, b, H: int, d: int):
+    """Check W and b for a map (W [H,d,d] for every map with a W, b [H,d] or None where the map has
+    a bias, None for the softmax maps); returns them, or (None, None) for the Taylor map."""
+    if map == HH_MAP_TAYLOR2:
+        return None, None
+    if W is None:
+        raise ValueError(f"W is required for map {map}")
+    _shape(W, "W", (H, d, d))
+    if map in (HH_MAP_HEDGEHOG_SOFTMAX, HH_MAP_SOFTMAX):
+        if b is not None:
+            raise ValueError("the softmax maps have no bias: b must be None")
+    else:
+        _shape(b, "b", (H, d))
+    return W, b
 
 
 def _shape(t, name: str, shape) -> None:
@@ -110,17 +127,14 @@ def hh_featuremap(x, W=None, b=None, *, map: int = HH_MAP_HEDGEHOG, out=None, st
     dp = lib.hh_feature_dim(map, d)
     if dp < 0:
         raise ValueError(f"invalid map/head dim ({map}, {d})")
-    if map == HH_MAP_HEDGEHOG:
-        _shape(W, "W", (H, d, d))
-        _shape(b, "b", (H, d))
+    W, b = _map_params(map, W, b, H, d)
     _shape(out, "out", (B, H, N, dp))
     _dev(x, "x")
     if out is None:
         out = torch.empty((B, H, N, dp), dtype=x.dtype, device=x.device)
     _dev(out, "out", x.dtype)
-    if map == HH_MAP_HEDGEHOG:
-        _dev(W, "W", x.dtype)
-        _dev(b, "b", x.dtype)
+    _dev(W, "W", x.dtype)
+    _dev(b, "b", x.dtype)
     _check(lib.hh_featuremap(map, _dtype_code(x), B, H, N, d, _ptr(x), _ptr(W), _ptr(b), _ptr(out),
                              _stream(stream)))
     return out
@@ -145,13 +159,7 @@ def hh_linattn_fwd(q, k, v, W=None, b=None, *, causal: bool = True, map: int = H
     dp = lib.hh_feature_dim(map, d)
     if dp < 0:
         raise ValueError(f"invalid map/head dim ({map}, {d})")
-    if map == HH_MAP_HEDGEHOG:
-        if W is None:
-            raise ValueError("W is required for the Hedgehog map")
-        _shape(W, "W", (H, d, d))
-        _shape(b, "b", (H, d))
-    else:
-        W = b = None
+    W, b = _map_params(map, W, b, H, d)
     _shape(out, "out", q.shape)
     for t, nm in ((S0, "S0"), (S_out, "S_out")):
         _shape(t, nm, (B, H, dp, d))
@@ -198,13 +206,7 @@ def hh_linattn_fwd_noalloc(q, k, v, W=None, b=None, *, causal: bool = True, map:
     dp = lib.hh_feature_dim(map, d)
     if dp < 0:
         raise ValueError(f"invalid map/head dim ({map}, {d})")
-    if map == HH_MAP_HEDGEHOG:
-        if W is None:
-            raise ValueError("W is required for the Hedgehog map")
-        _shape(W, "W", (H, d, d))
-        _shape(b, "b", (H, d))
-    else:
-        W = b = None
+    W, b = _map_params(map, W, b, H, d)
     _shape(out, "out", q.shape)
     for t, nm in ((S0, "S0"), (S_out, "S_out")):
         _shape(t, nm, (B, H, dp, d))
@@ -241,13 +243,7 @@ def hh_linattn_decode_step(q, k, v, W, b, S, z, *, map: int = HH_MAP_HEDGEHOG, o
     dp = lib.hh_feature_dim(map, d)
     if dp < 0:
         raise ValueError(f"invalid map/head dim ({map}, {d})")
-    if map == HH_MAP_HEDGEHOG:
-        if W is None:
-            raise ValueError("W is required for the Hedgehog map")
-        _shape(W, "W", (H, d, d))
-        _shape(b, "b", (H, d))
-    else:
-        W = b = None
+    W, b = _map_params(map, W, b, H, d)
     _shape(S, "S", (B, H, dp, d))
     _shape(z, "z", (B, H, dp))
     if out is not None and out.numel() != B * H * d:
@@ -280,13 +276,7 @@ def hh_distill_loss(q, k, W=None, b=None, *, map: int = HH_MAP_HEDGEHOG, out=Non
     B, H, N, d = q.shape
     if k.shape != q.shape:
         raise ValueError("q and k must have the same shape [B,H,N,d]")
-    if map == HH_MAP_HEDGEHOG:
-        if W is None:
-            raise ValueError("W is required for the Hedgehog map")
-        _shape(W, "W", (H, d, d))
-        _shape(b, "b", (H, d))
-    else:
-        W = b = None
+    W, b = _map_params(map, W, b, H, d)
     _shape(out, "out", (B, H, N))
     for t, nm in ((q, "q"), (k, "k")):
         _dev(t, nm, q.dtype)

@@ -54,23 +54,31 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 
 int feature_dim(int map, int d) {
     if (d < 1 || d > 1024) return -1;
-    if (map == HH_MAP_HEDGEHOG) return 2 * d;
+    if (map == HH_MAP_HEDGEHOG || map == HH_MAP_HEDGEHOG_SOFTMAX) return 2 * d;
     if (map == HH_MAP_TAYLOR2) return 1 + d + d * d;
+    if (map == HH_MAP_EXP || map == HH_MAP_SOFTMAX) return d;
     return -1;
 }
+
+// Maps with a W (every map but the Taylor map), and maps with a bias (the softmax maps have none).
+bool map_has_W(int map) { return map != HH_MAP_TAYLOR2; }
+bool map_has_b(int map) { return map == HH_MAP_HEDGEHOG || map == HH_MAP_EXP; }
+// Maps whose features the attention kernels read from a workspace (computed by the feature-map
+// kernel first) rather than computing them from q and k themselves.
+bool map_via_features(int map) { return map == HH_MAP_HEDGEHOG_SOFTMAX || map == HH_MAP_EXP || map == HH_MAP_SOFTMAX; }
 
 size_t elem_bytes(int dtype) { return dtype == HH_BF16 ? 2 : 4; }
 
 // Checks shared by the forward and the feature map.
 hh_status_t check_common(int map, int dtype, long B, long H, long N, int d) {
-    if (map != HH_MAP_HEDGEHOG && map != HH_MAP_TAYLOR2) return fail(HH_EINVAL, "unknown map %d", map);
+    if (map < HH_MAP_HEDGEHOG || map > HH_MAP_SOFTMAX) return fail(HH_EINVAL, "unknown map %d", map);
     if (dtype != HH_F32 && dtype != HH_BF16) return fail(HH_EINVAL, "unknown dtype %d", dtype);
     if (B < 1 || H < 1) return fail(HH_EINVAL, "B and H must be >= 1 (got B=%ld H=%ld)", B, H);
     if (B * H >= (1L << 24)) return fail(HH_EINVAL, "B*H = %ld exceeds 2^24", B * H);
     if (N < 0) return fail(HH_EINVAL, "N must be >= 0 (got %ld)", N);
-    if (map == HH_MAP_HEDGEHOG) {
+    if (map_has_W(map)) {
         if (d != 16 && d != 32 && d != 64 && d != 128)
-            return fail(HH_EUNSUPPORTED, "Hedgehog head dim %d not supported (16, 32, 64, 128)", d);
+            return fail(HH_EUNSUPPORTED, "head dim %d not supported for map %d (16, 32, 64, 128)", d, map);
     } else if (d != 16) {
         return fail(HH_EUNSUPPORTED, "Taylor map head dim %d not supported (16)", d);
     }
@@ -82,6 +90,46 @@ hh_status_t check_ptr(const void *p, const char *name, bool required) {
     if (!p) return required ? fail(HH_EINVAL, "%s is NULL", name) : HH_OK;
     if (!aligned16(p)) return fail(HH_EINVAL, "%s is not 16-byte aligned", name);
     return HH_OK;
+}
+
+// W and b of a map: W required (when there is work) for every map with a W; b optional where the
+// map has a bias, and must be NULL for the softmax maps (which omit it) and the Taylor map.
+hh_status_t check_params(int map, const void *W, const void *b, bool need) {
+    hh_status_t st;
+    if (map_has_W(map)) {
+        if ((st = check_ptr(W, "W", need)) != HH_OK) return st;
+    }
+    if (map_has_b(map)) return check_ptr(b, "b", false);
+    if (map_has_W(map) && b) return fail(HH_EINVAL, "map %d has no bias: b must be NULL", map);
+    return HH_OK;
+}
+
+// Workspace of the features-given path: phi(q), phi(k) (bf16), then the segment slots.
+struct FeatPlan {
+    int dp = 0, dpp = 0, nseg = 1, seg_len = 0;
+    size_t off_phik = 0, off_slots = 0, off_z = 0, bytes = 0;
+};
+
+FeatPlan make_feat_plan(int map, int causal, long BH, long N, int d) {
+    FeatPlan f;
+    f.dp = feature_dim(map, d);
+    f.dpp = hh::feat_padded_dim(f.dp);
+    const long C = 64;
+    const long nch = (N + C - 1) / C;
+    long nseg = 256L * hh::feat_wgs_per_cu(d, f.dp) / BH;
+    if (nseg < 1) nseg = 1;
+    if (nseg > nch) nseg = nch;
+    const long seg_chunks = nch > 0 ? (nch + nseg - 1) / nseg : 1;
+    nseg = nch > 0 ? (nch + seg_chunks - 1) / seg_chunks : 1;
+    f.nseg = (int)nseg;
+    f.seg_len = (int)(seg_chunks * C);
+    const size_t phi = ((size_t)BH * N * f.dp * sizeof(uint16_t) + 255) / 256 * 256;
+    f.off_phik = phi;
+    f.off_slots = 2 * phi;
+    const bool slots = !causal || f.nseg > 1;
+    f.off_z = f.off_slots + (slots ? (size_t)BH * f.nseg * f.dpp * d * sizeof(float) : 0);
+    f.bytes = f.off_z + (slots ? (size_t)BH * f.nseg * f.dpp * sizeof(float) : 0);
+    return f;
 }
 
 // ---- planning of the chunked bf16 path -------------------------------------------------
@@ -152,17 +200,16 @@ hh_status_t hh_featuremap(int map, int dtype, int B, int H, int N, int d, const 
     const size_t eb = elem_bytes(dtype);
     if ((st = check_ptr(x, "x", N > 0)) != HH_OK) return st;
     if ((st = check_ptr(phi, "phi", N > 0)) != HH_OK) return st;
-    if (hog) {
-        if ((st = check_ptr(W, "W", true)) != HH_OK) return st;
-        if ((st = check_ptr(b, "b", false)) != HH_OK) return st;
-    }
+    if ((st = check_params(map, W, b, true)) != HH_OK) return st;
     const size_t nx = (size_t)B * H * N * d * eb, nphi = (size_t)B * H * N * dp * eb;
     if (overlap(x, nx, phi, nphi)) return fail(HH_EINVAL, "phi overlaps x");
     if (N == 0) return ok();
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     clear_stale_hip_error();
     hipError_t e;
-    if (hog && dtype == HH_BF16)
+    if (map_via_features(map))
+        e = hh::launch_featuremap_variant(map, dtype, d, x, W, b, phi, (long)B * H, H, N, s);
+    else if (hog && dtype == HH_BF16)
         e = hh::launch_featuremap_hedgehog_bf16(d, (const hh::bf16_t *)x, (const hh::bf16_t *)W,
                                                 (const hh::bf16_t *)b, (hh::bf16_t *)phi, B * H, H, N, s);
     else
@@ -174,6 +221,8 @@ hh_status_t hh_featuremap(int map, int dtype, int B, int H, int N, int d, const 
 
 size_t hh_linattn_fwd_workspace(int map, int dtype, int causal, int B, int H, int N, int d) {
     if (check_common(map, dtype, B, H, N, d) != HH_OK || (causal != 0 && causal != 1)) return 0;
+    if (map_via_features(map))
+        return (dtype == HH_BF16 && N > 0) ? make_feat_plan(map, causal, (long)B * H, N, d).bytes : 0;
     // the larger of the plans with and without an initial state
     const Plan a = make_plan(map, dtype, causal, (long)B * H, N, d, false);
     const Plan b = make_plan(map, dtype, causal, (long)B * H, N, d, true);
@@ -187,7 +236,6 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
     hh_status_t st = check_common(map, dtype, B, H, N, d);
     if (st != HH_OK) return st;
     if (causal != 0 && causal != 1) return fail(HH_EINVAL, "causal must be 0 or 1 (got %d)", causal);
-    const bool hog = map == HH_MAP_HEDGEHOG;
     const int dp = feature_dim(map, d);
     const long BH = (long)B * H;
     const size_t eb = elem_bytes(dtype);
@@ -196,10 +244,7 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
     if ((st = check_ptr(k, "k", need_io)) != HH_OK) return st;
     if ((st = check_ptr(v, "v", need_io)) != HH_OK) return st;
     if ((st = check_ptr(y, "y", need_io)) != HH_OK) return st;
-    if (hog) {
-        if ((st = check_ptr(W, "W", need_io)) != HH_OK) return st;
-        if ((st = check_ptr(b, "b", false)) != HH_OK) return st;
-    }
+    if ((st = check_params(map, W, b, need_io)) != HH_OK) return st;
     if ((S0 == nullptr) != (z0 == nullptr)) return fail(HH_EINVAL, "S0 and z0 must be both set or both NULL");
     if ((S_out == nullptr) != (z_out == nullptr))
         return fail(HH_EINVAL, "S_out and z_out must be both set or both NULL");
@@ -213,6 +258,53 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
         return fail(HH_EINVAL, "y overlaps q, k or v");
     const size_t nS = (size_t)BH * dp * d * sizeof(float), nz = (size_t)BH * dp * sizeof(float);
     if (overlap(y, nio, S_out, nS) || overlap(y, nio, z_out, nz)) return fail(HH_EINVAL, "y overlaps S_out or z_out");
+
+    if (map_via_features(map) && dtype == HH_BF16 && N > 0) {
+        const FeatPlan fp = make_feat_plan(map, causal, BH, N, d);
+        if (!workspace) return fail(HH_EWORKSPACE, "workspace of %zu bytes required, got NULL", fp.bytes);
+        if (workspace_bytes < fp.bytes)
+            return fail(HH_EWORKSPACE, "workspace of %zu bytes required, got %zu", fp.bytes, workspace_bytes);
+        if (!aligned16(workspace)) return fail(HH_EINVAL, "workspace is not 16-byte aligned");
+        if (overlap(workspace, fp.bytes, y, nio) || overlap(workspace, fp.bytes, q, nio) ||
+            overlap(workspace, fp.bytes, k, nio) || overlap(workspace, fp.bytes, v, nio))
+            return fail(HH_EINVAL, "workspace overlaps an input or output");
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        clear_stale_hip_error();
+        char *ws = reinterpret_cast<char *>(workspace);
+        hh::bf16_t *phiq = reinterpret_cast<hh::bf16_t *>(ws), *phik = reinterpret_cast<hh::bf16_t *>(ws + fp.off_phik);
+        hipError_t e = hh::launch_featuremap_variant(map, dtype, d, q, W, b, phiq, BH, H, N, s);
+        if (e == hipSuccess) e = hh::launch_featuremap_variant(map, dtype, d, k, W, b, phik, BH, H, N, s);
+        if (e != hipSuccess) return hip_fail(e, "feature map launch");
+        hh::FeatParams f;
+        memset(&f, 0, sizeof f);
+        f.phiq = phiq; f.phik = phik; f.v = (const hh::bf16_t *)v; f.y = (hh::bf16_t *)y;
+        f.S_slots = reinterpret_cast<float *>(ws + fp.off_slots);
+        f.z_slots = reinterpret_cast<float *>(ws + fp.off_z);
+        f.slot_bh_stride = fp.nseg;
+        f.N = N; f.seg_len = fp.seg_len;
+        const bool direct = fp.nseg <= 8;
+        if (causal) {
+            if (fp.nseg > 1) {
+                f.nseg_grid = fp.nseg - 1;
+                e = hh::launch_feat(d, fp.dp, 0, f, (int)(BH * (fp.nseg - 1)), s);
+                if (e == hipSuccess && !direct) e = hh::launch_feat_scan(f.S_slots, f.z_slots, d, fp.dp, (int)BH, fp.nseg, 0, s);
+                if (e != hipSuccess) return hip_fail(e, "segment-state launch");
+            }
+            f.slot_mode = fp.nseg > 1 ? (direct ? 3 : 1) : 0;
+            f.S0 = S0; f.z0 = z0; f.S_out = S_out; f.z_out = z_out;
+            f.nseg_grid = fp.nseg;
+            e = hh::launch_feat(d, fp.dp, 1, f, (int)(BH * fp.nseg), s);
+        } else {
+            f.nseg_grid = fp.nseg;
+            e = hh::launch_feat(d, fp.dp, 0, f, (int)(BH * fp.nseg), s);
+            if (e == hipSuccess && fp.nseg > 1) e = hh::launch_feat_scan(f.S_slots, f.z_slots, d, fp.dp, (int)BH, fp.nseg, 1, s);
+            if (e != hipSuccess) return hip_fail(e, "segment-state launch");
+            f.slot_mode = 2;
+            e = hh::launch_feat(d, fp.dp, 2, f, (int)(BH * fp.nseg), s);
+        }
+        if (e != hipSuccess) return hip_fail(e, "chunked forward launch");
+        return ok();
+    }
 
     const Plan pl = make_plan(map, dtype, causal, BH, N, d, S0 != nullptr);
     if (pl.need_ws) {
@@ -237,8 +329,8 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
     if (!pl.chunked) {  // fp32 token-by-token path
         hh::SeqParams sp;
         sp.q = (const float *)q; sp.k = (const float *)k; sp.v = (const float *)v;
-        sp.W = hog ? (const float *)W : nullptr;
-        sp.b = hog ? (const float *)b : nullptr;
+        sp.W = map_has_W(map) ? (const float *)W : nullptr;
+        sp.b = map_has_b(map) ? (const float *)b : nullptr;
         sp.y = (float *)y;
         sp.S0 = S0; sp.z0 = z0; sp.S_out = S_out; sp.z_out = z_out;
         sp.N = N; sp.H = H; sp.d = d; sp.dp = dp; sp.map = map; sp.causal = causal;
@@ -392,6 +484,8 @@ hh_status_t hh_distill_loss(int map, int dtype, int B, int H, int N, int d, cons
     hh_status_t st = check_common(map, dtype, B, H, N, d);
     if (st != HH_OK) return st;
     if (dtype != HH_BF16) return fail(HH_EUNSUPPORTED, "distillation loss: bf16 inputs only");
+    if (map != HH_MAP_HEDGEHOG && map != HH_MAP_TAYLOR2)
+        return fail(HH_EUNSUPPORTED, "distillation loss: the Hedgehog and Taylor maps only");
     const bool hog = map == HH_MAP_HEDGEHOG;
     const bool need = N > 0;
     if ((st = check_ptr(q, "q", need)) != HH_OK) return st;
@@ -441,7 +535,6 @@ hh_status_t hh_linattn_decode_step(int map, int dtype, int B, int H, int d, cons
                                    void *stream) {
     hh_status_t st = check_common(map, dtype, B, H, 1, d);
     if (st != HH_OK) return st;
-    const bool hog = map == HH_MAP_HEDGEHOG;
     const int dp = feature_dim(map, d);
     const long BH = (long)B * H;
     const size_t eb = elem_bytes(dtype);
@@ -451,10 +544,7 @@ hh_status_t hh_linattn_decode_step(int map, int dtype, int B, int H, int d, cons
     if ((st = check_ptr(y, "y", true)) != HH_OK) return st;
     if ((st = check_ptr(S, "S", true)) != HH_OK) return st;
     if ((st = check_ptr(z, "z", true)) != HH_OK) return st;
-    if (hog) {
-        if ((st = check_ptr(W, "W", true)) != HH_OK) return st;
-        if ((st = check_ptr(b, "b", false)) != HH_OK) return st;
-    }
+    if ((st = check_params(map, W, b, true)) != HH_OK) return st;
     const size_t nio = (size_t)BH * d * eb;
     const size_t nS = (size_t)BH * dp * d * sizeof(float), nz = (size_t)BH * dp * sizeof(float);
     if (overlap(y, nio, q, nio) || overlap(y, nio, k, nio) || overlap(y, nio, v, nio) || overlap(y, nio, S, nS) ||
@@ -462,7 +552,7 @@ hh_status_t hh_linattn_decode_step(int map, int dtype, int B, int H, int d, cons
         return fail(HH_EINVAL, "y overlaps q, k, v, S or z");
     if (overlap(S, nS, z, nz)) return fail(HH_EINVAL, "S overlaps z");
     hh::DecodeParams dpar;
-    dpar.q = q; dpar.k = k; dpar.v = v; dpar.W = hog ? W : nullptr; dpar.b = hog ? b : nullptr;
+    dpar.q = q; dpar.k = k; dpar.v = v; dpar.W = map_has_W(map) ? W : nullptr; dpar.b = map_has_b(map) ? b : nullptr;
     dpar.y = y; dpar.S = S; dpar.z = z;
     dpar.H = H; dpar.d = d; dpar.dp = dp; dpar.map = map; dpar.dtype = dtype;
     clear_stale_hip_error();

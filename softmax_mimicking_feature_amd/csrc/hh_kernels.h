@@ -9,6 +9,11 @@ namespace hh {
 
 typedef uint16_t bf16_t;
 
+// Map and dtype codes of include/hh.h, for device code that does not include it.
+constexpr int HH_MAP_HEDGEHOG_ = 0, HH_MAP_TAYLOR2_ = 1, HH_MAP_HEDGEHOG_SOFTMAX_ = 2, HH_MAP_EXP_ = 3,
+              HH_MAP_SOFTMAX_ = 4;
+constexpr int HH_F32_ = 0, HH_BF16_ = 1;
+
 // Size of the library-owned scratch array behind hh_linattn_fwd_noalloc (one per device).
 constexpr size_t kNoAllocScratchBytes = 64u << 20;
 // Device address of that array on the current device (resolved once per device, then cached).
@@ -81,6 +86,29 @@ struct DistillParams {
     int N, BH, H;
 };
 hipError_t launch_distill(int map, int d, const DistillParams &p, int BH, hipStream_t st);
+
+// Linear attention over given bf16 features (the maps computed into a workspace first).
+// Modes: 0 segment aggregates into slots, 1 causal, 2 read-out against a total (bidirectional).
+// Slots: per (b,h) and segment, S [dpp][d] fp32 in the kernel's register image, then z [dpp]
+// fp32 (dpp = d' rounded up to a multiple of 32).
+struct FeatParams {
+    const bf16_t *phiq, *phik, *v;  // [BH][N][d'], [BH][N][d'], [BH][N][d]
+    bf16_t *y;
+    const float *S0, *z0;           // caller's initial state, canonical [BH][d'][d], [BH][d'] (or null)
+    float *S_out, *z_out;           // final state (causal, last segment), canonical (or null)
+    float *S_slots, *z_slots;
+    long slot_bh_stride;
+    int N, seg_len, nseg_grid;
+    int slot_mode;                  // 0 none, 1 exclusive prefix in slot s, 2 total in slot 0, 3 sum of slots < s
+};
+hipError_t launch_feat(int d, int dp, int mode, const FeatParams &p, int grid, hipStream_t st);
+hipError_t launch_feat_scan(float *S, float *z, int d, int dp, int BH, int nseg, int mode, hipStream_t st);
+int feat_wgs_per_cu(int d, int dp);
+int feat_padded_dim(int dp);
+// Feature maps 2, 3, 4 (softmax over the directions per half, single-sided exp, single-sided
+// softmax): bf16 on the matrix cores, fp32 on the vector units.  x [BH][N][d] -> phi [BH][N][d'].
+hipError_t launch_featuremap_variant(int map, int dtype, int d, const void *x, const void *W, const void *b, void *phi,
+                                     long BH, int H, int N, hipStream_t st);
 
 // fp32 path: one workgroup per (b,h) walks the sequence token by token.
 struct SeqParams {

@@ -114,19 +114,41 @@ hipError_t launch_state_copy(const float *S0, const float *z0, float *S_out, flo
 }
 
 // ----------------------------------------------------------------------------------------
-// Feature value f of token x (fp32), x already in shared memory.
+// Feature value f of token x (fp32), x already in shared memory.  For the softmax maps this is
+// the logit (+-w_l.x); softmax_halves turns a token's logits into features afterwards.
 template <typename LoadW>
 __device__ __forceinline__ float feature_value(int map, int d, int f, const float *x, LoadW wrow, float bias_l) {
-    if (map == 0) {
+    if (map != HH_MAP_TAYLOR2_) {
         const int l = f < d ? f : f - d;
         float u = bias_l;
         for (int m = 0; m < d; m++) u = fmaf(wrow(l, m), x[m], u);
-        return expf(f < d ? u : -u);
+        const float su = f < d ? u : -u;
+        return (map == HH_MAP_HEDGEHOG_SOFTMAX_ || map == HH_MAP_SOFTMAX_) ? su : expf(su);
     }
     if (f == 0) return 1.0f;
     if (f <= d) return x[f - 1];
     const int q = f - 1 - d;
     return x[q / d] * x[q % d] * 0.70710678118654752f;
+}
+
+// Softmax over each half (d logits) of a token's feature vector in shared memory, in place;
+// executed by one wave (lane l handles entries l and l + 64 of each half, d <= 128).
+__device__ __forceinline__ void softmax_halves(float *sf, int d, int halves, int lane) {
+    for (int hf = 0; hf < halves; hf++) {
+        float *x = sf + hf * d;
+        float v0 = lane < d ? x[lane] : -INFINITY, v1 = lane + 64 < d ? x[lane + 64] : -INFINITY;
+        float mx = fmaxf(v0, v1);
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        const float e0 = lane < d ? expf(v0 - mx) : 0.0f, e1 = lane + 64 < d ? expf(v1 - mx) : 0.0f;
+        float sum = e0 + e1;
+        for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+        if (lane < d) x[lane] = e0 / sum;
+        if (lane + 64 < d) x[lane + 64] = e1 / sum;
+    }
+}
+
+__device__ __forceinline__ bool is_softmax_map(int map) {
+    return map == HH_MAP_HEDGEHOG_SOFTMAX_ || map == HH_MAP_SOFTMAX_;
 }
 
 __device__ __forceinline__ float ld(const void *p, size_t i, int dtype) {
@@ -178,11 +200,17 @@ __global__ __launch_bounds__(kSeqThreads) void seq_f32_kernel(SeqParams p) {
             __syncthreads();
             for (int f = t; f < dp; f += kSeqThreads) {
                 const int l = f < d ? f : f - d;
-                const float bl = (p.map == 0 && bhp) ? bhp[l] : 0.0f;
+                const float bl = ((p.map == HH_MAP_HEDGEHOG_ || p.map == HH_MAP_EXP_) && bhp) ? bhp[l] : 0.0f;
                 if (do_update) sfk[f] = feature_value(p.map, d, f, sk, wrow, bl);
                 if (do_read) sfq[f] = feature_value(p.map, d, f, sq, wrow, bl);
             }
             __syncthreads();
+            if (is_softmax_map(p.map)) {
+                const int halves = p.map == HH_MAP_HEDGEHOG_SOFTMAX_ ? 2 : 1;
+                if (t < 64 && do_update) softmax_halves(sfk, d, halves, t);
+                if (t >= 64 && t < 128 && do_read) softmax_halves(sfq, d, halves, t - 64);
+                __syncthreads();
+            }
             if (do_update) {
 #pragma unroll
                 for (int m = 0; m < kSeqMaxE; m++) {
@@ -263,7 +291,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     __syncthreads();
     const void *W = p.W;
     const size_t woff = (size_t)h * d * d;
-    if (p.map == 0) {
+    if (p.map != HH_MAP_TAYLOR2_) {
         // u = W x for q and k together: kDecThreads / d consecutive threads share a row of W and
         // read contiguous pieces of it, then combine their partial dot products
         const int tpr = kDecThreads / d < d ? kDecThreads / d : d;
@@ -296,10 +324,28 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
         }
         if (part == 0 && l < d) {
             const float bl = p.b ? ld(p.b, (size_t)h * d + l, dt) : 0.0f;
-            sfq[l] = expf(uq + bl);
-            sfq[d + l] = expf(-(uq + bl));
-            sfk[l] = expf(uk + bl);
-            sfk[d + l] = expf(-(uk + bl));
+            if (p.map == HH_MAP_HEDGEHOG_) {
+                sfq[l] = expf(uq + bl);
+                sfq[d + l] = expf(-(uq + bl));
+                sfk[l] = expf(uk + bl);
+                sfk[d + l] = expf(-(uk + bl));
+            } else if (p.map == HH_MAP_EXP_) {
+                sfq[l] = expf(uq + bl);
+                sfk[l] = expf(uk + bl);
+            } else {  // softmax maps: logits first (no bias), normalised below
+                sfq[l] = uq;
+                sfk[l] = uk;
+                if (p.map == HH_MAP_HEDGEHOG_SOFTMAX_) {
+                    sfq[d + l] = -uq;
+                    sfk[d + l] = -uk;
+                }
+            }
+        }
+        if (is_softmax_map(p.map)) {
+            __syncthreads();
+            const int halves = p.map == HH_MAP_HEDGEHOG_SOFTMAX_ ? 2 : 1;
+            if (t < 64) softmax_halves(sfq, d, halves, t);
+            else if (t < 128) softmax_halves(sfk, d, halves, t - 64);
         }
     } else {
         auto wrow = [&](int l, int m) { return ld(W, woff + (size_t)l * d + m, dt); };

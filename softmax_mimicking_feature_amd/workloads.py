@@ -29,6 +29,9 @@ import numpy as np
 
 MAP_HEDGEHOG = 0
 MAP_TAYLOR2 = 1
+MAP_HEDGEHOG_SOFTMAX = 2
+MAP_EXP = 3
+MAP_SOFTMAX = 4
 DT_F32 = 0
 DT_BF16 = 1
 
@@ -36,7 +39,7 @@ DT_BF16 = 1
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    map: int            # MAP_HEDGEHOG or MAP_TAYLOR2
+    map: int            # MAP_HEDGEHOG, MAP_TAYLOR2, MAP_HEDGEHOG_SOFTMAX, MAP_EXP or MAP_SOFTMAX
     dtype: int          # DT_F32 or DT_BF16
     causal: bool
     B: int
@@ -78,6 +81,11 @@ def _cfg() -> Dict[str, Workload]:
         qk_scale=s3, v_scale=s3, w_std=128 ** -0.5, b_std=0.0,
         description="attention-weight distillation loss (Eq. 4) at the Llama-2-7B head shapes, bf16, "
                     "B1 H32 N4096 d128 (the causal workload's inputs; v unused)")
+    c["c3_llama2_softmax_map"] = Workload(
+        "c3_llama2_softmax_map", MAP_HEDGEHOG_SOFTMAX, DT_BF16, True, B=1, H=32, N=4096, d=128, seed=1003,
+        qk_scale=s3, v_scale=s3, w_std=128 ** -0.5, b_std=0.0,
+        description="Llama-2-7B-shaped causal with the softmax-over-features map per half (no bias), bf16, "
+                    "B1 H32 N4096 d128 d'256 (the causal workload's inputs)")
     c["c4_bert_bidir"] = Workload(
         "c4_bert_bidir", MAP_HEDGEHOG, DT_BF16, False, B=32, H=12, N=512, d=64, seed=1004,
         qk_scale=1.0, v_scale=1.0, w_std=64 ** -0.5, b_std=0.0,
@@ -119,7 +127,7 @@ def make_inputs(w: Workload, *, B: Optional[int] = None, H: Optional[int] = None
 
     All arrays are float32 holding values exactly representable in the
     workload's storage dtype.  For the Taylor map W and b are returned as
-    empty arrays (the map has no parameters).
+    empty arrays (the map has no parameters); the softmax maps use no b.
     """
     B = w.B if B is None else B
     H = w.H if H is None else H
@@ -131,7 +139,7 @@ def make_inputs(w: Workload, *, B: Optional[int] = None, H: Optional[int] = None
     k = rng.standard_normal((B, H, N, d)) * w.qk_scale
     v = rng.standard_normal((B, H, N, d)) * w.v_scale
     out = {"q": _store(q, w.dtype), "k": _store(k, w.dtype), "v": _store(v, w.dtype)}
-    if w.map == MAP_HEDGEHOG:
+    if w.map != MAP_TAYLOR2:
         W = rng.standard_normal((H, d, d)) * w.w_std
         b = rng.standard_normal((H, d)) * w.b_std
         out["W"] = _store(W, w.dtype)
@@ -156,8 +164,18 @@ def make_decode_token(w: Workload, *, B: Optional[int] = None, H: Optional[int] 
 
 
 def feature_dim(map_: int, d: int) -> int:
-    """Length of a feature vector: 2d for Hedgehog, 1 + d + d*d for the Taylor map."""
-    return 2 * d if map_ == MAP_HEDGEHOG else 1 + d + d * d
+    """Length of a feature vector: 2d (Hedgehog, per-half softmax), 1 + d + d*d (Taylor), d
+    (single-sided maps)."""
+    if map_ in (MAP_HEDGEHOG, MAP_HEDGEHOG_SOFTMAX):
+        return 2 * d
+    if map_ == MAP_TAYLOR2:
+        return 1 + d + d * d
+    return d
+
+
+def map_has_bias(map_: int) -> bool:
+    """Whether a map takes the bias b (the softmax maps and the Taylor map do not)."""
+    return map_ in (MAP_HEDGEHOG, MAP_EXP)
 
 
 def random_state(w: Workload, *, B: Optional[int] = None, H: Optional[int] = None,

@@ -43,6 +43,9 @@ def test_feature_dim_and_strings(lib):
     assert lib.hh_feature_dim(TAY, 16) == 273
     assert lib.hh_feature_dim(TAY, 64) == 4161
     assert lib.hh_feature_dim(7, 16) == -1
+    assert lib.hh_feature_dim(_lib.HH_MAP_HEDGEHOG_SOFTMAX, 64) == 128
+    assert lib.hh_feature_dim(_lib.HH_MAP_EXP, 64) == 64
+    assert lib.hh_feature_dim(_lib.HH_MAP_SOFTMAX, 16) == 16
     for s in range(5):
         assert lib.hh_status_str(s).decode().startswith("HH_")
 
@@ -79,6 +82,22 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, causal=0, S0=0x60000000, z0=0x61000000) == _lib.HH_EINVAL  # state with bidirectional
     assert fwd(lib, N=1 << 25, d=128) == _lib.HH_EINVAL              # N*d >= 2^31
     assert lib.hh_last_error().decode() != ""
+
+
+def test_variant_maps_rules(lib):
+    HS, EXP, SM = _lib.HH_MAP_HEDGEHOG_SOFTMAX, _lib.HH_MAP_EXP, _lib.HH_MAP_SOFTMAX
+    assert fwd(lib, map_=HS, b=0x60000000) == _lib.HH_EINVAL       # the softmax maps have no bias
+    assert "no bias" in lib.hh_last_error().decode()
+    assert fwd(lib, map_=SM, b=0x60000000) == _lib.HH_EINVAL
+    assert fwd(lib, map_=EXP, d=48) == _lib.HH_EUNSUPPORTED
+    assert fwd(lib, map_=EXP, W=None) == _lib.HH_EINVAL
+    # their attention reads features from the workspace: needed even with one segment
+    need = lib.hh_linattn_fwd_workspace(EXP, BF16, 1, 64, 8, 128, 64)
+    assert need >= 2 * 64 * 8 * 128 * 64 * 2
+    assert fwd(lib, map_=EXP, B=64, H=8, N=128, ws=None) == _lib.HH_EWORKSPACE
+    assert lib.hh_linattn_fwd_workspace(HS, F32, 1, 1, 2, 64, 64) == 0  # fp32: the token path
+    assert lib.hh_distill_loss(HS, BF16, 1, 2, 64, 64, A, Bp, Wp, None, Dp, Cp, 1 << 30, None) == \
+        _lib.HH_EUNSUPPORTED
 
 
 def test_fwd_workspace_rules(lib):

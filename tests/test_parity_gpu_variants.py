@@ -1,0 +1,192 @@
+"""GPU parity of the feature-map variants of the walkthrough's section 3.4, "The Hedgehog MLP
+Feature Map": the single-sided exp(W x + b) with d' = d (Choice 1, default d' = d), the softmax
+over the feature directions without bias (Choice 4), single-sided and per half with the
+negation mapping (Choice 3).  Against the fp64 oracle, element by element, with the bf16 rule
+(rtol 2e-2, atol 1e-2) for bf16 inputs and the fp32 rule (rtol 1e-4, atol 1e-5) for fp32
+inputs: the feature map alone, the causal and bidirectional forward at every head dim and
+ragged lengths, many segments with a resumed state, the decode step, and the fp32 path."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from softmax_mimicking_feature_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+HS, EXP, SM = oracle.MAP_HEDGEHOG_SOFTMAX, oracle.MAP_EXP, oracle.MAP_SOFTMAX
+VARIANTS = [HS, EXP, SM]
+
+
+def hh():
+    import softmax_mimicking_feature_amd as m
+    return m
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(a, dtype=torch.bfloat16):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dtype).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def close(got, want, rtol, atol, what):
+    got = np.asarray(got, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU output"
+    err = np.abs(got - want)
+    bad = err > atol + rtol * np.abs(want)
+    nrm = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30)
+    print(f"  {what}: max abs err {err.max():.3e}, normwise {nrm:.3e}, {int(bad.sum())}/{bad.size} out", flush=True)
+    assert not bad.any(), what
+
+
+def case(map_, d, B=2, H=3, N=200, dtype=wl.DT_BF16, seed=0):
+    w = wl.CONFIGS["c2_gpt2_causal"].replace(B=B, H=H, N=N, d=d, dtype=dtype, w_std=d ** -0.5,
+                                             b_std=0.1 if map_ == EXP else 0.0, seed=seed)
+    x = wl.make_inputs(w)
+    b = x["b"] if map_ == EXP else None
+    return w, x, b
+
+
+def params(x, b, dt):
+    return dev(x["W"], dt), (None if b is None else dev(b, dt))
+
+
+@pytest.mark.parametrize("map_", VARIANTS)
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", [wl.DT_BF16, wl.DT_F32])
+def test_featuremap_variant(map_, d, dtype):
+    w, x, b = case(map_, d, N=333, dtype=dtype, seed=11000 + 10 * map_ + d)
+    say(f"featuremap map={map_} d={d} dtype={dtype}")
+    dt = torch.bfloat16 if dtype == wl.DT_BF16 else torch.float32
+    W, bt = params(x, b, dt)
+    phi = hh().hh_featuremap(dev(x["q"], dt), W, bt, map=map_)
+    torch.cuda.synchronize()
+    want = oracle.featuremap(map_, x["q"], x["W"], b)
+    rtol, atol = (1e-2, 1e-6) if dtype == wl.DT_BF16 else (1e-5, 1e-7)
+    close(host(phi), want, rtol, atol, "phi")
+    if map_ != EXP:  # each half a distribution
+        halves = host(phi).reshape(*phi.shape[:3], -1, d).sum(axis=-1)
+        close(halves, np.ones_like(halves), 2e-2 if dtype == wl.DT_BF16 else 1e-5, 0.0, "half sums")
+
+
+@pytest.mark.parametrize("map_", VARIANTS)
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("N", [1, 65, 1000])
+@pytest.mark.parametrize("causal", [True, False])
+def test_forward_variant(map_, d, N, causal):
+    w, x, b = case(map_, d, N=N, seed=12000 + 10 * map_ + d + N)
+    say(f"forward map={map_} d={d} N={N} causal={causal}")
+    m = hh()
+    W, bt = params(x, b, torch.bfloat16)
+    q, k, v = (dev(x[n]) for n in ("q", "k", "v"))
+    rtol, atol = wl.tolerance(w.dtype)
+    if causal:
+        y, S, z = m.hh_linattn_fwd(q, k, v, W, bt, map=map_, want_state=True)
+        torch.cuda.synchronize()
+        yo, So, zo = oracle.causal(map_, x["q"], x["k"], x["v"], x["W"], b, want_state=True)
+        close(host(S), So, rtol, 1e-2 * float(np.abs(So).max()), "S_out")
+        close(host(z), zo, rtol, 1e-2 * float(np.abs(zo).max()), "z_out")
+    else:
+        y = m.hh_linattn_fwd(q, k, v, W, bt, map=map_, causal=False)
+        torch.cuda.synchronize()
+        yo = oracle.bidir(map_, x["q"], x["k"], x["v"], x["W"], b)
+    close(host(y), yo, rtol, atol, "y")
+
+
+@pytest.mark.parametrize("map_", VARIANTS)
+@pytest.mark.parametrize("d", [64, 128])
+def test_variant_many_segments_and_resume(map_, d):
+    # one sequence: cut into many segments (the scan of segment aggregates); then the second part
+    # resumed from the oracle's state after the first
+    w, x, b = case(map_, d, B=1, H=1, N=3000, seed=13000 + map_ + d)
+    say(f"segments + resume map={map_} d={d}")
+    m = hh()
+    W, bt = params(x, b, torch.bfloat16)
+    n1 = 1234
+    yo, So, zo = oracle.causal(map_, x["q"], x["k"], x["v"], x["W"], b, want_state=True)
+    _, S1, z1 = oracle.causal(map_, x["q"][:, :, :n1], x["k"][:, :, :n1], x["v"][:, :, :n1], x["W"], b, want_state=True)
+    rtol, atol = wl.tolerance(w.dtype)
+    y = m.hh_linattn_fwd(*(dev(x[n]) for n in ("q", "k", "v")), W, bt, map=map_)
+    close(host(y), yo, rtol, atol, "whole y")
+    y2, S2, z2 = m.hh_linattn_fwd(*(dev(x[n][:, :, n1:]) for n in ("q", "k", "v")), W, bt, map=map_,
+                                  S0=dev(S1, torch.float32), z0=dev(z1, torch.float32), want_state=True)
+    torch.cuda.synchronize()
+    close(host(y2), yo[:, :, n1:], rtol, atol, "resumed y")
+    close(host(S2), So, rtol, 1e-2 * float(np.abs(So).max()), "resumed S_out")
+
+
+@pytest.mark.parametrize("map_", VARIANTS)
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_variant(map_, d):
+    w, x, b = case(map_, d, B=4, H=8, N=300, seed=14000 + map_ + d)
+    say(f"decode map={map_} d={d}")
+    m = hh()
+    S64, z64 = oracle.prefix_state(map_, x["k"], x["v"], x["W"], b)
+    tok = wl.make_decode_token(w.replace(v_scale=1.0))
+    S = dev(S64, torch.float32)
+    z = dev(z64, torch.float32)
+    W, bt = params(x, b, torch.bfloat16)
+    y = m.hh_linattn_decode_step(dev(tok["q"]), dev(tok["k"]), dev(tok["v"]), W, bt, S, z, map=map_)
+    torch.cuda.synchronize()
+    yo, So, zo = oracle.decode_step(map_, tok["q"], tok["k"], tok["v"], x["W"], b, S64.astype(np.float32),
+                                    z64.astype(np.float32))
+    rtol, atol = wl.tolerance(w.dtype)
+    close(host(y), yo, rtol, atol, "decode y")
+    close(S.cpu().numpy(), So, 1e-5, 1e-6 * float(np.abs(So).max()), "decode S")
+    close(z.cpu().numpy(), zo, 1e-5, 0.0, "decode z")
+
+
+@pytest.mark.parametrize("map_", VARIANTS)
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp32_path_variant(map_, causal):
+    w, x, b = case(map_, 64, B=1, H=2, N=150, dtype=wl.DT_F32, seed=15000 + map_)
+    say(f"fp32 map={map_} causal={causal}")
+    m = hh()
+    W, bt = params(x, b, torch.float32)
+    q, k, v = (dev(x[n], torch.float32) for n in ("q", "k", "v"))
+    rtol, atol = wl.tolerance(w.dtype)
+    if causal:
+        y, S, z = m.hh_linattn_fwd(q, k, v, W, bt, map=map_, want_state=True)
+        torch.cuda.synchronize()
+        yo, So, zo = oracle.causal(map_, x["q"], x["k"], x["v"], x["W"], b, want_state=True)
+        close(host(S), So, 1e-5, 1e-6 * float(np.abs(So).max()), "S_out")
+    else:
+        y = m.hh_linattn_fwd(q, k, v, W, bt, map=map_, causal=False)
+        torch.cuda.synchronize()
+        yo = oracle.bidir(map_, x["q"], x["k"], x["v"], x["W"], b)
+    close(host(y), yo, rtol, atol, "y")
+
+
+def test_variant_llama2_heads_sampled_rows():
+    # the Llama-2-7B head shapes (B1 H32 N4096 d128) with the per-half softmax map: every output
+    # row of 4 heads, and sampled rows of the others by the explicit form
+    w = wl.CONFIGS["c3_llama2_causal"]
+    say("softmax map, B1 H32 N4096 d128")
+    x = wl.make_inputs(w)
+    m = hh()
+    y = host(m.hh_linattn_fwd(*(dev(x[n]) for n in ("q", "k", "v")), dev(x["W"]), None, map=HS))
+    torch.cuda.synchronize()
+    rtol, atol = wl.tolerance(w.dtype)
+    sub = {k_: (a[:, :4] if k_ in ("q", "k", "v") else a[:4]) for k_, a in x.items()}
+    close(y[:, :4], oracle.causal(HS, sub["q"], sub["k"], sub["v"], sub["W"]), rtol, atol, "heads 0-3, every row")
+    rows = [0, 63, 64, 511, 512, 2047, 2048, 3583, 3584, 4095]
+    close(y[:, :, rows], oracle.quadratic(HS, x["q"], x["k"], x["v"], x["W"], rows=rows), rtol, atol, "sampled rows")
+
+
+def test_softmax_maps_reject_a_bias():
+    m = hh()
+    w, x, b = case(HS, 64, N=10)
+    with pytest.raises(ValueError, match="no bias"):
+        m.hh_linattn_fwd(*(dev(x[n]) for n in ("q", "k", "v")), dev(x["W"]), dev(x["b"]), map=HS)
