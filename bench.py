@@ -76,6 +76,21 @@ def distill_counts(w: wl.Workload):
     return float(flops), float(byts)
 
 
+def backward_counts(w: wl.Workload):
+    """Algorithmic FLOPs and HBM bytes of one backward.
+
+    Per token-head: the feature maps of q and k again (4d^2), dL/dphi(q) = S g + c z (2 d' d),
+    dL/dphi(k) = R v + r and dL/dv = R^T phi(k) (4 d' d), the map's backward dq, dk = W^T du
+    (4d^2) and dW = sum du x^T (4d^2), plus O(d') for den, c and the normalisers.  Bytes: read
+    q, k, v, y, dy and write dq, dk, dv once, plus W, b and the fp32 dW, db once per head."""
+    d, dp = w.d, wl.feature_dim(w.map, w.d)
+    th = w.B * w.H * w.N
+    flops = th * (12 * d * d + 6 * dp * d + 4 * dp)
+    eb = wl.bytes_per_elem(w.dtype)
+    byts = eb * 8 * th * d + (eb + 4) * w.H * (d * d + d)
+    return float(flops), float(byts)
+
+
 def decode_counts(w: wl.Workload):
     d, dp = w.d, wl.feature_dim(w.map, w.d)
     bh = w.B * w.H
@@ -168,6 +183,7 @@ def main():
     tdt = torch.bfloat16 if w.dtype == wl.DT_BF16 else torch.float32
     decode = args.workload.endswith("decode")
     distill = args.workload.endswith("distill")
+    backward = args.workload.endswith("backward")
 
     # ---- input sets (set 0 from the seeded host generator, the others drawn on the GPU
     #      with the same distributions)
@@ -220,6 +236,24 @@ def main():
             hh.hh_linattn_decode_step(s["q"], s["k"], s["v"], W, b, S, z, map=w.map, out=outs[i % N_SETS],
                                       stream=st)
         flops, byts = decode_counts(w)
+    elif backward:
+        need = hh.hh_linattn_bwd_workspace(w.map, w.dtype, w.causal, w.B, w.H, w.N, w.d)
+        wss = [torch.empty((max(need, 16),), dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
+        shp = (w.B, w.H, w.N, w.d)
+        for s in sets:  # the forward's output and a random dL/dy per input set
+            s["y"] = hh.hh_linattn_fwd(s["q"], s["k"], s["v"], W, b, causal=w.causal, map=w.map)
+            s["dy"] = draw(shp, 1.0)
+        grads = [(torch.empty_like(sets[0]["q"]), torch.empty_like(sets[0]["q"]), torch.empty_like(sets[0]["q"]),
+                  torch.empty((w.H, w.d, w.d), dtype=torch.float32, device=dev),
+                  torch.empty((w.H, w.d), dtype=torch.float32, device=dev) if b is not None else None)
+                 for _ in range(N_SETS)]
+
+        def step(i, st):
+            s = sets[i % N_SETS]
+            dq, dk, dv, dW, db = grads[i % N_SETS]
+            hh.hh_linattn_bwd(s["q"], s["k"], s["v"], W, b, s["y"], s["dy"], causal=w.causal, map=w.map, dq=dq,
+                              dk=dk, dv=dv, dW=dW, db=db, workspace=wss[i % N_SETS], stream=st)
+        flops, byts = backward_counts(w)
     elif distill:
         need = hh.hh_distill_loss_workspace(w.map, w.dtype, w.B, w.H, w.N, w.d)
         wss = [torch.empty((max(need, 16),), dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
@@ -316,6 +350,9 @@ def main():
                 "unit": "TFLOP/s", "frac": round(ach_tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None}
     if decode:
         roof["kernel"] = "hh_linattn_decode_step (decode_kernel)"
+    elif backward:
+        roof["kernel"] = ("hh_linattn_bwd: every kernel of one call (feature maps, forward segment sums and scan, "
+                          "q-side pass, reverse-sum scan, k-side pass, feature-map backward, dW/db reduction)")
     elif distill:
         roof["kernel"] = "hh_distill_loss: every kernel of one call (feature map of k, then distill_kernel, which maps its queries itself)"
     elif w.map == wl.MAP_TAYLOR2:
@@ -365,6 +402,22 @@ def main():
                "cpu_model": cpu_model,
                "value_1_thread": round(len(rows) * w.B / t1, 2),
                "sample_1_thread": f"one round of 16 query rows per head on 1 thread, {t1:.2f} s wall"}
+    elif not args.no_cpu_baseline and backward:
+        import oracle
+        nthr = oracle.default_threads()
+        xw = host0
+        rng = np.random.default_rng(w.seed + 1)
+        hs = min(w.H, nthr)  # a bounded sample: the oracle's explicit form costs N^2 per head
+        dy = rng.standard_normal((w.B, hs, w.N, w.d))
+        sub = {k_: xw[k_][:, :hs] for k_ in ("q", "k", "v")}
+        t0 = time.perf_counter()
+        oracle.backward(w.map, sub["q"], sub["k"], sub["v"], xw["W"][:hs], xw["b"][:hs], dy, causal=w.causal,
+                        nthreads=nthr)
+        tc = time.perf_counter() - t0
+        cpu = {"value": round(w.B * w.N * hs / w.H / tc, 1), "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+               "sample": f"the backward of {hs} of the {w.H} heads of {w.name} (B{w.B} N{w.N} d{w.d}) by the fp64 "
+                         f"oracle's explicit form, {tc:.2f} s wall on {nthr} threads; scaled to the full workload",
+               "cpu_model": cpu_model}
     elif not args.no_cpu_baseline and not decode:
         import oracle
         nthr = oracle.default_threads()
@@ -396,6 +449,7 @@ def main():
     out = {
         "metric": (METRIC if w.name == "c3_llama2_causal" else
                    "decode step tokens/s (one token per sequence)" if decode else
+                   "backward tokens/s (dq, dk, dv, dW, db) at Llama-2-7B heads" if backward else
                    "distillation loss (Eq. 4) query tokens/s at Llama-2-7B heads" if distill else
                    f"{'causal' if w.causal else 'bidirectional'} linear-attn fwd tokens/s (\u03c6 incl.), {w.name}"),
         "value": round(value, 1),

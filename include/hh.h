@@ -134,6 +134,30 @@ hh_status_t hh_linattn_fwd_noalloc(int map, int dtype, int causal, int B, int H,
                                    const float *S0, const float *z0,
                                    void *y, float *S_out, float *z_out, void *stream);
 
+/* Bytes of workspace hh_linattn_bwd needs (0 for invalid or unsupported arguments, or N == 0). */
+size_t hh_linattn_bwd_workspace(int map, int dtype, int causal, int B, int H, int N, int d);
+
+/* Backward of hh_linattn_fwd: the gradients of a loss L given dL/dy, for training end to end
+ * with the task loss (section 3.4, "Training Protocols for the Three Regimes").  With
+ * den_i = sum_j phi(q_i).phi(k_j) over the keys query i sees, g_i = dy_i / den_i and
+ * c_i = -(dy_i . y_i) / den_i:  dL/dphi(q_i) = sum_j phi(k_j) (v_j . g_i + c_i),
+ * dL/dphi(k_j) = sum_i phi(q_i) (v_j . g_i + c_i), dL/dv_j = sum_i phi(q_i).phi(k_j) g_i, then
+ * the chain rule through the feature map to dq, dk, dW, db.  The sequence starts from a zero
+ * state (no S0).
+ *   map: every map with a W (the Taylor map returns HH_EUNSUPPORTED); dtype: HH_BF16 only.
+ *   q, k, v, W, b as in hh_linattn_fwd; y [B][H][N][d] the forward's output; dy = dL/dy.
+ *   dq, dk, dv [B][H][N][d] (bf16) outputs; dW [H][d][d] and db [H][d] fp32 outputs, summed
+ *   over the batch, the tokens and both q and k (db NULL exactly when the map has no bias or b
+ *   is NULL).  No output may overlap an input or another output.
+ *   workspace: at least hh_linattn_bwd_workspace() bytes.
+ * Features, the products' operands (g, the intra-chunk weights) and dq, dk, dv are rounded to
+ * bf16; sums run in fp32. */
+hh_status_t hh_linattn_bwd(int map, int dtype, int causal, int B, int H, int N, int d,
+                           const void *q, const void *k, const void *v,
+                           const void *W, const void *b, const void *y, const void *dy,
+                           void *dq, void *dk, void *dv, float *dW, float *db,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
 /* One recurrent decode step (running-sum update of section 3.4, "Complexity
  * Analysis"): for each (b, h), with f = phi(k), g = phi(q):
  *     S += f v^T;  z += f;  y = g^T S / g^T z     (update, then read: j <= i)

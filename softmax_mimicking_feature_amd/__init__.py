@@ -22,6 +22,7 @@ from ._lib import (HH_BF16, HH_EHIP, HH_EINVAL, HH_EUNSUPPORTED, HH_EWORKSPACE, 
                    HH_MAP_HEDGEHOG_SOFTMAX, HH_MAP_SOFTMAX, HH_MAP_TAYLOR2, HH_OK, LibraryMissing)
 
 __all__ = ["hh_feature_dim", "hh_featuremap", "hh_linattn_fwd_workspace", "hh_linattn_fwd", "hh_linattn_fwd_noalloc",
+           "hh_linattn_bwd_workspace", "hh_linattn_bwd",
            "hh_linattn_decode_step", "hh_distill_loss_workspace", "hh_distill_loss", "hh_status_str", "hh_last_error", "hh_abi_version", "HHError",
            "LibraryMissing", "HH_F32", "HH_BF16", "HH_MAP_HEDGEHOG", "HH_MAP_TAYLOR2", "HH_MAP_HEDGEHOG_SOFTMAX",
            "HH_MAP_EXP", "HH_MAP_SOFTMAX", "HH_OK", "HH_EINVAL",
@@ -228,6 +229,56 @@ def hh_linattn_fwd_noalloc(q, k, v, W=None, b=None, *, causal: bool = True, map:
     if S_out is not None:
         return out, S_out, z_out
     return out
+
+
+def hh_linattn_bwd_workspace(map: int, dtype: int, causal: bool, B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.load().hh_linattn_bwd_workspace(map, dtype, int(bool(causal)), B, H, N, d))
+
+
+def hh_linattn_bwd(q, k, v, W, b, y, dy, *, causal: bool = True, map: int = HH_MAP_HEDGEHOG, dq=None, dk=None,
+                   dv=None, dW=None, db=None, workspace=None, stream=None):
+    """Backward of hh_linattn_fwd given y (its output) and dy = dL/dy, all [B,H,N,d] bf16.
+
+    Returns (dq, dk, dv, dW, db): dq, dk, dv bf16 [B,H,N,d]; dW [H,d,d] and db [H,d] fp32 (db
+    None for the maps without a bias or when b is None)."""
+    lib = _lib.load()
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B,H,N,d], got {list(q.shape)}")
+    B, H, N, d = q.shape
+    for t, nm in ((k, "k"), (v, "v"), (y, "y"), (dy, "dy"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _shape(t, nm, q.shape)
+    W, b = _map_params(map, W, b, H, d)
+    if W is None:
+        raise ValueError("the backward needs a map with a W")
+    has_db = b is not None
+    _shape(dW, "dW", (H, d, d))
+    _shape(db, "db", (H, d))
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (y, "y"), (dy, "dy")):
+        _dev(t, nm, q.dtype)
+    dt = _dtype_code(q)
+    _dev(W, "W", q.dtype)
+    _dev(b, "b", q.dtype)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    dW = torch.empty((H, d, d), dtype=torch.float32, device=q.device) if dW is None else dW
+    if has_db and db is None:
+        db = torch.empty((H, d), dtype=torch.float32, device=q.device)
+    if not has_db:
+        db = None
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _dev(t, nm, q.dtype)
+    _dev(dW, "dW", torch.float32)
+    _dev(db, "db", torch.float32)
+    need = lib.hh_linattn_bwd_workspace(map, dt, int(bool(causal)), B, H, N, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.hh_linattn_bwd(map, dt, int(bool(causal)), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(b),
+                              _ptr(y), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dW), _ptr(db), _ptr(workspace),
+                              ws_bytes, _stream(stream)))
+    return dq, dk, dv, dW, db
 
 
 def hh_linattn_decode_step(q, k, v, W, b, S, z, *, map: int = HH_MAP_HEDGEHOG, out=None, stream=None):

@@ -14,7 +14,8 @@ HH_MAP_HEDGEHOG, HH_MAP_TAYLOR2, HH_MAP_HEDGEHOG_SOFTMAX, HH_MAP_EXP, HH_MAP_SOF
 
 # Every function declared in include/hh.h.
 EXPORTS = ("hh_abi_version", "hh_feature_dim", "hh_featuremap", "hh_linattn_fwd_workspace",
-           "hh_linattn_fwd", "hh_linattn_fwd_noalloc", "hh_linattn_decode_step", "hh_distill_loss_workspace", "hh_distill_loss",
+           "hh_linattn_fwd", "hh_linattn_fwd_noalloc", "hh_linattn_bwd_workspace", "hh_linattn_bwd",
+           "hh_linattn_decode_step", "hh_distill_loss_workspace", "hh_distill_loss",
            "hh_status_str", "hh_last_error")
 
 
@@ -54,6 +55,10 @@ def load() -> ctypes.CDLL:
     lib.hh_linattn_fwd.restype = I
     lib.hh_linattn_fwd_noalloc.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
     lib.hh_linattn_fwd_noalloc.restype = I
+    lib.hh_linattn_bwd_workspace.argtypes = [I, I, I, I, I, I, I]
+    lib.hh_linattn_bwd_workspace.restype = Z
+    lib.hh_linattn_bwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.hh_linattn_bwd.restype = I
     lib.hh_linattn_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P]
     lib.hh_linattn_decode_step.restype = I
     lib.hh_distill_loss_workspace.argtypes = [I, I, I, I, I, I]

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libhh.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 ARCH = os.environ.get("HH_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["hh_api.cpp", "hh_wide.hip", "hh_narrow.hip", "hh_misc.hip", "hh_distill.hip", "hh_noalloc.hip", "hh_feat.hip"]
+SOURCES = ["hh_api.cpp", "hh_wide.hip", "hh_narrow.hip", "hh_misc.hip", "hh_distill.hip", "hh_noalloc.hip", "hh_feat.hip", "hh_bwd.hip"]
 
 
 def _hipcc() -> str:

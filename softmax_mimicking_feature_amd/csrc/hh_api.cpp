@@ -170,6 +170,42 @@ Plan make_plan(int map, int dtype, int causal, long BH, long N, int d, bool has_
     return pl;
 }
 
+// Workspace of the backward: phi(q), phi(k) bf16, dphi(q), dphi(k) fp32, den and c per token,
+// forward and reverse segment sums (canonical fp32 slots), and the parts of dW, db.
+struct BwdPlan {
+    int dp = 0, dpp = 0, nseg = 1, seg_len = 0, wgs = 0;
+    size_t off_phik, off_dphiq, off_dphik, off_denc, off_S, off_z, off_R, off_r, off_parts, bytes = 0;
+};
+
+BwdPlan make_bwd_plan(int map, long BH, long N, int d) {
+    BwdPlan f;
+    f.dp = feature_dim(map, d);
+    f.dpp = hh::feat_padded_dim(f.dp);
+    const long C = 64, nch = (N + C - 1) / C;
+    long nseg = 256L / BH;  // one workgroup of d / 16 waves per segment
+    if (nseg < 1) nseg = 1;
+    if (nseg > nch) nseg = nch;
+    const long seg_chunks = (nch + nseg - 1) / nseg;
+    nseg = (nch + seg_chunks - 1) / seg_chunks;
+    f.nseg = (int)nseg;
+    f.seg_len = (int)(seg_chunks * C);
+    f.wgs = hh::bwd_wgs_per_seq((int)N);
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t phi = up((size_t)BH * N * f.dp * 2), dphi = up((size_t)BH * N * f.dp * 4);
+    const size_t slotS = up((size_t)BH * nseg * f.dpp * d * 4), slotz = up((size_t)BH * nseg * f.dpp * 4);
+    f.off_phik = phi;
+    f.off_dphiq = 2 * phi;
+    f.off_dphik = f.off_dphiq + dphi;
+    f.off_denc = f.off_dphik + dphi;
+    f.off_S = f.off_denc + up((size_t)BH * N * 8);
+    f.off_z = f.off_S + slotS;
+    f.off_R = f.off_z + slotz;
+    f.off_r = f.off_R + slotS;
+    f.off_parts = f.off_r + slotz;
+    f.bytes = f.off_parts + up((size_t)BH * f.wgs * ((size_t)d * d + d) * 4);
+    return f;
+}
+
 }  // namespace
 
 extern "C" {
@@ -471,6 +507,120 @@ hh_status_t hh_linattn_fwd_noalloc(int map, int dtype, int causal, int B, int H,
     }
     return hh_linattn_fwd(map, dtype, causal, B, H, N, d, q, k, v, W, b, S0, z0, y, S_out, z_out, ws,
                           need > 0 ? hh::kNoAllocScratchBytes : 0, stream);
+}
+
+size_t hh_linattn_bwd_workspace(int map, int dtype, int causal, int B, int H, int N, int d) {
+    if (check_common(map, dtype, B, H, N, d) != HH_OK || (causal != 0 && causal != 1) || dtype != HH_BF16 ||
+        map == HH_MAP_TAYLOR2 || N == 0)
+        return 0;
+    return make_bwd_plan(map, (long)B * H, N, d).bytes;
+}
+
+hh_status_t hh_linattn_bwd(int map, int dtype, int causal, int B, int H, int N, int d, const void *q, const void *k,
+                           const void *v, const void *W, const void *b, const void *y, const void *dy, void *dq,
+                           void *dk, void *dv, float *dW, float *db, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    hh_status_t st = check_common(map, dtype, B, H, N, d);
+    if (st != HH_OK) return st;
+    if (causal != 0 && causal != 1) return fail(HH_EINVAL, "causal must be 0 or 1 (got %d)", causal);
+    if (dtype != HH_BF16) return fail(HH_EUNSUPPORTED, "backward: bf16 inputs only");
+    if (map == HH_MAP_TAYLOR2) return fail(HH_EUNSUPPORTED, "backward: maps with a W only");
+    const bool need = N > 0;
+    const char *names[9] = {"q", "k", "v", "y", "dy", "dq", "dk", "dv", "dW"};
+    const void *ptrs[9] = {q, k, v, y, dy, dq, dk, dv, dW};
+    for (int i = 0; i < 9; i++)
+        if ((st = check_ptr(ptrs[i], names[i], need || i == 8)) != HH_OK) return st;
+    if ((st = check_params(map, W, b, true)) != HH_OK) return st;
+    if ((st = check_ptr(db, "db", false)) != HH_OK) return st;
+    if (map_has_b(map) ? (b != nullptr) != (db != nullptr) : db != nullptr)
+        return fail(HH_EINVAL, "db must be given exactly when the map has a bias and b is given");
+    const long BH = (long)B * H;
+    const size_t nio = (size_t)BH * N * d * 2, nW = (size_t)H * d * d * 4, nb = (size_t)H * d * 4;
+    const void *ins[6] = {q, k, v, y, dy, W};
+    void *outs[3] = {dq, dk, dv};
+    for (int o = 0; o < 3; o++) {
+        for (int i = 0; i < 6; i++)
+            if (overlap(outs[o], nio, ins[i], i == 5 ? (size_t)H * d * d * 2 : nio))
+                return fail(HH_EINVAL, "an input gradient overlaps an input");
+        for (int o2 = o + 1; o2 < 3; o2++)
+            if (overlap(outs[o], nio, outs[o2], nio)) return fail(HH_EINVAL, "input gradients overlap");
+        if (overlap(outs[o], nio, dW, nW) || overlap(outs[o], nio, db, nb)) return fail(HH_EINVAL, "gradients overlap");
+    }
+    if (overlap(dW, nW, db, nb)) return fail(HH_EINVAL, "dW overlaps db");
+    const BwdPlan pl = make_bwd_plan(map, BH, N, d);
+    if (N > 0) {
+        if (!workspace) return fail(HH_EWORKSPACE, "workspace of %zu bytes required, got NULL", pl.bytes);
+        if (workspace_bytes < pl.bytes)
+            return fail(HH_EWORKSPACE, "workspace of %zu bytes required, got %zu", pl.bytes, workspace_bytes);
+        if (!aligned16(workspace)) return fail(HH_EINVAL, "workspace is not 16-byte aligned");
+        for (int i = 0; i < 6; i++)
+            if (overlap(workspace, pl.bytes, ins[i], i == 5 ? (size_t)H * d * d * 2 : nio))
+                return fail(HH_EINVAL, "workspace overlaps an input");
+        for (int o = 0; o < 3; o++)
+            if (overlap(workspace, pl.bytes, outs[o], nio)) return fail(HH_EINVAL, "workspace overlaps an output");
+        if (overlap(workspace, pl.bytes, dW, nW) || overlap(workspace, pl.bytes, db, nb))
+            return fail(HH_EINVAL, "workspace overlaps an output");
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    clear_stale_hip_error();
+    hipError_t e;
+    if (N == 0) {  // no tokens: the parameter gradients are zero
+        e = hh::launch_state_copy(nullptr, nullptr, dW, db ? db : dW, (long)H * d * d, db ? (long)H * d : 0, s);
+        if (e != hipSuccess) return hip_fail(e, "zero gradients launch");
+        return ok();
+    }
+    char *ws = reinterpret_cast<char *>(workspace);
+    hh::bf16_t *phiq = reinterpret_cast<hh::bf16_t *>(ws), *phik = reinterpret_cast<hh::bf16_t *>(ws + pl.off_phik);
+    // features of q and k (bf16, as the forward's matrix cores take them)
+    if (map == HH_MAP_HEDGEHOG) {
+        e = hh::launch_featuremap_hedgehog_bf16(d, (const hh::bf16_t *)q, (const hh::bf16_t *)W, (const hh::bf16_t *)b,
+                                                phiq, (int)BH, H, N, s);
+        if (e == hipSuccess)
+            e = hh::launch_featuremap_hedgehog_bf16(d, (const hh::bf16_t *)k, (const hh::bf16_t *)W,
+                                                    (const hh::bf16_t *)b, phik, (int)BH, H, N, s);
+    } else {
+        e = hh::launch_featuremap_variant(map, dtype, d, q, W, b, phiq, BH, H, N, s);
+        if (e == hipSuccess) e = hh::launch_featuremap_variant(map, dtype, d, k, W, b, phik, BH, H, N, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "feature map launch");
+    float *Ssl = reinterpret_cast<float *>(ws + pl.off_S), *zsl = reinterpret_cast<float *>(ws + pl.off_z);
+    float *Rsl = reinterpret_cast<float *>(ws + pl.off_R), *rsl = reinterpret_cast<float *>(ws + pl.off_r);
+    // forward sums per segment (canonical), scanned into exclusive prefixes (causal) or the total
+    hh::FeatParams fp;
+    memset(&fp, 0, sizeof fp);
+    fp.phiq = phiq; fp.phik = phik; fp.v = (const hh::bf16_t *)v;
+    fp.S_slots = Ssl; fp.z_slots = zsl; fp.slot_bh_stride = pl.nseg; fp.slot_canonical = 1;
+    fp.N = N; fp.seg_len = pl.seg_len;
+    const int nstate = causal ? pl.nseg - 1 : pl.nseg;
+    if (nstate > 0) {
+        fp.nseg_grid = nstate;
+        e = hh::launch_feat(d, pl.dp, 0, fp, (int)(BH * nstate), s);
+        if (e == hipSuccess && pl.nseg > 1) e = hh::launch_feat_scan(Ssl, zsl, d, pl.dp, (int)BH, pl.nseg, causal ? 0 : 1, s);
+        if (e != hipSuccess) return hip_fail(e, "forward sums launch");
+    }
+    hh::BwdParams bp;
+    memset(&bp, 0, sizeof bp);
+    bp.phiq = phiq; bp.phik = phik; bp.v = (const hh::bf16_t *)v; bp.y = (const hh::bf16_t *)y;
+    bp.dy = (const hh::bf16_t *)dy; bp.q = (const hh::bf16_t *)q; bp.k = (const hh::bf16_t *)k;
+    bp.W = (const hh::bf16_t *)W; bp.b = map_has_b(map) ? (const hh::bf16_t *)b : nullptr;
+    bp.dphiq = reinterpret_cast<float *>(ws + pl.off_dphiq); bp.dphik = reinterpret_cast<float *>(ws + pl.off_dphik);
+    bp.den_c = reinterpret_cast<float *>(ws + pl.off_denc);
+    bp.S_slots = Ssl; bp.z_slots = zsl; bp.R_slots = Rsl; bp.r_slots = rsl;
+    bp.dq = (hh::bf16_t *)dq; bp.dk = (hh::bf16_t *)dk; bp.dv = (hh::bf16_t *)dv;
+    bp.dW_parts = reinterpret_cast<float *>(ws + pl.off_parts);
+    bp.N = N; bp.H = H; bp.nseg = pl.nseg; bp.seg_len = pl.seg_len;
+    e = hh::launch_bwd_pass(0, d, pl.dp, causal, bp, (int)(BH * pl.nseg), s);
+    if (e != hipSuccess) return hip_fail(e, "q-side backward launch");
+    if (pl.nseg > 1) {
+        e = hh::launch_feat_scan(Rsl, rsl, d, pl.dp, (int)BH, pl.nseg, causal ? 0 : 1, s);
+        if (e != hipSuccess) return hip_fail(e, "reverse sums launch");
+    }
+    e = hh::launch_bwd_pass(1, d, pl.dp, causal, bp, (int)(BH * pl.nseg), s);
+    if (e != hipSuccess) return hip_fail(e, "k-side backward launch");
+    e = hh::launch_bwd_map(map, d, bp, BH, s);
+    if (e == hipSuccess) e = hh::launch_bwd_reduce(bp.dW_parts, dW, db, B, H, d, N, s);
+    if (e != hipSuccess) return hip_fail(e, "feature-map backward launch");
+    return ok();
 }
 
 size_t hh_distill_loss_workspace(int map, int dtype, int B, int H, int N, int d) {

@@ -337,10 +337,17 @@ __device__ void feat_body(const FeatParams &p, unsigned char *smem, int bh, int 
     if (MODE == FM_STATE) {
         const size_t sl = (size_t)bh * p.slot_bh_stride + s;
         float *img = p.S_slots + sl * K::DPP * D;
+        if (p.slot_canonical) {  // [dpp][d] row-major, for the backward passes
 #pragma unroll
-        for (int j = 0; j < K::FB / 2; j++) {
-            *fslot(img, w * (K::FB / 2) + j, 0, lane) = sacc[2 * j];
-            *fslot(img, w * (K::FB / 2) + j, 1, lane) = sacc[2 * j + 1];
+            for (int fb = 0; fb < K::FB; fb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) img[(size_t)(16 * fb + 4 * g + r) * D + 16 * w + r16] = sacc[fb][r];
+        } else {
+#pragma unroll
+            for (int j = 0; j < K::FB / 2; j++) {
+                *fslot(img, w * (K::FB / 2) + j, 0, lane) = sacc[2 * j];
+                *fslot(img, w * (K::FB / 2) + j, 1, lane) = sacc[2 * j + 1];
+            }
         }
         float *zs = p.z_slots + sl * K::DPP;
         if (r16 == 0) {

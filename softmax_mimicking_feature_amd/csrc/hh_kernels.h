@@ -100,6 +100,7 @@ struct FeatParams {
     long slot_bh_stride;
     int N, seg_len, nseg_grid;
     int slot_mode;                  // 0 none, 1 exclusive prefix in slot s, 2 total in slot 0, 3 sum of slots < s
+    int slot_canonical;             // state mode: write S as [dpp][d] row-major instead of the register image
 };
 hipError_t launch_feat(int d, int dp, int mode, const FeatParams &p, int grid, hipStream_t st);
 hipError_t launch_feat_scan(float *S, float *z, int d, int dp, int BH, int nseg, int mode, hipStream_t st);
@@ -109,6 +110,25 @@ int feat_padded_dim(int dp);
 // softmax): bf16 on the matrix cores, fp32 on the vector units.  x [BH][N][d] -> phi [BH][N][d'].
 hipError_t launch_featuremap_variant(int map, int dtype, int d, const void *x, const void *W, const void *b, void *phi,
                                      long BH, int H, int N, hipStream_t st);
+
+// Backward of the forward over given features (hh_bwd.hip).  Per sequence bh: phi(q), phi(k)
+// [N][d'] bf16; v, y, dy [N][d] bf16; dphi(q), dphi(k) [N][d'] fp32 and den, c [N][2] fp32 written
+// by the q-side pass; forward sums S, z and reverse sums R, r per segment in canonical fp32 slots
+// ([nseg][dpp][d], [nseg][dpp]).
+struct BwdParams {
+    const bf16_t *phiq, *phik, *v, *y, *dy, *q, *k, *W, *b;
+    float *dphiq, *dphik, *den_c;
+    const float *S_slots, *z_slots;
+    float *R_slots, *r_slots;
+    bf16_t *dq, *dk, *dv;
+    float *dW_parts;               // [BH * wgs_per_seq][d*d + d]
+    int N, H, nseg, seg_len;
+};
+// which = 0: q-side pass, 1: k-side pass (grid = BH * nseg)
+hipError_t launch_bwd_pass(int which, int d, int dp, int causal, const BwdParams &p, int grid, hipStream_t st);
+hipError_t launch_bwd_map(int map, int d, const BwdParams &p, long BH, hipStream_t st);
+hipError_t launch_bwd_reduce(const float *parts, float *dW, float *db, int B, int H, int d, int N, hipStream_t st);
+int bwd_wgs_per_seq(int N);
 
 // fp32 path: one workgroup per (b,h) walks the sequence token by token.
 struct SeqParams {

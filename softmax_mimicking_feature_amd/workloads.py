@@ -86,6 +86,11 @@ def _cfg() -> Dict[str, Workload]:
         qk_scale=s3, v_scale=s3, w_std=128 ** -0.5, b_std=0.0,
         description="Llama-2-7B-shaped causal with the softmax-over-features map per half (no bias), bf16, "
                     "B1 H32 N4096 d128 d'256 (the causal workload's inputs)")
+    c["c3_llama2_backward"] = Workload(
+        "c3_llama2_backward", MAP_HEDGEHOG, DT_BF16, True, B=1, H=32, N=4096, d=128, seed=1003,
+        qk_scale=s3, v_scale=s3, w_std=128 ** -0.5, b_std=0.0,
+        description="backward (dq, dk, dv, dW, db) of the Llama-2-7B-shaped causal forward, bf16, "
+                    "B1 H32 N4096 d128 (the causal workload's inputs; dL/dy ~ N(0,1))")
     c["c4_bert_bidir"] = Workload(
         "c4_bert_bidir", MAP_HEDGEHOG, DT_BF16, False, B=32, H=12, N=512, d=64, seed=1004,
         qk_scale=1.0, v_scale=1.0, w_std=64 ** -0.5, b_std=0.0,
