@@ -1243,8 +1243,11 @@ hipError_t launch_bidir_fused(int d, const WideParams &p, int BH, hipStream_t st
 // two chunks ahead.
 struct CausalWsCfg {
     static constexpr int D = 128, C = 32, DP = 256, NT = 512;
-    static constexpr int RQ = DP + 16, RK = DP + 12, RA = C + 8;
-    static constexpr int SZ_PQ = C * RQ * 2, SZ_PK = C * RK * 2, SZ_X = C * D * 2, SZ_A = C * RA * 2;
+    // phi(q) [C][RQ] row-major (features in the permuted order); phi(k) transposed, [DP][PT]
+    // (rows features in natural order, C tokens each, 96-byte rows), so that the consumers'
+    // state-update operands (feature rows, K = tokens) are plain 16-byte reads
+    static constexpr int RQ = DP + 16, PT = C + 16, RA = C + 8;
+    static constexpr int SZ_PQ = C * RQ * 2, SZ_PK = DP * PT * 2, SZ_X = C * D * 2, SZ_A = C * RA * 2;
     static constexpr int NDEN = 6;                        // 4 consumer normaliser partials + 2 row sums
     static constexpr int SZ_DEN = NDEN * C * 4;
     static constexpr int OFF_PQ = 0;
@@ -1267,8 +1270,9 @@ struct CausalWsCfg {
 // that one wave keeps the LDS, matrix and vector pipes busy at once.
 template <bool FULL>
 __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsigned char *xk, int valid,
-                                             const bf16x8 (&wA)[4][4], const float (&bl2)[4][4], int p, int g,
-                                             int r16, bf16_t *sPQ, bf16_t *sPK) {
+                                             const bf16x8 (&wA)[4][4], const float (&bl2)[4][4],
+                                             const float (&bk2)[4], int p, int g, int r16, bf16_t *sPQ,
+                                             bf16_t *sPKT) {
     using S = CausalWsCfg;
     const int i = 16 * (p & 1) + r16;
     bf16x8 xb[2][4];  // [keys, queries][K step]
@@ -1276,6 +1280,9 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
     for (int t = 0; t < 2; t++)
 #pragma unroll
         for (int ks = 0; ks < 4; ks++) xb[t][ks] = staged_x_operand<128>(t == 0 ? xk : xq, i, ks, g);
+    // keys: u (tokens x directions), lane: direction 64 (p >> 1) + 16 mb + r16, tokens 4 g + r;
+    // queries: u^T (directions x tokens), lane: token i, directions 64 (p >> 1) + 16 mb + 4 g + r.
+    // The A and B operands hold the same per-lane data, so only their roles swap.
     f32x4 acc[2][4];
 #pragma unroll
     for (int t = 0; t < 2; t++)
@@ -1284,58 +1291,72 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
 #pragma unroll
     for (int ks = 0; ks < 4; ks++)
 #pragma unroll
-        for (int t = 0; t < 2; t++)
-#pragma unroll
-            for (int mb = 0; mb < 4; mb++) acc[t][mb] = mfma_bf16(wA[mb][ks], xb[t][ks], acc[t][mb]);
+        for (int mb = 0; mb < 4; mb++) {
+            acc[0][mb] = mfma_bf16(xb[0][ks], wA[mb][ks], acc[0][mb]);
+            acc[1][mb] = mfma_bf16(wA[mb][ks], xb[1][ks], acc[1][mb]);
+        }
     const int f0 = 64 * (p >> 1) + 4 * g;
+    {  // keys: phi(k)^T rows 64 (p >> 1) + 16 mb + r16 and 128 + that, tokens 16 (p & 1) + 4 g .. + 3
+        const int fk = 64 * (p >> 1) + r16;
+        const int tk = 16 * (p & 1) + 4 * g;
 #pragma unroll
-    for (int t = 0; t < 2; t++) {  // 0: keys, 1: queries
+        for (int mb = 0; mb < 4; mb++) {
+            f32x4 ep, en;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float u = acc[0][mb][r] * kLog2e + bk2[mb];
+                ep[r] = exp2_fast(u);
+                en[r] = exp2_fast(-u);
+                if (!FULL && tk + r >= valid) ep[r] = en[r] = 0.0f;  // keys past the end contribute nothing
+            }
+            store4(sPKT + (fk + 16 * mb) * S::PT + tk, to_bf16x4(ep));
+            store4(sPKT + (128 + fk + 16 * mb) * S::PT + tk, to_bf16x4(en));
+        }
+    }
+    {  // queries: direction blocks 2 h, 2 h + 1 share one 16-byte run of their 32-feature group
         bf16x4 pe[4], ne[4];
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) {
             f32x4 ep, en;
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const float u = acc[t][mb][r] * kLog2e + bl2[mb][r];
+                const float u = acc[1][mb][r] * kLog2e + bl2[mb][r];
                 ep[r] = exp2_fast(u);
                 en[r] = exp2_fast(-u);
-            }
-            if (!FULL && t == 0 && i >= valid) {  // keys past the end contribute nothing
-                ep = zero4();
-                en = zero4();
             }
             pe[mb] = to_bf16x4(ep);
             ne[mb] = to_bf16x4(en);
         }
-        if (t == 0) {
 #pragma unroll
-            for (int mb = 0; mb < 4; mb++) {
-                store4(sPK + i * S::RK + feat_pos<true>(f0 + 16 * mb), pe[mb]);
-                store4(sPK + i * S::RK + feat_pos<true>(128 + f0 + 16 * mb), ne[mb]);
-            }
-        } else {  // direction blocks 2 h, 2 h + 1 share one 16-byte run of their 32-feature group
-#pragma unroll
-            for (int hh = 0; hh < 2; hh++) {
-                store8(sPQ + i * S::RQ + feat_pos<true>(f0 + 32 * hh), cat(pe[2 * hh], pe[2 * hh + 1]));
-                store8(sPQ + i * S::RQ + feat_pos<true>(128 + f0 + 32 * hh), cat(ne[2 * hh], ne[2 * hh + 1]));
-            }
+        for (int hh = 0; hh < 2; hh++) {
+            store8(sPQ + i * S::RQ + feat_pos<true>(f0 + 32 * hh), cat(pe[2 * hh], pe[2 * hh + 1]));
+            store8(sPQ + i * S::RQ + feat_pos<true>(128 + f0 + 32 * hh), cat(ne[2 * hh], ne[2 * hh + 1]));
         }
     }
 }
 
 // Full chunks skip the per-lane masking of keys past the end.
 __device__ __forceinline__ void cws_features_any(const unsigned char *xq, const unsigned char *xk, int valid,
-                                                 const bf16x8 (&wA)[4][4], const float (&bl2)[4][4], int p, int g,
-                                                 int r16, bf16_t *sPQ, bf16_t *sPK) {
+                                                 const bf16x8 (&wA)[4][4], const float (&bl2)[4][4],
+                                                 const float (&bk2)[4], int p, int g, int r16, bf16_t *sPQ,
+                                                 bf16_t *sPKT) {
     if (valid >= CausalWsCfg::C)
-        cws_features<true>(xq, xk, valid, wA, bl2, p, g, r16, sPQ, sPK);
+        cws_features<true>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
     else
-        cws_features<false>(xq, xk, valid, wA, bl2, p, g, r16, sPQ, sPK);
+        cws_features<false>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
+}
+
+// MFMA operand from the transposed phi(k) tile in the permuted feature order of phi(q): lane
+// (g, r16) gets key c0 + r16 and features r0 + 4 g .. + 3, r0 + 16 + 4 g .. + 3 (two transposing
+// reads; lane_off_p = (4 g + r16 / 4) PT + 4 (r16 % 4)).
+__device__ __forceinline__ bf16x8 pkt_operand_perm(const bf16_t *sPKT, int lane_off_p, int r0, int c0) {
+    const bf16_t *p = sPKT + lane_off_p + r0 * CausalWsCfg::PT + c0;
+    return cat(lds_read_tr(p), lds_read_tr(p + 16 * CausalWsCfg::PT));
 }
 
 // Producer: scores of one chunk.  Tasks: p0 (0,0), p1 (1,0), p2 (1,1); p3 clears the masked
 // block (0,1) and the second row-sum slot of query block 0.
-__device__ __forceinline__ void cws_scores(const bf16_t *sPQ, const bf16_t *sPK, bf16_t *sA, float *sDen, int p,
+__device__ __forceinline__ void cws_scores(const bf16_t *sPQ, const bf16_t *sPKT, bf16_t *sA, float *sDen, int p,
                                            int g, int r16) {
     using S = CausalWsCfg;
     if (p == 3) {
@@ -1348,9 +1369,10 @@ __device__ __forceinline__ void cws_scores(const bf16_t *sPQ, const bf16_t *sPK,
     const int ib = p == 0 ? 0 : 1, jb = p == 2 ? 1 : 0, slot = p == 2 ? 5 : 4;
     // all operand reads first, then two product chains over alternate K steps
     bf16x8 ka[8], qb[8];
+    const int lop = (4 * g + (r16 >> 2)) * S::PT + 4 * (r16 & 3);
 #pragma unroll
     for (int ks = 0; ks < 8; ks++) {
-        ka[ks] = load8_as_halves(sPK + (16 * jb + r16) * S::RK + 32 * ks + 8 * g);
+        ka[ks] = pkt_operand_perm(sPKT, lop, 32 * ks, 16 * jb);
         qb[ks] = load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1442,7 +1464,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     const DmaLanes128<32> dl(w, lane);
     auto valid_of = [&](int c) { return min(S::C, t_end - (t_begin + S::C * c)); };
     auto pq_buf = [&](int b) { return reinterpret_cast<bf16_t *>(smem + S::OFF_PQ + b * S::SZ_PQ); };
-    auto pk_buf = [&](int b) { return reinterpret_cast<bf16_t *>(smem + S::OFF_PK + b * S::SZ_PK); };
+    auto pk_buf = [&](int b) { return reinterpret_cast<bf16_t *>(smem + S::OFF_PK + b * S::SZ_PK); };  // phi(k)^T
     auto v_buf = [&](int b) { return reinterpret_cast<const bf16_t *>(smem + S::OFF_V + b * S::SZ_X); };
     auto a_buf = [&](int b) { return reinterpret_cast<bf16_t *>(smem + S::OFF_A + b * S::SZ_A); };
     auto den_buf = [&](int b) { return reinterpret_cast<float *>(smem + S::OFF_DEN + b * S::SZ_DEN); };
@@ -1454,7 +1476,8 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     // one per chunk.
     if (w < 4) {
         bf16x8 wA[4][4];  // W operands, directions 64 (pv >> 1) .. + 63
-        float bl2[4][4];
+        float bl2[4][4];  // bias x log2(e) of the query accumulators' rows (directions 16 mb + 4 g + r)
+        float bk2[4];     // and of the key accumulators' column (direction 16 mb + r16)
         // Producers issue every staging load of the prologue (each moves the 1 KB blocks of waves w
         // and w + 4 of the eight-wave layout), so that the consumers' load queues hold only their
         // own prefix loads below: loads retire in order per wave, and a consumer waiting for a prefix
@@ -1492,9 +1515,13 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
                 for (int r = 0; r < 4; r++) bl2[2 * hh + mb][r] = b2[mb][r];
             }
         }
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++)
+            bk2[mb] = p.b ? bf16_bits_to_float(p.b[(size_t)h * 128 + 64 * (pv >> 1) + 16 * mb + r16]) * kLog2e : 0.0f;
         producer_barrier(psync, 8, lane);
         if (n > 0)
-            cws_features_any(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, pv, g, r16, pq_buf(0), pk_buf(0));
+            cws_features_any(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, bk2, pv, g, r16, pq_buf(0),
+                             pk_buf(0));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int c = 0; c < n; c++) {
@@ -1503,7 +1530,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
             cws_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), pv, g, r16);
             if (c + 1 < n)
                 cws_features_any(smem + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, smem + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
-                             valid_of(c + 1), wA, bl2, pv, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1));
+                             valid_of(c + 1), wA, bl2, bk2, pv, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -1575,7 +1602,6 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     f32x4 numT[2][2];
 #pragma unroll
     for (int ib = 0; ib < 2; ib++) numT[ib][0] = numT[ib][1] = zero4();
-    const int lane_k = (8 * g + (r16 >> 2)) * S::RK + 8 * (r16 & 3);
     const int r0 = 8 * g + (r16 >> 2);
     const int lane_v = r0 * S::D + 8 * v_pos(r0, 4 * pv + (r16 & 3));
     const bf16x8 ones = ones_bf16x8();
@@ -1609,7 +1635,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
 #pragma unroll
             for (int ib = 0; ib < 2; ib++) qo[ib] = load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g);
 #pragma unroll
-            for (int j = 0; j < 2; j++) ao2[j] = operand_down_rows(sPK, lane_k, perm_block_pos(2 * ks + j), S::RK);
+            for (int j = 0; j < 2; j++) ao2[j] = load8(sPK + (32 * ks + 16 * j + r16) * S::PT + 8 * g);
         };
         load_step(0, qn, an);
         __builtin_amdgcn_sched_barrier(0);
@@ -1684,11 +1710,10 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
         float *sDen = den_buf(b2);
         sDen[pv * S::C + r16] = dacc[0][0];
         sDen[pv * S::C + 16 + r16] = dacc[1][0];
-        {  // normaliser rows of this consumer
-            const bf16_t *sPKz = sPK + perm_block_pos(4 * pv);
+        {  // normaliser rows of this consumer (feature blocks 4 pv .. 4 pv + 3)
 #pragma unroll
             for (int zb = 0; zb < 4; zb++)
-                zacc[zb] = mfma_bf16(operand_down_rows(sPKz, lane_k, perm_block_pos(zb), S::RK), ones, zacc[zb]);
+                zacc[zb] = mfma_bf16(load8(sPK + (16 * (4 * pv + zb) + r16) * S::PT + 8 * g), ones, zacc[zb]);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
