@@ -1248,7 +1248,9 @@ struct CausalWsCfg {
     // state-update operands (feature rows, K = tokens) are plain 16-byte reads
     static constexpr int RQ = DP + 16, PT = C + 16, RA = C + 8;
     static constexpr int SZ_PQ = C * RQ * 2, SZ_PK = DP * PT * 2, SZ_X = C * D * 2, SZ_A = C * RA * 2;
-    static constexpr int NDEN = 6;                        // 4 consumer normaliser partials + 2 row sums
+    // per token 8 floats: the 4 consumers' normaliser partials, the 2 score row sums, 2 unused
+    // (one 16-byte and one 8-byte read give a token's six terms)
+    static constexpr int NDEN = 8;
     static constexpr int SZ_DEN = NDEN * C * 4;
     static constexpr int OFF_PQ = 0;
     static constexpr int OFF_PK = OFF_PQ + 2 * SZ_PQ;
@@ -1363,7 +1365,7 @@ __device__ __forceinline__ void cws_scores(const bf16_t *sPQ, const bf16_t *sPKT
         bf16x4 zz;
         zz[0] = zz[1] = zz[2] = zz[3] = (__bf16)0.0f;
         store4(sA + r16 * S::RA + 16 + 4 * g, zz);
-        sDen[5 * S::C + r16] = 0.0f;
+        sDen[r16 * S::NDEN + 5] = 0.0f;
         return;
     }
     const int ib = p == 0 ? 0 : 1, jb = p == 2 ? 1 : 0, slot = p == 2 ? 5 : 4;
@@ -1391,7 +1393,14 @@ __device__ __forceinline__ void cws_scores(const bf16_t *sPQ, const bf16_t *sPKT
     store4(sA + (16 * ib + r16) * S::RA + 16 * jb + 4 * g, ab);
     rs += __shfl_xor(rs, 16);
     rs += __shfl_xor(rs, 32);
-    sDen[slot * S::C + 16 * ib + r16] = rs;  // the same value in all four lane groups
+    sDen[(16 * ib + r16) * S::NDEN + slot] = rs;  // the same value in all four lane groups
+}
+
+// Normaliser of token i: the sum of its six partial terms.
+__device__ __forceinline__ float den_terms(const float *sDen, int i) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(sDen + i * CausalWsCfg::NDEN);
+    const float2 b = *reinterpret_cast<const float2 *>(sDen + i * CausalWsCfg::NDEN + 4);
+    return ((a[0] + a[1]) + (a[2] + a[3])) + (b.x + b.y);
 }
 
 // Consumer: finish the outputs of one chunk (held read-out + intra-chunk product, normalise,
@@ -1408,10 +1417,7 @@ __device__ __forceinline__ void cws_output(f32x4 (&numT)[2][2], const bf16_t *sA
         const bf16x8 a = load8(sA + i * S::RA + 8 * g);
 #pragma unroll
         for (int vb = 0; vb < 2; vb++) numT[ib][vb] = mfma_bf16(vop[vb], a, numT[ib][vb]);
-        float den = 0.0f;
-#pragma unroll
-        for (int sl = 0; sl < S::NDEN; sl++) den += sDen[sl * S::C + i];
-        const float rden = __builtin_amdgcn_rcpf(den);
+        const float rden = __builtin_amdgcn_rcpf(den_terms(sDen, i));
         f32x4 o0, o1;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
@@ -1653,14 +1659,9 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
 #pragma unroll
                     for (int vb = 0; vb < 2; vb++) numT[ib][vb] = mfma_bf16(vp[vb], ao[ib], numT[ib][vb]);
             }
-            if (ks == 1) {  // its normaliser: the partial slots of every wave
+            if (ks == 1) {  // its normaliser: the partial terms of every wave
 #pragma unroll
-                for (int ib = 0; ib < 2; ib++) {
-                    float d = 0.0f;
-#pragma unroll
-                    for (int sl = 0; sl < S::NDEN; sl++) d += sDp[sl * S::C + 16 * ib + r16];
-                    dsum[ib] = d;
-                }
+                for (int ib = 0; ib < 2; ib++) dsum[ib] = den_terms(sDp, 16 * ib + r16);
             }
             bf16x8 sb[2];
 #pragma unroll
@@ -1708,8 +1709,8 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
         }
         // every row of dacc holds the token's partial: all four lane groups write the same value
         float *sDen = den_buf(b2);
-        sDen[pv * S::C + r16] = dacc[0][0];
-        sDen[pv * S::C + 16 + r16] = dacc[1][0];
+        sDen[r16 * S::NDEN + pv] = dacc[0][0];
+        sDen[(16 + r16) * S::NDEN + pv] = dacc[1][0];
         {  // normaliser rows of this consumer (feature blocks 4 pv .. 4 pv + 3)
 #pragma unroll
             for (int zb = 0; zb < 4; zb++)
@@ -1808,41 +1809,59 @@ hipError_t launch_featuremap_hedgehog_bf16(int d, const bf16_t *x, const bf16_t 
     }
 }
 
-// Segment-slot scan (see launch_slot_scan), in fp32: one thread per 4 floats of S or per z
-// entry.  The sum runs over the slots of one (b,h) in segment order; the slot layout does not
-// matter (every slot of a head has the same layout).
+// Scan of the segment slots of each sequence, in place: mode 0 (causal) leaves in slot s the
+// exclusive prefix (the sum of slots 0 .. s - 1) for s >= 1 and in slot nseg - 1 the sum of the
+// first nseg - 1; mode 1 (bidirectional) leaves the total of all nseg slots in slot 0.  One
+// thread per 16 bytes of a slot (S and z alike); each thread loads eight slots before it adds or
+// stores any, so the loads of a sequence are in flight together; the slot layout does not matter
+// (every slot of a sequence has the same one).  Workgroup b works on a
+// sequence of XCD b mod 8 when BH is a multiple of 8, the XCD whose workgroups wrote its slots.
 template <int D>
-__global__ void slot_scan_kernel(float *__restrict__ S, float *__restrict__ z, int BH, int nseg, int mode) {
-    constexpr long PS = 2L * D * D / 4, PZ = 2L * D;
-    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (long)BH * (PS + PZ)) return;
-    const long bh = idx / (PS + PZ), e = idx % (PS + PZ);
-    const int nin = mode == 0 ? nseg - 1 : nseg;
-    if (e < PS) {
-        constexpr long stride = 2L * D * D / 4;
-        f32x4 *base = reinterpret_cast<f32x4 *>(S) + bh * nseg * stride + e;
-        f32x4 run = zero4();
-        for (int s = 0; s < nin; s++) {
-            const f32x4 a = base[s * stride];
-            if (mode == 0 && s > 0) base[s * stride] = run;
-            run += a;
-        }
-        base[mode == 0 ? (long)(nseg - 1) * stride : 0] = run;
+__global__ __launch_bounds__(256) void slot_scan_kernel(float *__restrict__ S, float *__restrict__ z, int BH, int nseg,
+                                                        int mode) {
+    constexpr int PS = 2 * D * D / 4, PZ = 2 * D / 4;  // f32x4 per slot: S, z
+    constexpr int WPH = (PS + PZ + 255) / 256;           // workgroups per sequence
+    const int b = blockIdx.x;
+    int bh, part;
+    if (BH % 8 == 0) {
+        const int j = b >> 3;
+        bh = (b & 7) + 8 * (j / WPH);
+        part = j % WPH;
     } else {
-        float *base = z + bh * nseg * PZ + (e - PS);
-        float run = 0.0f;
-        for (int s = 0; s < nin; s++) {
-            const float a = base[s * PZ];
-            if (mode == 0 && s > 0) base[s * PZ] = run;
-            run += a;
-        }
-        base[mode == 0 ? (long)(nseg - 1) * PZ : 0] = run;
+        bh = b / WPH;
+        part = b % WPH;
     }
+    const int e = part * 256 + threadIdx.x;
+    if (bh >= BH || e >= PS + PZ) return;
+    f32x4 *base;
+    long stride;
+    if (e < PS) {
+        base = reinterpret_cast<f32x4 *>(S) + (long)bh * nseg * PS + e;
+        stride = PS;
+    } else {
+        base = reinterpret_cast<f32x4 *>(z) + (long)bh * nseg * PZ + (e - PS);
+        stride = PZ;
+    }
+    const int nin = mode == 0 ? nseg - 1 : nseg;
+    f32x4 run = zero4();
+    for (int s0 = 0; s0 < nin; s0 += 8) {
+        f32x4 a[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            if (s0 + i < nin) a[i] = base[(s0 + i) * stride];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            if (s0 + i < nin) {
+                if (mode == 0 && s0 + i > 0) base[(s0 + i) * stride] = run;
+                run += a[i];
+            }
+    }
+    base[mode == 0 ? (long)(nseg - 1) * stride : 0] = run;
 }
 
 hipError_t launch_slot_scan(int d, float *S_slots, float *z_slots, int BH, int nseg, int mode, hipStream_t st) {
-    const long total = (long)BH * (2L * d * d / 4 + 2L * d);
-    const unsigned grid = (unsigned)((total + 255) / 256);
+    const long per = ((2L * d * d / 4 + 2L * d / 4) + 255) / 256;
+    const unsigned grid = (unsigned)(BH * per);
     switch (d) {
     case 16: hipLaunchKernelGGL(slot_scan_kernel<16>, dim3(grid), dim3(256), 0, st, S_slots, z_slots, BH, nseg, mode); break;
     case 32: hipLaunchKernelGGL(slot_scan_kernel<32>, dim3(grid), dim3(256), 0, st, S_slots, z_slots, BH, nseg, mode); break;
