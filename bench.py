@@ -114,11 +114,11 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str, decode: bool = False):
-    """HBM bytes per call from the committed FETCH_SIZE / WRITE_SIZE summary of this workload,
-    or None when there is none or the kernels changed since it was taken."""
-    entry = "hh_linattn_decode_step" if decode else "hh_linattn_fwd"
-    path = os.path.join(ROOT, "profiles", f"{entry}_{workload}_traffic.md")
+def recorded_traffic(workload: str, entry: str):
+    """L2-miss bytes per call (read + written, from the TCC request-size counters) in the committed
+    counter summary of this workload, or None when there is none or the kernels changed since it
+    was taken."""
+    path = os.path.join(ROOT, "profiles", f"{entry}_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -340,14 +340,18 @@ def main():
     ai = flops / byts
     ridge = PEAK_MFMA_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     bound = "hbm" if ai < ridge else "mfma"
+    entry = ("hh_linattn_decode_step" if decode else "hh_distill_loss" if distill else
+             "hh_linattn_bwd" if backward else "hh_linattn_fwd")
+    traffic = recorded_traffic(args.workload, entry)
+    traffic_gbs = None if traffic is None else round(traffic / (ms_per_step * 1e-3) / 1e9, 1)
     if bound == "hbm":
-        traffic = recorded_traffic(args.workload, decode)
         roof = {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach_gbs / PEAK_HBM_GBS, 4),
-                "traffic": None if traffic is None else round(traffic / (ms_per_step * 1e-3) / 1e9, 1)}
+                "frac": round(ach_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_gbs}
     else:
         roof = {"bound": "mfma", "achieved": round(ach_tflops, 1), "peak": PEAK_MFMA_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach_tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach_tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": traffic_gbs}
+    if traffic is not None:
+        roof["traffic_bytes_per_call"] = traffic
     if decode:
         roof["kernel"] = "hh_linattn_decode_step (decode_kernel)"
     elif backward:
