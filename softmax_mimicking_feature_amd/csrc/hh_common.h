@@ -87,4 +87,19 @@ __device__ __forceinline__ bf16_t float_to_bf16_bits(float f) {
     return *reinterpret_cast<bf16_t *>(&b);
 }
 
+// Workgroup -> (head bh, segment s) for grids of BH x nseg workgroups.  Workgroups are dealt to
+// the eight XCDs round-robin (blockIdx mod 8); when BH is a multiple of 8, all segments of a head
+// go to one XCD, so that the head's W (and its state slot) is fetched into that XCD's L2 once.
+__device__ __forceinline__ void wg_head_segment(int nseg, int &bh, int &s) {
+    const int b = blockIdx.x, BH = gridDim.x / nseg;
+    if (BH % 8 == 0) {
+        const int j = b >> 3;
+        bh = (b & 7) + 8 * (j / nseg);
+        s = j % nseg;
+    } else {
+        bh = b / nseg;
+        s = b % nseg;
+    }
+}
+
 }  // namespace hh

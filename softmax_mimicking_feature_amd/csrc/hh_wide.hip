@@ -113,21 +113,6 @@ struct WideCfg {
     static_assert(NBUF == 1 || (D == 128 && VB == 2), "rotated V tile assumes 16 granules per row");
 };
 
-// Workgroup -> (head bh, segment s) for grids of BH x nseg workgroups.  Workgroups are dealt to
-// the eight XCDs round-robin (blockIdx mod 8); when BH is a multiple of 8, all segments of a head
-// go to one XCD, so that the head's W (and its state slot) is fetched into that XCD's L2 once.
-__device__ __forceinline__ void wg_head_segment(int nseg, int &bh, int &s) {
-    const int b = blockIdx.x, BH = gridDim.x / nseg;
-    if (BH % 8 == 0) {
-        const int j = b >> 3;
-        bh = (b & 7) + 8 * (j / nseg);
-        s = j % nseg;
-    } else {
-        bh = b / nseg;
-        s = b % nseg;
-    }
-}
-
 // Segment slots keep S in fp32 in the register image of the kernel that reads them back:
 // the two accumulators (halves h = 0, 1) that lane L of a wave holds as piece e are stored as
 // f32x4 at index (2 e + h) 64 + L, so that each wave instruction writes or reads one contiguous
