@@ -13,7 +13,11 @@ the Porcupine: Expressive Linear Attentions with Softmax Mimicry"):
                  the single-sided exp(W x + b) with d' = d (Choice 1 and the
                  default d' = d of the same section); the softmax over the d
                  feature directions, no bias (Choice 4), single-sided (d' = d)
-                 or with the negation mapping as one softmax per half (d' = 2d).
+                 or with the negation mapping as one softmax per half (d' = 2d);
+                 the generalised quadratic [sqrt a, sqrt b x, sqrt c x_i x_j] of
+                 the kernel p(s) = a + b s + c s^2, coefficients per head
+                 (paperlayer.ai summary of arXiv 2610.13674, section 2 and
+                 App. D, "Global Reference and HD Realization").
   causal      -- Eq. 2 by running sums S_i, z_i (section 3.4, "Complexity
                  Analysis"), with optional initial and final state.
   bidir       -- the same sums over all keys (bidirectional encoders).
@@ -45,6 +49,7 @@ MAP_TAYLOR2 = 1
 MAP_HEDGEHOG_SOFTMAX = 2
 MAP_EXP = 3
 MAP_SOFTMAX = 4
+MAP_QUADRATIC = 5
 
 _lib = None
 
@@ -107,6 +112,8 @@ def feature_dim(map_: int, d: int) -> int:
 def _params(map_, W, b, H, d):
     if map_ == MAP_TAYLOR2:
         return None, None
+    if map_ == MAP_QUADRATIC:  # W holds the coefficients (a, b, c) of each head
+        return _f64(W).reshape(H, 3), None
     W = _f64(W).reshape(H, d, d)
     if map_ in (MAP_HEDGEHOG, MAP_EXP):
         b = None if b is None or np.size(b) == 0 else _f64(b).reshape(H, d)
@@ -246,7 +253,7 @@ def backward(map_: int, q, k, v, W=None, b=None, dy=None, causal: bool = True, n
     dbp = np.empty((B, H, d), np.float64)
     _load().hho_backward(map_, d, B, H, N, int(bool(causal)), _ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(b),
                          _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dWp), _ptr(dbp), nthreads or default_threads())
-    dW = None if map_ == MAP_TAYLOR2 else dWp.sum(axis=0)
+    dW = None if map_ in (MAP_TAYLOR2, MAP_QUADRATIC) else dWp.sum(axis=0)
     db = dbp.sum(axis=0) if map_ in (MAP_HEDGEHOG, MAP_EXP) else None
     return dq, dk, dv, dW, db
 

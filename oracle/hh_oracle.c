@@ -18,6 +18,12 @@
  *     negated half exp(-(W x + b)) to R^{2d} (Choice 3; paperlayer A.1).
  *   - Degree-2 Taylor map [1, x, x_i x_j] with kernel 1 + q.k + (q.k)^2/2
  *     (section 3.4, "The Taylor Exponential as a Bridge Result").
+ *   - Generalised quadratic kernel p(s) = a + b s + c s^2 of the learned global
+ *     quadratic (paperlayer.ai summary of arXiv 2610.13674, section 2 and App. D,
+ *     "Global Reference and HD Realization"), realised by the feature map
+ *     [sqrt(a), sqrt(b) x, sqrt(c) x_i x_j] so that phi(q).phi(k) = p(q.k); the
+ *     Taylor map is the case (a, b, c) = (1, 1, 1/2).  The coefficients are
+ *     per head and must be >= 0.
  *   - Bidirectional (encoder) attention: the same sums taken over every key
  *     (paperlayer section 1: bidirectional BERT conversions).
  *   - Attention-weight distillation loss, Eq. 4 (section 3.4, "The Attention
@@ -49,10 +55,11 @@
 #define HHO_HEDGEHOG_SOFTMAX 2
 #define HHO_EXP 3
 #define HHO_SOFTMAX 4
+#define HHO_QUADRATIC 5
 
 int hho_feature_dim(int map, int d) {
     if (map == HHO_HEDGEHOG || map == HHO_HEDGEHOG_SOFTMAX) return 2 * d;
-    if (map == HHO_TAYLOR2) return 1 + d + d * d;
+    if (map == HHO_TAYLOR2 || map == HHO_QUADRATIC) return 1 + d + d * d;
     if (map == HHO_EXP || map == HHO_SOFTMAX) return d;
     return -1;
 }
@@ -75,6 +82,17 @@ static void phi_taylor(int d, const double *x, double *out) {
     for (int m = 0; m < d; m++) out[1 + m] = x[m];
     for (int a = 0; a < d; a++)
         for (int c = 0; c < d; c++) out[1 + d + (size_t)a * d + c] = x[a] * x[c] * r;
+}
+
+/* Generalised quadratic map, coefficients abc = (a, b, c):
+ * (sqrt(a), sqrt(b) x_0..x_{d-1}, sqrt(c) x_a x_c for a, c in [d]), so that
+ * phi(q).phi(k) = a + b s + c s^2 with s = q.k. */
+static void phi_quadratic(int d, const double *x, const double *abc, double *out) {
+    const double sa = sqrt(abc[0]), sb = sqrt(abc[1]), sc = sqrt(abc[2]);
+    out[0] = sa;
+    for (int m = 0; m < d; m++) out[1 + m] = sb * x[m];
+    for (int a = 0; a < d; a++)
+        for (int c = 0; c < d; c++) out[1 + d + (size_t)a * d + c] = sc * x[a] * x[c];
 }
 
 /* Single-sided exponential map (Choice 1, the default d' = d): phi_l = exp(w_l.x + b_l). */
@@ -109,6 +127,7 @@ static void phi_one(int map, int d, const double *x, const double *W, const doub
     switch (map) {
     case HHO_HEDGEHOG: phi_hedgehog(d, x, W, b, out); break;
     case HHO_TAYLOR2: phi_taylor(d, x, out); break;
+    case HHO_QUADRATIC: phi_quadratic(d, x, W, out); break;
     case HHO_EXP: phi_exp(d, x, W, b, out); break;
     case HHO_SOFTMAX: softmax_dirs(d, x, W, 1.0, out); break;
     case HHO_HEDGEHOG_SOFTMAX:
@@ -137,6 +156,16 @@ void hho_featuremap_head(int map, int d, long ntok, const double *x, const doubl
  * Then dx = W^T du, dW += du x^T, db += du. */
 static void phi_backward(int map, int d, const double *x, const double *W, const double *b, const double *dphi,
                          double *dx, double *dW, double *db) {
+    if (map == HHO_QUADRATIC) {  /* phi = [sqrt a, sqrt b x_m, sqrt c x_a x_c]; only dx (no W) */
+        const double sb = sqrt(W[1]), sc = sqrt(W[2]);
+        for (int m = 0; m < d; m++) {
+            double g = sb * dphi[1 + m];
+            for (int c = 0; c < d; c++)
+                g += (dphi[1 + d + (size_t)m * d + c] + dphi[1 + d + (size_t)c * d + m]) * x[c] * sc;
+            dx[m] += g;
+        }
+        return;
+    }
     if (map == HHO_TAYLOR2) {
         const double r = 1.0 / sqrt(2.0);
         for (int m = 0; m < d; m++) {
@@ -444,7 +473,8 @@ static void run_pair(job_t *j, long p) {
     long h = p % j->H;
     const int has_W = j->map != HHO_TAYLOR2;
     const int has_b = j->map == HHO_HEDGEHOG || j->map == HHO_EXP;
-    const double *W = has_W ? j->W + (size_t)h * d * d : NULL;
+    /* the quadratic map's parameters are its three coefficients per head */
+    const double *W = !has_W ? NULL : j->map == HHO_QUADRATIC ? j->W + (size_t)h * 3 : j->W + (size_t)h * d * d;
     const double *b = (has_b && j->b) ? j->b + (size_t)h * d : NULL;
     size_t seq = (size_t)j->N * d;
     switch (j->op) {
