@@ -14,7 +14,9 @@
  *  Layout   q, k, v, y: [B][H][N][d] row-major.  W: [H][d][d], row l is the
  *           direction w_l (u = W x + b, "the l-th row of W", section 3.4,
  *           Choice 1).  b: [H][d].  phi: [B][H][N][d'].  State S: [B][H][d'][d]
- *           fp32, z: [B][H][d'] fp32.  d' = 2d (Hedgehog) or 1 + d + d*d (Taylor).
+ *           fp32, z: [B][H][d'] fp32.  d' = 2d (Hedgehog) or 1 + d + d*d (Taylor and
+ *           the generalised quadratic map, whose W is instead fp32 [H][3]: the
+ *           coefficients a, b, c of each head, in every dtype).
  *  Dtype    `dtype` selects the element type of q, k, v, W, b, y and phi
  *           (HH_F32 or HH_BF16).  The state S, z is always fp32.  Products are
  *           accumulated in fp32 on the GPU.
@@ -33,7 +35,8 @@
  *  Threads  Calls are thread-safe (no global mutable state).
  *  Sizes    B, H >= 1; N >= 0 (N == 0 is a no-op apart from the state outputs);
  *           N * d < 2^31 and B * H < 2^24.
- *  Supported head dims: d in {16, 32, 64, 128} for the maps with a W; Taylor d == 16.
+ *  Supported head dims: d in {16, 32, 64, 128} for the maps with a W; the Taylor and the
+ *  generalised quadratic map d == 16.
  *  Maps 2-4 run the attention over features that a feature-map kernel writes into the
  *  workspace first (bf16), so their forward needs a workspace even with one segment.
  */
@@ -74,7 +77,15 @@ typedef enum {
      * the same section ("The Hedgehog MLP Feature Map"). */
     HH_MAP_EXP = 3,
     /* phi(x) = softmax(W x), d' = d, no bias (b must be NULL): Choice 4 as printed. */
-    HH_MAP_SOFTMAX = 4
+    HH_MAP_SOFTMAX = 4,
+    /* phi(x) = [sqrt(a), sqrt(b) x_0..x_{d-1}, sqrt(c) x_a x_c for a, c in [d] (row-major)],
+     * d' = 1 + d + d^2, so phi(q)^T phi(k) = a + b q.k + c (q.k)^2: the learned global quadratic
+     * kernel of the paperlayer.ai summary of arXiv 2610.13674 (section 2, and App. D "Global
+     * Reference and HD Realization"); (a, b, c) = (1, 1, 1/2) is HH_MAP_TAYLOR2.  W points to
+     * the coefficients, fp32 [H][3] = (a, b, c) per head whatever the dtype, each >= 0 (a
+     * negative coefficient gives NaN features); b must be NULL.  Positive weights need
+     * b^2 < 4 a c.  The backward and the distillation loss do not take this map. */
+    HH_MAP_QUADRATIC = 5
 } hh_map_t;
 
 /* ABI revision of this header; bumped on any incompatible change. */

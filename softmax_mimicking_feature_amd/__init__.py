@@ -19,13 +19,13 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (HH_BF16, HH_EHIP, HH_EINVAL, HH_EUNSUPPORTED, HH_EWORKSPACE, HH_F32, HH_MAP_EXP, HH_MAP_HEDGEHOG,
-                   HH_MAP_HEDGEHOG_SOFTMAX, HH_MAP_SOFTMAX, HH_MAP_TAYLOR2, HH_OK, LibraryMissing)
+                   HH_MAP_HEDGEHOG_SOFTMAX, HH_MAP_QUADRATIC, HH_MAP_SOFTMAX, HH_MAP_TAYLOR2, HH_OK, LibraryMissing)
 
 __all__ = ["hh_feature_dim", "hh_featuremap", "hh_linattn_fwd_workspace", "hh_linattn_fwd", "hh_linattn_fwd_noalloc",
            "hh_linattn_bwd_workspace", "hh_linattn_bwd",
            "hh_linattn_decode_step", "hh_distill_loss_workspace", "hh_distill_loss", "hh_status_str", "hh_last_error", "hh_abi_version", "HHError",
            "LibraryMissing", "HH_F32", "HH_BF16", "HH_MAP_HEDGEHOG", "HH_MAP_TAYLOR2", "HH_MAP_HEDGEHOG_SOFTMAX",
-           "HH_MAP_EXP", "HH_MAP_SOFTMAX", "HH_OK", "HH_EINVAL",
+           "HH_MAP_EXP", "HH_MAP_SOFTMAX", "HH_MAP_QUADRATIC", "HH_OK", "HH_EINVAL",
            "HH_EUNSUPPORTED", "HH_EWORKSPACE", "HH_EHIP"]
 
 
@@ -69,11 +69,17 @@ def _dev(t, name: str, dtype=None):
 
 def _map_params(map: int, W, b, H: int, d: int):
     """Check W and b for a map (W [H,d,d] for every map with a W, b [H,d] or None where the map has
-    a bias, None for the softmax maps); returns them, or (None, None) for the Taylor map."""
+    a bias, None for the softmax maps; for the generalised quadratic map W is the coefficients
+    (a, b, c) of each head, [H,3]); returns them, or (None, None) for the Taylor map."""
     if map == HH_MAP_TAYLOR2:
         return None, None
     if W is None:
         raise ValueError(f"W is required for map {map}")
+    if map == HH_MAP_QUADRATIC:
+        _shape(W, "W", (H, 3))
+        if b is not None:
+            raise ValueError("the quadratic map has no bias: b must be None")
+        return W, None
     _shape(W, "W", (H, d, d))
     if map in (HH_MAP_HEDGEHOG_SOFTMAX, HH_MAP_SOFTMAX):
         if b is not None:
@@ -81,6 +87,11 @@ def _map_params(map: int, W, b, H: int, d: int):
     else:
         _shape(b, "b", (H, d))
     return W, b
+
+
+def _w_dtype(map: int, dtype):
+    """Element type of W: the generalised quadratic map's coefficients are fp32 in every dtype."""
+    return _torch().float32 if map == HH_MAP_QUADRATIC else dtype
 
 
 def _shape(t, name: str, shape) -> None:
@@ -134,7 +145,7 @@ def hh_featuremap(x, W=None, b=None, *, map: int = HH_MAP_HEDGEHOG, out=None, st
     if out is None:
         out = torch.empty((B, H, N, dp), dtype=x.dtype, device=x.device)
     _dev(out, "out", x.dtype)
-    _dev(W, "W", x.dtype)
+    _dev(W, "W", _w_dtype(map, x.dtype))
     _dev(b, "b", x.dtype)
     _check(lib.hh_featuremap(map, _dtype_code(x), B, H, N, d, _ptr(x), _ptr(W), _ptr(b), _ptr(out),
                              _stream(stream)))
@@ -169,7 +180,7 @@ def hh_linattn_fwd(q, k, v, W=None, b=None, *, causal: bool = True, map: int = H
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, nm, q.dtype)
     dt = _dtype_code(q)
-    _dev(W, "W", q.dtype)
+    _dev(W, "W", _w_dtype(map, q.dtype))
     _dev(b, "b", q.dtype)
     _dev(S0, "S0", torch.float32)
     _dev(z0, "z0", torch.float32)
@@ -216,7 +227,7 @@ def hh_linattn_fwd_noalloc(q, k, v, W=None, b=None, *, causal: bool = True, map:
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, nm, q.dtype)
     dt = _dtype_code(q)
-    _dev(W, "W", q.dtype)
+    _dev(W, "W", _w_dtype(map, q.dtype))
     _dev(b, "b", q.dtype)
     for t, nm in ((S0, "S0"), (z0, "z0"), (S_out, "S_out"), (z_out, "z_out")):
         _dev(t, nm, torch.float32)
@@ -257,7 +268,7 @@ def hh_linattn_bwd(q, k, v, W, b, y, dy, *, causal: bool = True, map: int = HH_M
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (y, "y"), (dy, "dy")):
         _dev(t, nm, q.dtype)
     dt = _dtype_code(q)
-    _dev(W, "W", q.dtype)
+    _dev(W, "W", _w_dtype(map, q.dtype))
     _dev(b, "b", q.dtype)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
@@ -302,7 +313,7 @@ def hh_linattn_decode_step(q, k, v, W, b, S, z, *, map: int = HH_MAP_HEDGEHOG, o
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, nm, q.dtype)
     dt = _dtype_code(q)
-    _dev(W, "W", q.dtype)
+    _dev(W, "W", _w_dtype(map, q.dtype))
     _dev(b, "b", q.dtype)
     _dev(S, "S", torch.float32)
     _dev(z, "z", torch.float32)
@@ -332,7 +343,7 @@ def hh_distill_loss(q, k, W=None, b=None, *, map: int = HH_MAP_HEDGEHOG, out=Non
     for t, nm in ((q, "q"), (k, "k")):
         _dev(t, nm, q.dtype)
     dt = _dtype_code(q)
-    _dev(W, "W", q.dtype)
+    _dev(W, "W", _w_dtype(map, q.dtype))
     _dev(b, "b", q.dtype)
     if out is None:
         out = torch.empty((B, H, N), dtype=torch.float32, device=q.device)

@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(PKG, "libhh.so")
 
 HH_OK, HH_EINVAL, HH_EUNSUPPORTED, HH_EWORKSPACE, HH_EHIP = 0, 1, 2, 3, 4
 HH_F32, HH_BF16 = 0, 1
-HH_MAP_HEDGEHOG, HH_MAP_TAYLOR2, HH_MAP_HEDGEHOG_SOFTMAX, HH_MAP_EXP, HH_MAP_SOFTMAX = 0, 1, 2, 3, 4
+HH_MAP_HEDGEHOG, HH_MAP_TAYLOR2, HH_MAP_HEDGEHOG_SOFTMAX, HH_MAP_EXP, HH_MAP_SOFTMAX, HH_MAP_QUADRATIC = 0, 1, 2, 3, 4, 5
 
 # Every function declared in include/hh.h.
 EXPORTS = ("hh_abi_version", "hh_feature_dim", "hh_featuremap", "hh_linattn_fwd_workspace",

@@ -55,13 +55,17 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 int feature_dim(int map, int d) {
     if (d < 1 || d > 1024) return -1;
     if (map == HH_MAP_HEDGEHOG || map == HH_MAP_HEDGEHOG_SOFTMAX) return 2 * d;
-    if (map == HH_MAP_TAYLOR2) return 1 + d + d * d;
+    if (map == HH_MAP_TAYLOR2 || map == HH_MAP_QUADRATIC) return 1 + d + d * d;
     if (map == HH_MAP_EXP || map == HH_MAP_SOFTMAX) return d;
     return -1;
 }
 
-// Maps with a W (every map but the Taylor map), and maps with a bias (the softmax maps have none).
+// Maps with a W (every map but the Taylor map; the generalised quadratic map's W is its fp32
+// coefficients [H][3]), and maps with a bias (the softmax maps have none).
 bool map_has_W(int map) { return map != HH_MAP_TAYLOR2; }
+// The quadratic kernels a + b s + c s^2 (Taylor and the generalised quadratic map): head dim 16,
+// the packed-state kernels.
+bool quadratic_family(int map) { return map == HH_MAP_TAYLOR2 || map == HH_MAP_QUADRATIC; }
 bool map_has_b(int map) { return map == HH_MAP_HEDGEHOG || map == HH_MAP_EXP; }
 // Maps whose features the attention kernels read from a workspace (computed by the feature-map
 // kernel first) rather than computing them from q and k themselves.
@@ -71,16 +75,16 @@ size_t elem_bytes(int dtype) { return dtype == HH_BF16 ? 2 : 4; }
 
 // Checks shared by the forward and the feature map.
 hh_status_t check_common(int map, int dtype, long B, long H, long N, int d) {
-    if (map < HH_MAP_HEDGEHOG || map > HH_MAP_SOFTMAX) return fail(HH_EINVAL, "unknown map %d", map);
+    if (map < HH_MAP_HEDGEHOG || map > HH_MAP_QUADRATIC) return fail(HH_EINVAL, "unknown map %d", map);
     if (dtype != HH_F32 && dtype != HH_BF16) return fail(HH_EINVAL, "unknown dtype %d", dtype);
     if (B < 1 || H < 1) return fail(HH_EINVAL, "B and H must be >= 1 (got B=%ld H=%ld)", B, H);
     if (B * H >= (1L << 24)) return fail(HH_EINVAL, "B*H = %ld exceeds 2^24", B * H);
     if (N < 0) return fail(HH_EINVAL, "N must be >= 0 (got %ld)", N);
-    if (map_has_W(map)) {
+    if (!quadratic_family(map)) {
         if (d != 16 && d != 32 && d != 64 && d != 128)
             return fail(HH_EUNSUPPORTED, "head dim %d not supported for map %d (16, 32, 64, 128)", d, map);
     } else if (d != 16) {
-        return fail(HH_EUNSUPPORTED, "Taylor map head dim %d not supported (16)", d);
+        return fail(HH_EUNSUPPORTED, "quadratic-kernel map %d: head dim %d not supported (16)", map, d);
     }
     if (N * (long)d >= (1L << 31)) return fail(HH_EINVAL, "N*d = %ld exceeds 2^31", N * (long)d);
     return HH_OK;
@@ -149,7 +153,7 @@ Plan make_plan(int map, int dtype, int causal, long BH, long N, int d, bool has_
     Plan pl;
     if (dtype != HH_BF16 || N == 0) return pl;
     pl.chunked = true;
-    pl.narrow = map == HH_MAP_TAYLOR2;
+    pl.narrow = quadratic_family(map);
     pl.dpi = pl.narrow ? hh::kTaylorRowsInternal : 2 * d;
     const long C = 64;
     const long nch = (N + C - 1) / C;
@@ -249,7 +253,8 @@ hh_status_t hh_featuremap(int map, int dtype, int B, int H, int N, int d, const 
         e = hh::launch_featuremap_hedgehog_bf16(d, (const hh::bf16_t *)x, (const hh::bf16_t *)W,
                                                 (const hh::bf16_t *)b, (hh::bf16_t *)phi, B * H, H, N, s);
     else
-        e = hh::launch_featuremap_generic(map, dtype, d, dp, x, hog ? W : nullptr, hog ? b : nullptr, phi,
+        e = hh::launch_featuremap_generic(map, dtype, d, dp, x, (hog || map == HH_MAP_QUADRATIC) ? W : nullptr,
+                                          hog ? b : nullptr, phi,
                                           (long)B * H, H, N, s);
     if (e != hipSuccess) return hip_fail(e, "feature map launch");
     return ok();
@@ -467,7 +472,8 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
         np.q = (const hh::bf16_t *)q; np.k = (const hh::bf16_t *)k; np.v = (const hh::bf16_t *)v;
         np.y = (hh::bf16_t *)y;
         np.S_ws = wsS; np.z_ws = wsZ; np.ws_bh_stride = slot_stride;
-        np.N = N; np.seg_len = pl.seg_len;
+        np.coef = map == HH_MAP_QUADRATIC ? (const float *)W : nullptr;
+        np.N = N; np.H = H; np.seg_len = pl.seg_len;
         if (run_state) {
             np.nseg_grid = state_segments;
             e = hh::launch_narrow(0, np, (int)(BH * state_segments), s);
@@ -511,7 +517,7 @@ hh_status_t hh_linattn_fwd_noalloc(int map, int dtype, int causal, int B, int H,
 
 size_t hh_linattn_bwd_workspace(int map, int dtype, int causal, int B, int H, int N, int d) {
     if (check_common(map, dtype, B, H, N, d) != HH_OK || (causal != 0 && causal != 1) || dtype != HH_BF16 ||
-        map == HH_MAP_TAYLOR2 || N == 0)
+        quadratic_family(map) || N == 0)
         return 0;
     return make_bwd_plan(map, (long)B * H, N, d).bytes;
 }
@@ -524,7 +530,7 @@ hh_status_t hh_linattn_bwd(int map, int dtype, int causal, int B, int H, int N, 
     if (st != HH_OK) return st;
     if (causal != 0 && causal != 1) return fail(HH_EINVAL, "causal must be 0 or 1 (got %d)", causal);
     if (dtype != HH_BF16) return fail(HH_EUNSUPPORTED, "backward: bf16 inputs only");
-    if (map == HH_MAP_TAYLOR2) return fail(HH_EUNSUPPORTED, "backward: maps with a W only");
+    if (quadratic_family(map)) return fail(HH_EUNSUPPORTED, "backward: the exponential and softmax maps only");
     const bool need = N > 0;
     const char *names[9] = {"q", "k", "v", "y", "dy", "dq", "dk", "dv", "dW"};
     const void *ptrs[9] = {q, k, v, y, dy, dq, dk, dv, dW};

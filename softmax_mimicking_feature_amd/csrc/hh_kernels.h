@@ -11,7 +11,26 @@ typedef uint16_t bf16_t;
 
 // Map and dtype codes of include/hh.h, for device code that does not include it.
 constexpr int HH_MAP_HEDGEHOG_ = 0, HH_MAP_TAYLOR2_ = 1, HH_MAP_HEDGEHOG_SOFTMAX_ = 2, HH_MAP_EXP_ = 3,
-              HH_MAP_SOFTMAX_ = 4;
+              HH_MAP_SOFTMAX_ = 4, HH_MAP_QUADRATIC_ = 5;
+
+// Coefficients of the quadratic kernels a + b s + c s^2 (s = q.k) of one head: the degree-2 Taylor
+// map is (1, 1, 1/2); the generalised quadratic map reads (a, b, c) of head h from coef[3 h ..].
+// Feature scales: sqrt(a) for the constant, sqrt(b) for x, sqrt(c) for the canonical pair
+// features x_i x_j (and so for the packed diagonal x_i^2), sqrt(2 c) for a packed off-diagonal pair.
+struct QuadCoef {
+    float a, b, c, sa, sb, sc, s2c;
+};
+__host__ __device__ inline QuadCoef quad_coef(const float *coef, int h) {
+    QuadCoef q;
+    q.a = coef ? coef[3 * h] : 1.0f;
+    q.b = coef ? coef[3 * h + 1] : 1.0f;
+    q.c = coef ? coef[3 * h + 2] : 0.5f;
+    q.sa = sqrtf(q.a);
+    q.sb = sqrtf(q.b);
+    q.sc = sqrtf(q.c);
+    q.s2c = sqrtf(2.0f * q.c);
+    return q;
+}
 constexpr int HH_F32_ = 0, HH_BF16_ = 1;
 
 // Size of the library-owned scratch array behind hh_linattn_fwd_noalloc (one per device).
@@ -61,7 +80,8 @@ struct NarrowParams {
     float *S_out, *z_out;  // canonical feature order
     const float *S0c, *z0c;  // the caller's initial state, canonical order (or null), read only for
                              // the part of S_out the packed basis does not hold
-    int N, nseg_grid, seg_len;
+    const float *coef;  // generalised quadratic map: (a, b, c) per head, fp32 [H][3]; null: Taylor
+    int N, H, nseg_grid, seg_len;
 };
 hipError_t launch_narrow(int mode, const NarrowParams &p, int grid, hipStream_t st);
 constexpr int kTaylorRowsInternal = 160;  // 153 packed symmetric features padded to 10 blocks of 16

@@ -117,19 +117,23 @@ hipError_t launch_state_copy(const float *S0, const float *z0, float *S_out, flo
 // Feature value f of token x (fp32), x already in shared memory.  For the softmax maps this is
 // the logit (+-w_l.x); softmax_halves turns a token's logits into features afterwards.
 template <typename LoadW>
-__device__ __forceinline__ float feature_value(int map, int d, int f, const float *x, LoadW wrow, float bias_l) {
-    if (map != HH_MAP_TAYLOR2_) {
+__device__ __forceinline__ float feature_value(int map, int d, int f, const float *x, LoadW wrow, float bias_l,
+                                               const QuadCoef &qc) {
+    if (map != HH_MAP_TAYLOR2_ && map != HH_MAP_QUADRATIC_) {
         const int l = f < d ? f : f - d;
         float u = bias_l;
         for (int m = 0; m < d; m++) u = fmaf(wrow(l, m), x[m], u);
         const float su = f < d ? u : -u;
         return (map == HH_MAP_HEDGEHOG_SOFTMAX_ || map == HH_MAP_SOFTMAX_) ? su : expf(su);
     }
-    if (f == 0) return 1.0f;
-    if (f <= d) return x[f - 1];
+    // quadratic kernels a + b s + c s^2: [sqrt a, sqrt b x, sqrt c x_a x_c] (Taylor: 1, 1, 1/2)
+    if (f == 0) return qc.sa;
+    if (f <= d) return x[f - 1] * qc.sb;
     const int q = f - 1 - d;
-    return x[q / d] * x[q % d] * 0.70710678118654752f;
+    return x[q / d] * x[q % d] * qc.sc;
 }
+
+__device__ __forceinline__ bool quadratic_family(int map) { return map == HH_MAP_TAYLOR2_ || map == HH_MAP_QUADRATIC_; }
 
 // Softmax over each half (d logits) of a token's feature vector in shared memory, in place;
 // executed by one wave (lane l handles entries l and l + 64 of each half, d <= 128).
@@ -172,7 +176,9 @@ __global__ __launch_bounds__(kSeqThreads) void seq_f32_kernel(SeqParams p) {
     __shared__ float sred[kSeqThreads];
     const int bh = blockIdx.x, h = bh % p.H, t = threadIdx.x;
     const int d = p.d, dp = p.dp, nE = dp * d;
-    const float *Wh = p.W ? p.W + (size_t)h * d * d : nullptr;
+    const bool quad = quadratic_family(p.map);
+    const float *Wh = (p.W && !quad) ? p.W + (size_t)h * d * d : nullptr;
+    const QuadCoef qc = quad_coef(p.map == HH_MAP_QUADRATIC_ ? p.W : nullptr, h);
     const float *bhp = p.b ? p.b + (size_t)h * d : nullptr;
     auto wrow = [&](int l, int m) { return Wh[l * d + m]; };
     const size_t seq = (size_t)bh * p.N * d;
@@ -201,8 +207,8 @@ __global__ __launch_bounds__(kSeqThreads) void seq_f32_kernel(SeqParams p) {
             for (int f = t; f < dp; f += kSeqThreads) {
                 const int l = f < d ? f : f - d;
                 const float bl = ((p.map == HH_MAP_HEDGEHOG_ || p.map == HH_MAP_EXP_) && bhp) ? bhp[l] : 0.0f;
-                if (do_update) sfk[f] = feature_value(p.map, d, f, sk, wrow, bl);
-                if (do_read) sfq[f] = feature_value(p.map, d, f, sq, wrow, bl);
+                if (do_update) sfk[f] = feature_value(p.map, d, f, sk, wrow, bl, qc);
+                if (do_read) sfq[f] = feature_value(p.map, d, f, sq, wrow, bl, qc);
             }
             __syncthreads();
             if (is_softmax_map(p.map)) {
@@ -291,7 +297,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     __syncthreads();
     const void *W = p.W;
     const size_t woff = (size_t)h * d * d;
-    if (p.map != HH_MAP_TAYLOR2_) {
+    if (!quadratic_family(p.map)) {
         // u = W x for q and k together: kDecThreads / d consecutive threads share a row of W and
         // read contiguous pieces of it, then combine their partial dot products
         const int tpr = kDecThreads / d < d ? kDecThreads / d : d;
@@ -348,10 +354,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
             else if (t < 128) softmax_halves(sfk, d, halves, t - 64);
         }
     } else {
-        auto wrow = [&](int l, int m) { return ld(W, woff + (size_t)l * d + m, dt); };
+        // quadratic kernels: W holds the generalised map's fp32 coefficients (null for Taylor)
+        auto wrow = [&](int, int) { return 0.0f; };
+        const QuadCoef qc = quad_coef(p.map == HH_MAP_QUADRATIC_ ? reinterpret_cast<const float *>(W) : nullptr, h);
         for (int f = t; f < dp; f += kDecThreads) {
-            sfk[f] = feature_value(p.map, d, f, sk, wrow, 0.0f);
-            sfq[f] = feature_value(p.map, d, f, sq, wrow, 0.0f);
+            sfk[f] = feature_value(p.map, d, f, sk, wrow, 0.0f, qc);
+            sfq[f] = feature_value(p.map, d, f, sq, wrow, 0.0f, qc);
         }
     }
     __syncthreads();
@@ -437,13 +445,14 @@ __global__ void fm_generic_kernel(int map, int dtype, int d, int dp, const void 
         for (int m = 0; m < d; m++) u = fmaf(ld(W, wo + m, dtype), ld(x, xo + m, dtype), u);
         st(phi, (size_t)tok * dp + f, expf(u), dtype);
         st(phi, (size_t)tok * dp + d + f, expf(-u), dtype);
-    } else {
+    } else {  // quadratic kernels; W: the generalised map's fp32 coefficients (null for Taylor)
+        const QuadCoef qc = quad_coef(reinterpret_cast<const float *>(W), (int)((tok / N) % H));
         float val;
-        if (f == 0) val = 1.0f;
-        else if (f <= d) val = ld(x, xo + f - 1, dtype);
+        if (f == 0) val = qc.sa;
+        else if (f <= d) val = ld(x, xo + f - 1, dtype) * qc.sb;
         else {
             const int q = f - 1 - d;
-            val = ld(x, xo + q / d, dtype) * ld(x, xo + q % d, dtype) * 0.70710678118654752f;
+            val = ld(x, xo + q / d, dtype) * ld(x, xo + q % d, dtype) * qc.sc;
         }
         st(phi, (size_t)tok * dp + f, val, dtype);
     }

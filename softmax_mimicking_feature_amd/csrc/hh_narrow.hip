@@ -3,12 +3,16 @@
 //
 // The Taylor map phi(x) = [1, x, x_a x_c / sqrt(2)] makes phi(q)^T phi(k) = 1 + s + s^2/2
 // with s = q.k exactly (paper-graph-ui walkthrough of "The Hedgehog & the Porcupine",
-// section 3.4, "The Taylor Exponential as a Bridge Result").  The chunk recurrence is the
+// section 3.4, "The Taylor Exponential as a Bridge Result").  The same kernels run the
+// generalised quadratic p(s) = a + b s + c s^2 of the learned global quadratic (paperlayer.ai
+// summary of arXiv 2610.13674, section 2 and App. D): the map [sqrt a, sqrt b x, sqrt c x_a x_c]
+// with per-head coefficients, of which the Taylor map is the case (1, 1, 1/2).  Every feature
+// block takes its coefficient's root as a scale and the closed form below uses a, b, c.  The chunk recurrence is the
 // same regrouping of Eq. 2 as in the Hedgehog kernels:
 //     y_c = (phiQ_c Sp + A_c V_c) / (phiQ_c zp + A_c 1),  A_c = tril(phiQ_c phiK_c^T)
 //     Sp += phiK_c^T V_c,  zp += phiK_c^T 1
 // Two choices specific to this map:
-//   * The intra-chunk kernel matrix A_c is formed from the closed form 1 + s + s^2/2
+//   * The intra-chunk kernel matrix A_c is formed from the closed form a + b s + c s^2
 //     with s = Q_c K_c^T (a K = 16 product), the identity above, instead of a K = 273
 //     product of feature vectors.
 //   * Features are never stored: each lane builds the 8 feature values an MFMA operand
@@ -43,19 +47,23 @@ enum { NM_STATE = 0, NM_CAUSAL = 1, NM_READOUT = 2 };
 
 // Packed feature of internal block fb at position 4 g + r of a token, from the token's values
 // rotated by the lane group: x[j] = value (4 g + j) mod 16.  m9 = (g < 2), c9 = (g == 2) select
-// block 9's pair rows, its constant and its zero rows.
-__device__ __forceinline__ float packed_feature(int fb, int r, const float (&x)[12], float m9, float c9) {
-    if (fb == 0) return x[r];
-    if (fb == 1) return x[r] * x[r] * kInvSqrt2;
-    if (fb < 9) return x[r] * x[r + fb - 1];
-    return r == 0 ? fmaf(x[0] * x[8], m9, c9) : x[r] * x[r + 8] * m9;
+// block 9's pair rows, its constant and its zero rows.  qc scales the constant, linear, diagonal
+// and off-diagonal features (for the Taylor map 1, 1, 1/sqrt 2 and 1).
+__device__ __forceinline__ float packed_feature(int fb, int r, const float (&x)[12], float m9, float c9,
+                                                const QuadCoef &qc) {
+    if (fb == 0) return x[r] * qc.sb;
+    if (fb == 1) return x[r] * x[r] * qc.sc;
+    if (fb < 9) return x[r] * x[r + fb - 1] * qc.s2c;
+    return r == 0 ? fmaf(x[0] * x[8] * qc.s2c, m9, c9 * qc.sa) : x[r] * x[r + 8] * qc.s2c * m9;
 }
 
 // Work of wave H of the two waves of a workgroup.  Wave H holds the state rows of the K steps
 // [KS0, KS1) (feature blocks 2 KS0 .. 2 KS1 - 1): wave 0 steps 0-2, wave 1 steps 3-4 plus the
 // intra-chunk part, so each wave builds only its own feature operands.  The read-out partials
-// over the two halves meet in LDS: each wave finishes two of the four 16-token blocks.
-template <int MODE, int H>
+// over the two halves meet in LDS: each wave finishes two of the four 16-token blocks.  GQ: the
+// generalised quadratic map (coefficients per head); otherwise the Taylor map, whose scales are
+// compile-time constants.
+template <int MODE, int H, bool GQ>
 __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s, int lane, bf16_t *sQ, bf16_t *sK,
                                             float *sQf, float *sKTf, bf16_t *sVT, f32x4 *sX) {
     constexpr int KS0 = H == 0 ? 0 : 3, KS1 = H == 0 ? 3 : KSF;
@@ -87,6 +95,7 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
     const bf16x8 ones = ones_bf16x8();
     const float m9 = g < 2 ? 1.0f : 0.0f, c9 = g == 2 ? 1.0f : 0.0f;          // query side, block 9
     const float m9k = r16 < 8 ? 1.0f : 0.0f;                                    // key side, block 9
+    const QuadCoef qc = GQ ? quad_coef(p.coef, bh % p.H) : quad_coef(nullptr, 0);
 
     // Chunk inputs (lane = token) are fetched into registers one chunk ahead, so their memory
     // latency overlaps the previous chunk's work: wave 0 q, k, v, wave 1 k.
@@ -184,15 +193,15 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                     bf16x8 a;
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
-                        a[r] = (__bf16)packed_feature(2 * ks, r, x, m9, c9);
-                        a[4 + r] = (__bf16)packed_feature(2 * ks + 1, r, x, m9, c9);
+                        a[r] = (__bf16)packed_feature(2 * ks, r, x, m9, c9, qc);
+                        a[4 + r] = (__bf16)packed_feature(2 * ks + 1, r, x, m9, c9, qc);
                     }
                     const int lb = 2 * (ks - KS0);
                     num[ib] = mfma_bf16(a, acc_pair_to_operand(sacc[lb], sacc[lb + 1]), num[ib]);
                     den[ib] = mfma_bf16(a, acc_pair_to_operand(zacc[lb], zacc[lb + 1]), den[ib]);
                 }
             }
-            // ---- intra-chunk part (causal, wave 1): A = 1 + s + s^2/2 on j <= i, s = k_j . q_i
+            // ---- intra-chunk part (causal, wave 1): A = a + b s + c s^2 on j <= i, s = k_j . q_i
             if (MODE == NM_CAUSAL && H == 1) {
                 // keys past the end of the chunk count in no row sum (their v rows are zero)
                 bf16x8 onesv[2];
@@ -224,7 +233,7 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
 #pragma unroll
                             for (int r = 0; r < 4; r++) {
                                 const float sv = sdot[r];
-                                const float av = fmaf(sv, fmaf(0.5f, sv, 1.0f), 1.0f);
+                                const float av = fmaf(sv, fmaf(qc.c, sv, qc.b), qc.a);
                                 at[jb][r] = jb < ib ? av : av * cm[r];
                             }
                         } else {
@@ -277,11 +286,11 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                 for (int r = 0; r < 4; r++) {
                     kr[ks][r] = lo[r];
                     kr[ks][4 + r] = hi[r];
-                    krs[ks][r] = kr[ks][r] * kInvSqrt2;
-                    krs[ks][4 + r] = kr[ks][4 + r] * kInvSqrt2;
+                    krs[ks][r] = kr[ks][r] * qc.sc;
+                    krs[ks][4 + r] = kr[ks][4 + r] * qc.sc;
                     const int jlo = 32 * ks + 4 * g + r, jhi = jlo + 16;
-                    okc[ks][r] = (r16 == 8 && jlo < valid) ? 1.0f : 0.0f;
-                    okc[ks][4 + r] = (r16 == 8 && jhi < valid) ? 1.0f : 0.0f;
+                    okc[ks][r] = (r16 == 8 && jlo < valid) ? qc.sa : 0.0f;
+                    okc[ks][4 + r] = (r16 == 8 && jhi < valid) ? qc.sa : 0.0f;
                 }
             }
 #pragma unroll
@@ -292,7 +301,7 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                     bf16x8 a;
                     if (fb == 0) {
 #pragma unroll
-                        for (int sl = 0; sl < 8; sl++) a[sl] = (__bf16)kr[ks][sl];
+                        for (int sl = 0; sl < 8; sl++) a[sl] = (__bf16)(kr[ks][sl] * qc.sb);
                     } else if (fb == 1) {
 #pragma unroll
                         for (int sl = 0; sl < 8; sl++) a[sl] = (__bf16)(kr[ks][sl] * krs[ks][sl]);
@@ -303,7 +312,7 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                         const f32x4 hi = *reinterpret_cast<const f32x4 *>(kp + 16);
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
-                            const float plo = lo[r] * kr[ks][r], phi_ = hi[r] * kr[ks][4 + r];
+                            const float plo = lo[r] * kr[ks][r] * qc.s2c, phi_ = hi[r] * kr[ks][4 + r] * qc.s2c;
                             a[r] = (__bf16)(fb < 9 ? plo : fmaf(plo, m9k, okc[ks][r]));
                             a[4 + r] = (__bf16)(fb < 9 ? phi_ : fmaf(phi_, m9k, okc[ks][4 + r]));
                         }
@@ -388,7 +397,7 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
     }
 }
 
-template <int MODE>
+template <int MODE, bool GQ>
 __global__ __launch_bounds__(128, 2) void narrow_kernel(NarrowParams p) {
     __shared__ __attribute__((aligned(16))) bf16_t sQ[C * RR];
     __shared__ __attribute__((aligned(16))) bf16_t sK[C * RR];
@@ -400,16 +409,26 @@ __global__ __launch_bounds__(128, 2) void narrow_kernel(NarrowParams p) {
     const int s = blockIdx.x % p.nseg_grid;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (w == 0)
-        narrow_wave<MODE, 0>(p, bh, s, lane, sQ, sK, sQf, sKTf, sVT, sX);
+        narrow_wave<MODE, 0, GQ>(p, bh, s, lane, sQ, sK, sQf, sKTf, sVT, sX);
     else
-        narrow_wave<MODE, 1>(p, bh, s, lane, sQ, sK, sQf, sKTf, sVT, sX);
+        narrow_wave<MODE, 1, GQ>(p, bh, s, lane, sQ, sK, sQf, sKTf, sVT, sX);
 }
 
 hipError_t launch_narrow(int mode, const NarrowParams &p, int grid, hipStream_t st) {
+    const bool gq = p.coef != nullptr;
     switch (mode) {
-    case NM_STATE: hipLaunchKernelGGL(narrow_kernel<NM_STATE>, dim3(grid), dim3(128), 0, st, p); break;
-    case NM_CAUSAL: hipLaunchKernelGGL(narrow_kernel<NM_CAUSAL>, dim3(grid), dim3(128), 0, st, p); break;
-    default: hipLaunchKernelGGL(narrow_kernel<NM_READOUT>, dim3(grid), dim3(128), 0, st, p); break;
+    case NM_STATE:
+        if (gq) hipLaunchKernelGGL((narrow_kernel<NM_STATE, true>), dim3(grid), dim3(128), 0, st, p);
+        else hipLaunchKernelGGL((narrow_kernel<NM_STATE, false>), dim3(grid), dim3(128), 0, st, p);
+        break;
+    case NM_CAUSAL:
+        if (gq) hipLaunchKernelGGL((narrow_kernel<NM_CAUSAL, true>), dim3(grid), dim3(128), 0, st, p);
+        else hipLaunchKernelGGL((narrow_kernel<NM_CAUSAL, false>), dim3(grid), dim3(128), 0, st, p);
+        break;
+    default:
+        if (gq) hipLaunchKernelGGL((narrow_kernel<NM_READOUT, true>), dim3(grid), dim3(128), 0, st, p);
+        else hipLaunchKernelGGL((narrow_kernel<NM_READOUT, false>), dim3(grid), dim3(128), 0, st, p);
+        break;
     }
     return hipGetLastError();
 }

@@ -32,6 +32,7 @@ MAP_TAYLOR2 = 1
 MAP_HEDGEHOG_SOFTMAX = 2
 MAP_EXP = 3
 MAP_SOFTMAX = 4
+MAP_QUADRATIC = 5
 DT_F32 = 0
 DT_BF16 = 1
 
@@ -39,7 +40,7 @@ DT_BF16 = 1
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    map: int            # MAP_HEDGEHOG, MAP_TAYLOR2, MAP_HEDGEHOG_SOFTMAX, MAP_EXP or MAP_SOFTMAX
+    map: int            # MAP_HEDGEHOG, MAP_TAYLOR2, MAP_HEDGEHOG_SOFTMAX, MAP_EXP, MAP_SOFTMAX or MAP_QUADRATIC
     dtype: int          # DT_F32 or DT_BF16
     causal: bool
     B: int
@@ -132,7 +133,11 @@ def make_inputs(w: Workload, *, B: Optional[int] = None, H: Optional[int] = None
 
     All arrays are float32 holding values exactly representable in the
     workload's storage dtype.  For the Taylor map W and b are returned as
-    empty arrays (the map has no parameters); the softmax maps use no b.
+    empty arrays (the map has no parameters); the softmax maps use no b.  For
+    the generalised quadratic map W is the fp32 coefficients (a, b, c) of each
+    head, [H,3] (never rounded), drawn so that every weight is positive:
+    a ~ U(0.5, 1.5), b ~ U(0.2, 1.2), c = b^2 / (4 a) times U(1.5, 3), and b
+    is empty.
     """
     B = w.B if B is None else B
     H = w.H if H is None else H
@@ -144,7 +149,13 @@ def make_inputs(w: Workload, *, B: Optional[int] = None, H: Optional[int] = None
     k = rng.standard_normal((B, H, N, d)) * w.qk_scale
     v = rng.standard_normal((B, H, N, d)) * w.v_scale
     out = {"q": _store(q, w.dtype), "k": _store(k, w.dtype), "v": _store(v, w.dtype)}
-    if w.map != MAP_TAYLOR2:
+    if w.map == MAP_QUADRATIC:
+        a = rng.uniform(0.5, 1.5, H)
+        bb = rng.uniform(0.2, 1.2, H)
+        c = bb * bb / (4.0 * a) * rng.uniform(1.5, 3.0, H)
+        out["W"] = np.stack([a, bb, c], axis=1).astype(np.float32)
+        out["b"] = np.zeros((0,), np.float32)
+    elif w.map != MAP_TAYLOR2:
         W = rng.standard_normal((H, d, d)) * w.w_std
         b = rng.standard_normal((H, d)) * w.b_std
         out["W"] = _store(W, w.dtype)
@@ -173,7 +184,7 @@ def feature_dim(map_: int, d: int) -> int:
     (single-sided maps)."""
     if map_ in (MAP_HEDGEHOG, MAP_HEDGEHOG_SOFTMAX):
         return 2 * d
-    if map_ == MAP_TAYLOR2:
+    if map_ in (MAP_TAYLOR2, MAP_QUADRATIC):
         return 1 + d + d * d
     return d
 

@@ -66,7 +66,7 @@ def fwd(lib, map_=HOG, dt=BF16, causal=1, B=1, H=2, N=64, d=64, q=A, k=Bp, v=Cp,
 
 
 def test_fwd_rejects_bad_arguments(lib):
-    assert fwd(lib, map_=5) == _lib.HH_EINVAL
+    assert fwd(lib, map_=6) == _lib.HH_EINVAL
     assert fwd(lib, dt=9) == _lib.HH_EINVAL
     assert fwd(lib, causal=2) == _lib.HH_EINVAL
     assert fwd(lib, B=0) == _lib.HH_EINVAL
@@ -127,6 +127,17 @@ def test_noalloc_rejects_problems_beyond_its_scratch(lib):
         _lib.HH_EUNSUPPORTED
     assert call(HOG, BF16, 2, 1, 2, 64, 64, A, Bp, Cp, Wp, None, None, None, Dp, None, None, None) == \
         _lib.HH_EINVAL
+
+
+def test_quadratic_map_rules(lib):
+    QD = _lib.HH_MAP_QUADRATIC
+    assert lib.hh_feature_dim(QD, 16) == 1 + 16 + 256
+    assert fwd(lib, map_=QD, d=64) == _lib.HH_EUNSUPPORTED            # head dim 16 only, like Taylor
+    assert fwd(lib, map_=QD, d=16, W=None) == _lib.HH_EINVAL          # the coefficients are required
+    assert fwd(lib, map_=QD, d=16, b=0x60000000) == _lib.HH_EINVAL    # no bias
+    assert lib.hh_distill_loss(QD, BF16, 1, 2, 64, 16, A, Bp, Wp, None, Dp, Cp, 1 << 30, None) == \
+        _lib.HH_EUNSUPPORTED
+    assert lib.hh_linattn_bwd_workspace(QD, BF16, 1, 1, 2, 64, 16) == 0
 
 
 def test_featuremap_and_decode_reject_bad_arguments(lib):

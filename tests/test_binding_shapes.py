@@ -98,3 +98,13 @@ def test_featuremap_and_distill_reject_bad_shapes():
         hh.hh_distill_loss(x, x, t(H, d, 1), t(H, d))
     with pytest.raises(ValueError, match="GPU tensor"):
         hh.hh_distill_loss(x, x, t(H, d, d), t(H, d))
+
+
+def test_quadratic_map_takes_per_head_coefficients():
+    kw = dict(q=t(B, H, N, d), k=t(B, H, N, d), v=t(B, H, N, d), map=hh.HH_MAP_QUADRATIC)
+    with pytest.raises(ValueError, match="shape"):
+        hh.hh_linattn_fwd(W=t(H, d, d, dtype=torch.float32), **kw)    # a Hedgehog W, not [H,3]
+    with pytest.raises(ValueError, match="no bias"):
+        hh.hh_linattn_fwd(W=t(H, 3, dtype=torch.float32), b=t(H, d), **kw)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        hh.hh_linattn_fwd(W=t(H, 3, dtype=torch.float32), **kw)
