@@ -401,22 +401,33 @@ __global__ void feat_scan_kernel(float *__restrict__ S, float *__restrict__ z, l
         base = z + bh * nseg * perZ + (e - perS);
         stride = perZ;
     }
+    // each thread loads eight slots before it adds or stores any, so its loads are in flight
+    // together rather than one round trip per slot
     const int nin = mode == 0 ? nseg - 1 : nseg;
     float run = 0.0f;
-    for (int t = 0; t < nin; t++) {
-        const float a = base[t * stride];
-        if (mode == 0 && t > 0) base[t * stride] = run;
-        run += a;
+    for (int t0 = 0; t0 < nin; t0 += 8) {
+        float a[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) a[i] = t0 + i < nin ? base[(t0 + i) * stride] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            if (t0 + i < nin) {
+                if (mode == 0 && t0 + i > 0) base[(t0 + i) * stride] = run;
+                run += a[i];
+            }
     }
     base[mode == 0 ? (long)(nseg - 1) * stride : 0] = run;
 }
 
 // ---------------------------------------------------------------------------------------
-// Feature maps with a W (maps 2, 3, 4) on the matrix cores, bf16: one workgroup per 64 tokens
-// of one sequence, one wave per 16 of them (the 16 tokens of an MFMA share its W rows, so they
-// must belong to one head); u^T = W x^T for every direction (lane: token r16, directions
+// Feature maps with a W (maps 2, 3, 4) on the matrix cores, bf16.  One workgroup per
+// kFmvBlocks x 64 tokens of one sequence; each wave loads the head's W operands into registers
+// once and walks kFmvBlocks blocks of 16 tokens (the 16 tokens of an MFMA share its W rows, so
+// they belong to one head).  u^T = W x^T for every direction (lane: token r16, directions
 // 16 lb + 4 g + r), so that a token's d projections sit in its 4 lane groups and the softmax
-// normaliser is two shuffles.
+// normaliser is two shuffles.  The next block's x is loaded while the current one is mapped.
+constexpr int kFmvBlocks = 4;
+
 template <int D, int MAP>
 __global__ __launch_bounds__(256) void fm_variant_kernel(const bf16_t *__restrict__ x, const bf16_t *__restrict__ W,
                                                          const bf16_t *__restrict__ b, bf16_t *__restrict__ phi,
@@ -425,74 +436,99 @@ __global__ __launch_bounds__(256) void fm_variant_kernel(const bf16_t *__restric
     constexpr int DP = MAP == HH_MAP_HEDGEHOG_SOFTMAX_ ? 2 * D : D;
     const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
     const long bh = blockIdx.x / tiles;
-    const int n = (blockIdx.x % tiles) * 64 + (threadIdx.x >> 6) * 16 + r16;  // token within the sequence
-    const bool live = n < N;
-    const long tk = bh * N + (live ? n : 0);
+    const int n0 = (blockIdx.x % tiles) * 64 * kFmvBlocks + (threadIdx.x >> 6) * 16 + r16;
     const int h = (int)(bh % H);
     const bf16_t *Wh = W + (size_t)h * D * D;
-    // B operand: token r16, input dims 32 ks + 8 g .. + 7 (D = 16: the upper half zero)
-    bf16x8 xb[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++)
-        xb[ks] = (32 * ks + 8 * g < D) ? *reinterpret_cast<const bf16x8 *>(x + (size_t)tk * D + 32 * ks + 8 * g)
-                                       : zero_bf16x8();
-    f32x4 u[LB];
-#pragma unroll
-    for (int lb = 0; lb < LB; lb++) {
-        u[lb] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++) {
-            const bf16x8 wa = (32 * ks + 8 * g < D)
-                                  ? *reinterpret_cast<const bf16x8 *>(Wh + (size_t)(16 * lb + r16) * D + 32 * ks + 8 * g)
-                                  : zero_bf16x8();
-            u[lb] = mfma_bf16(wa, xb[ks], u[lb]);
-        }
+    // the head's W through LDS once per workgroup (rows padded to 32 mod 256 bytes: the operand
+    // reads of 16 rows x 4 column runs fall in distinct banks)
+    constexpr int WP = D + 16;
+    __shared__ __attribute__((aligned(16))) bf16_t sW[D * WP];
+    for (int e = threadIdx.x; e < D * D / 8; e += 256) {
+        const int row = e / (D / 8), c8 = e % (D / 8);
+        *reinterpret_cast<bf16x8 *>(sW + row * WP + 8 * c8) = *reinterpret_cast<const bf16x8 *>(Wh + (size_t)row * D + 8 * c8);
     }
-    // lane holds u of directions 16 lb + 4 g + r for token r16
-    bf16_t *out = phi + (size_t)tk * DP;
-    if (MAP == HH_MAP_EXP_) {
+    __syncthreads();
+    // A operands: W rows 16 lb + r16, input dims 32 ks + 8 g .. + 7 (D = 16: the upper half zero)
+    bf16x8 wa[LB][KS];
+#pragma unroll
+    for (int lb = 0; lb < LB; lb++)
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            wa[lb][ks] = (32 * ks + 8 * g < D) ? *reinterpret_cast<const bf16x8 *>(sW + (16 * lb + r16) * WP + 32 * ks + 8 * g)
+                                               : zero_bf16x8();
+    float bl[LB][4];
+#pragma unroll
+    for (int lb = 0; lb < LB; lb++)
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            bl[lb][r] = (MAP == HH_MAP_EXP_ && b) ? bf16_bits_to_float(b[(size_t)h * D + 16 * lb + 4 * g + r]) : 0.0f;
+    // B operand of a block: token r16, input dims 32 ks + 8 g .. + 7
+    auto load_x = [&](int n, bf16x8 (&xb)[KS]) {
+        const long tk = bh * N + (n < N ? n : 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            xb[ks] = (32 * ks + 8 * g < D) ? *reinterpret_cast<const bf16x8 *>(x + (size_t)tk * D + 32 * ks + 8 * g)
+                                           : zero_bf16x8();
+    };
+    bf16x8 xn[KS];
+    load_x(n0, xn);
+    for (int blk = 0; blk < kFmvBlocks; blk++) {
+        const int n = n0 + 64 * blk;
+        if (n - r16 >= N) break;  // the whole 16-token block lies past the end (wave-uniform)
+        bf16x8 xb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) xb[ks] = xn[ks];
+        if (blk + 1 < kFmvBlocks) load_x(n + 64, xn);
+        const bool live = n < N;
+        f32x4 u[LB];
 #pragma unroll
         for (int lb = 0; lb < LB; lb++) {
-            f32x4 e;
+            u[lb] = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int l = 16 * lb + 4 * g + r;
-                const float bl = b ? bf16_bits_to_float(b[(size_t)h * D + l]) : 0.0f;
-                e[r] = exp2_fast((u[lb][r] + bl) * kLog2e);
-            }
-            if (live) store4(out + 16 * lb + 4 * g, to_bf16x4(e));
+            for (int ks = 0; ks < KS; ks++) u[lb] = mfma_bf16(wa[lb][ks], xb[ks], u[lb]);
         }
-        return;
-    }
-    // softmax over the d directions (and, two-sided, over their negations)
+        // lane holds u of directions 16 lb + 4 g + r for token r16
+        bf16_t *out = phi + (size_t)(bh * N + (live ? n : 0)) * DP;
+        if (MAP == HH_MAP_EXP_) {
 #pragma unroll
-    for (int half = 0; half < (MAP == HH_MAP_HEDGEHOG_SOFTMAX_ ? 2 : 1); half++) {
-        const float sg = half ? -1.0f : 1.0f;
-        float mx = -INFINITY;
+            for (int lb = 0; lb < LB; lb++) {
+                f32x4 e;
 #pragma unroll
-        for (int lb = 0; lb < LB; lb++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) mx = fmaxf(mx, sg * u[lb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        f32x4 e[LB];
-        float sum = 0.0f;
-#pragma unroll
-        for (int lb = 0; lb < LB; lb++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                e[lb][r] = exp2_fast((sg * u[lb][r] - mx) * kLog2e);
-                sum += e[lb][r];
+                for (int r = 0; r < 4; r++) e[r] = exp2_fast((u[lb][r] + bl[lb][r]) * kLog2e);
+                if (live) store4(out + 16 * lb + 4 * g, to_bf16x4(e));
             }
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
-        const float rs = 1.0f / sum;
+            continue;
+        }
+        // softmax over the d directions (and, two-sided, over their negations)
 #pragma unroll
-        for (int lb = 0; lb < LB; lb++) {
-            f32x4 o;
+        for (int half = 0; half < (MAP == HH_MAP_HEDGEHOG_SOFTMAX_ ? 2 : 1); half++) {
+            const float sg = half ? -1.0f : 1.0f;
+            float mx = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 4; r++) o[r] = e[lb][r] * rs;
-            if (live) store4(out + half * D + 16 * lb + 4 * g, to_bf16x4(o));
+            for (int lb = 0; lb < LB; lb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) mx = fmaxf(mx, sg * u[lb][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            f32x4 e[LB];
+            float sum = 0.0f;
+#pragma unroll
+            for (int lb = 0; lb < LB; lb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    e[lb][r] = exp2_fast((sg * u[lb][r] - mx) * kLog2e);
+                    sum += e[lb][r];
+                }
+            sum += __shfl_xor(sum, 16);
+            sum += __shfl_xor(sum, 32);
+            const float rs = 1.0f / sum;
+#pragma unroll
+            for (int lb = 0; lb < LB; lb++) {
+                f32x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; r++) o[r] = e[lb][r] * rs;
+                if (live) store4(out + half * D + 16 * lb + 4 * g, to_bf16x4(o));
+            }
         }
     }
 }
@@ -564,7 +600,7 @@ hipError_t launch_feat_d(int mode, const FeatParams &p, int grid, hipStream_t st
 template <int D, int MAP>
 hipError_t launch_fm_variant_d(const bf16_t *x, const bf16_t *W, const bf16_t *b, bf16_t *phi, long BH, int H, int N,
                                hipStream_t st) {
-    const int tiles = (N + 63) / 64;
+    const int tiles = (N + 64 * kFmvBlocks - 1) / (64 * kFmvBlocks);
     hipLaunchKernelGGL((fm_variant_kernel<D, MAP>), dim3((unsigned)(BH * tiles)), dim3(256), 0, st, x, W, b, phi, tiles,
                        H, N);
     return hipGetLastError();
