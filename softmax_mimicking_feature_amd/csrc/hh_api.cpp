@@ -155,9 +155,12 @@ Plan make_plan(int map, int dtype, int causal, long BH, long N, int d, bool has_
     pl.chunked = true;
     pl.narrow = quadratic_family(map);
     pl.dpi = pl.narrow ? hh::kTaylorRowsInternal : 2 * d;
-    const long C = 64;
+    // causal d = 64 runs two sequences per workgroup in 32-token chunks: segments in 32-token
+    // steps, about two sequence segments per CU
+    const bool pairs = causal && !pl.narrow && d == 64;
+    const long C = pairs ? 32 : 64;
     const long nch = (N + C - 1) / C;
-    const long target = pl.narrow ? 1024 : 256L * hh::wide_wgs_per_cu(d);
+    const long target = pl.narrow ? 1024 : pairs ? 512 : 256L * hh::wide_wgs_per_cu(d);
     long nseg = target / BH;
     if (nseg < 1) nseg = 1;
     if (nseg > nch) nseg = nch;
@@ -439,7 +442,7 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
         // causal with few segments per sequence: the chunked pass sums the aggregates of the
         // earlier segments itself (at most 7 slots, still in L2) instead of a separate scan
         const bool direct_prefix = causal && pl.nseg <= 8;
-        wp.N = N; wp.H = H; wp.seg_len = pl.seg_len;
+        wp.N = N; wp.H = H; wp.BH = (int)BH; wp.seg_len = pl.seg_len;
         if (!causal && pl.nseg == 1 && d == 64) {
             // one segment per sequence: state and read-out in one workgroup, the total in LDS
             wp.nseg_grid = 1;

@@ -50,6 +50,7 @@ struct WideParams {
     long slot_bh_stride;        // slots per (b,h)
     float *S_out, *z_out;       // final state (mode 1, last segment), or null
     int N, H, nseg_grid, seg_len;
+    int BH;                     // sequences (batch x heads)
     int slot_mode;              // slot added to the starting state of segment s (modes 1, 2):
                                 //   0 none, 1 slot s if s > 0 (exclusive prefixes), 2 slot 0 (total),
                                 //   3 the sum of slots 0 .. s - 1 (segment aggregates, summed by the

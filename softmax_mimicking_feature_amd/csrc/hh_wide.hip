@@ -251,12 +251,13 @@ constexpr int waitcnt_lds_vm(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | 
 
 // Per-lane source offsets of the direct loads of [C][128] bf16 tiles by 8 waves (wave w moves
 // 1 KB blocks w, w + 8, ...): byte offsets within the tile's rows for the q / k staging layout
-// (stage_pos) and the V layout (v_pos), the offset used when the lane's row lies past the end
-// (it then reads row 0, whose granule P is stored at position P in both layouts), and the row.
+// (stage_pos) and the V layout (v_pos), and the row.  A lane whose row lies past the end reads
+// the same granule of row 0 (x0, v0): the row is then a copy of row 0 in the tile's layout, so a
+// non-finite value met by the row's zero features stays in its own value column.
 template <int C>
 struct DmaLanes128 {
     static constexpr int NB = C / 32;
-    uint32_t ox[NB], ov[NB], o0[NB];
+    uint32_t ox[NB], ov[NB], x0[NB], v0[NB];
     int row[NB];
     __device__ __forceinline__ DmaLanes128(int w, int lane) {
 #pragma unroll
@@ -264,9 +265,11 @@ struct DmaLanes128 {
             const int slot = 64 * (w + 8 * bb) + lane;
             const int r = slot / 16, P = slot % 16;
             row[bb] = r;
-            ox[bb] = 2 * (r * 128 + 8 * stage_granule<128>(r, P));
-            ov[bb] = 2 * (r * 128 + 8 * ((P - 4 * r) & 15));
-            o0[bb] = 16 * P;
+            const int gx = stage_granule<128>(r, P), gv = (P - 4 * r) & 15;
+            ox[bb] = 2 * (r * 128 + 8 * gx);
+            ov[bb] = 2 * (r * 128 + 8 * gv);
+            x0[bb] = 16 * gx;
+            v0[bb] = 16 * gv;
         }
     }
     // tile rows t0 .. t0 + C - 1 of x (valid of them) into `stage`, q / k layout or V layout
@@ -275,7 +278,8 @@ struct DmaLanes128 {
         const bf16_t *src = x + (size_t)t0 * 128;
 #pragma unroll
         for (int bb = 0; bb < NB; bb++)
-            load_to_lds_16s(src, row[bb] < valid ? (V ? ov[bb] : ox[bb]) : o0[bb], stage + 1024 * (w + 8 * bb));
+            load_to_lds_16s(src, row[bb] < valid ? (V ? ov[bb] : ox[bb]) : (V ? v0[bb] : x0[bb]),
+                            stage + 1024 * (w + 8 * bb));
     }
 };
 
@@ -965,13 +969,15 @@ __device__ __forceinline__ int ssy_vpos(int r, int G) {
 
 // Direct loads of [C][D] bf16 tiles by NWV waves (wave w moves 1 KB blocks w, w + NWV, ...):
 // per-lane byte offsets within the tile for the q / k staging layout (stage_pos) and this
-// kernel's V layout, the offset for a lane whose row lies past the end (row 0, whose granule P
-// sits at position P in both layouts), and the row.
+// kernel's V layout, and the row.  A lane whose row lies past the end reads the same granule of
+// row 0 (offsets x0, v0), so such a row is a copy of row 0 in the tile's layout: its zero
+// features then meet row 0's values column by column, and a non-finite value stays in its own
+// value column.
 template <int D, int C, int NWV>
 struct DmaLanesT {
     static constexpr int NG = D / 8;
     static constexpr int NB = C * D * 2 / 1024 / NWV;
-    uint32_t ox[NB], ov[NB], o0[NB];
+    uint32_t ox[NB], ov[NB], x0[NB], v0[NB];
     int row[NB];
     __device__ __forceinline__ DmaLanesT(int w, int lane) {
 #pragma unroll
@@ -979,10 +985,12 @@ struct DmaLanesT {
             const int slot = 64 * (w + NWV * bb) + lane;
             const int r = slot / NG, P = slot % NG;
             row[bb] = r;
-            ox[bb] = 2 * (r * D + 8 * stage_granule<D>(r, P));
             // granule G is stored at ssy_vpos(r, G): position P holds G = P - rotation
-            ov[bb] = 2 * (r * D + 8 * (D == 128 ? ((P - 4 * r) & 15) : ((P - 2 * r) & 7)));
-            o0[bb] = 16 * P;
+            const int gx = stage_granule<D>(r, P), gv = D == 128 ? ((P - 4 * r) & 15) : ((P - 2 * r) & 7);
+            ox[bb] = 2 * (r * D + 8 * gx);
+            ov[bb] = 2 * (r * D + 8 * gv);
+            x0[bb] = 16 * gx;
+            v0[bb] = 16 * gv;
         }
     }
     template <bool V>
@@ -990,7 +998,8 @@ struct DmaLanesT {
         const bf16_t *src = x + (size_t)t0 * D;
 #pragma unroll
         for (int bb = 0; bb < NB; bb++)
-            load_to_lds_16s(src, row[bb] < valid ? (V ? ov[bb] : ox[bb]) : o0[bb], stage + 1024 * (w + NWV * bb));
+            load_to_lds_16s(src, row[bb] < valid ? (V ? ov[bb] : ox[bb]) : (V ? v0[bb] : x0[bb]),
+                            stage + 1024 * (w + NWV * bb));
     }
 };
 
@@ -1728,6 +1737,507 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Chunked causal pass for d = 64 with specialised waves: the d = 128 design at a quarter of
+// its width.  One workgroup of eight waves runs two independent pipelines, the same segment of
+// two sequences 2 j and 2 j + 1 (equal lengths, so both take the same barriers); pipeline q
+// has producers on waves 2 q, 2 q + 1 and consumers on waves 4 + 2 q, 4 + 2 q + 1, so every
+// SIMD (waves w and w + 4) pairs a producer with a consumer.  Per pipeline and 32-token chunk:
+//   producer p (token block p): the q and k features of its 16 tokens for all 64 directions,
+//     phi(q) row-major in the permuted feature order, phi(k) transposed (feature rows, natural
+//     order); scores p0: blocks (0,0), (1,1); p1: block (1,0) and the masked block (0,1);
+//   consumer v: value columns 32 v .. 32 v + 31 of the state for all 128 features and z of
+//     feature blocks 4 v .. 4 v + 3: read-out, update, normaliser partial, and the outputs of
+//     the chunk before (intra-chunk product with its scores).
+// Segment slots are those of the d = 64 segment-state pass (the register image of the generic
+// chunked kernel); a consumer reads each of its accumulators from there as one 16-byte piece.
+struct CausalWs64Cfg {
+    static constexpr int D = 64, C = 32, DP = 128, NT = 512;
+    static constexpr int RQ = DP + 16, PT = C + 16, RA = C + 8;
+    static constexpr int SZ_PQ = C * RQ * 2, SZ_PK = DP * PT * 2, SZ_X = C * D * 2, SZ_A = C * RA * 2;
+    static constexpr int NDEN = 4;  // per token: the 2 consumers' normaliser partials, 2 score row sums
+    static constexpr int SZ_DEN = NDEN * C * 4;
+    static constexpr int OFF_PQ = 0;
+    static constexpr int OFF_PK = OFF_PQ + 2 * SZ_PQ;
+    static constexpr int OFF_V = OFF_PK + 2 * SZ_PK;
+    static constexpr int OFF_A = OFF_V + 3 * SZ_X;
+    static constexpr int OFF_DEN = OFF_A + 2 * SZ_A;
+    static constexpr int OFF_XQ = OFF_DEN + 2 * SZ_DEN;
+    static constexpr int OFF_XK = OFF_XQ + 2 * SZ_X;
+    static constexpr int OFF_SYNC = OFF_XK + 2 * SZ_X;  // the producers' arrival counter
+    static constexpr int PIPE_BYTES = OFF_SYNC + 16;
+    static constexpr int LDS_BYTES = 2 * PIPE_BYTES;
+    static_assert(PIPE_BYTES % 16 == 0, "pipelines 16-byte aligned");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Stored position of granule G (8 values) of row r in this kernel's V tiles (128-byte rows
+// filled by direct loads): rotated by 4 on rows 2, 3 (mod 4), so the transposing reads of 16
+// rows x 4 granules spread over both halves of the banks; the rotation repeats every 4 rows.
+__device__ __forceinline__ int v_pos64(int r, int G) { return (G + 4 * ((r >> 1) & 1)) & 7; }
+
+// Per-lane offsets of the direct loads of [32][64] bf16 tiles by the four waves of a pipeline
+// (pipeline wave pw moves 1 KB block pw): byte offsets in the q / k staging layout (stage_pos)
+// and in the V layout (v_pos64), and the row.  A row past the end reads the same granule of
+// row 0 (x0, v0), a copy of row 0 in the tile's layout.
+struct Dma64Lanes {
+    uint32_t ox, ov, x0, v0;
+    int row;
+    __device__ __forceinline__ Dma64Lanes(int pw, int lane) {
+        const int slot = 64 * pw + lane;
+        const int r = slot / 8, P = slot % 8;
+        row = r;
+        const int gx = stage_granule<64>(r, P), gv = (P - 4 * ((r >> 1) & 1)) & 7;
+        ox = 2 * (r * 64 + 8 * gx);
+        ov = 2 * (r * 64 + 8 * gv);
+        x0 = 16 * gx;
+        v0 = 16 * gv;
+    }
+    template <bool V>
+    __device__ __forceinline__ void issue(const bf16_t *x, int t0, int valid, int pw, unsigned char *stage) const {
+        load_to_lds_16s(x + (size_t)t0 * 64, row < valid ? (V ? ov : ox) : (V ? v0 : x0), stage + 1024 * pw);
+    }
+};
+
+// Producer p: features of token block p of a chunk for all 64 directions.
+template <bool FULL>
+__device__ __forceinline__ void cw64_features(const unsigned char *xq, const unsigned char *xk, int valid,
+                                              const bf16x8 (&wA)[4][2], const float (&bl2)[4][4],
+                                              const float (&bk2)[4], int p, int g, int r16, bf16_t *sPQ,
+                                              bf16_t *sPKT) {
+    using S = CausalWs64Cfg;
+    const int i = 16 * p + r16;
+    bf16x8 xb[2][2];  // [keys, queries][K step]
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) xb[t][ks] = staged_x_operand<64>(t == 0 ? xk : xq, i, ks, g);
+    // keys: u (tokens x directions), lane: direction 16 mb + r16, tokens 16 p + 4 g + r;
+    // queries: u^T (directions x tokens), lane: token i, directions 16 mb + 4 g + r
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) acc[t][mb] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) {
+            acc[0][mb] = mfma_bf16(xb[0][ks], wA[mb][ks], acc[0][mb]);
+            acc[1][mb] = mfma_bf16(wA[mb][ks], xb[1][ks], acc[1][mb]);
+        }
+    {  // keys: phi(k)^T rows 16 mb + r16 and 64 + that, tokens 16 p + 4 g .. + 3
+        const int tk = 16 * p + 4 * g;
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) {
+            f32x4 ep, en;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float u = acc[0][mb][r] * kLog2e + bk2[mb];
+                ep[r] = exp2_fast(u);
+                en[r] = exp2_fast(-u);
+                if (!FULL && tk + r >= valid) ep[r] = en[r] = 0.0f;  // keys past the end contribute nothing
+            }
+            store4(sPKT + (16 * mb + r16) * S::PT + tk, to_bf16x4(ep));
+            store4(sPKT + (64 + 16 * mb + r16) * S::PT + tk, to_bf16x4(en));
+        }
+    }
+    {  // queries: direction blocks 2 h, 2 h + 1 share one 16-byte run of their 32-feature group
+        bf16x4 pe[4], ne[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) {
+            f32x4 ep, en;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float u = acc[1][mb][r] * kLog2e + bl2[mb][r];
+                ep[r] = exp2_fast(u);
+                en[r] = exp2_fast(-u);
+            }
+            pe[mb] = to_bf16x4(ep);
+            ne[mb] = to_bf16x4(en);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+            store8(sPQ + i * S::RQ + feat_pos<true>(32 * hh + 4 * g), cat(pe[2 * hh], pe[2 * hh + 1]));
+            store8(sPQ + i * S::RQ + feat_pos<true>(64 + 32 * hh + 4 * g), cat(ne[2 * hh], ne[2 * hh + 1]));
+        }
+    }
+}
+
+__device__ __forceinline__ void cw64_features_any(const unsigned char *xq, const unsigned char *xk, int valid,
+                                                  const bf16x8 (&wA)[4][2], const float (&bl2)[4][4],
+                                                  const float (&bk2)[4], int p, int g, int r16, bf16_t *sPQ,
+                                                  bf16_t *sPKT) {
+    if (valid >= CausalWs64Cfg::C)
+        cw64_features<true>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
+    else
+        cw64_features<false>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
+}
+
+// One score block (query block ib, key block jb) over the 128 features: A^T[j][i] (lane: query
+// 16 ib + r16, keys 16 jb + 4 g + r), causal mask on the diagonal block, bf16 into sA, and its
+// row sums into normaliser slot `slot` of the queries.
+__device__ __forceinline__ void cw64_score_block(const bf16_t *sPQ, const bf16_t *sPKT, bf16_t *sA, float *sDen, int ib,
+                                                 int jb, int slot, int g, int r16) {
+    using S = CausalWs64Cfg;
+    bf16x8 ka[4], qb[4];
+    const int lop = (4 * g + (r16 >> 2)) * S::PT + 4 * (r16 & 3);
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+        const bf16_t *pk = sPKT + lop + 32 * ks * S::PT + 16 * jb;
+        ka[ks] = cat(lds_read_tr(pk), lds_read_tr(pk + 16 * S::PT));
+        qb[ks] = load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g);
+    }
+    f32x4 a2[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) a2[ks & 1] = mfma_bf16(ka[ks], qb[ks], a2[ks & 1]);
+    f32x4 a = a2[0] + a2[1];
+    if (jb == ib) {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            if (4 * g + r > r16) a[r] = 0.0f;
+    }
+    const bf16x4 ab = to_bf16x4(a);
+    float rs = ((float)ab[0] + (float)ab[1]) + ((float)ab[2] + (float)ab[3]);
+    store4(sA + (16 * ib + r16) * S::RA + 16 * jb + 4 * g, ab);
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    sDen[(16 * ib + r16) * S::NDEN + slot] = rs;  // the same value in all four lane groups
+}
+
+// Producer p's scores of one chunk: p0 blocks (0,0) and (1,1); p1 block (1,0), and zeros for the
+// masked block (0,1) and its row-sum slot.  Slots 2 / 3: row sums over key blocks 0 / 1.
+__device__ __forceinline__ void cw64_scores(const bf16_t *sPQ, const bf16_t *sPKT, bf16_t *sA, float *sDen, int p,
+                                            int g, int r16) {
+    using S = CausalWs64Cfg;
+    if (p == 0) {
+        cw64_score_block(sPQ, sPKT, sA, sDen, 0, 0, 2, g, r16);
+        cw64_score_block(sPQ, sPKT, sA, sDen, 1, 1, 3, g, r16);
+    } else {
+        cw64_score_block(sPQ, sPKT, sA, sDen, 1, 0, 2, g, r16);
+        bf16x4 zz;
+        zz[0] = zz[1] = zz[2] = zz[3] = (__bf16)0.0f;
+        store4(sA + r16 * S::RA + 16 + 4 * g, zz);
+        sDen[r16 * S::NDEN + 3] = 0.0f;
+    }
+}
+
+__device__ __forceinline__ float cw64_den(const float *sDen, int i) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(sDen + i * CausalWs64Cfg::NDEN);
+    return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// Consumer v: finish the outputs of one chunk (held read-out + intra-chunk product, normalise,
+// store).  Lane (g, r16) owns token 16 ib + r16, value columns 32 v + 8 g .. + 7.
+__device__ __forceinline__ void cw64_output(f32x4 (&numT)[2][2], const bf16_t *sA, const bf16_t *sV,
+                                            const float *sDen, int lane_v, bf16_t *__restrict__ yrow0, int valid,
+                                            int v, int g, int r16, bool store) {
+    using S = CausalWs64Cfg;
+    bf16x8 vop[2];
+#pragma unroll
+    for (int vb = 0; vb < 2; vb++) vop[vb] = operand_down_rows(sV, lane_v, 4 * vb, S::D);
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++) {
+        const int i = 16 * ib + r16;
+        const bf16x8 a = load8(sA + i * S::RA + 8 * g);
+#pragma unroll
+        for (int vb = 0; vb < 2; vb++) numT[ib][vb] = mfma_bf16(vop[vb], a, numT[ib][vb]);
+        const float rden = __builtin_amdgcn_rcpf(cw64_den(sDen, i));
+        f32x4 o0, o1;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            o0[r] = numT[ib][0][r] * rden;
+            o1[r] = numT[ib][1][r] * rden;
+        }
+        if (store && i < valid)
+            store8(yrow0 + (size_t)i * S::D + value_col<2>(v, 0, 4 * g), cat(to_bf16x4(o0), to_bf16x4(o1)));
+    }
+}
+
+// Inputs of chunk c + 1 (V) and c + 2 (q, k) into the buffers freed by the last chunk; each
+// pipeline wave moves its own 1 KB block of each tile.
+__device__ __forceinline__ void cw64_issue(const WideParams &p, const Dma64Lanes &dl, size_t base, int t_begin,
+                                           int t_end, int c, int n, int pw, unsigned char *sm) {
+    using S = CausalWs64Cfg;
+    if (c + 1 < n) {
+        const int t = t_begin + S::C * (c + 1);
+        dl.issue<true>(p.v + base, t, min(S::C, t_end - t), pw, sm + S::OFF_V + ((c + 1) % 3) * S::SZ_X);
+    }
+    if (c + 2 < n) {
+        const int t = t_begin + S::C * (c + 2), b = c & 1;
+        dl.issue<false>(p.q + base, t, min(S::C, t_end - t), pw, sm + S::OFF_XQ + b * S::SZ_X);
+        dl.issue<false>(p.k + base, t, min(S::C, t_end - t), pw, sm + S::OFF_XK + b * S::SZ_X);
+    }
+}
+
+__global__ __launch_bounds__(512, 1) void causal_ws_kernel_64(WideParams p) {
+    using S = CausalWs64Cfg;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+    const int pipe = (w >> 1) & 1, role = w >> 2, idx = w & 1;
+    const int pw = 2 * role + idx;  // wave within the pipeline: producers 0, 1, consumers 2, 3
+    int pair, s;
+    wg_head_segment(p.nseg_grid, pair, s);
+    // sequence of this pipeline.  With a multiple of 16 sequences, pair j holds sequences
+    // x + 16 m and x + 16 m + 8 (x = j mod 8, m = j / 8): both of XCD x, where the segment-state
+    // pass wrote their slots and where this pair's workgroups run.  An odd count leaves the last
+    // pipeline repeating the sequence before without writing anything.
+    const int bh_raw = p.BH % 16 == 0 ? (pair & 7) + 16 * (pair >> 3) + 8 * pipe : 2 * pair + pipe;
+    const bool writes = bh_raw < p.BH;
+    const int bh = writes ? bh_raw : bh_raw - 1;
+    const int h = bh % p.H;
+    const int t_begin = s * p.seg_len;
+    const int t_end = min(p.N, t_begin + p.seg_len);
+    const size_t base = (size_t)bh * p.N * S::D;
+    const int n = t_end > t_begin ? (t_end - t_begin + S::C - 1) / S::C : 0;
+    unsigned char *sm = smem + pipe * S::PIPE_BYTES;
+    const Dma64Lanes dl(pw, lane);
+    auto valid_of = [&](int c) { return min(S::C, t_end - (t_begin + S::C * c)); };
+    auto pq_buf = [&](int b) { return reinterpret_cast<bf16_t *>(sm + S::OFF_PQ + b * S::SZ_PQ); };
+    auto pk_buf = [&](int b) { return reinterpret_cast<bf16_t *>(sm + S::OFF_PK + b * S::SZ_PK); };
+    auto v_buf = [&](int b) { return reinterpret_cast<const bf16_t *>(sm + S::OFF_V + b * S::SZ_X); };
+    auto a_buf = [&](int b) { return reinterpret_cast<bf16_t *>(sm + S::OFF_A + b * S::SZ_A); };
+    auto den_buf = [&](int b) { return reinterpret_cast<float *>(sm + S::OFF_DEN + b * S::SZ_DEN); };
+
+    unsigned int *psync = reinterpret_cast<unsigned int *>(sm + S::OFF_SYNC);
+    if (pw == 0 && lane == 0) *psync = 0u;
+    __syncthreads();
+    if (role == 0) {
+        // producer idx: the staging loads of the prologue (pipeline blocks idx and idx + 2)
+#pragma unroll
+        for (int hw = 0; hw < 2; hw++) {
+            const Dma64Lanes dh(idx + 2 * hw, lane);
+            if (n > 0) {
+                dh.issue<false>(p.q + base, t_begin, valid_of(0), idx + 2 * hw, sm + S::OFF_XQ);
+                dh.issue<false>(p.k + base, t_begin, valid_of(0), idx + 2 * hw, sm + S::OFF_XK);
+                dh.issue<true>(p.v + base, t_begin, valid_of(0), idx + 2 * hw, sm + S::OFF_V);
+            }
+            if (n > 1) {
+                dh.issue<false>(p.q + base, t_begin + S::C, valid_of(1), idx + 2 * hw, sm + S::OFF_XQ + S::SZ_X);
+                dh.issue<false>(p.k + base, t_begin + S::C, valid_of(1), idx + 2 * hw, sm + S::OFF_XK + S::SZ_X);
+            }
+        }
+        // W operands straight from memory (rows 16 mb + r16, input dims 32 ks + 8 g .. + 7) and
+        // the bias of the query rows (16 mb + 4 g + r) and of the key column (16 mb + r16)
+        bf16x8 wA[4][2];
+        float bl2[4][4], bk2[4];
+        const bf16_t *Wh = p.W + (size_t)h * 64 * 64;
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) wA[mb][ks] = load8(Wh + (size_t)(16 * mb + r16) * 64 + 32 * ks + 8 * g);
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                bl2[mb][r] = p.b ? bf16_bits_to_float(p.b[(size_t)h * 64 + 16 * mb + 4 * g + r]) * kLog2e : 0.0f;
+            bk2[mb] = p.b ? bf16_bits_to_float(p.b[(size_t)h * 64 + 16 * mb + r16]) * kLog2e : 0.0f;
+        }
+        producer_barrier(psync, 2, lane);
+        if (n > 0) cw64_features_any(sm + S::OFF_XQ, sm + S::OFF_XK, valid_of(0), wA, bl2, bk2, idx, g, r16, pq_buf(0),
+                                     pk_buf(0));
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int c = 0; c < n; c++) {
+            cw64_issue(p, dl, base, t_begin, t_end, c, n, pw, sm);
+            const int b2 = c & 1;
+            cw64_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), idx, g, r16);
+            if (c + 1 < n)
+                cw64_features_any(sm + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, sm + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
+                                  valid_of(c + 1), wA, bl2, bk2, idx, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1));
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        return;
+    }
+    // Consumer v = idx: value columns value_col<2>(v, vb, c) of S for all 128 features, z rows
+    // of feature blocks 4 v .. 4 v + 3.
+    const int v = idx;
+    f32x4 sacc[8][2];
+    f32x4 zacc[4];
+    {
+#pragma unroll
+        for (int fb = 0; fb < 8; fb++) sacc[fb][0] = sacc[fb][1] = zero4();
+#pragma unroll
+        for (int zb = 0; zb < 4; zb++) zacc[zb] = zero4();
+        if (p.S_in) {
+            const float *Si = p.S_in + (size_t)bh * p.in_bh_stride * S::DP * S::D;
+            const float *zi = p.z_in + (size_t)bh * p.in_bh_stride * S::DP;
+#pragma unroll
+            for (int fb = 0; fb < 8; fb++)
+#pragma unroll
+                for (int vb = 0; vb < 2; vb++) {
+                    const int nn = value_col<2>(v, vb, r16);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) sacc[fb][vb][r] = Si[(size_t)(16 * fb + 4 * g + r) * S::D + nn];
+                }
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) zacc[zb][r] = zi[16 * (4 * v + zb) + 4 * g + r];
+        }
+        int t0 = 0, t1 = 0;  // slots to add
+        if (s > 0 && p.slot_mode == 1) t0 = s, t1 = s + 1;
+        if (s > 0 && p.slot_mode == 3) t0 = 0, t1 = s;
+        // slot image of the d = 64 segment-state pass: value column nn, feature block fb of wave
+        // nn / 16 sits in piece (nn / 16) 4 + fb / 2, half fb % 2, lane 16 g + nn % 16
+        int lsrc[2], esrc[2];
+#pragma unroll
+        for (int vb = 0; vb < 2; vb++) {
+            const int nn = value_col<2>(v, vb, r16);
+            lsrc[vb] = 16 * g + (nn & 15);
+            esrc[vb] = (nn >> 4) * 4;
+        }
+        for (int t = t0; t < t1; t++) {
+            const size_t sl = (size_t)bh * p.slot_bh_stride + t;
+            const float *zs = p.z_slots + sl * S::DP;
+            const float *img = p.S_slots + sl * S::DP * S::D;
+            f32x4 zslot[4], raw[8][2];
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++) zslot[zb] = *reinterpret_cast<const f32x4 *>(zs + 16 * (4 * v + zb) + 4 * g);
+#pragma unroll
+            for (int fb = 0; fb < 8; fb++)
+#pragma unroll
+                for (int vb = 0; vb < 2; vb++) raw[fb][vb] = *slot_piece(img, esrc[vb] + (fb >> 1), fb & 1, lsrc[vb]);
+#pragma unroll
+            for (int fb = 0; fb < 8; fb++)
+#pragma unroll
+                for (int vb = 0; vb < 2; vb++) sacc[fb][vb] += raw[fb][vb];
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++) zacc[zb] += zslot[zb];
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    f32x4 numT[2][2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++) numT[ib][0] = numT[ib][1] = zero4();
+    const int r0 = 8 * g + (r16 >> 2);
+    const int lane_v = r0 * S::D + 8 * v_pos64(r0, 4 * v + (r16 & 3));
+    const bf16x8 ones = ones_bf16x8();
+    bf16_t *ybase = p.y + base;
+
+    for (int c = 0; c < n; c++) {
+        cw64_issue(p, dl, base, t_begin, t_end, c, n, pw, sm);
+        const int b2 = c & 1;
+        const bf16_t *sPQ = pq_buf(b2);
+        const bf16_t *sPK = pk_buf(b2);
+        const bf16_t *sVp = v_buf((c + 2) % 3);
+        const bf16_t *sAp = a_buf(b2 ^ 1);
+        const float *sDp = den_buf(b2 ^ 1);
+        bf16x8 vp[2], ao[2];
+#pragma unroll
+        for (int vb = 0; vb < 2; vb++) vp[vb] = operand_down_rows(sVp, lane_v, 4 * vb, S::D);
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++) ao[ib] = load8(sAp + (16 * ib + r16) * S::RA + 8 * g);
+        const bf16_t *sV = v_buf(c % 3);
+        bf16x8 vop[2];
+#pragma unroll
+        for (int vb = 0; vb < 2; vb++) vop[vb] = operand_down_rows(sV, lane_v, 4 * vb, S::D);
+        bf16x8 qn[2], an[2];
+        auto load_step = [&](int ks, bf16x8(&qo)[2], bf16x8(&ao2)[2]) {
+#pragma unroll
+            for (int ib = 0; ib < 2; ib++) qo[ib] = load8(sPQ + (16 * ib + r16) * S::RQ + 32 * ks + 8 * g);
+#pragma unroll
+            for (int j = 0; j < 2; j++) ao2[j] = load8(sPK + (32 * ks + 16 * j + r16) * S::PT + 8 * g);
+        };
+        load_step(0, qn, an);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 nt[2][2];
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++) nt[ib][0] = nt[ib][1] = zero4();
+        float dsum[2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) {
+            bf16x8 qc[2] = {qn[0], qn[1]}, ac[2] = {an[0], an[1]};
+            if (ks < 3) load_step(ks + 1, qn, an);
+            if (ks == 0) {  // intra-chunk product of chunk c - 1
+#pragma unroll
+                for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+                    for (int vb = 0; vb < 2; vb++) numT[ib][vb] = mfma_bf16(vp[vb], ao[ib], numT[ib][vb]);
+            }
+            if (ks == 1) {  // its normaliser
+#pragma unroll
+                for (int ib = 0; ib < 2; ib++) dsum[ib] = cw64_den(sDp, 16 * ib + r16);
+            }
+            bf16x8 sb[2];
+#pragma unroll
+            for (int vb = 0; vb < 2; vb++) sb[vb] = acc_pair_to_operand(sacc[2 * ks][vb], sacc[2 * ks + 1][vb]);
+#pragma unroll
+            for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+                for (int vb = 0; vb < 2; vb++) nt[ib][vb] = mfma_bf16(sb[vb], qc[ib], nt[ib][vb]);
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int vb = 0; vb < 2; vb++) sacc[2 * ks + j][vb] = mfma_bf16(ac[j], vop[vb], sacc[2 * ks + j][vb]);
+            if (ks == 2 && c > 0 && writes) {  // outputs of chunk c - 1 (every token of it is valid)
+                bf16_t *yrow0 = ybase + (size_t)(t_begin + S::C * (c - 1)) * S::D;
+#pragma unroll
+                for (int ib = 0; ib < 2; ib++) {
+                    const float rden = __builtin_amdgcn_rcpf(dsum[ib]);
+                    f32x4 o0, o1;
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        o0[r] = numT[ib][0][r] * rden;
+                        o1[r] = numT[ib][1][r] * rden;
+                    }
+                    store8(yrow0 + (size_t)(16 * ib + r16) * S::D + value_col<2>(v, 0, 4 * g),
+                           cat(to_bf16x4(o0), to_bf16x4(o1)));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++) {
+            numT[ib][0] = nt[ib][0];
+            numT[ib][1] = nt[ib][1];
+        }
+        f32x4 dacc[2] = {zero4(), zero4()};
+        {
+            const bf16_t *sPQz = sPQ + 64 * v;  // K steps 2 v, 2 v + 1
+#pragma unroll
+            for (int kz = 0; kz < 2; kz++) {
+                const bf16x8 zop = acc_pair_to_operand(zacc[2 * kz], zacc[2 * kz + 1]);
+#pragma unroll
+                for (int ib = 0; ib < 2; ib++)
+                    dacc[ib] = mfma_bf16(zop, load8(sPQz + (16 * ib + r16) * S::RQ + 32 * kz + 8 * g), dacc[ib]);
+            }
+        }
+        // every row of dacc holds the token's partial: all four lane groups write the same value
+        float *sDen = den_buf(b2);
+        sDen[r16 * S::NDEN + v] = dacc[0][0];
+        sDen[(16 + r16) * S::NDEN + v] = dacc[1][0];
+#pragma unroll
+        for (int zb = 0; zb < 4; zb++)
+            zacc[zb] = mfma_bf16(load8(sPK + (16 * (4 * v + zb) + r16) * S::PT + 8 * g), ones, zacc[zb]);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    if (n > 0)
+        cw64_output(numT, a_buf((n - 1) & 1), v_buf((n - 1) % 3), den_buf((n - 1) & 1), lane_v,
+                    ybase + (size_t)(t_begin + S::C * (n - 1)) * S::D, valid_of(n - 1), v, g, r16, writes);
+    if (writes && p.S_out && s == p.nseg_grid - 1) {
+        float *So = p.S_out + (size_t)bh * S::DP * S::D;
+        float *zo = p.z_out + (size_t)bh * S::DP;
+#pragma unroll
+        for (int fb = 0; fb < 8; fb++)
+#pragma unroll
+            for (int vb = 0; vb < 2; vb++) {
+                const int nn = value_col<2>(v, vb, r16);
+#pragma unroll
+                for (int r = 0; r < 4; r++) So[(size_t)(16 * fb + 4 * g + r) * S::D + nn] = sacc[fb][vb][r];
+            }
+        if (r16 == 0) {
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) zo[16 * (4 * v + zb) + 4 * g + r] = zacc[zb][r];
+        }
+    }
+}
+
 // Stand-alone feature map: each workgroup maps `cpw` chunks of 64 tokens of one head and
 // writes phi [token][2d] through an LDS tile so that global stores are full 16-byte rows.
 template <int D>
@@ -1871,6 +2381,9 @@ static hipError_t launch_wide_d(int mode, const WideParams &p, int grid, hipStre
     case WM_CAUSAL:
         if (D == 128)
             hipLaunchKernelGGL(causal_ws_kernel_128, dim3(grid), dim3(CausalWsCfg::NT), 0, st, p);
+        else if (D == 64)  // two sequences per workgroup
+            hipLaunchKernelGGL(causal_ws_kernel_64, dim3((unsigned)((p.BH + 1) / 2 * p.nseg_grid)),
+                               dim3(CausalWs64Cfg::NT), 0, st, p);
         else
             hipLaunchKernelGGL((wide_kernel<D, WM_CAUSAL>), dim3(grid), dim3(K::NT), 0, st, p);
         break;
