@@ -631,10 +631,9 @@ __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per
     bf16_t *sU = reinterpret_cast<bf16_t *>(smem + K::OFF_U);
     for (int i = tid; i < K::LDS_BYTES / 16; i += 256) reinterpret_cast<f32x4 *>(smem)[i] = zero4();
     __syncthreads();
-    for (int e2 = tid; e2 < D * D / 8; e2 += 256) {
-        const int l = e2 / (D / 8), m = 8 * (e2 % (D / 8));
-        *reinterpret_cast<bf16x8 *>(sW + l * K::PW + m) = *reinterpret_cast<const bf16x8 *>(Wh + (size_t)l * D + m);
-    }
+    stage_pieces<256, D * D / 8>(
+        tid, [&](int e) { return Wh + 8 * e; }, [&](int e) { return sW + (e / (D / 8)) * K::PW + 8 * (e % (D / 8)); },
+        [](int) { return true; });
     __syncthreads();
     // dW part: blocks (lb, mb) dealt over the 4 waves; db part: the ones trick
     constexpr int NBLK = (D / 16) * (D / 16);
@@ -646,6 +645,19 @@ __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per
     const bf16x8 ones = ones_bf16x8();
     const int lr = 8 * g + (r16 >> 2), lo = 4 * (r16 & 3);
     const int lrp = 4 * g + (r16 >> 2);
+    // bias of directions 16 lb + 4 g + r, loaded once behind one test of the pointer (a test per
+    // element would wait for each load before issuing the next)
+    float biasl[K::LB][4];
+#pragma unroll
+    for (int lb = 0; lb < K::LB; lb++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) biasl[lb][r] = 0.0f;
+    if (p.b) {
+#pragma unroll
+        for (int lb = 0; lb < K::LB; lb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) biasl[lb][r] = bf16_bits_to_float(p.b[(size_t)h * D + 16 * lb + 4 * g + r]);
+    }
 
     for (int src = 0; src < 2; src++) {
         const bf16_t *x = src == 0 ? p.q : p.k;
@@ -656,11 +668,10 @@ __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per
             if (tile >= tiles_per_seq) break;
             const int n0 = tile * 64;
             // x tile (rows past the end zero)
-            for (int e2 = tid; e2 < 64 * D / 8; e2 += 256) {
-                const int r = e2 / (D / 8), m = 8 * (e2 % (D / 8));
-                *reinterpret_cast<bf16x8 *>(sX + r * K::PX + m) =
-                    n0 + r < p.N ? *reinterpret_cast<const bf16x8 *>(x + ((size_t)bh * p.N + n0 + r) * D + m) : zero_bf16x8();
-            }
+            stage_pieces<256, 64 * D / 8>(
+                tid, [&](int e) { return x + ((size_t)bh * p.N + n0 + e / (D / 8)) * D + 8 * (e % (D / 8)); },
+                [&](int e) { return sX + (e / (D / 8)) * K::PX + 8 * (e % (D / 8)); },
+                [&](int e) { return n0 + e / (D / 8) < p.N; });
             __syncthreads();
             const int nn = n0 + 16 * wv + r16;       // this lane's token
             const bool live = nn < p.N;
@@ -688,9 +699,7 @@ __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per
                     if (MAP == HH_MAP_HEDGEHOG_) bneg = *reinterpret_cast<const f32x4 *>(dp_ + D + 16 * lb + 4 * g);
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
-                        const int l = 16 * lb + 4 * g + r;
-                        const float bl = p.b ? bf16_bits_to_float(p.b[(size_t)h * D + l]) : 0.0f;
-                        const float uu = u[lb][r] + bl;
+                        const float uu = u[lb][r] + biasl[lb][r];
                         float v = a[r] * __expf(uu);
                         if (MAP == HH_MAP_HEDGEHOG_) v -= bneg[r] * __expf(-uu);
                         du[lb][r] = v;

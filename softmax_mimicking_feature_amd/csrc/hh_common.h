@@ -87,6 +87,26 @@ __device__ __forceinline__ bf16_t float_to_bf16_bits(float f) {
     return *reinterpret_cast<bf16_t *>(&b);
 }
 
+// Copy of N16 16-byte pieces from global memory into LDS by the NT threads of a workgroup
+// (thread tid moves pieces tid, tid + NT, ...): piece e comes from src_of(e) (or is zero where
+// live(e) is false) and goes to dst_of(e).  Every load is issued before the first store: a loop
+// that stores each piece before loading the next waits one memory latency per piece.
+template <int NT, int N16, typename Src, typename Dst, typename Live>
+__device__ __forceinline__ void stage_pieces(int tid, Src src_of, Dst dst_of, Live live) {
+    constexpr int PER = (N16 + NT - 1) / NT;
+    bf16x8 tmp[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int e = tid + NT * i;
+        tmp[i] = (N16 % NT == 0 || e < N16) && live(e) ? load8(src_of(e)) : zero_bf16x8();
+    }
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int e = tid + NT * i;
+        if (N16 % NT == 0 || e < N16) store8(dst_of(e), tmp[i]);
+    }
+}
+
 // Workgroup -> (head bh, segment s) for grids of BH x nseg workgroups.  Workgroups are dealt to
 // the eight XCDs round-robin (blockIdx mod 8); when BH is a multiple of 8, all segments of a head
 // go to one XCD, so that the head's W (and its state slot) is fetched into that XCD's L2 once.

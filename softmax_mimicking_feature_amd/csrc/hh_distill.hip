@@ -89,9 +89,23 @@ __global__ __launch_bounds__(NT) void distill_kernel(DistillParams p) {
         const bf16_t *Wh = p.W + (size_t)h * D * D;
         constexpr int WP = D + 8;  // row pitch of W in LDS (the key-feature tile is free until the first tile)
         static_assert(D * WP <= KT * C::FP, "W fits in the key-feature tile");
-        for (int e = tid; e < D * D / 8; e += NT) store8(sF + (e / (D / 8)) * WP + 8 * (e % (D / 8)), load8(Wh + 8 * e));
+        stage_pieces<NT, D * D / 8>(
+            tid, [&](int e) { return Wh + 8 * e; }, [&](int e) { return sF + (e / (D / 8)) * WP + 8 * (e % (D / 8)); },
+            [](int) { return true; });
         __syncthreads();
         constexpr int NMB = D / 16;
+        // the bias of directions 16 mb + 4 g + rr, all loads issued behind one test of the pointer
+        float bq[NMB][4];
+#pragma unroll
+        for (int mb = 0; mb < NMB; mb++)
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) bq[mb][rr] = 0.0f;
+        if (p.b) {
+#pragma unroll
+            for (int mb = 0; mb < NMB; mb++)
+#pragma unroll
+                for (int rr = 0; rr < 4; rr++) bq[mb][rr] = bf16_bits_to_float(p.b[(size_t)h * D + 16 * mb + 4 * g + rr]);
+        }
         f32x4 u[NMB];
 #pragma unroll
         for (int mb = 0; mb < NMB; mb++) {
@@ -105,10 +119,7 @@ __global__ __launch_bounds__(NT) void distill_kernel(DistillParams p) {
 #pragma unroll
             for (int ks = 0; ks < C::KSD; ks++) u[mb] = mfma_bf16(wa[ks], qop[ks], u[mb]);
 #pragma unroll
-            for (int rr = 0; rr < 4; rr++) {
-                const float bb = p.b ? bf16_bits_to_float(p.b[(size_t)h * D + 16 * mb + 4 * g + rr]) : 0.0f;
-                u[mb][rr] = (u[mb][rr] + bb) * kLog2e;
-            }
+            for (int rr = 0; rr < 4; rr++) u[mb][rr] = (u[mb][rr] + bq[mb][rr]) * kLog2e;
         }
         // (d = 16: one step, exp(u) of the 16 directions then exp(-u) of the same)
         constexpr int HALF = C::KSF / 2 > 0 ? C::KSF / 2 : 1;

@@ -443,10 +443,9 @@ __global__ __launch_bounds__(256) void fm_variant_kernel(const bf16_t *__restric
     // reads of 16 rows x 4 column runs fall in distinct banks)
     constexpr int WP = D + 16;
     __shared__ __attribute__((aligned(16))) bf16_t sW[D * WP];
-    for (int e = threadIdx.x; e < D * D / 8; e += 256) {
-        const int row = e / (D / 8), c8 = e % (D / 8);
-        *reinterpret_cast<bf16x8 *>(sW + row * WP + 8 * c8) = *reinterpret_cast<const bf16x8 *>(Wh + (size_t)row * D + 8 * c8);
-    }
+    stage_pieces<256, D * D / 8>(
+        threadIdx.x, [&](int e) { return Wh + 8 * e; },
+        [&](int e) { return sW + (e / (D / 8)) * WP + 8 * (e % (D / 8)); }, [](int) { return true; });
     __syncthreads();
     // A operands: W rows 16 lb + r16, input dims 32 ks + 8 g .. + 7 (D = 16: the upper half zero)
     bf16x8 wa[LB][KS];
@@ -460,8 +459,13 @@ __global__ __launch_bounds__(256) void fm_variant_kernel(const bf16_t *__restric
 #pragma unroll
     for (int lb = 0; lb < LB; lb++)
 #pragma unroll
-        for (int r = 0; r < 4; r++)
-            bl[lb][r] = (MAP == HH_MAP_EXP_ && b) ? bf16_bits_to_float(b[(size_t)h * D + 16 * lb + 4 * g + r]) : 0.0f;
+        for (int r = 0; r < 4; r++) bl[lb][r] = 0.0f;
+    if (MAP == HH_MAP_EXP_ && b) {  // one test around the loads, so that they leave together
+#pragma unroll
+        for (int lb = 0; lb < LB; lb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) bl[lb][r] = bf16_bits_to_float(b[(size_t)h * D + 16 * lb + 4 * g + r]);
+    }
     // B operand of a block: token r16, input dims 32 ks + 8 g .. + 7
     auto load_x = [&](int n, bf16x8 (&xb)[KS]) {
         const long tk = bh * N + (n < N ? n : 0);

@@ -263,12 +263,16 @@ hipError_t launch_seq_f32(const SeqParams &p, int BH, hipStream_t st) {
 // ----------------------------------------------------------------------------------------
 // Decode step.  One workgroup per (b,h): features of the new q and k, then one streaming
 // pass over S [dp][d] (read, add phi(k) v^T, write back, accumulate phi(q)^T S), float4
-// per thread.  Thread t always touches column quad t % (d/4).
+// per thread.  Thread t always touches column quad t % (d/4).  Loads leave in the order they
+// are needed: the token's q, k, v and this thread's part of W, then the state pieces.  All
+// workgroups request their state at once, so a load queued behind them would arrive only
+// with the last of them, and the feature maps, and every write of S after them, would wait.
 #ifndef HH_DEC_THREADS
 #define HH_DEC_THREADS 256
 #endif
 constexpr int kDecThreads = HH_DEC_THREADS;
 constexpr int kDecHeld = 32;  // state pieces per thread fetched up front (all of them for d = 128)
+constexpr int kDecWPieces = 8;  // 16-byte pieces of W per thread held in registers (d = 128: 8)
 
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     __shared__ float sq[128], sk[128], sv[128];
@@ -283,6 +287,28 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     const int q4 = d / 4;
     const int n4 = dp * q4;
     f32x4 *S4 = reinterpret_cast<f32x4 *>(p.S + (size_t)bh * dp * d);
+    float xq = 0.0f, xk = 0.0f, xv = 0.0f;
+    if (t < d) {
+        xq = ld(p.q, (size_t)bh * d + t, dt);
+        xk = ld(p.k, (size_t)bh * d + t, dt);
+        xv = ld(p.v, (size_t)bh * d + t, dt);
+    }
+    const void *W = p.W;
+    const size_t woff = (size_t)h * d * d;
+    // u = W x for q and k together: kDecThreads / d consecutive threads share a row of W and
+    // read contiguous pieces of it (held in registers when they are whole 16-byte pieces of a
+    // bf16 W), then combine their partial dot products
+    const int tpr = kDecThreads / d < d ? kDecThreads / d : d;
+    const int l = t / tpr, part = t % tpr, ept = d / tpr;
+    const size_t ro = woff + (size_t)(l < d ? l : 0) * d + (size_t)part * ept;
+    const bool wreg_path = !quadratic_family(p.map) && dt == 1 && ept % 8 == 0 && ept / 8 <= kDecWPieces;
+    bf16x8 wreg[kDecWPieces];
+    if (wreg_path && l < d) {
+        const bf16x8 *wr = reinterpret_cast<const bf16x8 *>(reinterpret_cast<const bf16_t *>(W) + ro);
+#pragma unroll
+        for (int j = 0; j < kDecWPieces; j++)
+            if (j < ept / 8) wreg[j] = wr[j];
+    }
     f32x4 held[kDecHeld];
 #pragma unroll
     for (int i = 0; i < kDecHeld; i++) {
@@ -290,26 +316,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
         if (e4 < n4) held[i] = __builtin_nontemporal_load(S4 + e4);
     }
     if (t < d) {
-        sq[t] = ld(p.q, (size_t)bh * d + t, dt);
-        sk[t] = ld(p.k, (size_t)bh * d + t, dt);
-        sv[t] = ld(p.v, (size_t)bh * d + t, dt);
+        sq[t] = xq;
+        sk[t] = xk;
+        sv[t] = xv;
     }
     __syncthreads();
-    const void *W = p.W;
-    const size_t woff = (size_t)h * d * d;
     if (!quadratic_family(p.map)) {
-        // u = W x for q and k together: kDecThreads / d consecutive threads share a row of W and
-        // read contiguous pieces of it, then combine their partial dot products
-        const int tpr = kDecThreads / d < d ? kDecThreads / d : d;
-        const int l = t / tpr, part = t % tpr, ept = d / tpr;
         float uq = 0.0f, uk = 0.0f;
-        const size_t ro = woff + (size_t)(l < d ? l : 0) * d + (size_t)part * ept;
         if (l >= d) {
             // spare threads (more threads than d rows x d elements): nothing to add
-        } else if (dt == 1 && ept % 8 == 0) {
-            const bf16x8 *wr = reinterpret_cast<const bf16x8 *>(reinterpret_cast<const bf16_t *>(W) + ro);
-            for (int j = 0; j < ept / 8; j++) {
-                const bf16x8 wv = wr[j];
+        } else if (wreg_path) {
+#pragma unroll
+            for (int j = 0; j < kDecWPieces; j++) {
+                if (j >= ept / 8) break;
+                const bf16x8 wv = wreg[j];
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
                     const float wf = (float)wv[e];
