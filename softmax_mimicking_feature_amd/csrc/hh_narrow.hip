@@ -41,6 +41,10 @@ constexpr int RT = C + 8;       // row stride of [D][C] tiles (bf16)
 constexpr int QFP = D + 8;      // row stride of the fp32 [C][D] query tile: 96 bytes, so the 16-byte
                                 // reads of 16 rows x 4 column runs hit distinct banks
 constexpr int KTP = C + 8;      // row stride of the fp32 [D][C] key tile: 288 bytes (32 mod 256)
+// A zero state of one slot: the starting state read when the caller gives none, so that its
+// loads are unconditional and leave together (a test of the pointer per element would wait on
+// each load before issuing the next).
+__device__ float zero_slot[kTaylorRowsInternal * (D + 1)];
 constexpr float kInvSqrt2 = 0.70710678118654752f;
 enum { NM_STATE = 0, NM_CAUSAL = 1, NM_READOUT = 2 };
 }  // namespace
@@ -77,7 +81,7 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
     // State S[f][n] (lane: column n = r16, rows f = 16 fb + 4 g + r) and z (same rows, every column).
     f32x4 sacc[NB], zacc[NB];
     {
-        const float *Si = nullptr, *zi = nullptr;
+        const float *Si = zero_slot, *zi = zero_slot + kTaylorRowsInternal * D;
         if (MODE != NM_STATE && p.S_in) {
             const size_t slot = (size_t)bh * p.in_bh_stride + (size_t)s * p.in_seg_stride;
             Si = p.S_in + slot * kTaylorRowsInternal * D;
@@ -88,8 +92,8 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int f = 16 * (FB0 + lb) + 4 * g + r;
-                sacc[lb][r] = Si ? Si[(size_t)f * D + r16] : 0.0f;
-                zacc[lb][r] = zi ? zi[f] : 0.0f;
+                sacc[lb][r] = Si[(size_t)f * D + r16];
+                zacc[lb][r] = zi[f];
             }
     }
     const bf16x8 ones = ones_bf16x8();
@@ -352,12 +356,15 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
         // depends on), is added back so that S_out = S0 + the sum over the keys exactly.
         const float *S0c = p.S0c ? p.S0c + (size_t)bh * 273 * D : nullptr;
         const float *z0c = p.z0c ? p.z0c + (size_t)bh * 273 : nullptr;
+        // canonical rows of every element of this lane (-1: none); then the pair halves of the
+        // initial state, all loaded before the first is used (from the output rows, masked, where
+        // there is no initial state: a branch per element would wait on each load in turn)
+        int cas[NB][4], cbs[NB][4];
 #pragma unroll
         for (int lb = 0; lb < NB; lb++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int fb = FB0 + lb, pos = 4 * g + r;
-                const float sv = sacc[lb][r], zv = zacc[lb][r];
                 int ca = -1, cb = -1;
                 if (fb == 0) {
                     ca = 1 + pos;
@@ -370,23 +377,36 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
                 } else if (pos == 8) {
                     ca = 0;
                 }
+                cas[lb][r] = ca;
+                cbs[lb][r] = cb;
+            }
+        const float *Ssrc = S0c ? S0c : So;
+        const float *zsrc = z0c ? z0c : zo;
+        float hs[NB][4], hz[NB][4];
+#pragma unroll
+        for (int lb = 0; lb < NB; lb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int ca = cas[lb][r] < 0 ? 0 : cas[lb][r], cb = cbs[lb][r] < 0 ? 0 : cbs[lb][r];
+                hs[lb][r] = Ssrc[(size_t)ca * D + r16] - Ssrc[(size_t)cb * D + r16];
+                hz[lb][r] = zsrc[ca] - zsrc[cb];
+            }
+#pragma unroll
+        for (int lb = 0; lb < NB; lb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float sv = sacc[lb][r], zv = zacc[lb][r];
+                const int ca = cas[lb][r], cb = cbs[lb][r];
                 if (ca < 0) continue;
                 if (cb < 0) {
                     So[(size_t)ca * D + r16] = sv;
                     if (r16 == 0) zo[ca] = zv;
                     continue;
                 }
-                float sa = sv * kInvSqrt2, sb = sa, za = zv * kInvSqrt2, zb = za;
-                if (S0c) {
-                    const float h = 0.5f * (S0c[(size_t)ca * D + r16] - S0c[(size_t)cb * D + r16]);
-                    sa += h;
-                    sb -= h;
-                }
-                if (z0c) {
-                    const float h = 0.5f * (z0c[ca] - z0c[cb]);
-                    za += h;
-                    zb -= h;
-                }
+                // (selected, not scaled by zero: the stand-in rows may hold anything)
+                const float h = S0c ? 0.5f * hs[lb][r] : 0.0f, hzz = z0c ? 0.5f * hz[lb][r] : 0.0f;
+                const float sa = sv * kInvSqrt2 + h, sb = sv * kInvSqrt2 - h;
+                const float za = zv * kInvSqrt2 + hzz, zb = zv * kInvSqrt2 - hzz;
                 So[(size_t)ca * D + r16] = sa;
                 So[(size_t)cb * D + r16] = sb;
                 if (r16 == 0) {

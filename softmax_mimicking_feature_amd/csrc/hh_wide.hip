@@ -2033,21 +2033,24 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_64(WideParams p) {
         }
         // W operands straight from memory (rows 16 mb + r16, input dims 32 ks + 8 g .. + 7) and
         // the bias of the query rows (16 mb + 4 g + r) and of the key column (16 mb + r16).  The
-        // bias is loaded without a branch (from W in place of a missing bias, then masked): a
-        // test per element would wait for each of these loads before issuing the next.
+        // bias is loaded without a branch (from W in place of a missing bias, then replaced by
+        // zero): a test per element would wait for each of these loads before issuing the next.
         bf16x8 wA[4][2];
         float bl2[4][4], bk2[4];
         const bf16_t *Wh = p.W + (size_t)h * 64 * 64;
         const bool has_b = p.b != nullptr;
         const bf16_t *bsrc = has_b ? p.b + (size_t)h * 64 : Wh;  // W has 64 x 64 entries per head
-        const float bscale = has_b ? kLog2e : 0.0f;
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) {
 #pragma unroll
             for (int ks = 0; ks < 2; ks++) wA[mb][ks] = load8(Wh + (size_t)(16 * mb + r16) * 64 + 32 * ks + 8 * g);
 #pragma unroll
-            for (int r = 0; r < 4; r++) bl2[mb][r] = bf16_bits_to_float(bsrc[16 * mb + 4 * g + r]) * bscale;
-            bk2[mb] = bf16_bits_to_float(bsrc[16 * mb + r16]) * bscale;
+            for (int r = 0; r < 4; r++) {
+                const float bv = bf16_bits_to_float(bsrc[16 * mb + 4 * g + r]) * kLog2e;
+                bl2[mb][r] = has_b ? bv : 0.0f;
+            }
+            const float bv = bf16_bits_to_float(bsrc[16 * mb + r16]) * kLog2e;
+            bk2[mb] = has_b ? bv : 0.0f;
         }
         producer_barrier(psync, 2, lane);
         if (n > 0) cw64_features_any(sm + S::OFF_XQ, sm + S::OFF_XK, valid_of(0), wA, bl2, bk2, idx, g, r16, pq_buf(0),
