@@ -81,10 +81,12 @@ struct BwdCfg {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
+// (a uniform base plus the piece's 32-bit element offset: 64-bit per-piece addresses would be
+// kept live across the chunk loop and spill)
 template <int n>
 __device__ __forceinline__ bf16x8 load_piece(const bf16_t *src, int p, int valid) {
     const int row = p / (n / 8), col = 8 * (p % (n / 8));
-    return row < valid ? *reinterpret_cast<const bf16x8 *>(src + (size_t)row * n + col) : zero_bf16x8();
+    return row < valid ? *reinterpret_cast<const bf16x8 *>(src + (uint32_t)(row * n + col)) : zero_bf16x8();
 }
 template <int n, int pitch>
 __device__ __forceinline__ void store_piece(bf16_t *tile, int p, const bf16x8 &x) {
@@ -347,13 +349,20 @@ __device__ void bwd_q_body(const BwdParams &p, unsigned char *smem, int bh, int 
                         o = mfma_bf16(*reinterpret_cast<const bf16x8 *>(mrow + 32 * ks + 8 * g),
                                       down_rows(sK, lr * K::PF + lo, 32 * ks, 16 * fb, K::PF), o);
                 }
-                // lane: feature 16 fb + r16, queries 16 ib + 4 g + r
+                // lane: feature 16 fb + r16, queries 16 ib + 4 g + r.  Each store takes a uniform row
+                // base and the lane's 32-bit offset, so that no per-store 64-bit lane address stays
+                // live across the chunk loop.
+                // (c of the lane's four queries in one read, and validity as a count, for the same
+                // reason: per-query addresses and indices would be kept live across the loop)
                 const float zf = sZ[16 * fb + r16];
+                const uint32_t lane_off = (uint32_t)(4 * g * DP + 16 * fb + r16);
+                const f32x4 cq = *reinterpret_cast<const f32x4 *>(sC + 16 * ib + 4 * g);
+                const int rem = valid - 16 * ib - 4 * g;
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const int i = 16 * ib + 4 * g + r;
-                    o[r] = fmaf(sC[i], zf, o[r]);
-                    if (i < valid && 16 * fb + r16 < DP) p.dphiq[(tok_base + t0 + i) * DP + 16 * fb + r16] = o[r];
+                    o[r] = fmaf(cq[r], zf, o[r]);
+                    float *row = p.dphiq + (tok_base + t0 + 16 * ib + r) * DP;
+                    if (r < rem && 16 * fb + r16 < DP) row[lane_off] = o[r];
                 }
             }
         }
@@ -515,10 +524,12 @@ __device__ void bwd_k_body(const BwdParams &p, unsigned char *smem, int bh, int 
                     }
                 }
                 const float rf = sR[16 * fb + r16];
+                const uint32_t lane_off = (uint32_t)(4 * g * DP + 16 * fb + r16);
+                const int rem = valid - 16 * jb - 4 * g;
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const int jj = 16 * jb + 4 * g + r;
-                    if (jj < valid && 16 * fb + r16 < DP) p.dphik[(tok_base + t0 + jj) * DP + 16 * fb + r16] = o[r] + rf;
+                    float *row = p.dphik + (tok_base + t0 + 16 * jb + r) * DP;  // uniform row base
+                    if (r < rem && 16 * fb + r16 < DP) row[lane_off] = o[r] + rf;
                 }
             }
         }
