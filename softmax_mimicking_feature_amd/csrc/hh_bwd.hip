@@ -687,6 +687,17 @@ __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per
             const int nn = n0 + 16 * wv + r16;       // this lane's token
             const bool live = nn < p.N;
             const size_t tok = (size_t)bh * p.N + (live ? nn : 0);
+            const float *dp_ = dphi + tok * DP;
+            // dL/dphi of the token's directions (and, two-sided, their negations), requested before
+            // the products that recompute u, so that the loads overlap them
+            f32x4 dpa[K::LB], dpb[K::LB];
+#pragma unroll
+            for (int lb = 0; lb < K::LB; lb++) {
+                dpa[lb] = *reinterpret_cast<const f32x4 *>(dp_ + 16 * lb + 4 * g);
+                dpb[lb] = (MAP == HH_MAP_HEDGEHOG_ || MAP == HH_MAP_HEDGEHOG_SOFTMAX_)
+                              ? *reinterpret_cast<const f32x4 *>(dp_ + D + 16 * lb + 4 * g)
+                              : zero4();
+            }
             // u^T: A = W rows (directions), B = x^T (token r16)
             f32x4 u[K::LB];
 #pragma unroll
@@ -701,13 +712,11 @@ __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per
             }
             // dL/du for directions 16 lb + 4 g + r of token r16
             f32x4 du[K::LB];
-            const float *dp_ = dphi + tok * DP;
             if (MAP == HH_MAP_HEDGEHOG_ || MAP == HH_MAP_EXP_) {
 #pragma unroll
                 for (int lb = 0; lb < K::LB; lb++) {
-                    const f32x4 a = *reinterpret_cast<const f32x4 *>(dp_ + 16 * lb + 4 * g);
-                    f32x4 bneg = zero4();
-                    if (MAP == HH_MAP_HEDGEHOG_) bneg = *reinterpret_cast<const f32x4 *>(dp_ + D + 16 * lb + 4 * g);
+                    const f32x4 a = dpa[lb];
+                    const f32x4 bneg = dpb[lb];
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
                         const float uu = u[lb][r] + biasl[lb][r];
@@ -733,7 +742,7 @@ __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per
                     float sum = 0.0f, dot = 0.0f;
 #pragma unroll
                     for (int lb = 0; lb < K::LB; lb++) {
-                        dpv[lb] = *reinterpret_cast<const f32x4 *>(dp_ + half * D + 16 * lb + 4 * g);
+                        dpv[lb] = half ? dpb[lb] : dpa[lb];
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
                             e[lb][r] = __expf(sg * u[lb][r] - mx);
