@@ -94,13 +94,17 @@ __device__ __forceinline__ void store_piece(bf16_t *tile, int p, const bf16x8 &x
     *reinterpret_cast<bf16x8 *>(tile + row * pitch + col) = x;
 }
 
-// Stage one chunk (rows >= valid zero): phi(q), phi(k), v, dy.
-template <int D, int DP>
+// Stage one chunk (rows >= valid zero): phi(q), phi(k), v, dy, and with WITH_Y also y (into
+// the tile that holds G later).
+template <int D, int DP, bool WITH_Y = false>
 __device__ __forceinline__ void bwd_stage(const BwdParams &p, size_t tok0, int valid, unsigned char *smem, int tid) {
     using K = BwdCfg<D, DP>;
     bf16_t *sQ = reinterpret_cast<bf16_t *>(smem + K::OFF_Q), *sK = reinterpret_cast<bf16_t *>(smem + K::OFF_K);
     bf16_t *sV = reinterpret_cast<bf16_t *>(smem + K::OFF_V), *sDY = reinterpret_cast<bf16_t *>(smem + K::OFF_DY);
-    bf16x8 a[K::PQ], bq[K::PQ], c[K::PVV], e[K::PVV];
+    bf16x8 a[K::PQ], bq[K::PQ], c[K::PVV], e[K::PVV], yv[K::PVV];
+    // the piece offsets are recomputed per chunk from an opaque copy of the thread index: kept
+    // live across the chunk loop instead, they push the q-side kernel into spills
+    asm volatile("" : "+v"(tid));
 #pragma unroll
     for (int i = 0; i < K::PQ; i++) {
         a[i] = load_piece<DP>(p.phiq + tok0 * DP, tid + K::NT * i, valid);
@@ -110,6 +114,12 @@ __device__ __forceinline__ void bwd_stage(const BwdParams &p, size_t tok0, int v
     for (int i = 0; i < K::PVV; i++) {
         c[i] = load_piece<D>(p.v + tok0 * D, tid + K::NT * i, valid);
         e[i] = load_piece<D>(p.dy + tok0 * D, tid + K::NT * i, valid);
+        if (WITH_Y) yv[i] = load_piece<D>(p.y + tok0 * D, tid + K::NT * i, valid);
+    }
+    if (WITH_Y) {
+        bf16_t *sY = reinterpret_cast<bf16_t *>(smem + K::OFF_G);
+#pragma unroll
+        for (int i = 0; i < K::PVV; i++) store_piece<D, K::PV>(sY, tid + K::NT * i, yv[i]);
     }
 #pragma unroll
     for (int i = 0; i < K::PQ; i++) {
@@ -255,10 +265,16 @@ __device__ void bwd_q_body(const BwdParams &p, unsigned char *smem, int bh, int 
 
     const int lo = 4 * (r16 & 3), lr = 8 * g + (r16 >> 2);  // transposing-read lane offsets (column, row)
     const bf16x8 ones = ones_bf16x8();
+    // dy . y of query i is summed by the TPQ = D / 16 threads TPQ i .. TPQ i + TPQ - 1, each over
+    // 16 columns; y is staged with the chunk (in the G tile, free until G is formed), so that its
+    // loads share the chunk's one memory wait
+    constexpr int TPQ = K::NT / K::C;
+    static_assert(TPQ * K::C == K::NT && TPQ * 16 == D, "whole 16-column parts per thread");
+    const int yi = tid / TPQ, ypart = tid % TPQ;
     for (int c = 0; c < n; c++) {
         const int t0 = t_begin + K::C * c;
         const int valid = min(K::C, t_end - t0);
-        bwd_stage<D, DP>(p, tok_base + t0, valid, smem, tid);
+        bwd_stage<D, DP, true>(p, tok_base + t0, valid, smem, tid);
         __syncthreads();
         // ---- den: phi_q . z (partials per wave over its features) + intra row sums
         if (MODE == BW_CAUSAL) bwd_scores<D, DP, MODE>(sQ, sK, sP, sRS, w, g, r16);
@@ -290,8 +306,20 @@ __device__ void bwd_q_body(const BwdParams &p, unsigned char *smem, int bh, int 
         }
         __syncthreads();
         // ---- den, g = dy / den, c = -(dy . y) / den (queries past the end: 0)
-        if (tid < K::C) {
-            const int i = tid;
+        {
+            float dot = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const int col = 16 * ypart + 8 * j;
+                const bf16x8 yv = *reinterpret_cast<const bf16x8 *>(sG + yi * K::PV + col);
+                const bf16x8 dv = *reinterpret_cast<const bf16x8 *>(sDY + yi * K::PV + col);
+#pragma unroll
+                for (int e2 = 0; e2 < 8; e2++) dot = fmaf((float)dv[e2], (float)yv[e2], dot);
+            }
+#pragma unroll
+            for (int o = 1; o < TPQ; o <<= 1) dot += __shfl_xor(dot, o);
+            if (ypart == 0) {
+            const int i = yi;
             float den = 0.0f;
 #pragma unroll
             for (int pw = 0; pw < K::NW; pw++) den += sDen[pw * K::C + i];
@@ -300,21 +328,13 @@ __device__ void bwd_q_body(const BwdParams &p, unsigned char *smem, int bh, int 
                 for (int jb = 0; jb < 4; jb++) den += sRS[jb * K::C + i];
             }
             const bool live = i < valid;
-            float dot = 0.0f;
-            if (live) {
-                const bf16_t *yrow = p.y + (tok_base + t0 + i) * D;
-                for (int col = 0; col < D; col += 8) {
-                    const bf16x8 yv = *reinterpret_cast<const bf16x8 *>(yrow + col);
-#pragma unroll
-                    for (int e2 = 0; e2 < 8; e2++) dot = fmaf(bf16_bits_to_float(sDY[i * K::PV + col + e2]), (float)yv[e2], dot);
-                }
-            }
             const float rd = live ? 1.0f / den : 0.0f;
             sDn[i] = rd;
             sC[i] = live ? -dot * rd : 0.0f;
             if (live) {
                 p.den_c[2 * (tok_base + t0 + i)] = den;
                 p.den_c[2 * (tok_base + t0 + i) + 1] = -dot * rd;
+            }
             }
         }
         __syncthreads();
@@ -481,12 +501,14 @@ __device__ void bwd_k_body(const BwdParams &p, unsigned char *smem, int bh, int 
     for (int c = n - 1; c >= 0; c--) {
         const int t0 = t_begin + K::C * c;
         const int valid = min(K::C, t_end - t0);
+        // den and c of the chunk's queries, requested with the staging loads (one memory wait)
+        float2 dc = make_float2(1.0f, 0.0f);
+        const bool dc_live = tid < K::C && tid < valid;
+        if (dc_live) dc = *reinterpret_cast<const float2 *>(p.den_c + 2 * (tok_base + t0 + tid));
         bwd_stage<D, DP>(p, tok_base + t0, valid, smem, tid);
         if (tid < K::C) {
-            const int i = tid;
-            const bool live = i < valid;
-            sDn[i] = live ? 1.0f / p.den_c[2 * (tok_base + t0 + i)] : 0.0f;
-            sC[i] = live ? p.den_c[2 * (tok_base + t0 + i) + 1] : 0.0f;
+            sDn[tid] = dc_live ? 1.0f / dc.x : 0.0f;
+            sC[tid] = dc_live ? dc.y : 0.0f;
         }
         __syncthreads();
         for (int e2 = tid; e2 < K::C * D; e2 += K::NT) {
