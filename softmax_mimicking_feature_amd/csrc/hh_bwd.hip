@@ -211,6 +211,67 @@ __device__ __forceinline__ void bwd_mtile(const bf16_t *sG, const bf16_t *sV, co
     }
 }
 
+// The k side's tiles stored transposed, [key][query] (the operands swapped in the product), so
+// that its products read them as plain 16-byte rows: read down the rows of a 64-column tile
+// (128-byte rows) the transposing reads conflict in the LDS banks.  Scores without row sums.
+template <int D, int DP, int MODE>
+__device__ __forceinline__ void bwd_scores_t(const bf16_t *sQ, const bf16_t *sK, bf16_t *sPT, int w, int g, int r16) {
+    using K = BwdCfg<D, DP>;
+    const int nblk = MODE == BW_CAUSAL ? 10 : 16;
+    for (int t = w; t < nblk; t += K::NW) {
+        int ib, jb;
+        if (MODE == BW_CAUSAL) {
+            ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+            jb = t - ib * (ib + 1) / 2;
+        } else {
+            ib = t >> 2;
+            jb = t & 3;
+        }
+        // lane: key 16 jb + r16, queries 16 ib + 4 g + r; keep key <= query
+        f32x4 a = zero4();
+#pragma unroll
+        for (int ks = 0; ks < K::KSF; ks++)
+            a = mfma_bf16(*reinterpret_cast<const bf16x8 *>(sQ + (16 * ib + r16) * K::PF + 32 * ks + 8 * g),
+                          *reinterpret_cast<const bf16x8 *>(sK + (16 * jb + r16) * K::PF + 32 * ks + 8 * g), a);
+        if (MODE == BW_CAUSAL && jb == ib) {
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                if (4 * g + r < r16) a[r] = 0.0f;
+        }
+        store4(sPT + (16 * jb + r16) * K::PM + 16 * ib + 4 * g, to_bf16x4(a));
+    }
+}
+
+template <int D, int DP, int MODE>
+__device__ __forceinline__ void bwd_mtile_t(const bf16_t *sG, const bf16_t *sV, const float *sC, bf16_t *sMT, int w,
+                                            int g, int r16) {
+    using K = BwdCfg<D, DP>;
+    const int nblk = MODE == BW_CAUSAL ? 10 : 16;
+    for (int t = w; t < nblk; t += K::NW) {
+        int ib, jb;
+        if (MODE == BW_CAUSAL) {
+            ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+            jb = t - ib * (ib + 1) / 2;
+        } else {
+            ib = t >> 2;
+            jb = t & 3;
+        }
+        // lane: key 16 jb + r16, queries 16 ib + 4 g + r
+        f32x4 a = zero4();
+#pragma unroll
+        for (int ks = 0; ks < K::KSV; ks++)
+            a = mfma_bf16(*reinterpret_cast<const bf16x8 *>(sG + (16 * ib + r16) * K::PV + 32 * ks + 8 * g),
+                          *reinterpret_cast<const bf16x8 *>(sV + (16 * jb + r16) * K::PV + 32 * ks + 8 * g), a);
+        const f32x4 cq = *reinterpret_cast<const f32x4 *>(sC + 16 * ib + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            a[r] += cq[r];
+            if (MODE == BW_CAUSAL && jb == ib && 4 * g + r < r16) a[r] = 0.0f;
+        }
+        store4(sMT + (16 * jb + r16) * K::PM + 16 * ib + 4 * g, to_bf16x4(a));
+    }
+}
+
 // ---- q side -----------------------------------------------------------------------------
 template <int D, int DP, int MODE>
 __device__ void bwd_q_body(const BwdParams &p, unsigned char *smem, int bh, int s) {
@@ -515,9 +576,9 @@ __device__ void bwd_k_body(const BwdParams &p, unsigned char *smem, int bh, int 
             const int i = e2 / D, col = e2 % D;
             sG[i * K::PV + col] = float_to_bf16_bits(bf16_bits_to_float(sDY[i * K::PV + col]) * sDn[i]);
         }
-        if (MODE == BW_CAUSAL) bwd_scores<D, DP, MODE>(sQ, sK, sP, sRS, w, g, r16);
+        if (MODE == BW_CAUSAL) bwd_scores_t<D, DP, MODE>(sQ, sK, sP, w, g, r16);
         __syncthreads();
-        if (MODE == BW_CAUSAL) bwd_mtile<D, DP, MODE>(sG, sV, sC, sM, w, g, r16);
+        if (MODE == BW_CAUSAL) bwd_mtile_t<D, DP, MODE>(sG, sV, sC, sM, w, g, r16);
         __syncthreads();
         // ---- dphiK for this wave's features: V R^T + r (+ M^T phiQ within the chunk, causal)
         bf16x8 rop[K::KSV][K::FBW];
@@ -541,7 +602,7 @@ __device__ void bwd_k_body(const BwdParams &p, unsigned char *smem, int bh, int 
 #pragma unroll
                     for (int ks = 0; ks < 2; ks++) {
                         if (ks < jb / 2) continue;
-                        o = mfma_bf16(down_rows(sM, lr * K::PM + lo, 32 * ks, 16 * jb, K::PM),
+                        o = mfma_bf16(*reinterpret_cast<const bf16x8 *>(sM + (16 * jb + r16) * K::PM + 32 * ks + 8 * g),
                                       down_rows(sQ, lr * K::PF + lo, 32 * ks, 16 * fb, K::PF), o);
                     }
                 }
@@ -571,7 +632,7 @@ __device__ void bwd_k_body(const BwdParams &p, unsigned char *smem, int bh, int 
                     for (int ks = 0; ks < 2; ks++) {
                         if (ks < jb / 2) continue;
                         o = mfma_bf16(down_rows(sG, lr * K::PV + lo, 32 * ks, 16 * w, K::PV),
-                                      down_rows(sP, lr * K::PM + lo, 32 * ks, 16 * jb, K::PM), o);
+                                      *reinterpret_cast<const bf16x8 *>(sP + (16 * jb + r16) * K::PM + 32 * ks + 8 * g), o);
                     }
                 }
                 const int jj = 16 * jb + r16;
