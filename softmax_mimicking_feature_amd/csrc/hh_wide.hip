@@ -1651,6 +1651,10 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
             for (int j = 0; j < 2; j++) ao2[j] = load8(sPK + (32 * ks + 16 * j + r16) * S::PT + 8 * g);
         };
         load_step(0, qn, an);
+        // the read-out and update products at raised wave priority: when both waves of a SIMD
+        // have an instruction ready, the consumer's products go first (the producer's vector
+        // work fills the matrix pipe's busy cycles)
+        __builtin_amdgcn_s_setprio(2);
         __builtin_amdgcn_sched_barrier(0);
         f32x4 nt[2][2];
 #pragma unroll
@@ -1703,6 +1707,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
             numT[ib][0] = nt[ib][0];
             numT[ib][1] = nt[ib][1];
         }
+        __builtin_amdgcn_s_setprio(0);
         f32x4 dacc[2] = {zero4(), zero4()};
         {
             const bf16_t *sPQz = sPQ + 64 * pv;  // K steps 2 pv, 2 pv + 1
