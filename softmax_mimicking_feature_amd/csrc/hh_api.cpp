@@ -198,7 +198,7 @@ BwdPlan make_bwd_plan(int map, long BH, long N, int d) {
     f.seg_len = (int)(seg_chunks * C);
     f.wgs = hh::bwd_wgs_per_seq((int)N);
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t phi = up((size_t)BH * N * f.dp * 2), dphi = up((size_t)BH * N * f.dp * 4);
+    const size_t phi = up((size_t)BH * N * f.dp * 2), dphi = phi;
     const size_t slotS = up((size_t)BH * nseg * f.dpp * d * 4), slotz = up((size_t)BH * nseg * f.dpp * 4);
     f.off_phik = phi;
     f.off_dphiq = 2 * phi;
@@ -612,7 +612,7 @@ hh_status_t hh_linattn_bwd(int map, int dtype, int causal, int B, int H, int N, 
     bp.phiq = phiq; bp.phik = phik; bp.v = (const hh::bf16_t *)v; bp.y = (const hh::bf16_t *)y;
     bp.dy = (const hh::bf16_t *)dy; bp.q = (const hh::bf16_t *)q; bp.k = (const hh::bf16_t *)k;
     bp.W = (const hh::bf16_t *)W; bp.b = map_has_b(map) ? (const hh::bf16_t *)b : nullptr;
-    bp.dphiq = reinterpret_cast<float *>(ws + pl.off_dphiq); bp.dphik = reinterpret_cast<float *>(ws + pl.off_dphik);
+    bp.dphiq = reinterpret_cast<hh::bf16_t *>(ws + pl.off_dphiq); bp.dphik = reinterpret_cast<hh::bf16_t *>(ws + pl.off_dphik);
     bp.den_c = reinterpret_cast<float *>(ws + pl.off_denc);
     bp.S_slots = Ssl; bp.z_slots = zsl; bp.R_slots = Rsl; bp.r_slots = rsl;
     bp.dq = (hh::bf16_t *)dq; bp.dk = (hh::bf16_t *)dk; bp.dv = (hh::bf16_t *)dv;

@@ -14,9 +14,9 @@
 //     dphiQ_c = G_c S^T + c_c z^T + M_c phiK_c                    (chunks in order)
 //     dphiK_c = V_c R^T + 1 r^T + M_c^T phiQ_c,   dV_c = phiK_c R + P_c^T G_c   (chunks in reverse)
 // The same regrouping as the forward's chunks (only rounding differs).  Kernels:
-//   bwd_q_kernel   per segment, chunks in order: den and c per token, dphiQ (fp32), and the
+//   bwd_q_kernel   per segment, chunks in order: den and c per token, dphiQ (bf16), and the
 //                  segment's reverse-sum aggregate (R, r) for the k side;
-//   bwd_k_kernel   per segment, chunks in reverse: dphiK (fp32) and dV;
+//   bwd_k_kernel   per segment, chunks in reverse: dphiK (bf16) and dV;
 //   bwd_map_kernel per 64 tokens: u recomputed, dL/du from dL/dphi, dx = W^T du, and this
 //                  workgroup's part of dW = sum du x^T and db = sum du;
 //   bwd_reduce_kernel: the parts of dW and db summed per head.
@@ -442,8 +442,8 @@ __device__ void bwd_q_body(const BwdParams &p, unsigned char *smem, int bh, int 
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     o[r] = fmaf(cq[r], zf, o[r]);
-                    float *row = p.dphiq + (tok_base + t0 + 16 * ib + r) * DP;
-                    if (r < rem && 16 * fb + r16 < DP) row[lane_off] = o[r];
+                    bf16_t *row = p.dphiq + (tok_base + t0 + 16 * ib + r) * DP;
+                    if (r < rem && 16 * fb + r16 < DP) row[lane_off] = float_to_bf16_bits(o[r]);
                 }
             }
         }
@@ -611,8 +611,8 @@ __device__ void bwd_k_body(const BwdParams &p, unsigned char *smem, int bh, int 
                 const int rem = valid - 16 * jb - 4 * g;
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    float *row = p.dphik + (tok_base + t0 + 16 * jb + r) * DP;  // uniform row base
-                    if (r < rem && 16 * fb + r16 < DP) row[lane_off] = o[r] + rf;
+                    bf16_t *row = p.dphik + (tok_base + t0 + 16 * jb + r) * DP;  // uniform row base
+                    if (r < rem && 16 * fb + r16 < DP) row[lane_off] = float_to_bf16_bits(o[r] + rf);
                 }
             }
         }
@@ -755,7 +755,7 @@ __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per
 
     for (int src = 0; src < 2; src++) {
         const bf16_t *x = src == 0 ? p.q : p.k;
-        const float *dphi = src == 0 ? p.dphiq : p.dphik;
+        const bf16_t *dphi = src == 0 ? p.dphiq : p.dphik;
         bf16_t *dx = src == 0 ? p.dq : p.dk;
         for (int tl = 0; tl < kMapTiles; tl++) {
             const int tile = part * kMapTiles + tl;
@@ -770,16 +770,15 @@ __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per
             const int nn = n0 + 16 * wv + r16;       // this lane's token
             const bool live = nn < p.N;
             const size_t tok = (size_t)bh * p.N + (live ? nn : 0);
-            const float *dp_ = dphi + tok * DP;
+            const bf16_t *dp_ = dphi + tok * DP;
             // dL/dphi of the token's directions (and, two-sided, their negations), requested before
             // the products that recompute u, so that the loads overlap them
-            f32x4 dpa[K::LB], dpb[K::LB];
+            bf16x4 dpa16[K::LB], dpb16[K::LB];
 #pragma unroll
             for (int lb = 0; lb < K::LB; lb++) {
-                dpa[lb] = *reinterpret_cast<const f32x4 *>(dp_ + 16 * lb + 4 * g);
-                dpb[lb] = (MAP == HH_MAP_HEDGEHOG_ || MAP == HH_MAP_HEDGEHOG_SOFTMAX_)
-                              ? *reinterpret_cast<const f32x4 *>(dp_ + D + 16 * lb + 4 * g)
-                              : zero4();
+                dpa16[lb] = load4(dp_ + 16 * lb + 4 * g);
+                dpb16[lb] = (MAP == HH_MAP_HEDGEHOG_ || MAP == HH_MAP_HEDGEHOG_SOFTMAX_) ? load4(dp_ + D + 16 * lb + 4 * g)
+                                                                                    : to_bf16x4(zero4());
             }
             // u^T: A = W rows (directions), B = x^T (token r16)
             f32x4 u[K::LB];
@@ -793,6 +792,14 @@ __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per
                     u[lb] = mfma_bf16(wa, *reinterpret_cast<const bf16x8 *>(sX + (16 * wv + r16) * K::PX + 32 * ks + 8 * g), u[lb]);
                 }
             }
+            f32x4 dpa[K::LB], dpb[K::LB];
+#pragma unroll
+            for (int lb = 0; lb < K::LB; lb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    dpa[lb][r] = (float)dpa16[lb][r];
+                    dpb[lb][r] = (float)dpb16[lb][r];
+                }
             // dL/du for directions 16 lb + 4 g + r of token r16
             f32x4 du[K::LB];
             if (MAP == HH_MAP_HEDGEHOG_ || MAP == HH_MAP_EXP_) {

@@ -133,12 +133,13 @@ hipError_t launch_featuremap_variant(int map, int dtype, int d, const void *x, c
                                      long BH, int H, int N, hipStream_t st);
 
 // Backward of the forward over given features (hh_bwd.hip).  Per sequence bh: phi(q), phi(k)
-// [N][d'] bf16; v, y, dy [N][d] bf16; dphi(q), dphi(k) [N][d'] fp32 and den, c [N][2] fp32 written
+// [N][d'] bf16; v, y, dy [N][d] bf16; dphi(q), dphi(k) [N][d'] bf16 and den, c [N][2] fp32 written
 // by the q-side pass; forward sums S, z and reverse sums R, r per segment in canonical fp32 slots
 // ([nseg][dpp][d], [nseg][dpp]).
 struct BwdParams {
     const bf16_t *phiq, *phik, *v, *y, *dy, *q, *k, *W, *b;
-    float *dphiq, *dphik, *den_c;
+    bf16_t *dphiq, *dphik;
+    float *den_c;
     const float *S_slots, *z_slots;
     float *R_slots, *r_slots;
     bf16_t *dq, *dk, *dv;
