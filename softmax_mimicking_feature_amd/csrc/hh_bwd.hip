@@ -707,14 +707,18 @@ struct MapCfg {
     static constexpr int OFF_W = 0;                        // W [l][m], pitch PW, DK rows (rows >= D zero)
     static constexpr int OFF_X = OFF_W + DK * PW * 2;      // x tile [64][PX]
     static constexpr int OFF_U = OFF_X + 64 * PX * 2;      // du tile [64][PX] (bf16)
-    static constexpr int LDS_BYTES = OFF_U + 64 * PX * 2;
+    static constexpr int OFF_B = OFF_U + 64 * PX * 2;      // bias [D] (fp32)
+    static constexpr int LDS_BYTES = OFF_B + D * 4;
+    static constexpr int NX = 64 * D / 8;                  // 16-byte pieces of an x tile
+    static constexpr int PERX = (NX + 255) / 256;          // per thread
 };
 
 template <int D, int MAP>
 __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per_seq, int wgs_per_seq) {
     using K = MapCfg<D>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[K::LDS_BYTES];
-    constexpr int DP = MAP == HH_MAP_HEDGEHOG_ || MAP == HH_MAP_HEDGEHOG_SOFTMAX_ ? 2 * D : D;
+    constexpr bool TWO = MAP == HH_MAP_HEDGEHOG_ || MAP == HH_MAP_HEDGEHOG_SOFTMAX_;  // two-sided maps
+    constexpr int DP = TWO ? 2 * D : D;
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const long bh = blockIdx.x / wgs_per_seq;
     const int part = blockIdx.x % wgs_per_seq;
@@ -723,15 +727,17 @@ __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per
     bf16_t *sW = reinterpret_cast<bf16_t *>(smem + K::OFF_W);
     bf16_t *sX = reinterpret_cast<bf16_t *>(smem + K::OFF_X);
     bf16_t *sU = reinterpret_cast<bf16_t *>(smem + K::OFF_U);
-    for (int i = tid; i < K::LDS_BYTES / 16; i += 256) reinterpret_cast<f32x4 *>(smem)[i] = zero4();
+    float *sB = reinterpret_cast<float *>(smem + K::OFF_B);
+    for (int i = tid; i < K::OFF_B / 16; i += 256) reinterpret_cast<f32x4 *>(smem)[i] = zero4();
+    if (tid < D) sB[tid] = p.b ? bf16_bits_to_float(p.b[(size_t)h * D + tid]) : 0.0f;
     __syncthreads();
     stage_pieces<256, D * D / 8>(
         tid, [&](int e) { return Wh + 8 * e; }, [&](int e) { return sW + (e / (D / 8)) * K::PW + 8 * (e % (D / 8)); },
         [](int) { return true; });
-    __syncthreads();
     // dW part: blocks (lb, mb) dealt over the 4 waves; db part: the ones trick
     constexpr int NBLK = (D / 16) * (D / 16);
     constexpr int BPW = (NBLK + 3) / 4;
+    constexpr int NMB = K::LB >= 8 ? 2 : 1;  // input-dim blocks of a wave's dW blocks: mb = (wv + 4 i) % LB
     f32x4 dWacc[BPW];
 #pragma unroll
     for (int i = 0; i < BPW; i++) dWacc[i] = zero4();
@@ -739,165 +745,183 @@ __global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per
     const bf16x8 ones = ones_bf16x8();
     const int lr = 8 * g + (r16 >> 2), lo = 4 * (r16 & 3);
     const int lrp = 4 * g + (r16 >> 2);
-    // bias of directions 16 lb + 4 g + r, loaded once behind one test of the pointer (a test per
-    // element would wait for each load before issuing the next)
-    float biasl[K::LB][4];
-#pragma unroll
-    for (int lb = 0; lb < K::LB; lb++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) biasl[lb][r] = 0.0f;
-    if (p.b) {
-#pragma unroll
-        for (int lb = 0; lb < K::LB; lb++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) biasl[lb][r] = bf16_bits_to_float(p.b[(size_t)h * D + 16 * lb + 4 * g + r]);
-    }
 
-    for (int src = 0; src < 2; src++) {
-        const bf16_t *x = src == 0 ? p.q : p.k;
-        const bf16_t *dphi = src == 0 ? p.dphiq : p.dphik;
-        bf16_t *dx = src == 0 ? p.dq : p.dk;
-        for (int tl = 0; tl < kMapTiles; tl++) {
-            const int tile = part * kMapTiles + tl;
-            if (tile >= tiles_per_seq) break;
-            const int n0 = tile * 64;
-            // x tile (rows past the end zero)
-            stage_pieces<256, 64 * D / 8>(
-                tid, [&](int e) { return x + ((size_t)bh * p.N + n0 + e / (D / 8)) * D + 8 * (e % (D / 8)); },
-                [&](int e) { return sX + (e / (D / 8)) * K::PX + 8 * (e % (D / 8)); },
-                [&](int e) { return n0 + e / (D / 8) < p.N; });
-            __syncthreads();
-            const int nn = n0 + 16 * wv + r16;       // this lane's token
-            const bool live = nn < p.N;
-            const size_t tok = (size_t)bh * p.N + (live ? nn : 0);
-            const bf16_t *dp_ = dphi + tok * DP;
-            // dL/dphi of the token's directions (and, two-sided, their negations), requested before
-            // the products that recompute u, so that the loads overlap them
-            bf16x4 dpa16[K::LB], dpb16[K::LB];
+    // Tiles of this workgroup: the same ntl tiles of q, then of k.  Tile j's x and dL/dphi are
+    // requested as soon as tile j - 1 has formed du, so that they arrive during its dx and dW
+    // products (requested any earlier, the wait for tile j - 1's dL/dphi would also wait for
+    // them: loads retire in order).  Rows past the end are loaded from a stand-in row and zeroed
+    // when stored (a select right after a load would wait for it).
+    const int ntl = min(kMapTiles, tiles_per_seq - part * kMapTiles);
+    const int nit = 2 * ntl;
+    bf16x8 xbuf[K::PERX];
+    auto x_src = [&](int j) { return j < ntl ? p.q : p.k; };
+    auto n0_of = [&](int j) { return (part * kMapTiles + (j < ntl ? j : j - ntl)) * 64; };
+    auto load_x = [&](int j) {
+        const bf16_t *x = x_src(j);
+        const int n0 = n0_of(j);
 #pragma unroll
-            for (int lb = 0; lb < K::LB; lb++) {
-                dpa16[lb] = load4(dp_ + 16 * lb + 4 * g);
-                dpb16[lb] = (MAP == HH_MAP_HEDGEHOG_ || MAP == HH_MAP_HEDGEHOG_SOFTMAX_) ? load4(dp_ + D + 16 * lb + 4 * g)
-                                                                                    : to_bf16x4(zero4());
+        for (int i = 0; i < K::PERX; i++) {
+            const int e = tid + 256 * i;
+            const bool ok = (K::NX % 256 == 0 || e < K::NX) && n0 + e / (D / 8) < p.N;
+            const int row = ok ? n0 + e / (D / 8) : 0;  // a stand-in row where there is none
+            xbuf[i] = load8(x + ((size_t)bh * p.N + row) * D + 8 * (e % (D / 8)));
+        }
+    };
+    auto store_x = [&](int j) {
+        const int n0 = n0_of(j);
+#pragma unroll
+        for (int i = 0; i < K::PERX; i++) {
+            const int e = tid + 256 * i;
+            if (K::NX % 256 == 0 || e < K::NX)
+                store8(sX + (e / (D / 8)) * K::PX + 8 * (e % (D / 8)), n0 + e / (D / 8) < p.N ? xbuf[i] : zero_bf16x8());
+        }
+    };
+    // dL/dphi of the lane's token (its directions, and for two-sided maps their negations)
+    auto load_dphi = [&](int j, bf16x4 (&da)[K::LB], bf16x4 (&db_)[K::LB]) {
+        const int nn = n0_of(j) + 16 * wv + r16;
+        const size_t tok = (size_t)bh * p.N + (nn < p.N ? nn : 0);
+        const bf16_t *dp_ = (j < ntl ? p.dphiq : p.dphik) + tok * DP;
+#pragma unroll
+        for (int lb = 0; lb < K::LB; lb++) {
+            da[lb] = load4(dp_ + 16 * lb + 4 * g);
+            db_[lb] = TWO ? load4(dp_ + D + 16 * lb + 4 * g) : to_bf16x4(zero4());
+        }
+    };
+
+    bf16x4 dpa16[K::LB], dpb16[K::LB];
+    auto tile = [&](int j) {
+        store_x(j);
+        __syncthreads();
+        const int n0 = n0_of(j);
+        const int nn = n0 + 16 * wv + r16;  // this lane's token
+        const bool live = nn < p.N;
+        const size_t tok = (size_t)bh * p.N + (live ? nn : 0);
+        bf16_t *dx = j < ntl ? p.dq : p.dk;
+        // u^T: A = W rows (directions), B = x^T (token r16)
+        f32x4 u[K::LB];
+#pragma unroll
+        for (int lb = 0; lb < K::LB; lb++) {
+            u[lb] = *reinterpret_cast<const f32x4 *>(sB + 16 * lb + 4 * g);  // the bias
+#pragma unroll
+            for (int ks = 0; ks < K::KS; ks++) {
+                const bf16x8 wa = (32 * ks + 8 * g < D) ? *reinterpret_cast<const bf16x8 *>(sW + (16 * lb + r16) * K::PW + 32 * ks + 8 * g)
+                                                        : zero_bf16x8();
+                u[lb] = mfma_bf16(wa, *reinterpret_cast<const bf16x8 *>(sX + (16 * wv + r16) * K::PX + 32 * ks + 8 * g), u[lb]);
             }
-            // u^T: A = W rows (directions), B = x^T (token r16)
-            f32x4 u[K::LB];
-#pragma unroll
-            for (int lb = 0; lb < K::LB; lb++) {
-                u[lb] = zero4();
-#pragma unroll
-                for (int ks = 0; ks < K::KS; ks++) {
-                    const bf16x8 wa = (32 * ks + 8 * g < D) ? *reinterpret_cast<const bf16x8 *>(sW + (16 * lb + r16) * K::PW + 32 * ks + 8 * g)
-                                                            : zero_bf16x8();
-                    u[lb] = mfma_bf16(wa, *reinterpret_cast<const bf16x8 *>(sX + (16 * wv + r16) * K::PX + 32 * ks + 8 * g), u[lb]);
-                }
-            }
-            f32x4 dpa[K::LB], dpb[K::LB];
+        }
+        // dL/du for directions 16 lb + 4 g + r of token r16
+        f32x4 du[K::LB];
+        if (MAP == HH_MAP_HEDGEHOG_ || MAP == HH_MAP_EXP_) {
 #pragma unroll
             for (int lb = 0; lb < K::LB; lb++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    dpa[lb][r] = (float)dpa16[lb][r];
-                    dpb[lb][r] = (float)dpb16[lb][r];
+                    const float uu = u[lb][r];
+                    float v = (float)dpa16[lb][r] * __expf(uu);
+                    if (MAP == HH_MAP_HEDGEHOG_) v -= (float)dpb16[lb][r] * __expf(-uu);
+                    du[lb][r] = v;
                 }
-            // dL/du for directions 16 lb + 4 g + r of token r16
-            f32x4 du[K::LB];
-            if (MAP == HH_MAP_HEDGEHOG_ || MAP == HH_MAP_EXP_) {
+        } else {
+#pragma unroll
+            for (int lb = 0; lb < K::LB; lb++) du[lb] = zero4();
+#pragma unroll
+            for (int half = 0; half < (MAP == HH_MAP_HEDGEHOG_SOFTMAX_ ? 2 : 1); half++) {
+                const float sg = half ? -1.0f : 1.0f;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int lb = 0; lb < K::LB; lb++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) mx = fmaxf(mx, sg * u[lb][r]);
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                f32x4 e[K::LB], dpv[K::LB];
+                float sum = 0.0f, dot = 0.0f;
 #pragma unroll
                 for (int lb = 0; lb < K::LB; lb++) {
-                    const f32x4 a = dpa[lb];
-                    const f32x4 bneg = dpb[lb];
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
-                        const float uu = u[lb][r] + biasl[lb][r];
-                        float v = a[r] * __expf(uu);
-                        if (MAP == HH_MAP_HEDGEHOG_) v -= bneg[r] * __expf(-uu);
-                        du[lb][r] = v;
+                        dpv[lb][r] = (float)(half ? dpb16[lb][r] : dpa16[lb][r]);
+                        e[lb][r] = __expf(sg * u[lb][r] - mx);
+                        sum += e[lb][r];
                     }
                 }
-            } else {
+                sum += __shfl_xor(sum, 16);
+                sum += __shfl_xor(sum, 32);
+                const float rs = 1.0f / sum;
 #pragma unroll
-                for (int lb = 0; lb < K::LB; lb++) du[lb] = zero4();
+                for (int lb = 0; lb < K::LB; lb++)
 #pragma unroll
-                for (int half = 0; half < (MAP == HH_MAP_HEDGEHOG_SOFTMAX_ ? 2 : 1); half++) {
-                    const float sg = half ? -1.0f : 1.0f;
-                    float mx = -INFINITY;
+                    for (int r = 0; r < 4; r++) dot = fmaf(dpv[lb][r], e[lb][r] * rs, dot);
+                dot += __shfl_xor(dot, 16);
+                dot += __shfl_xor(dot, 32);
 #pragma unroll
-                    for (int lb = 0; lb < K::LB; lb++)
+                for (int lb = 0; lb < K::LB; lb++)
 #pragma unroll
-                        for (int r = 0; r < 4; r++) mx = fmaxf(mx, sg * u[lb][r]);
-                    mx = fmaxf(mx, __shfl_xor(mx, 16));
-                    mx = fmaxf(mx, __shfl_xor(mx, 32));
-                    f32x4 e[K::LB], dpv[K::LB];
-                    float sum = 0.0f, dot = 0.0f;
-#pragma unroll
-                    for (int lb = 0; lb < K::LB; lb++) {
-                        dpv[lb] = half ? dpb[lb] : dpa[lb];
-#pragma unroll
-                        for (int r = 0; r < 4; r++) {
-                            e[lb][r] = __expf(sg * u[lb][r] - mx);
-                            sum += e[lb][r];
-                        }
-                    }
-                    sum += __shfl_xor(sum, 16);
-                    sum += __shfl_xor(sum, 32);
-                    const float rs = 1.0f / sum;
-#pragma unroll
-                    for (int lb = 0; lb < K::LB; lb++)
-#pragma unroll
-                        for (int r = 0; r < 4; r++) dot = fmaf(dpv[lb][r], e[lb][r] * rs, dot);
-                    dot += __shfl_xor(dot, 16);
-                    dot += __shfl_xor(dot, 32);
-#pragma unroll
-                    for (int lb = 0; lb < K::LB; lb++)
-#pragma unroll
-                        for (int r = 0; r < 4; r++) du[lb][r] += sg * e[lb][r] * rs * (dpv[lb][r] - dot);
-                }
+                    for (int r = 0; r < 4; r++) du[lb][r] += sg * e[lb][r] * rs * (dpv[lb][r] - dot);
             }
-            if (!live) {
-#pragma unroll
-                for (int lb = 0; lb < K::LB; lb++) du[lb] = zero4();
-            }
-            // du tile [token][direction] (bf16) for the dW part
-#pragma unroll
-            for (int lb = 0; lb < K::LB; lb++) store4(sU + (16 * wv + r16) * K::PX + 16 * lb + 4 * g, to_bf16x4(du[lb]));
-            // dx^T = W^T du: rows input dims, column token; A = W^T (rows m, K directions in the
-            // accumulator pair order), B = du pair
-#pragma unroll
-            for (int mb = 0; mb < D / 16; mb++) {
-                f32x4 o = zero4();
-#pragma unroll
-                for (int ks = 0; ks < K::KS; ks++) {
-                    const bf16x8 bop = (2 * ks + 1 < K::LB) ? acc_pair_to_operand(du[2 * ks], du[2 * ks + 1])
-                                                            : acc_pair_to_operand(du[2 * ks], zero4());
-                    o = mfma_bf16(down_rows_perm(sW, lrp * K::PW + lo, 32 * ks, 16 * mb, K::PW), bop, o);
-                }
-                if (live) store4(dx + tok * D + 16 * mb + 4 * g, to_bf16x4(o));
-            }
-            __syncthreads();
-            // dW part += du^T x over the tile's tokens: A = du^T (rows directions, K tokens),
-            // B = x (K tokens, column input dim); db part += du^T 1
-#pragma unroll
-            for (int i = 0; i < BPW; i++) {
-                const int blk = wv + 4 * i;
-                if (blk >= NBLK) continue;
-                const int lb = blk / (D / 16), mb = blk % (D / 16);
-#pragma unroll
-                for (int ks = 0; ks < 2; ks++)
-                    dWacc[i] = mfma_bf16(down_rows(sU, lr * K::PX + lo, 32 * ks, 16 * lb, K::PX),
-                                         down_rows(sX, lr * K::PX + lo, 32 * ks, 16 * mb, K::PX), dWacc[i]);
-            }
-#pragma unroll
-            for (int hb = 0; hb < 2; hb++) {
-                const int lb = wv + 4 * hb;
-                if (lb >= K::LB) continue;
-#pragma unroll
-                for (int ks = 0; ks < 2; ks++)
-                    dbacc[hb] = mfma_bf16(down_rows(sU, lr * K::PX + lo, 32 * ks, 16 * lb, K::PX), ones, dbacc[hb]);
-            }
-            __syncthreads();
         }
+        if (!live) {
+#pragma unroll
+            for (int lb = 0; lb < K::LB; lb++) du[lb] = zero4();
+        }
+        if (j + 1 < nit) {
+            load_x(j + 1);
+            load_dphi(j + 1, dpa16, dpb16);
+        }
+        // du tile [token][direction] (bf16) for the dW part
+#pragma unroll
+        for (int lb = 0; lb < K::LB; lb++) store4(sU + (16 * wv + r16) * K::PX + 16 * lb + 4 * g, to_bf16x4(du[lb]));
+        // dx^T = W^T du: rows input dims, column token; A = W^T (rows m, K directions in the
+        // accumulator pair order), B = du pair
+#pragma unroll
+        for (int mb = 0; mb < D / 16; mb++) {
+            f32x4 o = zero4();
+#pragma unroll
+            for (int ks = 0; ks < K::KS; ks++) {
+                const bf16x8 bop = (2 * ks + 1 < K::LB) ? acc_pair_to_operand(du[2 * ks], du[2 * ks + 1])
+                                                        : acc_pair_to_operand(du[2 * ks], zero4());
+                o = mfma_bf16(down_rows_perm(sW, lrp * K::PW + lo, 32 * ks, 16 * mb, K::PW), bop, o);
+            }
+            if (live) store4(dx + tok * D + 16 * mb + 4 * g, to_bf16x4(o));
+        }
+        __syncthreads();
+        // dW part += du^T x over the tile's tokens: A = du^T (rows directions, K tokens),
+        // B = x (K tokens, column input dim); db part += du^T 1.  Each operand read once.
+        bf16x8 xop[NMB][2];
+#pragma unroll
+        for (int m = 0; m < NMB; m++)
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) xop[m][ks] = down_rows(sX, lr * K::PX + lo, 32 * ks, 16 * ((wv + 4 * m) % K::LB), K::PX);
+        bf16x8 uop[2];
+#pragma unroll
+        for (int i = 0; i < BPW; i++) {
+            const int blk = wv + 4 * i;
+            if (blk >= NBLK) continue;
+            const int lb = blk / K::LB;
+            if (i % NMB == 0) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++) uop[ks] = down_rows(sU, lr * K::PX + lo, 32 * ks, 16 * lb, K::PX);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) dWacc[i] = mfma_bf16(uop[ks], xop[i % NMB][ks], dWacc[i]);
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; hb++) {
+            const int lb = wv + 4 * hb;
+            if (lb >= K::LB) continue;
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+                dbacc[hb] = mfma_bf16(down_rows(sU, lr * K::PX + lo, 32 * ks, 16 * lb, K::PX), ones, dbacc[hb]);
+        }
+        __syncthreads();
+    };
+
+    if (nit > 0) {
+        load_x(0);
+        load_dphi(0, dpa16, dpb16);
     }
+    __syncthreads();  // W staged
+    for (int j = 0; j < nit; j++) tile(j);
     // this workgroup's parts: dW [D][D] rows directions 16 lb + 4 g + r, column input dim 16 mb + r16
     float *dWp = p.dW_parts + (size_t)blockIdx.x * (D * D + D);
 #pragma unroll
