@@ -106,12 +106,28 @@ __device__ __forceinline__ void feat_fetch(FeatPrefetch<D, DP, MODE> &pf, const 
     for (int i = 0; i < K::PVV; i++) pf.v[i] = load_piece<D>(p.v + tok0 * D, tid + K::NT * i, valid);
 }
 
+// phi(q) is kept in LDS with each 32-feature group reordered so that the 4-feature runs g and
+// g + 4 sit side by side at 8 g: the K order of an accumulator pair (features 4 g .. 4 g + 3 and
+// 16 + 4 g .. 16 + 4 g + 3 of a K step) is then one 16-byte read.  Run r of a group goes to
+// position 8 r (r < 4) or 8 (r - 4) + 4.
+__device__ __forceinline__ int qperm_pos(int col) {
+    const int r = (col & 31) >> 2;
+    return (col & ~31) + (r < 4 ? 8 * r : 8 * (r - 4) + 4) + (col & 3);
+}
+template <int n, int pitch>
+__device__ __forceinline__ void store_piece_qperm(bf16_t *tile, int p, const bf16x8 &x) {
+    const int row = p / (n / 8), col = 8 * (p % (n / 8));
+    bf16_t *rp = tile + row * pitch;
+    store4(rp + qperm_pos(col), __builtin_shufflevector(x, x, 0, 1, 2, 3));
+    store4(rp + qperm_pos(col + 4), __builtin_shufflevector(x, x, 4, 5, 6, 7));
+}
+
 template <int D, int DP, int MODE>
 __device__ __forceinline__ void feat_commit(const FeatPrefetch<D, DP, MODE> &pf, unsigned char *smem, int tid) {
     using K = FeatCfg<D, DP, MODE>;
 #pragma unroll
     for (int i = 0; i < K::PQ; i++)
-        store_piece<DP, K::PF>(reinterpret_cast<bf16_t *>(smem + K::OFF_Q), tid + K::NT * i, pf.q[i]);
+        store_piece_qperm<DP, K::PF>(reinterpret_cast<bf16_t *>(smem + K::OFF_Q), tid + K::NT * i, pf.q[i]);
 #pragma unroll
     for (int i = 0; i < K::PK; i++)
         store_piece<DP, K::PF>(reinterpret_cast<bf16_t *>(smem + K::OFF_K), tid + K::NT * i, pf.k[i]);
@@ -234,7 +250,9 @@ __device__ void feat_body(const FeatParams &p, unsigned char *smem, int bh, int 
                     f32x4 a = zero4();
 #pragma unroll
                     for (int ks = 0; ks < K::KSF; ks++) {
-                        const bf16x8 ko = *reinterpret_cast<const bf16x8 *>(sK + (16 * jb + r16) * K::PF + 32 * ks + 8 * g);
+                        // K in the reordered feature order of the phi(q) tile
+                        const bf16_t *krow = sK + (16 * jb + r16) * K::PF + 32 * ks;
+                        const bf16x8 ko = cat(load4(krow + 4 * g), load4(krow + 16 + 4 * g));
                         const bf16x8 qo = *reinterpret_cast<const bf16x8 *>(sQ + (16 * ib + r16) * K::PF + 32 * ks + 8 * g);
                         a = mfma_bf16(ko, qo, a);
                     }
@@ -259,13 +277,13 @@ __device__ void feat_body(const FeatParams &p, unsigned char *smem, int bh, int 
                 if (K::ZB == 2) {
                     const bf16x8 zo = acc_pair_to_operand(zacc[0], zacc[K::ZB - 1]);
                     const bf16_t *row = sQ + (16 * ib + r16) * K::PF + 32 * w;
-                    dacc = mfma_bf16(zo, cat(load4(row + 4 * g), load4(row + 16 + 4 * g)), dacc);
+                    dacc = mfma_bf16(zo, *reinterpret_cast<const bf16x8 *>(row + 8 * g), dacc);
                 } else {
                     // one block 16 w: the K step 32 (w / 2) with the other half zero
                     const f32x4 zz = zero4();
                     const bf16x8 zo = (w & 1) ? acc_pair_to_operand(zz, zacc[0]) : acc_pair_to_operand(zacc[0], zz);
                     const bf16_t *row = sQ + (16 * ib + r16) * K::PF + 32 * (w >> 1);
-                    dacc = mfma_bf16(zo, cat(load4(row + 4 * g), load4(row + 16 + 4 * g)), dacc);
+                    dacc = mfma_bf16(zo, *reinterpret_cast<const bf16x8 *>(row + 8 * g), dacc);
                 }
                 if (g == 0) sDen[w * K::C + 16 * ib + r16] = dacc[0];
             }
@@ -291,7 +309,7 @@ __device__ void feat_body(const FeatParams &p, unsigned char *smem, int bh, int 
                 const bf16_t *row = sQ + i * K::PF;
 #pragma unroll
                 for (int ks = 0; ks < K::KSF; ks++)
-                    num = mfma_bf16(sop[ks], cat(load4(row + 32 * ks + 4 * g), load4(row + 32 * ks + 16 + 4 * g)), num);
+                    num = mfma_bf16(sop[ks], *reinterpret_cast<const bf16x8 *>(row + 32 * ks + 8 * g), num);
                 if (MODE == FM_CAUSAL) {
 #pragma unroll
                     for (int ks = 0; ks <= ib / 2; ks++)
