@@ -95,8 +95,9 @@ __device__ __forceinline__ void store_piece(bf16_t *tile, int p, const bf16x8 &x
 }
 
 // Stage one chunk (rows >= valid zero): phi(q), phi(k), v, dy, and with WITH_Y also y (into
-// the tile that holds G later).
-template <int D, int DP, bool WITH_Y = false>
+// the tile that holds G later).  PERM_KV: phi(k) and v in the reordered column order of
+// qperm_pos (the k side, whose products take their rows in accumulator-pair K order).
+template <int D, int DP, bool WITH_Y = false, bool PERM_KV = false>
 __device__ __forceinline__ void bwd_stage(const BwdParams &p, size_t tok0, int valid, unsigned char *smem, int tid) {
     using K = BwdCfg<D, DP>;
     bf16_t *sQ = reinterpret_cast<bf16_t *>(smem + K::OFF_Q), *sK = reinterpret_cast<bf16_t *>(smem + K::OFF_K);
@@ -124,11 +125,15 @@ __device__ __forceinline__ void bwd_stage(const BwdParams &p, size_t tok0, int v
 #pragma unroll
     for (int i = 0; i < K::PQ; i++) {
         store_piece<DP, K::PF>(sQ, tid + K::NT * i, a[i]);
-        store_piece<DP, K::PF>(sK, tid + K::NT * i, bq[i]);
+        const int pe = tid + K::NT * i;
+        if (PERM_KV) store8_qperm(sK + (pe / (DP / 8)) * K::PF, 8 * (pe % (DP / 8)), bq[i]);
+        else store_piece<DP, K::PF>(sK, pe, bq[i]);
     }
 #pragma unroll
     for (int i = 0; i < K::PVV; i++) {
-        store_piece<D, K::PV>(sV, tid + K::NT * i, c[i]);
+        const int pe = tid + K::NT * i;
+        if (PERM_KV) store8_qperm(sV + (pe / (D / 8)) * K::PV, 8 * (pe % (D / 8)), c[i]);
+        else store_piece<D, K::PV>(sV, pe, c[i]);
         store_piece<D, K::PV>(sDY, tid + K::NT * i, e[i]);
     }
 }
@@ -214,6 +219,8 @@ __device__ __forceinline__ void bwd_mtile(const bf16_t *sG, const bf16_t *sV, co
 // The k side's tiles stored transposed, [key][query] (the operands swapped in the product), so
 // that its products read them as plain 16-byte rows: read down the rows of a 64-column tile
 // (128-byte rows) the transposing reads conflict in the LDS banks.  Scores without row sums.
+// phi(k) and V are held in the reordered column order (bwd_stage with PERM_KV), so their rows
+// are 16-byte reads here and phi(q), G are read in the matching order.
 template <int D, int DP, int MODE>
 __device__ __forceinline__ void bwd_scores_t(const bf16_t *sQ, const bf16_t *sK, bf16_t *sPT, int w, int g, int r16) {
     using K = BwdCfg<D, DP>;
@@ -231,7 +238,7 @@ __device__ __forceinline__ void bwd_scores_t(const bf16_t *sQ, const bf16_t *sK,
         f32x4 a = zero4();
 #pragma unroll
         for (int ks = 0; ks < K::KSF; ks++)
-            a = mfma_bf16(*reinterpret_cast<const bf16x8 *>(sQ + (16 * ib + r16) * K::PF + 32 * ks + 8 * g),
+            a = mfma_bf16(row_perm(sQ + (16 * ib + r16) * K::PF, 32 * ks, g),
                           *reinterpret_cast<const bf16x8 *>(sK + (16 * jb + r16) * K::PF + 32 * ks + 8 * g), a);
         if (MODE == BW_CAUSAL && jb == ib) {
 #pragma unroll
@@ -260,7 +267,7 @@ __device__ __forceinline__ void bwd_mtile_t(const bf16_t *sG, const bf16_t *sV, 
         f32x4 a = zero4();
 #pragma unroll
         for (int ks = 0; ks < K::KSV; ks++)
-            a = mfma_bf16(*reinterpret_cast<const bf16x8 *>(sG + (16 * ib + r16) * K::PV + 32 * ks + 8 * g),
+            a = mfma_bf16(row_perm(sG + (16 * ib + r16) * K::PV, 32 * ks, g),
                           *reinterpret_cast<const bf16x8 *>(sV + (16 * jb + r16) * K::PV + 32 * ks + 8 * g), a);
         const f32x4 cq = *reinterpret_cast<const f32x4 *>(sC + 16 * ib + 4 * g);
 #pragma unroll
@@ -566,7 +573,7 @@ __device__ void bwd_k_body(const BwdParams &p, unsigned char *smem, int bh, int 
         float2 dc = make_float2(1.0f, 0.0f);
         const bool dc_live = tid < K::C && tid < valid;
         if (dc_live) dc = *reinterpret_cast<const float2 *>(p.den_c + 2 * (tok_base + t0 + tid));
-        bwd_stage<D, DP>(p, tok_base + t0, valid, smem, tid);
+        bwd_stage<D, DP, false, true>(p, tok_base + t0, valid, smem, tid);
         if (tid < K::C) {
             sDn[tid] = dc_live ? 1.0f / dc.x : 0.0f;
             sC[tid] = dc_live ? dc.y : 0.0f;
@@ -596,7 +603,8 @@ __device__ void bwd_k_body(const BwdParams &p, unsigned char *smem, int bh, int 
                 f32x4 o = zero4();
                 const bf16_t *vrow = sV + (16 * jb + r16) * K::PV;
 #pragma unroll
-                for (int ks = 0; ks < K::KSV; ks++) o = mfma_bf16(row_perm(vrow, 32 * ks, g), rop[ks][j], o);
+                for (int ks = 0; ks < K::KSV; ks++)
+                    o = mfma_bf16(*reinterpret_cast<const bf16x8 *>(vrow + 32 * ks + 8 * g), rop[ks][j], o);
                 // M^T phiQ: A = M^T (row key, K queries), B = phiQ (K queries, column feature)
                 if (MODE == BW_CAUSAL) {
 #pragma unroll
@@ -626,7 +634,8 @@ __device__ void bwd_k_body(const BwdParams &p, unsigned char *smem, int bh, int 
                 f32x4 o = zero4();
                 const bf16_t *krow = sK + (16 * jb + r16) * K::PF;
 #pragma unroll
-                for (int ks = 0; ks < K::KSF; ks++) o = mfma_bf16(rvop[ks], row_perm(krow, 32 * ks, g), o);
+                for (int ks = 0; ks < K::KSF; ks++)
+                    o = mfma_bf16(rvop[ks], *reinterpret_cast<const bf16x8 *>(krow + 32 * ks + 8 * g), o);
                 if (MODE == BW_CAUSAL) {
 #pragma unroll
                     for (int ks = 0; ks < 2; ks++) {

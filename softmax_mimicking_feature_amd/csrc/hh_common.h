@@ -87,6 +87,21 @@ __device__ __forceinline__ bf16_t float_to_bf16_bits(float f) {
     return *reinterpret_cast<bf16_t *>(&b);
 }
 
+// A tile whose rows feed the matrix cores in the K order of an accumulator pair (elements
+// 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3 of each 32-wide K step, for lane group g) can be
+// kept with each 32-column group reordered so that the 4-column runs g and g + 4 sit side by
+// side at 8 g: each operand is then one 16-byte read.  Run r of a group goes to position 8 r
+// (r < 4) or 8 (r - 4) + 4.
+__device__ __forceinline__ int qperm_pos(int col) {
+    const int r = (col & 31) >> 2;
+    return (col & ~31) + (r < 4 ? 8 * r : 8 * (r - 4) + 4) + (col & 3);
+}
+// Eight consecutive columns col .. col + 7 (col a multiple of 8) of a reordered row.
+__device__ __forceinline__ void store8_qperm(bf16_t *row, int col, const bf16x8 &x) {
+    store4(row + qperm_pos(col), __builtin_shufflevector(x, x, 0, 1, 2, 3));
+    store4(row + qperm_pos(col + 4), __builtin_shufflevector(x, x, 4, 5, 6, 7));
+}
+
 // Copy of N16 16-byte pieces from global memory into LDS by the NT threads of a workgroup
 // (thread tid moves pieces tid, tid + NT, ...): piece e comes from src_of(e) (or is zero where
 // live(e) is false) and goes to dst_of(e).  Every load is issued before the first store: a loop

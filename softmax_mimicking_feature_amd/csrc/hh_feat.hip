@@ -106,20 +106,12 @@ __device__ __forceinline__ void feat_fetch(FeatPrefetch<D, DP, MODE> &pf, const 
     for (int i = 0; i < K::PVV; i++) pf.v[i] = load_piece<D>(p.v + tok0 * D, tid + K::NT * i, valid);
 }
 
-// phi(q) is kept in LDS with each 32-feature group reordered so that the 4-feature runs g and
-// g + 4 sit side by side at 8 g: the K order of an accumulator pair (features 4 g .. 4 g + 3 and
-// 16 + 4 g .. 16 + 4 g + 3 of a K step) is then one 16-byte read.  Run r of a group goes to
-// position 8 r (r < 4) or 8 (r - 4) + 4.
-__device__ __forceinline__ int qperm_pos(int col) {
-    const int r = (col & 31) >> 2;
-    return (col & ~31) + (r < 4 ? 8 * r : 8 * (r - 4) + 4) + (col & 3);
-}
+// phi(q) is kept in LDS in the reordered column order of qperm_pos (hh_common.h), so that the
+// read-out and normaliser operands, in the K order of an accumulator pair, are 16-byte reads.
 template <int n, int pitch>
 __device__ __forceinline__ void store_piece_qperm(bf16_t *tile, int p, const bf16x8 &x) {
     const int row = p / (n / 8), col = 8 * (p % (n / 8));
-    bf16_t *rp = tile + row * pitch;
-    store4(rp + qperm_pos(col), __builtin_shufflevector(x, x, 0, 1, 2, 3));
-    store4(rp + qperm_pos(col + 4), __builtin_shufflevector(x, x, 4, 5, 6, 7));
+    store8_qperm(tile + row * pitch, col, x);
 }
 
 template <int D, int DP, int MODE>
