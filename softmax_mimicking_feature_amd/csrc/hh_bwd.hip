@@ -186,6 +186,7 @@ __device__ __forceinline__ void bwd_scores(const bf16_t *sQ, const bf16_t *sK, b
 }
 
 // M = G V^T + c 1^T (keys after the query zeroed when causal) into an LDS tile [query][key].
+// G is held in the reordered column order of qperm_pos, V in the natural one.
 template <int D, int DP, int MODE>
 __device__ __forceinline__ void bwd_mtile(const bf16_t *sG, const bf16_t *sV, const float *sC, bf16_t *sM, int w,
                                           int g, int r16) {
@@ -204,7 +205,7 @@ __device__ __forceinline__ void bwd_mtile(const bf16_t *sG, const bf16_t *sV, co
         f32x4 a = zero4();
 #pragma unroll
         for (int ks = 0; ks < K::KSV; ks++)
-            a = mfma_bf16(*reinterpret_cast<const bf16x8 *>(sV + (16 * jb + r16) * K::PV + 32 * ks + 8 * g),
+            a = mfma_bf16(row_perm(sV + (16 * jb + r16) * K::PV, 32 * ks, g),
                           *reinterpret_cast<const bf16x8 *>(sG + (16 * ib + r16) * K::PV + 32 * ks + 8 * g), a);
         const float ci = sC[16 * ib + r16];
 #pragma unroll
@@ -406,9 +407,13 @@ __device__ void bwd_q_body(const BwdParams &p, unsigned char *smem, int bh, int 
             }
         }
         __syncthreads();
+        // G in the reordered column order (qperm_pos): the dphiQ product below reads its rows in
+        // accumulator-pair K order as single 16-byte reads
         for (int e2 = tid; e2 < K::C * D; e2 += K::NT) {
             const int i = e2 / D, col = e2 % D;
-            sG[i * K::PV + col] = float_to_bf16_bits(bf16_bits_to_float(sDY[i * K::PV + col]) * sDn[i]);
+            sG[i * K::PV + qperm_pos(col)] = float_to_bf16_bits(bf16_bits_to_float(sDY[i * K::PV + col]) * sDn[i]);
+            // d = 16: the group's other half is padding, which the staged y (read above) shares
+            if (D < 32) sG[i * K::PV + qperm_pos(col + 16)] = 0;
         }
         __syncthreads();
         if (MODE == BW_CAUSAL) bwd_mtile<D, DP, MODE>(sG, sV, sC, sM, w, g, r16);
@@ -429,7 +434,8 @@ __device__ void bwd_q_body(const BwdParams &p, unsigned char *smem, int bh, int 
                 f32x4 o = zero4();
                 const bf16_t *grow = sG + (16 * ib + r16) * K::PV;
 #pragma unroll
-                for (int ks = 0; ks < K::KSV; ks++) o = mfma_bf16(row_perm(grow, 32 * ks, g), sop[ks][j], o);
+                for (int ks = 0; ks < K::KSV; ks++)
+                    o = mfma_bf16(*reinterpret_cast<const bf16x8 *>(grow + 32 * ks + 8 * g), sop[ks][j], o);
                 if (MODE == BW_CAUSAL) {
                     const bf16_t *mrow = sM + (16 * ib + r16) * K::PM;
 #pragma unroll
@@ -457,7 +463,10 @@ __device__ void bwd_q_body(const BwdParams &p, unsigned char *smem, int bh, int 
         // ---- this segment's reverse sums: R += phiQ^T G (by value columns), r += phiQ^T c (by features)
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) {
-            const bf16x8 gop = down_rows(sG, lr * K::PV + lo, 32 * ks, 16 * w, K::PV);
+            // value columns 16 w .. 16 w + 15 of G down its rows: each lane addresses its 4-column
+            // run where the reordering put it
+            const bf16_t *gp = sG + (lr + 32 * ks) * K::PV + qperm_pos(16 * w + lo);
+            const bf16x8 gop = cat(tr_read(gp), tr_read(gp + 4 * K::PV));
 #pragma unroll
             for (int fb = 0; fb < K::FB; fb++)
                 Racc[fb] = mfma_bf16(down_rows(sQ, lr * K::PF + lo, 32 * ks, 16 * fb, K::PF), gop, Racc[fb]);
