@@ -970,9 +970,23 @@ __global__ void bwd_reduce_kernel(const float *__restrict__ parts, float *__rest
     if (idx >= (long)H * per) return;
     const int h = (int)(idx / per);
     const long e = idx % per;
+    // parts in groups of 16 with every load of a group issued before its sums (a load-then-add
+    // loop would wait one memory latency per part); the sum order is the parts' order
     float acc = 0.0f;
-    for (int b = 0; b < B; b++)
-        for (int wg = 0; wg < wgs_per_seq; wg++) acc += parts[((size_t)(b * H + h) * wgs_per_seq + wg) * per + e];
+    for (int b = 0; b < B; b++) {
+        const float *pb = parts + (size_t)(b * H + h) * wgs_per_seq * per + e;
+        for (int w0 = 0; w0 < wgs_per_seq; w0 += 16) {
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                const int wg = w0 + j < wgs_per_seq ? w0 + j : w0;  // a stand-in part past the end, not added
+                v[j] = pb[(size_t)wg * per];
+            }
+            __builtin_amdgcn_sched_barrier(0);  // the group's loads all in flight before the first sum
+#pragma unroll
+            for (int j = 0; j < 16; j++) acc += w0 + j < wgs_per_seq ? v[j] : 0.0f;
+        }
+    }
     if (e < (long)d * d) dW[(size_t)h * d * d + e] = acc;
     else if (db) db[(size_t)h * d + (e - (long)d * d)] = acc;
 }
