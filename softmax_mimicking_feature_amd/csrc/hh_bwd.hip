@@ -731,8 +731,12 @@ struct MapCfg {
     static constexpr int PERX = (NX + 255) / 256;          // per thread
 };
 
+// At least two waves per SIMD (two workgroups per CU, as the LDS allows): left free, the
+// compiler takes more than 256 registers (VGPRs plus AGPRs used as spill space) and runs one.
+// The two-sided softmax map's backward would spill at that budget and keeps one.
 template <int D, int MAP>
-__global__ __launch_bounds__(256) void bwd_map_kernel(BwdParams p, int tiles_per_seq, int wgs_per_seq) {
+__global__ __launch_bounds__(256, MAP == HH_MAP_HEDGEHOG_SOFTMAX_ ? 1 : 2) void bwd_map_kernel(BwdParams p, int tiles_per_seq,
+                                                                                                int wgs_per_seq) {
     using K = MapCfg<D>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[K::LDS_BYTES];
     constexpr bool TWO = MAP == HH_MAP_HEDGEHOG_ || MAP == HH_MAP_HEDGEHOG_SOFTMAX_;  // two-sided maps
