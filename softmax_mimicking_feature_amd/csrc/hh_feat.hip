@@ -513,7 +513,12 @@ __global__ __launch_bounds__(256) void fm_variant_kernel(const bf16_t *__restric
             }
             continue;
         }
-        // softmax over the d directions (and, two-sided, over their negations)
+        // softmax over the d directions (and, two-sided, over their negations), in base 2: u is
+        // scaled by log2(e) once for both halves
+#pragma unroll
+        for (int lb = 0; lb < LB; lb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) u[lb][r] *= kLog2e;
 #pragma unroll
         for (int half = 0; half < (MAP == HH_MAP_HEDGEHOG_SOFTMAX_ ? 2 : 1); half++) {
             const float sg = half ? -1.0f : 1.0f;
@@ -530,12 +535,13 @@ __global__ __launch_bounds__(256) void fm_variant_kernel(const bf16_t *__restric
             for (int lb = 0; lb < LB; lb++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    e[lb][r] = exp2_fast((sg * u[lb][r] - mx) * kLog2e);
+                    e[lb][r] = exp2_fast(sg * u[lb][r] - mx);
                     sum += e[lb][r];
                 }
             sum += __shfl_xor(sum, 16);
             sum += __shfl_xor(sum, 32);
-            const float rs = 1.0f / sum;
+            // the hardware reciprocal (about 1 ulp): the features are stored in bf16
+            const float rs = __builtin_amdgcn_rcpf(sum);
 #pragma unroll
             for (int lb = 0; lb < LB; lb++) {
                 f32x4 o;
