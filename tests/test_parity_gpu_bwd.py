@@ -7,7 +7,7 @@ matrix-core operands (relative rounding 2^-9 each) and sum in fp32; a gradient e
 many such terms with mixed signs, so its error scales with the largest entry of the gradient
 rather than with the entry itself: a few 2^-9 relative roundings of the largest terms.  Rule per
 tensor: |gpu - oracle| <= 2e-2 |oracle| + 3e-2 max|oracle| elementwise (measured up to 1.7e-2 max|oracle|), and normwise
-||gpu - oracle|| / ||oracle|| <= 1e-2 (measured at most 6e-3 over these cases).  A gradient that
+||gpu - oracle|| / ||oracle|| <= 1e-2 (measured at most 6.7e-3 over these cases).  A gradient that
 is exactly zero (a one-token sequence: y_0 = v_0 whatever q and k are, so dq = dk = dW = db = 0)
 is instead held to the rounding level of the terms that cancel in it: max|gpu| <= 2^-7 max|dv|
 (times B N for dW and db, which sum over the tokens)."""
@@ -111,3 +111,28 @@ def test_backward_model_shapes(d, H):
     N = 1024 if d == 64 else 4096
     say(f"backward hedgehog B1 H{H} N{N} d{d}")
     run_case(HH, True, 1, H, N, d, seed=18100 + d, b_std=0.1 if d == 64 else 0.0)
+
+
+def test_backward_llama2_bench_shape_sampled_heads():
+    # the backward workload as timed (B1 H32 N4096 d128: eight segments of 512 tokens per head,
+    # the launch configuration of that head count), every gradient of three heads against the
+    # oracle, which treats the heads independently (dW, db are per head at B = 1)
+    w = wl.CONFIGS["c3_llama2_backward"]
+    say(f"backward hedgehog B{w.B} H{w.H} N{w.N} d{w.d}, heads 0, 17, 31 against the oracle")
+    x = wl.make_inputs(w)
+    rng = np.random.default_rng(19000)
+    dy = wl.round_to_bf16(rng.standard_normal((w.B, w.H, w.N, w.d)).astype(np.float32))
+    import softmax_mimicking_feature_amd as m
+    q, k, v, W, b = (dev(x[n]) for n in ("q", "k", "v", "W", "b"))
+    y = m.hh_linattn_fwd(q, k, v, W, b, map=HH, causal=True)
+    dq, dk, dv, dW, db = m.hh_linattn_bwd(q, k, v, W, b, y, dev(dy), map=HH, causal=True)
+    torch.cuda.synchronize()
+    heads = [0, 17, 31]
+    sel = lambda a: a[:, heads]
+    oq, ok_, ov, oW, ob = oracle.backward(HH, sel(x["q"]), sel(x["k"]), sel(x["v"]), x["W"][heads], x["b"][heads],
+                                          sel(dy), causal=True)
+    close_grad(host(dv)[:, heads], ov, "dv")
+    close_grad(host(dq)[:, heads], oq, "dq")
+    close_grad(host(dk)[:, heads], ok_, "dk")
+    close_grad(host(dW)[heads], oW, "dW")
+    close_grad(host(db)[heads], ob, "db")
