@@ -70,6 +70,15 @@ bool map_has_b(int map) { return map == HH_MAP_HEDGEHOG || map == HH_MAP_EXP; }
 // Maps whose features the attention kernels read from a workspace (computed by the feature-map
 // kernel first) rather than computing them from q and k themselves.
 bool map_via_features(int map) { return map == HH_MAP_HEDGEHOG_SOFTMAX || map == HH_MAP_EXP || map == HH_MAP_SOFTMAX; }
+// The per-half softmax map in the causal bf16 forward at d = 128 runs on the Hedgehog kernels,
+// which form and normalise the features themselves (no feature tensors in memory).
+bool softmax_fused(int map, int dtype, int causal, int d) {
+    return map == HH_MAP_HEDGEHOG_SOFTMAX && dtype == HH_BF16 && causal == 1 && d == 128;
+}
+// Forwards whose features the kernels read from the workspace.
+bool fwd_via_features(int map, int dtype, int causal, int d) {
+    return map_via_features(map) && !softmax_fused(map, dtype, causal, d);
+}
 
 size_t elem_bytes(int dtype) { return dtype == HH_BF16 ? 2 : 4; }
 
@@ -265,7 +274,7 @@ hh_status_t hh_featuremap(int map, int dtype, int B, int H, int N, int d, const 
 
 size_t hh_linattn_fwd_workspace(int map, int dtype, int causal, int B, int H, int N, int d) {
     if (check_common(map, dtype, B, H, N, d) != HH_OK || (causal != 0 && causal != 1)) return 0;
-    if (map_via_features(map))
+    if (fwd_via_features(map, dtype, causal, d))
         return (dtype == HH_BF16 && N > 0) ? make_feat_plan(map, causal, (long)B * H, N, d).bytes : 0;
     // the larger of the plans with and without an initial state
     const Plan a = make_plan(map, dtype, causal, (long)B * H, N, d, false);
@@ -303,7 +312,7 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
     const size_t nS = (size_t)BH * dp * d * sizeof(float), nz = (size_t)BH * dp * sizeof(float);
     if (overlap(y, nio, S_out, nS) || overlap(y, nio, z_out, nz)) return fail(HH_EINVAL, "y overlaps S_out or z_out");
 
-    if (map_via_features(map) && dtype == HH_BF16 && N > 0) {
+    if (fwd_via_features(map, dtype, causal, d) && dtype == HH_BF16 && N > 0) {
         const FeatPlan fp = make_feat_plan(map, causal, BH, N, d);
         if (!workspace) return fail(HH_EWORKSPACE, "workspace of %zu bytes required, got NULL", fp.bytes);
         if (workspace_bytes < fp.bytes)
@@ -439,6 +448,7 @@ hh_status_t hh_linattn_fwd(int map, int dtype, int causal, int B, int H, int N, 
             slZ = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + wide_slot_S_bytes(BH, pl.nseg, d));
         }
         wp.S_slots = slS; wp.z_slots = slZ; wp.slot_bh_stride = pl.nseg;
+        wp.softmax = softmax_fused(map, dtype, causal, d) ? 1 : 0;
         // causal with few segments per sequence: the chunked pass sums the aggregates of the
         // earlier segments itself (at most 7 slots, still in L2) instead of a separate scan
         const bool direct_prefix = causal && pl.nseg <= 8;

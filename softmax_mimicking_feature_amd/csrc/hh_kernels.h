@@ -55,6 +55,7 @@ struct WideParams {
                                 //   0 none, 1 slot s if s > 0 (exclusive prefixes), 2 slot 0 (total),
                                 //   3 the sum of slots 0 .. s - 1 (segment aggregates, summed by the
                                 //   causal pass itself; no scan)
+    int softmax;                // 1: the per-half softmax map (d = 128, no bias), 0: the Hedgehog map
 };
 // Segment slots of the wide kernels: per (b,h), nseg slots of S (2 d * d floats) and z
 // (2 d floats).  Mode 0: aggregates of slots 0 .. nseg-2 become exclusive prefixes in slots

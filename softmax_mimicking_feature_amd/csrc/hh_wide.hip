@@ -963,7 +963,11 @@ struct StateSymCfg {
     static constexpr int OFF_W = 0;                       // W [D][D], x-tile layout
     static constexpr int OFF_V = OFF_W + D * D * 2;       // V tiles (granules at ssy_vpos)
     static constexpr int OFF_XK = OFF_V + NB * SZ_X;      // k staging tiles
-    static constexpr int LDS_BYTES = OFF_XK + NB * SZ_X;
+    // softmax maps (d = 128): per wave, token and half the local maximum and sum of the
+    // exponentials [NW][2][C] each, then each wave's scale [NW][2][C]
+    static constexpr int OFF_SM = OFF_XK + NB * SZ_X;
+    static constexpr int SM_BYTES = D == 128 ? 3 * NW * 2 * C * 4 : 0;
+    static constexpr int LDS_BYTES = OFF_SM + SM_BYTES;
     static constexpr int WG_PER_CU = D == 128 ? 1 : 2;
     static_assert(LDS_BYTES * WG_PER_CU <= 160 * 1024, "LDS budget");
 };
@@ -1021,11 +1025,42 @@ __device__ __forceinline__ bf16x8 ssy_v_operand(const bf16_t *sV, int lane_v, in
     return cat(lds_read_tr(sV + lane_v + 32 * kt * D), lds_read_tr(sV + lane_v + (32 * kt + 16) * D));
 }
 
-template <int D>
+// Maximum and sum over the 16 lanes of each lane group (lanes 16 g .. 16 g + 15), every lane
+// receiving the result: two quad exchanges, then rotations by 4 and 8 within the row (DPP).
+__device__ __forceinline__ float dpp_f(float v, int ctrl_sel) {
+    const int x = __builtin_bit_cast(int, v);
+    int y;
+    switch (ctrl_sel) {
+    case 0: y = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true); break;   // quad_perm [1,0,3,2]
+    case 1: y = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true); break;   // quad_perm [2,3,0,1]
+    case 2: y = __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, true); break;  // row_ror:4
+    default: y = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true); break; // row_ror:8
+    }
+    return __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float row16_max(float v) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) v = fmaxf(v, dpp_f(v, k));
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) v += dpp_f(v, k);
+    return v;
+}
+
+// SM: the per-half softmax map (section 3.4, Choice 4 with the negation mapping): the features of
+// key j are exp(+-u_j - m) / sum_l exp(+-u_jl - m) per half.  Each wave holds 16 directions of
+// the 64 tokens; it publishes, per token and half, the maximum m_w of its exponents and the sum
+// s_w of exp(x - m_w) over its directions; wave w then combines tokens 8 w .. 8 w + 7 over the
+// eight waves (m = max m_w, Z = sum s_w exp(m_w - m)) into each wave's scale exp(m_w - m) / Z
+// (Z >= 1: the largest term is exp(0)).
+template <int D, bool SM = false>
 __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t *sV, int valid,
                                           const bf16x8 (&wB)[StateSymCfg<D>::KSD], float bias2,
                                           const int (&lane_v)[StateSymCfg<D>::VB], const bf16x8 &ones,
-                                          f32x4 (&sacc)[2][StateSymCfg<D>::VB], f32x4 (&zacc)[2], int g, int r16) {
+                                          f32x4 (&sacc)[2][StateSymCfg<D>::VB], f32x4 (&zacc)[2], int g, int r16,
+                                          float *sm = nullptr, int w = 0) {
     using S = StateSymCfg<D>;
     // u^T for the four token blocks: rows tokens 16 tb + 4 g + r, column direction 16 w + r16
     // (x operands of K step ks + 1 read during the products of step ks)
@@ -1046,23 +1081,93 @@ __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t 
 #pragma unroll
         for (int tb = 0; tb < 4; tb++) u[tb] = mfma_bf16(xc[tb], wB[ks], u[tb]);
     }
-    // V operands of the first K step while the exponentials run
+    // V operands of the first K step while the exponentials run (softmax maps: after the
+    // normaliser exchange, whose registers they would otherwise take)
     bf16x8 vo[S::VB];
+    if constexpr (!SM) {
 #pragma unroll
-    for (int vb = 0; vb < S::VB; vb++) vo[vb] = ssy_v_operand<D>(sV, lane_v[vb], 0);
+        for (int vb = 0; vb < S::VB; vb++) vo[vb] = ssy_v_operand<D>(sV, lane_v[vb], 0);
+    }
     bf16x4 ep[4], en[4];
+    if constexpr (SM) {
+        static_assert(D == 128, "softmax state pass: d = 128");
+        constexpr int C = S::C, NW = S::NW;
+        float *sMax = sm, *sSum = sm + NW * 2 * C, *sScale = sm + 2 * NW * 2 * C;
+        f32x4 a[4], b[4];
+        // one token block at a time (the row reductions of all blocks at once would hold too many
+        // registers)
 #pragma unroll
-    for (int tb = 0; tb < 4; tb++) {
-        f32x4 a, b;
+        for (int tb = 0; tb < 4; tb++) {
+            float mp[4], mn[4];
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const float x = u[tb][r] * kLog2e + bias2;
-            a[r] = exp2_fast(x);
-            b[r] = exp2_fast(-x);
-            if (16 * tb + 4 * g + r >= valid) a[r] = b[r] = 0.0f;  // keys past the end add nothing
+            for (int r = 0; r < 4; r++) {
+                const float x = u[tb][r] * kLog2e;
+                mp[r] = row16_max(x);
+                mn[r] = row16_max(-x);
+                a[tb][r] = exp2_fast(x - mp[r]);
+                b[tb][r] = exp2_fast(-x - mn[r]);
+            }
+            float sa[4], sb[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                sa[r] = row16_sum(a[tb][r]);
+                sb[r] = row16_sum(b[tb][r]);
+            }
+            if (r16 == 0) {
+                const int t = 16 * tb + 4 * g;
+                *reinterpret_cast<f32x4 *>(sMax + (2 * w + 0) * C + t) = f32x4{mp[0], mp[1], mp[2], mp[3]};
+                *reinterpret_cast<f32x4 *>(sMax + (2 * w + 1) * C + t) = f32x4{mn[0], mn[1], mn[2], mn[3]};
+                *reinterpret_cast<f32x4 *>(sSum + (2 * w + 0) * C + t) = f32x4{sa[0], sa[1], sa[2], sa[3]};
+                *reinterpret_cast<f32x4 *>(sSum + (2 * w + 1) * C + t) = f32x4{sb[0], sb[1], sb[2], sb[3]};
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        ep[tb] = to_bf16x4(a);
-        en[tb] = to_bf16x4(b);
+        __syncthreads();
+        if (r16 < 16 && g == 0) {  // lanes 0-15: token 8 w + (lane & 7), half lane >> 3
+            const int t = 8 * w + (r16 & 7), hf = r16 >> 3;
+            float m = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < NW; v++) m = fmaxf(m, sMax[(2 * v + hf) * C + t]);
+            float ev[NW], z = 0.0f;
+#pragma unroll
+            for (int v = 0; v < NW; v++) {
+                ev[v] = exp2_fast(sMax[(2 * v + hf) * C + t] - m);
+                z = fmaf(sSum[(2 * v + hf) * C + t], ev[v], z);
+            }
+            const float rz = 1.0f / z;
+#pragma unroll
+            for (int v = 0; v < NW; v++) sScale[(2 * v + hf) * C + t] = ev[v] * rz;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int tb = 0; tb < 4; tb++) {
+            const f32x4 cp = *reinterpret_cast<const f32x4 *>(sScale + (2 * w + 0) * C + 16 * tb + 4 * g);
+            const f32x4 cn = *reinterpret_cast<const f32x4 *>(sScale + (2 * w + 1) * C + 16 * tb + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                a[tb][r] *= cp[r];
+                b[tb][r] *= cn[r];
+                if (16 * tb + 4 * g + r >= valid) a[tb][r] = b[tb][r] = 0.0f;  // keys past the end add nothing
+            }
+            ep[tb] = to_bf16x4(a[tb]);
+            en[tb] = to_bf16x4(b[tb]);
+        }
+#pragma unroll
+        for (int vb = 0; vb < S::VB; vb++) vo[vb] = ssy_v_operand<D>(sV, lane_v[vb], 0);
+    } else {
+#pragma unroll
+        for (int tb = 0; tb < 4; tb++) {
+            f32x4 a, b;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float x = u[tb][r] * kLog2e + bias2;
+                a[r] = exp2_fast(x);
+                b[r] = exp2_fast(-x);
+                if (16 * tb + 4 * g + r >= valid) a[r] = b[r] = 0.0f;  // keys past the end add nothing
+            }
+            ep[tb] = to_bf16x4(a);
+            en[tb] = to_bf16x4(b);
+        }
     }
 #pragma unroll
     for (int kt = 0; kt < 2; kt++) {
@@ -1080,7 +1185,7 @@ __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t 
 
 // One workgroup's work: the aggregate of segment s of sequence bh into slot bh slot_bh_stride + s,
 // with `smem` the S::LDS_BYTES of its tiles.
-template <int D>
+template <int D, bool SM = false>
 __device__ __forceinline__ void state_sym_body(const WideParams &p, unsigned char *smem, int bh, int s) {
     using S = StateSymCfg<D>;
     const int tid = threadIdx.x;
@@ -1139,7 +1244,8 @@ __device__ __forceinline__ void state_sym_body(const WideParams &p, unsigned cha
             dl.template issue<false>(p.k + base, t, min(S::C, t_end - t), w, x_buf(b2));
             dl.template issue<true>(p.v + base, t, min(S::C, t_end - t), w, smem + S::OFF_V + b2 * S::SZ_X);
         }
-        ssy_chunk<D>(x_buf(b), v_buf(b), valid_of(c), wB, bias2, lane_v, ones, sacc, zacc, g, r16);
+        ssy_chunk<D, SM>(x_buf(b), v_buf(b), valid_of(c), wB, bias2, lane_v, ones, sacc, zacc, g, r16,
+                         reinterpret_cast<float *>(smem + S::OFF_SM), w);
         // chunk c + 1's loads (issued a chunk ago) have landed; chunk c + 2's stay in flight
         if (ahead)
             __builtin_amdgcn_s_waitcnt(waitcnt_lds_vm(2 * DmaLanesT<D, S::C, S::NW>::NB));
@@ -1185,12 +1291,12 @@ __device__ __forceinline__ void state_sym_body(const WideParams &p, unsigned cha
     }
 }
 
-template <int D>
+template <int D, bool SM = false>
 __global__ __launch_bounds__(StateSymCfg<D>::NT, StateSymCfg<D>::WG_PER_CU) void state_sym_kernel(WideParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[StateSymCfg<D>::LDS_BYTES];
     int bh, s;
     wg_head_segment(p.nseg_grid, bh, s);
-    state_sym_body<D>(p, smem, bh, s);
+    state_sym_body<D, SM>(p, smem, bh, s);
 }
 
 // Bidirectional mode with one segment per sequence (d = 64): the total state S = phiK^T V,
@@ -1264,7 +1370,11 @@ struct CausalWsCfg {
     static constexpr int OFF_XK = OFF_XQ + 2 * SZ_X;
     static constexpr int OFF_W = 0;
     static constexpr int OFF_SYNC = OFF_XK + 2 * SZ_X;   // producers' arrival counter
-    static constexpr int LDS_BYTES = OFF_SYNC + 16;
+    // softmax maps: the two producer pairs' arrival counters, then the normaliser partials
+    // [pair (token block)][direction half][q, k][max, sum][feature half][16 tokens]
+    static constexpr int OFF_PAIR = OFF_SYNC + 16;
+    static constexpr int OFF_PART = OFF_PAIR + 16;
+    static constexpr int LDS_BYTES = OFF_PART + 2 * 2 * 2 * 2 * 2 * 16 * 4;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(D * D * 2 <= 2 * SZ_PQ + 2 * SZ_PK, "W fits in the feature tiles");
 };
@@ -1273,11 +1383,27 @@ struct CausalWsCfg {
 // 64 (p >> 1) .. 64 (p >> 1) + 63 (so each producer reads only its 16 tokens of q and k).  All
 // operand reads first, then the eight independent product chains, then the exponentials, so
 // that one wave keeps the LDS, matrix and vector pipes busy at once.
-template <bool FULL>
+// Barrier of the four producer waves alone, on a counter in LDS (the consumers take no part: they
+// are summing their starting state meanwhile).  Each producer's LDS writes and landed direct loads
+// are complete before it arrives; `target` counts arrivals since the counter was cleared.
+__device__ __forceinline__ void producer_barrier(unsigned int *cnt, unsigned int target, int lane) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) __builtin_amdgcn_s_sleep(1);
+}
+
+// Softmax maps (SM): the features of a token are exp(+-u - m) / sum over the half, u = W x without
+// a bias.  Producer p holds 64 of the 128 directions of its 16 tokens; it forms the maximum m_p
+// and the sum s_p of exp(x - m_p) over them, exchanges (m_p, s_p) with the producer holding the
+// other 64 directions (p ^ 2, the same token block) through LDS, and scales its exponentials by
+// exp(m_p - m) / (s_p exp(m_p - m) + s_q exp(m_q - m)), m = max(m_p, m_q).  `part` and `pcnt`
+// are the partials and the pair's arrival counter; ncall counts this producer's calls.
+template <bool FULL, bool SM = false>
 __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsigned char *xk, int valid,
                                              const bf16x8 (&wA)[4][4], const float (&bl2)[4][4],
                                              const float (&bk2)[4], int p, int g, int r16, bf16_t *sPQ,
-                                             bf16_t *sPKT) {
+                                             bf16_t *sPKT, float *part = nullptr, unsigned int *pcnt = nullptr,
+                                             unsigned int *ncall = nullptr) {
     using S = CausalWsCfg;
     const int i = 16 * (p & 1) + r16;
     bf16x8 xb[2][4];  // [keys, queries][K step]
@@ -1301,6 +1427,138 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
             acc[1][mb] = mfma_bf16(wA[mb][ks], xb[1][ks], acc[1][mb]);
         }
     const int f0 = 64 * (p >> 1) + 4 * g;
+    if constexpr (SM) {
+        // exponents in base 2; keys: lane direction 64 (p >> 1) + 16 mb + r16, token 4 g + r of the
+        // block; queries: lane token r16, directions 64 (p >> 1) + 16 mb + 4 g + r
+        f32x4 kp[4], kn[4], qp[4], qn[4];
+        float km[2][4], ksum[2][4], qm[2], qsum[2];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            float a = -INFINITY, b = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++) {
+                const float x = acc[0][mb][r] * kLog2e;
+                a = fmaxf(a, x);
+                b = fmaxf(b, -x);
+            }
+            km[0][r] = row16_max(a);
+            km[1][r] = row16_max(b);
+        }
+        {
+            float a = -INFINITY, b = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float x = acc[1][mb][r] * kLog2e;
+                    a = fmaxf(a, x);
+                    b = fmaxf(b, -x);
+                }
+            a = fmaxf(a, __shfl_xor(a, 16));
+            b = fmaxf(b, __shfl_xor(b, 16));
+            qm[0] = fmaxf(a, __shfl_xor(a, 32));
+            qm[1] = fmaxf(b, __shfl_xor(b, 32));
+        }
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            float a = 0.0f, b = 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++) {
+                const float x = acc[0][mb][r] * kLog2e;
+                kp[mb][r] = exp2_fast(x - km[0][r]);
+                kn[mb][r] = exp2_fast(-x - km[1][r]);
+                a += kp[mb][r];
+                b += kn[mb][r];
+            }
+            ksum[0][r] = row16_sum(a);
+            ksum[1][r] = row16_sum(b);
+        }
+        {
+            float a = 0.0f, b = 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float x = acc[1][mb][r] * kLog2e;
+                    qp[mb][r] = exp2_fast(x - qm[0]);
+                    qn[mb][r] = exp2_fast(-x - qm[1]);
+                    a += qp[mb][r];
+                    b += qn[mb][r];
+                }
+            a += __shfl_xor(a, 16);
+            b += __shfl_xor(b, 16);
+            qsum[0] = a + __shfl_xor(a, 32);
+            qsum[1] = b + __shfl_xor(b, 32);
+        }
+        // publish this producer's partials, meet the partner, combine
+        auto slot = [&](int dh, int qk, int ms, int hf) { return part + ((((p & 1) * 2 + dh) * 2 + qk) * 2 + ms) * 32 + 16 * hf; };
+        const int dh = p >> 1;
+        if (r16 == 0) {
+#pragma unroll
+            for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    slot(dh, 1, 0, hf)[4 * g + r] = km[hf][r];
+                    slot(dh, 1, 1, hf)[4 * g + r] = ksum[hf][r];
+                }
+        }
+        if (g == 0) {
+#pragma unroll
+            for (int hf = 0; hf < 2; hf++) {
+                slot(dh, 0, 0, hf)[r16] = qm[hf];
+                slot(dh, 0, 1, hf)[r16] = qsum[hf];
+            }
+        }
+        *ncall += 1;
+        producer_barrier(pcnt, 2u * *ncall, 16 * g + r16);
+        float kc[2][4], qc[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float mo = slot(dh ^ 1, 1, 0, hf)[4 * g + r], so = slot(dh ^ 1, 1, 1, hf)[4 * g + r];
+                const float m = fmaxf(km[hf][r], mo);
+                const float e = exp2_fast(km[hf][r] - m);
+                kc[hf][r] = e / fmaf(ksum[hf][r], e, so * exp2_fast(mo - m));
+            }
+            const float mo = slot(dh ^ 1, 0, 0, hf)[r16], so = slot(dh ^ 1, 0, 1, hf)[r16];
+            const float m = fmaxf(qm[hf], mo);
+            const float e = exp2_fast(qm[hf] - m);
+            qc[hf] = e / fmaf(qsum[hf], e, so * exp2_fast(mo - m));
+        }
+        const int fk = 64 * (p >> 1) + r16;
+        const int tk = 16 * (p & 1) + 4 * g;
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) {
+            f32x4 ep, en;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                ep[r] = kp[mb][r] * kc[0][r];
+                en[r] = kn[mb][r] * kc[1][r];
+                if (!FULL && tk + r >= valid) ep[r] = en[r] = 0.0f;  // keys past the end contribute nothing
+            }
+            store4(sPKT + (fk + 16 * mb) * S::PT + tk, to_bf16x4(ep));
+            store4(sPKT + (128 + fk + 16 * mb) * S::PT + tk, to_bf16x4(en));
+        }
+        bf16x4 pe[4], ne[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) {
+            f32x4 ep, en;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                ep[r] = qp[mb][r] * qc[0];
+                en[r] = qn[mb][r] * qc[1];
+            }
+            pe[mb] = to_bf16x4(ep);
+            ne[mb] = to_bf16x4(en);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+            store8(sPQ + i * S::RQ + feat_pos<true>(f0 + 32 * hh), cat(pe[2 * hh], pe[2 * hh + 1]));
+            store8(sPQ + i * S::RQ + feat_pos<true>(128 + f0 + 32 * hh), cat(ne[2 * hh], ne[2 * hh + 1]));
+        }
+        return;
+    }
     {  // keys: phi(k)^T rows 64 (p >> 1) + 16 mb + r16 and 128 + that, tokens 16 (p & 1) + 4 g .. + 3
         const int fk = 64 * (p >> 1) + r16;
         const int tk = 16 * (p & 1) + 4 * g;
@@ -1341,14 +1599,16 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
 }
 
 // Full chunks skip the per-lane masking of keys past the end.
+template <bool SM = false>
 __device__ __forceinline__ void cws_features_any(const unsigned char *xq, const unsigned char *xk, int valid,
                                                  const bf16x8 (&wA)[4][4], const float (&bl2)[4][4],
                                                  const float (&bk2)[4], int p, int g, int r16, bf16_t *sPQ,
-                                                 bf16_t *sPKT) {
+                                                 bf16_t *sPKT, float *part = nullptr, unsigned int *pcnt = nullptr,
+                                                 unsigned int *ncall = nullptr) {
     if (valid >= CausalWsCfg::C)
-        cws_features<true>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
+        cws_features<true, SM>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT, part, pcnt, ncall);
     else
-        cws_features<false>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
+        cws_features<false, SM>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT, part, pcnt, ncall);
 }
 
 // MFMA operand from the transposed phi(k) tile in the permuted feature order of phi(q): lane
@@ -1447,15 +1707,9 @@ __device__ __forceinline__ void cws_issue(const WideParams &p, const DmaLanes128
     }
 }
 
-// Barrier of the four producer waves alone, on a counter in LDS (the consumers take no part: they
-// are summing their starting state meanwhile).  Each producer's LDS writes and landed direct loads
-// are complete before it arrives; `target` counts arrivals since the counter was cleared.
-__device__ __forceinline__ void producer_barrier(unsigned int *cnt, unsigned int target, int lane) {
-    __builtin_amdgcn_s_waitcnt(0);
-    if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) __builtin_amdgcn_s_sleep(1);
-}
 
+// SM: the per-half softmax map (no bias; see cws_features) instead of the Hedgehog map.
+template <bool SM = false>
 __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     using S = CausalWsCfg;
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
@@ -1479,11 +1733,17 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     auto den_buf = [&](int b) { return reinterpret_cast<float *>(smem + S::OFF_DEN + b * S::SZ_DEN); };
 
     unsigned int *psync = reinterpret_cast<unsigned int *>(smem + S::OFF_SYNC);
-    if (tid == 0) *psync = 0u;
+    unsigned int *ppair = reinterpret_cast<unsigned int *>(smem + S::OFF_PAIR);  // [token block]
+    float *part = reinterpret_cast<float *>(smem + S::OFF_PART);
+    if (tid == 0) {
+        *psync = 0u;
+        ppair[0] = ppair[1] = 0u;
+    }
     __syncthreads();
     // The two roles run separate streams with the same barriers: one before the first chunk, then
     // one per chunk.
     if (w < 4) {
+        unsigned int ncall = 0;  // feature-map calls of this producer (softmax maps: pair meetings)
         bf16x8 wA[4][4];  // W operands, directions 64 (pv >> 1) .. + 63
         float bl2[4][4];  // bias x log2(e) of the query accumulators' rows (directions 16 mb + 4 g + r)
         float bk2[4];     // and of the key accumulators' column (direction 16 mb + r16)
@@ -1533,8 +1793,8 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
         }
         producer_barrier(psync, 8, lane);
         if (n > 0)
-            cws_features_any(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, bk2, pv, g, r16, pq_buf(0),
-                             pk_buf(0));
+            cws_features_any<SM>(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, bk2, pv, g, r16,
+                                 pq_buf(0), pk_buf(0), part, ppair + (pv & 1), &ncall);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int c = 0; c < n; c++) {
@@ -1542,8 +1802,9 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
             const int b2 = c & 1;
             cws_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), pv, g, r16);
             if (c + 1 < n)
-                cws_features_any(smem + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, smem + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
-                             valid_of(c + 1), wA, bl2, bk2, pv, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1));
+                cws_features_any<SM>(smem + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, smem + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
+                                     valid_of(c + 1), wA, bl2, bk2, pv, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1), part,
+                                     ppair + (pv & 1), &ncall);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -2397,15 +2658,19 @@ static hipError_t launch_wide_d(int mode, const WideParams &p, int grid, hipStre
     using K = WideCfg<D>;
     switch (mode) {
     case WM_STATE:
-        if (D == 128 || D == 64)
+        if (D == 128 && p.softmax)
+            hipLaunchKernelGGL((state_sym_kernel<128, true>), dim3(grid), dim3(StateSymCfg<128>::NT), 0, st, p);
+        else if (D == 128 || D == 64)
             hipLaunchKernelGGL((state_sym_kernel<D == 128 ? 128 : 64>), dim3(grid),
                                dim3(StateSymCfg<D == 128 ? 128 : 64>::NT), 0, st, p);
         else
             hipLaunchKernelGGL((wide_kernel<D, WM_STATE>), dim3(grid), dim3(K::NT), 0, st, p);
         break;
     case WM_CAUSAL:
-        if (D == 128)
-            hipLaunchKernelGGL(causal_ws_kernel_128, dim3(grid), dim3(CausalWsCfg::NT), 0, st, p);
+        if (D == 128 && p.softmax)
+            hipLaunchKernelGGL(causal_ws_kernel_128<true>, dim3(grid), dim3(CausalWsCfg::NT), 0, st, p);
+        else if (D == 128)
+            hipLaunchKernelGGL(causal_ws_kernel_128<false>, dim3(grid), dim3(CausalWsCfg::NT), 0, st, p);
         else if (D == 64)  // two sequences per workgroup
             hipLaunchKernelGGL(causal_ws_kernel_64, dim3((unsigned)((p.BH + 1) / 2 * p.nseg_grid)),
                                dim3(CausalWs64Cfg::NT), 0, st, p);
@@ -2420,6 +2685,8 @@ static hipError_t launch_wide_d(int mode, const WideParams &p, int grid, hipStre
 }
 
 hipError_t launch_wide(int d, int mode, const WideParams &p, int grid, hipStream_t st) {
+    // the softmax map runs on the d = 128 segment-state and causal kernels only
+    if (p.softmax && !(d == 128 && (mode == WM_STATE || mode == WM_CAUSAL))) return hipErrorInvalidValue;
     switch (d) {
     case 16: return launch_wide_d<16>(mode, p, grid, st);
     case 32: return launch_wide_d<32>(mode, p, grid, st);
