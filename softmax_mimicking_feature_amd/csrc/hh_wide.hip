@@ -1038,10 +1038,23 @@ __device__ __forceinline__ float dpp_f(float v, int ctrl_sel) {
     }
     return __builtin_bit_cast(float, y);
 }
+__device__ __forceinline__ int dpp_i(int x, int ctrl_sel) {
+    switch (ctrl_sel) {
+    case 0: return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);
+    case 1: return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);
+    case 2: return __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, true);
+    default: return __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);
+    }
+}
+// The maximum on integers whose order is that of the floats (negative floats with their magnitude
+// bits flipped), so that each step is one integer maximum with the lane exchange folded in.
 __device__ __forceinline__ float row16_max(float v) {
+    int k = __float_as_int(v);
+    k ^= (k >> 31) & 0x7fffffff;
 #pragma unroll
-    for (int k = 0; k < 4; k++) v = fmaxf(v, dpp_f(v, k));
-    return v;
+    for (int j = 0; j < 4; j++) k = max(k, dpp_i(k, j));
+    k ^= (k >> 31) & 0x7fffffff;
+    return __int_as_float(k);
 }
 __device__ __forceinline__ float row16_sum(float v) {
 #pragma unroll
@@ -1134,7 +1147,7 @@ __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t 
                 ev[v] = exp2_fast(sMax[(2 * v + hf) * C + t] - m);
                 z = fmaf(sSum[(2 * v + hf) * C + t], ev[v], z);
             }
-            const float rz = 1.0f / z;
+            const float rz = __builtin_amdgcn_rcpf(z);
 #pragma unroll
             for (int v = 0; v < NW; v++) sScale[(2 * v + hf) * C + t] = ev[v] * rz;
         }
@@ -1519,12 +1532,12 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
                 const float mo = slot(dh ^ 1, 1, 0, hf)[4 * g + r], so = slot(dh ^ 1, 1, 1, hf)[4 * g + r];
                 const float m = fmaxf(km[hf][r], mo);
                 const float e = exp2_fast(km[hf][r] - m);
-                kc[hf][r] = e / fmaf(ksum[hf][r], e, so * exp2_fast(mo - m));
+                kc[hf][r] = e * __builtin_amdgcn_rcpf(fmaf(ksum[hf][r], e, so * exp2_fast(mo - m)));
             }
             const float mo = slot(dh ^ 1, 0, 0, hf)[r16], so = slot(dh ^ 1, 0, 1, hf)[r16];
             const float m = fmaxf(qm[hf], mo);
             const float e = exp2_fast(qm[hf] - m);
-            qc[hf] = e / fmaf(qsum[hf], e, so * exp2_fast(mo - m));
+            qc[hf] = e * __builtin_amdgcn_rcpf(fmaf(qsum[hf], e, so * exp2_fast(mo - m)));
         }
         const int fk = 64 * (p >> 1) + r16;
         const int tk = 16 * (p & 1) + 4 * g;
