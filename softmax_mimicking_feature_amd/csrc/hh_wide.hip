@@ -1080,9 +1080,10 @@ __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t 
     bf16x8 xn[4], xc[4];
 #pragma unroll
     for (int tb = 0; tb < 4; tb++) xn[tb] = staged_x_operand<D>(xk, 16 * tb + r16, 0, g);
-    f32x4 u[4];
+    f32x4 u[4], ut[4];  // ut (softmax maps): u in the transposed layout, lane token 16 tb + r16,
+                        // directions 16 w + 4 g + r (the same operands in swapped roles)
 #pragma unroll
-    for (int tb = 0; tb < 4; tb++) u[tb] = zero4();
+    for (int tb = 0; tb < 4; tb++) u[tb] = ut[tb] = zero4();
 #pragma unroll
     for (int ks = 0; ks < S::KSD; ks++) {
 #pragma unroll
@@ -1092,7 +1093,10 @@ __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t 
             for (int tb = 0; tb < 4; tb++) xn[tb] = staged_x_operand<D>(xk, 16 * tb + r16, ks + 1, g);
         }
 #pragma unroll
-        for (int tb = 0; tb < 4; tb++) u[tb] = mfma_bf16(xc[tb], wB[ks], u[tb]);
+        for (int tb = 0; tb < 4; tb++) {
+            u[tb] = mfma_bf16(xc[tb], wB[ks], u[tb]);
+            if constexpr (SM) ut[tb] = mfma_bf16(wB[ks], xc[tb], ut[tb]);
+        }
     }
     // V operands of the first K step while the exponentials run (softmax maps: after the
     // normaliser exchange, whose registers they would otherwise take)
@@ -1107,33 +1111,52 @@ __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t 
         constexpr int C = S::C, NW = S::NW;
         float *sMax = sm, *sSum = sm + NW * 2 * C, *sScale = sm + 2 * NW * 2 * C;
         f32x4 a[4], b[4];
-        // one token block at a time (the row reductions of all blocks at once would hold too many
-        // registers)
+        // each token's maximum and sum over this wave's 16 directions, from the transposed layout:
+        // four values in the lane, then the four lane groups
 #pragma unroll
         for (int tb = 0; tb < 4; tb++) {
-            float mp[4], mn[4];
+            float mp = -INFINITY, mn = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float x = ut[tb][r] * kLog2e;
+                mp = fmaxf(mp, x);
+                mn = fmaxf(mn, -x);
+            }
+            mp = fmaxf(mp, __shfl_xor(mp, 16));
+            mn = fmaxf(mn, __shfl_xor(mn, 16));
+            mp = fmaxf(mp, __shfl_xor(mp, 32));
+            mn = fmaxf(mn, __shfl_xor(mn, 32));
+            float sp = 0.0f, sn = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float x = ut[tb][r] * kLog2e;
+                sp += exp2_fast(x - mp);
+                sn += exp2_fast(-x - mn);
+            }
+            sp += __shfl_xor(sp, 16);
+            sn += __shfl_xor(sn, 16);
+            sp += __shfl_xor(sp, 32);
+            sn += __shfl_xor(sn, 32);
+            if (g == 0) {
+                const int t = 16 * tb + r16;
+                sMax[(2 * w + 0) * C + t] = mp;
+                sMax[(2 * w + 1) * C + t] = mn;
+                sSum[(2 * w + 0) * C + t] = sp;
+                sSum[(2 * w + 1) * C + t] = sn;
+            }
+        }
+        // the features in the layout of u (tokens 16 tb + 4 g + r) with the same shifts, read back
+        // from this wave's own rows (its LDS writes above complete first, in order)
+#pragma unroll
+        for (int tb = 0; tb < 4; tb++) {
+            const f32x4 mp = *reinterpret_cast<const f32x4 *>(sMax + (2 * w + 0) * C + 16 * tb + 4 * g);
+            const f32x4 mn = *reinterpret_cast<const f32x4 *>(sMax + (2 * w + 1) * C + 16 * tb + 4 * g);
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const float x = u[tb][r] * kLog2e;
-                mp[r] = row16_max(x);
-                mn[r] = row16_max(-x);
                 a[tb][r] = exp2_fast(x - mp[r]);
                 b[tb][r] = exp2_fast(-x - mn[r]);
             }
-            float sa[4], sb[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                sa[r] = row16_sum(a[tb][r]);
-                sb[r] = row16_sum(b[tb][r]);
-            }
-            if (r16 == 0) {
-                const int t = 16 * tb + 4 * g;
-                *reinterpret_cast<f32x4 *>(sMax + (2 * w + 0) * C + t) = f32x4{mp[0], mp[1], mp[2], mp[3]};
-                *reinterpret_cast<f32x4 *>(sMax + (2 * w + 1) * C + t) = f32x4{mn[0], mn[1], mn[2], mn[3]};
-                *reinterpret_cast<f32x4 *>(sSum + (2 * w + 0) * C + t) = f32x4{sa[0], sa[1], sa[2], sa[3]};
-                *reinterpret_cast<f32x4 *>(sSum + (2 * w + 1) * C + t) = f32x4{sb[0], sb[1], sb[2], sb[3]};
-            }
-            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
         if (r16 < 16 && g == 0) {  // lanes 0-15: token 8 w + (lane & 7), half lane >> 3
