@@ -120,9 +120,15 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
             }
         }
     };
-    fetch(t_begin);
+    // The segment-state pass takes the chunks last to first (its sum does not depend on the
+    // order), so that the segment's first chunks are the ones still in L2 when the causal pass,
+    // which starts with them, begins.  Step k handles the chunk at chunk_t0(k).
+    const int nch = t_end > t_begin ? (t_end - t_begin + C - 1) / C : 0;
+    auto chunk_t0 = [&](int k) { return t_begin + C * (MODE == NM_STATE ? nch - 1 - k : k); };
+    if (nch > 0) fetch(chunk_t0(0));
 
-    for (int t0 = t_begin; t0 < t_end; t0 += C) {
+    for (int k = 0; k < nch; k++) {
+        const int t0 = chunk_t0(k);
         const int valid = min(C, t_end - t0);
         // ---- stage the chunk: wave 0 q in fp32 (feature values) and, for the intra-chunk
         // products, q and k in bf16, and v transposed; wave 1 k transposed in fp32 (tokens
@@ -156,7 +162,7 @@ __device__ __forceinline__ void narrow_wave(const NarrowParams &p, int bh, int s
             }
         }
         __syncthreads();
-        if (t0 + C < t_end) fetch(t0 + C);
+        if (k + 1 < nch) fetch(chunk_t0(k + 1));
 
         // V as a B operand, K = tokens in the order of two stacked accumulator blocks:
         // slot s < 4 -> j = 32 ks + 4 g + s, slot s >= 4 -> j = 32 ks + 16 + 4 g + s - 4.

@@ -1240,9 +1240,14 @@ __device__ __forceinline__ void state_sym_body(const WideParams &p, unsigned cha
         const DmaLanesT<D, D, S::NW> wl(w, lane);
         wl.template issue<false>(p.W + (size_t)h * D * D, 0, D, w, smem + S::OFF_W);
     }
-    for (int c = 0; c < 2 && c < n; c++) {  // chunks 0 and 1; the loop fetches two chunks ahead
-        dl.template issue<false>(p.k + base, t_begin + S::C * c, valid_of(c), w, x_buf(c));
-        dl.template issue<true>(p.v + base, t_begin + S::C * c, valid_of(c), w, smem + S::OFF_V + c * S::SZ_X);
+    // The chunks go last to first (the sum does not depend on the order): the segment's first
+    // chunks are then the ones still in L2 when the chunked pass, which starts with them, begins.
+    // Step c handles chunk n - 1 - c.
+    auto chunk_of = [&](int c) { return n - 1 - c; };
+    for (int c = 0; c < 2 && c < n; c++) {  // steps 0 and 1; the loop fetches two steps ahead
+        const int cc = chunk_of(c);
+        dl.template issue<false>(p.k + base, t_begin + S::C * cc, valid_of(cc), w, x_buf(c));
+        dl.template issue<true>(p.v + base, t_begin + S::C * cc, valid_of(cc), w, smem + S::OFF_V + c * S::SZ_X);
     }
     // bias of this lane's direction 16 w + r16, times log2(e)
     const float bias2 = p.b ? bf16_bits_to_float(p.b[(size_t)h * D + 16 * w + r16]) * kLog2e : 0.0f;
@@ -1275,14 +1280,14 @@ __device__ __forceinline__ void state_sym_body(const WideParams &p, unsigned cha
     for (int c = 0; c < n; c++) {
         const int b = c % S::NB;
         const bool ahead = c + 2 < n;
-        if (ahead) {  // k and V of chunk c + 2 into the buffers chunk c - 1 used
-            const int t = t_begin + S::C * (c + 2), b2 = (c + 2) % S::NB;
+        if (ahead) {  // k and V of step c + 2 into the buffers step c - 1 used
+            const int t = t_begin + S::C * chunk_of(c + 2), b2 = (c + 2) % S::NB;
             dl.template issue<false>(p.k + base, t, min(S::C, t_end - t), w, x_buf(b2));
             dl.template issue<true>(p.v + base, t, min(S::C, t_end - t), w, smem + S::OFF_V + b2 * S::SZ_X);
         }
-        ssy_chunk<D, SM>(x_buf(b), v_buf(b), valid_of(c), wB, bias2, lane_v, ones, sacc, zacc, g, r16,
+        ssy_chunk<D, SM>(x_buf(b), v_buf(b), valid_of(chunk_of(c)), wB, bias2, lane_v, ones, sacc, zacc, g, r16,
                          reinterpret_cast<float *>(smem + S::OFF_SM), w);
-        // chunk c + 1's loads (issued a chunk ago) have landed; chunk c + 2's stay in flight
+        // step c + 1's loads (issued a step ago) have landed; step c + 2's stay in flight
         if (ahead)
             __builtin_amdgcn_s_waitcnt(waitcnt_lds_vm(2 * DmaLanesT<D, S::C, S::NW>::NB));
         else
