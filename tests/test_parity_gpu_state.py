@@ -99,6 +99,45 @@ def test_fp32_carry_segmented_equals_one_segment(d):
     close(Sa, So[0, 0], 1e-3, 1e-4 * float(np.abs(So).max()), "S_out vs oracle (bf16 features)")
 
 
+def test_fp32_carry_softmax_map_d128():
+    # The per-half softmax map at d = 128 runs on the fused kernels, which normalise each token's
+    # features themselves (per-wave maxima and sums combined across waves); its segment hand-offs
+    # are the same fp32 slots.  Same two checks as above.
+    m = hh()
+    w = wl.CONFIGS["c3_llama2_softmax_map"].replace(B=1, H=1, seed=9811)
+    say("fp32 carry, softmax map per half d=128: one head alone (many segments) vs in a 256-head batch")
+    x = wl.make_inputs(w)
+    q, k, v, W = (dev(x[n]) for n in ("q", "k", "v", "W"))
+    y1, S1, z1 = m.hh_linattn_fwd(q, k, v, W, None, map=w.map, want_state=True)
+    rep = lambda t: t.expand(256, -1, -1, -1).contiguous()  # noqa: E731
+    y2, S2, z2 = m.hh_linattn_fwd(rep(q), rep(k), rep(v), W, None, map=w.map, want_state=True)
+    torch.cuda.synchronize()
+    assert m.hh_linattn_fwd_workspace(w.map, w.dtype, 1, 1, 1, w.N, w.d) > 0, "the single head must be cut into segments"
+    assert m.hh_linattn_fwd_workspace(w.map, w.dtype, 1, 256, 1, w.N, w.d) == 0, "one segment per sequence, no features in memory"
+    assert torch.equal(S2[:1].expand(256, -1, -1, -1), S2)
+    Sa, Sb = host(S1)[0, 0], host(S2)[0, 0]
+    za, zb = host(z1)[0, 0], host(z2)[0, 0]
+    e_s, e_z = normwise(Sa, Sb), normwise(za, zb)
+    print(f"  segmented vs one segment: S normwise {e_s:.3e}, z normwise {e_z:.3e}", flush=True)
+    # The segment-state pass and the chunked pass form a key's features with different partial
+    # maxima (8 waves of 16 directions vs 2 of 64), so a feature's last bf16 bit can differ between
+    # the two runs: up to a few 1e-5 normwise, where a bf16 hand-off of the aggregates gives ~1e-3.
+    assert e_s <= 1e-4 and e_z <= 1e-4
+    rtol, atol = wl.tolerance(w.dtype)
+    close(host(y1)[0, 0], host(y2)[0, 0], rtol, atol, "y segmented vs one segment")
+    # each half of every feature vector sums to 1, so z_out sums to N per half up to the bf16
+    # rounding of the features
+    assert abs(za[:w.d].sum() / w.N - 1.0) < 2e-3 and abs(za[w.d:].sum() / w.N - 1.0) < 2e-3
+    phik = bf16(oracle.featuremap(w.map, x["k"], x["W"], None))
+    phiq = bf16(oracle.featuremap(w.map, x["q"], x["W"], None))
+    _, So, zo = oracle.causal_features(phiq, phik, x["v"], want_state=True)
+    for what, Sx, zx in (("segmented", Sa, za), ("one segment", Sb, zb)):
+        e_so, e_zo = normwise(Sx, So[0, 0]), normwise(zx, zo[0, 0])
+        print(f"  {what} vs oracle sums of bf16 features: S normwise {e_so:.3e}, z normwise {e_zo:.3e}", flush=True)
+        assert e_so <= 1e-4 and e_zo <= 1e-4
+        close(Sx, So[0, 0], 1e-3, 1e-4 * float(np.abs(So).max()), f"S_out {what} vs oracle (bf16 features)")
+
+
 @pytest.mark.parametrize("d,B,H", [(128, 1, 4), (64, 2, 3)])
 def test_nan_in_values_stays_causal(d, B, H):
     m = hh()
