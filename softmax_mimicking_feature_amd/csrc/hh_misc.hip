@@ -442,8 +442,114 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeParams p) {
     }
 }
 
+// decode_kernel at compile-time sizes for the exponential maps with a bf16 W: the same loads and
+// arithmetic with no load behind a branch.  At a branch's join the compiler no longer counts the
+// outstanding loads and waits for all of them, so in decode_kernel the feature maps wait for the
+// whole state; here they wait only for the token and W, which are requested first, and run while
+// the state arrives (25.8 -> 24.9 us per step at B16 H32 d128).
+template <int D, int DP>
+__global__ __launch_bounds__(256) void decode_fixed_kernel(DecodeParams p) {
+    constexpr int NT = 256, Q4 = D / 4, NP = DP * Q4 / NT;
+    constexpr int TPR = NT / D, EPT = D / TPR, WP = EPT / 8;
+    static_assert(DP * Q4 % NT == 0 && WP >= 1, "whole pieces per thread");
+    __shared__ float sq[D], sk[D], sv[D];
+    __shared__ float sfq[DP], sfk[DP];
+    __shared__ f32x4 sred[NT];
+    __shared__ float sden[NT / 64];
+    const int bh = blockIdx.x, h = bh % p.H, t = threadIdx.x;
+    const bf16_t *Wb = reinterpret_cast<const bf16_t *>(p.W);
+    const int tc = t % D;
+    const bf16_t xq = reinterpret_cast<const bf16_t *>(p.q)[(size_t)bh * D + tc];
+    const bf16_t xk = reinterpret_cast<const bf16_t *>(p.k)[(size_t)bh * D + tc];
+    const bf16_t xv = reinterpret_cast<const bf16_t *>(p.v)[(size_t)bh * D + tc];
+    const int l = t / TPR, part = t % TPR;
+    bf16x8 wreg[WP];
+#pragma unroll
+    for (int j = 0; j < WP; j++) wreg[j] = load8(Wb + ((size_t)h * D + l) * D + part * EPT + 8 * j);
+    const bf16_t bb = *(p.b ? reinterpret_cast<const bf16_t *>(p.b) + (size_t)h * D + l : Wb);
+    __builtin_amdgcn_sched_barrier(0);  // these requests leave before the state's
+    f32x4 *S4 = reinterpret_cast<f32x4 *>(p.S + (size_t)bh * DP * D);
+    f32x4 held[NP];
+#pragma unroll
+    for (int i = 0; i < NP; i++) held[i] = __builtin_nontemporal_load(S4 + t + NT * i);
+    __builtin_amdgcn_sched_barrier(0);  // and the state's before anything waits for the token
+    sq[tc] = bf16_bits_to_float(xq);
+    sk[tc] = bf16_bits_to_float(xk);
+    sv[tc] = bf16_bits_to_float(xv);
+    __syncthreads();
+    float uq = 0.0f, uk = 0.0f;
+#pragma unroll
+    for (int j = 0; j < WP; j++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const float wf = (float)wreg[j][e];
+            uq = fmaf(wf, sq[part * EPT + 8 * j + e], uq);
+            uk = fmaf(wf, sk[part * EPT + 8 * j + e], uk);
+        }
+#pragma unroll
+    for (int o = TPR / 2; o > 0; o >>= 1) {
+        uq += __shfl_xor(uq, o);
+        uk += __shfl_xor(uk, o);
+    }
+    if (part == 0) {
+        const float bl = p.b ? bf16_bits_to_float(bb) : 0.0f;
+        sfq[l] = expf(uq + bl);
+        sfk[l] = expf(uk + bl);
+        if (DP == 2 * D) {
+            sfq[D + l] = expf(-(uq + bl));
+            sfk[D + l] = expf(-(uk + bl));
+        }
+    }
+    __syncthreads();
+    const int c4 = t % Q4;
+    const f32x4 vq = f32x4{sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]};
+    // every piece of the state in before the first update: the updates and their stores then go
+    // out in one burst (measured faster than updating each piece as it arrives)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int i = 0; i < NP; i++) {
+        const int f = (t + NT * i) / Q4;
+        f32x4 x4 = held[i];
+        const float a = sfk[f];
+        x4[0] = fmaf(a, vq[0], x4[0]);
+        x4[1] = fmaf(a, vq[1], x4[1]);
+        x4[2] = fmaf(a, vq[2], x4[2]);
+        x4[3] = fmaf(a, vq[3], x4[3]);
+        __builtin_nontemporal_store(x4, S4 + t + NT * i);
+        const float gq = sfq[f];
+        acc[0] = fmaf(gq, x4[0], acc[0]);
+        acc[1] = fmaf(gq, x4[1], acc[1]);
+        acc[2] = fmaf(gq, x4[2], acc[2]);
+        acc[3] = fmaf(gq, x4[3], acc[3]);
+    }
+    float dpart = 0.0f;
+    float *zb = p.z + (size_t)bh * DP;
+    if (t < DP) {
+        const float zz = zb[t] + sfk[t];
+        zb[t] = zz;
+        dpart = sfq[t] * zz;
+    }
+    sred[t] = acc;
+    for (int o = 32; o > 0; o >>= 1) dpart += __shfl_xor(dpart, o);
+    if ((t & 63) == 0) sden[t >> 6] = dpart;
+    __syncthreads();
+    if (t < Q4) {
+        f32x4 num = zero4();
+        for (int u = t; u < NT; u += Q4) num += sred[u];
+        float den = 0.0f;
+        for (int w = 0; w < NT / 64; w++) den += sden[w];
+        bf16_t *yb = reinterpret_cast<bf16_t *>(p.y) + (size_t)bh * D + 4 * t;
+        for (int c = 0; c < 4; c++) yb[c] = float_to_bf16_bits(num[c] / den);
+    }
+}
+
 hipError_t launch_decode(const DecodeParams &p, int BH, hipStream_t st) {
-    hipLaunchKernelGGL(decode_kernel, dim3(BH), dim3(kDecThreads), 0, st, p);
+    const bool fixed = p.dtype == 1 && (p.map == HH_MAP_HEDGEHOG_ || p.map == HH_MAP_EXP_);
+    if (fixed && p.d == 128 && p.dp == 256) hipLaunchKernelGGL((decode_fixed_kernel<128, 256>), dim3(BH), dim3(256), 0, st, p);
+    else if (fixed && p.d == 128 && p.dp == 128) hipLaunchKernelGGL((decode_fixed_kernel<128, 128>), dim3(BH), dim3(256), 0, st, p);
+    else if (fixed && p.d == 64 && p.dp == 128) hipLaunchKernelGGL((decode_fixed_kernel<64, 128>), dim3(BH), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL(decode_kernel, dim3(BH), dim3(kDecThreads), 0, st, p);
     return hipGetLastError();
 }
 
