@@ -362,7 +362,7 @@ def main():
     elif w.map == wl.MAP_TAYLOR2:
         roof["kernel"] = ("hh_linattn_fwd: every kernel of one call (segment aggregates, exclusive prefix "
                           "over segments, chunked causal pass)")
-    elif w.map == wl.MAP_HEDGEHOG_SOFTMAX and w.causal and w.d == 128:
+    elif w.map == wl.MAP_HEDGEHOG_SOFTMAX and w.causal and w.d in (64, 128):
         roof["kernel"] = ("hh_linattn_fwd: every kernel of one call (segment-state pass and chunked pass, each "
                           "forming and normalising the softmax features itself)")
     elif w.map != wl.MAP_HEDGEHOG:

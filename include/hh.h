@@ -39,7 +39,7 @@
  *  generalised quadratic map d == 16.
  *  Maps 2-4 run the attention over features that a feature-map kernel writes into the
  *  workspace first (bf16), so their forward needs a workspace even with one segment; the
- *  exception is map 2 in the causal bf16 forward at d == 128, whose kernels form and normalise
+ *  exception is map 2 in the causal bf16 forward at d == 64 and 128, whose kernels form and normalise
  *  the features themselves (its workspace then holds only segment slots, as for map 0).
  */
 #ifndef HH_H

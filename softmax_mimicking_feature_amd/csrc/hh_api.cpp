@@ -70,10 +70,10 @@ bool map_has_b(int map) { return map == HH_MAP_HEDGEHOG || map == HH_MAP_EXP; }
 // Maps whose features the attention kernels read from a workspace (computed by the feature-map
 // kernel first) rather than computing them from q and k themselves.
 bool map_via_features(int map) { return map == HH_MAP_HEDGEHOG_SOFTMAX || map == HH_MAP_EXP || map == HH_MAP_SOFTMAX; }
-// The per-half softmax map in the causal bf16 forward at d = 128 runs on the Hedgehog kernels,
-// which form and normalise the features themselves (no feature tensors in memory).
+// The per-half softmax map in the causal bf16 forward at d = 64 and 128 runs on the Hedgehog
+// kernels, which form and normalise the features themselves (no feature tensors in memory).
 bool softmax_fused(int map, int dtype, int causal, int d) {
-    return map == HH_MAP_HEDGEHOG_SOFTMAX && dtype == HH_BF16 && causal == 1 && d == 128;
+    return map == HH_MAP_HEDGEHOG_SOFTMAX && dtype == HH_BF16 && causal == 1 && (d == 128 || d == 64);
 }
 // Forwards whose features the kernels read from the workspace.
 bool fwd_via_features(int map, int dtype, int causal, int d) {

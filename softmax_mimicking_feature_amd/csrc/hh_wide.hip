@@ -963,13 +963,13 @@ struct StateSymCfg {
     static constexpr int OFF_W = 0;                       // W [D][D], x-tile layout
     static constexpr int OFF_V = OFF_W + D * D * 2;       // V tiles (granules at ssy_vpos)
     static constexpr int OFF_XK = OFF_V + NB * SZ_X;      // k staging tiles
-    // softmax maps (d = 128): per wave, token and half the local maximum and sum of the
-    // exponentials [NW][2][C] each, then each wave's scale [NW][2][C]
-    static constexpr int OFF_SM = OFF_XK + NB * SZ_X;
-    static constexpr int SM_BYTES = D == 128 ? 3 * NW * 2 * C * 4 : 0;
-    static constexpr int LDS_BYTES = OFF_SM + SM_BYTES;
+    static constexpr int LDS_BYTES = OFF_XK + NB * SZ_X;
+    // softmax maps only (allocated by their instantiation): per wave, token and half the local
+    // maximum and sum of the exponentials [NW][2][C] each, then each wave's scale [NW][2][C]
+    static constexpr int OFF_SM = LDS_BYTES;
+    static constexpr int SM_BYTES = 3 * NW * 2 * C * 4;
     static constexpr int WG_PER_CU = D == 128 ? 1 : 2;
-    static_assert(LDS_BYTES * WG_PER_CU <= 160 * 1024, "LDS budget");
+    static_assert((LDS_BYTES + SM_BYTES) * WG_PER_CU <= 160 * 1024, "LDS budget");
 };
 
 // Stored position of granule G of row r in this kernel's V tiles: rotated by 64 bytes per row
@@ -1107,8 +1107,8 @@ __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t 
     }
     bf16x4 ep[4], en[4];
     if constexpr (SM) {
-        static_assert(D == 128, "softmax state pass: d = 128");
-        constexpr int C = S::C, NW = S::NW;
+        constexpr int C = S::C, NW = S::NW, TPW = C / NW;  // tokens each wave combines
+        static_assert(2 * TPW <= 64, "one lane per token and half");
         float *sMax = sm, *sSum = sm + NW * 2 * C, *sScale = sm + 2 * NW * 2 * C;
         f32x4 a[4], b[4];
         // each token's maximum and sum over this wave's 16 directions, from the transposed layout:
@@ -1159,8 +1159,9 @@ __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t 
             }
         }
         __syncthreads();
-        if (r16 < 16 && g == 0) {  // lanes 0-15: token 8 w + (lane & 7), half lane >> 3
-            const int t = 8 * w + (r16 & 7), hf = r16 >> 3;
+        const int lane = 16 * g + r16;
+        if (lane < 2 * TPW) {  // lane: token TPW w + lane % TPW, half lane / TPW
+            const int t = TPW * w + lane % TPW, hf = lane / TPW;
             float m = -INFINITY;
 #pragma unroll
             for (int v = 0; v < NW; v++) m = fmaxf(m, sMax[(2 * v + hf) * C + t]);
@@ -1334,7 +1335,7 @@ __device__ __forceinline__ void state_sym_body(const WideParams &p, unsigned cha
 
 template <int D, bool SM = false>
 __global__ __launch_bounds__(StateSymCfg<D>::NT, StateSymCfg<D>::WG_PER_CU) void state_sym_kernel(WideParams p) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[StateSymCfg<D>::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[StateSymCfg<D>::LDS_BYTES + (SM ? StateSymCfg<D>::SM_BYTES : 0)];
     int bh, s;
     wg_head_segment(p.nseg_grid, bh, s);
     state_sym_body<D, SM>(p, smem, bh, s);
@@ -2120,7 +2121,10 @@ struct Dma64Lanes {
 };
 
 // Producer p: features of token block p of a chunk for all 64 directions.
-template <bool FULL>
+// SM: the per-half softmax map (no bias): a producer holds all 64 directions of its 16 tokens, so
+// each token's maximum and sum are reduced inside the wave (keys over the 16 lanes of a group,
+// queries over the four lane groups) and the features are stored normalised.
+template <bool FULL, bool SM = false>
 __device__ __forceinline__ void cw64_features(const unsigned char *xq, const unsigned char *xk, int valid,
                                               const bf16x8 (&wA)[4][2], const float (&bl2)[4][4],
                                               const float (&bk2)[4], int p, int g, int r16, bf16_t *sPQ,
@@ -2146,6 +2150,91 @@ __device__ __forceinline__ void cw64_features(const unsigned char *xq, const uns
             acc[0][mb] = mfma_bf16(xb[0][ks], wA[mb][ks], acc[0][mb]);
             acc[1][mb] = mfma_bf16(wA[mb][ks], xb[1][ks], acc[1][mb]);
         }
+    if constexpr (SM) {
+        const int tk = 16 * p + 4 * g;
+        // keys: lane direction 16 mb + r16, token 4 g + r of the block
+        f32x4 kp[4], kn[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            float a = -INFINITY, b = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++) {
+                const float x = acc[0][mb][r] * kLog2e;
+                a = fmaxf(a, x);
+                b = fmaxf(b, -x);
+            }
+            const float mp = row16_max(a), mn = row16_max(b);
+            float sp = 0.0f, sn = 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++) {
+                const float x = acc[0][mb][r] * kLog2e;
+                kp[mb][r] = exp2_fast(x - mp);
+                kn[mb][r] = exp2_fast(-x - mn);
+                sp += kp[mb][r];
+                sn += kn[mb][r];
+            }
+            const float zp = row16_sum(sp), zn = row16_sum(sn);  // (every lane takes part)
+            const bool live = FULL || tk + r < valid;           // keys past the end contribute nothing
+            const float cp = live ? __builtin_amdgcn_rcpf(zp) : 0.0f;
+            const float cn = live ? __builtin_amdgcn_rcpf(zn) : 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++) {
+                kp[mb][r] *= cp;
+                kn[mb][r] *= cn;
+            }
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) {
+            store4(sPKT + (16 * mb + r16) * S::PT + tk, to_bf16x4(kp[mb]));
+            store4(sPKT + (64 + 16 * mb + r16) * S::PT + tk, to_bf16x4(kn[mb]));
+        }
+        // queries: lane token i, directions 16 mb + 4 g + r
+        float a = -INFINITY, b = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float x = acc[1][mb][r] * kLog2e;
+                a = fmaxf(a, x);
+                b = fmaxf(b, -x);
+            }
+        a = fmaxf(a, __shfl_xor(a, 16));
+        b = fmaxf(b, __shfl_xor(b, 16));
+        const float mq = fmaxf(a, __shfl_xor(a, 32)), nq = fmaxf(b, __shfl_xor(b, 32));
+        f32x4 qp[4], qn[4];
+        float sp = 0.0f, sn = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float x = acc[1][mb][r] * kLog2e;
+                qp[mb][r] = exp2_fast(x - mq);
+                qn[mb][r] = exp2_fast(-x - nq);
+                sp += qp[mb][r];
+                sn += qn[mb][r];
+            }
+        sp += __shfl_xor(sp, 16);
+        sn += __shfl_xor(sn, 16);
+        const float cq = __builtin_amdgcn_rcpf(sp + __shfl_xor(sp, 32)), cqn = __builtin_amdgcn_rcpf(sn + __shfl_xor(sn, 32));
+        bf16x4 pe[4], ne[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) {
+            f32x4 ep, en;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                ep[r] = qp[mb][r] * cq;
+                en[r] = qn[mb][r] * cqn;
+            }
+            pe[mb] = to_bf16x4(ep);
+            ne[mb] = to_bf16x4(en);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+            store8(sPQ + i * S::RQ + feat_pos<true>(32 * hh + 4 * g), cat(pe[2 * hh], pe[2 * hh + 1]));
+            store8(sPQ + i * S::RQ + feat_pos<true>(64 + 32 * hh + 4 * g), cat(ne[2 * hh], ne[2 * hh + 1]));
+        }
+        return;
+    }
     {  // keys: phi(k)^T rows 16 mb + r16 and 64 + that, tokens 16 p + 4 g .. + 3
         const int tk = 16 * p + 4 * g;
 #pragma unroll
@@ -2184,14 +2273,15 @@ __device__ __forceinline__ void cw64_features(const unsigned char *xq, const uns
     }
 }
 
+template <bool SM = false>
 __device__ __forceinline__ void cw64_features_any(const unsigned char *xq, const unsigned char *xk, int valid,
                                                   const bf16x8 (&wA)[4][2], const float (&bl2)[4][4],
                                                   const float (&bk2)[4], int p, int g, int r16, bf16_t *sPQ,
                                                   bf16_t *sPKT) {
     if (valid >= CausalWs64Cfg::C)
-        cw64_features<true>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
+        cw64_features<true, SM>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
     else
-        cw64_features<false>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
+        cw64_features<false, SM>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
 }
 
 // One score block (query block ib, key block jb) over the 128 features: A^T[j][i] (lane: query
@@ -2290,6 +2380,8 @@ __device__ __forceinline__ void cw64_issue(const WideParams &p, const Dma64Lanes
     }
 }
 
+// SM: the per-half softmax map (no bias; see cw64_features) instead of the Hedgehog map.
+template <bool SM = false>
 __global__ __launch_bounds__(512, 1) void causal_ws_kernel_64(WideParams p) {
     using S = CausalWs64Cfg;
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
@@ -2360,7 +2452,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_64(WideParams p) {
             bk2[mb] = has_b ? bv : 0.0f;
         }
         producer_barrier(psync, 2, lane);
-        if (n > 0) cw64_features_any(sm + S::OFF_XQ, sm + S::OFF_XK, valid_of(0), wA, bl2, bk2, idx, g, r16, pq_buf(0),
+        if (n > 0) cw64_features_any<SM>(sm + S::OFF_XQ, sm + S::OFF_XK, valid_of(0), wA, bl2, bk2, idx, g, r16, pq_buf(0),
                                      pk_buf(0));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -2369,7 +2461,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_64(WideParams p) {
             const int b2 = c & 1;
             cw64_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), idx, g, r16);
             if (c + 1 < n)
-                cw64_features_any(sm + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, sm + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
+                cw64_features_any<SM>(sm + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, sm + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
                                   valid_of(c + 1), wA, bl2, bk2, idx, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -2701,6 +2793,8 @@ static hipError_t launch_wide_d(int mode, const WideParams &p, int grid, hipStre
     case WM_STATE:
         if (D == 128 && p.softmax)
             hipLaunchKernelGGL((state_sym_kernel<128, true>), dim3(grid), dim3(StateSymCfg<128>::NT), 0, st, p);
+        else if (D == 64 && p.softmax)
+            hipLaunchKernelGGL((state_sym_kernel<64, true>), dim3(grid), dim3(StateSymCfg<64>::NT), 0, st, p);
         else if (D == 128 || D == 64)
             hipLaunchKernelGGL((state_sym_kernel<D == 128 ? 128 : 64>), dim3(grid),
                                dim3(StateSymCfg<D == 128 ? 128 : 64>::NT), 0, st, p);
@@ -2712,8 +2806,11 @@ static hipError_t launch_wide_d(int mode, const WideParams &p, int grid, hipStre
             hipLaunchKernelGGL(causal_ws_kernel_128<true>, dim3(grid), dim3(CausalWsCfg::NT), 0, st, p);
         else if (D == 128)
             hipLaunchKernelGGL(causal_ws_kernel_128<false>, dim3(grid), dim3(CausalWsCfg::NT), 0, st, p);
-        else if (D == 64)  // two sequences per workgroup
-            hipLaunchKernelGGL(causal_ws_kernel_64, dim3((unsigned)((p.BH + 1) / 2 * p.nseg_grid)),
+        else if (D == 64 && p.softmax)  // two sequences per workgroup
+            hipLaunchKernelGGL(causal_ws_kernel_64<true>, dim3((unsigned)((p.BH + 1) / 2 * p.nseg_grid)),
+                               dim3(CausalWs64Cfg::NT), 0, st, p);
+        else if (D == 64)
+            hipLaunchKernelGGL(causal_ws_kernel_64<false>, dim3((unsigned)((p.BH + 1) / 2 * p.nseg_grid)),
                                dim3(CausalWs64Cfg::NT), 0, st, p);
         else
             hipLaunchKernelGGL((wide_kernel<D, WM_CAUSAL>), dim3(grid), dim3(K::NT), 0, st, p);
@@ -2726,8 +2823,8 @@ static hipError_t launch_wide_d(int mode, const WideParams &p, int grid, hipStre
 }
 
 hipError_t launch_wide(int d, int mode, const WideParams &p, int grid, hipStream_t st) {
-    // the softmax map runs on the d = 128 segment-state and causal kernels only
-    if (p.softmax && !(d == 128 && (mode == WM_STATE || mode == WM_CAUSAL))) return hipErrorInvalidValue;
+    // the softmax map runs on the d = 64 and 128 segment-state and causal kernels only
+    if (p.softmax && !((d == 128 || d == 64) && (mode == WM_STATE || mode == WM_CAUSAL))) return hipErrorInvalidValue;
     switch (d) {
     case 16: return launch_wide_d<16>(mode, p, grid, st);
     case 32: return launch_wide_d<32>(mode, p, grid, st);

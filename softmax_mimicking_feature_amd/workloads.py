@@ -68,6 +68,11 @@ def _cfg() -> Dict[str, Workload]:
         "c2_gpt2_causal", MAP_HEDGEHOG, DT_BF16, True, B=8, H=12, N=1024, d=64, seed=1002,
         qk_scale=1.0, v_scale=1.0, w_std=64 ** -0.5, b_std=0.1,
         description="GPT-2-125M-shaped causal, bf16, B8 H12 N1024 d64 d'128")
+    c["c2_gpt2_softmax_map"] = Workload(
+        "c2_gpt2_softmax_map", MAP_HEDGEHOG_SOFTMAX, DT_BF16, True, B=8, H=12, N=1024, d=64, seed=1002,
+        qk_scale=1.0, v_scale=1.0, w_std=64 ** -0.5, b_std=0.0,
+        description="GPT-2-125M-shaped causal with the softmax-over-features map per half (no bias), bf16, "
+                    "B8 H12 N1024 d64 d'128")
     s3 = 128 ** -0.25
     c["c3_llama2_causal"] = Workload(
         "c3_llama2_causal", MAP_HEDGEHOG, DT_BF16, True, B=1, H=32, N=4096, d=128, seed=1003,
