@@ -1440,7 +1440,8 @@ __device__ __forceinline__ void producer_barrier(unsigned int *cnt, unsigned int
 // other 64 directions (p ^ 2, the same token block) through LDS, and scales its exponentials by
 // exp(m_p - m) / (s_p exp(m_p - m) + s_q exp(m_q - m)), m = max(m_p, m_q).  `part` and `pcnt`
 // are the partials and the pair's arrival counter; ncall counts this producer's calls.
-template <bool FULL, bool SM = false>
+// KO: the keys' features only (the segment-state mode of the chunked pass).
+template <bool FULL, bool SM = false, bool KO = false>
 __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsigned char *xk, int valid,
                                              const bf16x8 (&wA)[4][4], const float (&bl2)[4][4],
                                              const float (&bk2)[4], int p, int g, int r16, bf16_t *sPQ,
@@ -1450,7 +1451,7 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
     const int i = 16 * (p & 1) + r16;
     bf16x8 xb[2][4];  // [keys, queries][K step]
 #pragma unroll
-    for (int t = 0; t < 2; t++)
+    for (int t = 0; t < (KO ? 1 : 2); t++)
 #pragma unroll
         for (int ks = 0; ks < 4; ks++) xb[t][ks] = staged_x_operand<128>(t == 0 ? xk : xq, i, ks, g);
     // keys: u (tokens x directions), lane: direction 64 (p >> 1) + 16 mb + r16, tokens 4 g + r;
@@ -1466,7 +1467,7 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) {
             acc[0][mb] = mfma_bf16(xb[0][ks], wA[mb][ks], acc[0][mb]);
-            acc[1][mb] = mfma_bf16(wA[mb][ks], xb[1][ks], acc[1][mb]);
+            if constexpr (!KO) acc[1][mb] = mfma_bf16(wA[mb][ks], xb[1][ks], acc[1][mb]);
         }
     const int f0 = 64 * (p >> 1) + 4 * g;
     if constexpr (SM) {
@@ -1486,7 +1487,7 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
             km[0][r] = row16_max(a);
             km[1][r] = row16_max(b);
         }
-        {
+        if constexpr (!KO) {
             float a = -INFINITY, b = -INFINITY;
 #pragma unroll
             for (int mb = 0; mb < 4; mb++)
@@ -1515,7 +1516,7 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
             ksum[0][r] = row16_sum(a);
             ksum[1][r] = row16_sum(b);
         }
-        {
+        if constexpr (!KO) {
             float a = 0.0f, b = 0.0f;
 #pragma unroll
             for (int mb = 0; mb < 4; mb++)
@@ -1544,7 +1545,7 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
                     slot(dh, 1, 1, hf)[4 * g + r] = ksum[hf][r];
                 }
         }
-        if (g == 0) {
+        if (!KO && g == 0) {
 #pragma unroll
             for (int hf = 0; hf < 2; hf++) {
                 slot(dh, 0, 0, hf)[r16] = qm[hf];
@@ -1563,10 +1564,12 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
                 const float e = exp2_fast(km[hf][r] - m);
                 kc[hf][r] = e * __builtin_amdgcn_rcpf(fmaf(ksum[hf][r], e, so * exp2_fast(mo - m)));
             }
-            const float mo = slot(dh ^ 1, 0, 0, hf)[r16], so = slot(dh ^ 1, 0, 1, hf)[r16];
-            const float m = fmaxf(qm[hf], mo);
-            const float e = exp2_fast(qm[hf] - m);
-            qc[hf] = e * __builtin_amdgcn_rcpf(fmaf(qsum[hf], e, so * exp2_fast(mo - m)));
+            if constexpr (!KO) {
+                const float mo = slot(dh ^ 1, 0, 0, hf)[r16], so = slot(dh ^ 1, 0, 1, hf)[r16];
+                const float m = fmaxf(qm[hf], mo);
+                const float e = exp2_fast(qm[hf] - m);
+                qc[hf] = e * __builtin_amdgcn_rcpf(fmaf(qsum[hf], e, so * exp2_fast(mo - m)));
+            }
         }
         const int fk = 64 * (p >> 1) + r16;
         const int tk = 16 * (p & 1) + 4 * g;
@@ -1582,6 +1585,7 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
             store4(sPKT + (fk + 16 * mb) * S::PT + tk, to_bf16x4(ep));
             store4(sPKT + (128 + fk + 16 * mb) * S::PT + tk, to_bf16x4(en));
         }
+        if constexpr (KO) return;
         bf16x4 pe[4], ne[4];
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) {
@@ -1618,7 +1622,7 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
             store4(sPKT + (128 + fk + 16 * mb) * S::PT + tk, to_bf16x4(en));
         }
     }
-    {  // queries: direction blocks 2 h, 2 h + 1 share one 16-byte run of their 32-feature group
+    if constexpr (!KO) {  // queries: direction blocks 2 h, 2 h + 1 share one 16-byte run of their 32-feature group
         bf16x4 pe[4], ne[4];
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) {
@@ -1641,16 +1645,16 @@ __device__ __forceinline__ void cws_features(const unsigned char *xq, const unsi
 }
 
 // Full chunks skip the per-lane masking of keys past the end.
-template <bool SM = false>
+template <bool SM = false, bool KO = false>
 __device__ __forceinline__ void cws_features_any(const unsigned char *xq, const unsigned char *xk, int valid,
                                                  const bf16x8 (&wA)[4][4], const float (&bl2)[4][4],
                                                  const float (&bk2)[4], int p, int g, int r16, bf16_t *sPQ,
                                                  bf16_t *sPKT, float *part = nullptr, unsigned int *pcnt = nullptr,
                                                  unsigned int *ncall = nullptr) {
     if (valid >= CausalWsCfg::C)
-        cws_features<true, SM>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT, part, pcnt, ncall);
+        cws_features<true, SM, KO>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT, part, pcnt, ncall);
     else
-        cws_features<false, SM>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT, part, pcnt, ncall);
+        cws_features<false, SM, KO>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT, part, pcnt, ncall);
 }
 
 // MFMA operand from the transposed phi(k) tile in the permuted feature order of phi(q): lane
@@ -1735,6 +1739,8 @@ __device__ __forceinline__ void cws_output(f32x4 (&numT)[2][2], const bf16_t *sA
 
 // Inputs of chunk c + 1 (V) and c + 2 (q, k) into the buffers freed by the last chunk; issued by
 // every wave (each moves its own 1 KB blocks).
+// ST: no query tiles (the segment-state mode).
+template <bool ST = false>
 __device__ __forceinline__ void cws_issue(const WideParams &p, const DmaLanes128<32> &dl, size_t base, int t_begin,
                                           int t_end, int c, int n, int w, unsigned char *smem) {
     using S = CausalWsCfg;
@@ -1744,14 +1750,16 @@ __device__ __forceinline__ void cws_issue(const WideParams &p, const DmaLanes128
     }
     if (c + 2 < n) {
         const int t = t_begin + S::C * (c + 2), b = c & 1;
-        dl.issue<false>(p.q + base, t, min(S::C, t_end - t), w, smem + S::OFF_XQ + b * S::SZ_X);
+        if (!ST) dl.issue<false>(p.q + base, t, min(S::C, t_end - t), w, smem + S::OFF_XQ + b * S::SZ_X);
         dl.issue<false>(p.k + base, t, min(S::C, t_end - t), w, smem + S::OFF_XK + b * S::SZ_X);
     }
 }
 
 
 // SM: the per-half softmax map (no bias; see cws_features) instead of the Hedgehog map.
-template <bool SM = false>
+// ST: segment-state mode: the same pipeline with the keys' features only and the consumers'
+// state update alone, from a zero state; the segment's aggregate is written to its slot.
+template <bool SM = false, bool ST = false>
 __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     using S = CausalWsCfg;
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
@@ -1797,12 +1805,13 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
         for (int hw = 0; hw < 2; hw++) {
             const int vw = w + 4 * hw;
             if (n > 0) {
-                stage_x<128, 32>(p.q + base, t_begin, valid_of(0), vw, lane, smem + S::OFF_XQ);
+                if (!ST) stage_x<128, 32>(p.q + base, t_begin, valid_of(0), vw, lane, smem + S::OFF_XQ);
                 stage_x<128, 32>(p.k + base, t_begin, valid_of(0), vw, lane, smem + S::OFF_XK);
                 stage_v<128, 32>(p.v + base, t_begin, valid_of(0), vw, lane, smem + S::OFF_V);
             }
             if (n > 1) {
-                stage_x<128, 32>(p.q + base, t_begin + S::C, valid_of(1), vw, lane, smem + S::OFF_XQ + S::SZ_X);
+                if (!ST)
+                    stage_x<128, 32>(p.q + base, t_begin + S::C, valid_of(1), vw, lane, smem + S::OFF_XQ + S::SZ_X);
                 stage_x<128, 32>(p.k + base, t_begin + S::C, valid_of(1), vw, lane, smem + S::OFF_XK + S::SZ_X);
             }
             stage_w_dma128(p.W, h, vw, lane, smem + S::OFF_W);
@@ -1835,18 +1844,18 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
         }
         producer_barrier(psync, 8, lane);
         if (n > 0)
-            cws_features_any<SM>(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, bk2, pv, g, r16,
-                                 pq_buf(0), pk_buf(0), part, ppair + (pv & 1), &ncall);
+            cws_features_any<SM, ST>(smem + S::OFF_XQ, smem + S::OFF_XK, valid_of(0), wA, bl2, bk2, pv, g, r16,
+                                     pq_buf(0), pk_buf(0), part, ppair + (pv & 1), &ncall);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int c = 0; c < n; c++) {
-            cws_issue(p, dl, base, t_begin, t_end, c, n, w, smem);
+            cws_issue<ST>(p, dl, base, t_begin, t_end, c, n, w, smem);
             const int b2 = c & 1;
-            cws_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), pv, g, r16);
+            if (!ST) cws_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), pv, g, r16);
             if (c + 1 < n)
-                cws_features_any<SM>(smem + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, smem + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
-                                     valid_of(c + 1), wA, bl2, bk2, pv, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1), part,
-                                     ppair + (pv & 1), &ncall);
+                cws_features_any<SM, ST>(smem + S::OFF_XQ + (b2 ^ 1) * S::SZ_X,
+                                         smem + S::OFF_XK + (b2 ^ 1) * S::SZ_X, valid_of(c + 1), wA, bl2, bk2, pv, g,
+                                         r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1), part, ppair + (pv & 1), &ncall);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -1865,7 +1874,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
         for (int fb = 0; fb < 16; fb++) sacc[fb][0] = sacc[fb][1] = zero4();
 #pragma unroll
         for (int zb = 0; zb < 4; zb++) zacc[zb] = zero4();
-        if (p.S_in) {
+        if (!ST && p.S_in) {
             const float *Si = p.S_in + (size_t)bh * p.in_bh_stride * S::DP * S::D;
             const float *zi = p.z_in + (size_t)bh * p.in_bh_stride * S::DP;
 #pragma unroll
@@ -1882,8 +1891,8 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
                 for (int r = 0; r < 4; r++) zacc[zb][r] = zi[16 * (4 * pv + zb) + 4 * g + r];
         }
         int t0 = 0, t1 = 0;  // slots to add
-        if (s > 0 && p.slot_mode == 1) t0 = s, t1 = s + 1;
-        if (s > 0 && p.slot_mode == 3) t0 = 0, t1 = s;
+        if (!ST && s > 0 && p.slot_mode == 1) t0 = s, t1 = s + 1;
+        if (!ST && s > 0 && p.slot_mode == 3) t0 = 0, t1 = s;
         for (int t = t0; t < t1; t++) {
             const size_t sl = (size_t)bh * p.slot_bh_stride + t;
             const float *zs = p.z_slots + sl * S::DP;
@@ -1915,12 +1924,63 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_128(WideParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    f32x4 numT[2][2];
-#pragma unroll
-    for (int ib = 0; ib < 2; ib++) numT[ib][0] = numT[ib][1] = zero4();
     const int r0 = 8 * g + (r16 >> 2);
     const int lane_v = r0 * S::D + 8 * v_pos(r0, 4 * pv + (r16 & 3));
     const bf16x8 ones = ones_bf16x8();
+    if constexpr (ST) {
+        // the update alone: S += phi(K)^T V and z += phi(K)^T 1 per chunk, as in the loop below
+        for (int c = 0; c < n; c++) {
+            cws_issue<true>(p, dl, base, t_begin, t_end, c, n, w, smem);
+            const bf16_t *sPK = pk_buf(c & 1);
+            const bf16_t *sV = v_buf(c % 3);
+            bf16x8 vop[2], an[2];
+#pragma unroll
+            for (int vb = 0; vb < 2; vb++) vop[vb] = operand_down_rows(sV, lane_v, 4 * vb, S::D);
+#pragma unroll
+            for (int j = 0; j < 2; j++) an[j] = load8(sPK + (16 * j + r16) * S::PT + 8 * g);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < 8; ks++) {
+                const bf16x8 ac[2] = {an[0], an[1]};
+                if (ks < 7) {
+#pragma unroll
+                    for (int j = 0; j < 2; j++) an[j] = load8(sPK + (32 * (ks + 1) + 16 * j + r16) * S::PT + 8 * g);
+                }
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+#pragma unroll
+                    for (int vb = 0; vb < 2; vb++)
+                        sacc[2 * ks + j][vb] = mfma_bf16(ac[j], vop[vb], sacc[2 * ks + j][vb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++)
+                zacc[zb] = mfma_bf16(load8(sPK + (16 * (4 * pv + zb) + r16) * S::PT + 8 * g), ones, zacc[zb]);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        // slot s: each accumulator as the 16-byte piece the slot sum above reads it back from
+        const size_t sl = (size_t)bh * p.slot_bh_stride + s;
+        float *img = p.S_slots + sl * S::DP * S::D;
+#pragma unroll
+        for (int fa = 0; fa < 2; fa++)
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+#pragma unroll
+                for (int vb = 0; vb < 2; vb++) *slot_piece(img, (4 * fa + pv) * 8 + j, vb, lane) = sacc[8 * fa + j][vb];
+        if (r16 == 0) {
+            float *zs = p.z_slots + sl * S::DP;
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) zs[16 * (4 * pv + zb) + 4 * g + r] = zacc[zb][r];
+        }
+        return;
+    }
+
+    f32x4 numT[2][2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++) numT[ib][0] = numT[ib][1] = zero4();
     bf16_t *ybase = p.y + base;
 
     for (int c = 0; c < n; c++) {
@@ -2791,8 +2851,11 @@ static hipError_t launch_wide_d(int mode, const WideParams &p, int grid, hipStre
     using K = WideCfg<D>;
     switch (mode) {
     case WM_STATE:
+        // the softmax map at d = 128: the chunked pass's pipeline in its segment-state mode (its
+        // producer pairs share the normalisation; at B1 H32 N4096 it takes 4 % less time per call than
+        // the all-wave segment-state pass)
         if (D == 128 && p.softmax)
-            hipLaunchKernelGGL((state_sym_kernel<128, true>), dim3(grid), dim3(StateSymCfg<128>::NT), 0, st, p);
+            hipLaunchKernelGGL((causal_ws_kernel_128<true, true>), dim3(grid), dim3(CausalWsCfg::NT), 0, st, p);
         else if (D == 64 && p.softmax)
             hipLaunchKernelGGL((state_sym_kernel<64, true>), dim3(grid), dim3(StateSymCfg<64>::NT), 0, st, p);
         else if (D == 128 || D == 64)
