@@ -964,12 +964,8 @@ struct StateSymCfg {
     static constexpr int OFF_V = OFF_W + D * D * 2;       // V tiles (granules at ssy_vpos)
     static constexpr int OFF_XK = OFF_V + NB * SZ_X;      // k staging tiles
     static constexpr int LDS_BYTES = OFF_XK + NB * SZ_X;
-    // softmax maps only (allocated by their instantiation): per wave, token and half the local
-    // maximum and sum of the exponentials [NW][2][C] each, then each wave's scale [NW][2][C]
-    static constexpr int OFF_SM = LDS_BYTES;
-    static constexpr int SM_BYTES = 3 * NW * 2 * C * 4;
     static constexpr int WG_PER_CU = D == 128 ? 1 : 2;
-    static_assert((LDS_BYTES + SM_BYTES) * WG_PER_CU <= 160 * 1024, "LDS budget");
+    static_assert(LDS_BYTES * WG_PER_CU <= 160 * 1024, "LDS budget");
 };
 
 // Stored position of granule G of row r in this kernel's V tiles: rotated by 64 bytes per row
@@ -1062,28 +1058,20 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-// SM: the per-half softmax map (section 3.4, Choice 4 with the negation mapping): the features of
-// key j are exp(+-u_j - m) / sum_l exp(+-u_jl - m) per half.  Each wave holds 16 directions of
-// the 64 tokens; it publishes, per token and half, the maximum m_w of its exponents and the sum
-// s_w of exp(x - m_w) over its directions; wave w then combines tokens 8 w .. 8 w + 7 over the
-// eight waves (m = max m_w, Z = sum s_w exp(m_w - m)) into each wave's scale exp(m_w - m) / Z
-// (Z >= 1: the largest term is exp(0)).
-template <int D, bool SM = false>
+template <int D>
 __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t *sV, int valid,
                                           const bf16x8 (&wB)[StateSymCfg<D>::KSD], float bias2,
                                           const int (&lane_v)[StateSymCfg<D>::VB], const bf16x8 &ones,
-                                          f32x4 (&sacc)[2][StateSymCfg<D>::VB], f32x4 (&zacc)[2], int g, int r16,
-                                          float *sm = nullptr, int w = 0) {
+                                          f32x4 (&sacc)[2][StateSymCfg<D>::VB], f32x4 (&zacc)[2], int g, int r16) {
     using S = StateSymCfg<D>;
     // u^T for the four token blocks: rows tokens 16 tb + 4 g + r, column direction 16 w + r16
     // (x operands of K step ks + 1 read during the products of step ks)
     bf16x8 xn[4], xc[4];
 #pragma unroll
     for (int tb = 0; tb < 4; tb++) xn[tb] = staged_x_operand<D>(xk, 16 * tb + r16, 0, g);
-    f32x4 u[4], ut[4];  // ut (softmax maps): u in the transposed layout, lane token 16 tb + r16,
-                        // directions 16 w + 4 g + r (the same operands in swapped roles)
+    f32x4 u[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; tb++) u[tb] = ut[tb] = zero4();
+    for (int tb = 0; tb < 4; tb++) u[tb] = zero4();
 #pragma unroll
     for (int ks = 0; ks < S::KSD; ks++) {
 #pragma unroll
@@ -1093,118 +1081,25 @@ __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t 
             for (int tb = 0; tb < 4; tb++) xn[tb] = staged_x_operand<D>(xk, 16 * tb + r16, ks + 1, g);
         }
 #pragma unroll
-        for (int tb = 0; tb < 4; tb++) {
-            u[tb] = mfma_bf16(xc[tb], wB[ks], u[tb]);
-            if constexpr (SM) ut[tb] = mfma_bf16(wB[ks], xc[tb], ut[tb]);
-        }
+        for (int tb = 0; tb < 4; tb++) u[tb] = mfma_bf16(xc[tb], wB[ks], u[tb]);
     }
-    // V operands of the first K step while the exponentials run (softmax maps: after the
-    // normaliser exchange, whose registers they would otherwise take)
+    // V operands of the first K step while the exponentials run
     bf16x8 vo[S::VB];
-    if constexpr (!SM) {
 #pragma unroll
-        for (int vb = 0; vb < S::VB; vb++) vo[vb] = ssy_v_operand<D>(sV, lane_v[vb], 0);
-    }
+    for (int vb = 0; vb < S::VB; vb++) vo[vb] = ssy_v_operand<D>(sV, lane_v[vb], 0);
     bf16x4 ep[4], en[4];
-    if constexpr (SM) {
-        constexpr int C = S::C, NW = S::NW, TPW = C / NW;  // tokens each wave combines
-        static_assert(2 * TPW <= 64, "one lane per token and half");
-        float *sMax = sm, *sSum = sm + NW * 2 * C, *sScale = sm + 2 * NW * 2 * C;
-        f32x4 a[4], b[4];
-        // each token's maximum and sum over this wave's 16 directions, from the transposed layout:
-        // four values in the lane, then the four lane groups
 #pragma unroll
-        for (int tb = 0; tb < 4; tb++) {
-            float mp = -INFINITY, mn = -INFINITY;
+    for (int tb = 0; tb < 4; tb++) {
+        f32x4 a, b;
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float x = ut[tb][r] * kLog2e;
-                mp = fmaxf(mp, x);
-                mn = fmaxf(mn, -x);
-            }
-            mp = fmaxf(mp, __shfl_xor(mp, 16));
-            mn = fmaxf(mn, __shfl_xor(mn, 16));
-            mp = fmaxf(mp, __shfl_xor(mp, 32));
-            mn = fmaxf(mn, __shfl_xor(mn, 32));
-            float sp = 0.0f, sn = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float x = ut[tb][r] * kLog2e;
-                sp += exp2_fast(x - mp);
-                sn += exp2_fast(-x - mn);
-            }
-            sp += __shfl_xor(sp, 16);
-            sn += __shfl_xor(sn, 16);
-            sp += __shfl_xor(sp, 32);
-            sn += __shfl_xor(sn, 32);
-            if (g == 0) {
-                const int t = 16 * tb + r16;
-                sMax[(2 * w + 0) * C + t] = mp;
-                sMax[(2 * w + 1) * C + t] = mn;
-                sSum[(2 * w + 0) * C + t] = sp;
-                sSum[(2 * w + 1) * C + t] = sn;
-            }
+        for (int r = 0; r < 4; r++) {
+            const float x = u[tb][r] * kLog2e + bias2;
+            a[r] = exp2_fast(x);
+            b[r] = exp2_fast(-x);
+            if (16 * tb + 4 * g + r >= valid) a[r] = b[r] = 0.0f;  // keys past the end add nothing
         }
-        // the features in the layout of u (tokens 16 tb + 4 g + r) with the same shifts, read back
-        // from this wave's own rows (its LDS writes above complete first, in order)
-#pragma unroll
-        for (int tb = 0; tb < 4; tb++) {
-            const f32x4 mp = *reinterpret_cast<const f32x4 *>(sMax + (2 * w + 0) * C + 16 * tb + 4 * g);
-            const f32x4 mn = *reinterpret_cast<const f32x4 *>(sMax + (2 * w + 1) * C + 16 * tb + 4 * g);
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float x = u[tb][r] * kLog2e;
-                a[tb][r] = exp2_fast(x - mp[r]);
-                b[tb][r] = exp2_fast(-x - mn[r]);
-            }
-        }
-        __syncthreads();
-        const int lane = 16 * g + r16;
-        if (lane < 2 * TPW) {  // lane: token TPW w + lane % TPW, half lane / TPW
-            const int t = TPW * w + lane % TPW, hf = lane / TPW;
-            float m = -INFINITY;
-#pragma unroll
-            for (int v = 0; v < NW; v++) m = fmaxf(m, sMax[(2 * v + hf) * C + t]);
-            float ev[NW], z = 0.0f;
-#pragma unroll
-            for (int v = 0; v < NW; v++) {
-                ev[v] = exp2_fast(sMax[(2 * v + hf) * C + t] - m);
-                z = fmaf(sSum[(2 * v + hf) * C + t], ev[v], z);
-            }
-            const float rz = __builtin_amdgcn_rcpf(z);
-#pragma unroll
-            for (int v = 0; v < NW; v++) sScale[(2 * v + hf) * C + t] = ev[v] * rz;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int tb = 0; tb < 4; tb++) {
-            const f32x4 cp = *reinterpret_cast<const f32x4 *>(sScale + (2 * w + 0) * C + 16 * tb + 4 * g);
-            const f32x4 cn = *reinterpret_cast<const f32x4 *>(sScale + (2 * w + 1) * C + 16 * tb + 4 * g);
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                a[tb][r] *= cp[r];
-                b[tb][r] *= cn[r];
-                if (16 * tb + 4 * g + r >= valid) a[tb][r] = b[tb][r] = 0.0f;  // keys past the end add nothing
-            }
-            ep[tb] = to_bf16x4(a[tb]);
-            en[tb] = to_bf16x4(b[tb]);
-        }
-#pragma unroll
-        for (int vb = 0; vb < S::VB; vb++) vo[vb] = ssy_v_operand<D>(sV, lane_v[vb], 0);
-    } else {
-#pragma unroll
-        for (int tb = 0; tb < 4; tb++) {
-            f32x4 a, b;
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float x = u[tb][r] * kLog2e + bias2;
-                a[r] = exp2_fast(x);
-                b[r] = exp2_fast(-x);
-                if (16 * tb + 4 * g + r >= valid) a[r] = b[r] = 0.0f;  // keys past the end add nothing
-            }
-            ep[tb] = to_bf16x4(a);
-            en[tb] = to_bf16x4(b);
-        }
+        ep[tb] = to_bf16x4(a);
+        en[tb] = to_bf16x4(b);
     }
 #pragma unroll
     for (int kt = 0; kt < 2; kt++) {
@@ -1222,7 +1117,7 @@ __device__ __forceinline__ void ssy_chunk(const unsigned char *xk, const bf16_t 
 
 // One workgroup's work: the aggregate of segment s of sequence bh into slot bh slot_bh_stride + s,
 // with `smem` the S::LDS_BYTES of its tiles.
-template <int D, bool SM = false>
+template <int D>
 __device__ __forceinline__ void state_sym_body(const WideParams &p, unsigned char *smem, int bh, int s) {
     using S = StateSymCfg<D>;
     const int tid = threadIdx.x;
@@ -1286,8 +1181,7 @@ __device__ __forceinline__ void state_sym_body(const WideParams &p, unsigned cha
             dl.template issue<false>(p.k + base, t, min(S::C, t_end - t), w, x_buf(b2));
             dl.template issue<true>(p.v + base, t, min(S::C, t_end - t), w, smem + S::OFF_V + b2 * S::SZ_X);
         }
-        ssy_chunk<D, SM>(x_buf(b), v_buf(b), valid_of(chunk_of(c)), wB, bias2, lane_v, ones, sacc, zacc, g, r16,
-                         reinterpret_cast<float *>(smem + S::OFF_SM), w);
+        ssy_chunk<D>(x_buf(b), v_buf(b), valid_of(chunk_of(c)), wB, bias2, lane_v, ones, sacc, zacc, g, r16);
         // step c + 1's loads (issued a step ago) have landed; step c + 2's stay in flight
         if (ahead)
             __builtin_amdgcn_s_waitcnt(waitcnt_lds_vm(2 * DmaLanesT<D, S::C, S::NW>::NB));
@@ -1333,12 +1227,12 @@ __device__ __forceinline__ void state_sym_body(const WideParams &p, unsigned cha
     }
 }
 
-template <int D, bool SM = false>
+template <int D>
 __global__ __launch_bounds__(StateSymCfg<D>::NT, StateSymCfg<D>::WG_PER_CU) void state_sym_kernel(WideParams p) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[StateSymCfg<D>::LDS_BYTES + (SM ? StateSymCfg<D>::SM_BYTES : 0)];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[StateSymCfg<D>::LDS_BYTES];
     int bh, s;
     wg_head_segment(p.nseg_grid, bh, s);
-    state_sym_body<D, SM>(p, smem, bh, s);
+    state_sym_body<D>(p, smem, bh, s);
 }
 
 // Bidirectional mode with one segment per sequence (d = 64): the total state S = phiK^T V,
@@ -2184,7 +2078,8 @@ struct Dma64Lanes {
 // SM: the per-half softmax map (no bias): a producer holds all 64 directions of its 16 tokens, so
 // each token's maximum and sum are reduced inside the wave (keys over the 16 lanes of a group,
 // queries over the four lane groups) and the features are stored normalised.
-template <bool FULL, bool SM = false>
+// KO: the keys' features only (the segment-state mode of the chunked pass).
+template <bool FULL, bool SM = false, bool KO = false>
 __device__ __forceinline__ void cw64_features(const unsigned char *xq, const unsigned char *xk, int valid,
                                               const bf16x8 (&wA)[4][2], const float (&bl2)[4][4],
                                               const float (&bk2)[4], int p, int g, int r16, bf16_t *sPQ,
@@ -2193,7 +2088,7 @@ __device__ __forceinline__ void cw64_features(const unsigned char *xq, const uns
     const int i = 16 * p + r16;
     bf16x8 xb[2][2];  // [keys, queries][K step]
 #pragma unroll
-    for (int t = 0; t < 2; t++)
+    for (int t = 0; t < (KO ? 1 : 2); t++)
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) xb[t][ks] = staged_x_operand<64>(t == 0 ? xk : xq, i, ks, g);
     // keys: u (tokens x directions), lane: direction 16 mb + r16, tokens 16 p + 4 g + r;
@@ -2208,7 +2103,7 @@ __device__ __forceinline__ void cw64_features(const unsigned char *xq, const uns
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) {
             acc[0][mb] = mfma_bf16(xb[0][ks], wA[mb][ks], acc[0][mb]);
-            acc[1][mb] = mfma_bf16(wA[mb][ks], xb[1][ks], acc[1][mb]);
+            if constexpr (!KO) acc[1][mb] = mfma_bf16(wA[mb][ks], xb[1][ks], acc[1][mb]);
         }
     if constexpr (SM) {
         const int tk = 16 * p + 4 * g;
@@ -2248,6 +2143,7 @@ __device__ __forceinline__ void cw64_features(const unsigned char *xq, const uns
             store4(sPKT + (16 * mb + r16) * S::PT + tk, to_bf16x4(kp[mb]));
             store4(sPKT + (64 + 16 * mb + r16) * S::PT + tk, to_bf16x4(kn[mb]));
         }
+        if constexpr (KO) return;
         // queries: lane token i, directions 16 mb + 4 g + r
         float a = -INFINITY, b = -INFINITY;
 #pragma unroll
@@ -2311,7 +2207,7 @@ __device__ __forceinline__ void cw64_features(const unsigned char *xq, const uns
             store4(sPKT + (64 + 16 * mb + r16) * S::PT + tk, to_bf16x4(en));
         }
     }
-    {  // queries: direction blocks 2 h, 2 h + 1 share one 16-byte run of their 32-feature group
+    if constexpr (!KO) {  // queries: direction blocks 2 h, 2 h + 1 share one 16-byte run of their 32-feature group
         bf16x4 pe[4], ne[4];
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) {
@@ -2333,15 +2229,15 @@ __device__ __forceinline__ void cw64_features(const unsigned char *xq, const uns
     }
 }
 
-template <bool SM = false>
+template <bool SM = false, bool KO = false>
 __device__ __forceinline__ void cw64_features_any(const unsigned char *xq, const unsigned char *xk, int valid,
                                                   const bf16x8 (&wA)[4][2], const float (&bl2)[4][4],
                                                   const float (&bk2)[4], int p, int g, int r16, bf16_t *sPQ,
                                                   bf16_t *sPKT) {
     if (valid >= CausalWs64Cfg::C)
-        cw64_features<true, SM>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
+        cw64_features<true, SM, KO>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
     else
-        cw64_features<false, SM>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
+        cw64_features<false, SM, KO>(xq, xk, valid, wA, bl2, bk2, p, g, r16, sPQ, sPKT);
 }
 
 // One score block (query block ib, key block jb) over the 128 features: A^T[j][i] (lane: query
@@ -2426,6 +2322,8 @@ __device__ __forceinline__ void cw64_output(f32x4 (&numT)[2][2], const bf16_t *s
 
 // Inputs of chunk c + 1 (V) and c + 2 (q, k) into the buffers freed by the last chunk; each
 // pipeline wave moves its own 1 KB block of each tile.
+// ST: no query tiles (the segment-state mode).
+template <bool ST = false>
 __device__ __forceinline__ void cw64_issue(const WideParams &p, const Dma64Lanes &dl, size_t base, int t_begin,
                                            int t_end, int c, int n, int pw, unsigned char *sm) {
     using S = CausalWs64Cfg;
@@ -2435,13 +2333,15 @@ __device__ __forceinline__ void cw64_issue(const WideParams &p, const Dma64Lanes
     }
     if (c + 2 < n) {
         const int t = t_begin + S::C * (c + 2), b = c & 1;
-        dl.issue<false>(p.q + base, t, min(S::C, t_end - t), pw, sm + S::OFF_XQ + b * S::SZ_X);
+        if (!ST) dl.issue<false>(p.q + base, t, min(S::C, t_end - t), pw, sm + S::OFF_XQ + b * S::SZ_X);
         dl.issue<false>(p.k + base, t, min(S::C, t_end - t), pw, sm + S::OFF_XK + b * S::SZ_X);
     }
 }
 
 // SM: the per-half softmax map (no bias; see cw64_features) instead of the Hedgehog map.
-template <bool SM = false>
+// ST: segment-state mode: the keys' features only and the consumers' update alone, from a zero
+// state; the segment's aggregate goes to its slot in the d = 64 segment-state pass's image.
+template <bool SM = false, bool ST = false>
 __global__ __launch_bounds__(512, 1) void causal_ws_kernel_64(WideParams p) {
     using S = CausalWs64Cfg;
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
@@ -2481,12 +2381,13 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_64(WideParams p) {
         for (int hw = 0; hw < 2; hw++) {
             const Dma64Lanes dh(idx + 2 * hw, lane);
             if (n > 0) {
-                dh.issue<false>(p.q + base, t_begin, valid_of(0), idx + 2 * hw, sm + S::OFF_XQ);
+                if (!ST) dh.issue<false>(p.q + base, t_begin, valid_of(0), idx + 2 * hw, sm + S::OFF_XQ);
                 dh.issue<false>(p.k + base, t_begin, valid_of(0), idx + 2 * hw, sm + S::OFF_XK);
                 dh.issue<true>(p.v + base, t_begin, valid_of(0), idx + 2 * hw, sm + S::OFF_V);
             }
             if (n > 1) {
-                dh.issue<false>(p.q + base, t_begin + S::C, valid_of(1), idx + 2 * hw, sm + S::OFF_XQ + S::SZ_X);
+                if (!ST)
+                    dh.issue<false>(p.q + base, t_begin + S::C, valid_of(1), idx + 2 * hw, sm + S::OFF_XQ + S::SZ_X);
                 dh.issue<false>(p.k + base, t_begin + S::C, valid_of(1), idx + 2 * hw, sm + S::OFF_XK + S::SZ_X);
             }
         }
@@ -2512,17 +2413,18 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_64(WideParams p) {
             bk2[mb] = has_b ? bv : 0.0f;
         }
         producer_barrier(psync, 2, lane);
-        if (n > 0) cw64_features_any<SM>(sm + S::OFF_XQ, sm + S::OFF_XK, valid_of(0), wA, bl2, bk2, idx, g, r16, pq_buf(0),
-                                     pk_buf(0));
+        if (n > 0)
+            cw64_features_any<SM, ST>(sm + S::OFF_XQ, sm + S::OFF_XK, valid_of(0), wA, bl2, bk2, idx, g, r16,
+                                      pq_buf(0), pk_buf(0));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int c = 0; c < n; c++) {
-            cw64_issue(p, dl, base, t_begin, t_end, c, n, pw, sm);
+            cw64_issue<ST>(p, dl, base, t_begin, t_end, c, n, pw, sm);
             const int b2 = c & 1;
-            cw64_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), idx, g, r16);
+            if (!ST) cw64_scores(pq_buf(b2), pk_buf(b2), a_buf(b2), den_buf(b2), idx, g, r16);
             if (c + 1 < n)
-                cw64_features_any<SM>(sm + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, sm + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
-                                  valid_of(c + 1), wA, bl2, bk2, idx, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1));
+                cw64_features_any<SM, ST>(sm + S::OFF_XQ + (b2 ^ 1) * S::SZ_X, sm + S::OFF_XK + (b2 ^ 1) * S::SZ_X,
+                                          valid_of(c + 1), wA, bl2, bk2, idx, g, r16, pq_buf(b2 ^ 1), pk_buf(b2 ^ 1));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -2538,7 +2440,7 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_64(WideParams p) {
         for (int fb = 0; fb < 8; fb++) sacc[fb][0] = sacc[fb][1] = zero4();
 #pragma unroll
         for (int zb = 0; zb < 4; zb++) zacc[zb] = zero4();
-        if (p.S_in) {
+        if (!ST && p.S_in) {
             const float *Si = p.S_in + (size_t)bh * p.in_bh_stride * S::DP * S::D;
             const float *zi = p.z_in + (size_t)bh * p.in_bh_stride * S::DP;
 #pragma unroll
@@ -2555,8 +2457,8 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_64(WideParams p) {
                 for (int r = 0; r < 4; r++) zacc[zb][r] = zi[16 * (4 * v + zb) + 4 * g + r];
         }
         int t0 = 0, t1 = 0;  // slots to add
-        if (s > 0 && p.slot_mode == 1) t0 = s, t1 = s + 1;
-        if (s > 0 && p.slot_mode == 3) t0 = 0, t1 = s;
+        if (!ST && s > 0 && p.slot_mode == 1) t0 = s, t1 = s + 1;
+        if (!ST && s > 0 && p.slot_mode == 3) t0 = 0, t1 = s;
         // slot image of the d = 64 segment-state pass: value column nn, feature block fb of wave
         // nn / 16 sits in piece (nn / 16) 4 + fb / 2, half fb % 2, lane 16 g + nn % 16
         int lsrc[2], esrc[2];
@@ -2588,12 +2490,64 @@ __global__ __launch_bounds__(512, 1) void causal_ws_kernel_64(WideParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    f32x4 numT[2][2];
-#pragma unroll
-    for (int ib = 0; ib < 2; ib++) numT[ib][0] = numT[ib][1] = zero4();
     const int r0 = 8 * g + (r16 >> 2);
     const int lane_v = r0 * S::D + 8 * v_pos64(r0, 4 * v + (r16 & 3));
     const bf16x8 ones = ones_bf16x8();
+    if constexpr (ST) {
+        // the update alone: S += phi(K)^T V and z += phi(K)^T 1 per chunk, as in the loop below
+        for (int c = 0; c < n; c++) {
+            cw64_issue<true>(p, dl, base, t_begin, t_end, c, n, pw, sm);
+            const bf16_t *sPK = pk_buf(c & 1);
+            const bf16_t *sV = v_buf(c % 3);
+            bf16x8 vop[2], an[2];
+#pragma unroll
+            for (int vb = 0; vb < 2; vb++) vop[vb] = operand_down_rows(sV, lane_v, 4 * vb, S::D);
+#pragma unroll
+            for (int j = 0; j < 2; j++) an[j] = load8(sPK + (16 * j + r16) * S::PT + 8 * g);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) {
+                const bf16x8 ac[2] = {an[0], an[1]};
+                if (ks < 3) {
+#pragma unroll
+                    for (int j = 0; j < 2; j++) an[j] = load8(sPK + (32 * (ks + 1) + 16 * j + r16) * S::PT + 8 * g);
+                }
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+#pragma unroll
+                    for (int vb = 0; vb < 2; vb++)
+                        sacc[2 * ks + j][vb] = mfma_bf16(ac[j], vop[vb], sacc[2 * ks + j][vb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++)
+                zacc[zb] = mfma_bf16(load8(sPK + (16 * (4 * v + zb) + r16) * S::PT + 8 * g), ones, zacc[zb]);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        if (!writes) return;
+        // slot s, in the pieces the slot sum above reads back
+        const size_t sl = (size_t)bh * p.slot_bh_stride + s;
+        float *img = p.S_slots + sl * S::DP * S::D;
+#pragma unroll
+        for (int vb = 0; vb < 2; vb++) {
+            const int nn = value_col<2>(v, vb, r16);
+#pragma unroll
+            for (int fb = 0; fb < 8; fb++) *slot_piece(img, (nn >> 4) * 4 + (fb >> 1), fb & 1, 16 * g + (nn & 15)) = sacc[fb][vb];
+        }
+        if (r16 == 0) {
+            float *zs = p.z_slots + sl * S::DP;
+#pragma unroll
+            for (int zb = 0; zb < 4; zb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) zs[16 * (4 * v + zb) + 4 * g + r] = zacc[zb][r];
+        }
+        return;
+    }
+
+    f32x4 numT[2][2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++) numT[ib][0] = numT[ib][1] = zero4();
     bf16_t *ybase = p.y + base;
 
     for (int c = 0; c < n; c++) {
@@ -2851,13 +2805,14 @@ static hipError_t launch_wide_d(int mode, const WideParams &p, int grid, hipStre
     using K = WideCfg<D>;
     switch (mode) {
     case WM_STATE:
-        // the softmax map at d = 128: the chunked pass's pipeline in its segment-state mode (its
-        // producer pairs share the normalisation; at B1 H32 N4096 it takes 4 % less time per call than
-        // the all-wave segment-state pass)
+        // the softmax maps: the chunked pass's pipeline in its segment-state mode (its producers
+        // normalise without workgroup barriers; at B1 H32 N4096 d128 and B8 H12 N1024 d64 it takes
+        // 11 % and 9 % less time per call than the all-wave segment-state pass with the softmax)
         if (D == 128 && p.softmax)
             hipLaunchKernelGGL((causal_ws_kernel_128<true, true>), dim3(grid), dim3(CausalWsCfg::NT), 0, st, p);
-        else if (D == 64 && p.softmax)
-            hipLaunchKernelGGL((state_sym_kernel<64, true>), dim3(grid), dim3(StateSymCfg<64>::NT), 0, st, p);
+        else if (D == 64 && p.softmax)  // likewise at d = 64, two sequences per workgroup
+            hipLaunchKernelGGL((causal_ws_kernel_64<true, true>), dim3((unsigned)((p.BH + 1) / 2 * p.nseg_grid)),
+                               dim3(CausalWs64Cfg::NT), 0, st, p);
         else if (D == 128 || D == 64)
             hipLaunchKernelGGL((state_sym_kernel<D == 128 ? 128 : 64>), dim3(grid),
                                dim3(StateSymCfg<D == 128 ? 128 : 64>::NT), 0, st, p);
