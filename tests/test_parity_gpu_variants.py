@@ -190,3 +190,20 @@ def test_softmax_maps_reject_a_bias():
     w, x, b = case(HS, 64, N=10)
     with pytest.raises(ValueError, match="no bias"):
         m.hh_linattn_fwd(*(dev(x[n]) for n in ("q", "k", "v")), dev(x["W"]), dev(x["b"]), map=HS)
+
+
+def test_variant_gpt2_heads_sampled_rows():
+    # the GPT-2-125M head shapes (B8 H12 N1024 d64, five segments of 224 tokens) with the per-half
+    # softmax map: every output row of 4 heads of every sequence, and sampled rows of the others
+    # (either side of each segment boundary) by the explicit form
+    w = wl.CONFIGS["c2_gpt2_softmax_map"]
+    say("softmax map, B8 H12 N1024 d64")
+    x = wl.make_inputs(w)
+    m = hh()
+    y = host(m.hh_linattn_fwd(*(dev(x[n]) for n in ("q", "k", "v")), dev(x["W"]), None, map=HS))
+    torch.cuda.synchronize()
+    rtol, atol = wl.tolerance(w.dtype)
+    sub = {k_: (a[:, :4] if k_ in ("q", "k", "v") else a[:4]) for k_, a in x.items()}
+    close(y[:, :4], oracle.causal(HS, sub["q"], sub["k"], sub["v"], sub["W"]), rtol, atol, "heads 0-3, every row")
+    rows = [0, 31, 32, 223, 224, 447, 448, 671, 672, 895, 896, 1023]
+    close(y[:, :, rows], oracle.quadratic(HS, x["q"], x["k"], x["v"], x["W"], rows=rows), rtol, atol, "sampled rows")
